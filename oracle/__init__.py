@@ -1,0 +1,321 @@
+"""fp64 CPU oracle for the CosmoFlow-style 3D-CNN training step.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product package.  It shares no
+code with the HIP path.
+
+Each numpy-level function wraps one definition in ``oracle.c``; the network
+functions at the bottom compose them in the order the method runs a step:
+forward through every block [conv -> leaky ReLU -> 2^3 max pool], flatten,
+three dense layers, mean squared error, then the backward pass in reverse and
+one SGD update (CosmoFlow, Sec. III-A and III-B; Oyama et al., Sec. II-A SGD
+equation and Sec. IV).
+
+Storage model.  The bf16 path stores activations and activation gradients in
+bfloat16 and keeps weight gradients, master weights and the dense head in
+fp32.  ``storage='bf16'`` rounds the oracle's own fp64 values at those same
+storage points (round to nearest, ties to even); ``'f32'`` rounds to fp32;
+``'f64'`` keeps full precision.  Arithmetic between storage points is fp64.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+_i64 = ctypes.c_int64
+_dbl = ctypes.c_double
+_P = ctypes.c_void_p
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = build_oracle(force=False)
+        L = ctypes.CDLL(path)
+        sig = {
+            "or_round_bf16": ([_dbl], _dbl),
+            "or_round_bf16_array": ([_i64, _P], None),
+            "or_round_f32_array": ([_i64, _P], None),
+            "or_num_threads": ([], ctypes.c_int),
+            "or_set_num_threads": ([ctypes.c_int], None),
+            "or_conv3d_fwd": ([_i64] * 6 + [_P, _P, _P], None),
+            "or_conv3d_bwd_data": ([_i64] * 6 + [_P, _P, _P], None),
+            "or_conv3d_bwd_weight": ([_i64] * 6 + [_P, _P, _P], None),
+            "or_conv3d_fwd_points": ([_i64] * 6 + [_P, _P, _i64, _P, _P], None),
+            "or_conv3d_bwd_data_points": ([_i64] * 6 + [_P, _P, _i64, _P, _P], None),
+            "or_conv3d_bwd_weight_points": ([_i64] * 6 + [_P, _P, _i64, _P, _P], None),
+            "or_lrelu_fwd": ([_i64, _dbl, _P, _P], None),
+            "or_lrelu_bwd": ([_i64, _dbl, _P, _P, _P], None),
+            "or_lrelu_maxpool_fwd": ([_i64] * 5 + [_dbl, _P, _P, _P], None),
+            "or_maxpool_lrelu_bwd": ([_i64] * 5 + [_dbl, _P, _P, _P, _P], None),
+            "or_dense_fwd": ([_i64] * 3 + [_P, _P, _P, _dbl, _P, _P], None),
+            "or_dense_bwd": ([_i64] * 3 + [_P, _P, _P, _P, _dbl, _P, _P, _P], None),
+            "or_mse": ([_i64, _i64, _P, _P, _P], _dbl),
+            "or_sgd": ([_i64, _dbl, _P, _P], None),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().or_set_num_threads(int(n))
+
+
+# ----------------------------------------------------------------- rounding
+def round_bf16(x):
+    """Round every element to the nearest bfloat16 value, ties to even."""
+    y = np.array(x, dtype=np.float64, copy=True, order="C")
+    lib().or_round_bf16_array(y.size, _ptr(y))
+    return y
+
+
+def round_f32(x):
+    y = np.array(x, dtype=np.float64, copy=True, order="C")
+    lib().or_round_f32_array(y.size, _ptr(y))
+    return y
+
+
+def store(x, storage: str):
+    """Model a storage point of the given precision ('f64', 'f32', 'bf16')."""
+    if storage == "bf16":
+        return round_bf16(x)
+    if storage == "f32":
+        return round_f32(x)
+    if storage == "f64":
+        return _f64(x)
+    raise ValueError(storage)
+
+
+# --------------------------------------------------------------------- conv
+def conv3d_fwd(x, w):
+    """x [N,D,H,W,Ci], w [3,3,3,Ci,Co] -> y [N,D,H,W,Co] (3^3, stride 1, pad 1)."""
+    x, w = _f64(x), _f64(w)
+    N, D, H, W, Ci = x.shape
+    assert w.shape[:4] == (3, 3, 3, Ci), w.shape
+    Co = w.shape[4]
+    y = np.empty((N, D, H, W, Co), np.float64)
+    lib().or_conv3d_fwd(N, D, H, W, Ci, Co, _ptr(x), _ptr(w), _ptr(y))
+    return y
+
+
+def conv3d_bwd_data(dy, w):
+    """dy [N,D,H,W,Co], w [3,3,3,Ci,Co] -> dx [N,D,H,W,Ci]."""
+    dy, w = _f64(dy), _f64(w)
+    N, D, H, W, Co = dy.shape
+    Ci = w.shape[3]
+    assert w.shape == (3, 3, 3, Ci, Co), w.shape
+    dx = np.empty((N, D, H, W, Ci), np.float64)
+    lib().or_conv3d_bwd_data(N, D, H, W, Ci, Co, _ptr(dy), _ptr(w), _ptr(dx))
+    return dx
+
+
+def conv3d_bwd_weight(x, dy):
+    """x [N,D,H,W,Ci], dy [N,D,H,W,Co] -> dw [3,3,3,Ci,Co]."""
+    x, dy = _f64(x), _f64(dy)
+    N, D, H, W, Ci = x.shape
+    Co = dy.shape[4]
+    assert dy.shape[:4] == x.shape[:4]
+    dw = np.empty((3, 3, 3, Ci, Co), np.float64)
+    lib().or_conv3d_bwd_weight(N, D, H, W, Ci, Co, _ptr(x), _ptr(dy), _ptr(dw))
+    return dw
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def conv3d_fwd_points(x32, w32, pts):
+    """Forward conv evaluated at flat output indices ``pts`` of y [N,D,H,W,Co].
+
+    x32 and w32 are float32 arrays of exactly representable inputs; the sums
+    are fp64."""
+    x32, w32 = _f32(x32), _f32(w32)
+    pts = np.ascontiguousarray(pts, dtype=np.int64)
+    N, D, H, W, Ci = x32.shape
+    Co = w32.shape[4]
+    out = np.empty(pts.size, np.float64)
+    lib().or_conv3d_fwd_points(N, D, H, W, Ci, Co, _ptr(x32), _ptr(w32), pts.size, _ptr(pts), _ptr(out))
+    return out
+
+
+def conv3d_bwd_data_points(dy32, w32, pts):
+    """Backward-data evaluated at flat indices ``pts`` of dx [N,D,H,W,Ci]."""
+    dy32, w32 = _f32(dy32), _f32(w32)
+    pts = np.ascontiguousarray(pts, dtype=np.int64)
+    N, D, H, W, Co = dy32.shape
+    Ci = w32.shape[3]
+    out = np.empty(pts.size, np.float64)
+    lib().or_conv3d_bwd_data_points(N, D, H, W, Ci, Co, _ptr(dy32), _ptr(w32), pts.size, _ptr(pts), _ptr(out))
+    return out
+
+
+def conv3d_bwd_weight_points(x32, dy32, pts):
+    """Backward-weight evaluated at flat indices ``pts`` of dw [3,3,3,Ci,Co]."""
+    x32, dy32 = _f32(x32), _f32(dy32)
+    pts = np.ascontiguousarray(pts, dtype=np.int64)
+    N, D, H, W, Ci = x32.shape
+    Co = dy32.shape[4]
+    out = np.empty(pts.size, np.float64)
+    lib().or_conv3d_bwd_weight_points(N, D, H, W, Ci, Co, _ptr(x32), _ptr(dy32), pts.size, _ptr(pts), _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------- activations
+def lrelu_fwd(x, slope):
+    x = _f64(x)
+    y = np.empty_like(x)
+    lib().or_lrelu_fwd(x.size, float(slope), _ptr(x), _ptr(y))
+    return y
+
+
+def lrelu_bwd(x, dy, slope):
+    x, dy = _f64(x), _f64(dy)
+    dx = np.empty_like(x)
+    lib().or_lrelu_bwd(x.size, float(slope), _ptr(x), _ptr(dy), _ptr(dx))
+    return dx
+
+
+def lrelu_maxpool_fwd(z, slope):
+    """z [N,D,H,W,C] (D,H,W even) -> (p [N,D/2,H/2,W/2,C], idx uint8 same shape)."""
+    z = _f64(z)
+    N, D, H, W, C = z.shape
+    assert D % 2 == 0 and H % 2 == 0 and W % 2 == 0
+    p = np.empty((N, D // 2, H // 2, W // 2, C), np.float64)
+    idx = np.empty(p.shape, np.uint8)
+    lib().or_lrelu_maxpool_fwd(N, D, H, W, C, float(slope), _ptr(z), _ptr(p), _ptr(idx))
+    return p, idx
+
+
+def maxpool_lrelu_bwd(dp, p, idx, slope):
+    """-> dz [N,2Dp,2Hp,2Wp,C]."""
+    dp, p = _f64(dp), _f64(p)
+    idx = np.ascontiguousarray(idx, dtype=np.uint8)
+    N, Dp, Hp, Wp, C = dp.shape
+    dz = np.empty((N, 2 * Dp, 2 * Hp, 2 * Wp, C), np.float64)
+    lib().or_maxpool_lrelu_bwd(N, 2 * Dp, 2 * Hp, 2 * Wp, C, float(slope), _ptr(dp), _ptr(p), _ptr(idx), _ptr(dz))
+    return dz
+
+
+# -------------------------------------------------------------------- dense
+def dense_fwd(x, w, b, slope):
+    """x [B,In], w [In,Out], b [Out]; slope < 0 means a linear layer."""
+    x, w = _f64(x), _f64(w)
+    b = _f64(b) if b is not None else None
+    B, In = x.shape
+    Out = w.shape[1]
+    pre = np.empty((B, Out), np.float64)
+    y = np.empty((B, Out), np.float64)
+    lib().or_dense_fwd(B, In, Out, _ptr(x), _ptr(w), _ptr(b), float(slope), _ptr(pre), _ptr(y))
+    return pre, y
+
+
+def dense_bwd(x, w, pre, dy, slope, need_dx=True):
+    x, w, pre, dy = _f64(x), _f64(w), _f64(pre), _f64(dy)
+    B, In = x.shape
+    Out = w.shape[1]
+    dx = np.empty((B, In), np.float64) if need_dx else None
+    dw = np.empty((In, Out), np.float64)
+    db = np.empty((Out,), np.float64)
+    lib().or_dense_bwd(B, In, Out, _ptr(x), _ptr(w), _ptr(pre), _ptr(dy), float(slope), _ptr(dx), _ptr(dw), _ptr(db))
+    return dx, dw, db
+
+
+def mse(yhat, t):
+    """-> (loss, dyhat) with loss = mean over all B*K entries."""
+    yhat, t = _f64(yhat), _f64(t)
+    B, K = yhat.shape
+    d = np.empty_like(yhat)
+    loss = lib().or_mse(B, K, _ptr(yhat), _ptr(t), _ptr(d))
+    return float(loss), d
+
+
+def sgd(w, dw, lr):
+    """Returns W - lr * dW (a new array)."""
+    w2 = np.array(w, dtype=np.float64, copy=True, order="C")
+    dw = _f64(dw)
+    lib().or_sgd(w2.size, float(lr), _ptr(w2), _ptr(dw))
+    return w2
+
+
+# ------------------------------------------------------------------ network
+def network_forward(x, conv_w, dense_w, slope, storage="f64"):
+    """Forward pass of the conv stack and the dense head.
+
+    x [B,D,H,W,Cin]; conv_w list of [3,3,3,Ci,Co]; dense_w list of three
+    (W [In,Out], b [Out]).  Returns (yhat, cache)."""
+    a = store(x, storage)
+    blocks = []
+    for w in conv_w:
+        z = store(conv3d_fwd(a, w), storage)
+        p, idx = lrelu_maxpool_fwd(z, slope)
+        p = store(p, storage)
+        blocks.append(dict(x=a, p=p, idx=idx))
+        a = p
+    B = a.shape[0]
+    h = a.reshape(B, -1)
+    dense = []
+    for li, (W, b) in enumerate(dense_w):
+        s = slope if li < len(dense_w) - 1 else -1.0
+        pre, y = dense_fwd(h, W, b, s)
+        dense.append(dict(x=h, pre=pre, slope=s))
+        h = y
+    return h, dict(blocks=blocks, dense=dense, last_shape=a.shape)
+
+
+def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_dgrad=False):
+    """Backward pass; returns (conv_dw list, dense grads list of (dW, db))."""
+    g = dyhat
+    dense_g = [None] * len(dense_w)
+    for li in reversed(range(len(dense_w))):
+        c = cache["dense"][li]
+        dx, dw, db = dense_bwd(c["x"], dense_w[li][0], c["pre"], g, c["slope"], need_dx=True)
+        dense_g[li] = (dw, db)
+        g = dx
+    dp = store(g.reshape(cache["last_shape"]), storage)
+    conv_g = [None] * len(conv_w)
+    for l in reversed(range(len(conv_w))):
+        blk = cache["blocks"][l]
+        dz = store(maxpool_lrelu_bwd(dp, blk["p"], blk["idx"], slope), storage)
+        conv_g[l] = conv3d_bwd_weight(blk["x"], dz)
+        if l > 0 or first_dgrad:
+            dp = store(conv3d_bwd_data(dz, conv_w[l]), storage)
+    return conv_g, dense_g
+
+
+def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64"):
+    """One full step.  Weights used in the passes are the masters rounded to
+    the storage precision (bf16 for the conv weights of the bf16 path); the
+    update is applied to the fp32/fp64 masters.
+
+    Returns dict(loss, yhat, conv_w, dense_w, conv_dw, dense_g)."""
+    conv_use = [store(w, storage) for w in conv_w32]
+    dense_use = [(_f64(W), _f64(b)) for W, b in dense_w32]
+    yhat, cache = network_forward(x, conv_use, dense_use, slope, storage)
+    loss, dy = mse(yhat, targets)
+    conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage)
+    master = "f64" if storage == "f64" else "f32"
+    new_conv = [store(sgd(w, g, lr), master) for w, g in zip(conv_w32, conv_g)]
+    new_dense = [(store(sgd(W, dW, lr), master), store(sgd(b, db, lr), master))
+                 for (W, b), (dW, db) in zip(dense_w32, dense_g)]
+    return dict(loss=loss, yhat=yhat, conv_w=new_conv, dense_w=new_dense,
+                conv_dw=conv_g, dense_g=dense_g)

@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle legs.
+
+This module draws random inputs only; it holds none of the method's
+arithmetic.  The real workloads are N-body dark-matter volumes: 4 channels
+(redshifts) of particle-count histograms, 128^3 sub-volumes cut from 512^3
+boxes (CosmoFlow, Sec. IV-C; Oyama et al., Sec. II-B), with the cosmological
+parameters normalised to [-1, 1] as regression targets (Oyama et al.,
+Sec. II-B).  Those data are not available here, so these generators stand in
+for them with the same shapes and a similar value structure: a unit-mean
+lognormal density per sample and channel, Poisson-sampled counts (many empty
+voxels), and log(1 + counts) as the network input.
+
+Streams: ``numpy.random.default_rng(SeedSequence([2026, cfg_id]))`` spawned
+into the fixed order [field, poisson, conv-weights, dense-weights, targets,
+upstream-grad].
+"""
+import numpy as np
+
+STREAMS = ("field", "poisson", "convw", "densew", "targets", "upstream")
+
+
+def streams(cfg_id: int, seed: int = 2026):
+    """Dict of independent numpy Generators for one configuration."""
+    ss = np.random.SeedSequence([seed, cfg_id])
+    return {name: np.random.default_rng(child) for name, child in zip(STREAMS, ss.spawn(len(STREAMS)))}
+
+
+def bf16_round_f32(x):
+    """Round float32 values to the nearest bfloat16 (ties to even), returned
+    as float32.  Used only to quantise generated inputs to the bf16 grid."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    # keep NaN/Inf as they are (not produced by these generators)
+    bad = ~np.isfinite(a)
+    if bad.any():
+        out = out.copy()
+        out[bad] = a[bad]
+    return out.reshape(np.shape(x))
+
+
+def lognormal_density(rng, shape_ndhw, channels, dtype=np.float32):
+    """delta = exp(g) / mean(exp(g)) per sample and channel, g ~ N(0,1) white.
+
+    Returns [N,D,H,W,C] float.  Generated channel by channel to bound RAM."""
+    N = shape_ndhw[0]
+    out = np.empty(tuple(shape_ndhw) + (channels,), dtype)
+    for n in range(N):
+        for c in range(channels):
+            e = np.exp(rng.standard_normal(shape_ndhw[1:], dtype=np.float32))
+            e /= e.mean(dtype=np.float64)
+            out[n, ..., c] = e
+    return out
+
+
+def lognormal_field_input(rng, shape_ndhw, channels):
+    """log(1 + delta) of a unit-mean lognormal field (no Poisson sampling)."""
+    d = lognormal_density(rng, shape_ndhw, channels)
+    np.log1p(d, out=d)
+    return d
+
+
+def lognormal_poisson_input(rng_field, rng_pois, shape_ndhw, channels, bf16=True):
+    """log(1 + Poisson(delta)) with delta a unit-mean lognormal density, per
+    sample and channel; optionally quantised to the bf16 grid."""
+    N = shape_ndhw[0]
+    out = np.empty(tuple(shape_ndhw) + (channels,), np.float32)
+    for n in range(N):
+        for c in range(channels):
+            e = np.exp(rng_field.standard_normal(shape_ndhw[1:], dtype=np.float32))
+            e /= e.mean(dtype=np.float64)
+            counts = rng_pois.poisson(e).astype(np.float32)
+            np.log1p(counts, out=counts)
+            out[n, ..., c] = counts
+    return bf16_round_f32(out) if bf16 else out
+
+
+def he_normal_conv(rng, cin, cout, dtype=np.float32):
+    """He-normal conv weights, DHWIO [3,3,3,cin,cout], N(0, 2/(27*cin))."""
+    std = np.sqrt(2.0 / (27.0 * cin))
+    return (rng.standard_normal((3, 3, 3, cin, cout)) * std).astype(dtype)
+
+
+def he_normal_dense(rng, fan_in, fan_out, dtype=np.float32):
+    """He-normal dense weights [in,out], N(0, 2/in); zero bias."""
+    std = np.sqrt(2.0 / fan_in)
+    w = (rng.standard_normal((fan_in, fan_out)) * std).astype(dtype)
+    return w, np.zeros((fan_out,), dtype)
+
+
+def targets(rng, batch, k=3, dtype=np.float32):
+    """Normalised regression targets U(-1, 1)."""
+    return rng.uniform(-1.0, 1.0, size=(batch, k)).astype(dtype)
+
+
+def normal(rng, shape, bf16=True, scale=1.0):
+    """N(0, scale^2) values (upstream gradients, synthetic activations)."""
+    x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+    return bf16_round_f32(x) if bf16 else x
+
+
+def pool_indices(rng, shape):
+    """Uniform window positions 0..7 (synthetic max-pool argmax)."""
+    return rng.integers(0, 8, size=shape, dtype=np.uint8)
