@@ -1,0 +1,277 @@
+"""ctypes binding of libcf.so (include/cf.h), one Python function per C entry
+point with the same name.  Argument marshalling only: shapes are read from
+torch tensors, outputs and workspaces are allocated with torch on the
+tensors' device, the call goes to the library on torch's current stream, and
+a non-zero status raises CfError.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcf.so")
+
+CF_OK, CF_ERR_INVALID, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_HIP = 0, -1, -2, -3, -4
+CF_F32, CF_BF16 = 0, 1
+CF_CONV_FWD, CF_CONV_BWD_DATA, CF_CONV_BWD_WEIGHT = 0, 1, 2
+CF_MAX_BLOCKS = 8
+
+
+class CfError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (status %d): %s" % (_status_name(status), status, msg))
+        self.status = status
+
+
+class cf_dims(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("w", ctypes.c_int64), ("c", ctypes.c_int64)]
+
+
+class cf_conv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("stride", ctypes.c_int32), ("pad", ctypes.c_int32)]
+
+
+class cf_model_desc(ctypes.Structure):
+    _fields_ = [("nblocks", ctypes.c_int32), ("cin", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("h", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("filters", ctypes.c_int32 * CF_MAX_BLOCKS), ("dense", ctypes.c_int32 * 3),
+                ("slope", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_SIG = {
+    "cf_abi_version": ([], ctypes.c_int32),
+    "cf_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "cf_last_error": ([], ctypes.c_char_p),
+    "cf_conv3d_workspace_size": ([ctypes.c_int, cf_dims, ctypes.c_int32, cf_conv, ctypes.c_int], ctypes.c_size_t),
+    "cf_conv3d_fwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_conv3d_bwd_data": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_conv3d_bwd_weight": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_pool3d_fwd": ([ctypes.c_int, cf_dims, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "cf_pool3d_bwd": ([ctypes.c_int, cf_dims, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "cf_lrelu": ([ctypes.c_int, ctypes.c_int64, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "cf_dense_workspace_size": ([ctypes.c_int32] * 3, ctypes.c_size_t),
+    "cf_dense_fwd": ([ctypes.c_int32] * 3 + [_P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_dense_bwd": ([ctypes.c_int32] * 3 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
+    "cf_mse": ([ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "cf_sgd": ([ctypes.c_int64, ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "cf_train_step_workspace_size": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32], ctypes.c_size_t),
+    "cf_train_step": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32, _P, _P, ctypes.POINTER(_P),
+                       ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libcf.so.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libcf.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIG.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _status_name(s):
+    return {0: "CF_OK", -1: "CF_ERR_INVALID", -2: "CF_ERR_UNSUPPORTED", -3: "CF_ERR_WORKSPACE",
+            -4: "CF_ERR_HIP"}.get(s, "?")
+
+
+def check(status):
+    if status != CF_OK:
+        raise CfError(status, lib().cf_last_error().decode())
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return CF_F32
+    if t == torch.bfloat16:
+        return CF_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dims(shape) -> cf_dims:
+    n, d, h, w, c = (int(v) for v in shape)
+    return cf_dims(n, d, h, w, c)
+
+
+CONV3 = cf_conv(3, 1, 1)
+
+
+def _ws(nbytes, device, ws=None):
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _wsbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+# --------------------------------------------------------------------- conv
+def cf_conv3d_workspace_size(dtype, xshape, cout, pass_):
+    return int(lib().cf_conv3d_workspace_size(dtype, dims(xshape), int(cout), CONV3, int(pass_)))
+
+
+def cf_conv3d_fwd(X, W, Y=None, ws=None, stream=None):
+    """X [N,D,H,W,Cin], W [3,3,3,Cin,Cout] (same dtype) -> Y [N,D,H,W,Cout]."""
+    dt = dtype_code(X.dtype)
+    cout = int(W.shape[4])
+    if Y is None:
+        Y = torch.empty(tuple(X.shape[:4]) + (cout,), dtype=X.dtype, device=X.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_FWD), X.device, ws)
+    check(lib().cf_conv3d_fwd(dt, dims(X.shape), _ptr(X), _ptr(W), cout, CONV3, _ptr(Y), _ptr(ws), _wsbytes(ws),
+                              _stream(stream)))
+    return Y
+
+
+def cf_conv3d_bwd_data(dY, W, dX=None, ws=None, stream=None):
+    """dY [N,D,H,W,Cout], W [3,3,3,Cin,Cout] -> dX [N,D,H,W,Cin]."""
+    dt = dtype_code(dY.dtype)
+    cin, cout = int(W.shape[3]), int(W.shape[4])
+    xshape = tuple(dY.shape[:4]) + (cin,)
+    if dX is None:
+        dX = torch.empty(xshape, dtype=dY.dtype, device=dY.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, xshape, cout, CF_CONV_BWD_DATA), dY.device, ws)
+    check(lib().cf_conv3d_bwd_data(dt, dims(xshape), _ptr(dY), _ptr(W), cout, CONV3, _ptr(dX), _ptr(ws),
+                                   _wsbytes(ws), _stream(stream)))
+    return dX
+
+
+def cf_conv3d_bwd_weight(X, dY, dW=None, ws=None, stream=None):
+    """X [N,D,H,W,Cin], dY [N,D,H,W,Cout] -> dW [3,3,3,Cin,Cout] fp32."""
+    dt = dtype_code(X.dtype)
+    cout = int(dY.shape[4])
+    if dW is None:
+        dW = torch.empty((3, 3, 3, int(X.shape[4]), cout), dtype=torch.float32, device=X.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_BWD_WEIGHT), X.device, ws)
+    check(lib().cf_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, CONV3, _ptr(dW), _ptr(ws),
+                                     _wsbytes(ws), _stream(stream)))
+    return dW
+
+
+# --------------------------------------------------------------------- pool
+def cf_pool3d_fwd(Z, slope, P=None, idx=None, stream=None):
+    """Z [N,D,H,W,C] -> (P [N,D/2,H/2,W/2,C], idx uint8)."""
+    dt = dtype_code(Z.dtype)
+    N, D, H, W, C = (int(v) for v in Z.shape)
+    pshape = (N, D // 2, H // 2, W // 2, C)
+    if P is None:
+        P = torch.empty(pshape, dtype=Z.dtype, device=Z.device)
+    if idx is None:
+        idx = torch.empty(pshape, dtype=torch.uint8, device=Z.device)
+    check(lib().cf_pool3d_fwd(dt, dims(Z.shape), _ptr(Z), float(slope), _ptr(P), _ptr(idx), _stream(stream)))
+    return P, idx
+
+
+def cf_pool3d_bwd(dP, P, idx, slope, dZ=None, stream=None):
+    dt = dtype_code(dP.dtype)
+    N, Dp, Hp, Wp, C = (int(v) for v in dP.shape)
+    zshape = (N, 2 * Dp, 2 * Hp, 2 * Wp, C)
+    if dZ is None:
+        dZ = torch.empty(zshape, dtype=dP.dtype, device=dP.device)
+    check(lib().cf_pool3d_bwd(dt, dims(zshape), _ptr(dP), _ptr(P), _ptr(idx), float(slope), _ptr(dZ),
+                              _stream(stream)))
+    return dZ
+
+
+def cf_lrelu(x, slope, dy=None, out=None, stream=None):
+    dt = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    check(lib().cf_lrelu(dt, x.numel(), _ptr(x), _ptr(dy), float(slope), _ptr(out), _stream(stream)))
+    return out
+
+
+# -------------------------------------------------------------------- dense
+def cf_dense_fwd(X, W, b, slope, pre=None, Y=None, ws=None, stream=None):
+    """X [B,in] fp32, W [in,out], b [out] or None -> (pre, Y)."""
+    B, fin = (int(v) for v in X.shape)
+    fout = int(W.shape[1])
+    if pre is None:
+        pre = torch.empty((B, fout), dtype=torch.float32, device=X.device)
+    if Y is None:
+        Y = torch.empty((B, fout), dtype=torch.float32, device=X.device)
+    ws = _ws(int(lib().cf_dense_workspace_size(B, fin, fout)), X.device, ws)
+    check(lib().cf_dense_fwd(B, fin, fout, _ptr(X), _ptr(W), _ptr(b), float(slope), _ptr(pre), _ptr(Y), _ptr(ws),
+                             _wsbytes(ws), _stream(stream)))
+    return pre, Y
+
+
+def cf_dense_bwd(X, W, pre, dY, slope, need_dx=True, stream=None):
+    B, fin = (int(v) for v in X.shape)
+    fout = int(W.shape[1])
+    dX = torch.empty((B, fin), dtype=torch.float32, device=X.device) if need_dx else None
+    dW = torch.empty((fin, fout), dtype=torch.float32, device=X.device)
+    db = torch.empty((fout,), dtype=torch.float32, device=X.device)
+    check(lib().cf_dense_bwd(B, fin, fout, _ptr(X), _ptr(W), _ptr(pre), _ptr(dY), float(slope), _ptr(dX), _ptr(dW),
+                             _ptr(db), _stream(stream)))
+    return dX, dW, db
+
+
+def cf_mse(yhat, t, stream=None):
+    """-> (loss [1] device tensor, dyhat)."""
+    B, K = (int(v) for v in yhat.shape)
+    loss = torch.empty((1,), dtype=torch.float32, device=yhat.device)
+    dy = torch.empty_like(yhat)
+    check(lib().cf_mse(B, K, _ptr(yhat), _ptr(t), _ptr(loss), _ptr(dy), _stream(stream)))
+    return loss, dy
+
+
+def cf_sgd(W, dW, lr, stream=None):
+    """In place: W -= lr * dW (fp32)."""
+    check(lib().cf_sgd(W.numel(), float(lr), _ptr(W), _ptr(dW), _stream(stream)))
+    return W
+
+
+# -------------------------------------------------------------- train step
+def model_desc(in_channels, size, filters, dense=(128, 64, 3), slope=0.3):
+    """cf_model_desc for a cubic input (or size = (d, h, w))."""
+    m = cf_model_desc()
+    d, h, w = (size, size, size) if isinstance(size, int) else size
+    m.nblocks, m.cin, m.d, m.h, m.w = len(filters), in_channels, d, h, w
+    for i, f in enumerate(filters):
+        m.filters[i] = f
+    for i, f in enumerate(dense):
+        m.dense[i] = f
+    m.slope = slope
+    return m
+
+
+def cf_train_step_workspace_size(m, dtype, B):
+    return int(lib().cf_train_step_workspace_size(ctypes.byref(m), dtype, int(B)))
+
+
+def cf_train_step(m, X, targets, params, lr, ws=None, loss=None, pred=None, stream=None):
+    """One training step; `params` (fp32 masters: conv W per block, then W1,
+    b1, W2, b2, W3, b3) are updated in place.  Returns (loss, pred)."""
+    dt = dtype_code(X.dtype)
+    B = int(X.shape[0])
+    ws = _ws(cf_train_step_workspace_size(m, dt, B), X.device, ws)
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=X.device)
+    arr = (_P * len(params))(*[p.data_ptr() for p in params])
+    check(lib().cf_train_step(ctypes.byref(m), dt, B, _ptr(X), _ptr(targets), arr, float(lr), _ptr(loss), _ptr(pred),
+                              _ptr(ws), _wsbytes(ws), _stream(stream)))
+    return loss, pred

@@ -1,0 +1,639 @@
+// C ABI of libcf.so: argument validation, path selection and the training
+// step.  Every entry point validates before enqueuing anything, enqueues on
+// the caller's stream, and never synchronises or allocates.
+#include "cf_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace cf {
+namespace {
+
+thread_local char g_err[512] = "";
+
+cf_status fail(cf_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+cf_status check_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return CF_OK;
+    return fail(CF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define CF_TRY_HIP(expr, what)                                   \
+    do {                                                         \
+        cf_status st_ = check_hip((expr), (what));               \
+        if (st_ != CF_OK) return st_;                            \
+    } while (0)
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+int roundup(int v, int m) { return (v + m - 1) / m * m; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+cf_status check_dims(const cf_dims& x, const char* name)
+{
+    if (x.n <= 0 || x.d <= 0 || x.h <= 0 || x.w <= 0 || x.c <= 0)
+        return fail(CF_ERR_INVALID, "%s: every dimension must be positive", name);
+    if (x.n > kMaxDim || x.d > kMaxDim || x.h > kMaxDim || x.w > kMaxDim || x.c > 65536)
+        return fail(CF_ERR_INVALID, "%s: dimension too large", name);
+    const double el = (double)x.n * (double)x.d * (double)x.h * (double)x.w * (double)x.c;
+    if (el > (double)kMaxElems) return fail(CF_ERR_INVALID, "%s: tensor too large", name);
+    return CF_OK;
+}
+
+cf_status check_dtype(cf_dtype dt)
+{
+    if (dt != CF_F32 && dt != CF_BF16) return fail(CF_ERR_INVALID, "unknown dtype %d", (int)dt);
+    return CF_OK;
+}
+
+cf_status check_conv(cf_dtype dt, const cf_dims& x, int32_t cout, const cf_conv& cv)
+{
+    cf_status s = check_dtype(dt);
+    if (s != CF_OK) return s;
+    if ((s = check_dims(x, "x")) != CF_OK) return s;
+    if (cout <= 0 || cout > 65536) return fail(CF_ERR_INVALID, "cout must be in 1..65536");
+    if (cv.k != 3 || cv.stride != 1 || cv.pad != 1)
+        return fail(CF_ERR_UNSUPPORTED, "only k=3, stride=1, pad=1 is implemented (got k=%d stride=%d pad=%d)", cv.k,
+                    cv.stride, cv.pad);
+    const double el = (double)x.n * x.d * x.h * x.w * (double)cout;
+    if (el > (double)kMaxElems) return fail(CF_ERR_INVALID, "output tensor too large");
+    return CF_OK;
+}
+
+// ------------------------------------------------------------ path choice
+enum class Fwd { Mfma, C4, Direct };
+enum class Wg { Mfma, C4, Direct };
+
+Fwd fwd_path(cf_dtype dt, int64_t cin, int cout)
+{
+    if (dt == CF_BF16 && cout % 4 == 0) {
+        if (cin % 32 == 0) return Fwd::Mfma;
+        if (cin == 4) return Fwd::C4;
+    }
+    return Fwd::Direct;
+}
+
+// backward-data runs the forward kernels with in = cout, out = cin
+Fwd dgrad_path(cf_dtype dt, int64_t cin, int cout)
+{
+    if (dt == CF_BF16 && cout % 32 == 0 && cin % 4 == 0) return Fwd::Mfma;
+    return Fwd::Direct;
+}
+
+Wg wgrad_path(cf_dtype dt, int64_t cin, int cout)
+{
+    if (dt == CF_BF16) {
+        if (cin % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
+        if (cin == 4 && cout == 32) return Wg::C4;
+    }
+    return Wg::Direct;
+}
+
+size_t esize(cf_dtype dt) { return dt == CF_F32 ? 4 : 2; }
+
+// Bytes of re-laid weights each path uses.
+size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
+{
+    switch (p) {
+    case Fwd::Mfma: return (size_t)27 * roundup(cout, 128) * (size_t)cin * 2;
+    case Fwd::C4: return (size_t)roundup(cout, 128) * 128 * 2;
+    default: return 0;
+    }
+}
+
+size_t dgrad_wk_bytes(Fwd p, cf_dtype dt, int64_t cin, int cout)
+{
+    if (p == Fwd::Mfma) return (size_t)27 * roundup((int)cin, 128) * (size_t)cout * 2;
+    return (size_t)27 * (size_t)cin * cout * esize(dt);
+}
+
+cf_dims with_c(const cf_dims& x, int64_t c) { cf_dims y = x; y.c = c; return y; }
+
+// Enqueue the forward conv given prepared weights `wk` (layout per path; for
+// the direct path `wk` is DHWIO in the data type).
+hipError_t run_fwd(Fwd p, cf_dtype dt, const cf_dims& x, const void* X, const void* wk, int cout, void* Y, float* part,
+                   hipStream_t s)
+{
+    switch (p) {
+    case Fwd::Mfma: {
+        const ConvPlan plan = plan_conv_mfma(x, cout);
+        return launch_conv_mfma(plan, (const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, part, x, cout,
+                                roundup(cout, 128), s);
+    }
+    case Fwd::C4:
+        return launch_conv_c4_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, roundup(cout, 128), s);
+    default:
+        if (dt == CF_F32) return launch_conv_direct<float>((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
+        return launch_conv_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, s);
+    }
+}
+
+size_t fwd_part_bytes(Fwd p, const cf_dims& x, int cout)
+{
+    return p == Fwd::Mfma ? plan_conv_mfma(x, cout).part_bytes : 0;
+}
+
+// Backward-data with prepared weights: x is the forward input shape.
+hipError_t run_dgrad(Fwd p, cf_dtype dt, const cf_dims& x, const void* dY, const void* wk, int cout, void* dX,
+                     float* part, hipStream_t s)
+{
+    const cf_dims y = with_c(x, cout);          // dY shape: forward output
+    if (p == Fwd::Mfma) {
+        const ConvPlan plan = plan_conv_mfma(y, (int)x.c);
+        return launch_conv_mfma(plan, (const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, part, y, (int)x.c,
+                                roundup((int)x.c, 128), s);
+    }
+    if (dt == CF_F32) return launch_conv_direct<float>((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
+    return launch_conv_direct<uint16_t>((const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, y, (int)x.c, s);
+}
+
+size_t dgrad_part_bytes(Fwd p, const cf_dims& x, int cout)
+{
+    return p == Fwd::Mfma ? plan_conv_mfma(with_c(x, cout), (int)x.c).part_bytes : 0;
+}
+
+size_t wgrad_part_bytes(Wg p, cf_dtype dt, const cf_dims& x, int cout)
+{
+    if (p != Wg::Direct) return plan_wgrad(x, cout).part_bytes;
+    return dt == CF_F32 ? wgrad_direct_part_bytes<float>(x, cout) : wgrad_direct_part_bytes<uint16_t>(x, cout);
+}
+
+hipError_t run_wgrad(Wg p, cf_dtype dt, const cf_dims& x, const void* X, const void* dY, int cout, float* dW,
+                     float* part, hipStream_t s)
+{
+    if (p != Wg::Direct) {
+        const WgradPlan plan = plan_wgrad(x, cout);
+        return launch_wgrad(plan, (const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
+    }
+    if (dt == CF_F32) return launch_wgrad_direct<float>((const float*)X, (const float*)dY, part, dW, x, cout, s);
+    return launch_wgrad_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
+}
+
+// Prepare forward weights from a DHWIO source (fp32 master or bf16).
+hipError_t prep_fwd(Fwd p, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
+{
+    switch (p) {
+    case Fwd::Mfma: return launch_wprep_fwd(W, src_f32, (int)cin, cout, roundup(cout, 128), (uint16_t*)wk, s);
+    case Fwd::C4: return launch_wprep_c4(W, src_f32, cout, roundup(cout, 128), (uint16_t*)wk, s);
+    default: return hipSuccess;
+    }
+}
+
+hipError_t prep_dgrad(Fwd p, cf_dtype dt, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
+{
+    if (p == Fwd::Mfma) return launch_wprep_dgrad(W, src_f32, (int)cin, cout, roundup((int)cin, 128), (uint16_t*)wk, s);
+    return launch_wprep_direct_dgrad(W, dt, (int)cin, cout, wk, s);
+}
+
+}  // namespace
+}  // namespace cf
+
+using namespace cf;
+
+extern "C" {
+
+int32_t cf_abi_version(void) { return CF_ABI_VERSION; }
+
+const char* cf_status_string(cf_status s)
+{
+    switch (s) {
+    case CF_OK: return "ok";
+    case CF_ERR_INVALID: return "invalid argument";
+    case CF_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CF_ERR_WORKSPACE: return "workspace too small";
+    case CF_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* cf_last_error(void) { return g_err; }
+
+size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv conv, cf_conv_pass pass)
+{
+    if (check_conv(dtype, x, cout, conv) != CF_OK) return 0;
+    switch (pass) {
+    case CF_CONV_FWD: {
+        const Fwd p = fwd_path(dtype, x.c, cout);
+        return up256(fwd_wk_bytes(p, x.c, cout)) + up256(fwd_part_bytes(p, x, cout));
+    }
+    case CF_CONV_BWD_DATA: {
+        const Fwd p = dgrad_path(dtype, x.c, cout);
+        return up256(dgrad_wk_bytes(p, dtype, x.c, cout)) + up256(dgrad_part_bytes(p, x, cout));
+    }
+    case CF_CONV_BWD_WEIGHT:
+        return up256(wgrad_part_bytes(wgrad_path(dtype, x.c, cout), dtype, x, cout));
+    default:
+        return 0;
+    }
+}
+
+cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv, void* Y,
+                        void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (!X || !W || !Y) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: null tensor pointer");
+    if (!al16(X) || !al16(W) || !al16(Y)) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: pointers must be 16-byte aligned");
+    const Fwd p = fwd_path(dtype, x.c, cout);
+    const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout));
+    const size_t need = wkb + up256(fwd_part_bytes(p, x, cout));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+    if (need && (!ws || !al16(ws))) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: workspace null or misaligned");
+    char* w8 = (char*)ws;
+    const void* wk = W;
+    if (p != Fwd::Direct) {
+        CF_TRY_HIP(prep_fwd(p, W, false, x.c, cout, w8, stream), "weight re-layout");
+        wk = w8;
+    }
+    CF_TRY_HIP(run_fwd(p, dtype, x, X, wk, cout, Y, (float*)(w8 ? w8 + wkb : nullptr), stream), "conv3d forward");
+    return CF_OK;
+}
+
+cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const void* W, int32_t cout, cf_conv conv,
+                             void* dX, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (!dY || !W || !dX) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: null tensor pointer");
+    if (!al16(dY) || !al16(W) || !al16(dX)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: pointers must be 16-byte aligned");
+    const Fwd p = dgrad_path(dtype, x.c, cout);
+    const size_t wkb = up256(dgrad_wk_bytes(p, dtype, x.c, cout));
+    const size_t need = wkb + up256(dgrad_part_bytes(p, x, cout));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_bwd_data: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: workspace null or misaligned");
+    char* w8 = (char*)ws;
+    CF_TRY_HIP(prep_dgrad(p, dtype, W, false, x.c, cout, w8, stream), "weight re-layout");
+    CF_TRY_HIP(run_dgrad(p, dtype, x, dY, w8, cout, dX, (float*)(w8 + wkb), stream), "conv3d backward-data");
+    return CF_OK;
+}
+
+cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout, cf_conv conv,
+                               float* dW, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (!X || !dY || !dW) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: null tensor pointer");
+    if (!al16(X) || !al16(dY) || !al16(dW)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: pointers must be 16-byte aligned");
+    const Wg p = wgrad_path(dtype, x.c, cout);
+    const size_t need = up256(wgrad_part_bytes(p, dtype, x, cout));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_bwd_weight: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: workspace null or misaligned");
+    CF_TRY_HIP(run_wgrad(p, dtype, x, X, dY, cout, dW, (float*)ws, stream), "conv3d backward-weight");
+    return CF_OK;
+}
+
+static cf_status check_pool(cf_dtype dtype, const cf_dims& z)
+{
+    cf_status st = check_dtype(dtype);
+    if (st != CF_OK) return st;
+    if ((st = check_dims(z, "z")) != CF_OK) return st;
+    if ((z.d & 1) || (z.h & 1) || (z.w & 1))
+        return fail(CF_ERR_UNSUPPORTED, "2^3 stride-2 pooling needs even D, H, W (got %lld, %lld, %lld)",
+                    (long long)z.d, (long long)z.h, (long long)z.w);
+    return CF_OK;
+}
+
+cf_status cf_pool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, void* P, uint8_t* idx,
+                        hipStream_t stream)
+{
+    cf_status st = check_pool(dtype, z);
+    if (st != CF_OK) return st;
+    if (!Z || !P || !idx) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: null pointer");
+    if (!al16(Z) || !al16(P) || !al16(idx)) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: pointers must be 16-byte aligned");
+    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: slope is NaN");
+    hipError_t e = dtype == CF_F32 ? launch_pool_fwd<float>((const float*)Z, (float*)P, idx, z, slope, stream)
+                                   : launch_pool_fwd<uint16_t>((const uint16_t*)Z, (uint16_t*)P, idx, z, slope, stream);
+    CF_TRY_HIP(e, "pool forward");
+    return CF_OK;
+}
+
+cf_status cf_pool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* P, const uint8_t* idx, float slope,
+                        void* dZ, hipStream_t stream)
+{
+    cf_status st = check_pool(dtype, z);
+    if (st != CF_OK) return st;
+    if (!dP || !P || !idx || !dZ) return fail(CF_ERR_INVALID, "cf_pool3d_bwd: null pointer");
+    if (!al16(dP) || !al16(P) || !al16(idx) || !al16(dZ))
+        return fail(CF_ERR_INVALID, "cf_pool3d_bwd: pointers must be 16-byte aligned");
+    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool3d_bwd: slope is NaN");
+    hipError_t e = dtype == CF_F32
+                       ? launch_pool_bwd<float>((const float*)dP, (const float*)P, idx, (float*)dZ, z, slope, stream)
+                       : launch_pool_bwd<uint16_t>((const uint16_t*)dP, (const uint16_t*)P, idx, (uint16_t*)dZ, z, slope,
+                                                   stream);
+    CF_TRY_HIP(e, "pool backward");
+    return CF_OK;
+}
+
+cf_status cf_lrelu(cf_dtype dtype, int64_t n, const void* x, const void* dy, float slope, void* out,
+                   hipStream_t stream)
+{
+    cf_status st = check_dtype(dtype);
+    if (st != CF_OK) return st;
+    if (n <= 0 || n > kMaxElems) return fail(CF_ERR_INVALID, "cf_lrelu: n out of range");
+    if (!x || !out) return fail(CF_ERR_INVALID, "cf_lrelu: null pointer");
+    if (!al16(x) || !al16(out) || (dy && !al16(dy))) return fail(CF_ERR_INVALID, "cf_lrelu: pointers must be 16-byte aligned");
+    hipError_t e = dtype == CF_F32
+                       ? launch_lrelu<float>((const float*)x, (const float*)dy, (float*)out, n, slope, stream)
+                       : launch_lrelu<uint16_t>((const uint16_t*)x, (const uint16_t*)dy, (uint16_t*)out, n, slope, stream);
+    CF_TRY_HIP(e, "leaky relu");
+    return CF_OK;
+}
+
+static cf_status check_dense(int32_t B, int32_t in, int32_t out)
+{
+    if (B <= 0 || in <= 0 || out <= 0) return fail(CF_ERR_INVALID, "dense: sizes must be positive");
+    if ((int64_t)in * out > ((int64_t)1 << 31) || (int64_t)B * in > ((int64_t)1 << 31))
+        return fail(CF_ERR_INVALID, "dense: sizes too large");
+    return CF_OK;
+}
+
+size_t cf_dense_workspace_size(int32_t B, int32_t in, int32_t out)
+{
+    if (check_dense(B, in, out) != CF_OK) return 0;
+    return up256(dense_fwd_part_bytes(B, in, out));
+}
+
+cf_status cf_dense_fwd(int32_t B, int32_t in, int32_t out, const float* X, const float* W, const float* bias,
+                       float slope, float* pre, float* Y, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_dense(B, in, out);
+    if (st != CF_OK) return st;
+    if (!X || !W || !pre || !Y) return fail(CF_ERR_INVALID, "cf_dense_fwd: null pointer");
+    const size_t need = up256(dense_fwd_part_bytes(B, in, out));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_dense_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_dense_fwd: workspace null or misaligned");
+    CF_TRY_HIP(launch_dense_fwd(B, in, out, X, nullptr, W, bias, slope, pre, Y, (float*)ws, stream), "dense forward");
+    return CF_OK;
+}
+
+cf_status cf_dense_bwd(int32_t B, int32_t in, int32_t out, const float* X, const float* W, const float* pre,
+                       const float* dY, float slope, float* dX, float* dW, float* db, hipStream_t stream)
+{
+    cf_status st = check_dense(B, in, out);
+    if (st != CF_OK) return st;
+    if (!X || !W || !pre || !dY || !dW || !db) return fail(CF_ERR_INVALID, "cf_dense_bwd: null pointer");
+    CF_TRY_HIP(launch_dense_bwd(B, in, out, X, nullptr, W, pre, dY, slope, dX, nullptr, dW, db, stream), "dense backward");
+    return CF_OK;
+}
+
+cf_status cf_mse(int32_t B, int32_t K, const float* yhat, const float* t, float* loss, float* dyhat,
+                 hipStream_t stream)
+{
+    if (B <= 0 || K <= 0 || (int64_t)B * K > (1 << 24)) return fail(CF_ERR_INVALID, "cf_mse: sizes out of range");
+    if (!yhat || !t || !loss) return fail(CF_ERR_INVALID, "cf_mse: null pointer");
+    CF_TRY_HIP(launch_mse(B, K, yhat, t, loss, dyhat, stream), "mse");
+    return CF_OK;
+}
+
+cf_status cf_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t stream)
+{
+    if (n <= 0 || n > kMaxElems) return fail(CF_ERR_INVALID, "cf_sgd: n out of range");
+    if (!W || !dW) return fail(CF_ERR_INVALID, "cf_sgd: null pointer");
+    CF_TRY_HIP(launch_sgd(n, lr, W, dW, stream), "sgd");
+    return CF_OK;
+}
+
+// ------------------------------------------------------------ training step
+namespace {
+
+struct LayerPlan {
+    cf_dims x;          // block input
+    int cout;
+    Fwd fwd;
+    Fwd dg;
+    Wg wg;
+    size_t wk_fwd, wk_dg, z, p, idx, dp, dw;   // offsets into the workspace
+};
+
+struct StepPlan {
+    int L;
+    LayerPlan layer[CF_MAX_BLOCKS];
+    int flat, d0, d1, d2;
+    size_t part;        // shared split-K buffer (conv fwd, dgrad, wgrad, dense)
+    size_t pre1, y1, pre2, y2, pre3, y3, dy3, dy2, dy1;
+    size_t dW1, db1, dW2, db2, dW3, db3;
+    size_t cast;        // bf16 DHWIO weight copy for direct bf16 fallbacks
+    size_t total;
+};
+
+cf_status check_model(const cf_model_desc* m, cf_dtype dt, int32_t B)
+{
+    cf_status st = check_dtype(dt);
+    if (st != CF_OK) return st;
+    if (!m) return fail(CF_ERR_INVALID, "model description is null");
+    if (B <= 0) return fail(CF_ERR_INVALID, "batch must be positive");
+    if (m->nblocks < 1 || m->nblocks > CF_MAX_BLOCKS) return fail(CF_ERR_INVALID, "nblocks must be 1..%d", CF_MAX_BLOCKS);
+    if (m->cin <= 0 || m->d <= 0 || m->h <= 0 || m->w <= 0) return fail(CF_ERR_INVALID, "input shape must be positive");
+    const int div = 1 << m->nblocks;
+    if (m->d % div || m->h % div || m->w % div)
+        return fail(CF_ERR_UNSUPPORTED, "input D, H, W must be divisible by 2^nblocks");
+    for (int l = 0; l < m->nblocks; ++l)
+        if (m->filters[l] <= 0 || m->filters[l] > 65536) return fail(CF_ERR_INVALID, "filters[%d] out of range", l);
+    for (int k = 0; k < 3; ++k)
+        if (m->dense[k] <= 0 || m->dense[k] > 65536) return fail(CF_ERR_INVALID, "dense[%d] out of range", k);
+    if (!(m->slope == m->slope)) return fail(CF_ERR_INVALID, "slope is NaN");
+    cf_dims x{B, m->d, m->h, m->w, m->cin};
+    if ((st = check_dims(x, "input")) != CF_OK) return st;
+    return CF_OK;
+}
+
+StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
+{
+    StepPlan P{};
+    P.L = m->nblocks;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += up256(bytes); return o; };
+    const size_t es = esize(dt);
+    size_t part = 0, cast = 0;
+    cf_dims x{B, m->d, m->h, m->w, m->cin};
+    for (int l = 0; l < P.L; ++l) {
+        LayerPlan& Lp = P.layer[l];
+        Lp.x = x;
+        Lp.cout = m->filters[l];
+        Lp.fwd = fwd_path(dt, x.c, Lp.cout);
+        Lp.dg = dgrad_path(dt, x.c, Lp.cout);
+        Lp.wg = wgrad_path(dt, x.c, Lp.cout);
+        const int64_t nvox = x.n * x.d * x.h * x.w;
+        const int64_t npool = nvox / 8;
+        Lp.wk_fwd = take(Lp.fwd == Fwd::Direct ? 0 : fwd_wk_bytes(Lp.fwd, x.c, Lp.cout));
+        Lp.wk_dg = take(l > 0 ? dgrad_wk_bytes(Lp.dg, dt, x.c, Lp.cout) : 0);
+        Lp.z = take((size_t)nvox * Lp.cout * es);
+        Lp.p = take((size_t)npool * Lp.cout * es);
+        Lp.idx = take((size_t)npool * Lp.cout);
+        Lp.dp = take((size_t)npool * Lp.cout * es);
+        Lp.dw = take((size_t)27 * x.c * Lp.cout * 4);
+        size_t pb = fwd_part_bytes(Lp.fwd, x, Lp.cout);
+        if (l > 0 && dgrad_part_bytes(Lp.dg, x, Lp.cout) > pb) pb = dgrad_part_bytes(Lp.dg, x, Lp.cout);
+        if (wgrad_part_bytes(Lp.wg, dt, x, Lp.cout) > pb) pb = wgrad_part_bytes(Lp.wg, dt, x, Lp.cout);
+        if (pb > part) part = pb;
+        if (dt == CF_BF16 && Lp.fwd == Fwd::Direct) {
+            const size_t c = (size_t)27 * x.c * Lp.cout * 2;
+            if (c > cast) cast = c;
+        }
+        x = cf_dims{B, x.d / 2, x.h / 2, x.w / 2, Lp.cout};
+    }
+    P.flat = (int)(x.d * x.h * x.w * x.c);
+    P.d0 = m->dense[0]; P.d1 = m->dense[1]; P.d2 = m->dense[2];
+    size_t dp = dense_fwd_part_bytes(B, P.flat, P.d0);
+    if (dense_fwd_part_bytes(B, P.d0, P.d1) > dp) dp = dense_fwd_part_bytes(B, P.d0, P.d1);
+    if (dense_fwd_part_bytes(B, P.d1, P.d2) > dp) dp = dense_fwd_part_bytes(B, P.d1, P.d2);
+    if (dp > part) part = dp;
+    P.part = take(part);
+    P.cast = take(cast);
+    const size_t f = 4;
+    P.pre1 = take((size_t)B * P.d0 * f); P.y1 = take((size_t)B * P.d0 * f);
+    P.pre2 = take((size_t)B * P.d1 * f); P.y2 = take((size_t)B * P.d1 * f);
+    P.pre3 = take((size_t)B * P.d2 * f); P.y3 = take((size_t)B * P.d2 * f);
+    P.dy3 = take((size_t)B * P.d2 * f); P.dy2 = take((size_t)B * P.d1 * f); P.dy1 = take((size_t)B * P.d0 * f);
+    P.dW1 = take((size_t)P.flat * P.d0 * f); P.db1 = take((size_t)P.d0 * f);
+    P.dW2 = take((size_t)P.d0 * P.d1 * f); P.db2 = take((size_t)P.d1 * f);
+    P.dW3 = take((size_t)P.d1 * P.d2 * f); P.db3 = take((size_t)P.d2 * f);
+    P.total = off;
+    return P;
+}
+
+__global__ void cast_bf16_kernel(const float* __restrict__ s, uint16_t* __restrict__ d, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) d[i] = f2bf(s[i]);
+}
+
+}  // namespace
+
+size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int32_t B)
+{
+    if (check_model(m, dtype, B) != CF_OK) return 0;
+    return plan_step(m, dtype, B).total;
+}
+
+cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const void* X, const float* targets,
+                        float* const* params, float lr, float* loss_out, float* pred_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream)
+{
+    cf_status st = check_model(m, dtype, B);
+    if (st != CF_OK) return st;
+    if (!X || !targets || !params || !loss_out) return fail(CF_ERR_INVALID, "cf_train_step: null pointer");
+    const int L = m->nblocks;
+    for (int i = 0; i < L + 6; ++i)
+        if (!params[i] || !al16(params[i])) return fail(CF_ERR_INVALID, "cf_train_step: params[%d] null or misaligned", i);
+    if (!al16(X)) return fail(CF_ERR_INVALID, "cf_train_step: X must be 16-byte aligned");
+    const StepPlan P = plan_step(m, dtype, B);
+    if (ws_bytes < P.total) return fail(CF_ERR_WORKSPACE, "cf_train_step: workspace %zu < %zu bytes", ws_bytes, P.total);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_train_step: workspace null or misaligned");
+    char* w = (char*)ws;
+    auto F = [&](size_t o) { return (float*)(w + o); };
+    float* part = F(P.part);
+    const float slope = m->slope;
+    const bool bf = dtype == CF_BF16;
+
+    // 1. weight copies for this step (bf16 rounding of the fp32 masters)
+    for (int l = 0; l < L; ++l) {
+        const LayerPlan& Lp = P.layer[l];
+        if (Lp.fwd != Fwd::Direct)
+            CF_TRY_HIP(prep_fwd(Lp.fwd, params[l], true, Lp.x.c, Lp.cout, w + Lp.wk_fwd, stream), "weight re-layout");
+        if (l > 0) {
+            if (Lp.dg == Fwd::Mfma) {
+                CF_TRY_HIP(prep_dgrad(Lp.dg, dtype, params[l], true, Lp.x.c, Lp.cout, w + Lp.wk_dg, stream),
+                           "weight re-layout");
+            } else if (bf) {
+                const int64_t n = (int64_t)27 * Lp.x.c * Lp.cout;
+                hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                                   params[l], (uint16_t*)(w + P.cast), n);
+                CF_TRY_HIP(hipGetLastError(), "weight cast");
+                CF_TRY_HIP(launch_wprep_direct_dgrad(w + P.cast, dtype, (int)Lp.x.c, Lp.cout, w + Lp.wk_dg, stream),
+                           "weight re-layout");
+            } else {
+                CF_TRY_HIP(launch_wprep_direct_dgrad(params[l], dtype, (int)Lp.x.c, Lp.cout, w + Lp.wk_dg, stream),
+                           "weight re-layout");
+            }
+        }
+    }
+
+    // 2. forward through the blocks
+    const void* a = X;
+    for (int l = 0; l < L; ++l) {
+        const LayerPlan& Lp = P.layer[l];
+        const void* wk = w + Lp.wk_fwd;
+        if (Lp.fwd == Fwd::Direct) {
+            if (bf) {
+                const int64_t n = (int64_t)27 * Lp.x.c * Lp.cout;
+                hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                                   params[l], (uint16_t*)(w + P.cast), n);
+                CF_TRY_HIP(hipGetLastError(), "weight cast");
+                wk = w + P.cast;
+            } else {
+                wk = params[l];
+            }
+        }
+        CF_TRY_HIP(run_fwd(Lp.fwd, dtype, Lp.x, a, wk, Lp.cout, w + Lp.z, part, stream), "conv3d forward");
+        const cf_dims z = with_c(Lp.x, Lp.cout);
+        hipError_t e = bf ? launch_pool_fwd<uint16_t>((const uint16_t*)(w + Lp.z), (uint16_t*)(w + Lp.p),
+                                                      (uint8_t*)(w + Lp.idx), z, slope, stream)
+                          : launch_pool_fwd<float>((const float*)(w + Lp.z), (float*)(w + Lp.p), (uint8_t*)(w + Lp.idx),
+                                                   z, slope, stream);
+        CF_TRY_HIP(e, "pool forward");
+        a = w + Lp.p;
+    }
+
+    // 3. dense head (the flattened NDHWC pooled volume is the dense input)
+    const LayerPlan& last = P.layer[L - 1];
+    const float* hX = bf ? nullptr : (const float*)(w + last.p);
+    const uint16_t* hXb = bf ? (const uint16_t*)(w + last.p) : nullptr;
+    const float* W1 = params[L], *b1 = params[L + 1], *W2 = params[L + 2], *b2 = params[L + 3], *W3 = params[L + 4],
+                *b3 = params[L + 5];
+    CF_TRY_HIP(launch_dense_fwd(B, P.flat, P.d0, hX, hXb, W1, b1, slope, F(P.pre1), F(P.y1), part, stream), "dense1");
+    CF_TRY_HIP(launch_dense_fwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, b2, slope, F(P.pre2), F(P.y2), part, stream), "dense2");
+    CF_TRY_HIP(launch_dense_fwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, b3, -1.f, F(P.pre3), F(P.y3), part, stream), "dense3");
+    CF_TRY_HIP(launch_mse(B, P.d2, F(P.y3), targets, loss_out, F(P.dy3), stream), "mse");
+    if (pred_out) CF_TRY_HIP(launch_copy_f32(F(P.y3), pred_out, (int64_t)B * P.d2, stream), "copy predictions");
+
+    // 4. dense backward
+    CF_TRY_HIP(launch_dense_bwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, F(P.pre3), F(P.dy3), -1.f, F(P.dy2), nullptr,
+                                F(P.dW3), F(P.db3), stream), "dense3 backward");
+    CF_TRY_HIP(launch_dense_bwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, F(P.pre2), F(P.dy2), slope, F(P.dy1), nullptr,
+                                F(P.dW2), F(P.db2), stream), "dense2 backward");
+    CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.pre1), F(P.dy1), slope,
+                                bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
+                                F(P.dW1), F(P.db1), stream), "dense1 backward");
+
+    // 5. conv blocks backward: pool backward -> weight gradient -> data gradient
+    for (int l = L - 1; l >= 0; --l) {
+        const LayerPlan& Lp = P.layer[l];
+        const cf_dims z = with_c(Lp.x, Lp.cout);
+        void* dz = w + Lp.z;    // the conv output buffer is reused for its gradient
+        hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
+                                                      (const uint8_t*)(w + Lp.idx), (uint16_t*)dz, z, slope, stream)
+                          : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
+                                                   (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
+        CF_TRY_HIP(e, "pool backward");
+        const void* xin = l == 0 ? X : (const void*)(w + P.layer[l - 1].p);
+        CF_TRY_HIP(run_wgrad(Lp.wg, dtype, Lp.x, xin, dz, Lp.cout, F(Lp.dw), part, stream), "conv3d backward-weight");
+        if (l > 0)
+            CF_TRY_HIP(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + P.layer[l - 1].dp, part, stream),
+                       "conv3d backward-data");
+    }
+
+    // 6. SGD on every master parameter
+    for (int l = 0; l < L; ++l)
+        CF_TRY_HIP(launch_sgd((int64_t)27 * P.layer[l].x.c * P.layer[l].cout, lr, params[l], F(P.layer[l].dw), stream), "sgd");
+    CF_TRY_HIP(launch_sgd((int64_t)P.flat * P.d0, lr, params[L], F(P.dW1), stream), "sgd");
+    CF_TRY_HIP(launch_sgd(P.d0, lr, params[L + 1], F(P.db1), stream), "sgd");
+    CF_TRY_HIP(launch_sgd((int64_t)P.d0 * P.d1, lr, params[L + 2], F(P.dW2), stream), "sgd");
+    CF_TRY_HIP(launch_sgd(P.d1, lr, params[L + 3], F(P.db2), stream), "sgd");
+    CF_TRY_HIP(launch_sgd((int64_t)P.d1 * P.d2, lr, params[L + 4], F(P.dW3), stream), "sgd");
+    CF_TRY_HIP(launch_sgd(P.d2, lr, params[L + 5], F(P.db3), stream), "sgd");
+    return CF_OK;
+}
+
+}  // extern "C"

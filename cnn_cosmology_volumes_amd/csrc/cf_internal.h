@@ -1,0 +1,126 @@
+// Internal declarations shared by the libcf translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "cf.h"
+
+namespace cf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;   // bfloat16 storage word
+
+#define CF_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+};
+
+// Spread consecutive logical block ids over the 8 XCDs so that neighbouring
+// tiles (which share halo data) run on the same XCD and share its L2.
+// Hardware dispatches block b to XCD (b % 8); logical id = xcd * per + b / 8.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
+    const uint32_t per = nblocks / 8u;
+    if (per == 0) return b;
+    const uint32_t full = per * 8u;
+    if (b >= full) return b;
+    return (b % 8u) * per + (b / 8u);
+}
+
+// ----------------------------------------------------------------- launchers
+// Every launcher enqueues on `s` and returns hipGetLastError() of the launch.
+
+// Weight re-layouts (fp32 or bf16 DHWIO source -> bf16 kernel layouts).
+// fwd:   Wk[t][co][ci]            (co padded to copad with zeros)
+// dgrad: Wk[t'][ci][co] = W[26-t'][ci][co] (ci padded to cipad with zeros)
+// c4:    Wk[co][128] with k = t*4 + ci, zero for t >= 27 (Cin == 4 only)
+hipError_t launch_wprep_fwd(const void* W, bool w_is_f32, int cin, int cout, int copad, uint16_t* Wk, hipStream_t s);
+hipError_t launch_wprep_dgrad(const void* W, bool w_is_f32, int cin, int cout, int cipad, uint16_t* Wk, hipStream_t s);
+hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, uint16_t* Wk, hipStream_t s);
+// fp32 dgrad weights for the direct path: Wt[t'][co][ci] = W[26-t'][ci][co] (float or bf16 source kept as-is)
+hipError_t launch_wprep_direct_dgrad(const void* W, cf_dtype dt, int cin, int cout, void* Wt, hipStream_t s);
+
+// MFMA implicit-GEMM 3^3 conv (forward orientation), in-channels % 32 == 0.
+// Used for the forward pass (Wk from wprep_fwd) and backward-data (Wk from
+// wprep_dgrad, in/out channels swapped).
+struct ConvPlan {
+    int cfg;          // tile configuration id
+    int bm;           // out-channels per block
+    int splits;       // split over in-channel chunks (fp32 partials when > 1)
+    size_t part_bytes;
+};
+ConvPlan plan_conv_mfma(const cf_dims& x, int cout);
+hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y,
+                            float* part, const cf_dims& x, int cout, int coutpad, hipStream_t s);
+
+// Layer-1 forward (Cin == 4) on MFMA, K = 27*4 padded to 128.
+hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, const cf_dims& x,
+                              int cout, int copad, hipStream_t s);
+
+// Backward-weight on MFMA.  Partial sums per voxel split into `part`
+// ([splits][27*cin*cout] fp32), then a fixed-order reduction into dW.
+struct WgradPlan {
+    int kind;         // 0: cin % 32 == 0; 1: cin == 4
+    int splits;
+    int64_t vox_per_split;
+    size_t part_bytes;
+};
+WgradPlan plan_wgrad(const cf_dims& x, int cout);
+hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, float* part, float* dW,
+                        const cf_dims& x, int cout, hipStream_t s);
+
+// Direct (non-MFMA) conv kernels for fp32 and for shapes outside the MFMA
+// paths.  T = float or uint16_t (bf16).  Wt layout is DHWIO for the forward;
+// for backward-data the caller passes the flipped/transposed weights.
+template <typename T>
+hipError_t launch_conv_direct(const T* X, const T* W, T* Y, const cf_dims& x, int cout, hipStream_t s);
+template <typename T>
+size_t wgrad_direct_part_bytes(const cf_dims& x, int cout);
+template <typename T>
+hipError_t launch_wgrad_direct(const T* X, const T* dY, float* part, float* dW, const cf_dims& x, int cout,
+                               hipStream_t s);
+
+// Pooling / activations.
+template <typename T>
+hipError_t launch_pool_fwd(const T* Z, T* P, uint8_t* idx, const cf_dims& z, float slope, hipStream_t s);
+template <typename T>
+hipError_t launch_pool_bwd(const T* dP, const T* P, const uint8_t* idx, T* dZ, const cf_dims& z, float slope,
+                           hipStream_t s);
+template <typename T>
+hipError_t launch_lrelu(const T* x, const T* dy, T* out, int64_t n, float slope, hipStream_t s);
+
+// Dense head and loss (fp32).  Xb: optional bf16 input (used instead of X).
+size_t dense_fwd_part_bytes(int B, int in, int out);
+hipError_t launch_dense_fwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
+                            const float* b, float slope, float* pre, float* Y, float* part, hipStream_t s);
+hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
+                            const float* pre, const float* dY, float slope, float* dX, uint16_t* dXb,
+                            float* dW, float* db, hipStream_t s);
+hipError_t launch_mse(int B, int K, const float* yhat, const float* t, float* loss, float* dyhat, hipStream_t s);
+hipError_t launch_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+}  // namespace cf

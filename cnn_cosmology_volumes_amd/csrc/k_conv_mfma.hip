@@ -1,0 +1,240 @@
+// Implicit-GEMM 3^3 convolution on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+//
+// Computes Y[v, co] = sum_{tap, ci} X[v + off(tap), ci] * Wk[tap][co][ci] for a
+// stride-1, pad-1 3^3 cross-correlation on NDHWC tensors (the forward
+// convolution of Oyama et al., Sec. IV / Table I: "same" padding, stride 1, no
+// bias).  With Wk prepared as the tap-flipped, channel-swapped weights the same
+// kernel computes the backward-data pass (the adjoint of the forward operator
+// for stride 1 and pad 1 is a pad-1 correlation with W[2-kd,2-kh,2-kw]^T).
+//
+// GEMM view: rows = output channels (MFMA A operand = weights), columns =
+// output voxels (MFMA B operand = input halo), K = 27 taps x in-channels.
+//  - A block owns a TD x TH x TW output tile of one sample and BM output
+//    channels.  For every 32-channel input chunk it stages the
+//    (TD+2)(TH+2)(TW+2) halo of the input in LDS once (80-byte voxel stride:
+//    64 bytes of data + 16 bytes of padding, which keeps the 16-byte
+//    per-lane reads of 16 consecutive voxels on distinct LDS banks) and then
+//    walks the 27 taps; a tap only shifts the LDS row index, so every B
+//    fragment is one aligned 16-byte LDS read at a compile-time offset.
+//  - A fragments (8 consecutive in-channels of one output channel) are
+//    16-byte global loads from the [tap][co][ci] weight copy, which is small
+//    and stays L2/L1 resident.
+//  - Accumulation is fp32; the epilogue rounds to bf16 (or writes fp32
+//    partial sums when the in-channel reduction is split across blocks).
+#include "cf_internal.h"
+
+namespace cf {
+
+namespace {
+
+constexpr int LDS_STRIDE = 40;   // bf16 per halo voxel: 32 data + 8 padding
+
+template <int BM, int WN, int TD, int TH, int TW>
+struct Tile {
+    static constexpr int VT = TD * TH * TW;
+    static constexpr int NW = VT / WN;
+    static constexpr int NT = NW * 64;
+    static constexpr int HD = TD + 2, HH = TH + 2, HW = TW + 2;
+    static constexpr int HV = HD * HH * HW;
+    static constexpr int MI = BM / 16;
+    static constexpr int NJ = WN / 16;
+    static_assert(VT % WN == 0 && (NW == 4 || NW == 8), "tile");
+    static_assert(BM % 16 == 0 && WN % 16 == 0, "frag");
+};
+
+template <int BM, int WN, int TD, int TH, int TW>
+__global__ __launch_bounds__((Tile<BM, WN, TD, TH, TW>::NT))
+void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
+                        uint16_t* __restrict__ Y, float* __restrict__ part,
+                        int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
+                        int tD, int tH, int tW, int chunks_per_split)
+{
+    using T = Tile<BM, WN, TD, TH, TW>;
+    __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LDS_STRIDE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int tw_ = tile % tW; tile /= tW;
+    const int th_ = tile % tH; tile /= tH;
+    const int td_ = tile % tD;
+    const int n = tile / tD;
+    const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
+    const int co_base = blockIdx.y * BM;
+    const int nchunks = Cin >> 5;
+    const int c_begin = blockIdx.z * chunks_per_split;
+    const int c_end = min(c_begin + chunks_per_split, nchunks);
+
+    // Per-lane LDS offsets (in bf16 units, tap 0) of the B fragments.
+    int hb[T::NJ];
+#pragma unroll
+    for (int j = 0; j < T::NJ; ++j) {
+        const int v = wave * WN + 16 * j + l16;
+        const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
+        hb[j] = ((td * T::HH + th) * T::HW + tw) * LDS_STRIDE + 8 * lg;
+    }
+
+    f32x4 acc[T::MI][T::NJ];
+#pragma unroll
+    for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < T::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t plane = (int64_t)H * W;
+    for (int c = c_begin; c < c_end; ++c) {
+        __syncthreads();
+        // Stage the input halo of this 32-channel chunk (zero outside the volume).
+        for (int e = threadIdx.x; e < T::HV * 4; e += T::NT) {
+            const int q = e & 3, hv = e >> 2;
+            const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
+            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H && (unsigned)gw < (unsigned)W) {
+                const int64_t vox = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
+                val = *reinterpret_cast<const uint4*>(X + vox * Cin + c * 32 + q * 8);
+            }
+            *reinterpret_cast<uint4*>(halo + hv * LDS_STRIDE + q * 8) = val;
+        }
+        __syncthreads();
+
+        const uint16_t* wrow = Wk + ((int64_t)(co_base + l16) * Cin + c * 32 + 8 * lg);
+        const int64_t tap_stride = (int64_t)CoutPad * Cin;
+#pragma unroll
+        for (int tap = 0; tap < 27; ++tap) {
+            const int kd = tap / 9, kh = (tap / 3) % 3, kw = tap % 3;
+            const int toff = ((kd * T::HH + kh) * T::HW + kw) * LDS_STRIDE;
+            bf16x8 a[T::MI], b[T::NJ];
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(wrow + tap * tap_stride + (int64_t)16 * i * Cin);
+#pragma unroll
+            for (int j = 0; j < T::NJ; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < T::NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // Epilogue: lane holds 4 consecutive output channels of one voxel per fragment.
+    const int64_t nvox = (int64_t)N * D * plane;
+#pragma unroll
+    for (int j = 0; j < T::NJ; ++j) {
+        const int v = wave * WN + 16 * j + l16;
+        const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
+        const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
+        if (gd >= D || gh >= H || gw >= W) continue;
+        const int64_t gv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
+#pragma unroll
+        for (int i = 0; i < T::MI; ++i) {
+            const int co = co_base + 16 * i + 4 * lg;
+            if (co >= Cout) continue;
+            const f32x4 r = acc[i][j];
+            if (part) {
+                float* dst = part + ((int64_t)blockIdx.z * nvox + gv) * Cout + co;
+                *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+            } else {
+                uint2 pk = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+                *reinterpret_cast<uint2*>(Y + gv * Cout + co) = pk;
+            }
+        }
+    }
+}
+
+// Sum the split partials in split order and round to bf16.
+__global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __restrict__ Y, int64_t n4,
+                                  int splits)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 s = reinterpret_cast<const float4*>(part)[i];
+        for (int k = 1; k < splits; ++k) {
+            const float4 p = reinterpret_cast<const float4*>(part)[(int64_t)k * n4 + i];
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        reinterpret_cast<uint2*>(Y)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    }
+}
+
+struct CfgInfo { int bm, wn, td, th, tw; };
+constexpr CfgInfo kCfgs[] = {
+    {128, 64, 4, 4, 16},   // 0
+    {128, 64, 4, 8, 8},    // 1
+    {64, 128, 4, 8, 16},   // 2
+    {64, 128, 8, 8, 8},    // 3
+    {32, 128, 4, 8, 16},   // 4
+    {32, 128, 8, 8, 8},    // 5
+    {16, 128, 4, 8, 16},   // 6
+    {16, 128, 8, 8, 8},    // 7
+};
+
+template <int BM, int WN, int TD, int TH, int TW>
+hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x,
+                      int cout, int coutpad, int splits, hipStream_t s)
+{
+    using T = Tile<BM, WN, TD, TH, TW>;
+    const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
+    const int nchunks = (int)(x.c / 32);
+    const int cps = (nchunks + splits - 1) / splits;
+    dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
+    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WN, TD, TH, TW>), grid, dim3(T::NT), 0, s, X, Wk, Y,
+                       splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
+                       coutpad, tD, tH, tW, cps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
+{
+    ConvPlan p{};
+    const bool narrow = x.w < 16;
+    if (cout > 64) p.cfg = narrow ? 1 : 0;
+    else if (cout > 32) p.cfg = narrow ? 3 : 2;
+    else if (cout > 16) p.cfg = narrow ? 5 : 4;
+    else p.cfg = narrow ? 7 : 6;
+    const CfgInfo& c = kCfgs[p.cfg];
+    p.bm = c.bm;
+    const int64_t tiles = x.n * ((x.d + c.td - 1) / c.td) * ((x.h + c.th - 1) / c.th) * ((x.w + c.tw - 1) / c.tw);
+    const int64_t blocks = tiles * ((cout + c.bm - 1) / c.bm);
+    const int nchunks = (int)(x.c / 32);
+    int splits = 1;
+    if (blocks < 512 && nchunks > 1) {
+        splits = (int)((512 + blocks - 1) / blocks);
+        if (splits > nchunks) splits = nchunks;
+        // equalise chunk counts per split
+        const int cps = (nchunks + splits - 1) / splits;
+        splits = (nchunks + cps - 1) / cps;
+    }
+    p.splits = splits;
+    p.part_bytes = splits > 1 ? (size_t)splits * (size_t)(x.n * x.d * x.h * x.w) * (size_t)cout * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part,
+                            const cf_dims& x, int cout, int coutpad, hipStream_t s)
+{
+    hipError_t e;
+    switch (p.cfg) {
+    case 0: e = launch_cfg<128, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 1: e = launch_cfg<128, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 2: e = launch_cfg<64, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 3: e = launch_cfg<64, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 4: e = launch_cfg<32, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 5: e = launch_cfg<32, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 6: e = launch_cfg<16, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    default: e = launch_cfg<16, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    }
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(split_reduce_bf16, dim3((unsigned)blocks), dim3(256), 0, s, part, Y, n4, p.splits);
+    return hipGetLastError();
+}
+
+}  // namespace cf

@@ -1,0 +1,223 @@
+/*
+ * cf.h -- C ABI of libcf.so: the CosmoFlow-style 3D-CNN training step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The network is a stack of blocks [3^3 convolution, zero "same" padding,
+ * stride 1, no bias -> leaky ReLU -> 2^3 max pool, stride 2] followed by three
+ * fully connected layers (leaky ReLU on all but the last), a mean-squared
+ * error loss and an SGD update.  Sources for each operation are cited at its
+ * declaration:
+ *   [CF]  Mathuriya et al., "CosmoFlow: Using Deep Learning to Learn the
+ *         Universe at Scale" (arXiv 1808.04728), Sec. III-A (network), III-B
+ *         (optimizer), III-C (single-node conv / pooling primitives).
+ *   [OY]  Oyama et al., "The Case for Strong Scaling in Deep Learning:
+ *         Training Large 3D CNNs with Hybrid Parallelism" (arXiv 2007.12856),
+ *         Sec. II-A (mini-batch SGD equation), Sec. IV and Table I (extended
+ *         network: "same" padding, stride-1 convs, stride-2 pools, no conv
+ *         bias, leaky ReLU except the last layer, MSE loss).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - Tensors are packed row-major.  Activations are NDHWC (channels
+ *    innermost).  Conv weights are DHWIO: [3][3][3][Cin][Cout].  Dense
+ *    weights are [in][out], biases [out].
+ *  - Data types: CF_F32 = IEEE fp32; CF_BF16 = bfloat16 stored as 16-bit
+ *    words.  Matrix work accumulates in fp32; bf16 outputs are rounded to
+ *    nearest even.  Weight gradients, master weights and the dense head are
+ *    always fp32.
+ *  - Every pointer argument is a DEVICE pointer unless stated otherwise and
+ *    must be 16-byte aligned.  The caller owns every buffer; the library
+ *    allocates no device memory and keeps no mutable global state.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *    synchronises.  Outputs are overwritten, never accumulated into.
+ *  - Arguments are validated before any GPU work is enqueued.  Failures
+ *    return a negative cf_status and enqueue nothing; cf_last_error() then
+ *    returns a thread-local message.  No call aborts or throws.
+ *  - Workspaces are caller-provided device scratch of at least the size the
+ *    matching *_workspace_size() call returns (CF_ERR_WORKSPACE otherwise).
+ *    Their contents on entry do not matter; they must not alias any other
+ *    argument, and concurrent calls must use distinct workspaces.
+ */
+#ifndef CF_H_
+#define CF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CF_ABI_VERSION 1
+#define CF_MAX_BLOCKS 8
+
+typedef enum {
+    CF_OK = 0,
+    CF_ERR_INVALID = -1,      /* null pointer, non-positive size, misalignment, bad enum */
+    CF_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. k != 3) */
+    CF_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the required workspace */
+    CF_ERR_HIP = -4           /* a HIP launch failed; see cf_last_error() */
+} cf_status;
+
+typedef enum { CF_F32 = 0, CF_BF16 = 1 } cf_dtype;
+
+/* Packed NDHWC tensor shape. */
+typedef struct { int64_t n, d, h, w, c; } cf_dims;
+
+/* Convolution geometry.  This build supports k = 3, stride = 1, pad = 1
+ * (the "same" stride-1 convolution of [OY] Sec. IV); anything else returns
+ * CF_ERR_UNSUPPORTED. */
+typedef struct { int32_t k, stride, pad; } cf_conv;
+
+/* Which pass a conv workspace is sized for. */
+typedef enum { CF_CONV_FWD = 0, CF_CONV_BWD_DATA = 1, CF_CONV_BWD_WEIGHT = 2 } cf_conv_pass;
+
+/* Network description for cf_train_step: `nblocks` blocks with output
+ * channels filters[0..nblocks-1] applied to a cin x d x h x w input (each of
+ * d, h, w divisible by 2^nblocks), then dense layers of widths dense[0],
+ * dense[1], dense[2] (the last has no activation), leaky-ReLU slope `slope`. */
+typedef struct {
+    int32_t nblocks;
+    int32_t cin;
+    int32_t d, h, w;
+    int32_t filters[CF_MAX_BLOCKS];
+    int32_t dense[3];
+    float slope;
+} cf_model_desc;
+
+/* ---------------------------------------------------------------- conv3d */
+
+/* Bytes of workspace the given conv pass needs (0 is possible).  `x` is the
+ * shape of the forward input X (x.c = Cin); `cout` the forward output
+ * channels.  Returns 0 also for invalid arguments (the call then fails). */
+size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv conv,
+                                cf_conv_pass pass);
+
+/* Forward 3D convolution ([CF] Sec. III-C; [OY] Sec. IV, Table I):
+ *   Y[n,d,h,w,co] = sum_{kd,kh,kw in 0..2} sum_ci X[n,d+kd-1,h+kh-1,w+kw-1,ci]
+ *                                                * W[kd,kh,kw,ci,co]
+ * with X read as zero outside the volume.
+ *   X [x.n, x.d, x.h, x.w, x.c]  (dtype)      input
+ *   W [3,3,3, x.c, cout]         (dtype)      weights, DHWIO
+ *   Y [x.n, x.d, x.h, x.w, cout] (dtype)      output, overwritten */
+cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout,
+                        cf_conv conv, void* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward-data of the forward convolution ([CF] Sec. III-C, the separate
+ * backward-data operator): the adjoint with respect to X,
+ *   dX[n,d,h,w,ci] = sum_taps sum_co dY[n,d-kd+1,h-kh+1,w-kw+1,co] * W[kd,kh,kw,ci,co]
+ *   dY [x.n, x.d, x.h, x.w, cout] (dtype)     upstream gradient
+ *   W  [3,3,3, x.c, cout]         (dtype)     forward weights, DHWIO
+ *   dX [x.n, x.d, x.h, x.w, x.c]  (dtype)     output, overwritten */
+cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const void* W, int32_t cout,
+                             cf_conv conv, void* dX, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward-weight of the forward convolution ([CF] Sec. III-C, the separate
+ * backward-weight operator): the adjoint with respect to W,
+ *   dW[kd,kh,kw,ci,co] = sum_{n,d,h,w} X[n,d+kd-1,h+kh-1,w+kw-1,ci] * dY[n,d,h,w,co]
+ *   X  [x.n, x.d, x.h, x.w, x.c]  (dtype)     forward input
+ *   dY [x.n, x.d, x.h, x.w, cout] (dtype)     upstream gradient
+ *   dW [3,3,3, x.c, cout]         (fp32)      output, overwritten
+ * The reduction over voxels is split into fixed partial sums that are added
+ * in a fixed order: results are bitwise reproducible run to run. */
+cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
+                               cf_conv conv, float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ leaky ReLU + max pooling */
+
+/* Leaky ReLU followed by 2^3 max pooling with stride 2 ([CF] Sec. III-A
+ * leaky ReLU on conv layers; 2^3 stride-2 pooling as in [OY] Table I; max
+ * rather than average pooling):
+ *   P[n,i,j,k,c] = max_{a,b,e in {0,1}} lrelu(Z[n,2i+a,2j+b,2k+e,c])
+ *   idx[n,i,j,k,c] = a*4 + b*2 + e of the first strict maximum in (a,b,e)
+ *                    lexicographic order
+ * lrelu(z) = z if z > 0 else slope*z; slope = 1 gives plain max pooling.
+ *   Z   [z.n, z.d, z.h, z.w, z.c]         (dtype)  z.d, z.h, z.w even
+ *   P   [z.n, z.d/2, z.h/2, z.w/2, z.c]   (dtype)  output
+ *   idx same shape as P                   (uint8)  output */
+cf_status cf_pool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, void* P,
+                        uint8_t* idx, hipStream_t stream);
+
+/* Backward of cf_pool3d_fwd: each pooled gradient goes to the window
+ * position idx, scaled by the leaky-ReLU derivative there (1 if P > 0, slope
+ * otherwise); the other seven positions of every window receive zero.
+ *   dP, P [z.n, z.d/2, z.h/2, z.w/2, z.c] (dtype); idx (uint8) same shape
+ *   dZ    [z.n, z.d, z.h, z.w, z.c]       (dtype)  output, fully overwritten */
+cf_status cf_pool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* P,
+                        const uint8_t* idx, float slope, void* dZ, hipStream_t stream);
+
+/* Elementwise leaky ReLU ([CF] Sec. III-A).  dy == NULL: out = lrelu(x).
+ * Otherwise out = dy * (x > 0 ? 1 : slope) (the backward).  n elements of
+ * dtype each. */
+cf_status cf_lrelu(cf_dtype dtype, int64_t n, const void* x, const void* dy, float slope,
+                   void* out, hipStream_t stream);
+
+/* ------------------------------------------------------------ dense head */
+
+/* Workspace bytes for cf_dense_fwd (partial sums of the split reduction). */
+size_t cf_dense_workspace_size(int32_t B, int32_t in, int32_t out);
+
+/* Fully connected layer with bias ([CF] Sec. III-A; [OY] Table I fc layers):
+ *   pre[b,o] = sum_i X[b,i] * W[i,o] + bias[o];  Y = lrelu(pre) if slope >= 0
+ *   else Y = pre (linear last layer).  All fp32.  bias may be NULL (zero).
+ *   X [B,in], W [in,out], bias [out], pre [B,out], Y [B,out].
+ * The reduction over `in` is split in fixed 256-row pieces summed in order. */
+cf_status cf_dense_fwd(int32_t B, int32_t in, int32_t out, const float* X, const float* W,
+                       const float* bias, float slope, float* pre, float* Y, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Backward of cf_dense_fwd (chain rule):
+ *   dpre = dY * lrelu'(pre)  (dY when slope < 0)
+ *   dW[i,o] = sum_b X[b,i] dpre[b,o];  db[o] = sum_b dpre[b,o];
+ *   dX[b,i] = sum_o dpre[b,o] W[i,o]   (skipped when dX is NULL). */
+cf_status cf_dense_bwd(int32_t B, int32_t in, int32_t out, const float* X, const float* W,
+                       const float* pre, const float* dY, float slope, float* dX, float* dW,
+                       float* db, hipStream_t stream);
+
+/* Mean squared error ([OY] Sec. IV) and its gradient, fp32:
+ *   loss = (1/(B*K)) sum (yhat - t)^2 ;  dyhat = 2 (yhat - t) / (B*K).
+ *   yhat, t, dyhat [B,K]; loss: one device float.  dyhat may be NULL. */
+cf_status cf_mse(int32_t B, int32_t K, const float* yhat, const float* t, float* loss,
+                 float* dyhat, hipStream_t stream);
+
+/* SGD update W <- W - lr * dW on n fp32 values ([OY] Sec. II-A). */
+cf_status cf_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t stream);
+
+/* --------------------------------------------------------- training step */
+
+/* Workspace bytes for cf_train_step with this network, dtype and batch. */
+size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int32_t B);
+
+/* One full training step ([CF] Sec. III; [OY] Sec. II-A, IV): forward through
+ * every block and the dense head, MSE against `targets`, backward, and one
+ * SGD update of every parameter with learning rate `lr`.
+ *   m        host pointer to the network description
+ *   dtype    CF_BF16: conv operands and activations in bf16 (weights are
+ *            rounded from the fp32 masters at the start of the step); CF_F32:
+ *            fp32 throughout
+ *   X        [B, m->d, m->h, m->w, m->cin] (dtype)
+ *   targets  [B, m->dense[2]] fp32
+ *   params   HOST array of DEVICE pointers to the fp32 master parameters, in
+ *            order: conv W_1..W_nblocks (DHWIO), then dense W1, b1, W2, b2,
+ *            W3, b3.  Updated in place.
+ *   loss_out one device float: the loss of this step (before the update)
+ *   pred_out [B, m->dense[2]] fp32 predictions of this step, or NULL
+ * Layer-1 backward-data is not computed (the input needs no gradient). */
+cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const void* X,
+                        const float* targets, float* const* params, float lr, float* loss_out,
+                        float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- status */
+
+/* Static description of a status code. */
+const char* cf_status_string(cf_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* cf_last_error(void);
+/* CF_ABI_VERSION of the built library. */
+int32_t cf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CF_H_ */

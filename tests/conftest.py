@@ -28,3 +28,12 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name every GPU case on stderr (flushed) before it touches the device."""
+    if "gpu" in request.node.keywords:
+        sys.stderr.write("\n[gpu-case] %s\n" % request.node.nodeid)
+        sys.stderr.flush()
+    yield

@@ -1,0 +1,262 @@
+"""GPU parity of every libcf entry point against the fp64 oracle at sizes the
+oracle finishes in seconds; shapes span several kernel tiles and end in a
+ragged tail in every spatial dimension.  Inputs come from the seeded
+generators in ``synthdata``; the oracle sees the same values (bf16 inputs are
+exact in fp64) and never any output of the HIP path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthdata as sd
+from cnn_cosmology_volumes_amd import cf
+from gpu_util import (TOL_BF16, TOL_F32, bf16_elementwise_ok, host64, rel_err, to_dev)
+
+pytestmark = pytest.mark.gpu
+BF, F32 = torch.bfloat16, torch.float32
+SLOPE = 0.3
+
+
+def act(rng, shape, dtype):
+    """Synthetic activations on the dtype's grid."""
+    return sd.normal(rng, shape, bf16=(dtype == BF))
+
+
+def weights(rng, cin, cout, dtype):
+    w = sd.he_normal_conv(rng, cin, cout)
+    return sd.bf16_round_f32(w) if dtype == BF else w
+
+
+# (N, D, H, W, Cin, Cout): ragged against the (4,8,16)/(4,4,16)/(8,8,8) tiles
+CONV_CASES = [
+    (2, 5, 9, 19, 32, 64),     # MFMA, BM 64, wide tiles
+    (1, 6, 10, 7, 64, 128),    # MFMA, BM 128, narrow tiles, 2 in-channel chunks
+    (1, 9, 5, 18, 32, 32),     # MFMA, BM 32
+    (2, 7, 6, 17, 32, 48),     # MFMA, partial out-channel block
+    (1, 8, 8, 8, 256, 256),    # MFMA, split over in-channel chunks
+    (1, 3, 4, 5, 32, 4),       # MFMA, BM 16 with 4 valid rows
+    (2, 5, 9, 21, 4, 32),      # Cin = 4 layer-1 kernel
+    (1, 6, 11, 17, 4, 16),     # Cin = 4, 16 outputs
+    (1, 4, 5, 6, 3, 5),        # direct bf16 fallback
+    (1, 1, 1, 1, 32, 32),      # single voxel
+]
+
+
+@pytest.mark.parametrize("shape", CONV_CASES)
+def test_conv3d_fwd_bf16(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(hash(shape) % 2**32)
+    x = act(rng, (N, D, H, W, Ci), BF)
+    w = weights(rng, Ci, Co, BF)
+    y = cf.cf_conv3d_fwd(to_dev(x, BF), to_dev(w, BF))
+    torch.cuda.synchronize()
+    o = oracle.conv3d_fwd(x, w)
+    g = host64(y)
+    assert rel_err(g, o) <= TOL_BF16
+    assert bf16_elementwise_ok(g, o) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 32, 32, 4, 16), (2, 5, 7, 9, 3, 5), (1, 6, 5, 17, 32, 8)])
+def test_conv3d_fwd_f32(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(11)
+    x = sd.lognormal_field_input(rng, (N, D, H, W), Ci)
+    w = sd.he_normal_conv(rng, Ci, Co)
+    y = cf.cf_conv3d_fwd(to_dev(x, F32), to_dev(w, F32))
+    torch.cuda.synchronize()
+    assert rel_err(host64(y), oracle.conv3d_fwd(x, w)) <= TOL_F32
+
+
+def test_conv3d_fwd_delta_kernel_is_bitwise_identity():
+    rng = np.random.default_rng(5)
+    x = act(rng, (2, 5, 9, 19, 32), BF)
+    w = np.zeros((3, 3, 3, 32, 32), np.float32)
+    for c in range(32):
+        w[1, 1, 1, c, c] = 1.0
+    y = cf.cf_conv3d_fwd(to_dev(x, BF), to_dev(w, BF))
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(y), x.astype(np.float64))
+
+
+@pytest.mark.parametrize("shape", [c for c in CONV_CASES if c[4] % 4 == 0 or c[4] == 3])
+def test_conv3d_bwd_data_bf16(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(hash(shape) % 2**32 + 1)
+    dy = act(rng, (N, D, H, W, Co), BF)
+    w = weights(rng, Ci, Co, BF)
+    dx = cf.cf_conv3d_bwd_data(to_dev(dy, BF), to_dev(w, BF))
+    torch.cuda.synchronize()
+    o = oracle.conv3d_bwd_data(dy, w)
+    g = host64(dx)
+    assert rel_err(g, o) <= TOL_BF16
+    assert bf16_elementwise_ok(g, o) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 9, 7, 11, 4, 16), (2, 5, 6, 7, 3, 5)])
+def test_conv3d_bwd_data_f32(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(12)
+    dy = sd.normal(rng, (N, D, H, W, Co), bf16=False)
+    w = sd.he_normal_conv(rng, Ci, Co)
+    dx = cf.cf_conv3d_bwd_data(to_dev(dy, F32), to_dev(w, F32))
+    torch.cuda.synchronize()
+    assert rel_err(host64(dx), oracle.conv3d_bwd_data(dy, w)) <= TOL_F32
+
+
+WGRAD_CASES = [
+    (2, 5, 9, 19, 32, 64),
+    (1, 6, 10, 7, 64, 32),
+    (1, 8, 8, 8, 256, 256),
+    (2, 7, 6, 21, 4, 32),     # layer-1 kernel
+    (1, 4, 5, 6, 3, 5),       # direct fallback
+    (1, 1, 1, 1, 32, 32),
+]
+
+
+@pytest.mark.parametrize("shape", WGRAD_CASES)
+def test_conv3d_bwd_weight_bf16(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(hash(shape) % 2**32 + 2)
+    x = act(rng, (N, D, H, W, Ci), BF)
+    dy = act(rng, (N, D, H, W, Co), BF)
+    dw = cf.cf_conv3d_bwd_weight(to_dev(x, BF), to_dev(dy, BF))
+    torch.cuda.synchronize()
+    o = oracle.conv3d_bwd_weight(x, dy)
+    # bf16 inputs are exact; only fp32 accumulation differs from the oracle
+    assert rel_err(host64(dw), o) <= 1e-4
+
+
+@pytest.mark.parametrize("shape", [(1, 9, 7, 11, 4, 16), (2, 5, 6, 7, 3, 5)])
+def test_conv3d_bwd_weight_f32(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(13)
+    x = sd.normal(rng, (N, D, H, W, Ci), bf16=False)
+    dy = sd.normal(rng, (N, D, H, W, Co), bf16=False)
+    dw = cf.cf_conv3d_bwd_weight(to_dev(x, F32), to_dev(dy, F32))
+    torch.cuda.synchronize()
+    assert rel_err(host64(dw), oracle.conv3d_bwd_weight(x, dy)) <= TOL_F32
+
+
+def test_conv3d_bwd_weight_deterministic():
+    rng = np.random.default_rng(3)
+    x = to_dev(act(rng, (2, 8, 12, 20, 32), BF), BF)
+    dy = to_dev(act(rng, (2, 8, 12, 20, 64), BF), BF)
+    a = cf.cf_conv3d_bwd_weight(x, dy)
+    b = cf.cf_conv3d_bwd_weight(x, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- pooling
+POOL_CASES = [(2, 6, 10, 18, 32), (1, 4, 2, 8, 64), (1, 2, 4, 6, 5), (3, 2, 2, 2, 16)]
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("shape", POOL_CASES)
+def test_pool3d_fwd_bwd(shape, dtype):
+    rng = np.random.default_rng(sum(shape))
+    z = act(rng, shape, dtype)
+    Np = (shape[0], shape[1] // 2, shape[2] // 2, shape[3] // 2, shape[4])
+    dp = act(rng, Np, dtype)
+    zt = to_dev(z, dtype)
+    P, idx = cf.cf_pool3d_fwd(zt, SLOPE)
+    dZ = cf.cf_pool3d_bwd(to_dev(dp, dtype), P, idx, SLOPE)
+    torch.cuda.synchronize()
+    po, io = oracle.lrelu_maxpool_fwd(z, SLOPE)
+    # the argmax is decided on identical stored values on both sides: exact
+    assert np.array_equal(idx.cpu().numpy(), io)
+    ulp = 2.0 ** -8 if dtype == BF else 2.0 ** -23
+    g = host64(P)
+    assert np.all(np.abs(g - po) <= ulp * np.abs(po))
+    # backward from the oracle's own pooled values and indices
+    dzo = oracle.maxpool_lrelu_bwd(dp, po, io, SLOPE)
+    gz = host64(dZ)
+    assert np.all(np.abs(gz - dzo) <= ulp * np.abs(dzo))
+    assert np.count_nonzero(gz) == np.count_nonzero(dzo)
+
+
+def test_pool3d_ties_pick_first():
+    z = np.full((1, 4, 4, 4, 16), -1.5, np.float32)
+    P, idx = cf.cf_pool3d_fwd(to_dev(z, BF), SLOPE)
+    torch.cuda.synchronize()
+    assert int(idx.max()) == 0
+    assert torch.all(P.float() == torch.tensor(-0.44921875, device=P.device))  # bf16(0.3 * -1.5)
+
+
+def test_pool3d_odd_dims_rejected():
+    z = torch.zeros((1, 3, 4, 4, 8), dtype=BF, device="cuda")
+    with pytest.raises(cf.CfError) as e:
+        cf.cf_pool3d_fwd(z, SLOPE)
+    assert e.value.status == cf.CF_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_lrelu(dtype):
+    rng = np.random.default_rng(21)
+    x = act(rng, (1000003,), dtype)
+    dy = act(rng, (1000003,), dtype)
+    y = cf.cf_lrelu(to_dev(x, dtype), SLOPE)
+    dx = cf.cf_lrelu(to_dev(x, dtype), SLOPE, dy=to_dev(dy, dtype))
+    torch.cuda.synchronize()
+    ulp = 2.0 ** -8 if dtype == BF else 2.0 ** -23
+    yo = oracle.lrelu_fwd(x, SLOPE)
+    do = oracle.lrelu_bwd(x, dy, SLOPE)
+    assert np.all(np.abs(host64(y) - yo) <= ulp * np.abs(yo))
+    assert np.all(np.abs(host64(dx) - do) <= ulp * np.abs(do))
+
+
+# ------------------------------------------------------------------ dense
+DENSE_CASES = [(8, 16384, 128, SLOPE), (8, 128, 64, SLOPE), (8, 64, 3, -1.0), (3, 1000, 77, SLOPE),
+               (11, 300, 5, -1.0), (1, 16384, 128, SLOPE)]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES)
+def test_dense_fwd_bwd(case):
+    B, fin, fout, slope = case
+    rng = np.random.default_rng(fin + fout)
+    x = rng.standard_normal((B, fin)).astype(np.float32)
+    w, _ = sd.he_normal_dense(rng, fin, fout)
+    b = (rng.standard_normal(fout) * 0.1).astype(np.float32)
+    dy = rng.standard_normal((B, fout)).astype(np.float32)
+    xt, wt, bt = to_dev(x, F32), to_dev(w, F32), to_dev(b, F32)
+    pre, y = cf.cf_dense_fwd(xt, wt, bt, slope)
+    dx, dw, db = cf.cf_dense_bwd(xt, wt, pre, to_dev(dy, F32), slope)
+    torch.cuda.synchronize()
+    pre_o, y_o = oracle.dense_fwd(x, w, b, slope)
+    assert rel_err(host64(pre), pre_o) <= TOL_F32
+    assert rel_err(host64(y), y_o) <= TOL_F32
+    # backward from the oracle's own pre-activations (sign of pre decides the gate)
+    dx_o, dw_o, db_o = oracle.dense_bwd(x, w, pre_o, dy, slope)
+    assert rel_err(host64(dx), dx_o) <= TOL_F32
+    assert rel_err(host64(dw), dw_o) <= TOL_F32
+    assert rel_err(host64(db), db_o) <= TOL_F32
+
+
+def test_mse_and_sgd():
+    rng = np.random.default_rng(4)
+    yhat = rng.standard_normal((8, 3)).astype(np.float32)
+    t = sd.targets(rng, 8)
+    loss, dy = cf.cf_mse(to_dev(yhat, F32), to_dev(t, F32))
+    w = rng.standard_normal(100001).astype(np.float32)
+    g = rng.standard_normal(100001).astype(np.float32)
+    wt = to_dev(w, F32)
+    cf.cf_sgd(wt, to_dev(g, F32), 1e-3)
+    torch.cuda.synchronize()
+    lo, do = oracle.mse(yhat, t)
+    assert abs(loss.item() - lo) <= TOL_F32 * lo
+    assert rel_err(host64(dy), do) <= TOL_F32
+    assert rel_err(host64(wt), oracle.sgd(w, g, 1e-3)) <= TOL_F32
+
+
+# ------------------------------------------------------------ error paths
+def test_error_statuses_on_device():
+    x = torch.zeros((1, 4, 4, 4, 32), dtype=BF, device="cuda")
+    w = torch.zeros((3, 3, 3, 32, 32), dtype=BF, device="cuda")
+    y = torch.empty_like(x)
+    L = cf.lib()
+    st = L.cf_conv3d_fwd(cf.CF_BF16, cf.dims(x.shape), cf._ptr(x), cf._ptr(w), 32, cf.CONV3, cf._ptr(y), None, 0,
+                         cf._stream())
+    assert st == cf.CF_ERR_WORKSPACE
+    st = L.cf_conv3d_fwd(cf.CF_BF16, cf.dims(x.shape), cf._ptr(x), cf._ptr(w), 32, cf.cf_conv(5, 1, 2), cf._ptr(y),
+                         None, 0, cf._stream())
+    assert st == cf.CF_ERR_UNSUPPORTED

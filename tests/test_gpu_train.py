@@ -1,0 +1,158 @@
+"""GPU parity of cf_train_step against the oracle's training step (same
+seeded inputs, bf16 storage modelled at the same points), plus consistency:
+the step equals the composition of the individual entry points bit for bit,
+and is deterministic."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthdata as sd
+from cnn_cosmology_volumes_amd import cf
+from gpu_util import TOL_BF16, host64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+BF, F32 = torch.bfloat16, torch.float32
+SLOPE = 0.3
+
+
+def make_problem(seed, B, size, filters, dense, dtype):
+    st = sd.streams(100 + seed)
+    x = sd.lognormal_poisson_input(st["field"], st["poisson"], (B, size, size, size), 4, bf16=(dtype == BF))
+    conv = []
+    cin = 4
+    for f in filters:
+        conv.append(sd.he_normal_conv(st["convw"], cin, f))
+        cin = f
+    flat = (size >> len(filters)) ** 3 * filters[-1]
+    dw = []
+    fan = flat
+    for o in dense:
+        W, b = sd.he_normal_dense(st["densew"], fan, o)
+        b = (st["densew"].standard_normal(o) * 0.05).astype(np.float32)
+        dw.append((W, b))
+        fan = o
+    t = sd.targets(st["targets"], B, dense[-1])
+    return x, conv, dw, t
+
+
+def device_params(conv, dense):
+    ps = [to_dev(w, F32) for w in conv]
+    for W, b in dense:
+        ps += [to_dev(W, F32), to_dev(b, F32)]
+    return ps
+
+
+def run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w):
+    m = cf.model_desc(4, size, filters, dense_w, SLOPE)
+    params = device_params(conv, dense)
+    old = [p.clone() for p in params]
+    pred = torch.empty((x.shape[0], dense_w[-1]), dtype=F32, device="cuda")
+    loss, _ = cf.cf_train_step(m, to_dev(x, dtype), to_dev(t, F32), params, lr, pred=pred)
+    torch.cuda.synchronize()
+    return loss.item(), host64(pred), old, params
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_train_step_matches_oracle(dtype):
+    B, size, filters, dense_w = 2, 16, [32, 64], [32, 16, 3]
+    x, conv, dense, t = make_problem(1, B, size, filters, dense_w, dtype)
+    lr = 1.0   # large step so the gradient is recovered exactly from the update
+    loss, pred, old, new = run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w)
+    storage = "bf16" if dtype == BF else "f32"
+    ref = oracle.train_step(x, t, conv, dense, lr, SLOPE, storage=storage)
+    tol = TOL_BF16 if dtype == BF else 1e-4
+    assert abs(loss - ref["loss"]) <= tol * ref["loss"]
+    assert rel_err(pred, ref["yhat"]) <= tol
+    L = len(filters)
+    for l in range(L):
+        g = (host64(old[l]) - host64(new[l])) / lr
+        assert rel_err(g, ref["conv_dw"][l]) <= tol, l
+    for k in range(3):
+        gW = (host64(old[L + 2 * k]) - host64(new[L + 2 * k])) / lr
+        gb = (host64(old[L + 2 * k + 1]) - host64(new[L + 2 * k + 1])) / lr
+        assert rel_err(gW, ref["dense_g"][k][0]) <= tol, k
+        assert rel_err(gb, ref["dense_g"][k][1]) <= tol, k
+
+
+def composed_step(xd, conv_d, dense_d, td, lr):
+    """The same step through the individual entry points (bf16)."""
+    L = len(conv_d)
+    a, cache = xd, []
+    for w in conv_d:
+        wb = w.to(BF)
+        z = cf.cf_conv3d_fwd(a, wb)
+        p, idx = cf.cf_pool3d_fwd(z, SLOPE)
+        cache.append((a, wb, p, idx))
+        a = p
+    B = a.shape[0]
+    h = a.reshape(B, -1).float()
+    dcache = []
+    for k in range(3):
+        W, b = dense_d[2 * k], dense_d[2 * k + 1]
+        s = SLOPE if k < 2 else -1.0
+        pre, y = cf.cf_dense_fwd(h, W, b, s)
+        dcache.append((h, W, pre, s))
+        h = y
+    loss, g = cf.cf_mse(h, td)
+    dgrads = [None] * 3
+    for k in reversed(range(3)):
+        hx, W, pre, s = dcache[k]
+        g, dW, db = cf.cf_dense_bwd(hx, W, pre, g, s)
+        dgrads[k] = (dW, db)
+    dp = g.to(BF).reshape(a.shape)
+    cgrads = [None] * L
+    for l in reversed(range(L)):
+        xin, wb, p, idx = cache[l]
+        dz = cf.cf_pool3d_bwd(dp, p, idx, SLOPE)
+        cgrads[l] = cf.cf_conv3d_bwd_weight(xin, dz)
+        if l > 0:
+            dp = cf.cf_conv3d_bwd_data(dz, wb)
+    for l in range(L):
+        cf.cf_sgd(conv_d[l], cgrads[l], lr)
+    for k in range(3):
+        cf.cf_sgd(dense_d[2 * k], dgrads[k][0], lr)
+        cf.cf_sgd(dense_d[2 * k + 1], dgrads[k][1], lr)
+    return loss
+
+
+@pytest.mark.parametrize("problem", [(2, 16, [32, 64], [32, 16, 3]), (1, 32, [32, 64, 128], [64, 32, 3])])
+def test_train_step_equals_composition_bitwise(problem):
+    B, size, filters, dense_w = problem
+    x, conv, dense, t = make_problem(2, B, size, filters, dense_w, BF)
+    m = cf.model_desc(4, size, filters, dense_w, SLOPE)
+    xd, td = to_dev(x, BF), to_dev(t, F32)
+    p1 = device_params(conv, dense)
+    p2 = device_params(conv, dense)
+    loss1, _ = cf.cf_train_step(m, xd, td, p1, 1e-3)
+    loss2 = composed_step(xd, p2[:len(filters)], p2[len(filters):], td, 1e-3)
+    torch.cuda.synchronize()
+    assert torch.equal(loss1, loss2)
+    for a, b in zip(p1, p2):
+        assert torch.equal(a, b)
+
+
+def test_train_step_deterministic_and_learns():
+    B, size, filters, dense_w = 2, 32, [32, 64, 128], [64, 32, 3]
+    x, conv, dense, t = make_problem(3, B, size, filters, dense_w, BF)
+    m = cf.model_desc(4, size, filters, dense_w, SLOPE)
+    xd, td = to_dev(x, BF), to_dev(t, F32)
+    pa, pb = device_params(conv, dense), device_params(conv, dense)
+    losses = []
+    for _ in range(3):
+        la, _ = cf.cf_train_step(m, xd, td, pa, 1e-2)
+        lb, _ = cf.cf_train_step(m, xd, td, pb, 1e-2)
+        torch.cuda.synchronize()
+        assert torch.equal(la, lb)
+        losses.append(la.item())
+    for a, b in zip(pa, pb):
+        assert torch.equal(a, b)
+    assert losses[-1] < losses[0]
+
+
+def test_train_step_rejects_bad_arguments():
+    m = cf.model_desc(4, 12, [32, 64], [8, 4, 3], SLOPE)   # 12 not divisible by 4
+    with pytest.raises(cf.CfError) as e:
+        cf.cf_train_step(m, torch.zeros((1, 12, 12, 12, 4), dtype=BF, device="cuda"),
+                         torch.zeros((1, 3), device="cuda"), [torch.zeros(4, device="cuda")] * 8, 1e-3)
+    assert e.value.status == cf.CF_ERR_UNSUPPORTED
