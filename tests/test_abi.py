@@ -1,0 +1,110 @@
+"""C-ABI contract on the CPU: the library loads, exports every function that
+include/cf.h declares, validates arguments before enqueuing anything (so no
+GPU is needed to see the error statuses), and sizes its workspaces as
+documented.  Pointers passed here are never dereferenced: every call fails
+validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cnn_cosmology_volumes_amd import cf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cf.h")
+FAKE = ctypes.c_void_p(0x100000)       # aligned, never dereferenced
+MIS = ctypes.c_void_p(0x100008)        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cf_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = cf.lib()
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.cf_abi_version() == 1
+
+
+def test_status_strings():
+    L = cf.lib()
+    assert L.cf_status_string(0) == b"ok"
+    assert L.cf_status_string(-3) == b"workspace too small"
+    assert L.cf_status_string(-4) == b"HIP error"
+
+
+def conv(dt, shape, cout, X, W, Y, ws=None, wsb=0, geom=cf.CONV3, fn="cf_conv3d_fwd"):
+    return getattr(cf.lib(), fn)(dt, cf.dims(shape), X, W, cout, geom, Y, ws, wsb, None)
+
+
+def test_conv_validation():
+    s = (1, 8, 8, 8, 32)
+    assert conv(cf.CF_BF16, s, 32, None, FAKE, FAKE) == cf.CF_ERR_INVALID
+    assert conv(cf.CF_BF16, s, 32, MIS, FAKE, FAKE) == cf.CF_ERR_INVALID
+    assert conv(cf.CF_BF16, (1, 0, 8, 8, 32), 32, FAKE, FAKE, FAKE) == cf.CF_ERR_INVALID
+    assert conv(cf.CF_BF16, s, 0, FAKE, FAKE, FAKE) == cf.CF_ERR_INVALID
+    assert conv(7, s, 32, FAKE, FAKE, FAKE) == cf.CF_ERR_INVALID
+    assert conv(cf.CF_BF16, s, 32, FAKE, FAKE, FAKE, geom=cf.cf_conv(5, 1, 2)) == cf.CF_ERR_UNSUPPORTED
+    assert conv(cf.CF_BF16, s, 32, FAKE, FAKE, FAKE, geom=cf.cf_conv(3, 2, 1)) == cf.CF_ERR_UNSUPPORTED
+    assert conv(cf.CF_BF16, s, 32, FAKE, FAKE, FAKE, FAKE, 16) == cf.CF_ERR_WORKSPACE
+    assert b"workspace" in cf.lib().cf_last_error()
+    for fn in ("cf_conv3d_bwd_data", "cf_conv3d_bwd_weight"):
+        assert conv(cf.CF_BF16, s, 32, FAKE, FAKE, FAKE, FAKE, 16, fn=fn) == cf.CF_ERR_WORKSPACE
+        assert conv(cf.CF_BF16, s, 32, FAKE, None, FAKE, fn=fn) == cf.CF_ERR_INVALID
+    assert b"null" in cf.lib().cf_last_error()
+
+
+def test_conv_workspace_sizes():
+    # forward on MFMA: bf16 weights [27][roundup(cout,128)][cin], 256-byte aligned
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 32), 64, cf.CF_CONV_FWD) == 27 * 128 * 32 * 2
+    # first layer (4 channels): [roundup(cout,128)][128]
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 128, 128, 128, 4), 32, cf.CF_CONV_FWD) == 128 * 128 * 2
+    # direct fp32 forward needs nothing
+    assert cf.cf_conv3d_workspace_size(cf.CF_F32, (1, 32, 32, 32, 4), 16, cf.CF_CONV_FWD) == 0
+    # small volume, many channels: split over in-channel chunks adds fp32 partials
+    ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 8, 8, 8, 256), 256, cf.CF_CONV_FWD)
+    assert ws > 27 * 256 * 256 * 2 and (ws - 27 * 256 * 256 * 2) % (4096 * 256 * 4) == 0
+    # backward-weight: fp32 partials, a whole number of dW copies
+    ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 32), 64, cf.CF_CONV_BWD_WEIGHT)
+    assert ws % (27 * 32 * 64 * 4) == 0 and ws > 0
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 32), 32, cf.CF_CONV_FWD + 9) == 0
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 32), -1, cf.CF_CONV_FWD) == 0
+
+
+def test_pool_and_elementwise_validation():
+    L = cf.lib()
+    assert L.cf_pool3d_fwd(cf.CF_BF16, cf.dims((1, 3, 4, 4, 8)), FAKE, 0.3, FAKE, FAKE, None) == cf.CF_ERR_UNSUPPORTED
+    assert L.cf_pool3d_fwd(cf.CF_BF16, cf.dims((1, 4, 4, 4, 8)), None, 0.3, FAKE, FAKE, None) == cf.CF_ERR_INVALID
+    assert L.cf_pool3d_fwd(cf.CF_BF16, cf.dims((1, 4, 4, 4, 8)), FAKE, float("nan"), FAKE, FAKE, None) == cf.CF_ERR_INVALID
+    assert L.cf_pool3d_bwd(cf.CF_F32, cf.dims((1, 4, 4, 6, 8)), FAKE, FAKE, MIS, 0.3, FAKE, None) == cf.CF_ERR_INVALID
+    assert L.cf_lrelu(cf.CF_F32, 0, FAKE, None, 0.3, FAKE, None) == cf.CF_ERR_INVALID
+    assert L.cf_dense_fwd(0, 4, 4, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 1 << 20, None) == cf.CF_ERR_INVALID
+    assert L.cf_dense_fwd(8, 16384, 128, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 0, None) == cf.CF_ERR_WORKSPACE
+    assert L.cf_dense_workspace_size(8, 16384, 128) == 64 * 8 * 128 * 4
+    assert L.cf_mse(0, 3, FAKE, FAKE, FAKE, None, None) == cf.CF_ERR_INVALID
+    assert L.cf_sgd(10, 1e-3, None, FAKE, None) == cf.CF_ERR_INVALID
+
+
+def test_train_step_validation_and_workspace():
+    m = cf.model_desc(4, 128, [32, 64, 128, 256, 256])
+    ws = cf.cf_train_step_workspace_size(m, cf.CF_BF16, 8)
+    # dominated by the first block's conv output (bf16 8x128^3x32)
+    assert 8 * 128 ** 3 * 32 * 2 < ws < 4 * 8 * 128 ** 3 * 32 * 2
+    bad = cf.model_desc(4, 100, [32, 64, 128])      # 100 not divisible by 8
+    assert cf.cf_train_step_workspace_size(bad, cf.CF_BF16, 8) == 0
+    L = cf.lib()
+    arr = (ctypes.c_void_p * 11)(*([0x100000] * 11))
+    st = L.cf_train_step(ctypes.byref(bad), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None)
+    assert st == cf.CF_ERR_UNSUPPORTED
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 16, None)
+    assert st == cf.CF_ERR_WORKSPACE
+    arr[3] = None
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None)
+    assert st == cf.CF_ERR_INVALID
+    m.nblocks = 9
+    assert cf.cf_train_step_workspace_size(m, cf.CF_BF16, 8) == 0
