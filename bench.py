@@ -1,0 +1,231 @@
+"""Benchmark: CosmoFlow-style 3D-CNN training step on one MI355X.
+
+Workload: batch 8 of 128^3 x 4 synthetic lognormal-Poisson volumes through
+5 blocks [conv 3^3 pad 1 -> leaky ReLU 0.3 -> max-pool 2^3] with filters
+32, 64, 128, 256, 256, dense 16384 -> 128 -> 64 -> 3, MSE, SGD lr 1e-3, bf16
+operands with fp32 accumulation and fp32 master weights.  One step = one
+cf_train_step call (every kernel of the path: forward, backward, update).
+Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  Besides the step rate it times every conv / pool
+entry point of the step on its own (HIP events on the launch stream) to give
+conv TFLOP/s and the roofline of the dominant kernel, and times the fp64 CPU
+oracle on a bounded sample of the same workload as a reported baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CosmoFlow 128^3x4 train samples/s; conv3d fwd+bwd TFLOP/s & % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (dense MFMA)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--op-reps", type=int, default=10, help="repetitions per entry point in the per-kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-ops", action="store_true", help="skip the per-entry-point timing")
+    return ap.parse_args()
+
+
+def build_inputs(dev, torch, cf, sd, c):
+    st = sd.streams(c.cfg_id)
+    x = sd.lognormal_poisson_input(st["field"], st["poisson"], (c.batch, c.in_size, c.in_size, c.in_size),
+                                   c.in_channels)
+    params, cin = [], c.in_channels
+    for f in c.filters:
+        params.append(torch.from_numpy(sd.he_normal_conv(st["convw"], cin, f)).to(dev))
+        cin = f
+    fan = (c.in_size >> len(c.filters)) ** 3 * c.filters[-1]
+    for o in c.dense:
+        W, b = sd.he_normal_dense(st["densew"], fan, o)
+        params += [torch.from_numpy(W).to(dev), torch.from_numpy(b).to(dev)]
+        fan = o
+    t = torch.from_numpy(sd.targets(st["targets"], c.batch)).to(dev)
+    xd = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    return xd, t, params
+
+
+def time_region(torch, fn, reps, stream):
+    """Average ms of fn() over reps calls, HIP events recorded on `stream`."""
+    fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def op_timings(torch, cf, c, dev, reps):
+    """Per-entry-point times of the step's conv and pool work at the
+    workload's shapes (bf16), each on the current stream."""
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    B, S, cin = c.batch, c.in_size, c.in_channels
+    ops = []
+    for l, f in enumerate(c.filters):
+        X = torch.randn((B, S, S, S, cin), generator=g, device=dev).to(torch.bfloat16)
+        W = (torch.randn((3, 3, 3, cin, f), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+        dZ = torch.randn((B, S, S, S, f), generator=g, device=dev).to(torch.bfloat16)
+        Z = torch.empty_like(dZ)
+        dX = torch.empty_like(X)
+        dW = torch.empty((3, 3, 3, cin, f), dtype=torch.float32, device=dev)
+        nvox = B * S ** 3
+        flops = 2 * 27 * cin * f * nvox
+        wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_FWD)),
+                          dtype=torch.uint8, device=dev)
+        wsd = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_DATA)),
+                          dtype=torch.uint8, device=dev)
+        wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_WEIGHT)),
+                          dtype=torch.uint8, device=dev)
+        xb, zb = X.numel() * 2, dZ.numel() * 2
+        wb = 27 * cin * f * 2
+        ops.append(dict(name="conv%d_fwd" % (l + 1), kind="conv", flops=flops, bytes=xb + wb + zb,
+                        ms=time_region(torch, lambda: cf.cf_conv3d_fwd(X, W, Z, ws=wsf), reps, stream)))
+        if l > 0:
+            ops.append(dict(name="conv%d_bwd_data" % (l + 1), kind="conv", flops=flops, bytes=zb + wb + xb,
+                            ms=time_region(torch, lambda: cf.cf_conv3d_bwd_data(dZ, W, dX, ws=wsd), reps, stream)))
+        ops.append(dict(name="conv%d_bwd_weight" % (l + 1), kind="conv", flops=flops, bytes=xb + zb + 27 * cin * f * 4,
+                        ms=time_region(torch, lambda: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=wsw), reps, stream)))
+        P = torch.empty((B, S // 2, S // 2, S // 2, f), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty(P.shape, dtype=torch.uint8, device=dev)
+        pb, ib = P.numel() * 2, P.numel()
+        ops.append(dict(name="pool%d_fwd" % (l + 1), kind="pool", flops=0, bytes=zb + pb + ib,
+                        ms=time_region(torch, lambda: cf.cf_pool3d_fwd(dZ, 0.3, P, idx), reps, stream)))
+        ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
+                        ms=time_region(torch, lambda: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z), reps, stream)))
+        del X, W, dZ, Z, dX, dW, wsf, wsd, wsw, P, idx
+        S //= 2
+        cin = f
+    torch.cuda.empty_cache()
+    return ops
+
+
+def cpu_baseline(c, seconds):
+    """The fp64 oracle's training step on one 64^3 x 4 sample through the
+    same blocks (1/8 of a 128^3 sample's voxels, hence of its conv work),
+    repeated for about `seconds`; scaled to 128^3-sample equivalents/s."""
+    import oracle
+    import synthdata as sd
+    st = sd.streams(c.cfg_id)
+    s = c.in_size // 2
+    x = sd.lognormal_poisson_input(st["field"], st["poisson"], (1, s, s, s), c.in_channels)
+    conv, cin = [], c.in_channels
+    for f in c.filters:
+        conv.append(sd.he_normal_conv(st["convw"], cin, f))
+        cin = f
+    dense, fan = [], (s >> len(c.filters)) ** 3 * c.filters[-1]
+    for o in c.dense:
+        dense.append(sd.he_normal_dense(st["densew"], fan, o))
+        fan = o
+    t = sd.targets(st["targets"], 1)
+    runs, t0 = 0, time.time()
+    while True:
+        oracle.train_step(x, t, conv, dense, c.lr, c.slope, storage="bf16")
+        runs += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / runs
+    frac = (s / c.in_size) ** 3
+    return {"value": frac / dt, "unit": "samples/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "fp64 oracle training step (bf16 storage model) on 1 x %d^3 x %d, same 5 blocks and dense "
+                      "head; %d run(s), %.2f s each; scaled by the voxel ratio %.4f to 128^3-sample equivalents"
+                      % (s, c.in_channels, runs, dt, frac)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from cnn_cosmology_volumes_amd import cf
+    from cnn_cosmology_volumes_amd.configs import CONFIGS, train_step_conv_flops
+    import synthdata as sd
+
+    c = CONFIGS[3]
+    dev = torch.device("cuda:0")
+    net = c.network()
+    conv_flops = train_step_conv_flops(net, c.batch)
+    xd, t, params = build_inputs(dev, torch, cf, sd, c)
+    m = cf.model_desc(c.in_channels, c.in_size, c.filters, c.dense, c.slope)
+    ws = torch.empty(cf.cf_train_step_workspace_size(m, cf.CF_BF16, c.batch), dtype=torch.uint8, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cf.cf_train_step(m, xd, t, params, c.lr, ws=ws, loss=loss)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+    value = c.batch / (ms / 1000.0)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "samples/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "cosmoflow_train_step_128c4_b8: 5 blocks (32,64,128,256,256) + dense 128-64-3, "
+                               "MSE, SGD lr 1e-3", "global_batch": c.batch, "input": "128^3x4",
+                   "parallelism": "single GPU"},
+        "wall_s_timed": round(wall, 3),
+        "step_conv_tflop": round(conv_flops / 1e12, 4),
+        "step_tflops_whole_step": round(conv_flops / (ms / 1e3) / 1e12, 2),
+        "loss_last": float(loss.item()),
+    }
+    if not a.no_ops:
+        ops = op_timings(torch, cf, c, dev, a.op_reps)
+        conv_ms = sum(o["ms"] for o in ops if o["kind"] == "conv")
+        pool_ms = sum(o["ms"] for o in ops if o["kind"] == "pool")
+        out["conv_ms_per_step"] = round(conv_ms, 4)
+        out["pool_ms_per_step"] = round(pool_ms, 4)
+        out["conv_tflops"] = round(conv_flops / (conv_ms / 1e3) / 1e12, 2)
+        out["conv_frac_mfma_peak"] = round(out["conv_tflops"] / PEAK_BF16_TFLOPS, 4)
+        out["ops"] = {o["name"]: round(o["ms"], 4) for o in ops}
+        dom = max(ops, key=lambda o: o["ms"])
+        ai = dom["flops"] / dom["bytes"] if dom["bytes"] else 0.0
+        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        if dom["kind"] == "conv" and ai >= ridge:
+            ach = dom["flops"] / (dom["ms"] / 1e3) / 1e12
+            out["roofline"] = {"kernel": dom["name"], "bound": "mfma", "achieved": round(ach, 2),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                               "traffic": None}
+        else:
+            ach = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
+            out["roofline"] = {"kernel": dom["name"], "bound": "hbm", "achieved": round(ach, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                               "traffic": None}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
