@@ -19,7 +19,7 @@ namespace {
 constexpr int DB = 8;        // batch rows per block
 constexpr int DO = 64;       // output columns per block
 constexpr int DI = 4;        // input lanes per block
-constexpr int DK = 256;      // input rows per split
+constexpr int DK = 128;      // input rows per split
 
 __device__ __forceinline__ float xin(const float* X, const uint16_t* Xb, int64_t i) {
     return Xb ? bf2f(Xb[i]) : X[i];
@@ -29,11 +29,14 @@ __device__ __forceinline__ float gate(float dy, float pre, float slope) {
     return (slope >= 0.f && !(pre > 0.f)) ? slope * dy : dy;
 }
 
-// part[ks][b][o] = sum_{i in split ks} X[b,i] W[i,o]
+// part[ks][b][o] = sum_{i in split ks} X[b,i] W[i,o].  The block's input
+// rows (DB x DK values) are staged in LDS once; each thread then streams W
+// rows (coalesced over o) and accumulates DB batch rows.
 __global__ __launch_bounds__(DO * DI)
 void dense_fwd_partial(const float* __restrict__ X, const uint16_t* __restrict__ Xb, const float* __restrict__ W,
                        float* __restrict__ part, int B, int In, int Out)
 {
+    __shared__ float xs[DB][DK];
     __shared__ float red[DI][DB][DO];
     const int ol = threadIdx.x % DO, il = threadIdx.x / DO;
     const int o = blockIdx.x * DO + ol;
@@ -41,27 +44,31 @@ void dense_fwd_partial(const float* __restrict__ X, const uint16_t* __restrict__
     const int b0 = blockIdx.z * DB;
     const int nb = min(DB, B - b0);
     const int i0 = ks * DK, i1 = min(In, i0 + DK);
+    for (int e = threadIdx.x; e < DB * DK; e += DO * DI) {
+        const int b = e / DK, i = i0 + e % DK;
+        xs[b][e % DK] = (b < nb && i < i1) ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+    }
+    __syncthreads();
     float acc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[b] = 0.f;
-    for (int i = i0 + il; i < i1; i += DI) {
-        const float w = o < Out ? W[(int64_t)i * Out + o] : 0.f;
+    if (o < Out) {
+        for (int i = i0 + il; i < i1; i += DI) {
+            const float w = W[(int64_t)i * Out + o];
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
-            if (b < nb) acc[b] = fmaf(xin(X, Xb, (int64_t)(b0 + b) * In + i), w, acc[b]);
+            for (int b = 0; b < DB; ++b) acc[b] = fmaf(xs[b][i - i0], w, acc[b]);
+        }
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) red[il][b][ol] = acc[b];
     __syncthreads();
     if (il == 0 && o < Out) {
-        const int nks = gridDim.y;
         for (int b = 0; b < nb; ++b) {
             float s = red[0][b][ol];
 #pragma unroll
             for (int k = 1; k < DI; ++k) s += red[k][b][ol];
             part[((int64_t)ks * B + b0 + b) * Out + o] = s;
         }
-        (void)nks;
     }
 }
 

@@ -283,14 +283,31 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     }
 }
 
-// dW[e] = sum_{s=0..splits-1} part[s][e], summed in increasing s.
-__global__ void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW, int64_t n, int splits)
+// dW[e] = sum over splits of part[s][e].  A block owns 64 consecutive
+// elements; its 16 split-lanes each sum the splits s = lane, lane + 16, ...
+// in increasing order, and the 16 lane sums are added in lane order.  The
+// order is fixed, so the result is deterministic.
+constexpr int RD_E = 64, RD_L = 16;
+
+__global__ __launch_bounds__(RD_E * RD_L)
+void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW, int64_t n, int splits)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+    __shared__ float red[RD_L][RD_E];
+    const int el = threadIdx.x % RD_E, sl = threadIdx.x / RD_E;
+    const int64_t i = (int64_t)blockIdx.x * RD_E + el;
     float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
-    dW[i] = s;
+    if (i < n) {
+#pragma unroll 4
+        for (int k = sl; k < splits; k += RD_L) s += part[(int64_t)k * n + i];
+    }
+    red[sl][el] = s;
+    __syncthreads();
+    if (sl == 0 && i < n) {
+        float t = red[0][el];
+#pragma unroll
+        for (int k = 1; k < RD_L; ++k) t += red[k][el];
+        dW[i] = t;
+    }
 }
 
 }  // namespace
@@ -353,7 +370,8 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)27 * x.c * cout;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, dW, n, p.splits);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_E * RD_L), 0, s, part, dW,
+                       n, p.splits);
     return hipGetLastError();
 }
 

@@ -104,3 +104,41 @@ def normal(rng, shape, bf16=True, scale=1.0):
 def pool_indices(rng, shape):
     """Uniform window positions 0..7 (synthetic max-pool argmax)."""
     return rng.integers(0, 8, size=shape, dtype=np.uint8)
+
+
+# ------------------------------------------------------------------------
+# Device-side generators for the 512^3 volumes (seeded torch Philox streams;
+# same recipes as above, drawn on the GPU because host generation of 10^9
+# values is slow).  They draw random numbers only.
+def torch_generator(seed, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def lognormal_poisson_input_torch(g, shape_ndhw, channels, device):
+    """log(1 + Poisson(delta)), delta = exp(N(0,1)) / mean, per sample and
+    channel; returned as a bf16 NDHWC device tensor."""
+    import torch
+    out = torch.empty(tuple(shape_ndhw) + (channels,), dtype=torch.bfloat16, device=device)
+    for n in range(shape_ndhw[0]):
+        for c in range(channels):
+            e = torch.randn(tuple(shape_ndhw[1:]), generator=g, device=device).exp_()
+            e /= e.mean(dtype=torch.float64).float()
+            counts = torch.poisson(e, generator=g)
+            out[n, ..., c] = counts.log1p_().to(torch.bfloat16)
+            del e, counts
+    return out
+
+
+def normal_torch(g, shape, device, scale=1.0):
+    """N(0, scale^2) bf16 device tensor, drawn in 2^28-element chunks."""
+    import torch
+    out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    step = 1 << 28
+    for s in range(0, flat.numel(), step):
+        e = min(flat.numel(), s + step)
+        flat[s:e] = (torch.randn(e - s, generator=g, device=device) * scale).to(torch.bfloat16)
+    return out

@@ -85,7 +85,7 @@ def test_pool_and_elementwise_validation():
     assert L.cf_lrelu(cf.CF_F32, 0, FAKE, None, 0.3, FAKE, None) == cf.CF_ERR_INVALID
     assert L.cf_dense_fwd(0, 4, 4, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 1 << 20, None) == cf.CF_ERR_INVALID
     assert L.cf_dense_fwd(8, 16384, 128, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 0, None) == cf.CF_ERR_WORKSPACE
-    assert L.cf_dense_workspace_size(8, 16384, 128) == 64 * 8 * 128 * 4
+    assert L.cf_dense_workspace_size(8, 16384, 128) == 128 * 8 * 128 * 4
     assert L.cf_mse(0, 3, FAKE, FAKE, FAKE, None, None) == cf.CF_ERR_INVALID
     assert L.cf_sgd(10, 1e-3, None, FAKE, None) == cf.CF_ERR_INVALID
 
