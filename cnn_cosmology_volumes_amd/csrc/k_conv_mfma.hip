@@ -11,10 +11,11 @@
 // output voxels (MFMA B operand = input halo), K = 27 taps x in-channels.
 //  - A block owns a TD x TH x TW output tile of one sample and BM output
 //    channels.  For every 32-channel input chunk it stages the
-//    (TD+2)(TH+2)(TW+2) halo of the input in LDS once (80-byte voxel stride:
-//    64 bytes of data + 16 bytes of padding, which keeps the 16-byte
-//    per-lane reads of 16 consecutive voxels on distinct LDS banks) and then
-//    walks the 27 taps; a tap only shifts the LDS row index, so every B
+//    (TD+2)(TH+2)(TW+2) halo of the input in LDS once (96-byte voxel stride:
+//    64 bytes of data + 32 bytes of padding; measured on gfx950, this stride
+//    lets the 16-byte per-lane reads of 16 consecutive voxels run at about
+//    310 B/clk per CU, against about 200 for an 80- or 64-byte stride) and
+//    then walks the 27 taps; a tap only shifts the LDS row index, so every B
 //    fragment is one aligned 16-byte LDS read at a compile-time offset.
 //  - A fragments (8 consecutive in-channels of one output channel) are
 //    16-byte global loads from the [tap][co][ci] weight copy, which is small
@@ -27,23 +28,29 @@ namespace cf {
 
 namespace {
 
-constexpr int LDS_STRIDE = 40;   // bf16 per halo voxel: 32 data + 8 padding
+constexpr int LDS_STRIDE = 48;   // bf16 per halo voxel: 32 data + 16 padding (96 B)
 
+// BM output channels per block split over BM/WM waves; TD*TH*TW voxels per
+// block split over VT/WN waves; each wave owns a WM x WN accumulator tile.
 template <int BM, int WN, int TD, int TH, int TW>
 struct Tile {
+    static constexpr int WM = BM < 64 ? BM : 64;
+    static constexpr int NWM = BM / WM;
     static constexpr int VT = TD * TH * TW;
-    static constexpr int NW = VT / WN;
+    static constexpr int NWV = VT / WN;
+    static constexpr int NW = NWM * NWV;
     static constexpr int NT = NW * 64;
     static constexpr int HD = TD + 2, HH = TH + 2, HW = TW + 2;
     static constexpr int HV = HD * HH * HW;
-    static constexpr int MI = BM / 16;
+    static constexpr int MI = WM / 16;
     static constexpr int NJ = WN / 16;
+    static constexpr int MINB = NW > 4 ? 1 : 2;   // blocks per CU the registers are sized for
     static_assert(VT % WN == 0 && (NW == 4 || NW == 8), "tile");
-    static_assert(BM % 16 == 0 && WN % 16 == 0, "frag");
+    static_assert(BM % WM == 0 && WM % 16 == 0 && WN % 16 == 0, "frag");
 };
 
 template <int BM, int WN, int TD, int TH, int TW>
-__global__ __launch_bounds__((Tile<BM, WN, TD, TH, TW>::NT))
+__global__ __launch_bounds__((Tile<BM, WN, TD, TH, TW>::NT), (Tile<BM, WN, TD, TH, TW>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                         uint16_t* __restrict__ Y, float* __restrict__ part,
                         int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
@@ -53,7 +60,8 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LDS_STRIDE];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wm = (threadIdx.x >> 6) % T::NWM;     // co slice of this wave
+    const int wave = (threadIdx.x >> 6) / T::NWM;   // voxel slice of this wave
     const int l16 = lane & 15, lg = lane >> 4;
 
     uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -62,7 +70,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int td_ = tile % tD;
     const int n = tile / tD;
     const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
-    const int co_base = blockIdx.y * BM;
+    const int co_base = blockIdx.y * BM + wm * T::WM;
     const int nchunks = Cin >> 5;
     const int c_begin = blockIdx.z * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
@@ -99,24 +107,46 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
         }
         __syncthreads();
 
+        // Software pipeline over the 27 taps: weight (A) fragments are
+        // loaded from global memory two taps ahead, halo (B) fragments are
+        // read from LDS one tap ahead, so neither latency sits in front of
+        // the MFMAs of the current tap.
         const uint16_t* wrow = Wk + ((int64_t)(co_base + l16) * Cin + c * 32 + 8 * lg);
         const int64_t tap_stride = (int64_t)CoutPad * Cin;
+        bf16x8 a0[T::MI], a1[T::MI], a2[T::MI], b0[T::NJ], b1[T::NJ];
+#pragma unroll
+        for (int i = 0; i < T::MI; ++i) {
+            a0[i] = *reinterpret_cast<const bf16x8*>(wrow + (int64_t)16 * i * Cin);
+            a1[i] = *reinterpret_cast<const bf16x8*>(wrow + tap_stride + (int64_t)16 * i * Cin);
+        }
+#pragma unroll
+        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j]);
 #pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
-            const int kd = tap / 9, kh = (tap / 3) % 3, kw = tap % 3;
-            const int toff = ((kd * T::HH + kh) * T::HW + kw) * LDS_STRIDE;
-            bf16x8 a[T::MI], b[T::NJ];
+            if (tap + 2 < 27) {
 #pragma unroll
-            for (int i = 0; i < T::MI; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(wrow + tap * tap_stride + (int64_t)16 * i * Cin);
+                for (int i = 0; i < T::MI; ++i)
+                    a2[i] = *reinterpret_cast<const bf16x8*>(wrow + (tap + 2) * tap_stride + (int64_t)16 * i * Cin);
+            }
+            if (tap + 1 < 27) {
+                const int tn = tap + 1;
+                const int toff = (((tn / 9) * T::HH + (tn / 3) % 3) * T::HW + tn % 3) * LDS_STRIDE;
 #pragma unroll
-            for (int j = 0; j < T::NJ; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
+                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
+            }
+            // Fence: keep the prefetches above in front of this tap's MFMAs
+            // (the scheduler would otherwise sink each load next to its use).
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < T::MI; ++i)
 #pragma unroll
                 for (int j = 0; j < T::NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; }
+#pragma unroll
+            for (int j = 0; j < T::NJ; ++j) b0[j] = b1[j];
         }
     }
 
@@ -164,12 +194,12 @@ struct CfgInfo { int bm, wn, td, th, tw; };
 constexpr CfgInfo kCfgs[] = {
     {128, 64, 4, 4, 16},   // 0
     {128, 64, 4, 8, 8},    // 1
-    {64, 128, 4, 8, 16},   // 2
-    {64, 128, 8, 8, 8},    // 3
-    {32, 128, 4, 8, 16},   // 4
-    {32, 128, 8, 8, 8},    // 5
-    {16, 128, 4, 8, 16},   // 6
-    {16, 128, 8, 8, 8},    // 7
+    {64, 64, 4, 4, 16},    // 2
+    {64, 64, 4, 8, 8},     // 3
+    {32, 64, 4, 4, 16},    // 4
+    {32, 64, 4, 8, 8},     // 5
+    {16, 64, 4, 4, 16},    // 6
+    {16, 64, 4, 8, 8},     // 7
 };
 
 template <int BM, int WN, int TD, int TH, int TW>
@@ -222,12 +252,12 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     switch (p.cfg) {
     case 0: e = launch_cfg<128, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     case 1: e = launch_cfg<128, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 2: e = launch_cfg<64, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 3: e = launch_cfg<64, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 4: e = launch_cfg<32, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 5: e = launch_cfg<32, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 6: e = launch_cfg<16, 128, 4, 8, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    default: e = launch_cfg<16, 128, 8, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 2: e = launch_cfg<64, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 3: e = launch_cfg<64, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 4: e = launch_cfg<32, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 5: e = launch_cfg<32, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 6: e = launch_cfg<16, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    default: e = launch_cfg<16, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
