@@ -2,7 +2,7 @@
 
 Workload: batch 8 of 128^3 x 4 synthetic lognormal-Poisson volumes through
 5 blocks [conv 3^3 pad 1 -> leaky ReLU 0.3 -> max-pool 2^3] with filters
-32, 64, 128, 256, 256, dense 16384 -> 128 -> 64 -> 3, MSE, SGD lr 1e-3, bf16
+32, 64, 128, 256, 256, dense 16384 -> 128 -> 64 -> 3, MSE, SGD lr 1e-6, bf16
 operands with fp32 accumulation and fp32 master weights.  One step = one
 cf_train_step call (every kernel of the path: forward, backward, update).
 Inputs are resident in HBM before the timed region.
@@ -74,7 +74,9 @@ def time_region(torch, fn, reps, stream):
 
 def op_timings(torch, cf, c, dev, reps):
     """Per-entry-point times of the step's conv and pool work at the
-    workload's shapes (bf16), each on the current stream."""
+    workload's shapes (bf16), each on the current stream.  The first block
+    runs fused exactly as in the step: conv + leaky ReLU + pool forward, and
+    pool backward + backward-weight, both counted as conv work."""
     stream = torch.cuda.current_stream()
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
@@ -83,35 +85,51 @@ def op_timings(torch, cf, c, dev, reps):
     for l, f in enumerate(c.filters):
         X = torch.randn((B, S, S, S, cin), generator=g, device=dev).to(torch.bfloat16)
         W = (torch.randn((3, 3, 3, cin, f), generator=g, device=dev) * 0.05).to(torch.bfloat16)
-        dZ = torch.randn((B, S, S, S, f), generator=g, device=dev).to(torch.bfloat16)
-        Z = torch.empty_like(dZ)
-        dX = torch.empty_like(X)
+        P = torch.randn((B, S // 2, S // 2, S // 2, f), generator=g, device=dev).to(torch.bfloat16)
+        idx = torch.randint(0, 8, P.shape, generator=g, device=dev, dtype=torch.uint8)
         dW = torch.empty((3, 3, 3, cin, f), dtype=torch.float32, device=dev)
         nvox = B * S ** 3
         flops = 2 * 27 * cin * f * nvox
-        wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_FWD)),
-                          dtype=torch.uint8, device=dev)
-        wsd = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_DATA)),
-                          dtype=torch.uint8, device=dev)
-        wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_WEIGHT)),
-                          dtype=torch.uint8, device=dev)
-        xb, zb = X.numel() * 2, dZ.numel() * 2
-        wb = 27 * cin * f * 2
-        ops.append(dict(name="conv%d_fwd" % (l + 1), kind="conv", flops=flops, bytes=xb + wb + zb,
-                        ms=time_region(torch, lambda: cf.cf_conv3d_fwd(X, W, Z, ws=wsf), reps, stream)))
-        if l > 0:
+        xb, zb, wb = X.numel() * 2, nvox * f * 2, 27 * cin * f * 2
+        pb, ib = P.numel() * 2, P.numel()
+        if l == 0:
+            wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_POOL_FWD)),
+                              dtype=torch.uint8, device=dev)
+            wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_POOL_CONV_BWD_WEIGHT)),
+                              dtype=torch.uint8, device=dev)
+            Po = torch.empty_like(P)
+            ido = torch.empty_like(idx)
+            ops.append(dict(name="block1_conv_pool_fwd", kind="conv", flops=flops, bytes=xb + wb + pb + ib,
+                            ms=time_region(torch, lambda: cf.cf_conv3d_pool_fwd(X, W, 0.3, Po, ido, ws=wsf), reps,
+                                           stream)))
+            ops.append(dict(name="block1_pool_bwd_weight", kind="conv", flops=flops,
+                            bytes=xb + 2 * pb + ib + 27 * cin * f * 4,
+                            ms=time_region(torch, lambda: cf.cf_pool_conv3d_bwd_weight(X, P, P, idx, 0.3, dW, ws=wsw),
+                                           reps, stream)))
+            del wsf, wsw, Po, ido
+        else:
+            dZ = torch.randn((B, S, S, S, f), generator=g, device=dev).to(torch.bfloat16)
+            Z = torch.empty_like(dZ)
+            dX = torch.empty_like(X)
+            wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_FWD)),
+                              dtype=torch.uint8, device=dev)
+            wsd = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_DATA)),
+                              dtype=torch.uint8, device=dev)
+            wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_WEIGHT)),
+                              dtype=torch.uint8, device=dev)
+            ops.append(dict(name="conv%d_fwd" % (l + 1), kind="conv", flops=flops, bytes=xb + wb + zb,
+                            ms=time_region(torch, lambda: cf.cf_conv3d_fwd(X, W, Z, ws=wsf), reps, stream)))
             ops.append(dict(name="conv%d_bwd_data" % (l + 1), kind="conv", flops=flops, bytes=zb + wb + xb,
                             ms=time_region(torch, lambda: cf.cf_conv3d_bwd_data(dZ, W, dX, ws=wsd), reps, stream)))
-        ops.append(dict(name="conv%d_bwd_weight" % (l + 1), kind="conv", flops=flops, bytes=xb + zb + 27 * cin * f * 4,
-                        ms=time_region(torch, lambda: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=wsw), reps, stream)))
-        P = torch.empty((B, S // 2, S // 2, S // 2, f), dtype=torch.bfloat16, device=dev)
-        idx = torch.empty(P.shape, dtype=torch.uint8, device=dev)
-        pb, ib = P.numel() * 2, P.numel()
-        ops.append(dict(name="pool%d_fwd" % (l + 1), kind="pool", flops=0, bytes=zb + pb + ib,
-                        ms=time_region(torch, lambda: cf.cf_pool3d_fwd(dZ, 0.3, P, idx), reps, stream)))
-        ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
-                        ms=time_region(torch, lambda: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z), reps, stream)))
-        del X, W, dZ, Z, dX, dW, wsf, wsd, wsw, P, idx
+            ops.append(dict(name="conv%d_bwd_weight" % (l + 1), kind="conv", flops=flops,
+                            bytes=xb + zb + 27 * cin * f * 4,
+                            ms=time_region(torch, lambda: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=wsw), reps, stream)))
+            ops.append(dict(name="pool%d_fwd" % (l + 1), kind="pool", flops=0, bytes=zb + pb + ib,
+                            ms=time_region(torch, lambda: cf.cf_pool3d_fwd(dZ, 0.3, P, idx), reps, stream)))
+            ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
+                            ms=time_region(torch, lambda: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z), reps, stream)))
+            del dZ, Z, dX, wsf, wsd, wsw
+        del X, W, P, idx, dW
         S //= 2
         cin = f
     torch.cuda.empty_cache()
@@ -174,8 +192,11 @@ def main():
     def step():
         cf.cf_train_step(m, xd, t, params, c.lr, ws=ws, loss=loss)
 
+    loss_first = None
     for _ in range(a.warmup):
         step()
+        if loss_first is None:
+            loss_first = float(loss.item())
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -193,11 +214,12 @@ def main():
         "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "cosmoflow_train_step_128c4_b8: 5 blocks (32,64,128,256,256) + dense 128-64-3, "
-                               "MSE, SGD lr 1e-3", "global_batch": c.batch, "input": "128^3x4",
+                               "MSE, SGD lr %g" % c.lr, "global_batch": c.batch, "input": "128^3x4",
                    "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 3),
         "step_conv_tflop": round(conv_flops / 1e12, 4),
         "step_tflops_whole_step": round(conv_flops / (ms / 1e3) / 1e12, 2),
+        "loss_first": loss_first,
         "loss_last": float(loss.item()),
     }
     if not a.no_ops:

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libcf.so")
 
 CF_OK, CF_ERR_INVALID, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_HIP = 0, -1, -2, -3, -4
 CF_F32, CF_BF16 = 0, 1
-CF_CONV_FWD, CF_CONV_BWD_DATA, CF_CONV_BWD_WEIGHT = 0, 1, 2
+CF_CONV_FWD, CF_CONV_BWD_DATA, CF_CONV_BWD_WEIGHT, CF_CONV_POOL_FWD, CF_POOL_CONV_BWD_WEIGHT = 0, 1, 2, 3, 4
 CF_MAX_BLOCKS = 8
 
 
@@ -50,6 +50,10 @@ _SIG = {
     "cf_conv3d_fwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_conv3d_bwd_data": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_conv3d_bwd_weight": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_conv3d_pool_fwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, ctypes.c_float, _P, _P, _P,
+                            ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_pool_conv3d_bwd_weight": ([ctypes.c_int, cf_dims, _P, _P, _P, _P, ctypes.c_int32, cf_conv, ctypes.c_float, _P,
+                                   _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_pool3d_fwd": ([ctypes.c_int, cf_dims, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "cf_pool3d_bwd": ([ctypes.c_int, cf_dims, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "cf_lrelu": ([ctypes.c_int, ctypes.c_int64, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
@@ -168,6 +172,34 @@ def cf_conv3d_bwd_weight(X, dY, dW=None, ws=None, stream=None):
     ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_BWD_WEIGHT), X.device, ws)
     check(lib().cf_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, CONV3, _ptr(dW), _ptr(ws),
                                      _wsbytes(ws), _stream(stream)))
+    return dW
+
+
+def cf_conv3d_pool_fwd(X, W, slope, P=None, idx=None, ws=None, stream=None):
+    """Fused block forward: pool(lrelu(conv(X, W))) -> (P, idx)."""
+    dt = dtype_code(X.dtype)
+    cout = int(W.shape[4])
+    N, D, H, Wd = (int(v) for v in X.shape[:4])
+    pshape = (N, D // 2, H // 2, Wd // 2, cout)
+    if P is None:
+        P = torch.empty(pshape, dtype=X.dtype, device=X.device)
+    if idx is None:
+        idx = torch.empty(pshape, dtype=torch.uint8, device=X.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_POOL_FWD), X.device, ws)
+    check(lib().cf_conv3d_pool_fwd(dt, dims(X.shape), _ptr(X), _ptr(W), cout, CONV3, float(slope), _ptr(P), _ptr(idx),
+                                   _ptr(ws), _wsbytes(ws), _stream(stream)))
+    return P, idx
+
+
+def cf_pool_conv3d_bwd_weight(X, dP, P, idx, slope, dW=None, ws=None, stream=None):
+    """Fused block weight gradient: wgrad(X, pool_bwd(dP, P, idx)) -> dW fp32."""
+    dt = dtype_code(X.dtype)
+    cout = int(dP.shape[4])
+    if dW is None:
+        dW = torch.empty((3, 3, 3, int(X.shape[4]), cout), dtype=torch.float32, device=X.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_POOL_CONV_BWD_WEIGHT), X.device, ws)
+    check(lib().cf_pool_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dP), _ptr(P), _ptr(idx), cout, CONV3,
+                                          float(slope), _ptr(dW), _ptr(ws), _wsbytes(ws), _stream(stream)))
     return dW
 
 

@@ -102,6 +102,10 @@ Wg wgrad_path(cf_dtype dt, int64_t cin, int cout)
 
 size_t esize(cf_dtype dt) { return dt == CF_F32 ? 4 : 2; }
 
+// Fused block kernels exist for the 4-channel first layer in bf16.
+bool fused_pool_fwd(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout % 32 == 0; }
+bool fused_pool_wgrad(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout == 32; }
+
 // Bytes of re-laid weights each path uses.
 size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
 {
@@ -233,9 +237,95 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
     }
     case CF_CONV_BWD_WEIGHT:
         return up256(wgrad_part_bytes(wgrad_path(dtype, x.c, cout), dtype, x, cout));
+    case CF_CONV_POOL_FWD: {
+        if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
+        const Fwd p = fwd_path(dtype, x.c, cout);
+        const size_t z = fused_pool_fwd(dtype, x.c, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
+        return up256(fwd_wk_bytes(p, x.c, cout)) + up256(fwd_part_bytes(p, x, cout)) + up256(z);
+    }
+    case CF_POOL_CONV_BWD_WEIGHT: {
+        if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
+        const size_t z = fused_pool_wgrad(dtype, x.c, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
+        return up256(wgrad_part_bytes(wgrad_path(dtype, x.c, cout), dtype, x, cout)) + up256(z);
+    }
     default:
         return 0;
     }
+}
+
+cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv,
+                             float slope, void* P, uint8_t* idx, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if ((x.d & 1) || (x.h & 1) || (x.w & 1))
+        return fail(CF_ERR_UNSUPPORTED, "cf_conv3d_pool_fwd: 2^3 stride-2 pooling needs even D, H, W");
+    if (!X || !W || !P || !idx) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: null tensor pointer");
+    if (!al16(X) || !al16(W) || !al16(P) || !al16(idx))
+        return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: pointers must be 16-byte aligned");
+    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: slope is NaN");
+    const Fwd p = fwd_path(dtype, x.c, cout);
+    const bool fused = fused_pool_fwd(dtype, x.c, cout);
+    const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout)), pb = up256(fwd_part_bytes(p, x, cout));
+    const size_t zb = fused ? 0 : up256((size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype));
+    if (ws_bytes < wkb + pb + zb)
+        return fail(CF_ERR_WORKSPACE, "cf_conv3d_pool_fwd: workspace %zu < %zu bytes", ws_bytes, wkb + pb + zb);
+    if (wkb + pb + zb && (!ws || !al16(ws))) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: workspace null or misaligned");
+    char* w8 = (char*)ws;
+    const void* wk = W;
+    if (p != Fwd::Direct) {
+        CF_TRY_HIP(prep_fwd(p, W, false, x.c, cout, w8, stream), "weight re-layout");
+        wk = w8;
+    }
+    if (fused) {
+        CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)P, idx, slope, x, cout,
+                                           stream), "fused conv3d + pool forward");
+        return CF_OK;
+    }
+    void* Z = w8 + wkb + pb;
+    CF_TRY_HIP(run_fwd(p, dtype, x, X, wk, cout, Z, (float*)(w8 ? w8 + wkb : nullptr), stream), "conv3d forward");
+    const cf_dims z = with_c(x, cout);
+    hipError_t e = dtype == CF_F32 ? launch_pool_fwd<float>((const float*)Z, (float*)P, idx, z, slope, stream)
+                                   : launch_pool_fwd<uint16_t>((const uint16_t*)Z, (uint16_t*)P, idx, z, slope, stream);
+    CF_TRY_HIP(e, "pool forward");
+    return CF_OK;
+}
+
+cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dP, const void* P,
+                                    const uint8_t* idx, int32_t cout, cf_conv conv, float slope, float* dW, void* ws,
+                                    size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if ((x.d & 1) || (x.h & 1) || (x.w & 1))
+        return fail(CF_ERR_UNSUPPORTED, "cf_pool_conv3d_bwd_weight: 2^3 stride-2 pooling needs even D, H, W");
+    if (!X || !dP || !P || !idx || !dW) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: null tensor pointer");
+    if (!al16(X) || !al16(dP) || !al16(P) || !al16(idx) || !al16(dW))
+        return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: pointers must be 16-byte aligned");
+    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: slope is NaN");
+    const Wg p = wgrad_path(dtype, x.c, cout);
+    const bool fused = fused_pool_wgrad(dtype, x.c, cout);
+    const size_t pb = up256(wgrad_part_bytes(p, dtype, x, cout));
+    const size_t zb = fused ? 0 : up256((size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype));
+    if (ws_bytes < pb + zb)
+        return fail(CF_ERR_WORKSPACE, "cf_pool_conv3d_bwd_weight: workspace %zu < %zu bytes", ws_bytes, pb + zb);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: workspace null or misaligned");
+    char* w8 = (char*)ws;
+    if (fused) {
+        CF_TRY_HIP(launch_wgrad_c4_pool(plan_wgrad(x, cout), (const uint16_t*)X, (const uint16_t*)dP,
+                                        (const uint16_t*)P, idx, slope, (float*)w8, dW, x, stream),
+                   "fused pool backward + conv3d backward-weight");
+        return CF_OK;
+    }
+    void* dZ = w8 + pb;
+    const cf_dims z = with_c(x, cout);
+    hipError_t e = dtype == CF_F32
+                       ? launch_pool_bwd<float>((const float*)dP, (const float*)P, idx, (float*)dZ, z, slope, stream)
+                       : launch_pool_bwd<uint16_t>((const uint16_t*)dP, (const uint16_t*)P, idx, (uint16_t*)dZ, z, slope,
+                                                   stream);
+    CF_TRY_HIP(e, "pool backward");
+    CF_TRY_HIP(run_wgrad(p, dtype, x, X, dZ, cout, dW, (float*)w8, stream), "conv3d backward-weight");
+    return CF_OK;
 }
 
 cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv, void* Y,
@@ -413,6 +503,7 @@ struct LayerPlan {
     Fwd fwd;
     Fwd dg;
     Wg wg;
+    bool fused;         // conv + pool forward and pool backward + wgrad fused (first block)
     size_t wk_fwd, wk_dg, z, p, idx, dp, dw;   // offsets into the workspace
 };
 
@@ -468,7 +559,8 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         const int64_t npool = nvox / 8;
         Lp.wk_fwd = take(Lp.fwd == Fwd::Direct ? 0 : fwd_wk_bytes(Lp.fwd, x.c, Lp.cout));
         Lp.wk_dg = take(l > 0 ? dgrad_wk_bytes(Lp.dg, dt, x.c, Lp.cout) : 0);
-        Lp.z = take((size_t)nvox * Lp.cout * es);
+        Lp.fused = l == 0 && fused_pool_fwd(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x.c, Lp.cout);
+        Lp.z = take(Lp.fused ? 0 : (size_t)nvox * Lp.cout * es);
         Lp.p = take((size_t)npool * Lp.cout * es);
         Lp.idx = take((size_t)npool * Lp.cout);
         Lp.dp = take((size_t)npool * Lp.cout * es);
@@ -576,6 +668,13 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                 wk = params[l];
             }
         }
+        if (Lp.fused) {
+            CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)a, (const uint16_t*)wk, (uint16_t*)(w + Lp.p),
+                                               (uint8_t*)(w + Lp.idx), slope, Lp.x, Lp.cout, stream),
+                       "fused conv3d + pool forward");
+            a = w + Lp.p;
+            continue;
+        }
         CF_TRY_HIP(run_fwd(Lp.fwd, dtype, Lp.x, a, wk, Lp.cout, w + Lp.z, part, stream), "conv3d forward");
         const cf_dims z = with_c(Lp.x, Lp.cout);
         hipError_t e = bf ? launch_pool_fwd<uint16_t>((const uint16_t*)(w + Lp.z), (uint16_t*)(w + Lp.p),
@@ -610,6 +709,13 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     // 5. conv blocks backward: pool backward -> weight gradient -> data gradient
     for (int l = L - 1; l >= 0; --l) {
         const LayerPlan& Lp = P.layer[l];
+        if (Lp.fused) {
+            CF_TRY_HIP(launch_wgrad_c4_pool(plan_wgrad(Lp.x, Lp.cout), (const uint16_t*)(l == 0 ? X : w + P.layer[l - 1].p),
+                                            (const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
+                                            (const uint8_t*)(w + Lp.idx), slope, part, F(Lp.dw), Lp.x, stream),
+                       "fused pool backward + conv3d backward-weight");
+            continue;
+        }
         const cf_dims z = with_c(Lp.x, Lp.cout);
         void* dz = w + Lp.z;    // the conv output buffer is reused for its gradient
         hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),

@@ -79,6 +79,10 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
 // Layer-1 forward (Cin == 4) on MFMA, K = 27*4 padded to 128.
 hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, const cf_dims& x,
                               int cout, int copad, hipStream_t s);
+// Same conv with leaky ReLU + 2^3 max pooling fused into the epilogue: writes
+// P [n, d/2, h/2, w/2, cout] and idx only (cout % 32 == 0; d, h, w even).
+hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx, float slope,
+                                   const cf_dims& x, int cout, hipStream_t s);
 
 // Backward-weight on MFMA.  Partial sums per voxel split into `part`
 // ([splits][27*cin*cout] fp32), then a fixed-order reduction into dW.
@@ -91,6 +95,12 @@ struct WgradPlan {
 WgradPlan plan_wgrad(const cf_dims& x, int cout);
 hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, float* part, float* dW,
                         const cf_dims& x, int cout, hipStream_t s);
+// Cin == 4, cout == 32 backward-weight with the pool backward fused into the
+// operand staging: dY is rebuilt per box from the pooled gradient dP, the
+// pooled values P and the window indices (plan from plan_wgrad(x, 32)).
+hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uint16_t* dP, const uint16_t* P,
+                                const uint8_t* idx, float slope, float* part, float* dW, const cf_dims& x,
+                                hipStream_t s);
 
 // Direct (non-MFMA) conv kernels for fp32 and for shapes outside the MFMA
 // paths.  T = float or uint16_t (bf16).  Wt layout is DHWIO for the forward;

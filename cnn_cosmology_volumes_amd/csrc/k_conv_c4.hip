@@ -18,14 +18,22 @@ constexpr int TD = 4, TH = 8, TW = 16, WN = 128;
 constexpr int VT = TD * TH * TW, NW = VT / WN, NT = NW * 64;
 constexpr int HD = TD + 2, HH = TH + 2, HW = TW + 2, HV = HD * HH * HW;
 
-template <int BM>
+// POOL = false: writes Y (the conv output).
+// POOL = true : rounds the tile to bf16 in LDS and writes only the leaky-ReLU
+//               + 2^3 max-pooled P and its window index (the same values the
+//               unfused conv -> pool pair produces), so the full-resolution
+//               conv output never goes to HBM.
+constexpr int ZS = 40;          // bf16 per voxel row of the pooled-epilogue tile (80 B)
+
+template <int BM, bool POOL>
 __global__ __launch_bounds__(NT)
 void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
-                          uint16_t* __restrict__ Y, int N, int D, int H, int W, int Cout,
-                          int tD, int tH, int tW)
+                          uint16_t* __restrict__ Y, uint8_t* __restrict__ idx, float slope,
+                          int N, int D, int H, int W, int Cout, int tD, int tH, int tW)
 {
     constexpr int MI = BM / 16, NJ = WN / 16;
     __shared__ __attribute__((aligned(16))) uint2 halo[HV];   // 4 bf16 per voxel
+    __shared__ __attribute__((aligned(16))) uint16_t zt[POOL ? VT * ZS : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -37,6 +45,15 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
     const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
     const int co_base = blockIdx.y * BM;
     const int64_t plane = (int64_t)H * W;
+
+    // All weight fragments of this block (K = 128 is four MFMA steps) are
+    // loaded up front so their latency overlaps the halo staging.
+    bf16x8 afr[4][MI];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            afr[s][i] = *reinterpret_cast<const bf16x8*>(Wk + (int64_t)(co_base + 16 * i + l16) * 128 + 32 * s + 8 * lg);
 
     for (int hv = threadIdx.x; hv < HV; hv += NT) {
         const int hw_ = hv % HW, hh_ = (hv / HW) % HH, hd_ = hv / (HW * HH);
@@ -64,19 +81,17 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        bf16x8 a[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(Wk + (int64_t)(co_base + 16 * i + l16) * 128 + 32 * s + 8 * lg);
-        // taps covered by this lane group at this step
+        const bf16x8* a = afr[s];
+        // Taps covered by this lane group at this step.  Taps 27..31 are the
+        // zero padding of K: their weights are zero, so any in-range (finite)
+        // halo value may stand in for the operand; offset 0 is used.
         const int t0 = 8 * s + 2 * lg, t1 = t0 + 1;
-        const int off0 = ((t0 / 9) * HH + (t0 / 3) % 3) * HW + t0 % 3;
-        const int off1 = ((t1 / 9) * HH + (t1 / 3) % 3) * HW + t1 % 3;
+        const int off0 = t0 < 27 ? ((t0 / 9) * HH + (t0 / 3) % 3) * HW + t0 % 3 : 0;
+        const int off1 = t1 < 27 ? ((t1 / 9) * HH + (t1 / 3) % 3) * HW + t1 % 3 : 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            uint2 u0 = make_uint2(0u, 0u), u1 = make_uint2(0u, 0u);
-            if (t0 < 27) u0 = halo[hb[j] + off0];
-            if (t1 < 27) u1 = halo[hb[j] + off1];
+            const uint2 u0 = halo[hb[j] + off0];
+            const uint2 u1 = halo[hb[j] + off1];
             const uint4 u = make_uint4(u0.x, u0.y, u1.x, u1.y);
             const bf16x8 b = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
@@ -85,21 +100,69 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         }
     }
 
+    if (!POOL) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int v = wave * WN + 16 * j + l16;
+            const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
+            const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
+            if (gd >= D || gh >= H || gw >= W) continue;
+            const int64_t gv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int co = co_base + 16 * i + 4 * lg;
+                if (co >= Cout) continue;
+                const f32x4 r = acc[i][j];
+                *reinterpret_cast<uint2*>(Y + gv * Cout + co) =
+                    make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+            }
+        }
+        return;
+    }
+    // Pooled epilogue: bf16 tile in LDS, then one thread per (pooled voxel,
+    // 8-channel group) takes the window maximum (first strict maximum in
+    // window order), applies leaky ReLU to it and stores P and idx.
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int v = wave * WN + 16 * j + l16;
-        const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
-        const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
-        if (gd >= D || gh >= H || gw >= W) continue;
-        const int64_t gv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int co = co_base + 16 * i + 4 * lg;
-            if (co >= Cout) continue;
             const f32x4 r = acc[i][j];
-            *reinterpret_cast<uint2*>(Y + gv * Cout + co) =
+            *reinterpret_cast<uint2*>(&zt[v * ZS + 16 * i + 4 * lg]) =
                 make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
         }
+    }
+    __syncthreads();
+    constexpr int PD = TD / 2, PH = TH / 2, PW = TW / 2, NG = BM / 8;
+    const int Dp = D / 2, Hp = H / 2, Wp = W / 2;
+    for (int e = threadIdx.x; e < PD * PH * PW * NG; e += NT) {
+        const int g = e % NG, pv = e / NG;
+        const int pk = pv % PW, pj = (pv / PW) % PH, pi = pv / (PW * PH);
+        const int gpd = d0 / 2 + pi, gph = h0 / 2 + pj, gpw = w0 / 2 + pk;
+        const int co = co_base + 8 * g;
+        if (gpd >= Dp || gph >= Hp || gpw >= Wp || co >= Cout) continue;
+        float best[8];
+        uint32_t bi[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int a = p >> 2, b = (p >> 1) & 1, c = p & 1;
+            const int v = ((2 * pi + a) * TH + 2 * pj + b) * TW + 2 * pk + c;
+            const uint4 u = *reinterpret_cast<const uint4*>(&zt[v * ZS + 8 * g]);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float z = __uint_as_float((k & 1) ? (w4[k >> 1] & 0xffff0000u) : (w4[k >> 1] << 16));
+                if (p == 0 || z > best[k]) { best[k] = z; bi[k] = (uint32_t)p; }
+            }
+        }
+        float out[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) out[k] = best[k] > 0.f ? best[k] : slope * best[k];
+        const int64_t o = ((((int64_t)n * Dp + gpd) * Hp + gph) * Wp + gpw) * Cout + co;
+        *reinterpret_cast<uint4*>(Y + o) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                                                      pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+        *reinterpret_cast<uint2*>(idx + o) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
+                                                        bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
     }
 }
 
@@ -112,12 +175,22 @@ hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
     if (cout <= 16) {
-        hipLaunchKernelGGL(conv3d_c4_fwd_kernel<16>, dim3(ntile, (unsigned)((cout + 15) / 16)), dim3(NT), 0, s, X, Wk,
-                           Y, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
+        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<16, false>), dim3(ntile, (unsigned)((cout + 15) / 16)), dim3(NT), 0, s,
+                           X, Wk, Y, nullptr, 0.f, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
     } else {
-        hipLaunchKernelGGL(conv3d_c4_fwd_kernel<32>, dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s, X, Wk,
-                           Y, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
+        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, false>), dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s,
+                           X, Wk, Y, nullptr, 0.f, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx, float slope,
+                                   const cf_dims& x, int cout, hipStream_t s)
+{
+    const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
+    const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
+    hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, true>), dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s, X,
+                       Wk, P, idx, slope, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
     return hipGetLastError();
 }
 

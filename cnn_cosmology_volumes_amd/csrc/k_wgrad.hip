@@ -35,34 +35,161 @@ __device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
 }
 
 // ---------------------------------------------------------------- general
-// Block: 9 waves; wave w handles taps (kd, kh) = (w / 3, w % 3), kw = 0..2,
-// for 32 input channels (ci block) x BO output channels (co block).
-// Voxel box: TD x TH x TW voxels of one sample (128), 4 K-steps of 32.
+// MFMA operands need 8 consecutive voxels of one channel per lane.  While a
+// voxel box is staged, every thread transposes 8x8 blocks (8 voxels along w
+// x 8 channels) in registers and stores them channel-major in LDS, so the
+// MFMA operands are single aligned 16-byte LDS reads:
+//   dYT[co][k]                      k = box voxel, 8 consecutive along w
+//   XT[ci][halo row (d,h)][w]       w = 0..17 of the halo, row padded to 24
+// A k-step of 32 voxels is 4 w-octets, one per 16-lane group.  For tap
+// (kd,kh,kw) the X operand of an octet starting at w0 is XT[..][w0+kw ..
+// w0+kw+7]: the lane reads w0..w0+15 once (two aligned 16-byte reads; the
+// row is padded to 24) and forms the three
+// kw-shifted operands by register selection (kw = 0, 2) and a 16-bit funnel
+// shift (kw = 1).  The next box is loaded into registers while the current
+// one is computed (two LDS buffers).
+// Block: 9 waves, wave w owns taps (kd, kh) = (w / 3, w % 3), kw = 0..2,
+// for 32 input channels x BO output channels.
 constexpr int GW_TD = 2, GW_TH = 4, GW_TW = 16;
-constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                         // 128 voxels
-constexpr int GW_HD = GW_TD + 2, GW_HH = GW_TH + 2, GW_HW = GW_TW + 2;
-constexpr int GW_HV = GW_HD * GW_HH * GW_HW;                         // 432 halo voxels
-constexpr int GW_XS = 48;        // bf16 per halo row: 32 data + 16 pad (96 B)
+constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                 // 128 voxels per box
+constexpr int GW_NOCT = GW_VB / 8;                          // 16 w-octets
+constexpr int GW_HH = GW_TH + 2;
+constexpr int GW_NR = (GW_TD + 2) * GW_HH;                  // 24 halo rows
+constexpr int GW_XW = 24;                                   // bf16 per XT row (18 used)
+constexpr int GW_XPL = GW_NR * GW_XW + 112;                 // per-channel plane, 1376 B
+constexpr int GW_DROW = GW_VB + 48;                         // dYT row, 352 B
 constexpr int GW_NT = 9 * 64;
 
+// Box coordinates (sample, box d, box h, box w) in row-major box order.
+// Decoded once per block, then advanced one box at a time in 32-bit
+// arithmetic (a 64-bit divide per box costs hundreds of VALU instructions).
+struct BoxPos {
+    int n, bd, bh, bw;
+};
+
+__device__ __forceinline__ BoxPos box_decode(int64_t box, int bD, int bH, int bW)
+{
+    BoxPos p;
+    p.bw = (int)(box % bW); box /= bW;
+    p.bh = (int)(box % bH); box /= bH;
+    p.bd = (int)(box % bD);
+    p.n = (int)(box / bD);
+    return p;
+}
+
+__device__ __forceinline__ BoxPos box_next(BoxPos p, int bD, int bH, int bW)
+{
+    if (++p.bw == bW) {
+        p.bw = 0;
+        if (++p.bh == bH) {
+            p.bh = 0;
+            if (++p.bd == bD) { p.bd = 0; ++p.n; }
+        }
+    }
+    return p;
+}
+
+// 8x8 transpose of bf16: in[v] holds 8 channels of voxel v; out[c] holds
+// voxel 0..7 of channel c.
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4& lo = in[2 * k];
+            const uint4& hi = in[2 * k + 1];
+            const uint32_t wl = (c >> 1) == 0 ? lo.x : (c >> 1) == 1 ? lo.y : (c >> 1) == 2 ? lo.z : lo.w;
+            const uint32_t wh = (c >> 1) == 0 ? hi.x : (c >> 1) == 1 ? hi.y : (c >> 1) == 2 ? hi.z : hi.w;
+            d[k] = __builtin_amdgcn_perm(wh, wl, sel);
+        }
+        out[c] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+
 template <int BO>
-__global__ __launch_bounds__(GW_NT)
+struct GwBox {
+    static constexpr int NDB = GW_NOCT * (BO / 8);           // dY blocks per box
+    static constexpr int NXB = GW_NR * 3 * 4;                // X blocks: rows x {0-7, 8-15, 16-17} x 4 ci-groups
+};
+
+template <int BO>
+__global__ __launch_bounds__(GW_NT, 1)
 void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY,
                        float* __restrict__ part, int N, int D, int H, int W, int Cin, int Cout,
                        int bD, int bH, int bW, int64_t nbox, int boxes_per_split)
 {
-    constexpr int DS = BO + 16;          // bf16 per dY row (pad 32 B)
-    constexpr int CI = BO / 16;          // co fragments
-    __shared__ __attribute__((aligned(16))) uint16_t xs[GW_HV * GW_XS];
-    __shared__ __attribute__((aligned(16))) uint16_t ds[GW_VB * DS];
+    constexpr int CI = BO / 16;
+    using G = GwBox<BO>;
+    static_assert(G::NDB + G::NXB <= GW_NT, "one block per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * GW_XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * GW_DROW];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int r4 = l16 >> 2, q4 = l16 & 3;      // transpose-read row / column quad
     const int kd = wave / 3, kh = wave % 3;
     const int co0 = blockIdx.x * BO, ci0 = blockIdx.y * 32;
     const int split = blockIdx.z;
     const int64_t plane = (int64_t)H * W;
+
+    // The block this thread stages: dY block, X block, or none.
+    const bool is_dy = tid < G::NDB;
+    const bool is_x = !is_dy && tid < G::NDB + G::NXB;
+    // Lane order: 16 consecutive lanes store 16 consecutive 16-byte columns
+    // of the same channel rows (octets for dY, (row, slot) for X).
+    int oct = 0, grp = 0, row = 0, slot = 0;
+    if (is_dy) { oct = tid % GW_NOCT; grp = tid / GW_NOCT; }
+    if (is_x) { const int t = tid - G::NDB; grp = t / (GW_NR * 3); slot = (t % (GW_NR * 3)) % 3; row = (t % (GW_NR * 3)) / 3; }
+    const int nvl = is_x && slot == 2 ? 2 : 8;                // voxels in this block
+
+    auto load_box = [&](const BoxPos& bp, uint4 (&u)[8]) {
+        const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (is_dy) {
+            const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
+            const int gd = bd * GW_TD + td, gh = bh * GW_TH + th;
+            if (gd < D && gh < H) {
+                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int gw = bw * GW_TW + w0 + j;
+                    if (gw < W) u[j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw) * Cout + co0 + grp * 8);
+                }
+            }
+        } else if (is_x) {
+            const int hd = row / GW_HH, hh = row % GW_HH;
+            const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
+            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
+                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int gw = bw * GW_TW + 8 * slot + j - 1;
+                    if (j < nvl && (unsigned)gw < (unsigned)W)
+                        u[j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + grp * 8);
+                }
+            }
+        }
+    };
+    auto store_box = [&](int buf, const uint4 (&u)[8]) {
+        uint4 t[8];
+        transpose8x8(u, t);
+        if (is_dy) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * GW_DROW + oct * 8]) = t[c];
+        } else if (is_x) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                uint16_t* dst = &xt[buf][(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8];
+                if (slot < 2) *reinterpret_cast<uint4*>(dst) = t[c];
+                else *reinterpret_cast<uint32_t*>(dst) = t[c].x;
+            }
+        }
+    };
 
     f32x4 acc[3][CI][2];
 #pragma unroll
@@ -75,62 +202,51 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 
     const int64_t b_begin = (int64_t)split * boxes_per_split;
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
+    uint4 u[8];
+    BoxPos bp = box_decode(b_begin, bD, bH, bW);
+    load_box(bp, u);
+    store_box(0, u);
+    __syncthreads();
+    int buf = 0;
     for (int64_t box = b_begin; box < b_end; ++box) {
-        int64_t bb = box;
-        const int bw = (int)(bb % bW); bb /= bW;
-        const int bh = (int)(bb % bH); bb /= bH;
-        const int bd = (int)(bb % bD);
-        const int n = (int)(bb / bD);
-        const int d0 = bd * GW_TD, h0 = bh * GW_TH, w0 = bw * GW_TW;
-
-        __syncthreads();
-        // X halo (32 channels of this ci block), zero outside the volume.
-        for (int e = threadIdx.x; e < GW_HV * 4; e += GW_NT) {
-            const int q = e & 3, hv = e >> 2;
-            const int hw_ = hv % GW_HW, hh_ = (hv / GW_HW) % GW_HH, hd_ = hv / (GW_HW * GW_HH);
-            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H && (unsigned)gw < (unsigned)W)
-                v = *reinterpret_cast<const uint4*>(X + (((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw) * Cin +
-                                                    ci0 + q * 8);
-            *reinterpret_cast<uint4*>(xs + hv * GW_XS + q * 8) = v;
+        const bool more = box + 1 < b_end;
+        if (more) {
+            bp = box_next(bp, bD, bH, bW);
+            load_box(bp, u);                   // in flight during this box's MFMAs
         }
-        // dY box (BO channels of this co block), zero outside the volume.
-        for (int e = threadIdx.x; e < GW_VB * (BO / 8); e += GW_NT) {
-            const int q = e % (BO / 8), v = e / (BO / 8);
-            const int tw = v % GW_TW, th = (v / GW_TW) % GW_TH, td = v / (GW_TW * GW_TH);
-            const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (gd < D && gh < H && gw < W)
-                val = *reinterpret_cast<const uint4*>(dY + (((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw) * Cout +
-                                                      co0 + q * 8);
-            *reinterpret_cast<uint4*>(ds + v * DS + q * 8) = val;
-        }
-        __syncthreads();
-
+        const uint16_t* xb = xt[buf];
+        const uint16_t* db = dt[buf];
 #pragma unroll
-        for (int s = 0; s < GW_VB / 32; ++s) {
-            // voxel rows read by this lane: k = 32 s + 8 lg + r4 (+4)
-            const int k0 = 32 * s + 8 * lg + r4, k1 = k0 + 4;
+        for (int s = 0; s < GW_NOCT / 4; ++s) {
+            const int o = 4 * s + lg;                      // this lane group's octet
+            const int td = o / (GW_TH * 2), th = (o / 2) % GW_TH, w0 = (o & 1) * 8;
+            const int r = (td + kd) * GW_HH + th + kh;
             bf16x8 a[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i)
-                a[i] = join8(lds_tr16(ds + k0 * DS + 16 * i + 4 * q4), lds_tr16(ds + k1 * DS + 16 * i + 4 * q4));
-            const int tw0 = k0 % GW_TW, th0 = (k0 / GW_TW) % GW_TH, td0 = k0 / (GW_TW * GW_TH);
-            const int tw1 = k1 % GW_TW, th1 = (k1 / GW_TW) % GW_TH, td1 = k1 / (GW_TW * GW_TH);
-            const int hv0 = ((td0 + kd) * GW_HH + th0 + kh) * GW_HW + tw0;
-            const int hv1 = ((td1 + kd) * GW_HH + th1 + kh) * GW_HW + tw1;
+                a[i] = *reinterpret_cast<const bf16x8*>(db + (16 * i + l16) * GW_DROW + o * 8);
 #pragma unroll
-            for (int kw = 0; kw < 3; ++kw) {
+            for (int jj = 0; jj < 2; ++jj) {
+                const uint16_t* xp = xb + (16 * jj + l16) * GW_XPL + r * GW_XW + w0;
+                const uint4 q = *reinterpret_cast<const uint4*>(xp);
+                const uint32_t e = reinterpret_cast<const uint4*>(xp)[1].x;   // aligned 16-byte read, w0+8..9 used
+                const uint4 s1 = make_uint4(__builtin_amdgcn_alignbit(q.y, q.x, 16), __builtin_amdgcn_alignbit(q.z, q.y, 16),
+                                            __builtin_amdgcn_alignbit(q.w, q.z, 16), __builtin_amdgcn_alignbit(e, q.w, 16));
+                const bf16x8 b0 = __builtin_bit_cast(bf16x8, q);
+                const bf16x8 b1 = __builtin_bit_cast(bf16x8, s1);
+                const bf16x8 b2 = __builtin_bit_cast(bf16x8, make_uint4(q.y, q.z, q.w, e));
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const bf16x8 b = join8(lds_tr16(xs + (hv0 + kw) * GW_XS + 16 * jj + 4 * q4),
-                                           lds_tr16(xs + (hv1 + kw) * GW_XS + 16 * jj + 4 * q4));
-#pragma unroll
-                    for (int i = 0; i < CI; ++i)
-                        acc[kw][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[kw][i][jj], 0, 0, 0);
+                for (int i = 0; i < CI; ++i) {
+                    acc[0][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b0, acc[0][i][jj], 0, 0, 0);
+                    acc[1][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b1, acc[1][i][jj], 0, 0, 0);
+                    acc[2][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2, acc[2][i][jj], 0, 0, 0);
                 }
             }
+        }
+        if (more) {
+            store_box(buf ^ 1, u);
+            __syncthreads();
+            buf ^= 1;
         }
     }
 
@@ -153,131 +269,273 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 }
 
 // --------------------------------------------------------- Cin == 4 layer
-// dW[tap][ci][co] for 4 input channels: N = 27 taps x 4 ci packed as 7
-// fragments of (4 taps x 4 ci) = 16 columns; every wave accumulates the whole
-// 32 x 108 result over its own quarter of each voxel box, and the four waves
-// are summed through LDS at the end (fixed order).
+// dW[tap][ci][co] for 4 input channels and 32 output channels.  Same
+// channel-major LDS tiles as above; the N dimension packs 4 (kd,kh) pairs x
+// 4 input channels per 16-column fragment (3 fragments cover the 9 pairs),
+// and kw is applied by the register shift, so one X read serves 3 taps.
+// Every wave accumulates the whole 32 x 108 result over its own k-steps of
+// each box; the waves are summed through LDS at the end in a fixed order.
+// FUSED: the conv-output gradient dY is not read; each box rebuilds it from
+// the pooled gradient, the pooled values and the window indices exactly as
+// the pool backward does (dY = dP * (P > 0 ? 1 : slope) at the recorded
+// window position, zero elsewhere, rounded to bf16).
 constexpr int C4_TD = 4, C4_TH = 4, C4_TW = 16;
-constexpr int C4_VB = C4_TD * C4_TH * C4_TW;                          // 256 voxels
-constexpr int C4_HD = C4_TD + 2, C4_HH = C4_TH + 2, C4_HW = C4_TW + 2;
-constexpr int C4_HV = C4_HD * C4_HH * C4_HW;                          // 648
+constexpr int C4_VB = C4_TD * C4_TH * C4_TW;               // 256 voxels per box
+constexpr int C4_NOCT = C4_VB / 8;                         // 32 octets
+constexpr int C4_HH = C4_TH + 2;
+constexpr int C4_NR = (C4_TD + 2) * C4_HH;                 // 36 halo rows
+constexpr int C4_XW = 24;
+constexpr int C4_XPL = C4_NR * C4_XW + 16;                 // per-channel plane: 1760 B (odd multiple of 32)
+constexpr int C4_DROW = C4_VB + 16;                        // dYT row: 544 B (odd multiple of 32)
 constexpr int C4_NT = 256;
+constexpr int C4_NDB = C4_NOCT * 4;                        // dY blocks: 32 octets x 4 groups of 8 co
+constexpr int C4_NXB = C4_NR * 3;                          // X blocks: rows x {0-7, 8-15, 16-17}
+constexpr int C4_NACC = 2 * 3 * 3;                         // co frags x pair frags x kw
 
-__device__ __forceinline__ int c4_tapoff(int t) {
-    return ((t / 9) * C4_HH + (t / 3) % 3) * C4_HW + t % 3;
-}
-
-__global__ __launch_bounds__(C4_NT)
-void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, float* __restrict__ part,
-                     int N, int D, int H, int W, int bD, int bH, int bW, int64_t nbox, int boxes_per_split)
+template <bool FUSED>
+__global__ __launch_bounds__(C4_NT, 2)
+void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY,
+                     const uint16_t* __restrict__ dP, const uint16_t* __restrict__ Pv, const uint8_t* __restrict__ pidx,
+                     float slope, float* __restrict__ part, int N, int D, int H, int W, int bD, int bH, int bW,
+                     int64_t nbox, int boxes_per_split)
 {
-    constexpr int CO = 32, DS = CO + 16;     // dY row: 32 data + 16 pad bf16
-    __shared__ __attribute__((aligned(16))) uint16_t xs[C4_HV * 4];
-    __shared__ __attribute__((aligned(16))) uint16_t ds[C4_VB * DS];
-    __shared__ float red[3][64 * 56];
+    constexpr int CO = 32;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][4 * C4_XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][CO * C4_DROW];
+    __shared__ __attribute__((aligned(16))) float red[64 * C4_NACC * 4];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int r4 = l16 >> 2, q4 = l16 & 3;
     const int split = blockIdx.x;
     const int64_t plane = (int64_t)H * W;
+    const int Dp = D / 2, Hp = H / 2, Wp = W / 2;
 
-    f32x4 acc[2][7];
+    static_assert(C4_NDB + C4_NXB <= C4_NT, "one block per thread");
+    const bool is_dy = tid < C4_NDB;
+    const bool is_x = !is_dy && tid < C4_NDB + C4_NXB;
+    int oct = 0, grp = 0, row = 0, slot = 0;
+    if (is_dy) { oct = tid % C4_NOCT; grp = tid / C4_NOCT; }
+    if (is_x) { const int t = tid - C4_NDB; row = t / 3; slot = t % 3; }
+    const int nvl = is_x && slot == 2 ? 2 : 8;
+
+    // staging registers (dY block: 8 voxels x 8 co; fused: 4 pooled voxels x 8 co of dP, P, idx)
+    uint4 u[8];
+    uint2 ui[4];
+
+    auto load_box = [&](const BoxPos& bp) {
+        const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ui[j] = make_uint2(0u, 0u);
+        if (is_dy) {
+            const int td = oct / (C4_TH * 2), th = (oct / 2) % C4_TH, w0 = (oct & 1) * 8;
+            const int gd = bd * C4_TD + td, gh = bh * C4_TH + th, gw0 = bw * C4_TW + w0;
+            if (!FUSED) {
+                if (gd < D && gh < H) {
+                    const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (gw0 + j < W) u[j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw0 + j) * CO + grp * 8);
+                }
+            } else {
+                if (gd < D && gh < H) {
+                    const int64_t prow = ((int64_t)n * Dp + gd / 2) * Hp + gh / 2;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int pw = gw0 / 2 + j;
+                        if (pw < Wp) {
+                            const int64_t o = (prow * Wp + pw) * CO + grp * 8;
+                            u[j] = *reinterpret_cast<const uint4*>(dP + o);
+                            u[4 + j] = *reinterpret_cast<const uint4*>(Pv + o);
+                            ui[j] = *reinterpret_cast<const uint2*>(pidx + o);
+                        }
+                    }
+                }
+            }
+        } else if (is_x) {
+            const int hd = row / C4_HH, hh = row % C4_HH;
+            const int gd = bd * C4_TD + hd - 1, gh = bh * C4_TH + hh - 1;
+            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
+                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int gw = bw * C4_TW + 8 * slot + j - 1;
+                    if (j < nvl && (unsigned)gw < (unsigned)W) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(X + (rowv + gw) * 4);
+                        u[j] = make_uint4(v.x, v.y, 0u, 0u);
+                    }
+                }
+            }
+        }
+    };
+
+    auto store_box = [&](int buf) {
+        if (is_dy) {
+            uint4 t[8];
+            if (!FUSED) {
+                transpose8x8(u, t);
+            } else {
+                // window position of voxel w0+j inside its pooled window: a*4 + b*2 + (j & 1)
+                const int td = oct / (C4_TH * 2), th = (oct / 2) % C4_TH;
+                const uint32_t pos_ab = (uint32_t)((td & 1) * 4 + (th & 1) * 2);
+                uint32_t g2[4][4];     // [pooled voxel j][dword c/2]: gated gradient, bf16 pairs
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t gd4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+                    const uint32_t pv4[4] = {u[4 + j].x, u[4 + j].y, u[4 + j].z, u[4 + j].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float gl = __uint_as_float(gd4[k] << 16), gh_ = __uint_as_float(gd4[k] & 0xffff0000u);
+                        const float pl = __uint_as_float(pv4[k] << 16), ph = __uint_as_float(pv4[k] & 0xffff0000u);
+                        gl = pl > 0.f ? gl : slope * gl;
+                        gh_ = ph > 0.f ? gh_ : slope * gh_;
+                        g2[j][k] = pack_bf16x2(gl, gh_);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {          // voxels 2k, 2k+1 share pooled voxel k
+                        const uint32_t ib = ((c < 4 ? ui[k].x : ui[k].y) >> (8 * (c & 3))) & 0xffu;
+                        const uint32_t gv = (g2[k][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+                        const uint32_t lo = ib == pos_ab ? gv : 0u;
+                        const uint32_t hi = ib == pos_ab + 1u ? gv : 0u;
+                        d[k] = lo | (hi << 16);
+                    }
+                    t[c] = make_uint4(d[0], d[1], d[2], d[3]);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * C4_DROW + oct * 8]) = t[c];
+        } else if (is_x) {
+            // transpose 8 voxels x 4 channels
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t d[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t wl = (c >> 1) ? u[2 * k].y : u[2 * k].x;
+                    const uint32_t wh = (c >> 1) ? u[2 * k + 1].y : u[2 * k + 1].x;
+                    d[k] = __builtin_amdgcn_perm(wh, wl, sel);
+                }
+                uint16_t* dst = &xt[buf][c * C4_XPL + row * C4_XW + slot * 8];
+                if (slot < 2) *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+                else *reinterpret_cast<uint32_t*>(dst) = d[0];
+            }
+        }
+    };
+
+    f32x4 acc[2][3][3];            // [co frag][pair frag][kw]
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int f = 0; f < 7; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // tap of the row this lane names in each N fragment (taps >= 27 padded)
-    int toff[7];
+        for (int f = 0; f < 3; ++f)
 #pragma unroll
-    for (int f = 0; f < 7; ++f) {
-        const int t = 4 * f + q4;
-        toff[f] = t < 27 ? c4_tapoff(t) : 0;
+            for (int kw = 0; kw < 3; ++kw) acc[i][f][kw] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // (kd,kh) pair of this lane's column in each pair fragment (pairs >= 9 read pair 0, result discarded)
+    int pkd[3], pkh[3];
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+        const int pr = 4 * f + (l16 >> 2);
+        pkd[f] = pr < 9 ? pr / 3 : 0;
+        pkh[f] = pr < 9 ? pr % 3 : 0;
     }
+    const int ci = l16 & 3;
 
     const int64_t b_begin = (int64_t)split * boxes_per_split;
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
+    BoxPos bp = box_decode(b_begin, bD, bH, bW);
+    load_box(bp);
+    store_box(0);
+    __syncthreads();
+    int buf = 0;
     for (int64_t box = b_begin; box < b_end; ++box) {
-        int64_t bb = box;
-        const int bw = (int)(bb % bW); bb /= bW;
-        const int bh = (int)(bb % bH); bb /= bH;
-        const int bd = (int)(bb % bD);
-        const int n = (int)(bb / bD);
-        const int d0 = bd * C4_TD, h0 = bh * C4_TH, w0 = bw * C4_TW;
-        __syncthreads();
-        for (int hv = threadIdx.x; hv < C4_HV; hv += C4_NT) {
-            const int hw_ = hv % C4_HW, hh_ = (hv / C4_HW) % C4_HH, hd_ = hv / (C4_HW * C4_HH);
-            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-            uint2 v = make_uint2(0u, 0u);
-            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H && (unsigned)gw < (unsigned)W)
-                v = *reinterpret_cast<const uint2*>(X + (((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw) * 4);
-            *reinterpret_cast<uint2*>(xs + hv * 4) = v;
+        const bool more = box + 1 < b_end;
+        if (more) {
+            bp = box_next(bp, bD, bH, bW);
+            load_box(bp);
         }
-        for (int e = threadIdx.x; e < C4_VB * 4; e += C4_NT) {
-            const int q = e & 3, v = e >> 2;
-            const int tw = v % C4_TW, th = (v / C4_TW) % C4_TH, td = v / (C4_TW * C4_TH);
-            const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (gd < D && gh < H && gw < W)
-                val = *reinterpret_cast<const uint4*>(dY + (((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw) * CO +
-                                                      q * 8);
-            *reinterpret_cast<uint4*>(ds + v * DS + q * 8) = val;
-        }
-        __syncthreads();
-
+        const uint16_t* xb = xt[buf];
+        const uint16_t* db = dt[buf];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int k0 = wave * 64 + 32 * s + 8 * lg + r4, k1 = k0 + 4;
+        for (int ss = 0; ss < 2; ++ss) {
+            const int s = wave + 4 * ss;                       // k-step of this wave
+            const int o = 4 * s + lg;                          // octet of this lane group
+            const int td = o / (C4_TH * 2), th = (o / 2) % C4_TH, w0 = (o & 1) * 8;
             bf16x8 a[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = join8(lds_tr16(ds + k0 * DS + 16 * i + 4 * q4), lds_tr16(ds + k1 * DS + 16 * i + 4 * q4));
-            const int hv0 = ((k0 / (C4_TW * C4_TH)) * C4_HH + (k0 / C4_TW) % C4_TH) * C4_HW + k0 % C4_TW;
-            const int hv1 = ((k1 / (C4_TW * C4_TH)) * C4_HH + (k1 / C4_TW) % C4_TH) * C4_HW + k1 % C4_TW;
+                a[i] = *reinterpret_cast<const bf16x8*>(db + (16 * i + l16) * C4_DROW + o * 8);
 #pragma unroll
-            for (int f = 0; f < 7; ++f) {
-                const bf16x8 b = join8(lds_tr16(xs + (hv0 + toff[f]) * 4), lds_tr16(xs + (hv1 + toff[f]) * 4));
+            for (int f = 0; f < 3; ++f) {
+                const int r = (td + pkd[f]) * C4_HH + th + pkh[f];
+                const uint16_t* xp = xb + ci * C4_XPL + r * C4_XW + w0;
+                const uint4 q = *reinterpret_cast<const uint4*>(xp);
+                const uint32_t e = reinterpret_cast<const uint4*>(xp)[1].x;
+                const uint4 s1 = make_uint4(__builtin_amdgcn_alignbit(q.y, q.x, 16), __builtin_amdgcn_alignbit(q.z, q.y, 16),
+                                            __builtin_amdgcn_alignbit(q.w, q.z, 16), __builtin_amdgcn_alignbit(e, q.w, 16));
+                const bf16x8 b0 = __builtin_bit_cast(bf16x8, q);
+                const bf16x8 b1 = __builtin_bit_cast(bf16x8, s1);
+                const bf16x8 b2 = __builtin_bit_cast(bf16x8, make_uint4(q.y, q.z, q.w, e));
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][f], 0, 0, 0);
+                for (int i = 0; i < 2; ++i) {
+                    acc[i][f][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b0, acc[i][f][0], 0, 0, 0);
+                    acc[i][f][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b1, acc[i][f][1], 0, 0, 0);
+                    acc[i][f][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2, acc[i][f][2], 0, 0, 0);
+                }
             }
+        }
+        if (more) {
+            store_box(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
         }
     }
 
-    // Sum the four waves' accumulators in wave order 0 + 1 + 2 + 3.
-    __syncthreads();
-    if (wave > 0) {
-        float* dst = red[wave - 1] + lane * 56;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int f = 0; f < 7; ++f)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(i * 7 + f) * 4 + r] = acc[i][f][r];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            const float* src = red[w] + lane * 56;
+    // Sum the four waves' accumulators in the order ((w0 + w3) + w2) + w1.
+    for (int w = 3; w >= 1; --w) {
+        __syncthreads();
+        if (wave == w) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int f = 0; f < 7; ++f)
+                for (int f = 0; f < 3; ++f)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][f][r] += src[(i * 7 + f) * 4 + r];
+                    for (int kw = 0; kw < 3; ++kw)
+                        *reinterpret_cast<f32x4*>(&red[(((i * 3 + f) * 3 + kw) * 64 + lane) * 4]) = acc[i][f][kw];
         }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int f = 0; f < 3; ++f)
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw)
+                        acc[i][f][kw] += *reinterpret_cast<const f32x4*>(&red[(((i * 3 + f) * 3 + kw) * 64 + lane) * 4]);
+        }
+    }
+    if (wave == 0) {
         float* out = part + (int64_t)split * (27 * 4 * CO);
 #pragma unroll
-        for (int f = 0; f < 7; ++f) {
-            const int t = 4 * f + (l16 >> 2), ci = l16 & 3;
-            if (t >= 27) continue;
+        for (int f = 0; f < 3; ++f) {
+            const int pr = 4 * f + (l16 >> 2);
+            if (pr >= 9) continue;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int co = 16 * i + 4 * lg;
-                const f32x4 r = acc[i][f];
-                *reinterpret_cast<float4*>(out + (t * 4 + ci) * CO + co) = make_float4(r[0], r[1], r[2], r[3]);
+            for (int kw = 0; kw < 3; ++kw) {
+                const int t = pr * 3 + kw;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int co = 16 * i + 4 * lg;
+                    const f32x4 r = acc[i][f][kw];
+                    *reinterpret_cast<float4*>(out + (t * 4 + ci) * CO + co) = make_float4(r[0], r[1], r[2], r[3]);
+                }
             }
         }
     }
@@ -327,7 +585,7 @@ WgradPlan plan_wgrad(const cf_dims& x, int cout)
         p.vox_per_split = per;   // boxes per split
     } else {
         p.kind = 0;
-        const int bo = (cout % 64 == 0) ? 64 : 32;
+        const int bo = 32;
         const int64_t nbox = x.n * ((x.d + GW_TD - 1) / GW_TD) * ((x.h + GW_TH - 1) / GW_TH) *
                              ((x.w + GW_TW - 1) / GW_TW);
         const int64_t outer = (int64_t)(cout / bo) * (x.c / 32);
@@ -352,24 +610,38 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
         const int bD = (int)((x.d + C4_TD - 1) / C4_TD), bH = (int)((x.h + C4_TH - 1) / C4_TH),
                   bW = (int)((x.w + C4_TW - 1) / C4_TW);
         const int64_t nbox = x.n * bD * bH * bW;
-        hipLaunchKernelGGL(wgrad_c4_kernel, dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, dY, part, (int)x.n,
-                           (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox, (int)p.vox_per_split);
+        hipLaunchKernelGGL(wgrad_c4_kernel<false>, dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, dY, nullptr, nullptr,
+                           nullptr, 0.f, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
+                           (int)p.vox_per_split);
     } else {
         const int bD = (int)((x.d + GW_TD - 1) / GW_TD), bH = (int)((x.h + GW_TH - 1) / GW_TH),
                   bW = (int)((x.w + GW_TW - 1) / GW_TW);
         const int64_t nbox = x.n * bD * bH * bW;
-        const int bo = (cout % 64 == 0) ? 64 : 32;
+        const int bo = 32;
         dim3 grid((unsigned)(cout / bo), (unsigned)(x.c / 32), (unsigned)p.splits);
-        if (bo == 64)
-            hipLaunchKernelGGL(wgrad_mfma_kernel<64>, grid, dim3(GW_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
-                               (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nbox, (int)p.vox_per_split);
-        else
-            hipLaunchKernelGGL(wgrad_mfma_kernel<32>, grid, dim3(GW_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
+        hipLaunchKernelGGL(wgrad_mfma_kernel<32>, grid, dim3(GW_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
                                (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nbox, (int)p.vox_per_split);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)27 * x.c * cout;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_E * RD_L), 0, s, part, dW,
+                       n, p.splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uint16_t* dP, const uint16_t* P,
+                                const uint8_t* idx, float slope, float* part, float* dW, const cf_dims& x,
+                                hipStream_t s)
+{
+    const int bD = (int)((x.d + C4_TD - 1) / C4_TD), bH = (int)((x.h + C4_TH - 1) / C4_TH),
+              bW = (int)((x.w + C4_TW - 1) / C4_TW);
+    const int64_t nbox = x.n * bD * bH * bW;
+    hipLaunchKernelGGL(wgrad_c4_kernel<true>, dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, nullptr, dP, P, idx,
+                       slope, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox, (int)p.vox_per_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)27 * 4 * 32;
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_E * RD_L), 0, s, part, dW,
                        n, p.splits);
     return hipGetLastError();

@@ -71,7 +71,13 @@ typedef struct { int64_t n, d, h, w, c; } cf_dims;
 typedef struct { int32_t k, stride, pad; } cf_conv;
 
 /* Which pass a conv workspace is sized for. */
-typedef enum { CF_CONV_FWD = 0, CF_CONV_BWD_DATA = 1, CF_CONV_BWD_WEIGHT = 2 } cf_conv_pass;
+typedef enum {
+    CF_CONV_FWD = 0,               /* cf_conv3d_fwd */
+    CF_CONV_BWD_DATA = 1,          /* cf_conv3d_bwd_data */
+    CF_CONV_BWD_WEIGHT = 2,        /* cf_conv3d_bwd_weight */
+    CF_CONV_POOL_FWD = 3,          /* cf_conv3d_pool_fwd */
+    CF_POOL_CONV_BWD_WEIGHT = 4    /* cf_pool_conv3d_bwd_weight */
+} cf_conv_pass;
 
 /* Network description for cf_train_step: `nblocks` blocks with output
  * channels filters[0..nblocks-1] applied to a cin x d x h x w input (each of
@@ -123,6 +129,32 @@ cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const vo
  * in a fixed order: results are bitwise reproducible run to run. */
 cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
                                cf_conv conv, float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Fused block forward: exactly cf_conv3d_fwd followed by cf_pool3d_fwd on
+ * its output (the conv output rounded to dtype first), i.e. one
+ * [conv -> leaky ReLU -> 2^3 max pool] block of [CF] Sec. III-A / [OY]
+ * Table I, without writing the full-resolution conv output to memory when
+ * a fused kernel exists for the shape (bf16, x.c == 4, cout % 32 == 0);
+ * other shapes run the two steps through the workspace.
+ *   X [x.n, x.d, x.h, x.w, x.c], W [3,3,3,x.c,cout]  (dtype)
+ *   P [x.n, x.d/2, x.h/2, x.w/2, cout] (dtype) and idx (uint8, same shape): outputs
+ * x.d, x.h, x.w must be even. */
+cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout,
+                             cf_conv conv, float slope, void* P, uint8_t* idx, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Fused block weight gradient: exactly cf_pool3d_bwd (dP, P, idx -> the conv
+ * output gradient dZ, rounded to dtype) followed by cf_conv3d_bwd_weight(X,
+ * dZ), without materialising dZ when a fused kernel exists for the shape
+ * (bf16, x.c == 4, cout == 32); other shapes run the two steps through the
+ * workspace.
+ *   X [x.n, x.d, x.h, x.w, x.c] (dtype)
+ *   dP, P [x.n, x.d/2, x.h/2, x.w/2, cout] (dtype), idx (uint8, same shape)
+ *   dW [3,3,3,x.c,cout] fp32, overwritten */
+cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dP,
+                                    const void* P, const uint8_t* idx, int32_t cout, cf_conv conv,
+                                    float slope, float* dW, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* ------------------------------------------------ leaky ReLU + max pooling */
 

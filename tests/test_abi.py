@@ -93,8 +93,17 @@ def test_pool_and_elementwise_validation():
 def test_train_step_validation_and_workspace():
     m = cf.model_desc(4, 128, [32, 64, 128, 256, 256])
     ws = cf.cf_train_step_workspace_size(m, cf.CF_BF16, 8)
-    # dominated by the first block's conv output (bf16 8x128^3x32)
-    assert 8 * 128 ** 3 * 32 * 2 < ws < 4 * 8 * 128 ** 3 * 32 * 2
+    # the first block is fused (its 8x128^3x32 conv output is never stored);
+    # the second block's conv output (bf16 8x64^3x64) is the largest buffer
+    assert 8 * 64 ** 3 * 64 * 2 < ws < 8 * 128 ** 3 * 32 * 2
+    # the fused first-block entry points need only weights / partial sums
+    fx = (8, 128, 128, 128, 4)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_CONV_POOL_FWD) == 128 * 128 * 2
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_POOL_CONV_BWD_WEIGHT) % (27 * 4 * 32 * 4) == 0
+    # unfused shapes carry the conv output through the workspace
+    ux = (2, 16, 16, 16, 32)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, ux, 64, cf.CF_CONV_POOL_FWD) >= 2 * 16 ** 3 * 64 * 2
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 3, 4, 4, 4), 32, cf.CF_CONV_POOL_FWD) == 0   # odd D
     bad = cf.model_desc(4, 100, [32, 64, 128])      # 100 not divisible by 8
     assert cf.cf_train_step_workspace_size(bad, cf.CF_BF16, 8) == 0
     L = cf.lib()

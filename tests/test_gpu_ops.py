@@ -260,3 +260,56 @@ def test_error_statuses_on_device():
     st = L.cf_conv3d_fwd(cf.CF_BF16, cf.dims(x.shape), cf._ptr(x), cf._ptr(w), 32, cf.cf_conv(5, 1, 2), cf._ptr(y),
                          None, 0, cf._stream())
     assert st == cf.CF_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------ fused block paths
+FUSED_CASES = [(2, 6, 10, 34, 4, 32), (1, 8, 8, 16, 4, 64), (1, 4, 4, 4, 32, 32), (1, 2, 2, 2, 4, 32)]
+
+
+@pytest.mark.parametrize("shape", FUSED_CASES)
+def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
+    """The fused block forward returns exactly what the two separate entry
+    points return (same accumulation, same bf16 rounding of the conv output,
+    same window rule), and matches the oracle's block with bf16 storage."""
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 7)
+    x = sd.lognormal_poisson_input(rng, rng, (N, D, H, W), Ci) if Ci == 4 else act(rng, (N, D, H, W, Ci), BF)
+    w = weights(rng, Ci, Co, BF)
+    xd, wd = to_dev(x, BF), to_dev(w, BF)
+    P, idx = cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+    P2, idx2 = cf.cf_pool3d_fwd(cf.cf_conv3d_fwd(xd, wd), SLOPE)
+    torch.cuda.synchronize()
+    assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
+    zo = oracle.round_bf16(oracle.conv3d_fwd(x, w))
+    po, io = oracle.lrelu_maxpool_fwd(zo, SLOPE)
+    g = host64(P)
+    assert rel_err(g, po) <= TOL_BF16
+    assert np.mean(idx.cpu().numpy() == io) > 0.995   # rare flips where two window values round alike
+
+
+@pytest.mark.parametrize("shape", FUSED_CASES)
+def test_pool_conv3d_bwd_weight_equals_pool_bwd_then_wgrad(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 11)
+    x = act(rng, (N, D, H, W, Ci), BF)
+    pshape = (N, D // 2, H // 2, W // 2, Co)
+    dp = act(rng, pshape, BF)
+    p = act(rng, pshape, BF)
+    idx = sd.pool_indices(rng, pshape)
+    xd = to_dev(x, BF)
+    dpd, pd = to_dev(dp, BF), to_dev(p, BF)
+    idd = torch.from_numpy(idx).cuda()
+    dw = cf.cf_pool_conv3d_bwd_weight(xd, dpd, pd, idd, SLOPE)
+    dw2 = cf.cf_conv3d_bwd_weight(xd, cf.cf_pool3d_bwd(dpd, pd, idd, SLOPE))
+    torch.cuda.synchronize()
+    assert torch.equal(dw, dw2)
+    dzo = oracle.round_bf16(oracle.maxpool_lrelu_bwd(dp, p, idx, SLOPE))
+    assert rel_err(host64(dw), oracle.conv3d_bwd_weight(x, dzo)) <= 1e-4
+
+
+def test_fused_block_odd_dims_rejected():
+    xd = torch.zeros((1, 5, 4, 4, 4), dtype=BF, device="cuda")
+    wd = torch.zeros((3, 3, 3, 4, 32), dtype=BF, device="cuda")
+    with pytest.raises(cf.CfError) as e:
+        cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+    assert e.value.status == cf.CF_ERR_UNSUPPORTED
