@@ -11,12 +11,12 @@
 // output voxels (MFMA B operand = input halo), K = 27 taps x in-channels.
 //  - A block owns a TD x TH x TW output tile of one sample and BM output
 //    channels.  For every 32-channel input chunk it stages the
-//    (TD+2)(TH+2)(TW+2) halo of the input in LDS once (96-byte voxel stride:
-//    64 bytes of data + 32 bytes of padding; measured on gfx950, this stride
-//    lets the 16-byte per-lane reads of 16 consecutive voxels run at about
-//    310 B/clk per CU, against about 200 for an 80- or 64-byte stride) and
-//    then walks the 27 taps; a tap only shifts the LDS row index, so every B
-//    fragment is one aligned 16-byte LDS read at a compile-time offset.
+//    (TD+2)(TH+2)(TW+2) halo of the input in LDS once and then walks the 27
+//    taps; a tap only shifts the LDS row index, so every B fragment is one
+//    aligned 16-byte LDS read at a compile-time offset.  The LDS voxel stride
+//    is 96 bytes (64 of data + 32 of padding) where it fits: measured on
+//    gfx950, 16-byte per-lane reads of 16 consecutive voxels run at about
+//    310 B/clk per CU with it, against about 200 for a 64- or 80-byte stride.
 //  - A fragments (8 consecutive in-channels of one output channel) are
 //    16-byte global loads from the [tap][co][ci] weight copy, which is small
 //    and stays L2/L1 resident.
@@ -28,13 +28,16 @@ namespace cf {
 
 namespace {
 
-constexpr int LDS_STRIDE = 48;   // bf16 per halo voxel: 32 data + 16 padding (96 B)
-
 // BM output channels per block split over BM/WM waves; TD*TH*TW voxels per
 // block split over VT/WN waves; each wave owns a WM x WN accumulator tile.
-template <int BM, int WN, int TD, int TH, int TW>
+// Waves that share a channel slice load the same weight fragments, so a
+// narrow WM (32) with a wide WN (128) halves the redundant weight traffic
+// against a 64 x 64 wave tile; the halo (B) side is read from LDS.
+// LS: bf16 per halo voxel in LDS.  48 (96 B: 64 B of data + 32 B padding)
+// gives the fastest B reads; 32 (64 B, unpadded) costs some bank conflicts
+// but lets two blocks with a 512-voxel tile share a CU.
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
 struct Tile {
-    static constexpr int WM = BM < 64 ? BM : 64;
     static constexpr int NWM = BM / WM;
     static constexpr int VT = TD * TH * TW;
     static constexpr int NWV = VT / WN;
@@ -45,19 +48,21 @@ struct Tile {
     static constexpr int MI = WM / 16;
     static constexpr int NJ = WN / 16;
     static constexpr int MINB = NW > 4 ? 1 : 2;   // blocks per CU the registers are sized for
+    static constexpr int NE = HV * 4;             // 16-byte halo pieces per chunk
+    static constexpr int IT = (NE + NT - 1) / NT; // halo pieces per thread
     static_assert(VT % WN == 0 && (NW == 4 || NW == 8), "tile");
     static_assert(BM % WM == 0 && WM % 16 == 0 && WN % 16 == 0, "frag");
 };
 
-template <int BM, int WN, int TD, int TH, int TW>
-__global__ __launch_bounds__((Tile<BM, WN, TD, TH, TW>::NT), (Tile<BM, WN, TD, TH, TW>::MINB))
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
+__global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                         uint16_t* __restrict__ Y, float* __restrict__ part,
                         int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
                         int tD, int tH, int tW, int chunks_per_split)
 {
-    using T = Tile<BM, WN, TD, TH, TW>;
-    __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LDS_STRIDE];
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LS];
 
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) % T::NWM;     // co slice of this wave
@@ -70,7 +75,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int td_ = tile % tD;
     const int n = tile / tD;
     const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
-    const int co_base = blockIdx.y * BM + wm * T::WM;
+    const int co_base = blockIdx.y * BM + wm * WM;
     const int nchunks = Cin >> 5;
     const int c_begin = blockIdx.z * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
@@ -81,7 +86,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     for (int j = 0; j < T::NJ; ++j) {
         const int v = wave * WN + 16 * j + l16;
         const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
-        hb[j] = ((td * T::HH + th) * T::HW + tw) * LDS_STRIDE + 8 * lg;
+        hb[j] = ((td * T::HH + th) * T::HW + tw) * LS + 8 * lg;
     }
 
     f32x4 acc[T::MI][T::NJ];
@@ -93,17 +98,31 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int64_t plane = (int64_t)H * W;
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
-        // Stage the input halo of this 32-channel chunk (zero outside the volume).
-        for (int e = threadIdx.x; e < T::HV * 4; e += T::NT) {
-            const int q = e & 3, hv = e >> 2;
-            const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
-            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H && (unsigned)gw < (unsigned)W) {
-                const int64_t vox = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
-                val = *reinterpret_cast<const uint4*>(X + vox * Cin + c * 32 + q * 8);
+        // Stage the input halo of this 32-channel chunk (zero outside the
+        // volume).  All of a thread's global loads are issued before any of
+        // its LDS stores, so their latencies overlap instead of adding up.
+        {
+            const uint16_t* xs = X + (int64_t)n * D * plane * Cin + c * 32;
+            uint4 val[T::IT];
+#pragma unroll
+            for (int it = 0; it < T::IT; ++it) {
+                const int e = threadIdx.x + it * T::NT;
+                const int q = e & 3, hv = e >> 2;
+                const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
+                const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+                val[it] = make_uint4(0u, 0u, 0u, 0u);
+                if ((T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
+                    (unsigned)gw < (unsigned)W) {
+                    const int64_t vox = (int64_t)(gd * H + gh) * W + gw;
+                    val[it] = *reinterpret_cast<const uint4*>(xs + vox * Cin + q * 8);
+                }
             }
-            *reinterpret_cast<uint4*>(halo + hv * LDS_STRIDE + q * 8) = val;
+#pragma unroll
+            for (int it = 0; it < T::IT; ++it) {
+                const int e = threadIdx.x + it * T::NT;
+                if (T::NE % T::NT == 0 || e < T::NE)
+                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS + (e & 3) * 8) = val[it];
+            }
         }
         __syncthreads();
 
@@ -130,7 +149,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
             }
             if (tap + 1 < 27) {
                 const int tn = tap + 1;
-                const int toff = (((tn / 9) * T::HH + (tn / 3) % 3) * T::HW + tn % 3) * LDS_STRIDE;
+                const int toff = (((tn / 9) * T::HH + (tn / 3) % 3) * T::HW + tn % 3) * LS;
 #pragma unroll
                 for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
             }
@@ -190,28 +209,28 @@ __global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __re
     }
 }
 
-struct CfgInfo { int bm, wn, td, th, tw; };
+struct CfgInfo { int bm, wm, wn, td, th, tw, ls; };
 constexpr CfgInfo kCfgs[] = {
-    {128, 64, 4, 4, 16},   // 0
-    {128, 64, 4, 8, 8},    // 1
-    {64, 64, 4, 4, 16},    // 2
-    {64, 64, 4, 8, 8},     // 3
-    {32, 64, 4, 4, 16},    // 4
-    {32, 64, 4, 8, 8},     // 5
-    {16, 64, 4, 4, 16},    // 6
-    {16, 64, 4, 8, 8},     // 7
+    {128, 32, 128, 4, 4, 16, 48},   // 0
+    {128, 32, 128, 4, 8, 8, 48},    // 1
+    {64, 32, 128, 4, 4, 16, 48},    // 2
+    {64, 32, 128, 4, 8, 8, 48},     // 3
+    {32, 32, 128, 4, 8, 16, 32},    // 4
+    {32, 32, 64, 4, 8, 8, 48},      // 5
+    {16, 16, 64, 4, 4, 16, 48},     // 6
+    {16, 16, 64, 4, 8, 8, 48},      // 7
 };
 
-template <int BM, int WN, int TD, int TH, int TW>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x,
                       int cout, int coutpad, int splits, hipStream_t s)
 {
-    using T = Tile<BM, WN, TD, TH, TW>;
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const int nchunks = (int)(x.c / 32);
     const int cps = (nchunks + splits - 1) / splits;
     dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
-    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WN, TD, TH, TW>), grid, dim3(T::NT), 0, s, X, Wk, Y,
+    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WM, WN, TD, TH, TW, LS>), grid, dim3(T::NT), 0, s, X, Wk, Y,
                        splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
                        coutpad, tD, tH, tW, cps);
     return hipGetLastError();
@@ -250,14 +269,14 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
 {
     hipError_t e;
     switch (p.cfg) {
-    case 0: e = launch_cfg<128, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 1: e = launch_cfg<128, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 2: e = launch_cfg<64, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 3: e = launch_cfg<64, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 4: e = launch_cfg<32, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 5: e = launch_cfg<32, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 6: e = launch_cfg<16, 64, 4, 4, 16>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    default: e = launch_cfg<16, 64, 4, 8, 8>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 0: e = launch_cfg<128, 32, 128, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 1: e = launch_cfg<128, 32, 128, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 2: e = launch_cfg<64, 32, 128, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 3: e = launch_cfg<64, 32, 128, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 4: e = launch_cfg<32, 32, 128, 4, 8, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 5: e = launch_cfg<32, 32, 64, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 6: e = launch_cfg<16, 16, 64, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    default: e = launch_cfg<16, 16, 64, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
