@@ -44,21 +44,28 @@ __device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
 // A k-step of 32 voxels is 4 w-octets, one per 16-lane group.  For tap
 // (kd,kh,kw) the X operand of an octet starting at w0 is XT[..][w0+kw ..
 // w0+kw+7]: the lane reads w0..w0+15 once (two aligned 16-byte reads; the
-// row is padded to 24) and forms the three
-// kw-shifted operands by register selection (kw = 0, 2) and a 16-bit funnel
-// shift (kw = 1).  The next box is loaded into registers while the current
-// one is computed (two LDS buffers).
-// Block: 9 waves, wave w owns taps (kd, kh) = (w / 3, w % 3), kw = 0..2,
-// for 32 input channels x BO output channels.
-constexpr int GW_TD = 2, GW_TH = 4, GW_TW = 16;
-constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                 // 128 voxels per box
-constexpr int GW_NOCT = GW_VB / 8;                          // 16 w-octets
+// row is padded to 24) and forms the three kw-shifted operands by register
+// selection (kw = 0, 2) and a 16-bit funnel shift (kw = 1).
+// Block: BO output channels x 32 input channels.  A wave owns two 16-wide
+// output-channel fragments, one 16-wide input-channel fragment and one kd,
+// i.e. 2 x 9 accumulator tiles.  A lane group walks the two w-octets of one
+// halo row together, so the first octet's kw-shift word is the second
+// octet's first word and only the second needs a separate 4-byte read: per
+// 36 MFMAs a wave issues 4 dY reads and 9 X reads.  LDS instruction issue,
+// not bytes, is what limits these loops on gfx950 (a 4-byte and a 16-byte
+// per-lane read cost about the same), so reads per MFMA is the figure that
+// matters.  Box: 4 x 4 x 16 voxels (halo 6 x 6 x 18).  The next box is
+// loaded into registers while the current one is computed.
+constexpr int GW_TD = 4, GW_TH = 4, GW_TW = 16;
+constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                 // 256 voxels per box
+constexpr int GW_NOCT = GW_VB / 8;                          // 32 w-octets
 constexpr int GW_HH = GW_TH + 2;
-constexpr int GW_NR = (GW_TD + 2) * GW_HH;                  // 24 halo rows
+constexpr int GW_NR = (GW_TD + 2) * GW_HH;                  // 36 halo rows
 constexpr int GW_XW = 24;                                   // bf16 per XT row (18 used)
-constexpr int GW_XPL = GW_NR * GW_XW + 112;                 // per-channel plane, 1376 B
-constexpr int GW_DROW = GW_VB + 48;                         // dYT row, 352 B
-constexpr int GW_NT = 9 * 64;
+constexpr int GW_XPL = GW_NR * GW_XW + 16;                  // per-channel plane: 1760 B (odd multiple of 32)
+constexpr int GW_DROW = GW_VB + 16;                         // dYT row: 544 B (odd multiple of 32)
+constexpr int GW_NXB = GW_NR * 2 * 4;                       // X blocks of 8 voxels: rows x {w 0-7, 8-15} x 4 ci-groups
+constexpr int GW_NXE = GW_NR * 4;                           // X edge blocks (w 16-17): rows x 4 ci-groups
 
 // Box coordinates (sample, box d, box h, box w) in row-major box order.
 // Decoded once per block, then advanced one box at a time in 32-bit
@@ -110,162 +117,220 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 }
 
 template <int BO>
-struct GwBox {
-    static constexpr int NDB = GW_NOCT * (BO / 8);           // dY blocks per box
-    static constexpr int NXB = GW_NR * 3 * 4;                // X blocks: rows x {0-7, 8-15, 16-17} x 4 ci-groups
+struct GwCfg {
+    static constexpr int NCP = BO / 32;                     // output-channel fragment pairs
+    static constexpr int NW = NCP * 2 * 3;                  // waves: co pair x ci fragment x kd
+    static constexpr int NT = NW * 64;
+    static constexpr int NDB = GW_NOCT * (BO / 8);          // dY blocks of 8 voxels x 8 co
+    static constexpr int NB = NDB + GW_NXB;                 // full 8-voxel blocks per box
+    static constexpr int KB = (NB + NT - 1) / NT;           // full blocks per thread
+    // Waves per SIMD the registers are sized for (the second launch bound):
+    // three for the 12-wave block; two for the 6-wave block, whose two
+    // staging blocks per thread do not fit in a third of the register file.
+    static constexpr int WPE = BO == 64 ? 3 : 2;
+    static_assert(GW_NXE <= NT, "one edge block per thread");
 };
 
 template <int BO>
-__global__ __launch_bounds__(GW_NT, 1)
+__global__ __launch_bounds__(GwCfg<BO>::NT, GwCfg<BO>::WPE)
 void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY,
                        float* __restrict__ part, int N, int D, int H, int W, int Cin, int Cout,
-                       int bD, int bH, int bW, int64_t nbox, int boxes_per_split)
+                       int bD, int bH, int bW, int nco, int nci, int64_t nbox, int boxes_per_split)
 {
-    constexpr int CI = BO / 16;
-    using G = GwBox<BO>;
-    static_assert(G::NDB + G::NXB <= GW_NT, "one block per thread");
-    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * GW_XPL];
-    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * GW_DROW];
+    using G = GwCfg<BO>;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[32 * GW_XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[BO * GW_DROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int kd = wave / 3, kh = wave % 3;
-    const int co0 = blockIdx.x * BO, ci0 = blockIdx.y * 32;
-    const int split = blockIdx.z;
+    const int kd = wave % 3, jf = (wave / 3) % 2, cp = wave / 6;
+    // Blocks that share a voxel range (all channel blocks of one split) get
+    // consecutive logical ids and therefore the same XCD and L2.
+    uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const int cob = (int)(id % (uint32_t)nco); id /= (uint32_t)nco;
+    const int cib = (int)(id % (uint32_t)nci);
+    const int split = (int)(id / (uint32_t)nci);
+    const int co0 = cob * BO, ci0 = cib * 32;
     const int64_t plane = (int64_t)H * W;
 
-    // The block this thread stages: dY block, X block, or none.
-    const bool is_dy = tid < G::NDB;
-    const bool is_x = !is_dy && tid < G::NDB + G::NXB;
-    // Lane order: 16 consecutive lanes store 16 consecutive 16-byte columns
-    // of the same channel rows (octets for dY, (row, slot) for X).
-    int oct = 0, grp = 0, row = 0, slot = 0;
-    if (is_dy) { oct = tid % GW_NOCT; grp = tid / GW_NOCT; }
-    if (is_x) { const int t = tid - G::NDB; grp = t / (GW_NR * 3); slot = (t % (GW_NR * 3)) % 3; row = (t % (GW_NR * 3)) / 3; }
-    const int nvl = is_x && slot == 2 ? 2 : 8;                // voxels in this block
+    // Staging: full blocks t = tid + k * NT (dY blocks first, then X blocks
+    // for halo w 0-15); edge blocks (X, halo w 16-17) for tid < GW_NXE.
+    // 16 consecutive lanes store 16 consecutive 16-byte columns of the same
+    // channel rows.
+    uint4 u[G::KB][8];
+    uint4 ue[2];
+    const bool has_edge = tid < GW_NXE;
+    const int erow = tid % GW_NR, egrp = tid / GW_NR;
 
-    auto load_box = [&](const BoxPos& bp, uint4 (&u)[8]) {
+    auto load_box = [&](const BoxPos& bp) {
         const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
+        const int64_t sbase = (int64_t)n * D;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) u[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (is_dy) {
-            const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
-            const int gd = bd * GW_TD + td, gh = bh * GW_TH + th;
-            if (gd < D && gh < H) {
-                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+        for (int k = 0; k < G::KB; ++k) {
+            const int t = tid + k * G::NT;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int gw = bw * GW_TW + w0 + j;
-                    if (gw < W) u[j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw) * Cout + co0 + grp * 8);
+            for (int j = 0; j < 8; ++j) u[k][j] = make_uint4(0u, 0u, 0u, 0u);
+            if (t < G::NDB) {
+                const int oct = t % GW_NOCT, grp = t / GW_NOCT;
+                const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
+                const int gd = bd * GW_TD + td, gh = bh * GW_TH + th;
+                if (gd < D && gh < H) {
+                    const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int gw = bw * GW_TW + w0 + j;
+                        if (gw < W) u[k][j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw) * Cout + co0 + grp * 8);
+                    }
+                }
+            } else if (t < G::NB) {
+                const int x = t - G::NDB;
+                const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
+                const int row = rem / 2, slot = rem % 2;
+                const int hd = row / GW_HH, hh = row % GW_HH;
+                const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
+                if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
+                    const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int gw = bw * GW_TW + 8 * slot + j - 1;
+                        if ((unsigned)gw < (unsigned)W)
+                            u[k][j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + grp * 8);
+                    }
                 }
             }
-        } else if (is_x) {
-            const int hd = row / GW_HH, hh = row % GW_HH;
+        }
+        ue[0] = ue[1] = make_uint4(0u, 0u, 0u, 0u);
+        if (has_edge) {
+            const int hd = erow / GW_HH, hh = erow % GW_HH;
             const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
             if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
-                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+                const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int gw = bw * GW_TW + 8 * slot + j - 1;
-                    if (j < nvl && (unsigned)gw < (unsigned)W)
-                        u[j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + grp * 8);
+                for (int j = 0; j < 2; ++j) {
+                    const int gw = bw * GW_TW + 15 + j;             // halo w = 16 + j
+                    if (gw < W) ue[j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + egrp * 8);
                 }
             }
         }
     };
-    auto store_box = [&](int buf, const uint4 (&u)[8]) {
-        uint4 t[8];
-        transpose8x8(u, t);
-        if (is_dy) {
+    auto store_box = [&]() {
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * GW_DROW + oct * 8]) = t[c];
-        } else if (is_x) {
+        for (int k = 0; k < G::KB; ++k) {
+            const int t = tid + k * G::NT;
+            if (t >= G::NB) continue;
+            uint4 tr[8];
+            transpose8x8(u[k], tr);
+            if (t < G::NDB) {
+                const int oct = t % GW_NOCT, grp = t / GW_NOCT;
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<uint4*>(&dt[(grp * 8 + c) * GW_DROW + oct * 8]) = tr[c];
+            } else {
+                const int x = t - G::NDB;
+                const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
+                const int row = rem / 2, slot = rem % 2;
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<uint4*>(&xt[(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8]) = tr[c];
+            }
+        }
+        if (has_edge) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                uint16_t* dst = &xt[buf][(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8];
-                if (slot < 2) *reinterpret_cast<uint4*>(dst) = t[c];
-                else *reinterpret_cast<uint32_t*>(dst) = t[c].x;
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                const int h = c >> 1;
+                const uint32_t w0v = h == 0 ? ue[0].x : h == 1 ? ue[0].y : h == 2 ? ue[0].z : ue[0].w;
+                const uint32_t w1v = h == 0 ? ue[1].x : h == 1 ? ue[1].y : h == 2 ? ue[1].z : ue[1].w;
+                *reinterpret_cast<uint32_t*>(&xt[(egrp * 8 + c) * GW_XPL + erow * GW_XW + 16]) =
+                    __builtin_amdgcn_perm(w1v, w0v, sel);
             }
         }
     };
 
-    f32x4 acc[3][CI][2];
+    f32x4 acc[2][3][3];      // [co fragment][kh][kw]
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < CI; ++i) {
-            acc[t][i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[t][i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) acc[c][kh][kw] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int64_t b_begin = (int64_t)split * boxes_per_split;
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
-    uint4 u[8];
     BoxPos bp = box_decode(b_begin, bD, bH, bW);
-    load_box(bp, u);
-    store_box(0, u);
+    load_box(bp);
+    store_box();
     __syncthreads();
-    int buf = 0;
+    const uint16_t* drow = dt + (32 * cp + l16) * GW_DROW;
+    const uint16_t* xpl = xt + (16 * jf + l16) * GW_XPL + kd * GW_HH * GW_XW;
     for (int64_t box = b_begin; box < b_end; ++box) {
         const bool more = box + 1 < b_end;
         if (more) {
             bp = box_next(bp, bD, bH, bW);
-            load_box(bp, u);                   // in flight during this box's MFMAs
+            load_box(bp);                      // in flight during this box's MFMAs
         }
-        const uint16_t* xb = xt[buf];
-        const uint16_t* db = dt[buf];
+#pragma unroll 1
+        for (int s2 = 0; s2 < GW_TD; ++s2) {
+            // lane group lg takes box row (td, th) = (s2, lg), both w-octets
+            const int o0 = (s2 * GW_TH + lg) * 2;           // octet index of w0 = 0
+            bf16x8 a[2][2];                                 // [co fragment][octet]
 #pragma unroll
-        for (int s = 0; s < GW_NOCT / 4; ++s) {
-            const int o = 4 * s + lg;                      // this lane group's octet
-            const int td = o / (GW_TH * 2), th = (o / 2) % GW_TH, w0 = (o & 1) * 8;
-            const int r = (td + kd) * GW_HH + th + kh;
-            bf16x8 a[CI];
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int i = 0; i < CI; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(db + (16 * i + l16) * GW_DROW + o * 8);
+                for (int h = 0; h < 2; ++h)
+                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (o0 + h) * 8);
+            const uint16_t* xr = xpl + (s2 * GW_HH + lg) * GW_XW;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const uint16_t* xp = xb + (16 * jj + l16) * GW_XPL + r * GW_XW + w0;
-                const uint4 q = *reinterpret_cast<const uint4*>(xp);
-                const uint32_t e = reinterpret_cast<const uint4*>(xp)[1].x;   // aligned 16-byte read, w0+8..9 used
-                const uint4 s1 = make_uint4(__builtin_amdgcn_alignbit(q.y, q.x, 16), __builtin_amdgcn_alignbit(q.z, q.y, 16),
-                                            __builtin_amdgcn_alignbit(q.w, q.z, 16), __builtin_amdgcn_alignbit(e, q.w, 16));
-                const bf16x8 b0 = __builtin_bit_cast(bf16x8, q);
-                const bf16x8 b1 = __builtin_bit_cast(bf16x8, s1);
-                const bf16x8 b2 = __builtin_bit_cast(bf16x8, make_uint4(q.y, q.z, q.w, e));
+            for (int kh = 0; kh < 3; ++kh) {
+                const uint16_t* xp = xr + kh * GW_XW;
+                const uint4 q0 = *reinterpret_cast<const uint4*>(xp);
+                const uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
+                const uint32_t e1 = *reinterpret_cast<const uint32_t*>(xp + 16);   // halo w 16-17
+                const uint32_t e0 = q1.x;                                          // halo w 8-9
+                bf16x8 b[2][3];                                                    // [octet][kw]
+                b[0][0] = __builtin_bit_cast(bf16x8, q0);
+                b[0][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q0.y, q0.x, 16),
+                                                                __builtin_amdgcn_alignbit(q0.z, q0.y, 16),
+                                                                __builtin_amdgcn_alignbit(q0.w, q0.z, 16),
+                                                                __builtin_amdgcn_alignbit(e0, q0.w, 16)));
+                b[0][2] = __builtin_bit_cast(bf16x8, make_uint4(q0.y, q0.z, q0.w, e0));
+                b[1][0] = __builtin_bit_cast(bf16x8, q1);
+                b[1][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q1.y, q1.x, 16),
+                                                                __builtin_amdgcn_alignbit(q1.z, q1.y, 16),
+                                                                __builtin_amdgcn_alignbit(q1.w, q1.z, 16),
+                                                                __builtin_amdgcn_alignbit(e1, q1.w, 16)));
+                b[1][2] = __builtin_bit_cast(bf16x8, make_uint4(q1.y, q1.z, q1.w, e1));
 #pragma unroll
-                for (int i = 0; i < CI; ++i) {
-                    acc[0][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b0, acc[0][i][jj], 0, 0, 0);
-                    acc[1][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b1, acc[1][i][jj], 0, 0, 0);
-                    acc[2][i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2, acc[2][i][jj], 0, 0, 0);
-                }
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[h][kw], acc[c][kh][kw], 0, 0, 0);
             }
         }
         if (more) {
-            store_box(buf ^ 1, u);
             __syncthreads();
-            buf ^= 1;
+            store_box();
+            __syncthreads();
         }
     }
 
-    // partial[split][tap][ci][co]; lane holds co rows 4 lg..4 lg+3 of column ci = l16
+    // partial[split][tap][ci][co]; lane holds co rows 4 lg..4 lg+3 of column ci
     const int64_t dwsize = (int64_t)27 * Cin * Cout;
+    const int ci = ci0 + 16 * jf + l16;
+    float* out = part + split * dwsize + (int64_t)ci * Cout + co0 + 32 * cp + 4 * lg;
 #pragma unroll
-    for (int kw = 0; kw < 3; ++kw) {
-        const int tap = (kd * 3 + kh) * 3 + kw;
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < CI; ++i)
+        for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int ci = ci0 + 16 * jj + l16;
-                const int co = co0 + 16 * i + 4 * lg;
-                const f32x4 r = acc[kw][i][jj];
-                *reinterpret_cast<float4*>(part + split * dwsize + ((int64_t)tap * Cin + ci) * Cout + co) =
-                    make_float4(r[0], r[1], r[2], r[3]);
+            for (int kw = 0; kw < 3; ++kw) {
+                const int tap = (kd * 3 + kh) * 3 + kw;
+                const f32x4 r = acc[c][kh][kw];
+                *reinterpret_cast<float4*>(out + (int64_t)tap * Cin * Cout + 16 * c) = make_float4(r[0], r[1], r[2], r[3]);
             }
-    }
 }
 
 // --------------------------------------------------------- Cin == 4 layer
@@ -585,11 +650,13 @@ WgradPlan plan_wgrad(const cf_dims& x, int cout)
         p.vox_per_split = per;   // boxes per split
     } else {
         p.kind = 0;
-        const int bo = 32;
+        const int bo = cout % 64 == 0 ? 64 : 32;
         const int64_t nbox = x.n * ((x.d + GW_TD - 1) / GW_TD) * ((x.h + GW_TH - 1) / GW_TH) *
                              ((x.w + GW_TW - 1) / GW_TW);
         const int64_t outer = (int64_t)(cout / bo) * (x.c / 32);
-        int64_t want = (512 + outer - 1) / outer;
+        // one round of blocks over the 256 CUs (one 12-wave or two 6-wave blocks per CU)
+        const int64_t conc = bo == 64 ? 256 : 512;
+        int64_t want = (conc + outer - 1) / outer;
         int64_t cap = (int64_t)(64ll << 20) / dw_bytes;   // bound the partial buffer to ~64 MiB
         if (cap < 1) cap = 1;
         if (want > cap) want = cap;
@@ -617,10 +684,18 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
         const int bD = (int)((x.d + GW_TD - 1) / GW_TD), bH = (int)((x.h + GW_TH - 1) / GW_TH),
                   bW = (int)((x.w + GW_TW - 1) / GW_TW);
         const int64_t nbox = x.n * bD * bH * bW;
-        const int bo = 32;
-        dim3 grid((unsigned)(cout / bo), (unsigned)(x.c / 32), (unsigned)p.splits);
-        hipLaunchKernelGGL(wgrad_mfma_kernel<32>, grid, dim3(GW_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
-                               (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nbox, (int)p.vox_per_split);
+        const int nci = (int)(x.c / 32);
+        if (cout % 64 == 0) {
+            const int nco = cout / 64;
+            hipLaunchKernelGGL(wgrad_mfma_kernel<64>, dim3((unsigned)((int64_t)nco * nci * p.splits)),
+                               dim3(GwCfg<64>::NT), 0, s, X, dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w,
+                               (int)x.c, cout, bD, bH, bW, nco, nci, nbox, (int)p.vox_per_split);
+        } else {
+            const int nco = cout / 32;
+            hipLaunchKernelGGL(wgrad_mfma_kernel<32>, dim3((unsigned)((int64_t)nco * nci * p.splits)),
+                               dim3(GwCfg<32>::NT), 0, s, X, dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w,
+                               (int)x.c, cout, bD, bH, bW, nco, nci, nbox, (int)p.vox_per_split);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
