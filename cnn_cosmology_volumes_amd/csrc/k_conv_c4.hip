@@ -55,13 +55,27 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         for (int i = 0; i < MI; ++i)
             afr[s][i] = *reinterpret_cast<const bf16x8*>(Wk + (int64_t)(co_base + 16 * i + l16) * 128 + 32 * s + 8 * lg);
 
-    for (int hv = threadIdx.x; hv < HV; hv += NT) {
-        const int hw_ = hv % HW, hh_ = (hv / HW) % HH, hd_ = hv / (HW * HH);
-        const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-        uint2 v = make_uint2(0u, 0u);
-        if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H && (unsigned)gw < (unsigned)W)
-            v = *reinterpret_cast<const uint2*>(X + (((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw) * 4);
-        halo[hv] = v;
+    // Halo staging: every global load of this thread is issued before its
+    // LDS stores, so the load latencies overlap.
+    {
+        constexpr int IT = (HV + NT - 1) / NT;
+        const uint16_t* xs = X + (int64_t)n * D * plane * 4;
+        uint2 v[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int hv = threadIdx.x + it * NT;
+            const int hw_ = hv % HW, hh_ = (hv / HW) % HH, hd_ = hv / (HW * HH);
+            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+            v[it] = make_uint2(0u, 0u);
+            if ((HV % NT == 0 || hv < HV) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
+                (unsigned)gw < (unsigned)W)
+                v[it] = *reinterpret_cast<const uint2*>(xs + ((int64_t)(gd * H + gh) * W + gw) * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int hv = threadIdx.x + it * NT;
+            if (HV % NT == 0 || hv < HV) halo[hv] = v[it];
+        }
     }
     __syncthreads();
 

@@ -356,6 +356,7 @@ constexpr int C4_NT = 256;
 constexpr int C4_NDB = C4_NOCT * 4;                        // dY blocks: 32 octets x 4 groups of 8 co
 constexpr int C4_NXB = C4_NR * 3;                          // X blocks: rows x {0-7, 8-15, 16-17}
 constexpr int C4_NACC = 2 * 3 * 3;                         // co frags x pair frags x kw
+constexpr int C4_NPV = (C4_TD / 2) * (C4_TH / 2) * (C4_TW / 2);   // 32 pooled voxels per box
 
 template <bool FUSED>
 __global__ __launch_bounds__(C4_NT, 2)
@@ -368,6 +369,9 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) uint16_t xt[2][4 * C4_XPL];
     __shared__ __attribute__((aligned(16))) uint16_t dt[2][CO * C4_DROW];
     __shared__ __attribute__((aligned(16))) float red[64 * C4_NACC * 4];
+    // fused: the box's gated pooled gradient (bf16) and window indices, [pooled voxel][co]
+    __shared__ __attribute__((aligned(16))) uint16_t gtile[FUSED ? C4_NPV * CO : 8];
+    __shared__ __attribute__((aligned(16))) uint8_t itile[FUSED ? C4_NPV * CO : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -376,50 +380,60 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     const int64_t plane = (int64_t)H * W;
     const int Dp = D / 2, Hp = H / 2, Wp = W / 2;
 
-    static_assert(C4_NDB + C4_NXB <= C4_NT, "one block per thread");
-    const bool is_dy = tid < C4_NDB;
-    const bool is_x = !is_dy && tid < C4_NDB + C4_NXB;
-    int oct = 0, grp = 0, row = 0, slot = 0;
-    if (is_dy) { oct = tid % C4_NOCT; grp = tid / C4_NOCT; }
-    if (is_x) { const int t = tid - C4_NDB; row = t / 3; slot = t % 3; }
-    const int nvl = is_x && slot == 2 ? 2 : 8;
+    // Staging.  dY: 256 tasks of 8 voxels (one w-octet) x 4 channels, one
+    // per thread, so every lane of every wave shares the dY work and no wave
+    // diverges on it.  X: 108 tasks (halo row x {w 0-7, 8-15, 16-17}) on
+    // threads 128-235.  Fused: the box's 32 pooled voxels x 32 channels of
+    // dP, P and the window indices are loaded once with 16-byte loads
+    // (threads 0-127: dP and P of one pooled voxel x 8 channels, gated right
+    // away; threads 128-191: 16 indices), staged in LDS, and every thread
+    // then rebuilds its dY task from there.
+    static_assert(C4_NOCT * 8 == C4_NT && C4_NXB <= 128 && C4_NPV * 4 == 128, "task layout");
+    const int oct = tid % C4_NOCT, cg = tid / C4_NOCT;       // dY: octet, 4-channel group
+    const int xtask = tid - 128;
+    const bool is_x = xtask >= 0 && xtask < C4_NXB;
+    const int row = xtask / 3, slot = xtask % 3;
+    const int nvl = slot == 2 ? 2 : 8;
+    const int td_o = oct / (C4_TH * 2), th_o = (oct / 2) % C4_TH, w0_o = (oct & 1) * 8;
+    // fused pooled loads: pooled voxel pv of the box (2 x 2 x 8), channel offset
+    const bool is_pg = FUSED && tid < 128;
+    const bool is_pi = FUSED && tid >= 128 && tid < 192;
+    const int pv = is_pg ? tid >> 2 : (tid - 128) >> 1;
+    const int pc = is_pg ? (tid & 3) * 8 : ((tid - 128) & 1) * 16;
 
-    // staging registers (dY block: 8 voxels x 8 co; fused: 4 pooled voxels x 8 co of dP, P, idx)
-    uint4 u[8];
-    uint2 ui[4];
+    // staging registers: non-fused dY 8 voxels x 4 co; fused pooled dP/P (8 co)
+    // or 16 indices; ux: X 8 voxels x 4 ci
+    uint2 ud[8];
+    uint4 upd, upp;
+    uint2 ux[8];
 
     auto load_box = [&](const BoxPos& bp) {
         const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) u[j] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < 8; ++j) { ud[j] = make_uint2(0u, 0u); ux[j] = make_uint2(0u, 0u); }
+        upd = upp = make_uint4(0u, 0u, 0u, 0u);
+        if (!FUSED) {
+            const int gd = bd * C4_TD + td_o, gh = bh * C4_TH + th_o, gw0 = bw * C4_TW + w0_o;
+            if (gd < D && gh < H) {
+                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ui[j] = make_uint2(0u, 0u);
-        if (is_dy) {
-            const int td = oct / (C4_TH * 2), th = (oct / 2) % C4_TH, w0 = (oct & 1) * 8;
-            const int gd = bd * C4_TD + td, gh = bh * C4_TH + th, gw0 = bw * C4_TW + w0;
-            if (!FUSED) {
-                if (gd < D && gh < H) {
-                    const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (gw0 + j < W) u[j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw0 + j) * CO + grp * 8);
-                }
-            } else {
-                if (gd < D && gh < H) {
-                    const int64_t prow = ((int64_t)n * Dp + gd / 2) * Hp + gh / 2;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int pw = gw0 / 2 + j;
-                        if (pw < Wp) {
-                            const int64_t o = (prow * Wp + pw) * CO + grp * 8;
-                            u[j] = *reinterpret_cast<const uint4*>(dP + o);
-                            u[4 + j] = *reinterpret_cast<const uint4*>(Pv + o);
-                            ui[j] = *reinterpret_cast<const uint2*>(pidx + o);
-                        }
-                    }
+                for (int j = 0; j < 8; ++j)
+                    if (gw0 + j < W) ud[j] = *reinterpret_cast<const uint2*>(dY + (rowv + gw0 + j) * CO + cg * 4);
+            }
+        } else if (is_pg || is_pi) {
+            const int pd = bd * (C4_TD / 2) + pv / 16, ph = bh * (C4_TH / 2) + (pv / 8) % 2,
+                      pw = bw * (C4_TW / 2) + pv % 8;
+            if (pd < Dp && ph < Hp && pw < Wp) {
+                const int64_t o = ((((int64_t)n * Dp + pd) * Hp + ph) * Wp + pw) * CO + pc;
+                if (is_pg) {
+                    upd = *reinterpret_cast<const uint4*>(dP + o);
+                    upp = *reinterpret_cast<const uint4*>(Pv + o);
+                } else {
+                    upd = *reinterpret_cast<const uint4*>(pidx + o);
                 }
             }
-        } else if (is_x) {
+        }
+        if (is_x) {
             const int hd = row / C4_HH, hh = row % C4_HH;
             const int gd = bd * C4_TD + hd - 1, gh = bh * C4_TH + hh - 1;
             if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
@@ -427,71 +441,94 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int gw = bw * C4_TW + 8 * slot + j - 1;
-                    if (j < nvl && (unsigned)gw < (unsigned)W) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(X + (rowv + gw) * 4);
-                        u[j] = make_uint4(v.x, v.y, 0u, 0u);
-                    }
+                    if (j < nvl && (unsigned)gw < (unsigned)W) ux[j] = *reinterpret_cast<const uint2*>(X + (rowv + gw) * 4);
                 }
             }
         }
     };
 
-    auto store_box = [&](int buf) {
-        if (is_dy) {
-            uint4 t[8];
-            if (!FUSED) {
-                transpose8x8(u, t);
-            } else {
-                // window position of voxel w0+j inside its pooled window: a*4 + b*2 + (j & 1)
-                const int td = oct / (C4_TH * 2), th = (oct / 2) % C4_TH;
-                const uint32_t pos_ab = (uint32_t)((td & 1) * 4 + (th & 1) * 2);
-                uint32_t g2[4][4];     // [pooled voxel j][dword c/2]: gated gradient, bf16 pairs
+    // 8 voxels x 4 channels (uint2 per voxel) -> 4 channel rows of 8 voxels
+    auto transpose8x4 = [](const uint2 (&v)[8], uint4 (&t)[4]) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t gd4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
-                    const uint32_t pv4[4] = {u[4 + j].x, u[4 + j].y, u[4 + j].z, u[4 + j].w};
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t d[4];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        float gl = __uint_as_float(gd4[k] << 16), gh_ = __uint_as_float(gd4[k] & 0xffff0000u);
-                        const float pl = __uint_as_float(pv4[k] << 16), ph = __uint_as_float(pv4[k] & 0xffff0000u);
-                        gl = pl > 0.f ? gl : slope * gl;
-                        gh_ = ph > 0.f ? gh_ : slope * gh_;
-                        g2[j][k] = pack_bf16x2(gl, gh_);
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    uint32_t d[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {          // voxels 2k, 2k+1 share pooled voxel k
-                        const uint32_t ib = ((c < 4 ? ui[k].x : ui[k].y) >> (8 * (c & 3))) & 0xffu;
-                        const uint32_t gv = (g2[k][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-                        const uint32_t lo = ib == pos_ab ? gv : 0u;
-                        const uint32_t hi = ib == pos_ab + 1u ? gv : 0u;
-                        d[k] = lo | (hi << 16);
-                    }
-                    t[c] = make_uint4(d[0], d[1], d[2], d[3]);
-                }
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t wl = (c >> 1) ? v[2 * k].y : v[2 * k].x;
+                const uint32_t wh = (c >> 1) ? v[2 * k + 1].y : v[2 * k + 1].x;
+                d[k] = __builtin_amdgcn_perm(wh, wl, sel);
             }
+            t[c] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+    };
+
+    auto store_box = [&](int buf) {
+        if (!FUSED) {
+            uint4 t[4];
+            transpose8x4(ud, t);
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * C4_DROW + oct * 8]) = t[c];
-        } else if (is_x) {
-            // transpose 8 voxels x 4 channels
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<uint4*>(&dt[buf][(cg * 4 + c) * C4_DROW + oct * 8]) = t[c];
+        } else {
+            if (is_pg) {
+                // dZ of the window maximum = dP * (P > 0 ? 1 : slope), rounded to bf16
+                const uint32_t gd4[4] = {upd.x, upd.y, upd.z, upd.w};
+                const uint32_t pv4[4] = {upp.x, upp.y, upp.z, upp.w};
+                uint32_t g[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float gl = __uint_as_float(gd4[m] << 16), gh_ = __uint_as_float(gd4[m] & 0xffff0000u);
+                    const float pl = __uint_as_float(pv4[m] << 16), ph = __uint_as_float(pv4[m] & 0xffff0000u);
+                    gl = pl > 0.f ? gl : slope * gl;
+                    gh_ = ph > 0.f ? gh_ : slope * gh_;
+                    g[m] = pack_bf16x2(gl, gh_);
+                }
+                *reinterpret_cast<uint4*>(&gtile[pv * CO + pc]) = make_uint4(g[0], g[1], g[2], g[3]);
+            } else if (is_pi) {
+                *reinterpret_cast<uint4*>(&itile[pv * CO + pc]) = upd;
+            }
+        }
+        if (is_x) {
+            uint4 tx[4];
+            transpose8x4(ux, tx);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                uint16_t* dst = &xt[buf][c * C4_XPL + row * C4_XW + slot * 8];
+                if (slot < 2) *reinterpret_cast<uint4*>(dst) = tx[c];
+                else *reinterpret_cast<uint32_t*>(dst) = tx[c].x;
+            }
+        }
+        if (FUSED) {
+            __syncthreads();
+            // Rebuild this thread's 8 voxels x 4 channels of dY: a voxel gets the
+            // gated gradient of its pooled voxel where the window index names it.
+            const uint32_t pos_ab = (uint32_t)((td_o & 1) * 4 + (th_o & 1) * 2);
+            const int pv0 = ((td_o >> 1) * 2 + (th_o >> 1)) * 8 + w0_o / 2;
+            uint4 t[4];
+            uint2 gq[4];
+            uint32_t iq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                gq[k] = *reinterpret_cast<const uint2*>(&gtile[(pv0 + k) * CO + cg * 4]);
+                iq[k] = *reinterpret_cast<const uint32_t*>(&itile[(pv0 + k) * CO + cg * 4]);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
                 uint32_t d[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t wl = (c >> 1) ? u[2 * k].y : u[2 * k].x;
-                    const uint32_t wh = (c >> 1) ? u[2 * k + 1].y : u[2 * k + 1].x;
-                    d[k] = __builtin_amdgcn_perm(wh, wl, sel);
+                for (int k = 0; k < 4; ++k) {          // voxels 2k, 2k+1 share pooled voxel k
+                    const uint32_t ib = (iq[k] >> (8 * c)) & 0xffu;
+                    const uint32_t gv = ((c >> 1 ? gq[k].y : gq[k].x) >> (16 * (c & 1))) & 0xffffu;
+                    const uint32_t lo = ib == pos_ab ? gv : 0u;
+                    const uint32_t hi = ib == pos_ab + 1u ? gv : 0u;
+                    d[k] = lo | (hi << 16);
                 }
-                uint16_t* dst = &xt[buf][c * C4_XPL + row * C4_XW + slot * 8];
-                if (slot < 2) *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
-                else *reinterpret_cast<uint32_t*>(dst) = d[0];
+                t[c] = make_uint4(d[0], d[1], d[2], d[3]);
             }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<uint4*>(&dt[buf][(cg * 4 + c) * C4_DROW + oct * 8]) = t[c];
         }
     };
 
