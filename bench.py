@@ -37,6 +37,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-ops", action="store_true", help="skip the per-entry-point timing")
+    ap.add_argument("--profile-op", default=None,
+                    help="only run the named entry point of the per-entry-point timing --op-reps times "
+                         "(for rocprofv3 passes), print nothing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --op-reps times (the reference "
+                         "kernel that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -72,17 +78,26 @@ def time_region(torch, fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
-def op_timings(torch, cf, c, dev, reps):
-    """Per-entry-point times of the step's conv and pool work at the
-    workload's shapes (bf16), each on the current stream.  The first block
-    runs fused exactly as in the step: conv + leaky ReLU + pool forward, and
-    pool backward + backward-weight, both counted as conv work."""
-    stream = torch.cuda.current_stream()
+def build_ops(torch, cf, c, dev):
+    """The step's conv and pool entry points at the workload's shapes (bf16),
+    each as a callable with its algorithmic flops and HBM bytes.  The first
+    block runs fused exactly as in the step: conv + leaky ReLU + pool
+    forward, and pool backward + backward-weight, both counted as conv work.
+    Algorithmic bytes: every operand read once and every result written
+    once (conv: input, weights, output; backward-weight: input, output
+    gradient, fp32 weight gradient; pool: input, output, indices)."""
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     B, S, cin = c.batch, c.in_size, c.in_channels
     ops = []
+
+    def ws_for(X, f, pas):
+        return torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, pas)), dtype=torch.uint8,
+                           device=dev)
+
     for l, f in enumerate(c.filters):
+        # every tensor of this layer is bound as a default argument, so each
+        # callable keeps its own layer's tensors alive
         X = torch.randn((B, S, S, S, cin), generator=g, device=dev).to(torch.bfloat16)
         W = (torch.randn((3, 3, 3, cin, f), generator=g, device=dev) * 0.05).to(torch.bfloat16)
         P = torch.randn((B, S // 2, S // 2, S // 2, f), generator=g, device=dev).to(torch.bfloat16)
@@ -93,47 +108,75 @@ def op_timings(torch, cf, c, dev, reps):
         xb, zb, wb = X.numel() * 2, nvox * f * 2, 27 * cin * f * 2
         pb, ib = P.numel() * 2, P.numel()
         if l == 0:
-            wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_POOL_FWD)),
-                              dtype=torch.uint8, device=dev)
-            wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_POOL_CONV_BWD_WEIGHT)),
-                              dtype=torch.uint8, device=dev)
-            Po = torch.empty_like(P)
-            ido = torch.empty_like(idx)
+            wsf = ws_for(X, f, cf.CF_CONV_POOL_FWD)
+            wsw = ws_for(X, f, cf.CF_POOL_CONV_BWD_WEIGHT)
+            Po, ido = torch.empty_like(P), torch.empty_like(idx)
             ops.append(dict(name="block1_conv_pool_fwd", kind="conv", flops=flops, bytes=xb + wb + pb + ib,
-                            ms=time_region(torch, lambda: cf.cf_conv3d_pool_fwd(X, W, 0.3, Po, ido, ws=wsf), reps,
-                                           stream)))
+                            fn=lambda X=X, W=W, Po=Po, ido=ido, ws=wsf: cf.cf_conv3d_pool_fwd(X, W, 0.3, Po, ido, ws=ws)))
             ops.append(dict(name="block1_pool_bwd_weight", kind="conv", flops=flops,
                             bytes=xb + 2 * pb + ib + 27 * cin * f * 4,
-                            ms=time_region(torch, lambda: cf.cf_pool_conv3d_bwd_weight(X, P, P, idx, 0.3, dW, ws=wsw),
-                                           reps, stream)))
-            del wsf, wsw, Po, ido
+                            fn=lambda X=X, P=P, idx=idx, dW=dW, ws=wsw:
+                            cf.cf_pool_conv3d_bwd_weight(X, P, P, idx, 0.3, dW, ws=ws)))
         else:
             dZ = torch.randn((B, S, S, S, f), generator=g, device=dev).to(torch.bfloat16)
-            Z = torch.empty_like(dZ)
-            dX = torch.empty_like(X)
-            wsf = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_FWD)),
-                              dtype=torch.uint8, device=dev)
-            wsd = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_DATA)),
-                              dtype=torch.uint8, device=dev)
-            wsw = torch.empty(max(1, cf.cf_conv3d_workspace_size(cf.CF_BF16, X.shape, f, cf.CF_CONV_BWD_WEIGHT)),
-                              dtype=torch.uint8, device=dev)
+            Z, dX = torch.empty_like(dZ), torch.empty_like(X)
+            wsf = ws_for(X, f, cf.CF_CONV_FWD)
+            wsd = ws_for(X, f, cf.CF_CONV_BWD_DATA)
+            wsw = ws_for(X, f, cf.CF_CONV_BWD_WEIGHT)
             ops.append(dict(name="conv%d_fwd" % (l + 1), kind="conv", flops=flops, bytes=xb + wb + zb,
-                            ms=time_region(torch, lambda: cf.cf_conv3d_fwd(X, W, Z, ws=wsf), reps, stream)))
+                            fn=lambda X=X, W=W, Z=Z, ws=wsf: cf.cf_conv3d_fwd(X, W, Z, ws=ws)))
             ops.append(dict(name="conv%d_bwd_data" % (l + 1), kind="conv", flops=flops, bytes=zb + wb + xb,
-                            ms=time_region(torch, lambda: cf.cf_conv3d_bwd_data(dZ, W, dX, ws=wsd), reps, stream)))
+                            fn=lambda dZ=dZ, W=W, dX=dX, ws=wsd: cf.cf_conv3d_bwd_data(dZ, W, dX, ws=ws)))
             ops.append(dict(name="conv%d_bwd_weight" % (l + 1), kind="conv", flops=flops,
                             bytes=xb + zb + 27 * cin * f * 4,
-                            ms=time_region(torch, lambda: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=wsw), reps, stream)))
+                            fn=lambda X=X, dZ=dZ, dW=dW, ws=wsw: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=ws)))
             ops.append(dict(name="pool%d_fwd" % (l + 1), kind="pool", flops=0, bytes=zb + pb + ib,
-                            ms=time_region(torch, lambda: cf.cf_pool3d_fwd(dZ, 0.3, P, idx), reps, stream)))
+                            fn=lambda dZ=dZ, P=P, idx=idx: cf.cf_pool3d_fwd(dZ, 0.3, P, idx)))
             ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
-                            ms=time_region(torch, lambda: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z), reps, stream)))
-            del dZ, Z, dX, wsf, wsd, wsw
-        del X, W, P, idx, dW
+                            fn=lambda P=P, idx=idx, Z=Z: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z)))
         S //= 2
         cin = f
+    return ops
+
+
+def op_timings(torch, cf, c, dev, reps):
+    """Average ms per call of every entry point (HIP events on the stream the
+    calls are launched on)."""
+    stream = torch.cuda.current_stream()
+    ops = build_ops(torch, cf, c, dev)
+    for o in ops:
+        o["ms"] = time_region(torch, o["fn"], reps, stream)
+        del o["fn"]
     torch.cuda.empty_cache()
     return ops
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(op_name):
+    """HBM bytes per launch of `op_name` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (scaled by the same counters on a plain
+    copy of known size), or None when there are none for this entry point or
+    its kernel source has changed since they were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("op") != op_name:
+        return None
+    h = hashlib.sha256()
+    for rel in t.get("sources", []):
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as fh:
+                h.update(fh.read())
+        except OSError:
+            return None
+    if h.hexdigest() != t.get("sources_sha256"):
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(c, seconds):
@@ -181,6 +224,22 @@ def main():
 
     c = CONFIGS[3]
     dev = torch.device("cuda:0")
+    if a.copy_mib:
+        src = torch.ones(a.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(a.op_reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+    if a.profile_op:
+        sel = [o for o in build_ops(torch, cf, c, dev) if o["name"] == a.profile_op]
+        if not sel:
+            print("unknown entry point %r" % a.profile_op, file=sys.stderr)
+            sys.exit(2)
+        for _ in range(a.op_reps):
+            sel[0]["fn"]()
+        torch.cuda.synchronize()
+        return
     net = c.network()
     conv_flops = train_step_conv_flops(net, c.batch)
     xd, t, params = build_inputs(dev, torch, cf, sd, c)
@@ -238,12 +297,12 @@ def main():
             ach = dom["flops"] / (dom["ms"] / 1e3) / 1e12
             out["roofline"] = {"kernel": dom["name"], "bound": "mfma", "achieved": round(ach, 2),
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                               "traffic": None}
+                               "traffic": measured_traffic(dom["name"])}
         else:
             ach = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
             out["roofline"] = {"kernel": dom["name"], "bound": "hbm", "achieved": round(ach, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                               "traffic": None}
+                               "traffic": measured_traffic(dom["name"])}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, a.cpu_seconds)
     print(json.dumps(out), flush=True)
