@@ -730,15 +730,23 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                        "conv3d backward-data");
     }
 
-    // 6. SGD on every master parameter
-    for (int l = 0; l < L; ++l)
-        CF_TRY_HIP(launch_sgd((int64_t)27 * P.layer[l].x.c * P.layer[l].cout, lr, params[l], F(P.layer[l].dw), stream), "sgd");
-    CF_TRY_HIP(launch_sgd((int64_t)P.flat * P.d0, lr, params[L], F(P.dW1), stream), "sgd");
-    CF_TRY_HIP(launch_sgd(P.d0, lr, params[L + 1], F(P.db1), stream), "sgd");
-    CF_TRY_HIP(launch_sgd((int64_t)P.d0 * P.d1, lr, params[L + 2], F(P.dW2), stream), "sgd");
-    CF_TRY_HIP(launch_sgd(P.d1, lr, params[L + 3], F(P.db2), stream), "sgd");
-    CF_TRY_HIP(launch_sgd((int64_t)P.d1 * P.d2, lr, params[L + 4], F(P.dW3), stream), "sgd");
-    CF_TRY_HIP(launch_sgd(P.d2, lr, params[L + 5], F(P.db3), stream), "sgd");
+    // 6. SGD on every master parameter (one launch for all tensors)
+    static_assert(CF_MAX_BLOCKS + 6 <= 16, "SgdList capacity");
+    SgdList sl{};
+    auto add = [&](float* wp, const float* g, int64_t n) {
+        sl.w[sl.count] = wp;
+        sl.dw[sl.count] = g;
+        sl.n[sl.count] = n;
+        ++sl.count;
+    };
+    for (int l = 0; l < L; ++l) add(params[l], F(P.layer[l].dw), (int64_t)27 * P.layer[l].x.c * P.layer[l].cout);
+    add(params[L], F(P.dW1), (int64_t)P.flat * P.d0);
+    add(params[L + 1], F(P.db1), P.d0);
+    add(params[L + 2], F(P.dW2), (int64_t)P.d0 * P.d1);
+    add(params[L + 3], F(P.db2), P.d1);
+    add(params[L + 4], F(P.dW3), (int64_t)P.d1 * P.d2);
+    add(params[L + 5], F(P.db3), P.d2);
+    CF_TRY_HIP(launch_sgd_multi(sl, lr, stream), "sgd");
     return CF_OK;
 }
 

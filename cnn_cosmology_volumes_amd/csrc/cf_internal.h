@@ -131,6 +131,14 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
                             float* dW, float* db, hipStream_t s);
 hipError_t launch_mse(int B, int K, const float* yhat, const float* t, float* loss, float* dyhat, hipStream_t s);
 hipError_t launch_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t s);
+// The same update for up to 16 tensors in one launch (identical arithmetic).
+struct SgdList {
+    int count;
+    float* w[16];
+    const float* dw[16];
+    int64_t n[16];
+};
+hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 
 }  // namespace cf

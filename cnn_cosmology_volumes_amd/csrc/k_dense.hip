@@ -53,10 +53,24 @@ void dense_fwd_partial(const float* __restrict__ X, const uint16_t* __restrict__
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[b] = 0.f;
     if (o < Out) {
-        for (int i = i0 + il; i < i1; i += DI) {
-            const float w = W[(int64_t)i * Out + o];
+        // rows i0+il, i0+il+DI, ... in increasing order; the weight loads of
+        // eight rows are issued together (latency, not bandwidth, bounds this)
+        constexpr int U = 8;
+        for (int i = i0 + il; i < i1; i += DI * U) {
+            float w[U];
 #pragma unroll
-            for (int b = 0; b < DB; ++b) acc[b] = fmaf(xs[b][i - i0], w, acc[b]);
+            for (int u = 0; u < U; ++u) {
+                const int ii = i + u * DI;
+                w[u] = ii < i1 ? W[(int64_t)ii * Out + o] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ii = i + u * DI;
+                if (ii < i1) {
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) acc[b] = fmaf(xs[b][ii - i0], w[u], acc[b]);
+                }
+            }
         }
     }
 #pragma unroll
@@ -72,17 +86,25 @@ void dense_fwd_partial(const float* __restrict__ X, const uint16_t* __restrict__
     }
 }
 
-__global__ void dense_fwd_finalize(const float* __restrict__ part, const float* __restrict__ bias, float slope,
-                                   float* __restrict__ pre, float* __restrict__ Y, int B, int Out, int nks)
+// One wave per output element: lane l sums the splits l, l + 64, ... in
+// increasing order, then the 64 lane sums are combined by a fixed butterfly.
+__global__ __launch_bounds__(256)
+void dense_fwd_finalize(const float* __restrict__ part, const float* __restrict__ bias, float slope,
+                        float* __restrict__ pre, float* __restrict__ Y, int B, int Out, int nks)
 {
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= B * Out) return;
     const int o = e % Out;
     float s = 0.f;
-    for (int k = 0; k < nks; ++k) s += part[(int64_t)k * B * Out + e];
-    if (bias) s += bias[o];
-    pre[e] = s;
-    Y[e] = slope >= 0.f ? (s > 0.f ? s : slope * s) : s;
+    for (int k = lane; k < nks; k += 64) s += part[(int64_t)k * B * Out + e];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (lane == 0) {
+        if (bias) s += bias[o];
+        pre[e] = s;
+        Y[e] = slope >= 0.f ? (s > 0.f ? s : slope * s) : s;
+    }
 }
 
 __global__ void dense_bwd_db(const float* __restrict__ pre, const float* __restrict__ dY, float slope,
@@ -91,7 +113,15 @@ __global__ void dense_bwd_db(const float* __restrict__ pre, const float* __restr
     const int o = blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= Out) return;
     float s = 0.f;
-    for (int b = 0; b < B; ++b) s += gate(dY[b * Out + o], pre[b * Out + o], slope);
+    for (int b0 = 0; b0 < B; b0 += DB) {
+        float g[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+            g[b] = b0 + b < B ? gate(dY[(b0 + b) * Out + o], pre[(b0 + b) * Out + o], slope) : 0.f;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+            if (b0 + b < B) s += g[b];
+    }
     db[o] = s;
 }
 
@@ -104,7 +134,18 @@ __global__ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __rest
     const int o = (int)(e % Out);
     const int64_t i = e / Out;
     float s = 0.f;
-    for (int b = 0; b < B; ++b) s = fmaf(xin(X, Xb, (int64_t)b * In + i), gate(dY[b * Out + o], pre[b * Out + o], slope), s);
+    for (int b0 = 0; b0 < B; b0 += DB) {
+        float x[DB], g[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const bool ok = b0 + b < B;
+            x[b] = ok ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+            g[b] = ok ? gate(dY[(b0 + b) * Out + o], pre[(b0 + b) * Out + o], slope) : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+            if (b0 + b < B) s = fmaf(x[b], g[b], s);
+    }
     dW[e] = s;
 }
 
@@ -160,10 +201,24 @@ __global__ void mse_kernel(const float* __restrict__ yhat, const float* __restri
     if (lane == 0) *loss = s * inv;
 }
 
+// One rounding: W - lr * dW as a fused multiply-add (both SGD kernels use this).
+__device__ __forceinline__ float sgd_update(float w, float g, float lr) { return fmaf(-lr, g, w); }
+
 __global__ void sgd_kernel(float* __restrict__ W, const float* __restrict__ dW, float lr, int64_t n)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) W[i] -= lr * dW[i];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) W[i] = sgd_update(W[i], dW[i], lr);
+}
+
+// Several tensors in one launch: blockIdx.y picks the tensor.
+__global__ void sgd_multi_kernel(SgdList l, float lr)
+{
+    const int t = blockIdx.y;
+    float* __restrict__ W = l.w[t];
+    const float* __restrict__ dW = l.dw[t];
+    const int64_t n = l.n[t];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) W[i] = sgd_update(W[i], dW[i], lr);
 }
 
 __global__ void copy_kernel(const float* __restrict__ s, float* __restrict__ d, int64_t n)
@@ -186,7 +241,7 @@ hipError_t launch_dense_fwd(int B, int in, int out, const float* X, const uint16
     hipLaunchKernelGGL(dense_fwd_partial, grid, dim3(DO * DI), 0, s, X, Xb, W, part, B, in, out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dense_fwd_finalize, dim3((unsigned)((B * out + 255) / 256)), dim3(256), 0, s, part, b, slope,
+    hipLaunchKernelGGL(dense_fwd_finalize, dim3((unsigned)((B * out + 3) / 4)), dim3(256), 0, s, part, b, slope,
                        pre, Y, B, out, nks);
     return hipGetLastError();
 }
@@ -222,6 +277,17 @@ hipError_t launch_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_
     int64_t b = (n + 255) / 256;
     if (b > 8192) b = 8192;
     hipLaunchKernelGGL(sgd_kernel, dim3((unsigned)(b < 1 ? 1 : b)), dim3(256), 0, s, W, dW, lr, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s)
+{
+    if (l.count <= 0) return hipSuccess;
+    int64_t m = 1;
+    for (int t = 0; t < l.count; ++t) m = l.n[t] > m ? l.n[t] : m;
+    int64_t b = (m + 255) / 256;
+    if (b > 2048) b = 2048;
+    hipLaunchKernelGGL(sgd_multi_kernel, dim3((unsigned)b, (unsigned)l.count), dim3(256), 0, s, l, lr);
     return hipGetLastError();
 }
 

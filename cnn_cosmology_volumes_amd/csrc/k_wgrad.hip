@@ -643,30 +643,47 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     }
 }
 
-// dW[e] = sum over splits of part[s][e].  A block owns 64 consecutive
-// elements; its 16 split-lanes each sum the splits s = lane, lane + 16, ...
-// in increasing order, and the 16 lane sums are added in lane order.  The
-// order is fixed, so the result is deterministic.
-constexpr int RD_E = 64, RD_L = 16;
+// dW[e] = sum over splits of part[s][e].  A block owns RD_E consecutive
+// elements (4 per thread, 16-byte loads); its 16 split-lanes each sum the
+// splits s = lane, lane + 16, ... in increasing order, and the 16 lane sums
+// are added in lane order.  The order is fixed, so the result is
+// deterministic.  n must be a multiple of 4 (27 * Cin * Cout with Cin a
+// multiple of 4).
+constexpr int RD_T = 64, RD_E = RD_T * 4, RD_L = 16;
 
-__global__ __launch_bounds__(RD_E * RD_L)
+__global__ __launch_bounds__(RD_T * RD_L)
 void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW, int64_t n, int splits)
 {
-    __shared__ float red[RD_L][RD_E];
-    const int el = threadIdx.x % RD_E, sl = threadIdx.x / RD_E;
-    const int64_t i = (int64_t)blockIdx.x * RD_E + el;
-    float s = 0.f;
+    __shared__ float4 red[RD_L][RD_T];
+    const int el = threadIdx.x % RD_T, sl = threadIdx.x / RD_T;
+    const int64_t i = (int64_t)blockIdx.x * RD_E + 4 * el;
+    const int64_t n4 = n / 4;
+    const float4* p4 = reinterpret_cast<const float4*>(part);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < n) {
-#pragma unroll 4
-        for (int k = sl; k < splits; k += RD_L) s += part[(int64_t)k * n + i];
+        int k = sl;
+        for (; k + 7 * RD_L < splits; k += 8 * RD_L) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p4[(int64_t)(k + u * RD_L) * n4 + i / 4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+        }
+        for (; k < splits; k += RD_L) {
+            const float4 v = p4[(int64_t)k * n4 + i / 4];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
     }
     red[sl][el] = s;
     __syncthreads();
     if (sl == 0 && i < n) {
-        float t = red[0][el];
+        float4 t = red[0][el];
 #pragma unroll
-        for (int k = 1; k < RD_L; ++k) t += red[k][el];
-        dW[i] = t;
+        for (int k = 1; k < RD_L; ++k) {
+            const float4 v = red[k][el];
+            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+        }
+        dW[i] = t.x; dW[i + 1] = t.y; dW[i + 2] = t.z; dW[i + 3] = t.w;
     }
 }
 
@@ -737,7 +754,7 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)27 * x.c * cout;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_E * RD_L), 0, s, part, dW,
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_T * RD_L), 0, s, part, dW,
                        n, p.splits);
     return hipGetLastError();
 }
@@ -754,7 +771,7 @@ hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uin
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)27 * 4 * 32;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_E * RD_L), 0, s, part, dW,
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + RD_E - 1) / RD_E)), dim3(RD_T * RD_L), 0, s, part, dW,
                        n, p.splits);
     return hipGetLastError();
 }
