@@ -80,9 +80,10 @@ def time_region(torch, fn, reps, stream):
 
 def build_ops(torch, cf, c, dev):
     """The step's conv and pool entry points at the workload's shapes (bf16),
-    each as a callable with its algorithmic flops and HBM bytes.  The first
-    block runs fused exactly as in the step: conv + leaky ReLU + pool
-    forward, and pool backward + backward-weight, both counted as conv work.
+    each as a callable with its algorithmic flops and HBM bytes.  Every block
+    forward is timed as cf_conv3d_pool_fwd (fused where the step fuses it);
+    the first block's pool backward + backward-weight runs fused as in the
+    step.  Both fused forms count as conv work.
     Algorithmic bytes: every operand read once and every result written
     once (conv: input, weights, output; backward-weight: input, output
     gradient, fp32 weight gradient; pool: input, output, indices)."""
@@ -120,20 +121,22 @@ def build_ops(torch, cf, c, dev):
         else:
             dZ = torch.randn((B, S, S, S, f), generator=g, device=dev).to(torch.bfloat16)
             Z, dX = torch.empty_like(dZ), torch.empty_like(X)
-            wsf = ws_for(X, f, cf.CF_CONV_FWD)
+            wsf = ws_for(X, f, cf.CF_CONV_POOL_FWD)
             wsd = ws_for(X, f, cf.CF_CONV_BWD_DATA)
             wsw = ws_for(X, f, cf.CF_CONV_BWD_WEIGHT)
-            ops.append(dict(name="conv%d_fwd" % (l + 1), kind="conv", flops=flops, bytes=xb + wb + zb,
-                            fn=lambda X=X, W=W, Z=Z, ws=wsf: cf.cf_conv3d_fwd(X, W, Z, ws=ws)))
+            Po, ido = torch.empty_like(P), torch.empty_like(idx)
+            # the block forward as the step runs it: conv + leaky ReLU + pool in
+            # one launch where the plan allows, else conv then pool
+            ops.append(dict(name="block%d_conv_pool_fwd" % (l + 1), kind="conv", flops=flops,
+                            bytes=xb + wb + pb + ib,
+                            fn=lambda X=X, W=W, Po=Po, ido=ido, ws=wsf: cf.cf_conv3d_pool_fwd(X, W, 0.3, Po, ido, ws=ws)))
+            ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
+                            fn=lambda P=P, idx=idx, Z=Z: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z)))
             ops.append(dict(name="conv%d_bwd_data" % (l + 1), kind="conv", flops=flops, bytes=zb + wb + xb,
                             fn=lambda dZ=dZ, W=W, dX=dX, ws=wsd: cf.cf_conv3d_bwd_data(dZ, W, dX, ws=ws)))
             ops.append(dict(name="conv%d_bwd_weight" % (l + 1), kind="conv", flops=flops,
                             bytes=xb + zb + 27 * cin * f * 4,
                             fn=lambda X=X, dZ=dZ, dW=dW, ws=wsw: cf.cf_conv3d_bwd_weight(X, dZ, dW, ws=ws)))
-            ops.append(dict(name="pool%d_fwd" % (l + 1), kind="pool", flops=0, bytes=zb + pb + ib,
-                            fn=lambda dZ=dZ, P=P, idx=idx: cf.cf_pool3d_fwd(dZ, 0.3, P, idx)))
-            ops.append(dict(name="pool%d_bwd" % (l + 1), kind="pool", flops=0, bytes=pb + pb + ib + zb,
-                            fn=lambda P=P, idx=idx, Z=Z: cf.cf_pool3d_bwd(P, P, idx, 0.3, Z)))
         S //= 2
         cin = f
     return ops

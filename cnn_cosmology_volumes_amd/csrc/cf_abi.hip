@@ -103,7 +103,17 @@ Wg wgrad_path(cf_dtype dt, int64_t cin, int cout)
 size_t esize(cf_dtype dt) { return dt == CF_F32 ? 4 : 2; }
 
 // Fused block kernels exist for the 4-channel first layer in bf16.
-bool fused_pool_fwd(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout % 32 == 0; }
+bool fused_pool_fwd_c4(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout % 32 == 0; }
+// The conv + pool forward runs as one launch for Cin = 4, and for the MFMA
+// path wherever its plan has 4x4x16 tiles and no channel split.
+bool fused_pool_fwd_mfma(cf_dtype dt, const cf_dims& x, int cout)
+{
+    return fwd_path(dt, x.c, cout) == Fwd::Mfma && conv_mfma_can_pool(plan_conv_mfma(x, cout), x);
+}
+bool fused_pool_fwd(cf_dtype dt, const cf_dims& x, int cout)
+{
+    return fused_pool_fwd_c4(dt, x.c, cout) || fused_pool_fwd_mfma(dt, x, cout);
+}
 bool fused_pool_wgrad(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout == 32; }
 
 // Bytes of re-laid weights each path uses.
@@ -240,7 +250,7 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
     case CF_CONV_POOL_FWD: {
         if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
         const Fwd p = fwd_path(dtype, x.c, cout);
-        const size_t z = fused_pool_fwd(dtype, x.c, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
+        const size_t z = fused_pool_fwd(dtype, x, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
         return up256(fwd_wk_bytes(p, x.c, cout)) + up256(fwd_part_bytes(p, x, cout)) + up256(z);
     }
     case CF_POOL_CONV_BWD_WEIGHT: {
@@ -265,7 +275,7 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
         return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: pointers must be 16-byte aligned");
     if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: slope is NaN");
     const Fwd p = fwd_path(dtype, x.c, cout);
-    const bool fused = fused_pool_fwd(dtype, x.c, cout);
+    const bool fused = fused_pool_fwd(dtype, x, cout);
     const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout)), pb = up256(fwd_part_bytes(p, x, cout));
     const size_t zb = fused ? 0 : up256((size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype));
     if (ws_bytes < wkb + pb + zb)
@@ -278,8 +288,13 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
         wk = w8;
     }
     if (fused) {
-        CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)P, idx, slope, x, cout,
-                                           stream), "fused conv3d + pool forward");
+        if (p == Fwd::Mfma)
+            CF_TRY_HIP(launch_conv_mfma_pool(plan_conv_mfma(x, cout), (const uint16_t*)X, (const uint16_t*)wk,
+                                             (uint16_t*)P, idx, slope, x, cout, roundup(cout, 128), stream),
+                       "fused conv3d + pool forward");
+        else
+            CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)P, idx, slope, x,
+                                               cout, stream), "fused conv3d + pool forward");
         return CF_OK;
     }
     void* Z = w8 + wkb + pb;
@@ -504,6 +519,7 @@ struct LayerPlan {
     Fwd dg;
     Wg wg;
     bool fused;         // conv + pool forward and pool backward + wgrad fused (first block)
+    bool pool_fused;    // conv + pool forward fused (MFMA path); backward unfused
     size_t wk_fwd, wk_dg, z, p, idx, dp, dw;   // offsets into the workspace
 };
 
@@ -559,7 +575,8 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         const int64_t npool = nvox / 8;
         Lp.wk_fwd = take(Lp.fwd == Fwd::Direct ? 0 : fwd_wk_bytes(Lp.fwd, x.c, Lp.cout));
         Lp.wk_dg = take(l > 0 ? dgrad_wk_bytes(Lp.dg, dt, x.c, Lp.cout) : 0);
-        Lp.fused = l == 0 && fused_pool_fwd(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x.c, Lp.cout);
+        Lp.fused = l == 0 && fused_pool_fwd_c4(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x.c, Lp.cout);
+        Lp.pool_fused = !Lp.fused && fused_pool_fwd_mfma(dt, x, Lp.cout);
         Lp.z = take(Lp.fused ? 0 : (size_t)nvox * Lp.cout * es);
         Lp.p = take((size_t)npool * Lp.cout * es);
         Lp.idx = take((size_t)npool * Lp.cout);
@@ -671,6 +688,14 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         if (Lp.fused) {
             CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)a, (const uint16_t*)wk, (uint16_t*)(w + Lp.p),
                                                (uint8_t*)(w + Lp.idx), slope, Lp.x, Lp.cout, stream),
+                       "fused conv3d + pool forward");
+            a = w + Lp.p;
+            continue;
+        }
+        if (Lp.pool_fused) {
+            CF_TRY_HIP(launch_conv_mfma_pool(plan_conv_mfma(Lp.x, Lp.cout), (const uint16_t*)a, (const uint16_t*)wk,
+                                             (uint16_t*)(w + Lp.p), (uint8_t*)(w + Lp.idx), slope, Lp.x, Lp.cout,
+                                             roundup(Lp.cout, 128), stream),
                        "fused conv3d + pool forward");
             a = w + Lp.p;
             continue;

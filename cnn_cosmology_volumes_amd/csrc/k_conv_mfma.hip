@@ -14,9 +14,9 @@
 //    (TD+2)(TH+2)(TW+2) halo of the input in LDS once and then walks the 27
 //    taps; a tap only shifts the LDS row index, so every B fragment is one
 //    aligned 16-byte LDS read at a compile-time offset.  The LDS voxel stride
-//    is 96 bytes (64 of data + 32 of padding) where it fits: measured on
-//    gfx950, 16-byte per-lane reads of 16 consecutive voxels run at about
-//    310 B/clk per CU with it, against about 200 for a 64- or 80-byte stride.
+//    is 64 bytes (unpadded).  A padded 96-byte stride reads faster in
+//    isolation (about 310 against 200 B/clk per CU on gfx950), but measured
+//    over the whole kernel the smaller halo wins by 1-5%.
 //  - A fragments (8 consecutive in-channels of one output channel) are
 //    16-byte global loads from the [tap][co][ci] weight copy, which is small
 //    and stays L2/L1 resident.
@@ -33,10 +33,9 @@ namespace {
 // Waves that share a channel slice load the same weight fragments, so a
 // narrow WM (32) with a wide WN (128) halves the redundant weight traffic
 // against a 64 x 64 wave tile; the halo (B) side is read from LDS.
-// LS: bf16 per halo voxel in LDS.  48 (96 B: 64 B of data + 32 B padding)
-// gives the fastest B reads; 32 (64 B, unpadded) costs some bank conflicts
-// but lets two blocks with a 512-voxel tile share a CU.
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
+// LS: bf16 per halo voxel in LDS (32 = 64 bytes, unpadded; 48 adds 32 bytes
+// of padding, which speeds the B reads but loses overall).
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0>
 struct Tile {
     static constexpr int NWM = BM / WM;
     static constexpr int VT = TD * TH * TW;
@@ -47,21 +46,29 @@ struct Tile {
     static constexpr int HV = HD * HH * HW;
     static constexpr int MI = WM / 16;
     static constexpr int NJ = WN / 16;
-    static constexpr int MINB = NW > 4 ? 1 : 2;   // blocks per CU the registers are sized for
+    // waves per SIMD the registers are sized for (the second launch bound)
+    static constexpr int MINB = WPE_ ? WPE_ : (NW > 4 ? 1 : 2);
     static constexpr int NE = HV * 4;             // 16-byte halo pieces per chunk
     static constexpr int IT = (NE + NT - 1) / NT; // halo pieces per thread
     static_assert(VT % WN == 0 && (NW == 4 || NW == 8), "tile");
     static_assert(BM % WM == 0 && WM % 16 == 0 && WN % 16 == 0, "frag");
 };
 
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
-__global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS>::MINB))
+// POOL: instead of Y, write the leaky-ReLU + 2^3 max-pooled output P
+// ([n][D/2][H/2][W/2][Cout]) and the window indices (first strict maximum
+// of the bf16-rounded conv outputs in window order a*4 + b*2 + e, then
+// leaky ReLU, exactly as the separate pool kernel computes them).  Needs a
+// wave to own two whole depth planes of a 16-wide tile (WN = 2*TH*TW,
+// TW = 16), so a window is 4 accumulator fragments of one lane and of its
+// neighbour lane, and no split of the channel reduction.
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false>
+__global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                         uint16_t* __restrict__ Y, float* __restrict__ part,
                         int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
-                        int tD, int tH, int tW, int chunks_per_split)
+                        int tD, int tH, int tW, int chunks_per_split, uint8_t* __restrict__ pidx, float slope)
 {
-    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>;
     __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LS];
 
     const int lane = threadIdx.x & 63;
@@ -169,6 +176,54 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
         }
     }
 
+    if constexpr (POOL) {
+        static_assert(TW == 16 && WN == 2 * TH * TW && TD % 2 == 0 && TH % 2 == 0, "pooled epilogue mapping");
+        // Fragment j of this wave holds tile voxels (2*wave + j / TH, j % TH, l16).
+        const int Dp = D >> 1, Hp = H >> 1, Wp = W >> 1;
+        const uint32_t c = l16 & 1;                        // window w offset of this lane
+        const int gpd = (d0 >> 1) + wave, gpw = (w0 >> 1) + (l16 >> 1);
+#pragma unroll
+        for (int ph = 0; ph < TH / 2; ++ph) {
+            const int gph = (h0 >> 1) + ph;
+            const bool inside = gpd < Dp && gph < Hp && gpw < Wp;
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i) {
+                const int co = co_base + 16 * i + 4 * lg;
+                float out[4];
+                uint32_t bix[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // this lane's four window members in window order (a, b) = 00, 01, 10, 11
+                    float z[4];
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab)
+                        z[ab] = __uint_as_float((uint32_t)f2bf(acc[i][(ab >> 1) * TH + 2 * ph + (ab & 1)][r]) << 16);
+                    // even lanes start from window position 0 like a sequential scan;
+                    // odd lanes from -inf, so a NaN at position 1 is skipped as the
+                    // scan would skip it
+                    float best = c ? -INFINITY : z[0];
+                    uint32_t bp = c;
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab)
+                        if (z[ab] > best) { best = z[ab]; bp = 2u * ab + c; }
+                    // combine with the neighbour lane (the other w position): larger
+                    // value, on a tie the earlier window position
+                    const float ob = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(best), 0xB1, 0xF, 0xF, false));
+                    const uint32_t op = (uint32_t)__builtin_amdgcn_mov_dpp((int)bp, 0xB1, 0xF, 0xF, false);
+                    if (ob > best || (ob == best && op < bp)) { best = ob; bp = op; }
+                    out[r] = best > 0.f ? best : slope * best;
+                    bix[r] = bp;
+                }
+                if (c == 0 && inside && co < Cout) {
+                    const int64_t o = (((int64_t)n * Dp + gpd) * Hp + gph) * Wp * Cout + (int64_t)gpw * Cout + co;
+                    *reinterpret_cast<uint2*>(Y + o) = make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
+                    *reinterpret_cast<uint32_t*>(pidx + o) = bix[0] | (bix[1] << 8) | (bix[2] << 16) | (bix[3] << 24);
+                }
+            }
+        }
+        return;
+    }
+
     // Epilogue: lane holds 4 consecutive output channels of one voxel per fragment.
     const int64_t nvox = (int64_t)N * D * plane;
 #pragma unroll
@@ -211,28 +266,28 @@ __global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __re
 
 struct CfgInfo { int bm, wm, wn, td, th, tw, ls; };
 constexpr CfgInfo kCfgs[] = {
-    {128, 32, 128, 4, 4, 16, 48},   // 0
-    {128, 32, 128, 4, 8, 8, 48},    // 1
-    {64, 32, 128, 4, 4, 16, 48},    // 2
-    {64, 32, 128, 4, 8, 8, 48},     // 3
+    {128, 32, 128, 4, 4, 16, 32},   // 0
+    {128, 32, 128, 4, 8, 8, 32},    // 1
+    {64, 32, 128, 4, 4, 16, 32},    // 2
+    {64, 32, 128, 4, 8, 8, 32},     // 3
     {32, 32, 128, 4, 8, 16, 32},    // 4
-    {32, 32, 64, 4, 8, 8, 48},      // 5
-    {16, 16, 64, 4, 4, 16, 48},     // 6
-    {16, 16, 64, 4, 8, 8, 48},      // 7
+    {32, 32, 64, 4, 8, 8, 32},      // 5
+    {16, 16, 64, 4, 4, 16, 32},     // 6
+    {16, 16, 64, 4, 8, 8, 32},      // 7
 };
 
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x,
-                      int cout, int coutpad, int splits, hipStream_t s)
+                      int cout, int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
 {
-    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>;
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const int nchunks = (int)(x.c / 32);
     const int cps = (nchunks + splits - 1) / splits;
     dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
-    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WM, WN, TD, TH, TW, LS>), grid, dim3(T::NT), 0, s, X, Wk, Y,
-                       splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
-                       coutpad, tD, tH, tW, cps);
+    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WM, WN, TD, TH, TW, LS, WPE_, POOL>), grid, dim3(T::NT), 0, s, X, Wk,
+                       Y, splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
+                       coutpad, tD, tH, tW, cps, pidx, slope);
     return hipGetLastError();
 }
 
@@ -269,14 +324,14 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
 {
     hipError_t e;
     switch (p.cfg) {
-    case 0: e = launch_cfg<128, 32, 128, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 1: e = launch_cfg<128, 32, 128, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 2: e = launch_cfg<64, 32, 128, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 3: e = launch_cfg<64, 32, 128, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 0: e = launch_cfg<128, 32, 128, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 1: e = launch_cfg<128, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 2: e = launch_cfg<64, 32, 128, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 3: e = launch_cfg<64, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     case 4: e = launch_cfg<32, 32, 128, 4, 8, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 5: e = launch_cfg<32, 32, 64, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 6: e = launch_cfg<16, 16, 64, 4, 4, 16, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    default: e = launch_cfg<16, 16, 64, 4, 8, 8, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 5: e = launch_cfg<32, 32, 64, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    case 6: e = launch_cfg<16, 16, 64, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    default: e = launch_cfg<16, 16, 64, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
@@ -284,6 +339,20 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(split_reduce_bf16, dim3((unsigned)blocks), dim3(256), 0, s, part, Y, n4, p.splits);
     return hipGetLastError();
+}
+
+bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x)
+{
+    return p.splits == 1 && (p.cfg == 0 || p.cfg == 2) && (x.d % 2 == 0) && (x.h % 2 == 0) && (x.w % 2 == 0);
+}
+
+hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx,
+                                 float slope, const cf_dims& x, int cout, int coutpad, hipStream_t s)
+{
+    if (!conv_mfma_can_pool(p, x)) return hipErrorInvalidValue;
+    if (p.cfg == 0)
+        return launch_cfg<128, 32, 128, 4, 4, 16, 32, 0, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
+    return launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
 }
 
 }  // namespace cf

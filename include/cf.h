@@ -134,8 +134,12 @@ cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const v
  * its output (the conv output rounded to dtype first), i.e. one
  * [conv -> leaky ReLU -> 2^3 max pool] block of [CF] Sec. III-A / [OY]
  * Table I, without writing the full-resolution conv output to memory when
- * a fused kernel exists for the shape (bf16, x.c == 4, cout % 32 == 0);
- * other shapes run the two steps through the workspace.
+ * a fused kernel exists for the shape: bf16 with x.c == 4 and cout % 32 == 0,
+ * or bf16 with x.c % 32 == 0 and cout % 32 == 0 where the kernel's plan uses
+ * 64- or 128-channel blocks on 4x4x16 tiles and does not split the channel
+ * reduction (cf_conv3d_workspace_size(..., CF_CONV_POOL_FWD) then counts no
+ * conv output).  Other shapes run the two steps through the workspace.  The
+ * result is the same bit for bit either way.
  *   X [x.n, x.d, x.h, x.w, x.c], W [3,3,3,x.c,cout]  (dtype)
  *   P [x.n, x.d/2, x.h/2, x.w/2, cout] (dtype) and idx (uint8, same shape): outputs
  * x.d, x.h, x.w must be even. */

@@ -264,9 +264,13 @@ def test_error_statuses_on_device():
 
 # ------------------------------------------------------ fused block paths
 FUSED_CASES = [(2, 6, 10, 34, 4, 32), (1, 8, 8, 16, 4, 64), (1, 4, 4, 4, 32, 32), (1, 2, 2, 2, 4, 32)]
+# MFMA path with the pooled epilogue: 64 and 128 output channels on 4x4x16
+# tiles with ragged edges, plus a 64-channel input whose plan splits the
+# channel reduction (falls back to conv + pool).
+FUSED_FWD_CASES = FUSED_CASES + [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 8, 8, 32, 64, 64)]
 
 
-@pytest.mark.parametrize("shape", FUSED_CASES)
+@pytest.mark.parametrize("shape", FUSED_FWD_CASES)
 def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     """The fused block forward returns exactly what the two separate entry
     points return (same accumulation, same bf16 rounding of the conv output,
@@ -285,6 +289,28 @@ def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     g = host64(P)
     assert rel_err(g, po) <= TOL_BF16
     assert np.mean(idx.cpu().numpy() == io) > 0.995   # rare flips where two window values round alike
+
+
+@pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128)])
+def test_conv3d_pool_fwd_ties_follow_window_order(shape):
+    """Integer inputs and weights in {-1, 0, 1} give conv outputs that tie
+    often inside a window; the fused epilogue (whose window is split over two
+    lanes) must still pick the first strict maximum in window order, as the
+    separate pool kernel does."""
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 5)
+    x = rng.choice([-1.0, 0.0, 1.0], p=[0.2, 0.6, 0.2], size=(N, D, H, W, Ci)).astype(np.float32)
+    w = rng.choice([-1.0, 0.0, 1.0], p=[0.05, 0.9, 0.05], size=(3, 3, 3, Ci, Co)).astype(np.float32)
+    xd, wd = to_dev(x, BF), to_dev(w, BF)
+    P, idx = cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+    Z = cf.cf_conv3d_fwd(xd, wd)
+    P2, idx2 = cf.cf_pool3d_fwd(Z, SLOPE)
+    torch.cuda.synchronize()
+    assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
+    # the ties are really there: some window holds its maximum more than once
+    z = Z.float().cpu().numpy().reshape(N, D // 2, 2, H // 2, 2, W // 2, 2, Co)
+    win = z.transpose(0, 1, 3, 5, 7, 2, 4, 6).reshape(-1, 8)
+    assert ((win == win.max(axis=1, keepdims=True)).sum(axis=1) > 1).mean() > 0.05
 
 
 @pytest.mark.parametrize("shape", FUSED_CASES)
