@@ -100,9 +100,16 @@ def test_train_step_validation_and_workspace():
     fx = (8, 128, 128, 128, 4)
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_CONV_POOL_FWD) == 128 * 128 * 2
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_POOL_CONV_BWD_WEIGHT) % (27 * 4 * 32 * 4) == 0
-    # unfused shapes carry the conv output through the workspace
-    ux = (2, 16, 16, 16, 32)
-    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, ux, 64, cf.CF_CONV_POOL_FWD) >= 2 * 16 ** 3 * 64 * 2
+    # MFMA shapes whose plan has 64/128-channel blocks on 4x4x16 tiles and no
+    # channel split run fused: weights only (27 taps x 128 padded co x Cin)
+    mx = (2, 16, 16, 16, 32)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, mx, 64, cf.CF_CONV_POOL_FWD) == 27 * 128 * 32 * 2
+    # unfused shapes carry the conv output through the workspace: 32 output
+    # channels (512-voxel tiles), an fp32 conv, a split channel reduction
+    for ux, co, dt in [((2, 16, 16, 16, 32), 32, cf.CF_BF16), ((2, 16, 16, 16, 32), 64, cf.CF_F32),
+                       ((1, 8, 8, 32, 64), 64, cf.CF_BF16)]:
+        zb = ux[0] * ux[1] * ux[2] * ux[3] * co * (4 if dt == cf.CF_F32 else 2)
+        assert cf.cf_conv3d_workspace_size(dt, ux, co, cf.CF_CONV_POOL_FWD) >= zb
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 3, 4, 4, 4), 32, cf.CF_CONV_POOL_FWD) == 0   # odd D
     bad = cf.model_desc(4, 100, [32, 64, 128])      # 100 not divisible by 8
     assert cf.cf_train_step_workspace_size(bad, cf.CF_BF16, 8) == 0
