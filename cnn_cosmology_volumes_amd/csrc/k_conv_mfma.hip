@@ -295,10 +295,12 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float*
 
 ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
 {
+    // 64-channel 4-wave blocks for every output width above 32: two of them
+    // share a CU and hide each other's halo staging, which measured faster
+    // than 128-channel 8-wave blocks (one per CU) at every layer shape.
     ConvPlan p{};
     const bool narrow = x.w < 16;
-    if (cout > 64) p.cfg = narrow ? 1 : 0;
-    else if (cout > 32) p.cfg = narrow ? 3 : 2;
+    if (cout > 32) p.cfg = narrow ? 3 : 2;
     else if (cout > 16) p.cfg = narrow ? 5 : 4;
     else p.cfg = narrow ? 7 : 6;
     const CfgInfo& c = kCfgs[p.cfg];
@@ -306,6 +308,8 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
     const int64_t tiles = x.n * ((x.d + c.td - 1) / c.td) * ((x.h + c.th - 1) / c.th) * ((x.w + c.tw - 1) / c.tw);
     const int64_t blocks = tiles * ((cout + c.bm - 1) / c.bm);
     const int nchunks = (int)(x.c / 32);
+    // split the channel reduction only while the grid has fewer than two
+    // blocks per CU (the split costs fp32 partials and a reduction launch)
     int splits = 1;
     if (blocks < 512 && nchunks > 1) {
         splits = (int)((512 + blocks - 1) / blocks);
