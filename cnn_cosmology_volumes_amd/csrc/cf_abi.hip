@@ -528,7 +528,7 @@ struct StepPlan {
     LayerPlan layer[CF_MAX_BLOCKS];
     int flat, d0, d1, d2;
     size_t part;        // shared split-K buffer (conv fwd, dgrad, wgrad, dense)
-    size_t pre1, y1, pre2, y2, pre3, y3, dy3, dy2, dy1;
+    size_t pre1, y1, pre2, y2, pre3, y3, dy3, dy2, dy1, g1;
     size_t dW1, db1, dW2, db2, dW3, db3;
     size_t cast;        // bf16 DHWIO weight copy for direct bf16 fallbacks
     size_t total;
@@ -605,6 +605,7 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
     P.pre2 = take((size_t)B * P.d1 * f); P.y2 = take((size_t)B * P.d1 * f);
     P.pre3 = take((size_t)B * P.d2 * f); P.y3 = take((size_t)B * P.d2 * f);
     P.dy3 = take((size_t)B * P.d2 * f); P.dy2 = take((size_t)B * P.d1 * f); P.dy1 = take((size_t)B * P.d0 * f);
+    P.g1 = take((size_t)B * P.d0 * f);
     P.dW1 = take((size_t)P.flat * P.d0 * f); P.db1 = take((size_t)P.d0 * f);
     P.dW2 = take((size_t)P.d0 * P.d1 * f); P.db2 = take((size_t)P.d1 * f);
     P.dW3 = take((size_t)P.d1 * P.d2 * f); P.db3 = take((size_t)P.d2 * f);
@@ -646,15 +647,22 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     const float slope = m->slope;
     const bool bf = dtype == CF_BF16;
 
-    // 1. weight copies for this step (bf16 rounding of the fp32 masters)
+    // 1. weight copies for this step (bf16 rounding of the fp32 masters); the
+    //    MFMA-path re-layouts of all blocks go in one launch
+    static_assert(CF_MAX_BLOCKS <= 8, "WprepList capacity");
+    WprepList wl{};
     for (int l = 0; l < L; ++l) {
         const LayerPlan& Lp = P.layer[l];
-        if (Lp.fwd != Fwd::Direct)
-            CF_TRY_HIP(prep_fwd(Lp.fwd, params[l], true, Lp.x.c, Lp.cout, w + Lp.wk_fwd, stream), "weight re-layout");
+        if (Lp.fwd == Fwd::Mfma)
+            wl.job[wl.count++] = WprepJob{0, true, (int)Lp.x.c, Lp.cout, roundup(Lp.cout, 128), params[l],
+                                          (uint16_t*)(w + Lp.wk_fwd)};
+        else if (Lp.fwd == Fwd::C4)
+            wl.job[wl.count++] = WprepJob{2, true, (int)Lp.x.c, Lp.cout, roundup(Lp.cout, 128), params[l],
+                                          (uint16_t*)(w + Lp.wk_fwd)};
         if (l > 0) {
             if (Lp.dg == Fwd::Mfma) {
-                CF_TRY_HIP(prep_dgrad(Lp.dg, dtype, params[l], true, Lp.x.c, Lp.cout, w + Lp.wk_dg, stream),
-                           "weight re-layout");
+                wl.job[wl.count++] = WprepJob{1, true, (int)Lp.x.c, Lp.cout, roundup((int)Lp.x.c, 128), params[l],
+                                              (uint16_t*)(w + Lp.wk_dg)};
             } else if (bf) {
                 const int64_t n = (int64_t)27 * Lp.x.c * Lp.cout;
                 hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
@@ -668,6 +676,7 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
             }
         }
     }
+    CF_TRY_HIP(launch_wprep_multi(wl, stream), "weight re-layout");
 
     // 2. forward through the blocks
     const void* a = X;
@@ -717,19 +726,37 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     const float* W1 = params[L], *b1 = params[L + 1], *W2 = params[L + 2], *b2 = params[L + 3], *W3 = params[L + 4],
                 *b3 = params[L + 5];
     CF_TRY_HIP(launch_dense_fwd(B, P.flat, P.d0, hX, hXb, W1, b1, slope, F(P.pre1), F(P.y1), part, stream), "dense1");
-    CF_TRY_HIP(launch_dense_fwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, b2, slope, F(P.pre2), F(P.y2), part, stream), "dense2");
-    CF_TRY_HIP(launch_dense_fwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, b3, -1.f, F(P.pre3), F(P.y3), part, stream), "dense3");
-    CF_TRY_HIP(launch_mse(B, P.d2, F(P.y3), targets, loss_out, F(P.dy3), stream), "mse");
-    if (pred_out) CF_TRY_HIP(launch_copy_f32(F(P.y3), pred_out, (int64_t)B * P.d2, stream), "copy predictions");
-
-    // 4. dense backward
-    CF_TRY_HIP(launch_dense_bwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, F(P.pre3), F(P.dy3), -1.f, F(P.dy2), nullptr,
-                                F(P.dW3), F(P.db3), stream), "dense3 backward");
-    CF_TRY_HIP(launch_dense_bwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, F(P.pre2), F(P.dy2), slope, F(P.dy1), nullptr,
-                                F(P.dW2), F(P.db2), stream), "dense2 backward");
-    CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.pre1), F(P.dy1), slope,
-                                bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
-                                F(P.dW1), F(P.db1), stream), "dense1 backward");
+    if (dense_head_fits(B, P.d0, P.d1, P.d2)) {
+        // layers 2-3, the loss and their backward in one launch; layer 1's
+        // gated output gradient g1 then feeds its weight and data gradients
+        // with the gate switched off (slope < 0), which gives the same values
+        DenseHead h{};
+        h.B = B; h.d0 = P.d0; h.d1 = P.d1; h.d2 = P.d2; h.slope = slope;
+        h.y1 = F(P.y1); h.pre1 = F(P.pre1); h.W2 = W2; h.b2 = b2; h.W3 = W3; h.b3 = b3; h.t = targets;
+        h.pre2 = F(P.pre2); h.y2 = F(P.y2); h.pre3 = F(P.pre3); h.y3 = F(P.y3); h.dy3 = F(P.dy3);
+        h.loss = loss_out; h.pred = pred_out;
+        h.dy2 = F(P.dy2); h.dW3 = F(P.dW3); h.db3 = F(P.db3);
+        h.dy1 = F(P.dy1); h.dW2 = F(P.dW2); h.db2 = F(P.db2);
+        h.g1 = F(P.g1); h.db1 = F(P.db1);
+        CF_TRY_HIP(launch_dense_head(h, stream), "dense head");
+        CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.g1), F(P.g1), -1.f,
+                                    bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
+                                    F(P.dW1), nullptr, stream), "dense1 backward");
+    } else {
+        CF_TRY_HIP(launch_dense_fwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, b2, slope, F(P.pre2), F(P.y2), part, stream),
+                   "dense2");
+        CF_TRY_HIP(launch_dense_fwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, b3, -1.f, F(P.pre3), F(P.y3), part, stream),
+                   "dense3");
+        CF_TRY_HIP(launch_mse(B, P.d2, F(P.y3), targets, loss_out, F(P.dy3), stream), "mse");
+        if (pred_out) CF_TRY_HIP(launch_copy_f32(F(P.y3), pred_out, (int64_t)B * P.d2, stream), "copy predictions");
+        CF_TRY_HIP(launch_dense_bwd(B, P.d1, P.d2, F(P.y2), nullptr, W3, F(P.pre3), F(P.dy3), -1.f, F(P.dy2), nullptr,
+                                    F(P.dW3), F(P.db3), stream), "dense3 backward");
+        CF_TRY_HIP(launch_dense_bwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, F(P.pre2), F(P.dy2), slope, F(P.dy1), nullptr,
+                                    F(P.dW2), F(P.db2), stream), "dense2 backward");
+        CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.pre1), F(P.dy1), slope,
+                                    bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
+                                    F(P.dW1), F(P.db1), stream), "dense1 backward");
+    }
 
     // 5. conv blocks backward: pool backward -> weight gradient -> data gradient
     for (int l = L - 1; l >= 0; --l) {

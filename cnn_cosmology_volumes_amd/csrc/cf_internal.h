@@ -60,6 +60,19 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
 hipError_t launch_wprep_fwd(const void* W, bool w_is_f32, int cin, int cout, int copad, uint16_t* Wk, hipStream_t s);
 hipError_t launch_wprep_dgrad(const void* W, bool w_is_f32, int cin, int cout, int cipad, uint16_t* Wk, hipStream_t s);
 hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, uint16_t* Wk, hipStream_t s);
+// The same re-layouts, several in one launch (identical results).
+struct WprepJob {
+    int kind;           // 0: fwd (pad = copad), 1: dgrad (pad = cipad), 2: c4 (pad = copad)
+    bool f32;
+    int cin, cout, pad;
+    const void* src;
+    uint16_t* dst;
+};
+struct WprepList {
+    int count;
+    WprepJob job[2 * 8];
+};
+hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s);
 // fp32 dgrad weights for the direct path: Wt[t'][co][ci] = W[26-t'][ci][co] (float or bf16 source kept as-is)
 hipError_t launch_wprep_direct_dgrad(const void* W, cf_dtype dt, int cin, int cout, void* Wt, hipStream_t s);
 
@@ -135,6 +148,18 @@ hipError_t launch_dense_fwd(int B, int in, int out, const float* X, const uint16
 hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
                             const float* pre, const float* dY, float slope, float* dX, uint16_t* dXb,
                             float* dW, float* db, hipStream_t s);
+// Layers 2 and 3 of the head, MSE, their backward and layer 1's gated
+// gradient and bias gradient in one launch (same arithmetic as the
+// standalone kernels).  Fits when the two small layers have In <= 128.
+struct DenseHead {
+    int B, d0, d1, d2;
+    float slope;
+    const float *y1, *pre1, *W2, *b2, *W3, *b3, *t;
+    float *pre2, *y2, *pre3, *y3, *dy3, *loss, *pred;
+    float *dy2, *dW3, *db3, *dy1, *dW2, *db2, *g1, *db1;
+};
+bool dense_head_fits(int B, int d0, int d1, int d2);
+hipError_t launch_dense_head(const DenseHead& h, hipStream_t s);
 hipError_t launch_mse(int B, int K, const float* yhat, const float* t, float* loss, float* dyhat, hipStream_t s);
 hipError_t launch_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t s);
 // The same update for up to 16 tensors in one launch (identical arithmetic).

@@ -20,6 +20,7 @@ constexpr int DB = 8;        // batch rows per block
 constexpr int DO = 64;       // output columns per block
 constexpr int DI = 4;        // input lanes per block
 constexpr int DK = 128;      // input rows per split
+constexpr int HEAD_RED = 8192;   // LDS partials of the fused head kernel (floats)
 
 __device__ __forceinline__ float xin(const float* X, const uint16_t* Xb, int64_t i) {
     return Xb ? bf2f(Xb[i]) : X[i];
@@ -149,14 +150,13 @@ __global__ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __rest
     dW[e] = s;
 }
 
-// One wave per input row i: lanes stride over o, then a fixed butterfly sum.
-__global__ __launch_bounds__(256)
-void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, const float* __restrict__ dY,
-                  float slope, float* __restrict__ dX, uint16_t* __restrict__ dXb, int B, int In, int Out)
+// dX for input row i, computed by one wave: lanes stride over o, then a
+// fixed butterfly sum per batch row; lane 0 writes.  Shared by the
+// standalone backward kernel and the fused head kernel.
+__device__ __forceinline__ void dx_row_wave(const float* __restrict__ W, const float* __restrict__ pre,
+                                            const float* __restrict__ dY, float slope, float* __restrict__ dX,
+                                            uint16_t* __restrict__ dXb, int B, int In, int Out, int64_t i, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= In) return;
     for (int b0 = 0; b0 < B; b0 += DB) {
         const int nb = min(DB, B - b0);
         float acc[DB];
@@ -182,6 +182,126 @@ void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, co
                 else dX[o2] = acc[b];
             }
         }
+    }
+}
+
+// One wave per input row i.
+__global__ __launch_bounds__(256)
+void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, const float* __restrict__ dY,
+                  float slope, float* __restrict__ dX, uint16_t* __restrict__ dXb, int B, int In, int Out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= In) return;
+    dx_row_wave(W, pre, dY, slope, dX, dXb, B, In, Out, i, lane);
+}
+
+// The small layers of the head in one block (In <= 128 for layers 2 and 3,
+// so each has a single K split): layer 2 and 3 forward, MSE, layer 3 and 2
+// backward, and layer 1's gated output gradient and bias gradient.  Every
+// value is computed with the same operations in the same order as the
+// standalone kernels (partial fmaf chains over i = il mod 4, their sum in il
+// order, the split finalize, the MSE and backward reductions), so the fused
+// step matches the entry points bit for bit.
+__device__ __forceinline__ void head_fwd_layer(const float* __restrict__ X, const float* __restrict__ W,
+                                               const float* __restrict__ bias, float slope, float* __restrict__ pre,
+                                               float* __restrict__ Y, float* red, int B, int In, int Out)
+{
+    const int n = B * Out;
+    for (int task = threadIdx.x; task < n * DI; task += blockDim.x) {
+        const int il = task / n, e = task % n, b = e / Out, o = e % Out;
+        float acc = 0.f;
+        for (int i = il; i < In; i += DI) acc = fmaf(X[b * In + i], W[(int64_t)i * Out + o], acc);
+        red[task] = acc;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        float p = red[e];
+#pragma unroll
+        for (int k = 1; k < DI; ++k) p += red[k * n + e];
+        float sum = 0.f;
+        sum += p;                       // the finalize's single-split lane sum
+        if (bias) sum += bias[e % Out];
+        pre[e] = sum;
+        Y[e] = slope >= 0.f ? (sum > 0.f ? sum : slope * sum) : sum;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void head_bwd_layer(const float* __restrict__ X, const float* __restrict__ W,
+                                               const float* __restrict__ pre, const float* __restrict__ dY,
+                                               float slope, float* __restrict__ dX, float* __restrict__ dW,
+                                               float* __restrict__ db, int B, int In, int Out)
+{
+    for (int o = threadIdx.x; o < Out; o += blockDim.x) {
+        float sum = 0.f;
+        for (int b = 0; b < B; ++b) sum += gate(dY[b * Out + o], pre[b * Out + o], slope);
+        db[o] = sum;
+    }
+    for (int e = threadIdx.x; e < In * Out; e += blockDim.x) {
+        const int i = e / Out, o = e % Out;
+        float sum = 0.f;
+        for (int b = 0; b < B; ++b) sum = fmaf(X[b * In + i], gate(dY[b * Out + o], pre[b * Out + o], slope), sum);
+        dW[e] = sum;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (dX)
+        for (int i = wave; i < In; i += nw) dx_row_wave(W, pre, dY, slope, dX, nullptr, B, In, Out, i, lane);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(1024)
+void dense_head_kernel(DenseHead h)
+{
+    // Every operand and intermediate lives in LDS (tens of KB): the
+    // reductions are short dependent chains, so LDS latency instead of L2
+    // latency is what makes one block fast enough.
+    extern __shared__ float lds[];
+    const int B = h.B, d0 = h.d0, d1 = h.d1, d2 = h.d2;
+    float* red = lds;                      // HEAD_RED
+    float* y1 = red + HEAD_RED;            // B*d0
+    float* pre1 = y1 + B * d0;             // B*d0
+    float* W2 = pre1 + B * d0;             // d0*d1
+    float* W3 = W2 + d0 * d1;              // d1*d2
+    float* pre2 = W3 + d1 * d2;            // B*d1
+    float* y2 = pre2 + B * d1;             // B*d1
+    float* pre3 = y2 + B * d1;             // B*d2
+    float* y3 = pre3 + B * d2;             // B*d2
+    float* dy3 = y3 + B * d2;              // B*d2
+    float* dy2 = dy3 + B * d2;             // B*d1
+    float* dy1 = dy2 + B * d1;             // B*d0
+    for (int e = threadIdx.x; e < B * d0; e += blockDim.x) { y1[e] = h.y1[e]; pre1[e] = h.pre1[e]; }
+    for (int e = threadIdx.x; e < d0 * d1; e += blockDim.x) W2[e] = h.W2[e];
+    for (int e = threadIdx.x; e < d1 * d2; e += blockDim.x) W3[e] = h.W3[e];
+    __syncthreads();
+    head_fwd_layer(y1, W2, h.b2, h.slope, pre2, y2, red, B, d0, d1);
+    head_fwd_layer(y2, W3, h.b3, -1.f, pre3, y3, red, B, d1, d2);
+    const int n = B * d2;
+    if (threadIdx.x < 64) {
+        // mean squared error, as mse_kernel
+        const int lane = threadIdx.x;
+        const float inv = 1.0f / (float)n;
+        float sum = 0.f;
+        for (int e = lane; e < n; e += 64) {
+            const float r = y3[e] - h.t[e];
+            sum = fmaf(r, r, sum);
+            dy3[e] = 2.0f * r * inv;
+            if (h.pred) h.pred[e] = y3[e];
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+        if (lane == 0) *h.loss = sum * inv;
+    }
+    __syncthreads();
+    head_bwd_layer(y2, W3, pre3, dy3, -1.f, dy2, h.dW3, h.db3, B, d1, d2);
+    head_bwd_layer(y1, W2, pre2, dy2, h.slope, dy1, h.dW2, h.db2, B, d0, d1);
+    // layer 1: gated output gradient (consumed by its weight / data gradient
+    // kernels with the gate switched off) and the bias gradient
+    for (int e = threadIdx.x; e < B * d0; e += blockDim.x) h.g1[e] = gate(dy1[e], pre1[e], h.slope);
+    for (int o = threadIdx.x; o < d0; o += blockDim.x) {
+        float sum = 0.f;
+        for (int b = 0; b < B; ++b) sum += gate(dy1[b * d0 + o], pre1[b * d0 + o], h.slope);
+        h.db1[o] = sum;
     }
 }
 
@@ -250,9 +370,13 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
                             const float* pre, const float* dY, float slope, float* dX, uint16_t* dXb, float* dW,
                             float* db, hipStream_t s)
 {
-    hipLaunchKernelGGL(dense_bwd_db, dim3((unsigned)((out + 255) / 256)), dim3(256), 0, s, pre, dY, slope, db, B, out);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (db) {
+        hipLaunchKernelGGL(dense_bwd_db, dim3((unsigned)((out + 255) / 256)), dim3(256), 0, s, pre, dY, slope, db, B,
+                           out);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t ndw = (int64_t)in * out;
     hipLaunchKernelGGL(dense_bwd_dw, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, X, Xb, pre, dY, slope, dW,
                        B, in, out);
@@ -264,6 +388,25 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
         e = hipGetLastError();
     }
     return e;
+}
+
+size_t head_lds_bytes(int B, int d0, int d1, int d2)
+{
+    return sizeof(float) * ((size_t)HEAD_RED + 3 * (size_t)B * d0 + (size_t)d0 * d1 + (size_t)d1 * d2 +
+                            3 * (size_t)B * d1 + 3 * (size_t)B * d2);
+}
+
+bool dense_head_fits(int B, int d0, int d1, int d2)
+{
+    return d0 <= DK && d1 <= DK && (int64_t)B * d1 * DI <= HEAD_RED && (int64_t)B * d2 * DI <= HEAD_RED &&
+           B * d2 <= 64 && head_lds_bytes(B, d0, d1, d2) <= 96 * 1024;
+}
+
+hipError_t launch_dense_head(const DenseHead& h, hipStream_t s)
+{
+    if (!dense_head_fits(h.B, h.d0, h.d1, h.d2)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dense_head_kernel, dim3(1), dim3(1024), head_lds_bytes(h.B, h.d0, h.d1, h.d2), s, h);
+    return hipGetLastError();
 }
 
 hipError_t launch_mse(int B, int K, const float* yhat, const float* t, float* loss, float* dyhat, hipStream_t s)

@@ -19,39 +19,73 @@ __device__ __forceinline__ float wload(const void* W, bool f32, int64_t i) {
     return f32 ? reinterpret_cast<const float*>(W)[i] : bf2f(reinterpret_cast<const uint16_t*>(W)[i]);
 }
 
-// Wk[t][co][ci], co < copad (zero rows beyond cout).
+// Element e of each layout (the single-layout kernels and the batched one
+// share these, so their results are identical).
+// fwd:   Wk[t][co][ci], co < copad (zero rows beyond cout).
+// Element indices stay far below 2^31 (27 taps x padded channels), so the
+// index arithmetic is 32-bit.
+__device__ __forceinline__ uint16_t wk_fwd_elem(const void* W, bool f32, int cin, int cout, int copad, int64_t e64)
+{
+    const uint32_t e = (uint32_t)e64;
+    const int ci = (int)(e % (uint32_t)cin);
+    const int co = (int)((e / (uint32_t)cin) % (uint32_t)copad);
+    const int t = (int)(e / ((uint32_t)cin * (uint32_t)copad));
+    return co < cout ? f2bf(wload(W, f32, ((int64_t)t * cin + ci) * cout + co)) : (uint16_t)0;
+}
+// dgrad: Wk[t'][ci][co] = W[26 - t'][ci][co], ci < cipad (zero rows beyond cin).
+__device__ __forceinline__ uint16_t wk_dgrad_elem(const void* W, bool f32, int cin, int cout, int cipad, int64_t e64)
+{
+    const uint32_t e = (uint32_t)e64;
+    const int co = (int)(e % (uint32_t)cout);
+    const int ci = (int)((e / (uint32_t)cout) % (uint32_t)cipad);
+    const int t = (int)(e / ((uint32_t)cout * (uint32_t)cipad));
+    return ci < cin ? f2bf(wload(W, f32, ((int64_t)(26 - t) * cin + ci) * cout + co)) : (uint16_t)0;
+}
+// c4:    Wk[co][k], k = t*4 + ci for t < 27, zero for k >= 108 or co >= cout.
+__device__ __forceinline__ uint16_t wk_c4_elem(const void* W, bool f32, int cout, int64_t e64)
+{
+    const uint32_t e = (uint32_t)e64;
+    const int k = (int)(e % 128u);
+    const int co = (int)(e / 128u);
+    const int t = k / 4, ci = k % 4;
+    return (co < cout && t < 27) ? f2bf(wload(W, f32, ((int64_t)t * 4 + ci) * cout + co)) : (uint16_t)0;
+}
+
+__device__ __forceinline__ int64_t wk_total(int kind, int cin, int cout, int pad)
+{
+    return kind == 0 ? (int64_t)27 * pad * cin : kind == 1 ? (int64_t)27 * pad * cout : (int64_t)pad * 128;
+}
+
 __global__ void wprep_fwd_kernel(const void* W, bool f32, int cin, int cout, int copad, uint16_t* Wk)
 {
     const int64_t total = (int64_t)27 * copad * cin;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int ci = (int)(e % cin);
-        const int co = (int)((e / cin) % copad);
-        const int t = (int)(e / ((int64_t)cin * copad));
-        Wk[e] = co < cout ? f2bf(wload(W, f32, ((int64_t)t * cin + ci) * cout + co)) : (uint16_t)0;
-    }
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+        Wk[e] = wk_fwd_elem(W, f32, cin, cout, copad, e);
 }
 
-// Wk[t'][ci][co] = W[26 - t'][ci][co], ci < cipad (zero rows beyond cin).
 __global__ void wprep_dgrad_kernel(const void* W, bool f32, int cin, int cout, int cipad, uint16_t* Wk)
 {
     const int64_t total = (int64_t)27 * cipad * cout;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int co = (int)(e % cout);
-        const int ci = (int)((e / cout) % cipad);
-        const int t = (int)(e / ((int64_t)cout * cipad));
-        Wk[e] = ci < cin ? f2bf(wload(W, f32, ((int64_t)(26 - t) * cin + ci) * cout + co)) : (uint16_t)0;
-    }
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+        Wk[e] = wk_dgrad_elem(W, f32, cin, cout, cipad, e);
 }
 
-// Wk[co][k], k = t*4 + ci for t < 27, zero for k >= 108 or co >= cout.
 __global__ void wprep_c4_kernel(const void* W, bool f32, int cout, int copad, uint16_t* Wk)
 {
     const int64_t total = (int64_t)copad * 128;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+        Wk[e] = wk_c4_elem(W, f32, cout, e);
+}
+
+// Several re-layouts in one launch: blockIdx.y picks the job.
+__global__ void wprep_multi_kernel(WprepList l)
+{
+    const WprepJob& j = l.job[blockIdx.y];
+    const int64_t total = wk_total(j.kind, j.cin, j.cout, j.pad);
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int k = (int)(e % 128);
-        const int co = (int)(e / 128);
-        const int t = k / 4, ci = k % 4;
-        Wk[e] = (co < cout && t < 27) ? f2bf(wload(W, f32, ((int64_t)t * 4 + ci) * cout + co)) : (uint16_t)0;
+        j.dst[e] = j.kind == 0 ? wk_fwd_elem(j.src, j.f32, j.cin, j.cout, j.pad, e)
+                 : j.kind == 1 ? wk_dgrad_elem(j.src, j.f32, j.cin, j.cout, j.pad, e)
+                               : wk_c4_elem(j.src, j.f32, j.cout, e);
     }
 }
 
@@ -95,6 +129,20 @@ hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, ui
 {
     hipLaunchKernelGGL(wprep_c4_kernel, dim3(blocks_for((int64_t)copad * 128)), dim3(256), 0, s, W, w_is_f32, cout,
                        copad, Wk);
+    return hipGetLastError();
+}
+
+hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s)
+{
+    if (l.count <= 0) return hipSuccess;
+    int64_t m = 1;
+    for (int i = 0; i < l.count; ++i) {
+        const WprepJob& j = l.job[i];
+        const int64_t t = j.kind == 0 ? (int64_t)27 * j.pad * j.cin : j.kind == 1 ? (int64_t)27 * j.pad * j.cout
+                                                                              : (int64_t)j.pad * 128;
+        m = t > m ? t : m;
+    }
+    hipLaunchKernelGGL(wprep_multi_kernel, dim3(blocks_for(m), (unsigned)l.count), dim3(256), 0, s, l);
     return hipGetLastError();
 }
 

@@ -158,17 +158,25 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
     // for halo w 0-15); edge blocks (X, halo w 16-17) for tid < GW_NXE.
     // 16 consecutive lanes store 16 consecutive 16-byte columns of the same
     // channel rows.
+    // The task indices are re-derived from an opaque copy of the thread id
+    // in every load and store: kept live across the compute loop they were
+    // spilled, and each scratch reload then waited for the whole in-order
+    // queue of the next box's prefetch loads.
     uint4 u[G::KB][8];
     uint4 ue[2];
-    const bool has_edge = tid < GW_NXE;
-    const int erow = tid % GW_NR, egrp = tid / GW_NR;
+    auto opaque_tid = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
 
     auto load_box = [&](const BoxPos& bp) {
         const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
         const int64_t sbase = (int64_t)n * D;
+        const int tid_ = opaque_tid();
 #pragma unroll
         for (int k = 0; k < G::KB; ++k) {
-            const int t = tid + k * G::NT;
+            const int t = tid_ + k * G::NT;
 #pragma unroll
             for (int j = 0; j < 8; ++j) u[k][j] = make_uint4(0u, 0u, 0u, 0u);
             if (t < G::NDB) {
@@ -201,7 +209,8 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
             }
         }
         ue[0] = ue[1] = make_uint4(0u, 0u, 0u, 0u);
-        if (has_edge) {
+        if (tid_ < GW_NXE) {
+            const int erow = tid_ % GW_NR, egrp = tid_ / GW_NR;
             const int hd = erow / GW_HH, hh = erow % GW_HH;
             const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
             if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
@@ -215,17 +224,21 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
         }
     };
     auto store_box = [&]() {
+        const int tid_ = opaque_tid();
 #pragma unroll
         for (int k = 0; k < G::KB; ++k) {
-            const int t = tid + k * G::NT;
+            const int t = tid_ + k * G::NT;
             if (t >= G::NB) continue;
             uint4 tr[8];
             transpose8x8(u[k], tr);
             if (t < G::NDB) {
                 const int oct = t % GW_NOCT, grp = t / GW_NOCT;
+                // octet slot (w half, box row): the 4 lane groups of a k-step then
+                // read adjacent 16-byte slots, which the LDS serves without conflict
+                const int slot = (oct & 1) * (GW_NOCT / 2) + (oct >> 1);
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint4*>(&dt[(grp * 8 + c) * GW_DROW + oct * 8]) = tr[c];
+                    *reinterpret_cast<uint4*>(&dt[(grp * 8 + c) * GW_DROW + slot * 8]) = tr[c];
             } else {
                 const int x = t - G::NDB;
                 const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
@@ -235,7 +248,8 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                     *reinterpret_cast<uint4*>(&xt[(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8]) = tr[c];
             }
         }
-        if (has_edge) {
+        if (tid_ < GW_NXE) {
+            const int erow = tid_ % GW_NR, egrp = tid_ / GW_NR;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
@@ -273,13 +287,13 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 #pragma unroll 1
         for (int s2 = 0; s2 < GW_TD; ++s2) {
             // lane group lg takes box row (td, th) = (s2, lg), both w-octets
-            const int o0 = (s2 * GW_TH + lg) * 2;           // octet index of w0 = 0
+            const int row = s2 * GW_TH + lg;
             bf16x8 a[2][2];                                 // [co fragment][octet]
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (o0 + h) * 8);
+                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (h * (GW_NOCT / 2) + row) * 8);
             const uint16_t* xr = xpl + (s2 * GW_HH + lg) * GW_XW;
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh) {
