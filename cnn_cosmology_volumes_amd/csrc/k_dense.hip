@@ -150,13 +150,18 @@ __global__ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __rest
     dW[e] = s;
 }
 
-// dX for input row i, computed by one wave: lanes stride over o, then a
-// fixed butterfly sum per batch row; lane 0 writes.  Shared by the
-// standalone backward kernel and the fused head kernel.
+// dX for input row i, computed by one wave: lanes stride over o, then the
+// 64 lane sums of the DB = 8 batch rows are reduced together in a fixed
+// order: three exchange steps (lane bits 5, 4, 3) halve the number of values
+// per lane while summing pairs, then three butterfly steps (bits 2, 1, 0) sum
+// within groups of 8 lanes; batch row b ends in lane 8 b.  Ten shuffles per
+// 8 rows instead of 48.  Shared by the standalone backward kernel and the
+// fused head kernel.
 __device__ __forceinline__ void dx_row_wave(const float* __restrict__ W, const float* __restrict__ pre,
                                             const float* __restrict__ dY, float slope, float* __restrict__ dX,
                                             uint16_t* __restrict__ dXb, int B, int In, int Out, int64_t i, int lane)
 {
+    static_assert(DB == 8, "reduction layout");
     for (int b0 = 0; b0 < B; b0 += DB) {
         const int nb = min(DB, B - b0);
         float acc[DB];
@@ -168,19 +173,47 @@ __device__ __forceinline__ void dx_row_wave(const float* __restrict__ W, const f
             for (int b = 0; b < DB; ++b)
                 if (b < nb) acc[b] = fmaf(gate(dY[(b0 + b) * Out + o], pre[(b0 + b) * Out + o], slope), w, acc[b]);
         }
+        // exchange steps: keep the half named by this lane's bit, add the
+        // partner's copy of it (lower lane's value first)
+        float v4[4], v2[2], v1;
+        {
+            const bool hi = lane & 32;
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            float v = acc[b];
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-            acc[b] = v;
-        }
-        if (lane == 0) {
-            for (int b = 0; b < nb; ++b) {
-                const int64_t o2 = (int64_t)(b0 + b) * In + i;
-                if (dXb) dXb[o2] = f2bf(acc[b]);
-                else dX[o2] = acc[b];
+            for (int k = 0; k < 4; ++k) {
+                const float send = hi ? acc[k] : acc[k + 4];
+                const float keep = hi ? acc[k + 4] : acc[k];
+                const float recv = __shfl_xor(send, 32, 64);
+                v4[k] = hi ? recv + keep : keep + recv;
             }
+        }
+        {
+            const bool hi = lane & 16;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float send = hi ? v4[k] : v4[k + 2];
+                const float keep = hi ? v4[k + 2] : v4[k];
+                const float recv = __shfl_xor(send, 16, 64);
+                v2[k] = hi ? recv + keep : keep + recv;
+            }
+        }
+        {
+            const bool hi = lane & 8;
+            const float send = hi ? v2[0] : v2[1];
+            const float keep = hi ? v2[1] : v2[0];
+            const float recv = __shfl_xor(send, 8, 64);
+            v1 = hi ? recv + keep : keep + recv;
+        }
+        // lane holds batch row b = 4 (bit 5) + 2 (bit 4) + (bit 3); sum its group of 8
+#pragma unroll
+        for (int m = 4; m >= 1; m >>= 1) {
+            const float r = __shfl_xor(v1, m, 64);
+            v1 = (lane & m) ? r + v1 : v1 + r;
+        }
+        const int b = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+        if ((lane & 7) == 0 && b < nb) {
+            const int64_t o2 = (int64_t)(b0 + b) * In + i;
+            if (dXb) dXb[o2] = f2bf(v1);
+            else dX[o2] = v1;
         }
     }
 }
