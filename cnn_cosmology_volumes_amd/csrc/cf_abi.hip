@@ -475,6 +475,8 @@ cf_status cf_dense_fwd(int32_t B, int32_t in, int32_t out, const float* X, const
     cf_status st = check_dense(B, in, out);
     if (st != CF_OK) return st;
     if (!X || !W || !pre || !Y) return fail(CF_ERR_INVALID, "cf_dense_fwd: null pointer");
+    if (!al16(X) || !al16(W) || !al16(pre) || !al16(Y) || (bias && !al16(bias)))
+        return fail(CF_ERR_INVALID, "cf_dense_fwd: pointers must be 16-byte aligned");
     const size_t need = up256(dense_fwd_part_bytes(B, in, out));
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_dense_fwd: workspace %zu < %zu bytes", ws_bytes, need);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_dense_fwd: workspace null or misaligned");
@@ -488,6 +490,8 @@ cf_status cf_dense_bwd(int32_t B, int32_t in, int32_t out, const float* X, const
     cf_status st = check_dense(B, in, out);
     if (st != CF_OK) return st;
     if (!X || !W || !pre || !dY || !dW || !db) return fail(CF_ERR_INVALID, "cf_dense_bwd: null pointer");
+    if (!al16(X) || !al16(W) || !al16(pre) || !al16(dY) || !al16(dW) || !al16(db) || (dX && !al16(dX)))
+        return fail(CF_ERR_INVALID, "cf_dense_bwd: pointers must be 16-byte aligned");
     CF_TRY_HIP(launch_dense_bwd(B, in, out, X, nullptr, W, pre, dY, slope, dX, nullptr, dW, db, stream), "dense backward");
     return CF_OK;
 }

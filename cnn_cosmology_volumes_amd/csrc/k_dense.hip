@@ -126,28 +126,35 @@ __global__ void dense_bwd_db(const float* __restrict__ pre, const float* __restr
     db[o] = s;
 }
 
+// dW[i][o] = sum over b of X[b][i] * g[b][o] (fmaf chain in b order).  A
+// thread owns four consecutive o of one i when Out % 4 == 0 (one 16-byte
+// store), else one element; the per-element operations are the same.
 __global__ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __restrict__ Xb,
                              const float* __restrict__ pre, const float* __restrict__ dY, float slope,
                              float* __restrict__ dW, int B, int In, int Out)
 {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (int64_t)In * Out) return;
-    const int o = (int)(e % Out);
-    const int64_t i = e / Out;
-    float s = 0.f;
+    const int V = (Out % 4 == 0) ? 4 : 1;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t * V >= (int64_t)In * Out) return;
+    const int64_t e0 = t * V;
+    const int o0 = (int)(e0 % Out);
+    const int64_t i = e0 / Out;
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
     for (int b0 = 0; b0 < B; b0 += DB) {
-        float x[DB], g[DB];
+        float x[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) x[b] = b0 + b < B ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-            const bool ok = b0 + b < B;
-            x[b] = ok ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
-            g[b] = ok ? gate(dY[(b0 + b) * Out + o], pre[(b0 + b) * Out + o], slope) : 0.f;
-        }
+            if (b0 + b >= B) break;
+            const int64_t r = (int64_t)(b0 + b) * Out + o0;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
-            if (b0 + b < B) s = fmaf(x[b], g[b], s);
+            for (int v = 0; v < 4; ++v)
+                if (v < V) sum[v] = fmaf(x[b], gate(dY[r + v], pre[r + v], slope), sum[v]);
+        }
     }
-    dW[e] = s;
+    if (V == 4) *reinterpret_cast<float4*>(dW + e0) = make_float4(sum[0], sum[1], sum[2], sum[3]);
+    else dW[e0] = sum[0];
 }
 
 // dX for input row i, computed by one wave: lanes stride over o, then the
@@ -410,7 +417,7 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t ndw = (int64_t)in * out;
+    const int64_t ndw = (int64_t)in * out / (out % 4 == 0 ? 4 : 1);
     hipLaunchKernelGGL(dense_bwd_dw, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, X, Xb, pre, dY, slope, dW,
                        B, in, out);
     e = hipGetLastError();

@@ -51,10 +51,6 @@ __device__ __forceinline__ uint16_t wk_c4_elem(const void* W, bool f32, int cout
     return (co < cout && t < 27) ? f2bf(wload(W, f32, ((int64_t)t * 4 + ci) * cout + co)) : (uint16_t)0;
 }
 
-__device__ __forceinline__ int64_t wk_total(int kind, int cin, int cout, int pad)
-{
-    return kind == 0 ? (int64_t)27 * pad * cin : kind == 1 ? (int64_t)27 * pad * cout : (int64_t)pad * 128;
-}
 
 __global__ void wprep_fwd_kernel(const void* W, bool f32, int cin, int cout, int copad, uint16_t* Wk)
 {
@@ -77,15 +73,51 @@ __global__ void wprep_c4_kernel(const void* W, bool f32, int cout, int copad, ui
         Wk[e] = wk_c4_elem(W, f32, cout, e);
 }
 
-// Several re-layouts in one launch: blockIdx.y picks the job.
-__global__ void wprep_multi_kernel(WprepList l)
+// Several re-layouts in one launch: blockIdx.y picks the job.  The fwd and
+// c4 layouts transpose (input channel or k) x (output channel) matrices, so
+// those jobs go through 32 x 32 LDS tiles: the fp32 source is read along its
+// contiguous output channels and the bf16 copy written along its contiguous
+// rows.  The dgrad layout keeps the source's channel order and is copied
+// element by element.  Values are the same f2bf roundings either way.
+constexpr int WT = 32;
+
+__global__ __launch_bounds__(256)
+void wprep_multi_kernel(WprepList l)
 {
+    __shared__ float tile[WT][WT + 1];
     const WprepJob& j = l.job[blockIdx.y];
-    const int64_t total = wk_total(j.kind, j.cin, j.cout, j.pad);
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        j.dst[e] = j.kind == 0 ? wk_fwd_elem(j.src, j.f32, j.cin, j.cout, j.pad, e)
-                 : j.kind == 1 ? wk_dgrad_elem(j.src, j.f32, j.cin, j.cout, j.pad, e)
-                               : wk_c4_elem(j.src, j.f32, j.cout, e);
+    if (j.kind == 1) {
+        const int64_t total = (int64_t)27 * j.pad * j.cout;
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+            j.dst[e] = wk_dgrad_elem(j.src, j.f32, j.cin, j.cout, j.pad, e);
+        return;
+    }
+    // source S[r][c] (c = output channel, contiguous), R rows per matrix;
+    // destination D[c][r] with row length Rpad, c < pad (zero beyond cout),
+    // r < Rpad (zero beyond R)
+    const bool c4 = j.kind == 2;
+    const int R = c4 ? 108 : j.cin, Rpad = c4 ? 128 : j.cin, C = j.cout, Cpad = j.pad;
+    const int nmat = c4 ? 1 : 27;
+    const int tr = (Rpad + WT - 1) / WT, tc = (Cpad + WT - 1) / WT;
+    const int ntiles = nmat * tr * tc;
+    const int lx = threadIdx.x % WT, ly = threadIdx.x / WT;     // 32 x 8
+    for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+        const int m = tile_id / (tr * tc), rt = (tile_id / tc) % tr, ct = tile_id % tc;
+        const int r0 = rt * WT, c0 = ct * WT;
+        const int64_t sbase = (int64_t)m * R * C, dbase = (int64_t)m * Cpad * Rpad;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WT / 8; ++k) {
+            const int r = r0 + ly + 8 * k, c = c0 + lx;
+            tile[ly + 8 * k][lx] = (r < R && c < C) ? wload(j.src, j.f32, sbase + (int64_t)r * C + c) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WT / 8; ++k) {
+            const int c = c0 + ly + 8 * k, r = r0 + lx;
+            if (c < Cpad && r < Rpad)
+                j.dst[dbase + (int64_t)c * Rpad + r] = (r < R && c < C) ? f2bf(tile[lx][ly + 8 * k]) : (uint16_t)0;
+        }
     }
 }
 
@@ -138,11 +170,14 @@ hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s)
     int64_t m = 1;
     for (int i = 0; i < l.count; ++i) {
         const WprepJob& j = l.job[i];
-        const int64_t t = j.kind == 0 ? (int64_t)27 * j.pad * j.cin : j.kind == 1 ? (int64_t)27 * j.pad * j.cout
-                                                                              : (int64_t)j.pad * 128;
-        m = t > m ? t : m;
+        int64_t b;
+        if (j.kind == 1) b = blocks_for((int64_t)27 * j.pad * j.cout);
+        else if (j.kind == 0) b = (int64_t)27 * ((j.cin + WT - 1) / WT) * ((j.pad + WT - 1) / WT);
+        else b = (int64_t)(128 / WT) * ((j.pad + WT - 1) / WT);
+        m = b > m ? b : m;
     }
-    hipLaunchKernelGGL(wprep_multi_kernel, dim3(blocks_for(m), (unsigned)l.count), dim3(256), 0, s, l);
+    if (m > 4096) m = 4096;
+    hipLaunchKernelGGL(wprep_multi_kernel, dim3((unsigned)m, (unsigned)l.count), dim3(256), 0, s, l);
     return hipGetLastError();
 }
 

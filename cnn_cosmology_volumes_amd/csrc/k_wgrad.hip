@@ -658,12 +658,13 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
 }
 
 // dW[e] = sum over splits of part[s][e].  A block owns RD_E consecutive
-// elements (4 per thread, 16-byte loads); its 16 split-lanes each sum the
+// elements (4 per thread, 16-byte loads; small blocks, so even a few
+// thousand elements spread over all CUs); its 16 split-lanes each sum the
 // splits s = lane, lane + 16, ... in increasing order, and the 16 lane sums
 // are added in lane order.  The order is fixed, so the result is
 // deterministic.  n must be a multiple of 4 (27 * Cin * Cout with Cin a
 // multiple of 4).
-constexpr int RD_T = 64, RD_E = RD_T * 4, RD_L = 16;
+constexpr int RD_T = 16, RD_E = RD_T * 4, RD_L = 16;   // 256 threads, 64 elements per block
 
 __global__ __launch_bounds__(RD_T * RD_L)
 void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW, int64_t n, int splits)

@@ -86,6 +86,9 @@ def test_pool_and_elementwise_validation():
     assert L.cf_dense_fwd(0, 4, 4, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 1 << 20, None) == cf.CF_ERR_INVALID
     assert L.cf_dense_fwd(8, 16384, 128, FAKE, FAKE, None, 0.3, FAKE, FAKE, FAKE, 0, None) == cf.CF_ERR_WORKSPACE
     assert L.cf_dense_workspace_size(8, 16384, 128) == 128 * 8 * 128 * 4
+    # dense pointers must be 16-byte aligned (the kernels use 16-byte stores)
+    assert L.cf_dense_fwd(8, 64, 16, FAKE, MIS, None, 0.3, FAKE, FAKE, FAKE, 1 << 20, None) == cf.CF_ERR_INVALID
+    assert L.cf_dense_bwd(8, 64, 16, FAKE, FAKE, FAKE, FAKE, 0.3, None, MIS, FAKE, None) == cf.CF_ERR_INVALID
     assert L.cf_mse(0, 3, FAKE, FAKE, FAKE, None, None) == cf.CF_ERR_INVALID
     assert L.cf_sgd(10, 1e-3, None, FAKE, None) == cf.CF_ERR_INVALID
 
