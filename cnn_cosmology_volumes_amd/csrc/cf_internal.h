@@ -83,6 +83,7 @@ struct ConvPlan {
     int cfg;          // tile configuration id
     int bm;           // out-channels per block
     int splits;       // split over in-channel chunks (fp32 partials when > 1)
+    bool ring;        // weights through the block's LDS ring (else per-wave loads)
     size_t part_bytes;
 };
 ConvPlan plan_conv_mfma(const cf_dims& x, int cout);
