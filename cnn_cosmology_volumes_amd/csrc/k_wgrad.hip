@@ -20,6 +20,8 @@
 // order by wgrad_reduce: the result is deterministic.
 #include "cf_internal.h"
 
+#include <type_traits>
+
 namespace cf {
 
 namespace {
@@ -415,13 +417,20 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     const int pv = is_pg ? tid >> 2 : (tid - 128) >> 1;
     const int pc = is_pg ? (tid & 3) * 8 : ((tid - 128) & 1) * 16;
 
-    // staging registers: non-fused dY 8 voxels x 4 co; fused pooled dP/P (8 co)
-    // or 16 indices; ux: X 8 voxels x 4 ci
-    uint2 ud[8];
-    uint4 upd, upp;
-    uint2 ux[8];
+    // staging registers, two sets (the box loop is unrolled by two, so each
+    // box's loads are issued two compute phases before they are stored):
+    // non-fused dY 8 voxels x 4 co; fused pooled dP/P (8 co) or 16 indices;
+    // ux: X 8 voxels x 4 ci
+    uint2 ud_[2][8];
+    uint4 upd_[2], upp_[2];
+    uint2 ux_[2][8];
 
-    auto load_box = [&](const BoxPos& bp) {
+    auto load_box = [&](const BoxPos& bp, auto set) {
+        constexpr int S = decltype(set)::value;
+        uint2 (&ud)[8] = ud_[S];
+        uint4& upd = upd_[S];
+        uint4& upp = upp_[S];
+        uint2 (&ux)[8] = ux_[S];
         const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
 #pragma unroll
         for (int j = 0; j < 8; ++j) { ud[j] = make_uint2(0u, 0u); ux[j] = make_uint2(0u, 0u); }
@@ -477,7 +486,12 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         }
     };
 
-    auto store_box = [&](int buf) {
+    auto store_box = [&](int buf, auto set) {
+        constexpr int S = decltype(set)::value;
+        uint2 (&ud)[8] = ud_[S];
+        const uint4& upd = upd_[S];
+        const uint4& upp = upp_[S];
+        uint2 (&ux)[8] = ux_[S];
         if (!FUSED) {
             uint4 t[4];
             transpose8x4(ud, t);
@@ -566,17 +580,9 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
 
     const int64_t b_begin = (int64_t)split * boxes_per_split;
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
-    BoxPos bp = box_decode(b_begin, bD, bH, bW);
-    load_box(bp);
-    store_box(0);
-    __syncthreads();
-    int buf = 0;
-    for (int64_t box = b_begin; box < b_end; ++box) {
-        const bool more = box + 1 < b_end;
-        if (more) {
-            bp = box_next(bp, bD, bH, bW);
-            load_box(bp);
-        }
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
+    auto compute_box = [&](int buf) {
         const uint16_t* xb = xt[buf];
         const uint16_t* db = dt[buf];
 #pragma unroll
@@ -607,11 +613,37 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
                 }
             }
         }
-        if (more) {
-            store_box(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
+    };
+    BoxPos bp = box_decode(b_begin, bD, bH, bW);
+    load_box(bp, Set0{});
+    store_box(0, Set0{});
+    __syncthreads();
+    if (b_begin + 1 < b_end) {
+        bp = box_next(bp, bD, bH, bW);
+        load_box(bp, Set1{});
+    }
+    int buf = 0;
+    for (int64_t box = b_begin; box < b_end; box += 2) {
+        // box is in LDS buffer buf, box + 1 in register set 1; set 0 is free
+        if (box + 2 < b_end) {
+            bp = box_next(bp, bD, bH, bW);
+            load_box(bp, Set0{});
         }
+        compute_box(buf);
+        if (box + 1 >= b_end) break;
+        store_box(buf ^ 1, Set1{});
+        __syncthreads();
+        buf ^= 1;
+        // box + 1 is in LDS, box + 2 in register set 0; set 1 is free
+        if (box + 3 < b_end) {
+            bp = box_next(bp, bD, bH, bW);
+            load_box(bp, Set1{});
+        }
+        compute_box(buf);
+        if (box + 2 >= b_end) break;
+        store_box(buf ^ 1, Set0{});
+        __syncthreads();
+        buf ^= 1;
     }
 
     // Sum the four waves' accumulators in the order ((w0 + w3) + w2) + w1.
