@@ -91,11 +91,11 @@ Fwd dgrad_path(cf_dtype dt, int64_t cin, int cout)
     return Fwd::Direct;
 }
 
-Wg wgrad_path(cf_dtype dt, int64_t cin, int cout)
+Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     if (dt == CF_BF16) {
-        if (cin % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
-        if (cin == 4 && cout == 32) return Wg::C4;
+        if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
+        if (x.c == 4 && cout == 32 && wgrad_c4_fits(x)) return Wg::C4;
     }
     return Wg::Direct;
 }
@@ -114,7 +114,7 @@ bool fused_pool_fwd(cf_dtype dt, const cf_dims& x, int cout)
 {
     return fused_pool_fwd_c4(dt, x.c, cout) || fused_pool_fwd_mfma(dt, x, cout);
 }
-bool fused_pool_wgrad(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout == 32; }
+bool fused_pool_wgrad(cf_dtype dt, const cf_dims& x, int cout) { return wgrad_path(dt, x, cout) == Wg::C4; }
 
 // Bytes of re-laid weights each path uses.
 size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
@@ -246,7 +246,7 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
         return up256(dgrad_wk_bytes(p, dtype, x.c, cout)) + up256(dgrad_part_bytes(p, x, cout));
     }
     case CF_CONV_BWD_WEIGHT:
-        return up256(wgrad_part_bytes(wgrad_path(dtype, x.c, cout), dtype, x, cout));
+        return up256(wgrad_part_bytes(wgrad_path(dtype, x, cout), dtype, x, cout));
     case CF_CONV_POOL_FWD: {
         if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
         const Fwd p = fwd_path(dtype, x.c, cout);
@@ -255,8 +255,8 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
     }
     case CF_POOL_CONV_BWD_WEIGHT: {
         if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
-        const size_t z = fused_pool_wgrad(dtype, x.c, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
-        return up256(wgrad_part_bytes(wgrad_path(dtype, x.c, cout), dtype, x, cout)) + up256(z);
+        const size_t z = fused_pool_wgrad(dtype, x, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
+        return up256(wgrad_part_bytes(wgrad_path(dtype, x, cout), dtype, x, cout)) + up256(z);
     }
     default:
         return 0;
@@ -318,8 +318,8 @@ cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, co
     if (!al16(X) || !al16(dP) || !al16(P) || !al16(idx) || !al16(dW))
         return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: pointers must be 16-byte aligned");
     if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: slope is NaN");
-    const Wg p = wgrad_path(dtype, x.c, cout);
-    const bool fused = fused_pool_wgrad(dtype, x.c, cout);
+    const Wg p = wgrad_path(dtype, x, cout);
+    const bool fused = fused_pool_wgrad(dtype, x, cout);
     const size_t pb = up256(wgrad_part_bytes(p, dtype, x, cout));
     const size_t zb = fused ? 0 : up256((size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype));
     if (ws_bytes < pb + zb)
@@ -390,7 +390,7 @@ cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const v
     if (st != CF_OK) return st;
     if (!X || !dY || !dW) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: null tensor pointer");
     if (!al16(X) || !al16(dY) || !al16(dW)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: pointers must be 16-byte aligned");
-    const Wg p = wgrad_path(dtype, x.c, cout);
+    const Wg p = wgrad_path(dtype, x, cout);
     const size_t need = up256(wgrad_part_bytes(p, dtype, x, cout));
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_bwd_weight: workspace %zu < %zu bytes", ws_bytes, need);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: workspace null or misaligned");
@@ -574,12 +574,12 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         Lp.cout = m->filters[l];
         Lp.fwd = fwd_path(dt, x.c, Lp.cout);
         Lp.dg = dgrad_path(dt, x.c, Lp.cout);
-        Lp.wg = wgrad_path(dt, x.c, Lp.cout);
+        Lp.wg = wgrad_path(dt, x, Lp.cout);
         const int64_t nvox = x.n * x.d * x.h * x.w;
         const int64_t npool = nvox / 8;
         Lp.wk_fwd = take(Lp.fwd == Fwd::Direct ? 0 : fwd_wk_bytes(Lp.fwd, x.c, Lp.cout));
         Lp.wk_dg = take(l > 0 ? dgrad_wk_bytes(Lp.dg, dt, x.c, Lp.cout) : 0);
-        Lp.fused = l == 0 && fused_pool_fwd_c4(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x.c, Lp.cout);
+        Lp.fused = l == 0 && fused_pool_fwd_c4(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x, Lp.cout);
         Lp.pool_fused = !Lp.fused && fused_pool_fwd_mfma(dt, x, Lp.cout);
         Lp.z = take(Lp.fused ? 0 : (size_t)nvox * Lp.cout * es);
         Lp.p = take((size_t)npool * Lp.cout * es);

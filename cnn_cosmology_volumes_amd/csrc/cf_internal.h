@@ -50,6 +50,24 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
     return (b % 8u) * per + (b / 8u);
 }
 
+// Workgroup barrier for LDS traffic only: waits until this wave's LDS
+// accesses are done (lgkmcnt 0) but leaves its global loads in flight,
+// which __syncthreads() would drain (its fence waits for vmcnt 0 as well).
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Raw buffer resource over `bytes` bytes from p.  A lane whose offset is
+// >= bytes reads zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // ----------------------------------------------------------------- launchers
 // Every launcher enqueues on `s` and returns hipGetLastError() of the launch.
 
@@ -113,6 +131,9 @@ struct WgradPlan {
     size_t part_bytes;
 };
 WgradPlan plan_wgrad(const cf_dims& x, int cout);
+// The Cin == 4 kernel addresses each box through 32-bit offsets from the
+// box's first (d) plane; that needs H * W <= 2^23.
+bool wgrad_c4_fits(const cf_dims& x);
 hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, float* part, float* dW,
                         const cf_dims& x, int cout, hipStream_t s);
 // Cin == 4, cout == 32 backward-weight with the pool backward fused into the

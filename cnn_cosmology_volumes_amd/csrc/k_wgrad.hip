@@ -98,6 +98,17 @@ __device__ __forceinline__ BoxPos box_next(BoxPos p, int bD, int bH, int bW)
     return p;
 }
 
+// The same position, marked wave-uniform (scalar registers), so that
+// buffer resources built from it need no per-lane handling.
+__device__ __forceinline__ BoxPos box_uniform(BoxPos p)
+{
+    p.n = __builtin_amdgcn_readfirstlane(p.n);
+    p.bd = __builtin_amdgcn_readfirstlane(p.bd);
+    p.bh = __builtin_amdgcn_readfirstlane(p.bh);
+    p.bw = __builtin_amdgcn_readfirstlane(p.bw);
+    return p;
+}
+
 // 8x8 transpose of bf16: in[v] holds 8 channels of voxel v; out[c] holds
 // voxel 0..7 of channel c.
 __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8])
@@ -365,8 +376,13 @@ constexpr int C4_VB = C4_TD * C4_TH * C4_TW;               // 256 voxels per box
 constexpr int C4_NOCT = C4_VB / 8;                         // 32 octets
 constexpr int C4_HH = C4_TH + 2;
 constexpr int C4_NR = (C4_TD + 2) * C4_HH;                 // 36 halo rows
-constexpr int C4_XW = 24;
-constexpr int C4_XPL = C4_NR * C4_XW + 16;                 // per-channel plane: 1760 B (odd multiple of 32)
+// X tile [ci][halo row][w]: 64-byte rows and a 2336-byte channel plane.  The
+// operand read pairs 4 channels with 4 (kd,kh) rows per 16 lanes; of the
+// plane/row pitches that keep 16-byte alignment, this pair gave the fewest
+// LDS bank conflicts for that pattern when measured on gfx950 (about 7 clk
+// per 16-byte wave read against 12 with 48-byte rows and 1760-byte planes).
+constexpr int C4_XW = 32;
+constexpr int C4_XPL = C4_NR * C4_XW + 16;                 // per-channel plane: 2336 B
 constexpr int C4_DROW = C4_VB + 16;                        // dYT row: 544 B (odd multiple of 32)
 constexpr int C4_NT = 256;
 constexpr int C4_NDB = C4_NOCT * 4;                        // dY blocks: 32 octets x 4 groups of 8 co
@@ -385,9 +401,15 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) uint16_t xt[2][4 * C4_XPL];
     __shared__ __attribute__((aligned(16))) uint16_t dt[2][CO * C4_DROW];
     __shared__ __attribute__((aligned(16))) float red[64 * C4_NACC * 4];
-    // fused: the box's gated pooled gradient (bf16) and window indices, [pooled voxel][co]
-    __shared__ __attribute__((aligned(16))) uint16_t gtile[FUSED ? C4_NPV * CO : 8];
-    __shared__ __attribute__((aligned(16))) uint8_t itile[FUSED ? C4_NPV * CO : 16];
+    // fused: the box's gated pooled gradient (bf16) and window indices, stored
+    // [4-channel group][pooled voxel] so that a thread's 4 pooled voxels x 4
+    // channels are contiguous (two 16-byte reads of gradient, one of
+    // indices).  The gradient's group stride of 34 entries (272 B) and the
+    // index group stride of 128 B put the two groups a wave reads on
+    // disjoint banks.
+    constexpr int GT_S = C4_NPV + 2;                        // gradient entries per channel group
+    __shared__ __attribute__((aligned(16))) uint16_t gtile[FUSED ? 8 * GT_S * 4 : 8];
+    __shared__ __attribute__((aligned(16))) uint32_t itile[FUSED ? 8 * C4_NPV : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -417,56 +439,77 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     const int pv = is_pg ? tid >> 2 : (tid - 128) >> 1;
     const int pc = is_pg ? (tid & 3) * 8 : ((tid - 128) & 1) * 16;
 
-    // staging registers, two sets (the box loop is unrolled by two, so each
+    // Staging registers, two sets (the box loop is unrolled by two, so each
     // box's loads are issued two compute phases before they are stored):
     // non-fused dY 8 voxels x 4 co; fused pooled dP/P (8 co) or 16 indices;
-    // ux: X 8 voxels x 4 ci
+    // ux: X 8 voxels x 4 ci.
+    //
+    // Every wave issues the same buffer loads for every box, whatever its
+    // role and wherever the box lies: a lane with nothing to fetch (no role,
+    // a voxel outside the volume, a box past the end of the split) gets an
+    // offset beyond the resource and reads zeros without a memory access.
+    // With no load under a branch, the number of loads in flight is the same
+    // on every path, so the compiler waits only for the set being stored and
+    // leaves the other set in flight (a conditional load makes it wait for
+    // all of them).  Offsets are 32-bit, relative to the box's first plane.
     uint2 ud_[2][8];
     uint4 upd_[2], upp_[2];
     uint2 ux_[2][8];
+    constexpr uint32_t OOB = 0x80000000u;
+    // offset or OOB, held in a register so the choice stays a select (the
+    // compiler would otherwise turn it into a branch around the load)
+    auto pick = [](bool ok, uint32_t off) {
+        uint32_t r = ok ? off : OOB;
+        asm volatile("" : "+v"(r));
+        return r;
+    };
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int hd_x = row / C4_HH, hh_x = row % C4_HH;
 
-    auto load_box = [&](const BoxPos& bp, auto set) {
+    auto load_box = [&](const BoxPos& bp, bool valid, auto set) {
         constexpr int S = decltype(set)::value;
         uint2 (&ud)[8] = ud_[S];
         uint4& upd = upd_[S];
         uint4& upp = upp_[S];
         uint2 (&ux)[8] = ux_[S];
-        const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { ud[j] = make_uint2(0u, 0u); ux[j] = make_uint2(0u, 0u); }
-        upd = upp = make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t lim = valid ? OOB : 0u;
+        const int gd0 = bp.bd * C4_TD;
         if (!FUSED) {
-            const int gd = bd * C4_TD + td_o, gh = bh * C4_TH + th_o, gw0 = bw * C4_TW + w0_o;
-            if (gd < D && gh < H) {
-                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+            const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * CO, lim);
+            const int gh = bp.bh * C4_TH + th_o, gw0 = bp.bw * C4_TW + w0_o;
+            const bool rok = (gd0 + td_o < D) & (gh < H);
+            const uint32_t rbase = ((uint32_t)td_o * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (gw0 + j < W) ud[j] = *reinterpret_cast<const uint2*>(dY + (rowv + gw0 + j) * CO + cg * 4);
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t off = pick(rok & (gw0 + j < W), (rbase + j) * (CO * 2) + cg * 8);
+                ud[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rd, off, 0, 0));
             }
-        } else if (is_pg || is_pi) {
-            const int pd = bd * (C4_TD / 2) + pv / 16, ph = bh * (C4_TH / 2) + (pv / 8) % 2,
-                      pw = bw * (C4_TW / 2) + pv % 8;
-            if (pd < Dp && ph < Hp && pw < Wp) {
-                const int64_t o = ((((int64_t)n * Dp + pd) * Hp + ph) * Wp + pw) * CO + pc;
-                if (is_pg) {
-                    upd = *reinterpret_cast<const uint4*>(dP + o);
-                    upp = *reinterpret_cast<const uint4*>(Pv + o);
-                } else {
-                    upd = *reinterpret_cast<const uint4*>(pidx + o);
-                }
-            }
+        } else {
+            // waves 0-1: dP and P; wave 2: window indices; wave 3: nothing
+            const int pd0 = bp.bd * (C4_TD / 2);
+            const int64_t pe = ((int64_t)bp.n * Dp + pd0) * ((int64_t)Hp * Wp) * CO;
+            const auto r1 = wu == 2 ? buf_rsrc(pidx + pe, lim) : buf_rsrc(dP + pe, lim);
+            const auto r2 = buf_rsrc(Pv + pe, lim);
+            const int pd = pd0 + pv / 16, ph = bp.bh * (C4_TH / 2) + (pv / 8) % 2, pw = bp.bw * (C4_TW / 2) + pv % 8;
+            const bool pok = (is_pg | is_pi) & (pd < Dp) & (ph < Hp) & (pw < Wp);
+            const uint32_t e = ((uint32_t)(pd - pd0) * (uint32_t)Hp + (uint32_t)ph) * (uint32_t)Wp * CO +
+                               (uint32_t)pw * CO + (uint32_t)pc;
+            const uint32_t off1 = pick(pok, is_pg ? 2 * e : e);
+            const uint32_t off2 = pick(pok & is_pg, 2 * e);
+            upd = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, off1, 0, 0));
+            upp = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r2, off2, 0, 0));
         }
-        if (is_x) {
-            const int hd = row / C4_HH, hh = row % C4_HH;
-            const int gd = bd * C4_TD + hd - 1, gh = bh * C4_TH + hh - 1;
-            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
-                const int64_t rowv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W;
+        // X halo planes gd0-1 .. gd0+4, addressed from the first one inside the volume
+        const int xd0 = gd0 > 0 ? gd0 - 1 : 0;
+        const auto rx = buf_rsrc(X + ((int64_t)bp.n * D + xd0) * plane * 4, lim);
+        const int gd = gd0 + hd_x - 1, gh = bp.bh * C4_TH + hh_x - 1;
+        const bool rok = is_x & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
+        const int gwb = bp.bw * C4_TW + 8 * slot - 1;
+        const uint32_t rbase = ((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int gw = bw * C4_TW + 8 * slot + j - 1;
-                    if (j < nvl && (unsigned)gw < (unsigned)W) ux[j] = *reinterpret_cast<const uint2*>(X + (rowv + gw) * 4);
-                }
-            }
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = pick(rok & (j < nvl) & ((unsigned)(gwb + j) < (unsigned)W), (rbase + j) * 8u);
+            ux[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0));
         }
     };
 
@@ -492,6 +535,17 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         const uint4& upd = upd_[S];
         const uint4& upp = upp_[S];
         uint2 (&ux)[8] = ux_[S];
+        // Every lane takes delivery of the whole set here, whatever its role,
+        // so the loads are complete on every path before their registers are
+        // reused (a use only under a role branch leaves them pending on the
+        // other paths, and the next write to those registers waits for all
+        // loads in flight).
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (!FUSED) asm volatile("" ::"v"(ud[j].x), "v"(ud[j].y));
+            asm volatile("" ::"v"(ux[j].x), "v"(ux[j].y));
+        }
+        if (FUSED) asm volatile("" ::"v"(upd.x), "v"(upd.y), "v"(upd.z), "v"(upd.w), "v"(upp.x), "v"(upp.y), "v"(upp.z), "v"(upp.w));
         if (!FUSED) {
             uint4 t[4];
             transpose8x4(ud, t);
@@ -512,9 +566,13 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
                     gh_ = ph > 0.f ? gh_ : slope * gh_;
                     g[m] = pack_bf16x2(gl, gh_);
                 }
-                *reinterpret_cast<uint4*>(&gtile[pv * CO + pc]) = make_uint4(g[0], g[1], g[2], g[3]);
+                *reinterpret_cast<uint2*>(&gtile[((pc / 4) * GT_S + pv) * 4]) = make_uint2(g[0], g[1]);
+                *reinterpret_cast<uint2*>(&gtile[((pc / 4 + 1) * GT_S + pv) * 4]) = make_uint2(g[2], g[3]);
             } else if (is_pi) {
-                *reinterpret_cast<uint4*>(&itile[pv * CO + pc]) = upd;
+                itile[(pc / 4) * C4_NPV + pv] = upd.x;
+                itile[(pc / 4 + 1) * C4_NPV + pv] = upd.y;
+                itile[(pc / 4 + 2) * C4_NPV + pv] = upd.z;
+                itile[(pc / 4 + 3) * C4_NPV + pv] = upd.w;
             }
         }
         if (is_x) {
@@ -528,19 +586,18 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             }
         }
         if (FUSED) {
-            __syncthreads();
+            lds_barrier();
             // Rebuild this thread's 8 voxels x 4 channels of dY: a voxel gets the
             // gated gradient of its pooled voxel where the window index names it.
             const uint32_t pos_ab = (uint32_t)((td_o & 1) * 4 + (th_o & 1) * 2);
             const int pv0 = ((td_o >> 1) * 2 + (th_o >> 1)) * 8 + w0_o / 2;
             uint4 t[4];
-            uint2 gq[4];
-            uint32_t iq[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                gq[k] = *reinterpret_cast<const uint2*>(&gtile[(pv0 + k) * CO + cg * 4]);
-                iq[k] = *reinterpret_cast<const uint32_t*>(&itile[(pv0 + k) * CO + cg * 4]);
-            }
+            const uint4 g01 = *reinterpret_cast<const uint4*>(&gtile[(cg * GT_S + pv0) * 4]);
+            const uint4 g23 = *reinterpret_cast<const uint4*>(&gtile[(cg * GT_S + pv0 + 2) * 4]);
+            const uint4 i4 = *reinterpret_cast<const uint4*>(&itile[cg * C4_NPV + pv0]);
+            const uint2 gq[4] = {make_uint2(g01.x, g01.y), make_uint2(g01.z, g01.w), make_uint2(g23.x, g23.y),
+                                 make_uint2(g23.z, g23.w)};
+            const uint32_t iq[4] = {i4.x, i4.y, i4.z, i4.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 uint32_t d[4];
@@ -614,35 +671,33 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             }
         }
     };
-    BoxPos bp = box_decode(b_begin, bD, bH, bW);
-    load_box(bp, Set0{});
+    // The loop handles two boxes per iteration and leaves only at its end:
+    // an exit between the halves would be a path on which the set loaded
+    // for the next box is never consumed, and the compiler would then drain
+    // every load at the top of each iteration.  With an odd number of boxes
+    // the last half computes a box past the end, which was loaded as zeros
+    // and adds exactly zero.
+    BoxPos bp = box_uniform(box_decode(b_begin, bD, bH, bW));
+    load_box(bp, true, Set0{});
     store_box(0, Set0{});
-    __syncthreads();
-    if (b_begin + 1 < b_end) {
-        bp = box_next(bp, bD, bH, bW);
-        load_box(bp, Set1{});
-    }
+    lds_barrier();
+    bp = box_uniform(box_next(bp, bD, bH, bW));
+    load_box(bp, b_begin + 1 < b_end, Set1{});
     int buf = 0;
     for (int64_t box = b_begin; box < b_end; box += 2) {
         // box is in LDS buffer buf, box + 1 in register set 1; set 0 is free
-        if (box + 2 < b_end) {
-            bp = box_next(bp, bD, bH, bW);
-            load_box(bp, Set0{});
-        }
+        bp = box_uniform(box_next(bp, bD, bH, bW));
+        load_box(bp, box + 2 < b_end, Set0{});
         compute_box(buf);
-        if (box + 1 >= b_end) break;
         store_box(buf ^ 1, Set1{});
-        __syncthreads();
+        lds_barrier();
         buf ^= 1;
         // box + 1 is in LDS, box + 2 in register set 0; set 1 is free
-        if (box + 3 < b_end) {
-            bp = box_next(bp, bD, bH, bW);
-            load_box(bp, Set1{});
-        }
+        bp = box_uniform(box_next(bp, bD, bH, bW));
+        load_box(bp, box + 3 < b_end, Set1{});
         compute_box(buf);
-        if (box + 2 >= b_end) break;
         store_box(buf ^ 1, Set0{});
-        __syncthreads();
+        lds_barrier();
         buf ^= 1;
     }
 
@@ -735,6 +790,11 @@ void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW,
 }
 
 }  // namespace
+
+bool wgrad_c4_fits(const cf_dims& x)
+{
+    return x.h * x.w <= ((int64_t)1 << 23);
+}
 
 WgradPlan plan_wgrad(const cf_dims& x, int cout)
 {
