@@ -655,8 +655,11 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             for (int f = 0; f < 3; ++f) {
                 const int r = (td + pkd[f]) * C4_HH + th + pkh[f];
                 const uint16_t* xp = xb + ci * C4_XPL + r * C4_XW + w0;
-                const uint4 q = *reinterpret_cast<const uint4*>(xp);
-                const uint32_t e = reinterpret_cast<const uint4*>(xp)[1].x;
+                uint4 q = *reinterpret_cast<const uint4*>(xp);
+                uint32_t e = reinterpret_cast<const uint4*>(xp)[1].x;
+                // opaque to the optimizer: it would otherwise re-read the kw = 2
+                // operand (bytes 4..19, unaligned) from LDS as two more reads
+                asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w), "+v"(e));
                 const uint4 s1 = make_uint4(__builtin_amdgcn_alignbit(q.y, q.x, 16), __builtin_amdgcn_alignbit(q.z, q.y, 16),
                                             __builtin_amdgcn_alignbit(q.w, q.z, 16), __builtin_amdgcn_alignbit(e, q.w, 16));
                 const bf16x8 b0 = __builtin_bit_cast(bf16x8, q);
