@@ -598,19 +598,31 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             const uint2 gq[4] = {make_uint2(g01.x, g01.y), make_uint2(g01.z, g01.w), make_uint2(g23.x, g23.y),
                                  make_uint2(g23.z, g23.w)};
             const uint32_t iq[4] = {i4.x, i4.y, i4.z, i4.w};
+            // Byte lookups (v_perm) instead of per-channel compares: x has byte
+            // c = idx_c ^ pos, which is 0 where the window maximum is the even-w
+            // voxel of this thread's pair and 1 where it is the odd one (pos is
+            // even); a lookup turns those bytes into 0xff masks for all four
+            // channels at once, the masks are widened to the 16-bit lanes of
+            // the gradient pairs, and a permute assembles each output word
+            // (even voxel in the low half, odd voxel in the high half).
+            const uint32_t posrep = pos_ab * 0x01010101u;
+            uint32_t wd[4][4];                        // [pooled voxel k][channel c]
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                uint32_t d[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {          // voxels 2k, 2k+1 share pooled voxel k
-                    const uint32_t ib = (iq[k] >> (8 * c)) & 0xffu;
-                    const uint32_t gv = ((c >> 1 ? gq[k].y : gq[k].x) >> (16 * (c & 1))) & 0xffffu;
-                    const uint32_t lo = ib == pos_ab ? gv : 0u;
-                    const uint32_t hi = ib == pos_ab + 1u ? gv : 0u;
-                    d[k] = lo | (hi << 16);
-                }
-                t[c] = make_uint4(d[0], d[1], d[2], d[3]);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t x = iq[k] ^ posrep;
+                const uint32_t lom = __builtin_amdgcn_perm(0u, 0x000000ffu, x);
+                const uint32_t him = __builtin_amdgcn_perm(0u, 0x0000ff00u, x);
+                const uint32_t a01 = gq[k].x & __builtin_amdgcn_perm(lom, lom, 0x01010000u);
+                const uint32_t b01 = gq[k].x & __builtin_amdgcn_perm(him, him, 0x01010000u);
+                const uint32_t a23 = gq[k].y & __builtin_amdgcn_perm(lom, lom, 0x03030202u);
+                const uint32_t b23 = gq[k].y & __builtin_amdgcn_perm(him, him, 0x03030202u);
+                wd[k][0] = __builtin_amdgcn_perm(b01, a01, 0x05040100u);
+                wd[k][1] = __builtin_amdgcn_perm(b01, a01, 0x07060302u);
+                wd[k][2] = __builtin_amdgcn_perm(b23, a23, 0x05040100u);
+                wd[k][3] = __builtin_amdgcn_perm(b23, a23, 0x07060302u);
             }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = make_uint4(wd[0][c], wd[1][c], wd[2][c], wd[3][c]);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 *reinterpret_cast<uint4*>(&dt[buf][(cg * 4 + c) * C4_DROW + oct * 8]) = t[c];
