@@ -311,9 +311,13 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh) {
                 const uint16_t* xp = xr + kh * GW_XW;
-                const uint4 q0 = *reinterpret_cast<const uint4*>(xp);
-                const uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
-                const uint32_t e1 = *reinterpret_cast<const uint32_t*>(xp + 16);   // halo w 16-17
+                uint4 q0 = *reinterpret_cast<const uint4*>(xp);
+                uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
+                uint32_t e1 = *reinterpret_cast<const uint32_t*>(xp + 16);         // halo w 16-17
+                // opaque to the optimizer, which would otherwise re-read the
+                // kw = 2 operands (unaligned) from LDS as extra 4-byte reads
+                asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(q1.x), "+v"(q1.y),
+                             "+v"(q1.z), "+v"(q1.w), "+v"(e1));
                 const uint32_t e0 = q1.x;                                          // halo w 8-9
                 bf16x8 b[2][3];                                                    // [octet][kw]
                 b[0][0] = __builtin_bit_cast(bf16x8, q0);
