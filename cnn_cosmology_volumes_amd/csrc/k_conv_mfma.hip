@@ -13,10 +13,13 @@
 //    channels.  For every 32-channel input chunk it stages the
 //    (TD+2)(TH+2)(TW+2) halo of the input in LDS once and then walks the 27
 //    taps; a tap only shifts the LDS row index, so every B fragment is one
-//    aligned 16-byte LDS read at a compile-time offset.  The LDS voxel stride
-//    is 64 bytes (unpadded).  A padded 96-byte stride reads faster in
-//    isolation (about 310 against 200 B/clk per CU on gfx950), but measured
-//    over the whole kernel the smaller halo wins by 1-5%.
+//    aligned 16-byte LDS read at a compile-time offset from one of three
+//    per-lane bases.  The LDS voxel stride is 64 bytes (unpadded), and the
+//    two 32-byte halves of a voxel are swapped where bit 2 of its halo w is
+//    set: 16 lanes read 16 consecutive voxels, and without the swap voxels
+//    w and w + 4 fall on the same LDS banks (a measured 2-way conflict on
+//    gfx950: 8.7 against 4.4 clocks per 16-byte wave read).  One tile that
+//    is at the register limit keeps the plain layout (see SWZ).
 //  - A fragments (8 consecutive in-channels of one output channel) are
 //    16-byte global loads from the [tap][co][ci] weight copy, which is small
 //    and stays L2/L1 resident.
@@ -61,6 +64,10 @@ struct Tile {
 // wave to own two whole depth planes of a 16-wide tile (WN = 2*TH*TW,
 // TW = 16), so a window is 4 accumulator fragments of one lane and of its
 // neighbour lane, and no split of the channel reduction.
+// 16-byte chunk (0..3) of a halo voxel that holds channels 8q..8q+7: the two
+// 32-byte halves are swapped where bit 2 of the voxel's halo w is set.
+__device__ __forceinline__ int halo_chunk(int q, int hw) { return q ^ (((hw >> 2) & 1) << 1); }
+
 template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false, int AR = 0>
 __global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
@@ -94,14 +101,23 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int c_begin = blockIdx.z * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
 
-    // Per-lane LDS offsets (in bf16 units, tap 0) of the B fragments.
+    // Per-lane LDS offsets (in bf16 units) of the B fragments: voxel base of
+    // tap 0 per fragment, plus the lane's swizzled 16-byte chunk for each
+    // kw (the halo w of a lane's voxel is tw + kw, the same for every j).
     int hb[T::NJ];
 #pragma unroll
     for (int j = 0; j < T::NJ; ++j) {
         const int v = wave * WN + 16 * j + l16;
         const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
-        hb[j] = ((td * T::HH + th) * T::HW + tw) * LS + 8 * lg;
+        hb[j] = ((td * T::HH + th) * T::HW + tw) * LS;
     }
+    // The 32-channel ring tile with a 512-voxel halo (17 staging pieces per
+    // thread) is already at 256 VGPRs; the swizzle's extra registers make it
+    // spill (measured slower), so it keeps the plain layout.
+    constexpr bool SWZ = !(AR > 0 && T::IT > 16);
+    int sw[3];
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw) sw[kw] = (SWZ ? halo_chunk(lg, (l16 % TW) + kw) : lg) * 8;
 
     f32x4 acc[T::MI][T::NJ];
 #pragma unroll
@@ -146,7 +162,8 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
             for (int it = 0; it < T::IT; ++it) {
                 const int e = threadIdx.x + it * T::NT;
                 if (T::NE % T::NT == 0 || e < T::NE)
-                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS + (e & 3) * 8) = val[it];
+                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS +
+                                              (SWZ ? halo_chunk(e & 3, (e >> 2) % T::HW) : (e & 3)) * 8) = val[it];
             }
             if constexpr (AR > 0) {
                 if (ald0) {
@@ -173,7 +190,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
             a1[i] = *reinterpret_cast<const bf16x8*>(wrow + tap_stride + (int64_t)16 * i * Cin);
         }
 #pragma unroll
-        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j]);
+        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + sw[0]);
 #pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
             if (tap + 2 < 27) {
@@ -185,7 +202,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
                 const int tn = tap + 1;
                 const int toff = (((tn / 9) * T::HH + (tn / 3) % 3) * T::HW + tn % 3) * LS;
 #pragma unroll
-                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
+                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + (hb[j] + sw[tn % 3]) + toff);
             }
             // Fence: keep the prefetches above in front of this tap's MFMAs
             // (the scheduler would otherwise sink each load next to its use).
@@ -223,7 +240,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < T::MI; ++i) a0[i] = *reinterpret_cast<const bf16x8*>(aring + aoff[i]);
 #pragma unroll
-        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j]);
+        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + sw[0]);
 #pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
             uint4 rn = make_uint4(0u, 0u, 0u, 0u);
@@ -235,7 +252,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
                 for (int i = 0; i < T::MI; ++i)
                     a1[i] = *reinterpret_cast<const bf16x8*>(aring + (tn % AR) * BM * AS + aoff[i]);
 #pragma unroll
-                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + toff);
+                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + (hb[j] + sw[tn % 3]) + toff);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
