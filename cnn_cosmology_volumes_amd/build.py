@@ -28,6 +28,9 @@ COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions are disabled for every kernel in this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs rather than AGPRs: saves the AGPR-to-VGPR copies
+    # of accumulators that feed VALU epilogues (no other kernel changes)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
 

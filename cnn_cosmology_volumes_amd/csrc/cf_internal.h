@@ -62,6 +62,19 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// K order of the Cin = 4 forward: k = slot * 4 + ci, slot 0..31, and
+// C4_SLOT_TAP[slot] is the tap (kd * 9 + kh * 3 + kw) of that slot, or -1 for
+// a zero slot.  An MFMA lane takes slots 2p and 2p + 1 of a 32-deep step;
+// within each step the second tap of every lane lies the same halo offset
+// from its first (one voxel along w in steps 0, 1 and 3, one row along h in
+// step 2), so the two 8-byte reads share one base and pair into one LDS
+// access.  The weight re-layout and the kernel both use this table.
+__host__ __device__ constexpr int c4_slot_tap(int slot) {
+    constexpr int t[32] = {0,  1,  3,  4,  6,  7,  9,  10, 12, 13, 15, 16, 18, 19, 21, 22,
+                           2,  5,  11, 14, 20, 23, 8,  -1, 24, 25, 17, -1, 26, -1, -1, -1};
+    return t[slot];
+}
+
 // Raw buffer resource over `bytes` bytes from p.  A lane whose offset is
 // >= bytes reads zeros and touches no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {

@@ -2,12 +2,14 @@
 //
 // Same definition as the general forward (Oyama et al., Sec. IV / Table I:
 // stride 1, "same" zero padding, no bias), specialised for the 4-channel
-// input volume: the reduction K = 27 taps x 4 channels = 108 is packed as
-// k = tap*4 + ci and padded with zero taps to 128 (four 32-deep MFMA steps).
-// A lane's 8 K-values are then two taps x 4 channels, i.e. two 8-byte LDS
-// reads from an [halo voxel][4] tile.  This layer is bound by HBM bandwidth
-// (it writes 32 output channels per voxel while reading 4), so the tile is
-// large and the halo cheap: 8 bytes per voxel.
+// input volume: the reduction K = 27 taps x 4 channels = 108 is packed into
+// 32 tap slots x 4 channels = 128 (four 32-deep MFMA steps) in the order of
+// c4_slot_tap.  A lane's 8 K-values are two taps x 4 channels, i.e. two
+// 8-byte LDS reads from an [halo voxel][4] tile; the slot order makes the
+// second tap a fixed offset from the first within each step, so both reads
+// use one base register with immediate offsets and land in the operand's
+// registers directly.  The halo is cheap (8 bytes per voxel) and the tile
+// large.
 #include "cf_internal.h"
 
 namespace cf {
@@ -32,7 +34,9 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
                           int N, int D, int H, int W, int Cout, int tD, int tH, int tW)
 {
     constexpr int MI = BM / 16, NJ = WN / 16;
-    __shared__ __attribute__((aligned(16))) uint2 halo[HV];   // 4 bf16 per voxel
+    // 4 bf16 per voxel, plus one zero voxel past the end (read, with zero
+    // weight, as the padded partner of the last tap)
+    __shared__ __attribute__((aligned(16))) uint2 halo[HV + 1];
     __shared__ __attribute__((aligned(16))) uint16_t zt[POOL ? VT * ZS : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -76,16 +80,14 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
             const int hv = threadIdx.x + it * NT;
             if (HV % NT == 0 || hv < HV) halo[hv] = v[it];
         }
+        if (threadIdx.x == 0) halo[HV] = make_uint2(0u, 0u);
     }
     __syncthreads();
 
-    int hb[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int v = wave * WN + 16 * j + l16;
-        const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
-        hb[j] = (td * HH + th) * HW + tw;
-    }
+    // A wave owns one depth plane of the tile: fragment j is row th = j, lane
+    // l16 is tw, so fragment j's halo voxel is hb0 + j * HW.
+    static_assert(WN == TH * TW && NJ == TH, "one depth plane per wave");
+    const int hb0 = wave * HH * HW + l16;
 
     f32x4 acc[MI][NJ];
 #pragma unroll
@@ -93,19 +95,23 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // halo voxel offset of a tap (an empty slot reads tap 0's voxel)
+    auto voff = [](int t) { return t < 0 ? 0 : ((t / 9) * HH + (t / 3) % 3) * HW + t % 3; };
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const bf16x8* a = afr[s];
-        // Taps covered by this lane group at this step.  Taps 27..31 are the
-        // zero padding of K: their weights are zero, so any in-range (finite)
-        // halo value may stand in for the operand; offset 0 is used.
-        const int t0 = 8 * s + 2 * lg, t1 = t0 + 1;
-        const int off0 = t0 < 27 ? ((t0 / 9) * HH + (t0 / 3) % 3) * HW + t0 % 3 : 0;
-        const int off1 = t1 < 27 ? ((t1 / 9) * HH + (t1 / 3) % 3) * HW + t1 % 3 : 0;
+        // This lane group's first tap at this step, and the offset of the
+        // second tap (the same for every lane group of the step).  A zero
+        // slot has zero weights, so the finite halo value it reads (a
+        // neighbouring voxel, or the zero voxel past the end) adds nothing.
+        const int ta = lg == 0 ? voff(c4_slot_tap(8 * s)) : lg == 1 ? voff(c4_slot_tap(8 * s + 2))
+                     : lg == 2 ? voff(c4_slot_tap(8 * s + 4)) : voff(c4_slot_tap(8 * s + 6));
+        const int dt = s == 2 ? HW : 1;
+        const uint2* hp = halo + hb0 + ta;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const uint2 u0 = halo[hb[j] + off0];
-            const uint2 u1 = halo[hb[j] + off1];
+            const uint2 u0 = hp[j * HW];
+            const uint2 u1 = hp[j * HW + dt];
             const uint4 u = make_uint4(u0.x, u0.y, u1.x, u1.y);
             const bf16x8 b = __builtin_bit_cast(bf16x8, u);
 #pragma unroll

@@ -41,14 +41,15 @@ __device__ __forceinline__ uint16_t wk_dgrad_elem(const void* W, bool f32, int c
     const int t = (int)(e / ((uint32_t)cout * (uint32_t)cipad));
     return ci < cin ? f2bf(wload(W, f32, ((int64_t)(26 - t) * cin + ci) * cout + co)) : (uint16_t)0;
 }
-// c4:    Wk[co][k], k = t*4 + ci for t < 27, zero for k >= 108 or co >= cout.
+// c4:    Wk[co][k], k = slot*4 + ci with the tap of each slot from
+//        c4_slot_tap (zero for empty slots and for co >= cout).
 __device__ __forceinline__ uint16_t wk_c4_elem(const void* W, bool f32, int cout, int64_t e64)
 {
     const uint32_t e = (uint32_t)e64;
     const int k = (int)(e % 128u);
     const int co = (int)(e / 128u);
-    const int t = k / 4, ci = k % 4;
-    return (co < cout && t < 27) ? f2bf(wload(W, f32, ((int64_t)t * 4 + ci) * cout + co)) : (uint16_t)0;
+    const int t = c4_slot_tap(k / 4), ci = k % 4;
+    return (co < cout && t >= 0) ? f2bf(wload(W, f32, ((int64_t)t * 4 + ci) * cout + co)) : (uint16_t)0;
 }
 
 
@@ -73,12 +74,13 @@ __global__ void wprep_c4_kernel(const void* W, bool f32, int cout, int copad, ui
         Wk[e] = wk_c4_elem(W, f32, cout, e);
 }
 
-// Several re-layouts in one launch: blockIdx.y picks the job.  The fwd and
-// c4 layouts transpose (input channel or k) x (output channel) matrices, so
-// those jobs go through 32 x 32 LDS tiles: the fp32 source is read along its
+// Several re-layouts in one launch: blockIdx.y picks the job.  The fwd
+// layout transposes (input channel) x (output channel) matrices, so those
+// jobs go through 32 x 32 LDS tiles: the fp32 source is read along its
 // contiguous output channels and the bf16 copy written along its contiguous
-// rows.  The dgrad layout keeps the source's channel order and is copied
-// element by element.  Values are the same f2bf roundings either way.
+// rows.  The dgrad layout keeps the source's channel order and the c4 layout
+// is a small permutation; both are copied element by element.  Values are
+// the same f2bf roundings either way.
 constexpr int WT = 32;
 
 __global__ __launch_bounds__(256)
@@ -92,12 +94,17 @@ void wprep_multi_kernel(WprepList l)
             j.dst[e] = wk_dgrad_elem(j.src, j.f32, j.cin, j.cout, j.pad, e);
         return;
     }
+    if (j.kind == 2) {            // c4: a permutation of taps, tiny (copad x 128)
+        const int64_t total = (int64_t)j.pad * 128;
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+            j.dst[e] = wk_c4_elem(j.src, j.f32, j.cout, e);
+        return;
+    }
     // source S[r][c] (c = output channel, contiguous), R rows per matrix;
     // destination D[c][r] with row length Rpad, c < pad (zero beyond cout),
     // r < Rpad (zero beyond R)
-    const bool c4 = j.kind == 2;
-    const int R = c4 ? 108 : j.cin, Rpad = c4 ? 128 : j.cin, C = j.cout, Cpad = j.pad;
-    const int nmat = c4 ? 1 : 27;
+    const int R = j.cin, Rpad = j.cin, C = j.cout, Cpad = j.pad;
+    const int nmat = 27;
     const int tr = (Rpad + WT - 1) / WT, tc = (Cpad + WT - 1) / WT;
     const int ntiles = nmat * tr * tc;
     const int lx = threadIdx.x % WT, ly = threadIdx.x / WT;     // 32 x 8
@@ -173,7 +180,7 @@ hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s)
         int64_t b;
         if (j.kind == 1) b = blocks_for((int64_t)27 * j.pad * j.cout);
         else if (j.kind == 0) b = (int64_t)27 * ((j.cin + WT - 1) / WT) * ((j.pad + WT - 1) / WT);
-        else b = (int64_t)(128 / WT) * ((j.pad + WT - 1) / WT);
+        else b = blocks_for((int64_t)j.pad * 128);
         m = b > m ? b : m;
     }
     if (m > 4096) m = 4096;
