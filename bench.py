@@ -168,7 +168,10 @@ def measured_traffic(op_name):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("op") != op_name:
+    # {"ops": {name: entry}} (one entry per profiled entry point) or one entry
+    entries = t.get("ops") if isinstance(t.get("ops"), dict) else {t.get("op"): t}
+    t = entries.get(op_name)
+    if not isinstance(t, dict):
         return None
     h = hashlib.sha256()
     for rel in t.get("sources", []):
