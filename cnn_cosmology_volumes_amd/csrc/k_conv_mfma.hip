@@ -401,7 +401,9 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
     ConvPlan p{};
     const bool narrow = x.w < 16;
     if (cout > 32) p.cfg = narrow ? 3 : 2;
-    else if (cout > 16) p.cfg = narrow ? 5 : 4;
+    // 17..32 channels: the 4x8x8 tile (its halo takes the bank swizzle; the
+    // 4x8x16 tile is at the register limit without it) measured faster
+    else if (cout > 16) p.cfg = 5;
     else p.cfg = narrow ? 7 : 6;
     const CfgInfo& c = kCfgs[p.cfg];
     p.bm = c.bm;
