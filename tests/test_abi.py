@@ -103,6 +103,12 @@ def test_train_step_validation_and_workspace():
     fx = (8, 128, 128, 128, 4)
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_CONV_POOL_FWD) == 128 * 128 * 2
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, fx, 32, cf.CF_POOL_CONV_BWD_WEIGHT) % (27 * 4 * 32 * 4) == 0
+    # the fused kernel addresses a box by 32-bit offsets (H * W <= 2^23); a larger plane
+    # takes the unfused path, which carries the full-resolution conv gradient
+    big = (1, 2, 4096, 4096, 4)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, big, 32, cf.CF_POOL_CONV_BWD_WEIGHT) >= 2 * 4096 * 4096 * 32 * 2
+    edge = (1, 2, 2048, 4096, 4)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, edge, 32, cf.CF_POOL_CONV_BWD_WEIGHT) < 2 * 2048 * 4096 * 32 * 2
     # MFMA shapes whose plan has 64/128-channel blocks on 4x4x16 tiles and no
     # channel split run fused: weights only (27 taps x 128 padded co x Cin)
     mx = (2, 16, 16, 16, 32)
