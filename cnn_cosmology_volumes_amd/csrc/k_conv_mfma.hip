@@ -178,25 +178,26 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 
         if constexpr (AR == 0) {
         // Software pipeline over the 27 taps: weight (A) fragments are
-        // loaded from global memory two taps ahead, halo (B) fragments are
+        // loaded from global memory three taps ahead, halo (B) fragments are
         // read from LDS one tap ahead, so neither latency sits in front of
         // the MFMAs of the current tap.
         const uint16_t* wrow = Wk + ((int64_t)(co_base + l16) * Cin + c * 32 + 8 * lg);
         const int64_t tap_stride = (int64_t)CoutPad * Cin;
-        bf16x8 a0[T::MI], a1[T::MI], a2[T::MI], b0[T::NJ], b1[T::NJ];
+        bf16x8 a0[T::MI], a1[T::MI], a2[T::MI], a3[T::MI], b0[T::NJ], b1[T::NJ];
 #pragma unroll
         for (int i = 0; i < T::MI; ++i) {
             a0[i] = *reinterpret_cast<const bf16x8*>(wrow + (int64_t)16 * i * Cin);
             a1[i] = *reinterpret_cast<const bf16x8*>(wrow + tap_stride + (int64_t)16 * i * Cin);
+            a2[i] = *reinterpret_cast<const bf16x8*>(wrow + 2 * tap_stride + (int64_t)16 * i * Cin);
         }
 #pragma unroll
         for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + sw[0]);
 #pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
-            if (tap + 2 < 27) {
+            if (tap + 3 < 27) {
 #pragma unroll
                 for (int i = 0; i < T::MI; ++i)
-                    a2[i] = *reinterpret_cast<const bf16x8*>(wrow + (tap + 2) * tap_stride + (int64_t)16 * i * Cin);
+                    a3[i] = *reinterpret_cast<const bf16x8*>(wrow + (tap + 3) * tap_stride + (int64_t)16 * i * Cin);
             }
             if (tap + 1 < 27) {
                 const int tn = tap + 1;
@@ -214,7 +215,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; }
+            for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; a2[i] = a3[i]; }
 #pragma unroll
             for (int j = 0; j < T::NJ; ++j) b0[j] = b1[j];
         }
