@@ -127,34 +127,72 @@ __global__ void dense_bwd_db(const float* __restrict__ pre, const float* __restr
 }
 
 // dW[i][o] = sum over b of X[b][i] * g[b][o] (fmaf chain in b order).  A
-// thread owns four consecutive o of one i when Out % 4 == 0 (one 16-byte
-// store), else one element; the per-element operations are the same.
-__global__ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __restrict__ Xb,
-                             const float* __restrict__ pre, const float* __restrict__ dY, float slope,
-                             float* __restrict__ dW, int B, int In, int Out)
+// block owns DW_RI input rows x DW_OC output columns.  Per chunk of up to
+// DW_BC batch rows it stages the gated gradient g (DW_BC x DW_OC) and the
+// input rows (DW_BC x DW_RI) in LDS, so every operand is loaded from global
+// memory once per block (loading them per output element made this kernel
+// bound by the load-instruction rate).  A thread owns 4 rows x 4 consecutive
+// columns; results go out with 16-byte stores when Out % 4 == 0.
+constexpr int DW_OC = 128, DW_RI = 32, DW_BC = 32;
+__global__ __launch_bounds__(256)
+void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __restrict__ Xb,
+                  const float* __restrict__ pre, const float* __restrict__ dY, float slope,
+                  float* __restrict__ dW, int B, int In, int Out)
 {
-    const int V = (Out % 4 == 0) ? 4 : 1;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t * V >= (int64_t)In * Out) return;
-    const int64_t e0 = t * V;
-    const int o0 = (int)(e0 % Out);
-    const int64_t i = e0 / Out;
-    float sum[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int b0 = 0; b0 < B; b0 += DB) {
-        float x[DB];
+    __shared__ __attribute__((aligned(16))) float gs[DW_BC][DW_OC];
+    __shared__ float xs[DW_BC][DW_RI];
+    const int64_t i_blk = (int64_t)blockIdx.x * DW_RI;
+    const int tcol = threadIdx.x % (DW_OC / 4), trow = threadIdx.x / (DW_OC / 4);   // 32 column quads x 8 rows
+    constexpr int NR = DW_RI / 8;
+    const int nch = (Out + DW_OC - 1) / DW_OC;
+    for (int ch = blockIdx.y; ch < nch; ch += gridDim.y) {
+    const int o_blk = ch * DW_OC;
+    float sum[NR][4];
 #pragma unroll
-        for (int b = 0; b < DB; ++b) x[b] = b0 + b < B ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            if (b0 + b >= B) break;
-            const int64_t r = (int64_t)(b0 + b) * Out + o0;
+        for (int v = 0; v < 4; ++v) sum[r][v] = 0.f;
+    for (int b0 = 0; b0 < B; b0 += DW_BC) {
+        const int nb = min(DW_BC, B - b0);
+        __syncthreads();
+        for (int e = threadIdx.x; e < nb * DW_OC; e += blockDim.x) {
+            const int b = e / DW_OC, oo = e % DW_OC, og = o_blk + oo;
+            const int64_t r = (int64_t)(b0 + b) * Out + og;
+            gs[b][oo] = og < Out ? gate(dY[r], pre[r], slope) : 0.f;
+        }
+        for (int e = threadIdx.x; e < nb * DW_RI; e += blockDim.x) {
+            const int b = e / DW_RI, ii = e % DW_RI;
+            const int64_t i = i_blk + ii;
+            xs[b][ii] = i < In ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+        }
+        __syncthreads();
+        for (int b = 0; b < nb; ++b) {
+            const float4 g = *reinterpret_cast<const float4*>(&gs[b][tcol * 4]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (v < V) sum[v] = fmaf(x[b], gate(dY[r + v], pre[r + v], slope), sum[v]);
+            for (int r = 0; r < NR; ++r) {
+                const float x = xs[b][trow + 8 * r];
+                sum[r][0] = fmaf(x, g.x, sum[r][0]);
+                sum[r][1] = fmaf(x, g.y, sum[r][1]);
+                sum[r][2] = fmaf(x, g.z, sum[r][2]);
+                sum[r][3] = fmaf(x, g.w, sum[r][3]);
+            }
         }
     }
-    if (V == 4) *reinterpret_cast<float4*>(dW + e0) = make_float4(sum[0], sum[1], sum[2], sum[3]);
-    else dW[e0] = sum[0];
+    const int o = o_blk + tcol * 4;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int64_t i = i_blk + trow + 8 * r;
+        if (i >= In) continue;
+        float* d = dW + i * Out + o;
+        if (Out % 4 == 0) {
+            if (o < Out) *reinterpret_cast<float4*>(d) = make_float4(sum[r][0], sum[r][1], sum[r][2], sum[r][3]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (o + v < Out) d[v] = sum[r][v];
+        }
+    }
+    }
 }
 
 // dX for input row i, computed by one wave: lanes stride over o, then the
@@ -417,9 +455,9 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t ndw = (int64_t)in * out / (out % 4 == 0 ? 4 : 1);
-    hipLaunchKernelGGL(dense_bwd_dw, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, s, X, Xb, pre, dY, slope, dW,
-                       B, in, out);
+    const int nch = (out + DW_OC - 1) / DW_OC;
+    hipLaunchKernelGGL(dense_bwd_dw, dim3((unsigned)((in + DW_RI - 1) / DW_RI), (unsigned)(nch < 65535 ? nch : 65535)),
+                       dim3(256), 0, s, X, Xb, pre, dY, slope, dW, B, in, out);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dX || dXb) {
