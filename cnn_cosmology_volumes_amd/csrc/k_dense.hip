@@ -45,18 +45,29 @@ void dense_fwd_partial(const float* __restrict__ X, const uint16_t* __restrict__
     const int b0 = blockIdx.z * DB;
     const int nb = min(DB, B - b0);
     const int i0 = ks * DK, i1 = min(In, i0 + DK);
-    for (int e = threadIdx.x; e < DB * DK; e += DO * DI) {
-        const int b = e / DK, i = i0 + e % DK;
-        xs[b][e % DK] = (b < nb && i < i1) ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+    {
+        constexpr int KX = DB * DK / (DO * DI);    // staging loads per thread, issued before the stores
+        float xv[KX];
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            const int e = threadIdx.x + k * DO * DI, b = e / DK, i = i0 + e % DK;
+            xv[k] = (b < nb && i < i1) ? xin(X, Xb, (int64_t)(b0 + b) * In + i) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            const int e = threadIdx.x + k * DO * DI;
+            xs[e / DK][e % DK] = xv[k];
+        }
     }
     __syncthreads();
     float acc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[b] = 0.f;
     if (o < Out) {
-        // rows i0+il, i0+il+DI, ... in increasing order; the weight loads of
-        // eight rows are issued together (latency, not bandwidth, bounds this)
-        constexpr int U = 8;
+        // rows i0+il, i0+il+DI, ... in increasing order; all of a thread's
+        // weight loads (DK / DI rows) are issued together: latency, not
+        // bandwidth, bounds this kernel
+        constexpr int U = DK / DI;
         for (int i = i0 + il; i < i1; i += DI * U) {
             float w[U];
 #pragma unroll
@@ -195,83 +206,71 @@ void dense_bwd_dw(const float* __restrict__ X, const uint16_t* __restrict__ Xb,
     }
 }
 
-// dX for input row i, computed by one wave: lanes stride over o, then the
-// 64 lane sums of the DB = 8 batch rows are reduced together in a fixed
-// order: three exchange steps (lane bits 5, 4, 3) halve the number of values
-// per lane while summing pairs, then three butterfly steps (bits 2, 1, 0) sum
-// within groups of 8 lanes; batch row b ends in lane 8 b.  Ten shuffles per
-// 8 rows instead of 48.  Shared by the standalone backward kernel and the
-// fused head kernel.
-__device__ __forceinline__ void dx_row_wave(const float* __restrict__ W, const float* __restrict__ pre,
-                                            const float* __restrict__ dY, float slope, float* __restrict__ dX,
-                                            uint16_t* __restrict__ dXb, int B, int In, int Out, int64_t i, int lane)
+// dX[b][i] = sum over o of g[b][o] * W[i][o], g the gated output gradient:
+// one sequential fmaf chain in o order per output element.  The standalone
+// kernel and the fused head kernel both use this order, so the training
+// step equals the composed entry points bit for bit.
+__device__ __forceinline__ float dx_dot(float acc, const float* __restrict__ g, const float* __restrict__ w, int n)
 {
-    static_assert(DB == 8, "reduction layout");
-    for (int b0 = 0; b0 < B; b0 += DB) {
-        const int nb = min(DB, B - b0);
-        float acc[DB];
-#pragma unroll
-        for (int b = 0; b < DB; ++b) acc[b] = 0.f;
-        for (int o = lane; o < Out; o += 64) {
-            const float w = W[i * Out + o];
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-                if (b < nb) acc[b] = fmaf(gate(dY[(b0 + b) * Out + o], pre[(b0 + b) * Out + o], slope), w, acc[b]);
-        }
-        // exchange steps: keep the half named by this lane's bit, add the
-        // partner's copy of it (lower lane's value first)
-        float v4[4], v2[2], v1;
-        {
-            const bool hi = lane & 32;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float send = hi ? acc[k] : acc[k + 4];
-                const float keep = hi ? acc[k + 4] : acc[k];
-                const float recv = __shfl_xor(send, 32, 64);
-                v4[k] = hi ? recv + keep : keep + recv;
-            }
-        }
-        {
-            const bool hi = lane & 16;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const float send = hi ? v4[k] : v4[k + 2];
-                const float keep = hi ? v4[k + 2] : v4[k];
-                const float recv = __shfl_xor(send, 16, 64);
-                v2[k] = hi ? recv + keep : keep + recv;
-            }
-        }
-        {
-            const bool hi = lane & 8;
-            const float send = hi ? v2[0] : v2[1];
-            const float keep = hi ? v2[1] : v2[0];
-            const float recv = __shfl_xor(send, 8, 64);
-            v1 = hi ? recv + keep : keep + recv;
-        }
-        // lane holds batch row b = 4 (bit 5) + 2 (bit 4) + (bit 3); sum its group of 8
-#pragma unroll
-        for (int m = 4; m >= 1; m >>= 1) {
-            const float r = __shfl_xor(v1, m, 64);
-            v1 = (lane & m) ? r + v1 : v1 + r;
-        }
-        const int b = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
-        if ((lane & 7) == 0 && b < nb) {
-            const int64_t o2 = (int64_t)(b0 + b) * In + i;
-            if (dXb) dXb[o2] = f2bf(v1);
-            else dX[o2] = v1;
-        }
-    }
+    for (int o = 0; o < n; ++o) acc = fmaf(g[o], w[o], acc);
+    return acc;
 }
 
-// One wave per input row i.
+// A block owns DX_RI input rows x DB batch rows (one output per thread).
+// Per chunk of DX_OC output columns it stages those rows of W and the gated
+// gradient in LDS (each loaded once per block), then every thread extends
+// its chain over the chunk.
+constexpr int DX_RI = 32, DX_OC = 128;
 __global__ __launch_bounds__(256)
 void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, const float* __restrict__ dY,
                   float slope, float* __restrict__ dX, uint16_t* __restrict__ dXb, int B, int In, int Out)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= In) return;
-    dx_row_wave(W, pre, dY, slope, dX, dXb, B, In, Out, i, lane);
+    static_assert(DX_RI * DB == 256, "one output per thread");
+    __shared__ float ws[DX_RI][DX_OC + 1];      // +1: the threads of a wave read 8 rows at one column
+    __shared__ float gs[DB][DX_OC + 1];
+    const int64_t i_blk = (int64_t)blockIdx.x * DX_RI;
+    const int bl = threadIdx.x % DB, r = threadIdx.x / DB;
+    const int64_t i = i_blk + r;
+    for (int b0 = 0; b0 < B; b0 += DB) {
+        const int nb = min(DB, B - b0);
+        float acc = 0.f;
+        for (int oc = 0; oc < Out; oc += DX_OC) {
+            const int no = min(DX_OC, Out - oc);
+            // every thread issues all of its staging loads before its LDS stores
+            constexpr int KW = DX_RI * DX_OC / 256, KG = DB * DX_OC / 256;
+            float wv[KW], gv[KG];
+#pragma unroll
+            for (int k = 0; k < KW; ++k) {
+                const int e = threadIdx.x + 256 * k, rr = e / DX_OC, oo = e % DX_OC;
+                const int64_t ii = i_blk + rr;
+                wv[k] = (ii < In && oo < no) ? W[ii * Out + oc + oo] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                const int e = threadIdx.x + 256 * k, bb = e / DX_OC, oo = e % DX_OC;
+                const int64_t q = (int64_t)(b0 + bb) * Out + oc + oo;
+                gv[k] = (bb < nb && oo < no) ? gate(dY[q], pre[q], slope) : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < KW; ++k) {
+                const int e = threadIdx.x + 256 * k;
+                ws[e / DX_OC][e % DX_OC] = wv[k];
+            }
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                const int e = threadIdx.x + 256 * k;
+                gs[e / DX_OC][e % DX_OC] = gv[k];
+            }
+            __syncthreads();
+            acc = dx_dot(acc, gs[bl], ws[r], no);
+        }
+        if (i < In && bl < nb) {
+            const int64_t q = (int64_t)(b0 + bl) * In + i;
+            if (dXb) dXb[q] = f2bf(acc);
+            else dX[q] = acc;
+        }
+    }
 }
 
 // The small layers of the head in one block (In <= 128 for layers 2 and 3,
@@ -281,7 +280,7 @@ void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, co
 // standalone kernels (partial fmaf chains over i = il mod 4, their sum in il
 // order, the split finalize, the MSE and backward reductions), so the fused
 // step matches the entry points bit for bit.
-__device__ __forceinline__ void head_fwd_layer(const float* __restrict__ X, const float* __restrict__ W,
+__device__ __forceinline__ void head_fwd_layer(const float* __restrict__ X, const float* __restrict__ W, int ldw,
                                                const float* __restrict__ bias, float slope, float* __restrict__ pre,
                                                float* __restrict__ Y, float* red, int B, int In, int Out)
 {
@@ -289,7 +288,7 @@ __device__ __forceinline__ void head_fwd_layer(const float* __restrict__ X, cons
     for (int task = threadIdx.x; task < n * DI; task += blockDim.x) {
         const int il = task / n, e = task % n, b = e / Out, o = e % Out;
         float acc = 0.f;
-        for (int i = il; i < In; i += DI) acc = fmaf(X[b * In + i], W[(int64_t)i * Out + o], acc);
+        for (int i = il; i < In; i += DI) acc = fmaf(X[b * In + i], W[i * ldw + o], acc);
         red[task] = acc;
     }
     __syncthreads();
@@ -306,26 +305,80 @@ __device__ __forceinline__ void head_fwd_layer(const float* __restrict__ X, cons
     __syncthreads();
 }
 
-__device__ __forceinline__ void head_bwd_layer(const float* __restrict__ X, const float* __restrict__ W,
+// g (B x Out, LDS scratch) receives the gated output gradient once; the bias,
+// weight and data gradients then read it (the gate is exact, so this is the
+// same arithmetic as gating inside each sum, as the standalone kernels do).
+// g: LDS scratch for the gated gradient, rows of Out + 1 floats; W (LDS)
+// has rows of ldw floats.  Both strides are odd multiples of 4 bytes apart
+// from a power of two, so the 8 rows a wave reads in the dX dots fall on
+// distinct banks.
+__device__ __forceinline__ void head_bwd_layer(const float* __restrict__ X, const float* __restrict__ W, int ldw,
                                                const float* __restrict__ pre, const float* __restrict__ dY,
                                                float slope, float* __restrict__ dX, float* __restrict__ dW,
-                                               float* __restrict__ db, int B, int In, int Out)
+                                               float* __restrict__ db, float* __restrict__ g, int B, int In, int Out)
 {
+    const int ldg = Out + 1;
+    for (int e = threadIdx.x; e < B * Out; e += blockDim.x) g[(e / Out) * ldg + e % Out] = gate(dY[e], pre[e], slope);
+    __syncthreads();
     for (int o = threadIdx.x; o < Out; o += blockDim.x) {
         float sum = 0.f;
-        for (int b = 0; b < B; ++b) sum += gate(dY[b * Out + o], pre[b * Out + o], slope);
+        for (int b = 0; b < B; ++b) sum += g[b * ldg + o];
         db[o] = sum;
     }
     for (int e = threadIdx.x; e < In * Out; e += blockDim.x) {
         const int i = e / Out, o = e % Out;
         float sum = 0.f;
-        for (int b = 0; b < B; ++b) sum = fmaf(X[b * In + i], gate(dY[b * Out + o], pre[b * Out + o], slope), sum);
+        for (int b = 0; b < B; ++b) sum = fmaf(X[b * In + i], g[b * ldg + o], sum);
         dW[e] = sum;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     if (dX)
-        for (int i = wave; i < In; i += nw) dx_row_wave(W, pre, dY, slope, dX, nullptr, B, In, Out, i, lane);
+        for (int e = threadIdx.x; e < B * In; e += blockDim.x) {
+            const int b = e % B, i = e / B;
+            dX[b * In + i] = dx_dot(0.f, g + b * ldg, W + i * ldw, Out);
+        }
     __syncthreads();
+}
+
+// dst (rows of ldd floats) = src (rows x cols, dense) by the whole block,
+// every thread issuing its loads before its stores.
+__device__ __forceinline__ void block_copy_rows(float* __restrict__ dst, int ldd, const float* __restrict__ src,
+                                                int rows, int cols)
+{
+    constexpr int U = 8;
+    const int n = rows * cols;
+    for (int e0 = threadIdx.x; e0 < n; e0 += U * blockDim.x) {
+        float v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int e = e0 + k * blockDim.x;
+            v[k] = e < n ? src[e] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int e = e0 + k * blockDim.x;
+            if (e < n) dst[(e / cols) * ldd + e % cols] = v[k];
+        }
+    }
+}
+
+// dst[e] = src[e] for e < n by the whole block, every thread issuing its
+// loads before its stores (a load-store loop would wait on each load in turn).
+__device__ __forceinline__ void block_copy(float* __restrict__ dst, const float* __restrict__ src, int n)
+{
+    constexpr int U = 8;
+    for (int e0 = threadIdx.x; e0 < n; e0 += U * blockDim.x) {
+        float v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int e = e0 + k * blockDim.x;
+            v[k] = e < n ? src[e] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int e = e0 + k * blockDim.x;
+            if (e < n) dst[e] = v[k];
+        }
+    }
 }
 
 __global__ __launch_bounds__(1024)
@@ -339,21 +392,23 @@ void dense_head_kernel(DenseHead h)
     float* red = lds;                      // HEAD_RED
     float* y1 = red + HEAD_RED;            // B*d0
     float* pre1 = y1 + B * d0;             // B*d0
-    float* W2 = pre1 + B * d0;             // d0*d1
-    float* W3 = W2 + d0 * d1;              // d1*d2
-    float* pre2 = W3 + d1 * d2;            // B*d1
+    const int ld2 = d1 + 1, ld3 = d2 + 1;  // padded rows (see head_bwd_layer)
+    float* W2 = pre1 + B * d0;             // d0 x ld2
+    float* W3 = W2 + d0 * ld2;             // d1 x ld3
+    float* pre2 = W3 + d1 * ld3;           // B*d1
     float* y2 = pre2 + B * d1;             // B*d1
     float* pre3 = y2 + B * d1;             // B*d2
     float* y3 = pre3 + B * d2;             // B*d2
     float* dy3 = y3 + B * d2;              // B*d2
     float* dy2 = dy3 + B * d2;             // B*d1
     float* dy1 = dy2 + B * d1;             // B*d0
-    for (int e = threadIdx.x; e < B * d0; e += blockDim.x) { y1[e] = h.y1[e]; pre1[e] = h.pre1[e]; }
-    for (int e = threadIdx.x; e < d0 * d1; e += blockDim.x) W2[e] = h.W2[e];
-    for (int e = threadIdx.x; e < d1 * d2; e += blockDim.x) W3[e] = h.W3[e];
+    block_copy(y1, h.y1, B * d0);
+    block_copy(pre1, h.pre1, B * d0);
+    block_copy_rows(W2, ld2, h.W2, d0, d1);
+    block_copy_rows(W3, ld3, h.W3, d1, d2);
     __syncthreads();
-    head_fwd_layer(y1, W2, h.b2, h.slope, pre2, y2, red, B, d0, d1);
-    head_fwd_layer(y2, W3, h.b3, -1.f, pre3, y3, red, B, d1, d2);
+    head_fwd_layer(y1, W2, ld2, h.b2, h.slope, pre2, y2, red, B, d0, d1);
+    head_fwd_layer(y2, W3, ld3, h.b3, -1.f, pre3, y3, red, B, d1, d2);
     const int n = B * d2;
     if (threadIdx.x < 64) {
         // mean squared error, as mse_kernel
@@ -371,8 +426,9 @@ void dense_head_kernel(DenseHead h)
         if (lane == 0) *h.loss = sum * inv;
     }
     __syncthreads();
-    head_bwd_layer(y2, W3, pre3, dy3, -1.f, dy2, h.dW3, h.db3, B, d1, d2);
-    head_bwd_layer(y1, W2, pre2, dy2, h.slope, dy1, h.dW2, h.db2, B, d0, d1);
+    // red (free after the forward layers) holds each layer's gated gradient
+    head_bwd_layer(y2, W3, ld3, pre3, dy3, -1.f, dy2, h.dW3, h.db3, red, B, d1, d2);
+    head_bwd_layer(y1, W2, ld2, pre2, dy2, h.slope, dy1, h.dW2, h.db2, red, B, d0, d1);
     // layer 1: gated output gradient (consumed by its weight / data gradient
     // kernels with the gate switched off) and the bias gradient
     for (int e = threadIdx.x; e < B * d0; e += blockDim.x) h.g1[e] = gate(dy1[e], pre1[e], h.slope);
@@ -461,7 +517,7 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dX || dXb) {
-        hipLaunchKernelGGL(dense_bwd_dx, dim3((unsigned)((in + 3) / 4)), dim3(256), 0, s, W, pre, dY, slope, dX, dXb, B,
+        hipLaunchKernelGGL(dense_bwd_dx, dim3((unsigned)((in + DX_RI - 1) / DX_RI)), dim3(256), 0, s, W, pre, dY, slope, dX, dXb, B,
                            in, out);
         e = hipGetLastError();
     }
@@ -470,7 +526,7 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
 
 size_t head_lds_bytes(int B, int d0, int d1, int d2)
 {
-    return sizeof(float) * ((size_t)HEAD_RED + 3 * (size_t)B * d0 + (size_t)d0 * d1 + (size_t)d1 * d2 +
+    return sizeof(float) * ((size_t)HEAD_RED + 3 * (size_t)B * d0 + (size_t)d0 * (d1 + 1) + (size_t)d1 * (d2 + 1) +
                             3 * (size_t)B * d1 + 3 * (size_t)B * d2);
 }
 
