@@ -465,14 +465,44 @@ __global__ void sgd_kernel(float* __restrict__ W, const float* __restrict__ dW, 
 }
 
 // Several tensors in one launch: blockIdx.y picks the tensor.
-__global__ void sgd_multi_kernel(SgdList l, float lr)
+// A thread updates SGD_E consecutive elements, issuing all of its loads
+// (16-byte when both tensors are 16-byte aligned) before any update, so one
+// memory latency is paid per thread instead of one per element.
+constexpr int SGD_E = 4;
+__global__ __launch_bounds__(256)
+void sgd_multi_kernel(SgdList l, float lr)
 {
     const int t = blockIdx.y;
     float* __restrict__ W = l.w[t];
     const float* __restrict__ dW = l.dw[t];
     const int64_t n = l.n[t];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) W[i] = sgd_update(W[i], dW[i], lr);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * SGD_E;
+    const bool vec = (((uintptr_t)W | (uintptr_t)dW) & 15u) == 0;
+    for (int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * SGD_E; i0 < n; i0 += stride) {
+        if (vec && i0 + SGD_E <= n) {
+            float4 w[SGD_E / 4], g[SGD_E / 4];
+#pragma unroll
+            for (int k = 0; k < SGD_E / 4; ++k) {
+                w[k] = reinterpret_cast<const float4*>(W + i0)[k];
+                g[k] = reinterpret_cast<const float4*>(dW + i0)[k];
+            }
+#pragma unroll
+            for (int k = 0; k < SGD_E / 4; ++k)
+                reinterpret_cast<float4*>(W + i0)[k] =
+                    make_float4(sgd_update(w[k].x, g[k].x, lr), sgd_update(w[k].y, g[k].y, lr),
+                                sgd_update(w[k].z, g[k].z, lr), sgd_update(w[k].w, g[k].w, lr));
+        } else {
+            float w[SGD_E], g[SGD_E];
+#pragma unroll
+            for (int k = 0; k < SGD_E; ++k) {
+                w[k] = i0 + k < n ? W[i0 + k] : 0.f;
+                g[k] = i0 + k < n ? dW[i0 + k] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < SGD_E; ++k)
+                if (i0 + k < n) W[i0 + k] = sgd_update(w[k], g[k], lr);
+        }
+    }
 }
 
 __global__ void copy_kernel(const float* __restrict__ s, float* __restrict__ d, int64_t n)
@@ -562,7 +592,7 @@ hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s)
     if (l.count <= 0) return hipSuccess;
     int64_t m = 1;
     for (int t = 0; t < l.count; ++t) m = l.n[t] > m ? l.n[t] : m;
-    int64_t b = (m + 255) / 256;
+    int64_t b = (m + 256 * SGD_E - 1) / (256 * SGD_E);
     if (b > 2048) b = 2048;
     hipLaunchKernelGGL(sgd_multi_kernel, dim3((unsigned)b, (unsigned)l.count), dim3(256), 0, s, l, lr);
     return hipGetLastError();
