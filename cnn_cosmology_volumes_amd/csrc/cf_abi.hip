@@ -1,8 +1,11 @@
 // C ABI of libcf.so: argument validation, path selection and the training
 // step.  Every entry point validates before enqueuing anything, enqueues on
-// the caller's stream, and never synchronises or allocates.
+// the caller's stream, and never synchronises or allocates device memory.
+// The training step also forks work onto one auxiliary stream per device,
+// created on its first call there, and joins it back before returning.
 #include "cf_internal.h"
 
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -531,7 +534,8 @@ struct StepPlan {
     int L;
     LayerPlan layer[CF_MAX_BLOCKS];
     int flat, d0, d1, d2;
-    size_t part;        // shared split-K buffer (conv fwd, dgrad, wgrad, dense)
+    size_t part;        // split-K buffer of the main stream (conv fwd, dgrad, fused block-1 wgrad, dense)
+    size_t part_w;      // partial sums of the weight gradients run on the auxiliary stream
     size_t pre1, y1, pre2, y2, pre3, y3, dy3, dy2, dy1, g1;
     size_t dW1, db1, dW2, db2, dW3, db3;
     size_t cast;        // bf16 DHWIO weight copy for direct bf16 fallbacks
@@ -566,7 +570,7 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += up256(bytes); return o; };
     const size_t es = esize(dt);
-    size_t part = 0, cast = 0;
+    size_t part = 0, part_w = 0, cast = 0;
     cf_dims x{B, m->d, m->h, m->w, m->cin};
     for (int l = 0; l < P.L; ++l) {
         LayerPlan& Lp = P.layer[l];
@@ -588,7 +592,11 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         Lp.dw = take((size_t)27 * x.c * Lp.cout * 4);
         size_t pb = fwd_part_bytes(Lp.fwd, x, Lp.cout);
         if (l > 0 && dgrad_part_bytes(Lp.dg, x, Lp.cout) > pb) pb = dgrad_part_bytes(Lp.dg, x, Lp.cout);
-        if (wgrad_part_bytes(Lp.wg, dt, x, Lp.cout) > pb) pb = wgrad_part_bytes(Lp.wg, dt, x, Lp.cout);
+        if (Lp.fused) {
+            if (wgrad_part_bytes(Lp.wg, dt, x, Lp.cout) > pb) pb = wgrad_part_bytes(Lp.wg, dt, x, Lp.cout);
+        } else if (wgrad_part_bytes(Lp.wg, dt, x, Lp.cout) > part_w) {
+            part_w = wgrad_part_bytes(Lp.wg, dt, x, Lp.cout);
+        }
         if (pb > part) part = pb;
         if (dt == CF_BF16 && Lp.fwd == Fwd::Direct) {
             const size_t c = (size_t)27 * x.c * Lp.cout * 2;
@@ -603,6 +611,7 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
     if (dense_fwd_part_bytes(B, P.d1, P.d2) > dp) dp = dense_fwd_part_bytes(B, P.d1, P.d2);
     if (dp > part) part = dp;
     P.part = take(part);
+    P.part_w = take(part_w);
     P.cast = take(cast);
     const size_t f = 4;
     P.pre1 = take((size_t)B * P.d0 * f); P.y1 = take((size_t)B * P.d0 * f);
@@ -615,6 +624,37 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
     P.dW3 = take((size_t)P.d1 * P.d2 * f); P.db3 = take((size_t)P.d2 * f);
     P.total = off;
     return P;
+}
+
+// Per-device auxiliary stream for the training step's weight gradients and
+// the events that order it against the caller's stream.  Created on first
+// use (default priority, non-blocking) and kept until the process ends.  A
+// step's fork/join sequence is enqueued under the device's mutex: a stream
+// wait binds to the event's most recent record, so reusing the events is safe
+// while one call's records and waits are not interleaved with another's.
+struct AuxState {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[CF_MAX_BLOCKS + 1] = {};
+};
+constexpr int kMaxDevices = 64;
+AuxState g_aux[kMaxDevices];
+
+cf_status aux_get(AuxState** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(CF_ERR_HIP, "cf_train_step: no usable current device");
+    *out = &g_aux[dev];
+    return CF_OK;
+}
+
+cf_status aux_init(AuxState& ax)
+{
+    if (!ax.s) CF_TRY_HIP(hipStreamCreateWithFlags(&ax.s, hipStreamNonBlocking), "auxiliary stream");
+    for (int i = 0; i <= CF_MAX_BLOCKS; ++i)
+        if (!ax.ev[i]) CF_TRY_HIP(hipEventCreateWithFlags(&ax.ev[i], hipEventDisableTiming), "auxiliary event");
+    return CF_OK;
 }
 
 __global__ void cast_bf16_kernel(const float* __restrict__ s, uint16_t* __restrict__ d, int64_t n)
@@ -645,6 +685,13 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     const StepPlan P = plan_step(m, dtype, B);
     if (ws_bytes < P.total) return fail(CF_ERR_WORKSPACE, "cf_train_step: workspace %zu < %zu bytes", ws_bytes, P.total);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_train_step: workspace null or misaligned");
+    // the auxiliary stream exists before anything is enqueued; the device's
+    // lock is held while this call enqueues its fork/join sequence
+    AuxState* axp = nullptr;
+    if ((st = aux_get(&axp)) != CF_OK) return st;
+    AuxState& ax = *axp;
+    std::lock_guard<std::mutex> guard(ax.mu);
+    if ((st = aux_init(ax)) != CF_OK) return st;
     char* w = (char*)ws;
     auto F = [&](size_t o) { return (float*)(w + o); };
     float* part = F(P.part);
@@ -762,28 +809,54 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                                     F(P.dW1), F(P.db1), stream), "dense1 backward");
     }
 
-    // 5. conv blocks backward: pool backward -> weight gradient -> data gradient
-    for (int l = L - 1; l >= 0; --l) {
-        const LayerPlan& Lp = P.layer[l];
-        if (Lp.fused) {
-            CF_TRY_HIP(launch_wgrad_c4_pool(plan_wgrad(Lp.x, Lp.cout), (const uint16_t*)(l == 0 ? X : w + P.layer[l - 1].p),
-                                            (const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
-                                            (const uint8_t*)(w + Lp.idx), slope, part, F(Lp.dw), Lp.x, stream),
-                       "fused pool backward + conv3d backward-weight");
-            continue;
+    // 5. conv blocks backward: pool backward -> data gradient on the caller's
+    //    stream; each block's weight gradient (with its split reduction) on
+    //    the auxiliary stream once its conv-output gradient exists, so it
+    //    overlaps the rest of the backward chain.  The streams join before SGD.
+    {
+        float* part_w = F(P.part_w);
+        bool forked = false;
+        cf_status bst = CF_OK;
+        for (int l = L - 1; l >= 0 && bst == CF_OK; --l) {
+            const LayerPlan& Lp = P.layer[l];
+            if (Lp.fused) {
+                bst = check_hip(launch_wgrad_c4_pool(plan_wgrad(Lp.x, Lp.cout),
+                                                     (const uint16_t*)(l == 0 ? X : w + P.layer[l - 1].p),
+                                                     (const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
+                                                     (const uint8_t*)(w + Lp.idx), slope, part, F(Lp.dw), Lp.x,
+                                                     stream),
+                                "fused pool backward + conv3d backward-weight");
+                continue;
+            }
+            const cf_dims z = with_c(Lp.x, Lp.cout);
+            void* dz = w + Lp.z;    // the conv output buffer is reused for its gradient
+            hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
+                                                          (const uint8_t*)(w + Lp.idx), (uint16_t*)dz, z, slope, stream)
+                              : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
+                                                       (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
+            if ((bst = check_hip(e, "pool backward")) != CF_OK) break;
+            // fork: the weight gradient reads dz and the block input, which
+            // nothing on the caller's stream writes until the join
+            if ((bst = check_hip(hipEventRecord(ax.ev[l], stream), "fork event")) != CF_OK) break;
+            if ((bst = check_hip(hipStreamWaitEvent(ax.s, ax.ev[l], 0), "fork wait")) != CF_OK) break;
+            forked = true;
+            const void* xin = l == 0 ? X : (const void*)(w + P.layer[l - 1].p);
+            if ((bst = check_hip(run_wgrad(Lp.wg, dtype, Lp.x, xin, dz, Lp.cout, F(Lp.dw), part_w, ax.s),
+                                 "conv3d backward-weight")) != CF_OK)
+                break;
+            if (l > 0)
+                bst = check_hip(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + P.layer[l - 1].dp, part,
+                                          stream),
+                                "conv3d backward-data");
         }
-        const cf_dims z = with_c(Lp.x, Lp.cout);
-        void* dz = w + Lp.z;    // the conv output buffer is reused for its gradient
-        hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
-                                                      (const uint8_t*)(w + Lp.idx), (uint16_t*)dz, z, slope, stream)
-                          : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
-                                                   (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
-        CF_TRY_HIP(e, "pool backward");
-        const void* xin = l == 0 ? X : (const void*)(w + P.layer[l - 1].p);
-        CF_TRY_HIP(run_wgrad(Lp.wg, dtype, Lp.x, xin, dz, Lp.cout, F(Lp.dw), part, stream), "conv3d backward-weight");
-        if (l > 0)
-            CF_TRY_HIP(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + P.layer[l - 1].dp, part, stream),
-                       "conv3d backward-data");
+        if (forked) {
+            // join even after an error, so no work of this call outlives it on the auxiliary stream
+            const cf_status j1 = check_hip(hipEventRecord(ax.ev[CF_MAX_BLOCKS], ax.s), "join event");
+            const cf_status j2 = j1 == CF_OK ? check_hip(hipStreamWaitEvent(stream, ax.ev[CF_MAX_BLOCKS], 0), "join wait")
+                                             : j1;
+            if (bst == CF_OK) bst = j2;
+        }
+        if (bst != CF_OK) return bst;
     }
 
     // 6. SGD on every master parameter (one launch for all tensors)

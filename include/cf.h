@@ -239,7 +239,13 @@ size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int3
  *            W3, b3.  Updated in place.
  *   loss_out one device float: the loss of this step (before the update)
  *   pred_out [B, m->dense[2]] fp32 predictions of this step, or NULL
- * Layer-1 backward-data is not computed (the input needs no gradient). */
+ * Layer-1 backward-data is not computed (the input needs no gradient).
+ * Stream use: the weight gradients of the blocks run on an auxiliary stream
+ * that the library creates on the first call on each device (default
+ * priority, non-blocking) and keeps; it is forked from and joined back into
+ * `stream` with events within the call, so all of the step's work is ordered
+ * on `stream` as seen by the caller.  Calls from several host threads on one
+ * device are serialised while they enqueue. */
 cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const void* X,
                         const float* targets, float* const* params, float lr, float* loss_out,
                         float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream);
