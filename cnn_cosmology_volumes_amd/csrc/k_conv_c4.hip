@@ -34,10 +34,14 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
                           int N, int D, int H, int W, int Cout, int tD, int tH, int tW)
 {
     constexpr int MI = BM / 16, NJ = WN / 16;
-    // 4 bf16 per voxel, plus one zero voxel past the end (read, with zero
-    // weight, as the padded partner of the last tap)
-    __shared__ __attribute__((aligned(16))) uint2 halo[HV + 1];
-    __shared__ __attribute__((aligned(16))) uint16_t zt[POOL ? VT * ZS : 1];
+    // Halo: 4 bf16 per voxel, plus one zero voxel past the end (read, with
+    // zero weight, as the padded partner of the last tap).  The pooled
+    // epilogue's bf16 tile reuses the same LDS once every wave has finished
+    // reading the halo, which keeps a block at 40 KB (four blocks per CU).
+    constexpr int HALO_BYTES = (HV + 1) * 8, ZT_BYTES = POOL ? VT * ZS * 2 : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[HALO_BYTES > ZT_BYTES ? HALO_BYTES : ZT_BYTES];
+    uint2* const halo = reinterpret_cast<uint2*>(lds);
+    uint16_t* const zt = reinterpret_cast<uint16_t*>(lds);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -141,7 +145,9 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
     }
     // Pooled epilogue: bf16 tile in LDS, then one thread per (pooled voxel,
     // 8-channel group) takes the window maximum (first strict maximum in
-    // window order), applies leaky ReLU to it and stores P and idx.
+    // window order), applies leaky ReLU to it and stores P and idx.  The
+    // tile overwrites the halo, so every wave's halo reads come first.
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int v = wave * WN + 16 * j + l16;
