@@ -54,6 +54,19 @@ struct Tile {
     static constexpr int NE = HV * 4;             // 16-byte halo pieces per chunk
     static constexpr int IT = (NE + NT - 1) / NT; // halo pieces per thread
     static_assert(VT % WN == 0 && (NW == 4 || NW == 8), "tile");
+    // halo voxel offset (tap 0) of tile voxel v, in voxels
+    __host__ __device__ static constexpr int vox_off(int v) {
+        return ((v / (TH * TW)) * HH + (v / TW) % TH) * HW + v % TW;
+    }
+    // vox_off(w*WN + 16j + l) == vox_off(w*WN + l) + vox_off(16j) for every
+    // wave w, fragment j and lane l16
+    __host__ __device__ static constexpr bool frag_split() {
+        for (int w = 0; w < NWV; ++w)
+            for (int j = 0; j < NJ; ++j)
+                for (int l = 0; l < 16; ++l)
+                    if (vox_off(w * WN + 16 * j + l) != vox_off(w * WN + l) + vox_off(16 * j)) return false;
+        return true;
+    }
     static_assert(BM % WM == 0 && WM % 16 == 0 && WN % 16 == 0, "frag");
 };
 
@@ -101,16 +114,18 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int c_begin = blockIdx.z * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
 
-    // Per-lane LDS offsets (in bf16 units) of the B fragments: voxel base of
-    // tap 0 per fragment, plus the lane's swizzled 16-byte chunk for each
-    // kw (the halo w of a lane's voxel is tw + kw, the same for every j).
+    // Per-lane LDS offsets (in bf16 units) of the B fragments: the halo
+    // offset of a tile voxel splits exactly into a per-lane part (the wave's
+    // planes and l16) and a compile-time part per fragment j (checked by
+    // T::frag_split), so every fragment of a tap reads from one base
+    // register per kw with an immediate offset.  Plus the lane's swizzled
+    // 16-byte chunk for each kw (the halo w of a lane's voxel is tw + kw,
+    // the same for every j).
+    static_assert(T::frag_split(), "fragment offsets must split into lane and fragment parts");
+    const int hb0 = T::vox_off(wave * WN + l16) * LS;
     int hb[T::NJ];
 #pragma unroll
-    for (int j = 0; j < T::NJ; ++j) {
-        const int v = wave * WN + 16 * j + l16;
-        const int td = v / (TH * TW), th = (v / TW) % TH, tw = v % TW;
-        hb[j] = ((td * T::HH + th) * T::HW + tw) * LS;
-    }
+    for (int j = 0; j < T::NJ; ++j) hb[j] = hb0 + T::vox_off(16 * j) * LS;
     // The 32-channel ring tile with a 512-voxel halo (17 staging pieces per
     // thread) is already at 256 VGPRs; the swizzle's extra registers make it
     // spill (measured slower), so it keeps the plain layout.
@@ -176,7 +191,40 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
         }
         __syncthreads();
 
-        if constexpr (AR == 0) {
+        if constexpr (AR == 0 && T::MINB >= 3) {
+        // Register-lean pipeline for three waves per SIMD: weight (A)
+        // fragments come from global memory two taps ahead; a tap's halo (B)
+        // fragments are read from LDS at the start of the tap, and the other
+        // waves on the SIMD cover their latency.
+        const uint16_t* wrow = Wk + ((int64_t)(co_base + l16) * Cin + c * 32 + 8 * lg);
+        const int64_t tap_stride = (int64_t)CoutPad * Cin;
+        bf16x8 a0[T::MI], a1[T::MI], a2[T::MI], b0[T::NJ];
+#pragma unroll
+        for (int i = 0; i < T::MI; ++i) {
+            a0[i] = *reinterpret_cast<const bf16x8*>(wrow + (int64_t)16 * i * Cin);
+            a1[i] = *reinterpret_cast<const bf16x8*>(wrow + tap_stride + (int64_t)16 * i * Cin);
+        }
+#pragma unroll
+        for (int tap = 0; tap < 27; ++tap) {
+            if (tap + 2 < 27) {
+#pragma unroll
+                for (int i = 0; i < T::MI; ++i)
+                    a2[i] = *reinterpret_cast<const bf16x8*>(wrow + (tap + 2) * tap_stride + (int64_t)16 * i * Cin);
+            }
+            const int toff = (((tap / 9) * T::HH + (tap / 3) % 3) * T::HW + tap % 3) * LS;
+#pragma unroll
+            for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + (hb[j] + sw[tap % 3]) + toff);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < T::NJ; ++j)
+#pragma unroll
+                for (int i = 0; i < T::MI; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; }
+        }
+        } else if constexpr (AR == 0) {
         // Software pipeline over the 27 taps: weight (A) fragments are
         // loaded from global memory three taps ahead, halo (B) fragments are
         // read from LDS one tap ahead, so neither latency sits in front of
@@ -441,7 +489,7 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     case 1: e = launch_cfg<128, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
     case 2:
         e = p.ring ? launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s)
-                   : launch_cfg<64, 32, 128, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s);
+                   : launch_cfg<64, 32, 128, 4, 4, 16, 32, 3>(X, Wk, Y, part, x, cout, coutpad, p.splits, s);
         break;
     case 3:
         e = p.ring ? launch_cfg<64, 32, 128, 4, 8, 8, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s)
@@ -473,7 +521,7 @@ hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uin
         return launch_cfg<128, 32, 128, 4, 4, 16, 32, 0, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
     if (p.ring)
         return launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, true, 4>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
-    return launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
+    return launch_cfg<64, 32, 128, 4, 4, 16, 32, 3, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
 }
 
 }  // namespace cf
