@@ -25,8 +25,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two values rounded as by f2bf, packed low | high << 16.  Written as one
+// two-lane conversion so that it is a single v_cvt_pk_bf16_f32 (two scalar
+// conversions compile to two of them plus an OR).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    const bf16x2_t r = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 template <typename T> struct Elem;

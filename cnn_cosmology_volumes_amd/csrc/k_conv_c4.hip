@@ -108,8 +108,11 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         // second tap (the same for every lane group of the step).  A zero
         // slot has zero weights, so the finite halo value it reads (a
         // neighbouring voxel, or the zero voxel past the end) adds nothing.
-        const int ta = lg == 0 ? voff(c4_slot_tap(8 * s)) : lg == 1 ? voff(c4_slot_tap(8 * s + 2))
-                     : lg == 2 ? voff(c4_slot_tap(8 * s + 4)) : voff(c4_slot_tap(8 * s + 6));
+        // (the four lane groups' offsets packed 16 bits each and picked by a
+        // shift, which stays free of branches)
+        const uint64_t tab = (uint64_t)voff(c4_slot_tap(8 * s)) | (uint64_t)voff(c4_slot_tap(8 * s + 2)) << 16 |
+                             (uint64_t)voff(c4_slot_tap(8 * s + 4)) << 32 | (uint64_t)voff(c4_slot_tap(8 * s + 6)) << 48;
+        const int ta = (int)((tab >> (16 * lg)) & 0xffffu);
         const int dt = s == 2 ? HW : 1;
         const uint2* hp = halo + hb0 + ta;
 #pragma unroll
