@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--op-reps", type=int, default=10, help="repetitions per entry point in the per-kernel timing")
+    ap.add_argument("--op-reps", type=int, default=30, help="repetitions per entry point in the per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-ops", action="store_true", help="skip the per-entry-point timing")
@@ -64,9 +64,11 @@ def build_inputs(dev, torch, cf, sd, c):
     return xd, t, params
 
 
-def time_region(torch, fn, reps, stream):
-    """Average ms of fn() over reps calls, HIP events recorded on `stream`."""
-    fn()
+def time_region(torch, fn, reps, stream, warm=3):
+    """Average ms of fn() over reps calls after `warm` untimed calls, HIP
+    events recorded on `stream`."""
+    for _ in range(warm):
+        fn()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
