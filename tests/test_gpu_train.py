@@ -163,3 +163,53 @@ def test_train_step_rejects_bad_arguments():
     with pytest.raises(cf.CfError) as e:
         cf.cf_train_step(m, xd, to_dev(t, F32), params, 1e-3)
     assert e.value.status == cf.CF_ERR_UNSUPPORTED
+
+
+def test_train_step_concurrent_threads_and_streams_match_sequential():
+    """Steps enqueued from two host threads on two streams at once share the
+    library's auxiliary stream and events for the blocks' weight gradients;
+    each thread's losses and parameters must equal, bit for bit, the same
+    steps run one after another on one stream."""
+    import threading
+    B, size, filters, dense_w = 2, 32, [32, 64, 128], [64, 32, 3]
+    m = cf.model_desc(4, size, filters, dense_w, SLOPE)
+    probs = [make_problem(20 + k, B, size, filters, dense_w, BF) for k in range(2)]
+    nsteps, lr = 3, 1e-5
+
+    ref = []
+    for x, conv, dense, t in probs:
+        xd, td, p = to_dev(x, BF), to_dev(t, F32), device_params(conv, dense)
+        losses = [cf.cf_train_step(m, xd, td, p, lr)[0].clone() for _ in range(nsteps)]
+        torch.cuda.synchronize()
+        ref.append(([l.item() for l in losses], [q.cpu() for q in p]))
+
+    inputs = [(to_dev(x, BF), to_dev(t, F32), device_params(conv, dense)) for x, conv, dense, t in probs]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+    start = threading.Barrier(2)
+
+    def work(k):
+        try:
+            xd, td, p = inputs[k]
+            s = streams[k]
+            with torch.cuda.stream(s):
+                start.wait(timeout=60)
+                losses = [cf.cf_train_step(m, xd, td, p, lr, stream=s)[0].clone() for _ in range(nsteps)]
+            s.synchronize()
+            results[k] = losses
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    assert all(not th.is_alive() for th in threads)
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert [l.item() for l in results[k]] == ref[k][0]
+        for a, b in zip(inputs[k][2], ref[k][1]):
+            assert torch.equal(a.cpu(), b)
