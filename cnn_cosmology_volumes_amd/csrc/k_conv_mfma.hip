@@ -81,7 +81,7 @@ struct Tile {
 // 32-byte halves are swapped where bit 2 of the voxel's halo w is set.
 __device__ __forceinline__ int halo_chunk(int q, int hw) { return q ^ (((hw >> 2) & 1) << 1); }
 
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false, int AR = 0>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false>
 __global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                         uint16_t* __restrict__ Y, float* __restrict__ part,
@@ -90,14 +90,6 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 {
     using T = Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>;
     __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LS];
-    // AR > 0: the block's weight tile of each tap (BM rows x 32 channels) is
-    // loaded once, by BM*4 threads, into a ring of AR LDS slots two taps
-    // ahead, and every wave reads its fragments from there (instead of each
-    // wave loading the same fragments from L2).  Row stride AS bf16.
-    constexpr int AS = 48;
-    __shared__ __attribute__((aligned(16))) uint16_t aring[AR > 0 ? AR * BM * AS : 8];
-    static_assert(AR == 0 || (AR >= 4 && BM * 4 <= T::NT), "weight ring");
-
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) % T::NWM;     // co slice of this wave
     const int wave = (threadIdx.x >> 6) / T::NWM;   // voxel slice of this wave
@@ -126,13 +118,9 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     int hb[T::NJ];
 #pragma unroll
     for (int j = 0; j < T::NJ; ++j) hb[j] = hb0 + T::vox_off(16 * j) * LS;
-    // The 32-channel ring tile with a 512-voxel halo (17 staging pieces per
-    // thread) is already at 256 VGPRs; the swizzle's extra registers make it
-    // spill (measured slower), so it keeps the plain layout.
-    constexpr bool SWZ = !(AR > 0 && T::IT > 16);
     int sw[3];
 #pragma unroll
-    for (int kw = 0; kw < 3; ++kw) sw[kw] = (SWZ ? halo_chunk(lg, (l16 % TW) + kw) : lg) * 8;
+    for (int kw = 0; kw < 3; ++kw) sw[kw] = halo_chunk(lg, (l16 % TW) + kw) * 8;
 
     f32x4 acc[T::MI][T::NJ];
 #pragma unroll
@@ -162,36 +150,16 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
                     val[it] = *reinterpret_cast<const uint4*>(xs + vox * Cin + q * 8);
                 }
             }
-            // weight ring prologue: taps 0..AR-3
-            uint4 wv[AR > 2 ? AR - 2 : 1];
-            const bool ald0 = AR > 0 && threadIdx.x < BM * 4;
-            if constexpr (AR > 0) {
-                const uint16_t* asrc0 = Wk + ((int64_t)(blockIdx.y * BM + (threadIdx.x >> 2)) * Cin + c * 32 +
-                                              (threadIdx.x & 3) * 8);
-#pragma unroll
-                for (int k = 0; k < AR - 2; ++k)
-                    wv[k] = ald0 ? *reinterpret_cast<const uint4*>(asrc0 + (int64_t)k * CoutPad * Cin)
-                                 : make_uint4(0u, 0u, 0u, 0u);
-            }
 #pragma unroll
             for (int it = 0; it < T::IT; ++it) {
                 const int e = threadIdx.x + it * T::NT;
                 if (T::NE % T::NT == 0 || e < T::NE)
-                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS +
-                                              (SWZ ? halo_chunk(e & 3, (e >> 2) % T::HW) : (e & 3)) * 8) = val[it];
-            }
-            if constexpr (AR > 0) {
-                if (ald0) {
-#pragma unroll
-                    for (int k = 0; k < AR - 2; ++k)
-                        *reinterpret_cast<uint4*>(aring + k * BM * AS + (threadIdx.x >> 2) * AS + (threadIdx.x & 3) * 8) =
-                            wv[k];
-                }
+                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS + halo_chunk(e & 3, (e >> 2) % T::HW) * 8) = val[it];
             }
         }
         __syncthreads();
 
-        if constexpr (AR == 0 && T::MINB >= 3) {
+        if constexpr (T::MINB >= 3) {
         // Register-lean pipeline for three waves per SIMD: weight (A)
         // fragments come from global memory two taps ahead; a tap's halo (B)
         // fragments are read from LDS at the start of the tap, and the other
@@ -224,7 +192,7 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 #pragma unroll
             for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; }
         }
-        } else if constexpr (AR == 0) {
+        } else {
         // Software pipeline over the 27 taps: weight (A) fragments are
         // loaded from global memory three taps ahead, halo (B) fragments are
         // read from LDS one tap ahead, so neither latency sits in front of
@@ -264,61 +232,6 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < T::MI; ++i) { a0[i] = a1[i]; a1[i] = a2[i]; a2[i] = a3[i]; }
-#pragma unroll
-            for (int j = 0; j < T::NJ; ++j) b0[j] = b1[j];
-        }
-        } else {
-        // Weight ring: taps 0..AR-3 were staged with the halo (below the
-        // first barrier of this chunk); tap t+AR-2 is written into slot
-        // (t+AR-2) % AR after tap t's MFMAs from a register loaded one tap
-        // earlier, and read back one tap before use.  A slot is rewritten
-        // only after a barrier that follows its last read.  The barrier
-        // between taps waits for LDS only: an outstanding weight load must
-        // not be waited for there.
-        const bool ald = threadIdx.x < BM * 4;
-        const int arow = threadIdx.x >> 2, aq = threadIdx.x & 3;
-        const int64_t tap_stride = (int64_t)CoutPad * Cin;
-        const uint16_t* asrc = Wk + ((int64_t)(blockIdx.y * BM + arow) * Cin + c * 32 + aq * 8);
-        uint16_t* adst = aring + arow * AS + aq * 8;
-        int aoff[T::MI];
-#pragma unroll
-        for (int i = 0; i < T::MI; ++i) aoff[i] = (wm * WM + 16 * i + l16) * AS + 8 * lg;
-        uint4 ra = make_uint4(0u, 0u, 0u, 0u);
-        if (ald) ra = *reinterpret_cast<const uint4*>(asrc + (int64_t)(AR - 2) * tap_stride);
-        bf16x8 a0[T::MI], a1[T::MI], b0[T::NJ], b1[T::NJ];
-#pragma unroll
-        for (int i = 0; i < T::MI; ++i) a0[i] = *reinterpret_cast<const bf16x8*>(aring + aoff[i]);
-#pragma unroll
-        for (int j = 0; j < T::NJ; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(halo + hb[j] + sw[0]);
-#pragma unroll
-        for (int tap = 0; tap < 27; ++tap) {
-            uint4 rn = make_uint4(0u, 0u, 0u, 0u);
-            if (ald && tap + AR - 1 < 27) rn = *reinterpret_cast<const uint4*>(asrc + (int64_t)(tap + AR - 1) * tap_stride);
-            if (tap + 1 < 27) {
-                const int tn = tap + 1;
-                const int toff = (((tn / 9) * T::HH + (tn / 3) % 3) * T::HW + tn % 3) * LS;
-#pragma unroll
-                for (int i = 0; i < T::MI; ++i)
-                    a1[i] = *reinterpret_cast<const bf16x8*>(aring + (tn % AR) * BM * AS + aoff[i]);
-#pragma unroll
-                for (int j = 0; j < T::NJ; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(halo + (hb[j] + sw[tn % 3]) + toff);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i)
-#pragma unroll
-                for (int j = 0; j < T::NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (ald && tap + AR - 2 < 27)
-                *reinterpret_cast<uint4*>(adst + ((tap + AR - 2) % AR) * BM * AS) = ra;
-            ra = rn;
-            if (tap + 1 < 27) {
-                __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's LDS writes done
-                __builtin_amdgcn_s_barrier();
-            }
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i) a0[i] = a1[i];
 #pragma unroll
             for (int j = 0; j < T::NJ; ++j) b0[j] = b1[j];
         }
@@ -398,6 +311,236 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     }
 }
 
+// kd-reuse variant of the same convolution.  The taps are walked as 9 (kh, kw)
+// steps with the three kd taps inside each step, and a wave's fragments are
+// whole depth columns of its h rows: fragment j covers tile depth j / JH and
+// h rows (wave * JH + j % JH) * RPF .. + RPF - 1.  At step (kh, kw) the B
+// operand of fragment j under tap kd is then the halo fragment that fragment
+// j + JH * kd reads under tap 0, so a step reads (TD + 2) * JH B fragments
+// for 3 * NJ fragment-taps (6 for 12 on a 4-deep, one-fragment-per-plane
+// wave) instead of one per fragment-tap.  The operand reads per MFMA drop
+// by about a third; the sums over the taps are taken in (kh, kw)-major,
+// kd-minor order.
+// The block's weight tiles of a step's three taps (BM rows x 32 channels
+// each, row stride AS bf16) are loaded once into one of two 3-slot LDS groups
+// (one group per step, alternating), from registers filled two steps ahead;
+// a group is rewritten only after the barrier that ends the step which read
+// it.  AS = 40 keeps the 32-channel block at 53.8 KB of LDS (three blocks per
+// CU); the 64-channel blocks measured faster with AS = 48.
+// POOL as in conv3d_mfma_kernel: a 2^3 window is the fragments (2 pd + a) *
+// JH + b of one lane (a = d, b = h offset) and of its w-neighbour lane.
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
+__global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS>::MINB))
+void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
+                            uint16_t* __restrict__ Y, float* __restrict__ part,
+                            int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
+                            int tD, int tH, int tW, int chunks_per_split, uint8_t* __restrict__ pidx, float slope)
+{
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    constexpr int RPF = 16 / TW;            // h rows per fragment
+    constexpr int JH = T::NJ / TD;          // fragments per depth plane of a wave
+    constexpr int RPW = JH * RPF;           // h rows of a wave
+    constexpr int NB = (TD + 2) * JH;       // distinct B fragments per step
+    static_assert(TW * RPF == 16 && T::NJ % TD == 0 && T::NWV * RPW == TH, "kd-reuse fragment layout");
+    __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LS];
+    __shared__ __attribute__((aligned(16))) uint16_t aring[6 * BM * AS];
+    static_assert(BM * 4 <= T::NT && AS >= 32 && AS % 8 == 0, "weight ring");
+
+    const int lane = threadIdx.x & 63;
+    const int wm = (threadIdx.x >> 6) % T::NWM;
+    const int wave = (threadIdx.x >> 6) / T::NWM;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int tw_ = tile % tW; tile /= tW;
+    const int th_ = tile % tH; tile /= tH;
+    const int td_ = tile % tD;
+    const int n = tile / tD;
+    const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
+    const int co_base = blockIdx.y * BM + wm * WM;
+    const int nchunks = Cin >> 5;
+    const int c_begin = blockIdx.z * chunks_per_split;
+    const int c_end = min(c_begin + chunks_per_split, nchunks);
+
+    // lane part of the halo offset (depth plane 0, h-sub 0, tap 0); the
+    // plane, h-sub and tap parts are compile-time immediates
+    const int hbl = ((wave * RPW + l16 / TW) * T::HW + l16 % TW) * LS;
+    int sw[3];
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw) sw[kw] = hbl + halo_chunk(lg, (l16 % TW) + kw) * 8;
+
+    f32x4 acc[T::MI][T::NJ];
+#pragma unroll
+    for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < T::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t plane = (int64_t)H * W;
+    const int64_t tap_stride = (int64_t)CoutPad * Cin;
+    const bool ald = threadIdx.x < BM * 4;       // the ring's loader threads
+    const int arow = threadIdx.x >> 2, aq = threadIdx.x & 3;
+    for (int c = c_begin; c < c_end; ++c) {
+        __syncthreads();
+        const uint16_t* asrc = Wk + ((int64_t)(blockIdx.y * BM + arow) * Cin + c * 32 + aq * 8);
+        uint4 ra[3];
+        {
+            const uint16_t* xs = X + (int64_t)n * D * plane * Cin + c * 32;
+            uint4 val[T::IT];
+#pragma unroll
+            for (int it = 0; it < T::IT; ++it) {
+                const int e = threadIdx.x + it * T::NT;
+                const int q = e & 3, hv = e >> 2;
+                const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
+                const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+                val[it] = make_uint4(0u, 0u, 0u, 0u);
+                if ((T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
+                    (unsigned)gw < (unsigned)W) {
+                    const int64_t vox = (int64_t)(gd * H + gh) * W + gw;
+                    val[it] = *reinterpret_cast<const uint4*>(xs + vox * Cin + q * 8);
+                }
+            }
+            // weight ring prologue: step 0's tiles go to group 0 with the
+            // halo, step 1's are held in registers until step 0 stores them
+            uint4 w0v[3];
+#pragma unroll
+            for (int kd = 0; kd < 3; ++kd) {
+                w0v[kd] = ald ? *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd) * tap_stride)
+                              : make_uint4(0u, 0u, 0u, 0u);
+                ra[kd] = ald ? *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd + 1) * tap_stride)
+                             : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int it = 0; it < T::IT; ++it) {
+                const int e = threadIdx.x + it * T::NT;
+                if (T::NE % T::NT == 0 || e < T::NE)
+                    *reinterpret_cast<uint4*>(halo + (e >> 2) * LS + halo_chunk(e & 3, (e >> 2) % T::HW) * 8) = val[it];
+            }
+            if (ald) {
+#pragma unroll
+                for (int kd = 0; kd < 3; ++kd)
+                    *reinterpret_cast<uint4*>(aring + kd * BM * AS + arow * AS + aq * 8) = w0v[kd];
+            }
+        }
+        __syncthreads();
+
+        int aoff[T::MI];
+#pragma unroll
+        for (int i = 0; i < T::MI; ++i) aoff[i] = (wm * WM + 16 * i + l16) * AS + 8 * lg;
+        bf16x8 a[3][T::MI], b[NB];
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            const int kh = s / 3, kw = s % 3;
+            // ring loads two steps ahead, then this step's operands
+            uint4 rn[3];
+#pragma unroll
+            for (int kd = 0; kd < 3; ++kd) {
+                rn[kd] = make_uint4(0u, 0u, 0u, 0u);
+                if (ald && s + 2 < 9)
+                    rn[kd] = *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd + s + 2) * tap_stride);
+            }
+#pragma unroll
+            for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+                for (int i = 0; i < T::MI; ++i)
+                    a[kd][i] = *reinterpret_cast<const bf16x8*>(aring + ((s & 1) * 3 + kd) * BM * AS + aoff[i]);
+#pragma unroll
+            for (int p = 0; p < TD + 2; ++p)
+#pragma unroll
+                for (int hs = 0; hs < JH; ++hs)
+                    b[p * JH + hs] = *reinterpret_cast<const bf16x8*>(
+                        halo + sw[kw] + ((p * T::HH + hs * RPF + kh) * T::HW + kw) * LS);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+                for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < T::NJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kd][i], b[j + kd * JH], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next step's tiles into the other group (last read in the
+            // step before this one, behind its barrier)
+            if (ald && s + 1 < 9) {
+#pragma unroll
+                for (int kd = 0; kd < 3; ++kd)
+                    *reinterpret_cast<uint4*>(aring + (((s + 1) & 1) * 3 + kd) * BM * AS + arow * AS + aq * 8) = ra[kd];
+            }
+#pragma unroll
+            for (int kd = 0; kd < 3; ++kd) ra[kd] = rn[kd];
+            if (s + 1 < 9) lds_barrier();
+        }
+    }
+
+    if constexpr (POOL) {
+        static_assert(TW == 16 && JH == 2 && TD % 2 == 0, "pooled epilogue mapping");
+        const int Dp = D >> 1, Hp = H >> 1, Wp = W >> 1;
+        const uint32_t c = l16 & 1;                        // window w offset of this lane
+        const int gph = (h0 >> 1) + wave, gpw = (w0 >> 1) + (l16 >> 1);
+#pragma unroll
+        for (int pd = 0; pd < TD / 2; ++pd) {
+            const int gpd = (d0 >> 1) + pd;
+            const bool inside = gpd < Dp && gph < Hp && gpw < Wp;
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i) {
+                const int co = co_base + 16 * i + 4 * lg;
+                float out[4];
+                uint32_t bix[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // this lane's four window members in window order (a, b) = 00, 01, 10, 11
+                    float z[4];
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab)
+                        z[ab] = __uint_as_float((uint32_t)f2bf(acc[i][(2 * pd + (ab >> 1)) * JH + (ab & 1)][r]) << 16);
+                    // even lanes start from window position 0 like a sequential scan;
+                    // odd lanes from -inf, so a NaN at position 1 is skipped as the
+                    // scan would skip it
+                    float best = c ? -INFINITY : z[0];
+                    uint32_t bp = c;
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab)
+                        if (z[ab] > best) { best = z[ab]; bp = 2u * ab + c; }
+                    // combine with the neighbour lane (the other w position): larger
+                    // value, on a tie the earlier window position
+                    const float ob = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(best), 0xB1, 0xF, 0xF, false));
+                    const uint32_t op = (uint32_t)__builtin_amdgcn_mov_dpp((int)bp, 0xB1, 0xF, 0xF, false);
+                    if (ob > best || (ob == best && op < bp)) { best = ob; bp = op; }
+                    out[r] = best > 0.f ? best : slope * best;
+                    bix[r] = bp;
+                }
+                if (c == 0 && inside && co < Cout) {
+                    const int64_t o = (((int64_t)n * Dp + gpd) * Hp + gph) * Wp * Cout + (int64_t)gpw * Cout + co;
+                    *reinterpret_cast<uint2*>(Y + o) = make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
+                    *reinterpret_cast<uint32_t*>(pidx + o) = bix[0] | (bix[1] << 8) | (bix[2] << 16) | (bix[3] << 24);
+                }
+            }
+        }
+        return;
+    }
+
+    const int64_t nvox = (int64_t)N * D * plane;
+#pragma unroll
+    for (int j = 0; j < T::NJ; ++j) {
+        const int td = j / JH, th = (wave * JH + j % JH) * RPF + l16 / TW, tw = l16 % TW;
+        const int gd = d0 + td, gh = h0 + th, gw = w0 + tw;
+        if (gd >= D || gh >= H || gw >= W) continue;
+        const int64_t gv = ((int64_t)n * D + gd) * plane + (int64_t)gh * W + gw;
+#pragma unroll
+        for (int i = 0; i < T::MI; ++i) {
+            const int co = co_base + 16 * i + 4 * lg;
+            if (co >= Cout) continue;
+            const f32x4 r = acc[i][j];
+            if (part) {
+                float* dst = part + ((int64_t)blockIdx.z * nvox + gv) * Cout + co;
+                *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+            } else {
+                uint2 pk = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+                *reinterpret_cast<uint2*>(Y + gv * Cout + co) = pk;
+            }
+        }
+    }
+}
+
 // Sum the split partials in split order and round to bf16.
 __global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __restrict__ Y, int64_t n4,
                                   int splits)
@@ -413,19 +556,31 @@ __global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __re
     }
 }
 
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
+hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x, int cout,
+                      int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
+{
+    using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
+    const int nchunks = (int)(x.c / 32);
+    const int cps = (nchunks + splits - 1) / splits;
+    dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
+    hipLaunchKernelGGL((conv3d_mfma_kdr_kernel<BM, WM, WN, TD, TH, TW, LS, AS, POOL>), grid, dim3(T::NT), 0, s, X, Wk,
+                       Y, splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, coutpad,
+                       tD, tH, tW, cps, pidx, slope);
+    return hipGetLastError();
+}
+
 struct CfgInfo { int bm, wm, wn, td, th, tw, ls; };
 constexpr CfgInfo kCfgs[] = {
-    {128, 32, 128, 4, 4, 16, 32},   // 0
-    {128, 32, 128, 4, 8, 8, 32},    // 1
-    {64, 32, 128, 4, 4, 16, 32},    // 2
-    {64, 32, 128, 4, 8, 8, 32},     // 3
-    {32, 32, 128, 4, 8, 16, 32},    // 4
-    {32, 32, 64, 4, 8, 8, 32},      // 5
-    {16, 16, 64, 4, 4, 16, 32},     // 6
-    {16, 16, 64, 4, 8, 8, 32},      // 7
+    {64, 32, 128, 4, 4, 16, 32},    // 0
+    {64, 32, 128, 4, 8, 8, 32},     // 1
+    {32, 32, 64, 4, 8, 8, 32},      // 2
+    {16, 16, 64, 4, 4, 16, 32},     // 3
+    {16, 16, 64, 4, 8, 8, 32},      // 4
 };
 
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false, int AR = 0>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x,
                       int cout, int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
 {
@@ -434,7 +589,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float*
     const int nchunks = (int)(x.c / 32);
     const int cps = (nchunks + splits - 1) / splits;
     dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
-    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WM, WN, TD, TH, TW, LS, WPE_, POOL, AR>), grid, dim3(T::NT), 0, s, X, Wk,
+    hipLaunchKernelGGL((conv3d_mfma_kernel<BM, WM, WN, TD, TH, TW, LS, WPE_, POOL>), grid, dim3(T::NT), 0, s, X, Wk,
                        Y, splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
                        coutpad, tD, tH, tW, cps, pidx, slope);
     return hipGetLastError();
@@ -449,11 +604,11 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
     // than 128-channel 8-wave blocks (one per CU) at every layer shape.
     ConvPlan p{};
     const bool narrow = x.w < 16;
-    if (cout > 32) p.cfg = narrow ? 3 : 2;
+    if (cout > 32) p.cfg = narrow ? 1 : 0;
     // 17..32 channels: the 4x8x8 tile (its halo takes the bank swizzle; the
     // 4x8x16 tile is at the register limit without it) measured faster
-    else if (cout > 16) p.cfg = 5;
-    else p.cfg = narrow ? 7 : 6;
+    else if (cout > 16) p.cfg = 2;
+    else p.cfg = narrow ? 4 : 3;
     const CfgInfo& c = kCfgs[p.cfg];
     p.bm = c.bm;
     const int64_t tiles = x.n * ((x.d + c.td - 1) / c.td) * ((x.h + c.th - 1) / c.th) * ((x.w + c.tw - 1) / c.tw);
@@ -470,12 +625,14 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
         splits = (nchunks + cps - 1) / cps;
     }
     p.splits = splits;
-    // The weight ring loads each tap's weights once per block instead of once
-    // per wave; it pays off where four waves share a 32-channel slice, or a
-    // block walks several channel chunks (measured 7-16% faster there, 3%
-    // slower on a single-chunk 64-channel block).
+    // The weight ring (conv3d_mfma_kdr_kernel) loads each tap's weights once
+    // per block instead of once per wave; it pays off where four waves share
+    // a 32-channel slice, or a block walks several channel chunks.  A
+    // single-chunk 64-channel block is faster with per-wave weight loads
+    // and three waves per SIMD (conv3d_mfma_kernel).  The 16-channel tiles
+    // always take per-wave loads.
     const int cps = (nchunks + splits - 1) / splits;
-    p.ring = c.bm == 32 || cps >= 2;
+    p.ring = p.cfg <= 2 && (c.bm == 32 || cps >= 2);
     p.part_bytes = splits > 1 ? (size_t)splits * (size_t)(x.n * x.d * x.h * x.w) * (size_t)cout * sizeof(float) : 0;
     return p;
 }
@@ -484,21 +641,21 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
                             const cf_dims& x, int cout, int coutpad, hipStream_t s)
 {
     hipError_t e;
-    switch (p.cfg) {
-    case 0: e = launch_cfg<128, 32, 128, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 1: e = launch_cfg<128, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 2:
-        e = p.ring ? launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s)
-                   : launch_cfg<64, 32, 128, 4, 4, 16, 32, 3>(X, Wk, Y, part, x, cout, coutpad, p.splits, s);
-        break;
-    case 3:
-        e = p.ring ? launch_cfg<64, 32, 128, 4, 8, 8, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s)
-                   : launch_cfg<64, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s);
-        break;
-    case 4: e = launch_cfg<32, 32, 128, 4, 8, 16, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 5: e = launch_cfg<32, 32, 64, 4, 8, 8, 32, 0, false, 4>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    case 6: e = launch_cfg<16, 16, 64, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-    default: e = launch_cfg<16, 16, 64, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+    if (p.ring) {
+        switch (p.cfg) {
+        case 0: e = launch_kdr<64, 32, 128, 4, 4, 16, 32, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        case 1: e = launch_kdr<64, 32, 128, 4, 8, 8, 32, 48>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        case 2: e = launch_kdr<32, 32, 64, 4, 8, 8, 32, 40>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.cfg) {
+        case 0: e = launch_cfg<64, 32, 128, 4, 4, 16, 32, 3>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        case 1: e = launch_cfg<64, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        case 3: e = launch_cfg<16, 16, 64, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        case 4: e = launch_cfg<16, 16, 64, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
@@ -508,19 +665,20 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     return hipGetLastError();
 }
 
+// The pooled epilogue runs in the same kernel and tap order as the plain
+// launch of the same plan, so the fused result equals conv then pool bit
+// for bit.
 bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x)
 {
-    return p.splits == 1 && (p.cfg == 0 || p.cfg == 2) && (x.d % 2 == 0) && (x.h % 2 == 0) && (x.w % 2 == 0);
+    return p.splits == 1 && p.cfg == 0 && (x.d % 2 == 0) && (x.h % 2 == 0) && (x.w % 2 == 0);
 }
 
 hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx,
                                  float slope, const cf_dims& x, int cout, int coutpad, hipStream_t s)
 {
     if (!conv_mfma_can_pool(p, x)) return hipErrorInvalidValue;
-    if (p.cfg == 0)
-        return launch_cfg<128, 32, 128, 4, 4, 16, 32, 0, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
     if (p.ring)
-        return launch_cfg<64, 32, 128, 4, 4, 16, 32, 0, true, 4>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
+        return launch_kdr<64, 32, 128, 4, 4, 16, 32, 48, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
     return launch_cfg<64, 32, 128, 4, 4, 16, 32, 3, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
 }
 
