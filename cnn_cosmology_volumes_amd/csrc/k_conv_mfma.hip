@@ -626,13 +626,16 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
     }
     p.splits = splits;
     // The weight ring (conv3d_mfma_kdr_kernel) loads each tap's weights once
-    // per block instead of once per wave; it pays off where four waves share
-    // a 32-channel slice, or a block walks several channel chunks.  A
-    // single-chunk 64-channel block is faster with per-wave weight loads
-    // and three waves per SIMD (conv3d_mfma_kernel).  The 16-channel tiles
-    // always take per-wave loads.
+    // per block instead of once per wave, six taps ahead; it pays off where
+    // four waves share a 32-channel slice, where a block walks several
+    // channel chunks, and on the narrow (8-wide) tiles of the small late
+    // layers, whose per-wave weight loads three taps ahead left their few
+    // waves waiting on L2 (8^3 x 256 -> 256: 0.046 -> 0.042 ms).  A
+    // single-chunk 64-channel block on a 16-wide tile is faster with per-wave
+    // weight loads and three waves per SIMD (conv3d_mfma_kernel).  The
+    // 16-channel tiles always take per-wave loads.
     const int cps = (nchunks + splits - 1) / splits;
-    p.ring = p.cfg <= 2 && (c.bm == 32 || cps >= 2);
+    p.ring = p.cfg <= 2 && !(p.cfg == 0 && cps == 1);
     p.part_bytes = splits > 1 ? (size_t)splits * (size_t)(x.n * x.d * x.h * x.w) * (size_t)cout * sizeof(float) : 0;
     return p;
 }
@@ -651,7 +654,6 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     } else {
         switch (p.cfg) {
         case 0: e = launch_cfg<64, 32, 128, 4, 4, 16, 32, 3>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
-        case 1: e = launch_cfg<64, 32, 128, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
         case 3: e = launch_cfg<16, 16, 64, 4, 4, 16, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
         case 4: e = launch_cfg<16, 16, 64, 4, 8, 8, 32>(X, Wk, Y, part, x, cout, coutpad, p.splits, s); break;
         default: return hipErrorInvalidValue;
