@@ -379,35 +379,57 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     const int64_t tap_stride = (int64_t)CoutPad * Cin;
     const bool ald = threadIdx.x < BM * 4;       // the ring's loader threads
     const int arow = threadIdx.x >> 2, aq = threadIdx.x & 3;
+    // Every global load of this kernel is a raw buffer load at a 32-bit byte
+    // offset computed once for all channel chunks; a piece outside the volume
+    // (or a thread that loads nothing) gets an offset beyond the buffer, which
+    // reads zeros.  Halo offsets are relative to the tile's first in-volume
+    // depth plane (the host keeps (TD + 2) planes below 2^31 bytes); weight
+    // offsets to the block's first row, with the tap in the scalar offset.
+    constexpr uint32_t OOB = 0x80000000u;
+    auto pick = [](bool ok, uint32_t off) {
+        uint32_t r = ok ? off : OOB;
+        asm volatile("" : "+v"(r));     // keeps the choice a select, not a branch around the load
+        return r;
+    };
+    const int dlo = d0 > 0 ? d0 - 1 : 0;
+    const int dhi = min(d0 + TD + 1, D);
+    const uint16_t* xbase = X + ((int64_t)n * D + dlo) * plane * Cin;
+    const uint32_t xbytes = (uint32_t)((int64_t)(dhi - dlo) * plane * Cin * 2);
+    uint32_t hoff[T::IT];
+#pragma unroll
+    for (int it = 0; it < T::IT; ++it) {
+        const int e = threadIdx.x + it * T::NT;
+        const int q = e & 3, hv = e >> 2;
+        const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
+        const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+        const bool ok = (T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
+                        (unsigned)gw < (unsigned)W;
+        hoff[it] = pick(ok, (((uint32_t)(gd - dlo) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) *
+                                (uint32_t)(Cin * 2) + (uint32_t)q * 16u);
+    }
+    const uint32_t wbytes = (uint32_t)(27 * tap_stride * 2);
+    const uint16_t* wbase = Wk + (int64_t)blockIdx.y * BM * Cin;
+    const uint32_t aoffb = pick(ald, ((uint32_t)arow * (uint32_t)Cin + (uint32_t)aq * 8u) * 2u);
+    auto wload = [&](int c, int tap) {
+        const auto rw = buf_rsrc(wbase + c * 32, wbytes - (uint32_t)(blockIdx.y * BM * Cin + c * 32) * 2u);
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, aoffb, (int)(tap * tap_stride * 2), 0));
+    };
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
-        const uint16_t* asrc = Wk + ((int64_t)(blockIdx.y * BM + arow) * Cin + c * 32 + aq * 8);
         uint4 ra[3];
         {
-            const uint16_t* xs = X + (int64_t)n * D * plane * Cin + c * 32;
+            const auto rx = buf_rsrc(xbase + c * 32, xbytes - (uint32_t)c * 64u);
             uint4 val[T::IT];
 #pragma unroll
-            for (int it = 0; it < T::IT; ++it) {
-                const int e = threadIdx.x + it * T::NT;
-                const int q = e & 3, hv = e >> 2;
-                const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
-                const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-                val[it] = make_uint4(0u, 0u, 0u, 0u);
-                if ((T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
-                    (unsigned)gw < (unsigned)W) {
-                    const int64_t vox = (int64_t)(gd * H + gh) * W + gw;
-                    val[it] = *reinterpret_cast<const uint4*>(xs + vox * Cin + q * 8);
-                }
-            }
+            for (int it = 0; it < T::IT; ++it)
+                val[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, hoff[it], 0, 0));
             // weight ring prologue: step 0's tiles go to group 0 with the
             // halo, step 1's are held in registers until step 0 stores them
             uint4 w0v[3];
 #pragma unroll
             for (int kd = 0; kd < 3; ++kd) {
-                w0v[kd] = ald ? *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd) * tap_stride)
-                              : make_uint4(0u, 0u, 0u, 0u);
-                ra[kd] = ald ? *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd + 1) * tap_stride)
-                             : make_uint4(0u, 0u, 0u, 0u);
+                w0v[kd] = wload(c, 9 * kd);
+                ra[kd] = wload(c, 9 * kd + 1);
             }
 #pragma unroll
             for (int it = 0; it < T::IT; ++it) {
@@ -433,11 +455,7 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             // ring loads two steps ahead, then this step's operands
             uint4 rn[3];
 #pragma unroll
-            for (int kd = 0; kd < 3; ++kd) {
-                rn[kd] = make_uint4(0u, 0u, 0u, 0u);
-                if (ald && s + 2 < 9)
-                    rn[kd] = *reinterpret_cast<const uint4*>(asrc + (int64_t)(9 * kd + s + 2) * tap_stride);
-            }
+            for (int kd = 0; kd < 3; ++kd) rn[kd] = s + 2 < 9 ? wload(c, 9 * kd + s + 2) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int kd = 0; kd < 3; ++kd)
 #pragma unroll
@@ -561,6 +579,11 @@ hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float*
                       int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
 {
     using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
+    // the kernel's 32-bit buffer offsets: a tile's TD + 2 input planes and
+    // the weight copy must stay below 2^31 bytes
+    if ((int64_t)(TD + 2) * x.h * x.w * x.c * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)27 * coutpad * x.c * 2 >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const int nchunks = (int)(x.c / 32);
     const int cps = (nchunks + splits - 1) / splits;
