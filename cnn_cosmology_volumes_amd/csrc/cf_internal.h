@@ -108,6 +108,7 @@ struct WprepJob {
 struct WprepList {
     int count;
     WprepJob job[2 * 8];
+    int start[2 * 8 + 1];   // first block of each job in the flattened grid (set by the launcher)
 };
 hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s);
 // fp32 dgrad weights for the direct path: Wt[t'][co][ci] = W[26-t'][ci][co] (float or bf16 source kept as-is)

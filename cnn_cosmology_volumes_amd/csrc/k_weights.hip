@@ -87,16 +87,20 @@ __global__ __launch_bounds__(256)
 void wprep_multi_kernel(WprepList l)
 {
     __shared__ float tile[WT][WT + 1];
-    const WprepJob& j = l.job[blockIdx.y];
+    // the grid is the jobs' block ranges laid end to end: find this block's job
+    int ji = 0;
+    while (ji + 1 < l.count && (int)blockIdx.x >= l.start[ji + 1]) ++ji;
+    const WprepJob& j = l.job[ji];
+    const int bid = (int)blockIdx.x - l.start[ji], nblk = l.start[ji + 1] - l.start[ji];
     if (j.kind == 1) {
         const int64_t total = (int64_t)27 * j.pad * j.cout;
-        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+        for (int64_t e = (int64_t)bid * blockDim.x + threadIdx.x; e < total; e += (int64_t)nblk * blockDim.x)
             j.dst[e] = wk_dgrad_elem(j.src, j.f32, j.cin, j.cout, j.pad, e);
         return;
     }
     if (j.kind == 2) {            // c4: a permutation of taps, tiny (copad x 128)
         const int64_t total = (int64_t)j.pad * 128;
-        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
+        for (int64_t e = (int64_t)bid * blockDim.x + threadIdx.x; e < total; e += (int64_t)nblk * blockDim.x)
             j.dst[e] = wk_c4_elem(j.src, j.f32, j.cout, e);
         return;
     }
@@ -108,7 +112,7 @@ void wprep_multi_kernel(WprepList l)
     const int tr = (Rpad + WT - 1) / WT, tc = (Cpad + WT - 1) / WT;
     const int ntiles = nmat * tr * tc;
     const int lx = threadIdx.x % WT, ly = threadIdx.x / WT;     // 32 x 8
-    for (int tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    for (int tile_id = bid; tile_id < ntiles; tile_id += nblk) {
         const int m = tile_id / (tr * tc), rt = (tile_id / tc) % tr, ct = tile_id % tc;
         const int r0 = rt * WT, c0 = ct * WT;
         const int64_t sbase = (int64_t)m * R * C, dbase = (int64_t)m * Cpad * Rpad;
@@ -171,20 +175,26 @@ hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, ui
     return hipGetLastError();
 }
 
-hipError_t launch_wprep_multi(const WprepList& l, hipStream_t s)
+hipError_t launch_wprep_multi(const WprepList& l_in, hipStream_t s)
 {
-    if (l.count <= 0) return hipSuccess;
-    int64_t m = 1;
+    if (l_in.count <= 0) return hipSuccess;
+    // each job gets the blocks it needs (capped), laid end to end in one grid,
+    // instead of every job getting the largest job's count
+    WprepList l = l_in;
+    int total = 0;
     for (int i = 0; i < l.count; ++i) {
         const WprepJob& j = l.job[i];
         int64_t b;
         if (j.kind == 1) b = blocks_for((int64_t)27 * j.pad * j.cout);
         else if (j.kind == 0) b = (int64_t)27 * ((j.cin + WT - 1) / WT) * ((j.pad + WT - 1) / WT);
         else b = blocks_for((int64_t)j.pad * 128);
-        m = b > m ? b : m;
+        if (b < 1) b = 1;
+        if (b > 4096) b = 4096;
+        l.start[i] = total;
+        total += (int)b;
     }
-    if (m > 4096) m = 4096;
-    hipLaunchKernelGGL(wprep_multi_kernel, dim3((unsigned)m, (unsigned)l.count), dim3(256), 0, s, l);
+    l.start[l.count] = total;
+    hipLaunchKernelGGL(wprep_multi_kernel, dim3((unsigned)total), dim3(256), 0, s, l);
     return hipGetLastError();
 }
 
