@@ -92,6 +92,38 @@ void wprep_multi_kernel(WprepList l)
     while (ji + 1 < l.count && (int)blockIdx.x >= l.start[ji + 1]) ++ji;
     const WprepJob& j = l.job[ji];
     const int bid = (int)blockIdx.x - l.start[ji], nblk = l.start[ji + 1] - l.start[ji];
+    if (j.kind == 1 && j.cout % 8 == 0) {
+        // 8 consecutive output channels per thread: the tap flip keeps the
+        // channel order, so both sides are contiguous (16-byte-aligned
+        // sources; the same f2bf roundings as wk_dgrad_elem)
+        const uint32_t total8 = (uint32_t)(27 * j.pad * j.cout / 8);
+        const uint32_t c8 = (uint32_t)(j.cout / 8);
+        for (uint32_t e = (uint32_t)bid * blockDim.x + threadIdx.x; e < total8; e += (uint32_t)nblk * blockDim.x) {
+            const uint32_t co = (e % c8) * 8u, ci = (e / c8) % (uint32_t)j.pad, t = e / (c8 * (uint32_t)j.pad);
+            uint4 o = make_uint4(0u, 0u, 0u, 0u);
+            if (ci < (uint32_t)j.cin) {
+                const int64_t si = ((int64_t)(26 - t) * j.cin + ci) * j.cout + co;
+                float v[8];
+                if (j.f32) {
+                    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(j.src) + si);
+                    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(j.src) + si + 4);
+                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                } else {
+                    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(j.src) + si);
+                    const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        v[2 * k] = __uint_as_float(w4[k] << 16);
+                        v[2 * k + 1] = __uint_as_float(w4[k] & 0xffff0000u);
+                    }
+                }
+                o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7]));
+            }
+            reinterpret_cast<uint4*>(j.dst)[e] = o;
+        }
+        return;
+    }
     if (j.kind == 1) {
         const int64_t total = (int64_t)27 * j.pad * j.cout;
         for (int64_t e = (int64_t)bid * blockDim.x + threadIdx.x; e < total; e += (int64_t)nblk * blockDim.x)
@@ -185,7 +217,7 @@ hipError_t launch_wprep_multi(const WprepList& l_in, hipStream_t s)
     for (int i = 0; i < l.count; ++i) {
         const WprepJob& j = l.job[i];
         int64_t b;
-        if (j.kind == 1) b = blocks_for((int64_t)27 * j.pad * j.cout);
+        if (j.kind == 1) b = blocks_for((int64_t)27 * j.pad * j.cout / (j.cout % 8 == 0 ? 8 : 1));
         else if (j.kind == 0) b = (int64_t)27 * ((j.cin + WT - 1) / WT) * ((j.pad + WT - 1) / WT);
         else b = blocks_for((int64_t)j.pad * 128);
         if (b < 1) b = 1;
