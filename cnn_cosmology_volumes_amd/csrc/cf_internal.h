@@ -210,6 +210,7 @@ struct SgdList {
     float* w[16];
     const float* dw[16];
     int64_t n[16];
+    int start[17];      // first block of each tensor in the flattened grid (set by the launcher)
 };
 hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);

@@ -464,7 +464,8 @@ __global__ void sgd_kernel(float* __restrict__ W, const float* __restrict__ dW, 
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) W[i] = sgd_update(W[i], dW[i], lr);
 }
 
-// Several tensors in one launch: blockIdx.y picks the tensor.
+// Several tensors in one launch: the grid is the tensors' block ranges laid
+// end to end, and a block finds its tensor in the list's start table.
 // A thread updates SGD_E consecutive elements, issuing all of its loads
 // (16-byte when both tensors are 16-byte aligned) before any update, so one
 // memory latency is paid per thread instead of one per element.
@@ -472,13 +473,15 @@ constexpr int SGD_E = 4;
 __global__ __launch_bounds__(256)
 void sgd_multi_kernel(SgdList l, float lr)
 {
-    const int t = blockIdx.y;
+    int t = 0;
+    while (t + 1 < l.count && (int)blockIdx.x >= l.start[t + 1]) ++t;
+    const int bid = (int)blockIdx.x - l.start[t], nblk = l.start[t + 1] - l.start[t];
     float* __restrict__ W = l.w[t];
     const float* __restrict__ dW = l.dw[t];
     const int64_t n = l.n[t];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * SGD_E;
+    const int64_t stride = (int64_t)nblk * blockDim.x * SGD_E;
     const bool vec = (((uintptr_t)W | (uintptr_t)dW) & 15u) == 0;
-    for (int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * SGD_E; i0 < n; i0 += stride) {
+    for (int64_t i0 = ((int64_t)bid * blockDim.x + threadIdx.x) * SGD_E; i0 < n; i0 += stride) {
         if (vec && i0 + SGD_E <= n) {
             float4 w[SGD_E / 4], g[SGD_E / 4];
 #pragma unroll
@@ -587,14 +590,22 @@ hipError_t launch_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s)
+hipError_t launch_sgd_multi(const SgdList& l_in, float lr, hipStream_t s)
 {
-    if (l.count <= 0) return hipSuccess;
-    int64_t m = 1;
-    for (int t = 0; t < l.count; ++t) m = l.n[t] > m ? l.n[t] : m;
-    int64_t b = (m + 256 * SGD_E - 1) / (256 * SGD_E);
-    if (b > 2048) b = 2048;
-    hipLaunchKernelGGL(sgd_multi_kernel, dim3((unsigned)b, (unsigned)l.count), dim3(256), 0, s, l, lr);
+    if (l_in.count <= 0) return hipSuccess;
+    // each tensor gets the blocks it needs (capped), laid end to end in one
+    // grid, instead of every tensor getting the largest tensor's count
+    SgdList l = l_in;
+    int total = 0;
+    for (int t = 0; t < l.count; ++t) {
+        int64_t b = (l.n[t] + 256 * SGD_E - 1) / (256 * SGD_E);
+        if (b < 1) b = 1;
+        if (b > 2048) b = 2048;
+        l.start[t] = total;
+        total += (int)b;
+    }
+    l.start[l.count] = total;
+    hipLaunchKernelGGL(sgd_multi_kernel, dim3((unsigned)total), dim3(256), 0, s, l, lr);
     return hipGetLastError();
 }
 
