@@ -341,3 +341,39 @@ def test_fused_block_odd_dims_rejected():
     with pytest.raises(cf.CfError) as e:
         cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
     assert e.value.status == cf.CF_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------ weight-ring (kd-reuse) plans
+# 64-channel blocks on 4x4x16 tiles take the weight-ring kernel when a block
+# walks two or more 32-channel chunks.  That needs enough blocks to leave the
+# channel reduction unsplit (or split into multi-chunk pieces), so these
+# shapes are checked on sampled outputs with the oracle's point evaluators.
+RING_CASES = [
+    # fwd: 256 in-channel chunks split 4 ways (2 chunks each); bwd-data: 128
+    # in-channels, split 2 ways; ragged in every dimension
+    (2, 15, 14, 31, 256, 128),
+    # 512 blocks of a 64 -> 128 layer: unsplit, 2 chunks, pooled epilogue
+    (4, 16, 32, 32, 64, 128),
+]
+
+
+@pytest.mark.parametrize("shape", RING_CASES)
+def test_conv3d_ring_plans_sampled(shape):
+    from test_gpu_configs import check_conv_dgrad, check_conv_fwd
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 11)
+    x = act(rng, (N, D, H, W, Ci), BF)
+    w = weights(rng, Ci, Co, BF)
+    dz = act(rng, (N, D, H, W, Co), BF)
+    xd, wd, dzd = to_dev(x, BF), to_dev(w, BF), to_dev(dz, BF)
+    y = cf.cf_conv3d_fwd(xd, wd)
+    dx = cf.cf_conv3d_bwd_data(dzd, wd)
+    torch.cuda.synchronize()
+    check_conv_fwd(x, w, y, rng)
+    check_conv_dgrad(dz, w, dx, rng)
+    if D % 2 == 0 and H % 2 == 0 and W % 2 == 0:
+        # the pooled launch of the same plan equals conv then pool bit for bit
+        P, idx = cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+        P2, idx2 = cf.cf_pool3d_fwd(y, SLOPE)
+        torch.cuda.synchronize()
+        assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
