@@ -78,19 +78,30 @@ cf_status check_conv(cf_dtype dt, const cf_dims& x, int32_t cout, const cf_conv&
 enum class Fwd { Mfma, C4, Direct };
 enum class Wg { Mfma, C4, Direct };
 
-Fwd fwd_path(cf_dtype dt, int64_t cin, int cout)
+// The MFMA conv kernels address a tile's six input planes (of `cin`
+// channels) and the weight copy with 32-bit byte offsets; a shape beyond
+// that takes the direct kernel.
+bool mfma_offsets_fit(const cf_dims& x, int64_t cin, int64_t cout)
 {
+    const int64_t lim = (int64_t)1 << 31;
+    return 6 * x.h * x.w * cin * 2 < lim && 27 * roundup((int)cout, 128) * cin * 2 < lim;
+}
+
+Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
+{
+    const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 4 == 0) {
-        if (cin % 32 == 0) return Fwd::Mfma;
+        if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
         if (cin == 4) return Fwd::C4;
     }
     return Fwd::Direct;
 }
 
 // backward-data runs the forward kernels with in = cout, out = cin
-Fwd dgrad_path(cf_dtype dt, int64_t cin, int cout)
+Fwd dgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
-    if (dt == CF_BF16 && cout % 32 == 0 && cin % 4 == 0) return Fwd::Mfma;
+    const int64_t cin = x.c;
+    if (dt == CF_BF16 && cout % 32 == 0 && cin % 4 == 0 && mfma_offsets_fit(x, cout, cin)) return Fwd::Mfma;
     return Fwd::Direct;
 }
 
@@ -111,7 +122,7 @@ bool fused_pool_fwd_c4(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF1
 // path wherever its plan has 4x4x16 tiles and no channel split.
 bool fused_pool_fwd_mfma(cf_dtype dt, const cf_dims& x, int cout)
 {
-    return fwd_path(dt, x.c, cout) == Fwd::Mfma && conv_mfma_can_pool(plan_conv_mfma(x, cout), x);
+    return fwd_path(dt, x, cout) == Fwd::Mfma && conv_mfma_can_pool(plan_conv_mfma(x, cout), x);
 }
 bool fused_pool_fwd(cf_dtype dt, const cf_dims& x, int cout)
 {
@@ -241,18 +252,18 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
     if (check_conv(dtype, x, cout, conv) != CF_OK) return 0;
     switch (pass) {
     case CF_CONV_FWD: {
-        const Fwd p = fwd_path(dtype, x.c, cout);
+        const Fwd p = fwd_path(dtype, x, cout);
         return up256(fwd_wk_bytes(p, x.c, cout)) + up256(fwd_part_bytes(p, x, cout));
     }
     case CF_CONV_BWD_DATA: {
-        const Fwd p = dgrad_path(dtype, x.c, cout);
+        const Fwd p = dgrad_path(dtype, x, cout);
         return up256(dgrad_wk_bytes(p, dtype, x.c, cout)) + up256(dgrad_part_bytes(p, x, cout));
     }
     case CF_CONV_BWD_WEIGHT:
         return up256(wgrad_part_bytes(wgrad_path(dtype, x, cout), dtype, x, cout));
     case CF_CONV_POOL_FWD: {
         if ((x.d & 1) || (x.h & 1) || (x.w & 1)) return 0;
-        const Fwd p = fwd_path(dtype, x.c, cout);
+        const Fwd p = fwd_path(dtype, x, cout);
         const size_t z = fused_pool_fwd(dtype, x, cout) ? 0 : (size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype);
         return up256(fwd_wk_bytes(p, x.c, cout)) + up256(fwd_part_bytes(p, x, cout)) + up256(z);
     }
@@ -277,7 +288,7 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
     if (!al16(X) || !al16(W) || !al16(P) || !al16(idx))
         return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: pointers must be 16-byte aligned");
     if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: slope is NaN");
-    const Fwd p = fwd_path(dtype, x.c, cout);
+    const Fwd p = fwd_path(dtype, x, cout);
     const bool fused = fused_pool_fwd(dtype, x, cout);
     const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout)), pb = up256(fwd_part_bytes(p, x, cout));
     const size_t zb = fused ? 0 : up256((size_t)(x.n * x.d * x.h * x.w) * cout * esize(dtype));
@@ -353,7 +364,7 @@ cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W,
     if (st != CF_OK) return st;
     if (!X || !W || !Y) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: null tensor pointer");
     if (!al16(X) || !al16(W) || !al16(Y)) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: pointers must be 16-byte aligned");
-    const Fwd p = fwd_path(dtype, x.c, cout);
+    const Fwd p = fwd_path(dtype, x, cout);
     const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout));
     const size_t need = wkb + up256(fwd_part_bytes(p, x, cout));
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_fwd: workspace %zu < %zu bytes", ws_bytes, need);
@@ -375,7 +386,7 @@ cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const vo
     if (st != CF_OK) return st;
     if (!dY || !W || !dX) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: null tensor pointer");
     if (!al16(dY) || !al16(W) || !al16(dX)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: pointers must be 16-byte aligned");
-    const Fwd p = dgrad_path(dtype, x.c, cout);
+    const Fwd p = dgrad_path(dtype, x, cout);
     const size_t wkb = up256(dgrad_wk_bytes(p, dtype, x.c, cout));
     const size_t need = wkb + up256(dgrad_part_bytes(p, x, cout));
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_bwd_data: workspace %zu < %zu bytes", ws_bytes, need);
@@ -576,8 +587,8 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         LayerPlan& Lp = P.layer[l];
         Lp.x = x;
         Lp.cout = m->filters[l];
-        Lp.fwd = fwd_path(dt, x.c, Lp.cout);
-        Lp.dg = dgrad_path(dt, x.c, Lp.cout);
+        Lp.fwd = fwd_path(dt, x, Lp.cout);
+        Lp.dg = dgrad_path(dt, x, Lp.cout);
         Lp.wg = wgrad_path(dt, x, Lp.cout);
         const int64_t nvox = x.n * x.d * x.h * x.w;
         const int64_t npool = nvox / 8;
