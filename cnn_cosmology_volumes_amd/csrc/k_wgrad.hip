@@ -63,8 +63,9 @@ constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                 // 256 voxels per b
 constexpr int GW_NOCT = GW_VB / 8;                          // 32 w-octets
 constexpr int GW_HH = GW_TH + 2;
 constexpr int GW_NR = (GW_TD + 2) * GW_HH;                  // 36 halo rows
-constexpr int GW_XW = 24;                                   // bf16 per XT row (18 used)
-constexpr int GW_XPL = GW_NR * GW_XW + 16;                  // per-channel plane: 1760 B (odd multiple of 32)
+constexpr int GW_XW = 16;                                   // bf16 per XT row: halo w 0-15
+constexpr int GW_XE = GW_NR * GW_XW;                        // halo w 16-17 of the rows, one bf16 pair each
+constexpr int GW_XPL = GW_XE + 2 * GW_NR + 16;              // per-channel plane: 1328 B (odd multiple of 16)
 constexpr int GW_DROW = GW_VB + 16;                         // dYT row: 544 B (odd multiple of 32)
 constexpr int GW_NXB = GW_NR * 2 * 4;                       // X blocks of 8 voxels: rows x {w 0-7, 8-15} x 4 ci-groups
 constexpr int GW_NXE = GW_NR * 4;                           // X edge blocks (w 16-17): rows x 4 ci-groups
@@ -151,8 +152,14 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                        int bD, int bH, int bW, int nco, int nci, int64_t nbox, int boxes_per_split)
 {
     using G = GwCfg<BO>;
-    __shared__ __attribute__((aligned(16))) uint16_t xt[32 * GW_XPL];
-    __shared__ __attribute__((aligned(16))) uint16_t dt[BO * GW_DROW];
+    // Two buffers of each tile: a box is staged into one while the waves
+    // still compute the previous box from the other, so a box costs one
+    // barrier (after its staging) instead of two.  Halo w 16-17 of the X
+    // rows sit together after the rows of their channel plane (one bf16
+    // pair per row), which keeps the rows 16 wide and both buffers within
+    // the LDS.
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * GW_XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * GW_DROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -236,7 +243,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
             }
         }
     };
-    auto store_box = [&]() {
+    auto store_box = [&](int buf) {
         const int tid_ = opaque_tid();
 #pragma unroll
         for (int k = 0; k < G::KB; ++k) {
@@ -251,14 +258,14 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                 const int slot = (oct & 1) * (GW_NOCT / 2) + (oct >> 1);
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint4*>(&dt[(grp * 8 + c) * GW_DROW + slot * 8]) = tr[c];
+                    *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * GW_DROW + slot * 8]) = tr[c];
             } else {
                 const int x = t - G::NDB;
                 const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
                 const int row = rem / 2, slot = rem % 2;
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint4*>(&xt[(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8]) = tr[c];
+                    *reinterpret_cast<uint4*>(&xt[buf][(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8]) = tr[c];
             }
         }
         if (tid_ < GW_NXE) {
@@ -269,7 +276,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                 const int h = c >> 1;
                 const uint32_t w0v = h == 0 ? ue[0].x : h == 1 ? ue[0].y : h == 2 ? ue[0].z : ue[0].w;
                 const uint32_t w1v = h == 0 ? ue[1].x : h == 1 ? ue[1].y : h == 2 ? ue[1].z : ue[1].w;
-                *reinterpret_cast<uint32_t*>(&xt[(egrp * 8 + c) * GW_XPL + erow * GW_XW + 16]) =
+                *reinterpret_cast<uint32_t*>(&xt[buf][(egrp * 8 + c) * GW_XPL + GW_XE + 2 * erow]) =
                     __builtin_amdgcn_perm(w1v, w0v, sel);
             }
         }
@@ -287,11 +294,16 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
     BoxPos bp = box_decode(b_begin, bD, bH, bW);
     load_box(bp);
-    store_box();
+    store_box(0);
     __syncthreads();
-    const uint16_t* drow = dt + (32 * cp + l16) * GW_DROW;
-    const uint16_t* xpl = xt + (16 * jf + l16) * GW_XPL + kd * GW_HH * GW_XW;
+    // lane bases in buffer 0; the buffer offset is wave-uniform (scalar)
+    const uint16_t* drow0 = dt[0] + (32 * cp + l16) * GW_DROW;
+    const uint16_t* xpl0 = xt[0] + (16 * jf + l16) * GW_XPL + kd * GW_HH * GW_XW;
+    int buf = 0;
     for (int64_t box = b_begin; box < b_end; ++box) {
+        const int sb = __builtin_amdgcn_readfirstlane(buf);
+        const uint16_t* drow = drow0 + sb * (BO * GW_DROW);
+        const uint16_t* xpl = xpl0 + sb * (32 * GW_XPL);
         const bool more = box + 1 < b_end;
         if (more) {
             bp = box_next(bp, bD, bH, bW);
@@ -308,12 +320,15 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                 for (int h = 0; h < 2; ++h)
                     a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (h * (GW_NOCT / 2) + row) * 8);
             const uint16_t* xr = xpl + (s2 * GW_HH + lg) * GW_XW;
+            // this lane's edge pairs: row (kd + s2) * GW_HH + lg + kh of its plane
+            const uint32_t* er = reinterpret_cast<const uint32_t*>(xpl - kd * GW_HH * GW_XW + GW_XE) +
+                                 (kd + s2) * GW_HH + lg;
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh) {
                 const uint16_t* xp = xr + kh * GW_XW;
                 uint4 q0 = *reinterpret_cast<const uint4*>(xp);
                 uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
-                uint32_t e1 = *reinterpret_cast<const uint32_t*>(xp + 16);         // halo w 16-17
+                uint32_t e1 = er[kh];                                              // halo w 16-17
                 // opaque to the optimizer, which would otherwise re-read the
                 // kw = 2 operands (unaligned) from LDS as extra 4-byte reads
                 asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(q1.x), "+v"(q1.y),
@@ -341,10 +356,12 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                             acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[h][kw], acc[c][kh][kw], 0, 0, 0);
             }
         }
+        // the next box goes into the other buffer (read last in the box
+        // before this one, behind the barrier that ended it)
         if (more) {
+            store_box(buf ^ 1);
             __syncthreads();
-            store_box();
-            __syncthreads();
+            buf ^= 1;
         }
     }
 
