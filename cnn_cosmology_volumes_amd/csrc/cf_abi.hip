@@ -87,12 +87,15 @@ bool mfma_offsets_fit(const cf_dims& x, int64_t cin, int64_t cout)
     return 6 * x.h * x.w * cin * 2 < lim && 27 * roundup((int)cout, 128) * cin * 2 < lim;
 }
 
+// The Cin = 4 forward addresses a sample with 32-bit byte offsets.
+bool c4_offsets_fit(const cf_dims& x) { return x.d * x.h * x.w * 8 < ((int64_t)1 << 31); }
+
 Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 4 == 0) {
         if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
-        if (cin == 4) return Fwd::C4;
+        if (cin == 4 && c4_offsets_fit(x)) return Fwd::C4;
     }
     return Fwd::Direct;
 }
@@ -117,7 +120,10 @@ Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 size_t esize(cf_dtype dt) { return dt == CF_F32 ? 4 : 2; }
 
 // Fused block kernels exist for the 4-channel first layer in bf16.
-bool fused_pool_fwd_c4(cf_dtype dt, int64_t cin, int cout) { return dt == CF_BF16 && cin == 4 && cout % 32 == 0; }
+bool fused_pool_fwd_c4(cf_dtype dt, const cf_dims& x, int cout)
+{
+    return dt == CF_BF16 && x.c == 4 && cout % 32 == 0 && c4_offsets_fit(x);
+}
 // The conv + pool forward runs as one launch for Cin = 4, and for the MFMA
 // path wherever its plan has 4x4x16 tiles and no channel split.
 bool fused_pool_fwd_mfma(cf_dtype dt, const cf_dims& x, int cout)
@@ -126,7 +132,7 @@ bool fused_pool_fwd_mfma(cf_dtype dt, const cf_dims& x, int cout)
 }
 bool fused_pool_fwd(cf_dtype dt, const cf_dims& x, int cout)
 {
-    return fused_pool_fwd_c4(dt, x.c, cout) || fused_pool_fwd_mfma(dt, x, cout);
+    return fused_pool_fwd_c4(dt, x, cout) || fused_pool_fwd_mfma(dt, x, cout);
 }
 bool fused_pool_wgrad(cf_dtype dt, const cf_dims& x, int cout) { return wgrad_path(dt, x, cout) == Wg::C4; }
 
@@ -594,7 +600,7 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
         const int64_t npool = nvox / 8;
         Lp.wk_fwd = take(Lp.fwd == Fwd::Direct ? 0 : fwd_wk_bytes(Lp.fwd, x.c, Lp.cout));
         Lp.wk_dg = take(l > 0 ? dgrad_wk_bytes(Lp.dg, dt, x.c, Lp.cout) : 0);
-        Lp.fused = l == 0 && fused_pool_fwd_c4(dt, x.c, Lp.cout) && fused_pool_wgrad(dt, x, Lp.cout);
+        Lp.fused = l == 0 && fused_pool_fwd_c4(dt, x, Lp.cout) && fused_pool_wgrad(dt, x, Lp.cout);
         Lp.pool_fused = !Lp.fused && fused_pool_fwd_mfma(dt, x, Lp.cout);
         Lp.z = take(Lp.fused ? 0 : (size_t)nvox * Lp.cout * es);
         Lp.p = take((size_t)npool * Lp.cout * es);

@@ -63,26 +63,33 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         for (int i = 0; i < MI; ++i)
             afr[s][i] = *reinterpret_cast<const bf16x8*>(Wk + (int64_t)(co_base + 16 * i + l16) * 128 + 32 * s + 8 * lg);
 
-    // Halo staging: every global load of this thread is issued before its
-    // LDS stores, so the load latencies overlap.
+    // Halo staging: a thread owns one halo column w and every RS-th halo
+    // row (d, h) from its first, so the column's bounds and offset are
+    // computed once; the loads are raw buffer loads at 32-bit byte offsets
+    // from the sample (the host keeps a sample below 2^31 bytes), and a voxel
+    // outside the volume gets an offset beyond the buffer, which reads zeros.
+    // Every global load of this thread is issued before its LDS stores, so
+    // the load latencies overlap.
     {
-        constexpr int IT = (HV + NT - 1) / NT;
-        const uint16_t* xs = X + (int64_t)n * D * plane * 4;
+        constexpr int NR = HD * HH, RS = NT / HW, IT = (NR + RS - 1) / RS;
+        const int cw = threadIdx.x % HW, rr = threadIdx.x / HW;
+        const int gw = w0 + cw - 1;
+        const bool col_ok = rr < RS && (unsigned)gw < (unsigned)W;
+        const auto rx = buf_rsrc(X + (int64_t)n * D * plane * 4, (uint32_t)((int64_t)D * plane * 8));
         uint2 v[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int hv = threadIdx.x + it * NT;
-            const int hw_ = hv % HW, hh_ = (hv / HW) % HH, hd_ = hv / (HW * HH);
-            const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-            v[it] = make_uint2(0u, 0u);
-            if ((HV % NT == 0 || hv < HV) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
-                (unsigned)gw < (unsigned)W)
-                v[it] = *reinterpret_cast<const uint2*>(xs + ((int64_t)(gd * H + gh) * W + gw) * 4);
+            const int r = rr + it * RS;
+            const int gd = d0 + r / HH - 1, gh = h0 + r % HH - 1;
+            uint32_t off = (((uint32_t)gd * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) * 8u;
+            off = (col_ok && r < NR && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) ? off : 0x80000000u;
+            asm volatile("" : "+v"(off));     // a select, not a branch around the load
+            v[it] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0));
         }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int hv = threadIdx.x + it * NT;
-            if (HV % NT == 0 || hv < HV) halo[hv] = v[it];
+            const int r = rr + it * RS;
+            if (rr < RS && r < NR) halo[r * HW + cw] = v[it];
         }
         if (threadIdx.x == 0) halo[HV] = make_uint2(0u, 0u);
     }
@@ -201,6 +208,7 @@ hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y
                               int copad, hipStream_t s)
 {
     (void)copad;
+    if (x.d * x.h * x.w * 8 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit sample offsets
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
     if (cout <= 16) {
@@ -216,6 +224,7 @@ hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y
 hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx, float slope,
                                    const cf_dims& x, int cout, hipStream_t s)
 {
+    if (x.d * x.h * x.w * 8 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit sample offsets
     const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
     const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
     hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, true>), dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s, X,
