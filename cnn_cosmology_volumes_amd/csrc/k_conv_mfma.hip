@@ -344,7 +344,7 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     static_assert(TW * RPF == 16 && T::NJ % TD == 0 && T::NWV * RPW == TH, "kd-reuse fragment layout");
     __shared__ __attribute__((aligned(16))) uint16_t halo[T::HV * LS];
     __shared__ __attribute__((aligned(16))) uint16_t aring[6 * BM * AS];
-    static_assert(BM * 4 <= T::NT && AS >= 32 && AS % 8 == 0, "weight ring");
+    static_assert(AS >= 32 && AS % 8 == 0, "weight ring");
 
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) % T::NWM;
@@ -377,8 +377,11 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 
     const int64_t plane = (int64_t)H * W;
     const int64_t tap_stride = (int64_t)CoutPad * Cin;
-    const bool ald = threadIdx.x < BM * 4;       // the ring's loader threads
-    const int arow = threadIdx.x >> 2, aq = threadIdx.x & 3;
+    // Ring pieces: a step's three weight tiles are 3 * BM * 4 16-byte pieces,
+    // spread over all threads (piece threadIdx.x + k * NT, k < PPT), so that
+    // every wave takes a share of the ring stores before each step's barrier.
+    constexpr int NPC = 3 * BM * 4, PPT = (NPC + T::NT - 1) / T::NT;
+    uint32_t pl[PPT];                            // LDS offset of each piece in a group (bf16 units)
     // Every global load of this kernel is a raw buffer load at a 32-bit byte
     // offset computed once for all channel chunks; a piece outside the volume
     // (or a thread that loads nothing) gets an offset beyond the buffer, which
@@ -409,14 +412,25 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     }
     const uint32_t wbytes = (uint32_t)(27 * tap_stride * 2);
     const uint16_t* wbase = Wk + (int64_t)blockIdx.y * BM * Cin;
-    const uint32_t aoffb = pick(ald, ((uint32_t)arow * (uint32_t)Cin + (uint32_t)aq * 8u) * 2u);
-    auto wload = [&](int c, int tap) {
+    // global byte offset of each piece: its row and quarter, plus its tap
+    // (kd * 9) in the weight copy; the step's tap (kh, kw) goes in the scalar offset
+    uint32_t pg[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int pc = threadIdx.x + k * T::NT;
+        const int kd = pc / (BM * 4), row = (pc >> 2) % BM, q = pc & 3;
+        pl[k] = (uint32_t)(kd * BM * AS + row * AS + q * 8);
+        pg[k] = pick(pc < NPC, ((uint32_t)row * (uint32_t)Cin + (uint32_t)q * 8u) * 2u +
+                                   (uint32_t)(kd * 9) * (uint32_t)(tap_stride * 2));
+    }
+    auto wload = [&](int c, int k, int step) {
         const auto rw = buf_rsrc(wbase + c * 32, wbytes - (uint32_t)(blockIdx.y * BM * Cin + c * 32) * 2u);
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, aoffb, (int)(tap * tap_stride * 2), 0));
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, pg[k], (int)(step * tap_stride * 2), 0));
     };
+    auto pvalid = [&](int k) { return T::NT * (k + 1) <= NPC || (int)threadIdx.x + k * T::NT < NPC; };
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
-        uint4 ra[3];
+        uint4 ra[PPT];
         {
             const auto rx = buf_rsrc(xbase + c * 32, xbytes - (uint32_t)c * 64u);
             uint4 val[T::IT];
@@ -425,11 +439,11 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
                 val[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, hoff[it], 0, 0));
             // weight ring prologue: step 0's tiles go to group 0 with the
             // halo, step 1's are held in registers until step 0 stores them
-            uint4 w0v[3];
+            uint4 w0v[PPT];
 #pragma unroll
-            for (int kd = 0; kd < 3; ++kd) {
-                w0v[kd] = wload(c, 9 * kd);
-                ra[kd] = wload(c, 9 * kd + 1);
+            for (int k = 0; k < PPT; ++k) {
+                w0v[k] = wload(c, k, 0);
+                ra[k] = wload(c, k, 1);
             }
 #pragma unroll
             for (int it = 0; it < T::IT; ++it) {
@@ -437,11 +451,9 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
                 if (T::NE % T::NT == 0 || e < T::NE)
                     *reinterpret_cast<uint4*>(halo + (e >> 2) * LS + halo_chunk(e & 3, (e >> 2) % T::HW) * 8) = val[it];
             }
-            if (ald) {
 #pragma unroll
-                for (int kd = 0; kd < 3; ++kd)
-                    *reinterpret_cast<uint4*>(aring + kd * BM * AS + arow * AS + aq * 8) = w0v[kd];
-            }
+            for (int k = 0; k < PPT; ++k)
+                if (pvalid(k)) *reinterpret_cast<uint4*>(aring + pl[k]) = w0v[k];
         }
         __syncthreads();
 
@@ -453,9 +465,9 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
         for (int s = 0; s < 9; ++s) {
             const int kh = s / 3, kw = s % 3;
             // ring loads two steps ahead, then this step's operands
-            uint4 rn[3];
+            uint4 rn[PPT];
 #pragma unroll
-            for (int kd = 0; kd < 3; ++kd) rn[kd] = s + 2 < 9 ? wload(c, 9 * kd + s + 2) : make_uint4(0u, 0u, 0u, 0u);
+            for (int k = 0; k < PPT; ++k) rn[k] = s + 2 < 9 ? wload(c, k, s + 2) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int kd = 0; kd < 3; ++kd)
 #pragma unroll
@@ -478,13 +490,13 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             __builtin_amdgcn_sched_barrier(0);
             // the next step's tiles into the other group (last read in the
             // step before this one, behind its barrier)
-            if (ald && s + 1 < 9) {
+            if (s + 1 < 9) {
 #pragma unroll
-                for (int kd = 0; kd < 3; ++kd)
-                    *reinterpret_cast<uint4*>(aring + (((s + 1) & 1) * 3 + kd) * BM * AS + arow * AS + aq * 8) = ra[kd];
+                for (int k = 0; k < PPT; ++k)
+                    if (pvalid(k)) *reinterpret_cast<uint4*>(aring + ((s + 1) & 1) * 3 * BM * AS + pl[k]) = ra[k];
             }
 #pragma unroll
-            for (int kd = 0; kd < 3; ++kd) ra[kd] = rn[kd];
+            for (int k = 0; k < PPT; ++k) ra[k] = rn[k];
             if (s + 1 < 9) lds_barrier();
         }
     }
