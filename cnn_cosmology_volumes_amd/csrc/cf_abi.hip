@@ -829,7 +829,21 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     // 5. conv blocks backward: pool backward -> data gradient on the caller's
     //    stream; each block's weight gradient (with its split reduction) on
     //    the auxiliary stream once its conv-output gradient exists, so it
-    //    overlaps the rest of the backward chain.  The streams join before SGD.
+    //    overlaps the rest of the backward chain.
+    // 6. SGD.  The fp32 masters are read only by the weight copies, the
+    //    forward and the dense backward, all enqueued on the caller's stream
+    //    before the first fork, so the masters whose gradients the auxiliary
+    //    stream holds (the dense head's, and those of the blocks whose weight
+    //    gradient runs there) are updated there in one launch, overlapping the
+    //    end of the backward chain; the rest are updated after the join.
+    static_assert(CF_MAX_BLOCKS + 6 <= 16, "SgdList capacity");
+    SgdList sl_aux{}, sl_main{};
+    auto add = [](SgdList& sl, float* wp, const float* g, int64_t n) {
+        sl.w[sl.count] = wp;
+        sl.dw[sl.count] = g;
+        sl.n[sl.count] = n;
+        ++sl.count;
+    };
     {
         float* part_w = F(P.part_w);
         bool forked = false;
@@ -866,6 +880,17 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                                           stream),
                                 "conv3d backward-data");
         }
+        SgdList& dense_sl = forked ? sl_aux : sl_main;
+        add(dense_sl, params[L], F(P.dW1), (int64_t)P.flat * P.d0);
+        add(dense_sl, params[L + 1], F(P.db1), P.d0);
+        add(dense_sl, params[L + 2], F(P.dW2), (int64_t)P.d0 * P.d1);
+        add(dense_sl, params[L + 3], F(P.db2), P.d1);
+        add(dense_sl, params[L + 4], F(P.dW3), (int64_t)P.d1 * P.d2);
+        add(dense_sl, params[L + 5], F(P.db3), P.d2);
+        for (int l = 0; l < L; ++l)    // a fused block's weight gradient is made on the caller's stream
+            add(forked && !P.layer[l].fused ? sl_aux : sl_main, params[l], F(P.layer[l].dw),
+                (int64_t)27 * P.layer[l].x.c * P.layer[l].cout);
+        if (forked && bst == CF_OK) bst = check_hip(launch_sgd_multi(sl_aux, lr, ax.s), "sgd");
         if (forked) {
             // join even after an error, so no work of this call outlives it on the auxiliary stream
             const cf_status j1 = check_hip(hipEventRecord(ax.ev[CF_MAX_BLOCKS], ax.s), "join event");
@@ -876,23 +901,7 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         if (bst != CF_OK) return bst;
     }
 
-    // 6. SGD on every master parameter (one launch for all tensors)
-    static_assert(CF_MAX_BLOCKS + 6 <= 16, "SgdList capacity");
-    SgdList sl{};
-    auto add = [&](float* wp, const float* g, int64_t n) {
-        sl.w[sl.count] = wp;
-        sl.dw[sl.count] = g;
-        sl.n[sl.count] = n;
-        ++sl.count;
-    };
-    for (int l = 0; l < L; ++l) add(params[l], F(P.layer[l].dw), (int64_t)27 * P.layer[l].x.c * P.layer[l].cout);
-    add(params[L], F(P.dW1), (int64_t)P.flat * P.d0);
-    add(params[L + 1], F(P.db1), P.d0);
-    add(params[L + 2], F(P.dW2), (int64_t)P.d0 * P.d1);
-    add(params[L + 3], F(P.db2), P.d1);
-    add(params[L + 4], F(P.dW3), (int64_t)P.d1 * P.d2);
-    add(params[L + 5], F(P.db3), P.d2);
-    CF_TRY_HIP(launch_sgd_multi(sl, lr, stream), "sgd");
+    CF_TRY_HIP(launch_sgd_multi(sl_main, lr, stream), "sgd");
     return CF_OK;
 }
 
