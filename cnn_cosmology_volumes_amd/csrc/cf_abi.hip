@@ -847,6 +847,7 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     {
         float* part_w = F(P.part_w);
         bool forked = false;
+        int deferred = -1;    // a block whose weight gradient waits for the next fork
         cf_status bst = CF_OK;
         for (int l = L - 1; l >= 0 && bst == CF_OK; --l) {
             const LayerPlan& Lp = P.layer[l];
@@ -866,15 +867,30 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                               : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
                                                        (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
             if ((bst = check_hip(e, "pool backward")) != CF_OK) break;
-            // fork: the weight gradient reads dz and the block input, which
-            // nothing on the caller's stream writes until the join
-            if ((bst = check_hip(hipEventRecord(ax.ev[l], stream), "fork event")) != CF_OK) break;
-            if ((bst = check_hip(hipStreamWaitEvent(ax.s, ax.ev[l], 0), "fork wait")) != CF_OK) break;
-            forked = true;
-            const void* xin = l == 0 ? X : (const void*)(w + P.layer[l - 1].p);
-            if ((bst = check_hip(run_wgrad(Lp.wg, dtype, Lp.x, xin, dz, Lp.cout, F(Lp.dw), part_w, ax.s),
-                                 "conv3d backward-weight")) != CF_OK)
-                break;
+            // The deepest block's weight gradient is the smallest, and the
+            // auxiliary stream has nothing else to do yet: it waits for the
+            // next block's fork (block l - 1 >= 1, never fused, so it forks),
+            // which saves one fork on the caller's stream.  Its dz and input
+            // are not written before the join.
+            if (l == L - 1 && l >= 2) {
+                deferred = l;
+            } else {
+                // fork: the weight gradients read dz and the block inputs,
+                // which nothing on the caller's stream writes until the join
+                if ((bst = check_hip(hipEventRecord(ax.ev[l], stream), "fork event")) != CF_OK) break;
+                if ((bst = check_hip(hipStreamWaitEvent(ax.s, ax.ev[l], 0), "fork wait")) != CF_OK) break;
+                forked = true;
+                for (const int q : {deferred, l}) {
+                    if (q < 0) continue;
+                    const LayerPlan& Lq = P.layer[q];
+                    const void* xin = q == 0 ? X : (const void*)(w + P.layer[q - 1].p);
+                    if ((bst = check_hip(run_wgrad(Lq.wg, dtype, Lq.x, xin, w + Lq.z, Lq.cout, F(Lq.dw), part_w, ax.s),
+                                         "conv3d backward-weight")) != CF_OK)
+                        break;
+                }
+                deferred = -1;
+                if (bst != CF_OK) break;
+            }
             if (l > 0)
                 bst = check_hip(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + P.layer[l - 1].dp, part,
                                           stream),
