@@ -124,8 +124,9 @@ bool fused_pool_fwd_c4(cf_dtype dt, const cf_dims& x, int cout)
 {
     return dt == CF_BF16 && x.c == 4 && cout % 32 == 0 && c4_offsets_fit(x);
 }
-// The conv + pool forward runs as one launch for Cin = 4, and for the MFMA
-// path wherever its plan has 4x4x16 tiles and no channel split.
+// The conv + pool forward is fused for Cin = 4 (one launch), and on the
+// MFMA path for plans with 4x4x16 tiles and no channel split (one launch) or
+// with a channel split (the partials' reduction pools).
 bool fused_pool_fwd_mfma(cf_dtype dt, const cf_dims& x, int cout)
 {
     return fwd_path(dt, x, cout) == Fwd::Mfma && conv_mfma_can_pool(plan_conv_mfma(x, cout), x);
@@ -310,7 +311,8 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
     if (fused) {
         if (p == Fwd::Mfma)
             CF_TRY_HIP(launch_conv_mfma_pool(plan_conv_mfma(x, cout), (const uint16_t*)X, (const uint16_t*)wk,
-                                             (uint16_t*)P, idx, slope, x, cout, roundup(cout, 128), stream),
+                                             (uint16_t*)P, idx, slope, x, cout, roundup(cout, 128),
+                                             pb ? (float*)(w8 + wkb) : nullptr, stream),
                        "fused conv3d + pool forward");
         else
             CF_TRY_HIP(launch_conv_c4_pool_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)P, idx, slope, x,
@@ -772,7 +774,7 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         if (Lp.pool_fused) {
             CF_TRY_HIP(launch_conv_mfma_pool(plan_conv_mfma(Lp.x, Lp.cout), (const uint16_t*)a, (const uint16_t*)wk,
                                              (uint16_t*)(w + Lp.p), (uint8_t*)(w + Lp.idx), slope, Lp.x, Lp.cout,
-                                             roundup(Lp.cout, 128), stream),
+                                             roundup(Lp.cout, 128), part, stream),
                        "fused conv3d + pool forward");
             a = w + Lp.p;
             continue;

@@ -128,11 +128,13 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout);
 hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y,
                             float* part, const cf_dims& x, int cout, int coutpad, hipStream_t s);
 
-// Conv + leaky ReLU + 2^3 max pool in one launch (P and idx only, no Z), for
-// plans with 4x4x16 tiles and no split (d, h, w even).
+// Conv + leaky ReLU + 2^3 max pool writing P and idx only (no Z), for plans
+// with 4x4x16 tiles and no split (one launch, pooled in the conv epilogue)
+// and for split plans (the partials' reduction pools; part as for
+// launch_conv_mfma); d, h, w even.
 bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x);
 hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx,
-                                 float slope, const cf_dims& x, int cout, int coutpad, hipStream_t s);
+                                 float slope, const cf_dims& x, int cout, int coutpad, float* part, hipStream_t s);
 
 // Layer-1 forward (Cin == 4) on MFMA, K = 27*4 padded to 128.
 hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, const cf_dims& x,

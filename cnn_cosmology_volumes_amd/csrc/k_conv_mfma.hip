@@ -586,6 +586,87 @@ __global__ void split_reduce_bf16(const float* __restrict__ part, uint16_t* __re
     }
 }
 
+// The split partials summed and rounded as by split_reduce_bf16, then the
+// leaky-ReLU + 2^3 max-pool of those bf16 values with the pool forward's rule
+// (fp32 comparison, first strict maximum in window order, leaky ReLU on the
+// maximum), so P and idx equal split_reduce_bf16 followed by the pool
+// forward bit for bit, and the full-resolution conv output is never stored.
+// Eight consecutive lanes take one (pooled voxel, 4 channels) item, lane q
+// summing window position q = a*4 + b*2 + c.  The eight (value, position)
+// pairs are combined in three butterfly steps, the right (later) pair taken
+// only when it is valid and compares strictly greater (or the left one is
+// not valid); position 0 is always valid, any other position only when it
+// is not NaN.  That gives what the sequential scan gives: position 0's NaN
+// if it is one, else the first occurrence of the maximum of the non-NaN
+// values (a NaN after position 0 is never taken, ties keep the earlier one).
+// D, H, W even, C % 4 == 0.
+__global__ __launch_bounds__(256)
+void split_reduce_pool_bf16(const float* __restrict__ part, uint16_t* __restrict__ P, uint8_t* __restrict__ idx,
+                            int N, int D, int H, int W, int C, int splits, float slope)
+{
+    const int Dp = D / 2, Hp = H / 2, Wp = W / 2, cg = C / 4;
+    const int64_t total = (int64_t)N * Dp * Hp * Wp * cg;
+    const int64_t n4 = (int64_t)N * D * H * W * cg;   // float4 per split
+    const float4* __restrict__ p4 = reinterpret_cast<const float4*>(part);
+    const int q = threadIdx.x & 7;
+    const int a = q >> 2, b = (q >> 1) & 1, c = q & 1;
+    const int per_block = blockDim.x / 8;
+    const int64_t stride = (int64_t)gridDim.x * per_block;
+    // the trip count is the same for every lane of a block, so all lanes
+    // reach the shuffles; an item's eight lanes are all in or all out
+    for (int64_t e0 = (int64_t)blockIdx.x * per_block; e0 < total; e0 += stride) {
+        const int64_t e = e0 + (threadIdx.x >> 3);
+        const bool ok = e < total;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            const int g = (int)(e % cg);
+            int64_t r = e / cg;
+            const int k = (int)(r % Wp); r /= Wp;
+            const int j = (int)(r % Hp); r /= Hp;
+            const int i = (int)(r % Dp);
+            const int n = (int)(r / Dp);
+            const int64_t vi = ((((int64_t)n * D + 2 * i + a) * H + 2 * j + b) * W + 2 * k + c) * cg + g;
+            float4 sum = p4[vi];
+            for (int sp = 1; sp < splits; ++sp) {
+                const float4 t = p4[(int64_t)sp * n4 + vi];
+                sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
+            }
+            const uint32_t lo = pack_bf16x2(sum.x, sum.y), hi = pack_bf16x2(sum.z, sum.w);
+            v[0] = __uint_as_float(lo << 16); v[1] = __uint_as_float(lo & 0xffff0000u);
+            v[2] = __uint_as_float(hi << 16); v[3] = __uint_as_float(hi & 0xffff0000u);
+        }
+        // per channel a nibble: position (3 bits) | valid << 3
+        uint32_t meta = 0;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+            meta |= ((uint32_t)q | ((q == 0 || v[ch] == v[ch]) ? 8u : 0u)) << (4 * ch);
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            const bool right = (q & m) != 0;   // this lane holds the later positions
+            const uint32_t om = (uint32_t)__shfl_xor((int)meta, m, 8);
+            uint32_t nm = 0;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const float ov = __shfl_xor(v[ch], m, 8);
+                const float lv = right ? ov : v[ch], rv = right ? v[ch] : ov;
+                const uint32_t lm = ((right ? om : meta) >> (4 * ch)) & 15u, rm = ((right ? meta : om) >> (4 * ch)) & 15u;
+                const bool take_r = (rm & 8u) && (!(lm & 8u) || rv > lv);
+                v[ch] = take_r ? rv : lv;
+                nm |= (take_r ? rm : lm) << (4 * ch);
+            }
+            meta = nm;
+        }
+        if (ok && q == 0) {
+            float o[4];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) o[ch] = v[ch] > 0.f ? v[ch] : slope * v[ch];
+            reinterpret_cast<uint2*>(P)[e] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            reinterpret_cast<uint32_t*>(idx)[e] = (meta & 7u) | ((meta >> 4) & 7u) << 8 | ((meta >> 8) & 7u) << 16 |
+                                                  ((meta >> 12) & 7u) << 24;
+        }
+    }
+}
+
 template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
 hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x, int cout,
                       int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
@@ -675,8 +756,12 @@ ConvPlan plan_conv_mfma(const cf_dims& x, int cout)
     return p;
 }
 
-hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part,
-                            const cf_dims& x, int cout, int coutpad, hipStream_t s)
+namespace {
+
+// The plan's conv kernel alone: with a split, the fp32 partials go to part
+// ([splits][voxels][cout]) for one of the two reductions below.
+hipError_t launch_conv_mfma_kernel(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part,
+                                   const cf_dims& x, int cout, int coutpad, hipStream_t s)
 {
     hipError_t e;
     if (p.ring) {
@@ -694,6 +779,15 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
         default: return hipErrorInvalidValue;
         }
     }
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part,
+                            const cf_dims& x, int cout, int coutpad, hipStream_t s)
+{
+    const hipError_t e = launch_conv_mfma_kernel(p, X, Wk, Y, part, x, cout, coutpad, s);
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
     int64_t blocks = (n4 + 255) / 256;
@@ -702,18 +796,30 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     return hipGetLastError();
 }
 
-// The pooled epilogue runs in the same kernel and tap order as the plain
-// launch of the same plan, so the fused result equals conv then pool bit
-// for bit.
+// Unsplit 4x4x16-tile plans pool in the conv kernel's epilogue (same kernel
+// and tap order as the plain launch); split plans pool in the reduction of
+// their partials (same summation order as split_reduce_bf16).  Either way
+// the fused result equals conv then pool bit for bit.
 bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x)
 {
-    return p.splits == 1 && p.cfg == 0 && (x.d % 2 == 0) && (x.h % 2 == 0) && (x.w % 2 == 0);
+    return (p.splits > 1 || p.cfg == 0) && (x.d % 2 == 0) && (x.h % 2 == 0) && (x.w % 2 == 0);
 }
 
 hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx,
-                                 float slope, const cf_dims& x, int cout, int coutpad, hipStream_t s)
+                                 float slope, const cf_dims& x, int cout, int coutpad, float* part, hipStream_t s)
 {
     if (!conv_mfma_can_pool(p, x)) return hipErrorInvalidValue;
+    if (p.splits > 1) {
+        if (!part) return hipErrorInvalidValue;
+        const hipError_t e = launch_conv_mfma_kernel(p, X, Wk, nullptr, part, x, cout, coutpad, s);
+        if (e != hipSuccess) return e;
+        const int64_t total = x.n * (x.d / 2) * (x.h / 2) * (x.w / 2) * (int64_t)cout / 4;   // 8 lanes each
+        int64_t blocks = (total + 31) / 32;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(split_reduce_pool_bf16, dim3((unsigned)blocks), dim3(256), 0, s, part, P, idx, (int)x.n,
+                           (int)x.d, (int)x.h, (int)x.w, cout, p.splits, slope);
+        return hipGetLastError();
+    }
     if (p.ring)
         return launch_kdr<64, 32, 128, 4, 4, 16, 32, 48, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);
     return launch_cfg<64, 32, 128, 4, 4, 16, 32, 3, true>(X, Wk, P, nullptr, x, cout, coutpad, 1, s, idx, slope);

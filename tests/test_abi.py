@@ -124,10 +124,13 @@ def test_train_step_validation_and_workspace():
     # channel split run fused: weights only (27 taps x 128 padded co x Cin)
     mx = (2, 16, 16, 16, 32)
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, mx, 64, cf.CF_CONV_POOL_FWD) == 27 * 128 * 32 * 2
+    # a plan with a channel split pools in the reduction of its partials:
+    # weights and the fp32 partials (2 splits of 2048 voxels x 64), no conv output
+    sx = (1, 8, 8, 32, 64)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, sx, 64, cf.CF_CONV_POOL_FWD) == 27 * 128 * 64 * 2 + 2 * 2048 * 64 * 4
     # unfused shapes carry the conv output through the workspace: 32 output
-    # channels (512-voxel tiles), an fp32 conv, a split channel reduction
-    for ux, co, dt in [((2, 16, 16, 16, 32), 32, cf.CF_BF16), ((2, 16, 16, 16, 32), 64, cf.CF_F32),
-                       ((1, 8, 8, 32, 64), 64, cf.CF_BF16)]:
+    # channels (512-voxel tiles), an fp32 conv
+    for ux, co, dt in [((2, 16, 16, 16, 32), 32, cf.CF_BF16), ((2, 16, 16, 16, 32), 64, cf.CF_F32)]:
         zb = ux[0] * ux[1] * ux[2] * ux[3] * co * (4 if dt == cf.CF_F32 else 2)
         assert cf.cf_conv3d_workspace_size(dt, ux, co, cf.CF_CONV_POOL_FWD) >= zb
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 3, 4, 4, 4), 32, cf.CF_CONV_POOL_FWD) == 0   # odd D

@@ -267,9 +267,12 @@ def test_error_statuses_on_device():
 # ------------------------------------------------------ fused block paths
 FUSED_CASES = [(2, 6, 10, 34, 4, 32), (1, 8, 8, 16, 4, 64), (1, 4, 4, 4, 32, 32), (1, 2, 2, 2, 4, 32)]
 # MFMA path with the pooled epilogue: 64 and 128 output channels on 4x4x16
-# tiles with ragged edges, plus a 64-channel input whose plan splits the
-# channel reduction (falls back to conv + pool).
-FUSED_FWD_CASES = FUSED_CASES + [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 8, 8, 32, 64, 64)]
+# tiles with ragged edges; plans that split the channel reduction (pooled in
+# the partials' reduction): a 64-channel input on 4x4x16 tiles, and narrow
+# 8-wide volumes on 4x8x8 tiles (as the late blocks) split 4 and 3 ways, one
+# with a ragged depth tile.
+FUSED_FWD_CASES = FUSED_CASES + [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 8, 8, 32, 64, 64),
+                                 (1, 6, 8, 8, 128, 64), (2, 8, 8, 8, 96, 64)]
 
 
 @pytest.mark.parametrize("shape", FUSED_FWD_CASES)
@@ -293,12 +296,13 @@ def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     assert np.mean(idx.cpu().numpy() == io) > 0.995   # rare flips where two window values round alike
 
 
-@pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128)])
+@pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 6, 8, 8, 64, 64)])
 def test_conv3d_pool_fwd_ties_follow_window_order(shape):
     """Integer inputs and weights in {-1, 0, 1} give conv outputs that tie
     often inside a window; the fused epilogue (whose window is split over two
-    lanes) must still pick the first strict maximum in window order, as the
-    separate pool kernel does."""
+    lanes), and the pooling reduction of a split plan (the last shape), must
+    still pick the first strict maximum in window order, as the separate pool
+    kernel does."""
     N, D, H, W, Ci, Co = shape
     rng = np.random.default_rng(sum(shape) + 5)
     x = rng.choice([-1.0, 0.0, 1.0], p=[0.2, 0.6, 0.2], size=(N, D, H, W, Ci)).astype(np.float32)
