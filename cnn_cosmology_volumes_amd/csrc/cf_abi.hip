@@ -850,6 +850,7 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         float* part_w = F(P.part_w);
         bool forked = false;
         int deferred = -1;    // a block whose weight gradient waits for the next fork
+        bool unpooled = false;   // this block's dz was written by the previous block's backward-data
         cf_status bst = CF_OK;
         for (int l = L - 1; l >= 0 && bst == CF_OK; --l) {
             const LayerPlan& Lp = P.layer[l];
@@ -864,11 +865,15 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
             }
             const cf_dims z = with_c(Lp.x, Lp.cout);
             void* dz = w + Lp.z;    // the conv output buffer is reused for its gradient
-            hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
-                                                          (const uint8_t*)(w + Lp.idx), (uint16_t*)dz, z, slope, stream)
-                              : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
-                                                       (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
-            if ((bst = check_hip(e, "pool backward")) != CF_OK) break;
+            if (!unpooled) {
+                hipError_t e = bf ? launch_pool_bwd<uint16_t>((const uint16_t*)(w + Lp.dp), (const uint16_t*)(w + Lp.p),
+                                                              (const uint8_t*)(w + Lp.idx), (uint16_t*)dz, z, slope,
+                                                              stream)
+                                  : launch_pool_bwd<float>((const float*)(w + Lp.dp), (const float*)(w + Lp.p),
+                                                           (const uint8_t*)(w + Lp.idx), (float*)dz, z, slope, stream);
+                if ((bst = check_hip(e, "pool backward")) != CF_OK) break;
+            }
+            unpooled = false;
             // The deepest block's weight gradient is the smallest, and the
             // auxiliary stream has nothing else to do yet: it waits for the
             // next block's fork (block l - 1 >= 1, never fused, so it forks),
@@ -893,10 +898,31 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                 deferred = -1;
                 if (bst != CF_OK) break;
             }
-            if (l > 0)
-                bst = check_hip(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + P.layer[l - 1].dp, part,
-                                          stream),
-                                "conv3d backward-data");
+            if (l > 0) {
+                // The deepest block's backward-data, when split, applies the
+                // previous block's pool backward in the reduction of its
+                // partials and writes that block's dz directly; its pooled
+                // gradient dp is read by nothing else (the previous block is
+                // not fused).  Doing the same for the next block down was
+                // slower: the caller's stream then reaches the big
+                // backward-data while the auxiliary stream's weight gradients
+                // still hold the GPU, and the two share it badly.
+                const LayerPlan& Lm = P.layer[l - 1];
+                const cf_dims y = with_c(Lp.x, Lp.cout);
+                const bool split = Lp.dg == Fwd::Mfma && plan_conv_mfma(y, (int)Lp.x.c).splits > 1;
+                if (split && bf && !Lm.fused && l == L - 1) {
+                    bst = check_hip(launch_conv_mfma_unpool(plan_conv_mfma(y, (int)Lp.x.c), (const uint16_t*)dz,
+                                                            (const uint16_t*)(w + Lp.wk_dg), part,
+                                                            (const uint16_t*)(w + Lm.p), (const uint8_t*)(w + Lm.idx),
+                                                            (uint16_t*)(w + Lm.z), slope, y, (int)Lp.x.c,
+                                                            roundup((int)Lp.x.c, 128), stream),
+                                    "conv3d backward-data + pool backward");
+                    unpooled = true;
+                } else {
+                    bst = check_hip(run_dgrad(Lp.dg, dtype, Lp.x, dz, w + Lp.wk_dg, Lp.cout, w + Lm.dp, part, stream),
+                                    "conv3d backward-data");
+                }
+            }
         }
         SgdList& dense_sl = forked ? sl_aux : sl_main;
         add(dense_sl, params[L], F(P.dW1), (int64_t)P.flat * P.d0);

@@ -133,6 +133,14 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
 // and for split plans (the partials' reduction pools; part as for
 // launch_conv_mfma); d, h, w even.
 bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x);
+// A split plan's conv (x: its input, cout: its output channels) whose output
+// is the pooled gradient dP of a 2^3 max-pool: the partials' reduction applies
+// the pool backward (P, idx: the pool's output and window indices, shape of
+// the conv output) and writes dZ (2x the conv output's D, H, W) in place of
+// dP; equal to launch_conv_mfma then the pool backward bit for bit.
+hipError_t launch_conv_mfma_unpool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, float* part,
+                                   const uint16_t* P, const uint8_t* idx, uint16_t* dZ, float slope, const cf_dims& x,
+                                   int cout, int coutpad, hipStream_t s);
 hipError_t launch_conv_mfma_pool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx,
                                  float slope, const cf_dims& x, int cout, int coutpad, float* part, hipStream_t s);
 

@@ -667,6 +667,56 @@ void split_reduce_pool_bf16(const float* __restrict__ part, uint16_t* __restrict
     }
 }
 
+// The split partials of a pooled-resolution gradient dP summed and rounded
+// as by split_reduce_bf16, then the pool backward applied to it as the pool
+// backward kernel does (dZ at the recorded window position = dP, times the
+// slope where the pooled value P is not positive; the other seven positions
+// zero; dZ written densely), so dZ equals split_reduce_bf16 followed by the
+// pool backward bit for bit and dP is never stored.  One thread per (pooled
+// voxel, 4 channels).  Dp, Hp, Wp: the pooled (partials') shape; dZ is
+// 2Dp x 2Hp x 2Wp; C % 4 == 0.
+__global__ __launch_bounds__(256)
+void split_reduce_unpool_bf16(const float* __restrict__ part, const uint16_t* __restrict__ P,
+                              const uint8_t* __restrict__ idx, uint16_t* __restrict__ dZ, int N, int Dp, int Hp, int Wp,
+                              int C, int splits, float slope)
+{
+    const int cg = C / 4, D = 2 * Dp, H = 2 * Hp, W = 2 * Wp;
+    const int64_t n4 = (int64_t)N * Dp * Hp * Wp * cg;   // float4 per split = items
+    const float4* __restrict__ p4 = reinterpret_cast<const float4*>(part);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += stride) {
+        float4 sum = p4[e];
+        for (int sp = 1; sp < splits; ++sp) {
+            const float4 t = p4[(int64_t)sp * n4 + e];
+            sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
+        }
+        const uint32_t lo = pack_bf16x2(sum.x, sum.y), hi = pack_bf16x2(sum.z, sum.w);
+        float gv[4] = {__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
+                       __uint_as_float(hi & 0xffff0000u)};
+        const uint2 pp = reinterpret_cast<const uint2*>(P)[e];
+        const float pv[4] = {__uint_as_float(pp.x << 16), __uint_as_float(pp.x & 0xffff0000u),
+                             __uint_as_float(pp.y << 16), __uint_as_float(pp.y & 0xffff0000u)};
+        const uint32_t ib = reinterpret_cast<const uint32_t*>(idx)[e];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gv[c] = pv[c] > 0.f ? gv[c] : slope * gv[c];
+        const int g = (int)(e % cg);
+        int64_t r = e / cg;
+        const int k = (int)(r % Wp); r /= Wp;
+        const int j = (int)(r % Hp); r /= Hp;
+        const int i = (int)(r % Dp);
+        const int n = (int)(r / Dp);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int a = q >> 2, b = (q >> 1) & 1, c2 = q & 1;
+            float o[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = ((ib >> (8 * c)) & 0xffu) == (uint32_t)q ? gv[c] : 0.f;
+            const int64_t vox = (((int64_t)n * D + 2 * i + a) * H + 2 * j + b) * W + 2 * k + c2;
+            reinterpret_cast<uint2*>(dZ)[vox * cg + g] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
+    }
+}
+
 template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
 hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x, int cout,
                       int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
@@ -793,6 +843,21 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(split_reduce_bf16, dim3((unsigned)blocks), dim3(256), 0, s, part, Y, n4, p.splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_mfma_unpool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, float* part,
+                                   const uint16_t* P, const uint8_t* idx, uint16_t* dZ, float slope, const cf_dims& x,
+                                   int cout, int coutpad, hipStream_t s)
+{
+    if (p.splits < 2 || !part || cout % 4 != 0) return hipErrorInvalidValue;
+    const hipError_t e = launch_conv_mfma_kernel(p, X, Wk, nullptr, part, x, cout, coutpad, s);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = x.n * x.d * x.h * x.w * (int64_t)cout / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(split_reduce_unpool_bf16, dim3((unsigned)blocks), dim3(256), 0, s, part, P, idx, dZ, (int)x.n,
+                       (int)x.d, (int)x.h, (int)x.w, cout, p.splits, slope);
     return hipGetLastError();
 }
 
