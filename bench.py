@@ -47,7 +47,7 @@ def parse():
 
 
 def build_inputs(dev, torch, cf, sd, c):
-    st = sd.streams(c.cfg_id)
+    st = sd.streams(c.seed_id)
     x = sd.lognormal_poisson_input(st["field"], st["poisson"], (c.batch, c.in_size, c.in_size, c.in_size),
                                    c.in_channels)
     params, cin = [], c.in_channels
@@ -193,7 +193,7 @@ def cpu_baseline(c, seconds):
     repeated for about `seconds`; scaled to 128^3-sample equivalents/s."""
     import oracle
     import synthdata as sd
-    st = sd.streams(c.cfg_id)
+    st = sd.streams(c.seed_id)
     s = c.in_size // 2
     x = sd.lognormal_poisson_input(st["field"], st["poisson"], (1, s, s, s), c.in_channels)
     conv, cin = [], c.in_channels
@@ -230,7 +230,7 @@ def main():
     from cnn_cosmology_volumes_amd.configs import CONFIGS, train_step_conv_flops
     import synthdata as sd
 
-    c = CONFIGS[3]
+    c = CONFIGS["train_bf16_128c4_b8"]
     dev = torch.device("cuda:0")
     if a.copy_mib:
         src = torch.ones(a.copy_mib << 20, dtype=torch.uint8, device=dev)

@@ -100,7 +100,7 @@ def oyama_table1_net(in_size: int) -> Network:
 
 @dataclass
 class Config:
-    cfg_id: int
+    seed_id: int                    # stream id of the seeded input generators
     name: str
     batch: int
     in_size: int
@@ -121,18 +121,20 @@ class Config:
                                    self.in_channels, self.slope)
 
 
-CONFIGS = {
-    1: Config(1, "conv3d_fwd_f32_32c4", 1, 32, [16], "f32", "conv_fwd",
-              note="single conv forward, fp32, 1x32^3x4 -> 16, lognormal field input"),
-    2: Config(2, "block_bf16_128c4_b4", 4, 128, [32], "bf16", "block",
-              note="one block fwd+dgrad+wgrad, 4x128^3x4 -> 32, upstream grad N(0,1)"),
-    3: Config(3, "train_bf16_128c4_b8", 8, 128, [32, 64, 128, 256, 256], "bf16", "train",
-              dense=[128, 64, 3], note="full 5-block network training step"),
-    4: Config(4, "partial_bf16_512c4_b1", 1, 512, [32, 64], "bf16", "partial",
-              note="first two blocks fwd+bwd at 512^3"),
-    5: Config(5, "train_bf16_512c4_b1", 1, 512, [32, 64, 128, 256, 256, 256, 256], "bf16", "train",
-              dense=[128, 64, 3], note="full 7-block network training step at 512^3"),
-}
+_ALL = (
+    Config(1, "conv3d_fwd_f32_32c4", 1, 32, [16], "f32", "conv_fwd",
+           note="single conv forward, fp32, 1x32^3x4 -> 16, lognormal field input"),
+    Config(2, "block_bf16_128c4_b4", 4, 128, [32], "bf16", "block",
+           note="one block fwd+dgrad+wgrad, 4x128^3x4 -> 32, upstream grad N(0,1)"),
+    Config(3, "train_bf16_128c4_b8", 8, 128, [32, 64, 128, 256, 256], "bf16", "train",
+           dense=[128, 64, 3], note="full 5-block network training step"),
+    Config(4, "partial_bf16_512c4_b1", 1, 512, [32, 64], "bf16", "partial",
+           note="first two blocks fwd+bwd at 512^3"),
+    Config(5, "train_bf16_512c4_b1", 1, 512, [32, 64, 128, 256, 256, 256, 256], "bf16", "train",
+           dense=[128, 64, 3], note="full 7-block network training step at 512^3"),
+)
+# the workloads by name
+CONFIGS = {c.name: c for c in _ALL}
 
 
 def train_step_conv_flops(net: Network, batch: int, first_dgrad: bool = False) -> int:

@@ -10,7 +10,7 @@ for them with the same shapes and a similar value structure: a unit-mean
 lognormal density per sample and channel, Poisson-sampled counts (many empty
 voxels), and log(1 + counts) as the network input.
 
-Streams: ``numpy.random.default_rng(SeedSequence([2026, cfg_id]))`` spawned
+Streams: ``numpy.random.default_rng(SeedSequence([2026, seed_id]))`` spawned
 into the fixed order [field, poisson, conv-weights, dense-weights, targets,
 upstream-grad].
 """
@@ -19,9 +19,9 @@ import numpy as np
 STREAMS = ("field", "poisson", "convw", "densew", "targets", "upstream")
 
 
-def streams(cfg_id: int, seed: int = 2026):
+def streams(seed_id: int, seed: int = 2026):
     """Dict of independent numpy Generators for one configuration."""
-    ss = np.random.SeedSequence([seed, cfg_id])
+    ss = np.random.SeedSequence([seed, seed_id])
     return {name: np.random.default_rng(child) for name, child in zip(STREAMS, ss.spawn(len(STREAMS)))}
 
 

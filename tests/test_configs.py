@@ -38,9 +38,9 @@ def test_table1_output_widths(w):
 
 def test_config_networks():
     # the headline configuration: 5 blocks at 128^3 end in 4^3 x 256 = 16384
-    n3 = CONFIGS[3].network()
+    n3 = CONFIGS["train_bf16_128c4_b8"].network()
     assert n3.flatten_size() == 4 ** 3 * 256
-    n5 = CONFIGS[5].network()
+    n5 = CONFIGS["train_bf16_512c4_b1"].network()
     assert n5.flatten_size() == 4 ** 3 * 256
     # conv work of one training step of the headline config (layer-1
     # backward-data not computed): 186.6 GF/sample

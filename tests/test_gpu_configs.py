@@ -68,10 +68,10 @@ def check_pool_slabs(z32, p_dev, idx_dev, dp32, dz_dev, rng, nslab=2):
         assert np.all(np.abs(gz - dzo) <= 2.0 ** -8 * np.abs(dzo))
 
 
-# --------------------------------------------------------------------- c1
-def test_config1_conv_fwd_f32_full():
-    c = CONFIGS[1]
-    st = sd.streams(1)
+# ------------------------------------- one conv forward, fp32, 1 x 32^3 x 4 -> 16
+def test_conv_fwd_f32_32c4_full():
+    c = CONFIGS["conv3d_fwd_f32_32c4"]
+    st = sd.streams(c.seed_id)
     x = sd.lognormal_field_input(st["field"], (c.batch, c.in_size, c.in_size, c.in_size), c.in_channels)
     w = sd.he_normal_conv(st["convw"], c.in_channels, c.filters[0])
     y = cf.cf_conv3d_fwd(to_dev(x, F32), to_dev(w, F32))
@@ -79,10 +79,10 @@ def test_config1_conv_fwd_f32_full():
     assert rel_err(host64(y), oracle.conv3d_fwd(x, w)) <= TOL_F32
 
 
-# --------------------------------------------------------------------- c2
-def test_config2_block_full():
-    c = CONFIGS[2]
-    st = sd.streams(2)
+# ----------------------------------- one block, bf16, 4 x 128^3 x 4 -> 32
+def test_block_128c4_b4_full():
+    c = CONFIGS["block_bf16_128c4_b4"]
+    st = sd.streams(c.seed_id)
     S, B, Cin, Co = c.in_size, c.batch, c.in_channels, c.filters[0]
     x = sd.lognormal_poisson_input(st["field"], st["poisson"], (B, S, S, S), Cin)
     w = sd.bf16_round_f32(sd.he_normal_conv(st["convw"], Cin, Co))
@@ -111,20 +111,20 @@ def test_config2_block_full():
     check_conv_wgrad(x, z, dw, rng)
 
 
-# --------------------------------------------------------------------- c3
-C3 = CONFIGS[3]
+# ---------------------------- 5-block network training step, bf16, 8 x 128^3 x 4
+TRAIN128 = CONFIGS["train_bf16_128c4_b8"]
 C3_LAYERS = []
-_s, _c = C3.in_size, C3.in_channels
-for _f in C3.filters:
+_s, _c = TRAIN128.in_size, TRAIN128.in_channels
+for _f in TRAIN128.filters:
     C3_LAYERS.append((_s, _c, _f))
     _s, _c = _s // 2, _f
 
 
 @pytest.mark.parametrize("layer", range(len(C3_LAYERS)))
-def test_config3_conv_layer_full(layer):
+def test_train128_conv_layer_full(layer):
     S, Cin, Co = C3_LAYERS[layer]
-    B = C3.batch
-    st = sd.streams(3)
+    B = TRAIN128.batch
+    st = sd.streams(TRAIN128.seed_id)
     rng = np.random.default_rng(30 + layer)
     if layer == 0:
         x = sd.lognormal_poisson_input(st["field"], st["poisson"], (B, S, S, S), Cin)
@@ -147,10 +147,10 @@ def test_config3_conv_layer_full(layer):
 
 
 @pytest.mark.parametrize("layer", range(len(C3_LAYERS)))
-def test_config3_pool_level_full(layer):
+def test_train128_pool_level_full(layer):
     S, _, Co = C3_LAYERS[layer]
-    B = C3.batch
-    st = sd.streams(3)
+    B = TRAIN128.batch
+    st = sd.streams(TRAIN128.seed_id)
     rng = np.random.default_rng(40 + layer)
     z = sd.normal(st["upstream"], (B, S, S, S, Co))
     dp = sd.normal(st["upstream"], (B, S // 2, S // 2, S // 2, Co))
@@ -160,12 +160,12 @@ def test_config3_pool_level_full(layer):
     check_pool_slabs(z, P, idx, dp, dZ, rng)
 
 
-def test_config3_dense_head_full():
+def test_train128_dense_head_full():
     """Dense head at the headline shape; the oracle runs its own chain from
     the same synthetic input and weights."""
-    st = sd.streams(3)
-    B = C3.batch
-    widths = [4 ** 3 * 256] + C3.dense
+    st = sd.streams(TRAIN128.seed_id)
+    B = TRAIN128.batch
+    widths = [4 ** 3 * 256] + TRAIN128.dense
     x = sd.normal(st["field"], (B, widths[0]), bf16=True)
     h = x.astype(np.float64)
     hd = to_dev(x, F32)
@@ -187,12 +187,12 @@ def test_config3_dense_head_full():
         hd, h = y, y_o
 
 
-def test_config3_train_step_full_consistency():
+def test_train128_train_step_full_consistency():
     """Full-size headline step: finite loss, bitwise deterministic, and equal
     to the composition of the individual entry points."""
     from test_gpu_train import composed_step, device_params
-    c = C3
-    st = sd.streams(3)
+    c = TRAIN128
+    st = sd.streams(TRAIN128.seed_id)
     x = sd.lognormal_poisson_input(st["field"], st["poisson"], (c.batch, c.in_size, c.in_size, c.in_size), 4)
     conv, cin = [], 4
     for f in c.filters:
@@ -216,14 +216,14 @@ def test_config3_train_step_full_consistency():
         assert torch.equal(a, b) and torch.equal(a, cc)
 
 
-def test_config3_training_lowers_loss():
+def test_train128_training_lowers_loss():
     """Repeated steps on one fixed batch of the 128^3 x 4 workload: every
     loss is finite, the loss falls over the first steps (gradient descent on
     a smooth loss with a small step), and after 20 steps it is below a tenth
     of the first one."""
     from test_gpu_train import device_params
-    c = C3
-    st = sd.streams(3)
+    c = TRAIN128
+    st = sd.streams(TRAIN128.seed_id)
     x = sd.lognormal_poisson_input(st["field"], st["poisson"], (c.batch, c.in_size, c.in_size, c.in_size), 4)
     conv, cin = [], 4
     for f in c.filters:

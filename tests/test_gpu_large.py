@@ -68,9 +68,9 @@ def pool_slabs(z_dev, p_dev, idx_dev, dp_dev, dz_dev, rng, nslab=2):
         assert np.all(np.abs(gz - dzo) <= 2.0 ** -8 * np.abs(dzo))
 
 
-def test_config4_block1_full():
+def test_partial512_block1_full():
     """512^3 x 4 -> 32: layer-1 forward, pooling, backward-weight."""
-    c = CONFIGS[4]
+    c = CONFIGS["partial_bf16_512c4_b1"]
     S, Co = c.in_size, c.filters[0]
     g = sd.torch_generator(4001, DEV)
     rng = np.random.default_rng(41)
@@ -95,9 +95,9 @@ def test_config4_block1_full():
     wgrad_points(x, zs, dw, rng, 6)
 
 
-def test_config4_block2_full():
+def test_partial512_block2_full():
     """256^3 x 32 -> 64: forward, backward-data, backward-weight."""
-    c = CONFIGS[4]
+    c = CONFIGS["partial_bf16_512c4_b1"]
     S, Ci, Co = c.in_size // 2, c.filters[0], c.filters[1]
     g = sd.torch_generator(4002, DEV)
     rng = np.random.default_rng(43)
@@ -114,17 +114,17 @@ def test_config4_block2_full():
     wgrad_points(x, dz, dw, rng, 10)
 
 
-C5 = CONFIGS[5]
+TRAIN512 = CONFIGS["train_bf16_512c4_b1"]
 C5_LAYERS = []
-_s, _c = C5.in_size, C5.in_channels
-for _f in C5.filters:
+_s, _c = TRAIN512.in_size, TRAIN512.in_channels
+for _f in TRAIN512.filters:
     C5_LAYERS.append((_s, _c, _f))
     _s, _c = _s // 2, _f
 
 
-# layers 1 and 2 of configuration 5 have the shapes of configuration 4's blocks
+# layers 1 and 2 of the 7-block 512^3 network have the shapes of the two-block 512^3 workload's blocks
 @pytest.mark.parametrize("layer", range(2, len(C5_LAYERS)))
-def test_config5_layer_full(layer):
+def test_train512_layer_full(layer):
     S, Ci, Co = C5_LAYERS[layer]
     g = sd.torch_generator(5000 + layer, DEV)
     rng = np.random.default_rng(50 + layer)
@@ -144,14 +144,14 @@ def test_config5_layer_full(layer):
     pool_slabs(dz, P, idx, dp, dZ, rng)
 
 
-def test_config5_train_step_full_consistency():
+def test_train512_train_step_full_consistency():
     """Full 7-block step at 512^3: finite loss, bitwise deterministic, equal
     to the composition of the individual entry points."""
     from test_gpu_train import composed_step
-    c = C5
+    c = TRAIN512
     g = sd.torch_generator(5100, DEV)
     x = sd.lognormal_poisson_input_torch(g, (1, c.in_size, c.in_size, c.in_size), 4, DEV)
-    st = sd.streams(5)
+    st = sd.streams(TRAIN512.seed_id)
     conv, cin = [], 4
     for f in c.filters:
         conv.append(sd.he_normal_conv(st["convw"], cin, f))
