@@ -255,9 +255,10 @@ def main():
     ws = torch.empty(cf.cf_train_step_workspace_size(m, cf.CF_BF16, c.batch), dtype=torch.uint8, device=dev)
     loss = torch.empty((1,), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    aux = cf.StepAux()
 
     def step():
-        cf.cf_train_step(m, xd, t, params, c.lr, ws=ws, loss=loss)
+        cf.cf_train_step(m, xd, t, params, c.lr, ws=ws, loss=loss, aux=aux)
 
     loss_first = None
     for _ in range(a.warmup):

@@ -41,6 +41,10 @@ class cf_model_desc(ctypes.Structure):
                 ("slope", ctypes.c_float)]
 
 
+class cf_step_aux(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p * CF_MAX_BLOCKS), ("join", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _SIG = {
     "cf_abi_version": ([], ctypes.c_int32),
@@ -63,8 +67,10 @@ _SIG = {
     "cf_mse": ([ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "cf_sgd": ([ctypes.c_int64, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "cf_train_step_workspace_size": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32], ctypes.c_size_t),
+    "cf_step_aux_create": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
+    "cf_step_aux_destroy": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
     "cf_train_step": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32, _P, _P, ctypes.POINTER(_P),
-                       ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+                       ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(cf_step_aux)], ctypes.c_int),
 }
 
 _lib = None
@@ -295,15 +301,39 @@ def cf_train_step_workspace_size(m, dtype, B):
     return int(lib().cf_train_step_workspace_size(ctypes.byref(m), dtype, int(B)))
 
 
-def cf_train_step(m, X, targets, params, lr, ws=None, loss=None, pred=None, stream=None):
+class StepAux:
+    """A cf_step_aux (second stream and events for cf_train_step) created on
+    the current device; destroyed with the object or by close()."""
+
+    def __init__(self):
+        self.aux = cf_step_aux()
+        check(lib().cf_step_aux_create(ctypes.byref(self.aux)))
+
+    def close(self):
+        if self.aux is not None:
+            torch.cuda.synchronize()
+            check(lib().cf_step_aux_destroy(ctypes.byref(self.aux)))
+            self.aux = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cf_train_step(m, X, targets, params, lr, ws=None, loss=None, pred=None, stream=None, aux=None):
     """One training step; `params` (fp32 masters: conv W per block, then W1,
-    b1, W2, b2, W3, b3) are updated in place.  Returns (loss, pred)."""
+    b1, W2, b2, W3, b3) are updated in place.  `aux`: a StepAux whose stream
+    runs the weight gradients beside the rest of the backward pass, or None
+    (everything on one stream).  Returns (loss, pred)."""
     dt = dtype_code(X.dtype)
     B = int(X.shape[0])
     ws = _ws(cf_train_step_workspace_size(m, dt, B), X.device, ws)
     if loss is None:
         loss = torch.empty((1,), dtype=torch.float32, device=X.device)
     arr = (_P * len(params))(*[p.data_ptr() for p in params])
+    auxp = None if aux is None else ctypes.byref(aux.aux)
     check(lib().cf_train_step(ctypes.byref(m), dt, B, _ptr(X), _ptr(targets), arr, float(lr), _ptr(loss), _ptr(pred),
-                              _ptr(ws), _wsbytes(ws), _stream(stream)))
+                              _ptr(ws), _wsbytes(ws), _stream(stream), auxp))
     return loss, pred

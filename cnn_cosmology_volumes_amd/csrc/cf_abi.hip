@@ -1,11 +1,11 @@
 // C ABI of libcf.so: argument validation, path selection and the training
 // step.  Every entry point validates before enqueuing anything, enqueues on
 // the caller's stream, and never synchronises or allocates device memory.
-// The training step also forks work onto one auxiliary stream per device,
-// created on its first call there, and joins it back before returning.
+// The library keeps no host state between calls besides the thread-local
+// error text: the training step's second stream and its events, when used,
+// are the caller's (cf_step_aux).
 #include "cf_internal.h"
 
-#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -294,7 +294,7 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
     if (!X || !W || !P || !idx) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: null tensor pointer");
     if (!al16(X) || !al16(W) || !al16(P) || !al16(idx))
         return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: pointers must be 16-byte aligned");
-    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: slope is NaN");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: slope must be >= 0 (got %g)", (double)slope);
     const Fwd p = fwd_path(dtype, x, cout);
     const bool fused = fused_pool_fwd(dtype, x, cout);
     const size_t wkb = up256(fwd_wk_bytes(p, x.c, cout)), pb = up256(fwd_part_bytes(p, x, cout));
@@ -339,7 +339,7 @@ cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, co
     if (!X || !dP || !P || !idx || !dW) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: null tensor pointer");
     if (!al16(X) || !al16(dP) || !al16(P) || !al16(idx) || !al16(dW))
         return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: pointers must be 16-byte aligned");
-    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: slope is NaN");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: slope must be >= 0 (got %g)", (double)slope);
     const Wg p = wgrad_path(dtype, x, cout);
     const bool fused = fused_pool_wgrad(dtype, x, cout);
     const size_t pb = up256(wgrad_part_bytes(p, dtype, x, cout));
@@ -438,7 +438,7 @@ cf_status cf_pool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, v
     if (st != CF_OK) return st;
     if (!Z || !P || !idx) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: null pointer");
     if (!al16(Z) || !al16(P) || !al16(idx)) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: pointers must be 16-byte aligned");
-    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: slope is NaN");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_pool3d_fwd: slope must be >= 0 (got %g)", (double)slope);
     hipError_t e = dtype == CF_F32 ? launch_pool_fwd<float>((const float*)Z, (float*)P, idx, z, slope, stream)
                                    : launch_pool_fwd<uint16_t>((const uint16_t*)Z, (uint16_t*)P, idx, z, slope, stream);
     CF_TRY_HIP(e, "pool forward");
@@ -453,7 +453,7 @@ cf_status cf_pool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* P
     if (!dP || !P || !idx || !dZ) return fail(CF_ERR_INVALID, "cf_pool3d_bwd: null pointer");
     if (!al16(dP) || !al16(P) || !al16(idx) || !al16(dZ))
         return fail(CF_ERR_INVALID, "cf_pool3d_bwd: pointers must be 16-byte aligned");
-    if (!(slope == slope)) return fail(CF_ERR_INVALID, "cf_pool3d_bwd: slope is NaN");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_pool3d_bwd: slope must be >= 0 (got %g)", (double)slope);
     hipError_t e = dtype == CF_F32
                        ? launch_pool_bwd<float>((const float*)dP, (const float*)P, idx, (float*)dZ, z, slope, stream)
                        : launch_pool_bwd<uint16_t>((const uint16_t*)dP, (const uint16_t*)P, idx, (uint16_t*)dZ, z, slope,
@@ -576,7 +576,7 @@ cf_status check_model(const cf_model_desc* m, cf_dtype dt, int32_t B)
         if (m->filters[l] <= 0 || m->filters[l] > 65536) return fail(CF_ERR_INVALID, "filters[%d] out of range", l);
     for (int k = 0; k < 3; ++k)
         if (m->dense[k] <= 0 || m->dense[k] > 65536) return fail(CF_ERR_INVALID, "dense[%d] out of range", k);
-    if (!(m->slope == m->slope)) return fail(CF_ERR_INVALID, "slope is NaN");
+    if (!(m->slope >= 0.f)) return fail(CF_ERR_INVALID, "slope must be >= 0 (got %g)", (double)m->slope);
     cf_dims x{B, m->d, m->h, m->w, m->cin};
     if ((st = check_dims(x, "input")) != CF_OK) return st;
     return CF_OK;
@@ -645,37 +645,6 @@ StepPlan plan_step(const cf_model_desc* m, cf_dtype dt, int32_t B)
     return P;
 }
 
-// Per-device auxiliary stream for the training step's weight gradients and
-// the events that order it against the caller's stream.  Created on first
-// use (default priority, non-blocking) and kept until the process ends.  A
-// step's fork/join sequence is enqueued under the device's mutex: a stream
-// wait binds to the event's most recent record, so reusing the events is safe
-// while one call's records and waits are not interleaved with another's.
-struct AuxState {
-    std::mutex mu;
-    hipStream_t s = nullptr;
-    hipEvent_t ev[CF_MAX_BLOCKS + 1] = {};
-};
-constexpr int kMaxDevices = 64;
-AuxState g_aux[kMaxDevices];
-
-cf_status aux_get(AuxState** out)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return fail(CF_ERR_HIP, "cf_train_step: no usable current device");
-    *out = &g_aux[dev];
-    return CF_OK;
-}
-
-cf_status aux_init(AuxState& ax)
-{
-    if (!ax.s) CF_TRY_HIP(hipStreamCreateWithFlags(&ax.s, hipStreamNonBlocking), "auxiliary stream");
-    for (int i = 0; i <= CF_MAX_BLOCKS; ++i)
-        if (!ax.ev[i]) CF_TRY_HIP(hipEventCreateWithFlags(&ax.ev[i], hipEventDisableTiming), "auxiliary event");
-    return CF_OK;
-}
-
 __global__ void cast_bf16_kernel(const float* __restrict__ s, uint16_t* __restrict__ d, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -683,6 +652,44 @@ __global__ void cast_bf16_kernel(const float* __restrict__ s, uint16_t* __restri
 }
 
 }  // namespace
+
+cf_status cf_step_aux_create(cf_step_aux* aux)
+{
+    if (!aux) return fail(CF_ERR_INVALID, "cf_step_aux_create: aux is null");
+    memset(aux, 0, sizeof(*aux));
+    cf_status st = check_hip(hipStreamCreateWithFlags(&aux->stream, hipStreamNonBlocking), "auxiliary stream");
+    for (int i = 0; i < CF_MAX_BLOCKS && st == CF_OK; ++i)
+        st = check_hip(hipEventCreateWithFlags(&aux->fork[i], hipEventDisableTiming), "fork event");
+    if (st == CF_OK) st = check_hip(hipEventCreateWithFlags(&aux->join, hipEventDisableTiming), "join event");
+    if (st != CF_OK) {
+        char keep[sizeof(g_err)];
+        memcpy(keep, g_err, sizeof(keep));
+        cf_step_aux_destroy(aux);
+        memcpy(g_err, keep, sizeof(keep));
+    }
+    return st;
+}
+
+cf_status cf_step_aux_destroy(cf_step_aux* aux)
+{
+    if (!aux) return CF_OK;
+    cf_status st = CF_OK;
+    for (int i = 0; i < CF_MAX_BLOCKS; ++i)
+        if (aux->fork[i]) {
+            const cf_status e = check_hip(hipEventDestroy(aux->fork[i]), "fork event");
+            if (st == CF_OK) st = e;
+        }
+    if (aux->join) {
+        const cf_status e = check_hip(hipEventDestroy(aux->join), "join event");
+        if (st == CF_OK) st = e;
+    }
+    if (aux->stream) {
+        const cf_status e = check_hip(hipStreamDestroy(aux->stream), "auxiliary stream");
+        if (st == CF_OK) st = e;
+    }
+    memset(aux, 0, sizeof(*aux));
+    return st;
+}
 
 size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int32_t B)
 {
@@ -692,7 +699,7 @@ size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int3
 
 cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const void* X, const float* targets,
                         float* const* params, float lr, float* loss_out, float* pred_out, void* ws, size_t ws_bytes,
-                        hipStream_t stream)
+                        hipStream_t stream, const cf_step_aux* aux)
 {
     cf_status st = check_model(m, dtype, B);
     if (st != CF_OK) return st;
@@ -704,13 +711,15 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     const StepPlan P = plan_step(m, dtype, B);
     if (ws_bytes < P.total) return fail(CF_ERR_WORKSPACE, "cf_train_step: workspace %zu < %zu bytes", ws_bytes, P.total);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_train_step: workspace null or misaligned");
-    // the auxiliary stream exists before anything is enqueued; the device's
-    // lock is held while this call enqueues its fork/join sequence
-    AuxState* axp = nullptr;
-    if ((st = aux_get(&axp)) != CF_OK) return st;
-    AuxState& ax = *axp;
-    std::lock_guard<std::mutex> guard(ax.mu);
-    if ((st = aux_init(ax)) != CF_OK) return st;
+    if (aux) {
+        if (!aux->stream || !aux->join) return fail(CF_ERR_INVALID, "cf_train_step: aux stream or join event is null");
+        if (aux->stream == stream) return fail(CF_ERR_INVALID, "cf_train_step: aux->stream must differ from stream");
+        for (int i = 0; i < CF_MAX_BLOCKS; ++i)
+            if (!aux->fork[i]) return fail(CF_ERR_INVALID, "cf_train_step: aux->fork[%d] is null", i);
+    }
+    // weight gradients go to the caller's second stream when one is given
+    const bool two = aux != nullptr;
+    hipStream_t as = two ? aux->stream : stream;
     char* w = (char*)ws;
     auto F = [&](size_t o) { return (float*)(w + o); };
     float* part = F(P.part);
@@ -884,14 +893,16 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
             } else {
                 // fork: the weight gradients read dz and the block inputs,
                 // which nothing on the caller's stream writes until the join
-                if ((bst = check_hip(hipEventRecord(ax.ev[l], stream), "fork event")) != CF_OK) break;
-                if ((bst = check_hip(hipStreamWaitEvent(ax.s, ax.ev[l], 0), "fork wait")) != CF_OK) break;
-                forked = true;
+                if (two) {
+                    if ((bst = check_hip(hipEventRecord(aux->fork[l], stream), "fork event")) != CF_OK) break;
+                    if ((bst = check_hip(hipStreamWaitEvent(as, aux->fork[l], 0), "fork wait")) != CF_OK) break;
+                    forked = true;
+                }
                 for (const int q : {deferred, l}) {
                     if (q < 0) continue;
                     const LayerPlan& Lq = P.layer[q];
                     const void* xin = q == 0 ? X : (const void*)(w + P.layer[q - 1].p);
-                    if ((bst = check_hip(run_wgrad(Lq.wg, dtype, Lq.x, xin, w + Lq.z, Lq.cout, F(Lq.dw), part_w, ax.s),
+                    if ((bst = check_hip(run_wgrad(Lq.wg, dtype, Lq.x, xin, w + Lq.z, Lq.cout, F(Lq.dw), part_w, as),
                                          "conv3d backward-weight")) != CF_OK)
                         break;
                 }
@@ -934,11 +945,11 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         for (int l = 0; l < L; ++l)    // a fused block's weight gradient is made on the caller's stream
             add(forked && !P.layer[l].fused ? sl_aux : sl_main, params[l], F(P.layer[l].dw),
                 (int64_t)27 * P.layer[l].x.c * P.layer[l].cout);
-        if (forked && bst == CF_OK) bst = check_hip(launch_sgd_multi(sl_aux, lr, ax.s), "sgd");
+        if (forked && bst == CF_OK) bst = check_hip(launch_sgd_multi(sl_aux, lr, as), "sgd");
         if (forked) {
             // join even after an error, so no work of this call outlives it on the auxiliary stream
-            const cf_status j1 = check_hip(hipEventRecord(ax.ev[CF_MAX_BLOCKS], ax.s), "join event");
-            const cf_status j2 = j1 == CF_OK ? check_hip(hipStreamWaitEvent(stream, ax.ev[CF_MAX_BLOCKS], 0), "join wait")
+            const cf_status j1 = check_hip(hipEventRecord(aux->join, as), "join event");
+            const cf_status j2 = j1 == CF_OK ? check_hip(hipStreamWaitEvent(stream, aux->join, 0), "join wait")
                                              : j1;
             if (bst == CF_OK) bst = j2;
         }

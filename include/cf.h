@@ -26,8 +26,9 @@
  *    nearest even.  Weight gradients, master weights and the dense head are
  *    always fp32.
  *  - Every pointer argument is a DEVICE pointer unless stated otherwise and
- *    must be 16-byte aligned.  The caller owns every buffer; the library
- *    allocates no device memory and keeps no mutable global state.
+ *    must be 16-byte aligned.  The caller owns every buffer, stream and
+ *    event; the library allocates no device memory and keeps no host state
+ *    between calls other than the thread-local text of cf_last_error().
  *  - Every call is asynchronous on `stream` (0 = the null stream) and never
  *    synchronises.  Outputs are overwritten, never accumulated into.
  *  - Arguments are validated before any GPU work is enqueued.  Failures
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CF_ABI_VERSION 1
+#define CF_ABI_VERSION 2
 #define CF_MAX_BLOCKS 8
 
 typedef enum {
@@ -82,7 +83,8 @@ typedef enum {
 /* Network description for cf_train_step: `nblocks` blocks with output
  * channels filters[0..nblocks-1] applied to a cin x d x h x w input (each of
  * d, h, w divisible by 2^nblocks), then dense layers of widths dense[0],
- * dense[1], dense[2] (the last has no activation), leaky-ReLU slope `slope`. */
+ * dense[1], dense[2] (the last has no activation), leaky-ReLU slope
+ * `slope` >= 0. */
 typedef struct {
     int32_t nblocks;
     int32_t cin;
@@ -169,6 +171,10 @@ cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, co
  *   idx[n,i,j,k,c] = a*4 + b*2 + e of the first strict maximum in (a,b,e)
  *                    lexicographic order
  * lrelu(z) = z if z > 0 else slope*z; slope = 1 gives plain max pooling.
+ * slope must be >= 0 (leaky ReLU is then non-decreasing, so the maximum of
+ * lrelu over a window is lrelu of the window maximum); a negative or NaN
+ * slope returns CF_ERR_INVALID.  The same holds for every entry point below
+ * that takes a pooling slope and for cf_model_desc.slope.
  *   Z   [z.n, z.d, z.h, z.w, z.c]         (dtype)  z.d, z.h, z.w even
  *   P   [z.n, z.d/2, z.h/2, z.w/2, z.c]   (dtype)  output
  *   idx same shape as P                   (uint8)  output */
@@ -222,6 +228,29 @@ cf_status cf_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t str
 
 /* --------------------------------------------------------- training step */
 
+/* Caller-owned second stream for cf_train_step.  The blocks' weight
+ * gradients read only tensors that the rest of the backward pass leaves
+ * alone, so they can run beside it on a second stream; `fork` events order
+ * that stream after the caller's stream and `join` orders the caller's
+ * stream after it.  All handles belong to the device that was current when
+ * they were created and must be used with streams of that device.  One
+ * cf_step_aux serves one call at a time: calls that may overlap in time
+ * (e.g. from several host threads) need one each, as they need distinct
+ * workspaces. */
+typedef struct {
+    hipStream_t stream;                 /* non-blocking, default priority */
+    hipEvent_t fork[CF_MAX_BLOCKS];     /* timing disabled */
+    hipEvent_t join;                    /* timing disabled */
+} cf_step_aux;
+
+/* Create the stream and events of `aux` (HOST pointer) on the current device.
+ * On failure nothing is left allocated and `aux` is zeroed. */
+cf_status cf_step_aux_create(cf_step_aux* aux);
+/* Destroy what cf_step_aux_create made and zero `aux`; NULL is a no-op.  No
+ * call that uses `aux` may still be enqueued on a stream that has not
+ * finished it (synchronise first). */
+cf_status cf_step_aux_destroy(cf_step_aux* aux);
+
 /* Workspace bytes for cf_train_step with this network, dtype and batch. */
 size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int32_t B);
 
@@ -240,15 +269,17 @@ size_t cf_train_step_workspace_size(const cf_model_desc* m, cf_dtype dtype, int3
  *   loss_out one device float: the loss of this step (before the update)
  *   pred_out [B, m->dense[2]] fp32 predictions of this step, or NULL
  * Layer-1 backward-data is not computed (the input needs no gradient).
- * Stream use: the weight gradients of the blocks run on an auxiliary stream
- * that the library creates on the first call on each device (default
- * priority, non-blocking) and keeps; it is forked from and joined back into
- * `stream` with events within the call, so all of the step's work is ordered
- * on `stream` as seen by the caller.  Calls from several host threads on one
- * device are serialised while they enqueue. */
+ * aux      HOST pointer to a cf_step_aux, or NULL.  With NULL every kernel
+ *          runs on `stream`.  Otherwise the blocks' weight gradients and the
+ *          updates of the parameters they feed run on aux->stream, forked from
+ *          `stream` with aux->fork[] and joined back with aux->join within the
+ *          call, so all of the step's work is still ordered on `stream` as the
+ *          caller sees it.  Results are identical bit for bit either way.
+ *          aux->stream must not be `stream`. */
 cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const void* X,
                         const float* targets, float* const* params, float lr, float* loss_out,
-                        float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream);
+                        float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                        const cf_step_aux* aux);
 
 /* ---------------------------------------------------------------- status */
 

@@ -258,15 +258,18 @@ def sgd(w, dw, lr):
 
 
 # ------------------------------------------------------------------ network
-def network_forward(x, conv_w, dense_w, slope, storage="f64"):
+def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None):
     """Forward pass of the conv stack and the dense head.
 
     x [B,D,H,W,Cin]; conv_w list of [3,3,3,Ci,Co]; dense_w list of three
-    (W [In,Out], b [Out]).  Returns (yhat, cache)."""
+    (W [In,Out], b [Out]).  Returns (yhat, cache).  If ``trace`` is a dict,
+    each block's stored conv output is appended to trace["z"]."""
     a = store(x, storage)
     blocks = []
     for w in conv_w:
         z = store(conv3d_fwd(a, w), storage)
+        if trace is not None:
+            trace.setdefault("z", []).append(z)
         p, idx = lrelu_maxpool_fwd(z, slope)
         p = store(p, storage)
         blocks.append(dict(x=a, p=p, idx=idx))
@@ -282,8 +285,10 @@ def network_forward(x, conv_w, dense_w, slope, storage="f64"):
     return h, dict(blocks=blocks, dense=dense, last_shape=a.shape)
 
 
-def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_dgrad=False):
-    """Backward pass; returns (conv_dw list, dense grads list of (dW, db))."""
+def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_dgrad=False, trace=None):
+    """Backward pass; returns (conv_dw list, dense grads list of (dW, db)).
+    If ``trace`` is a dict, the stored pooled gradient and conv-output
+    gradient of each block are recorded in trace["dp"][l] and trace["dz"][l]."""
     g = dyhat
     dense_g = [None] * len(dense_w)
     for li in reversed(range(len(dense_w))):
@@ -293,26 +298,36 @@ def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_
         g = dx
     dp = store(g.reshape(cache["last_shape"]), storage)
     conv_g = [None] * len(conv_w)
+    if trace is not None:
+        trace["dp"] = [None] * len(conv_w)
+        trace["dz"] = [None] * len(conv_w)
     for l in reversed(range(len(conv_w))):
         blk = cache["blocks"][l]
         dz = store(maxpool_lrelu_bwd(dp, blk["p"], blk["idx"], slope), storage)
+        if trace is not None:
+            trace["dp"][l] = dp
+            trace["dz"][l] = dz
         conv_g[l] = conv3d_bwd_weight(blk["x"], dz)
         if l > 0 or first_dgrad:
             dp = store(conv3d_bwd_data(dz, conv_w[l]), storage)
     return conv_g, dense_g
 
 
-def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64"):
+def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64", trace=None):
     """One full step.  Weights used in the passes are the masters rounded to
     the storage precision (bf16 for the conv weights of the bf16 path); the
-    update is applied to the fp32/fp64 masters.
+    update is applied to the fp32/fp64 masters.  ``trace``: as for
+    network_forward / network_backward, plus trace["conv_w"], the conv
+    weights the passes used.
 
     Returns dict(loss, yhat, conv_w, dense_w, conv_dw, dense_g)."""
     conv_use = [store(w, storage) for w in conv_w32]
+    if trace is not None:
+        trace["conv_w"] = conv_use
     dense_use = [(_f64(W), _f64(b)) for W, b in dense_w32]
-    yhat, cache = network_forward(x, conv_use, dense_use, slope, storage)
+    yhat, cache = network_forward(x, conv_use, dense_use, slope, storage, trace=trace)
     loss, dy = mse(yhat, targets)
-    conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage)
+    conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage, trace=trace)
     master = "f64" if storage == "f64" else "f32"
     new_conv = [store(sgd(w, g, lr), master) for w, g in zip(conv_w32, conv_g)]
     new_dense = [(store(sgd(W, dW, lr), master), store(sgd(b, db, lr), master))

@@ -57,3 +57,72 @@ def sample_points(rng, shape, n, include_corners=True):
                         for c in (0, C - 1):
                             pts.add(base + c)
     return np.array(sorted(pts), dtype=np.int64)
+
+
+def windows(z):
+    """[N,D,H,W,C] -> [N,D/2,H/2,W/2,C,8] with the last axis in window order
+    a*4 + b*2 + e (depth, height, width offsets)."""
+    N, D, H, W, C = z.shape
+    return z.reshape(N, D // 2, 2, H // 2, 2, W // 2, 2, C).transpose(0, 1, 3, 5, 7, 2, 4, 6).reshape(
+        N, D // 2, H // 2, W // 2, C, 8)
+
+
+def window_values(z, where):
+    """Window values [K, 8] (window order) of z [N,D,H,W,C] at the K pooled
+    positions of the boolean mask ``where`` [N,D/2,H/2,W/2,C]."""
+    n, i, j, k, c = np.nonzero(where)
+    out = np.empty((n.size, 8), np.float64)
+    for pos in range(8):
+        a, b, e = pos >> 2, (pos >> 1) & 1, pos & 1
+        out[:, pos] = z[n, 2 * i + a, 2 * j + b, 2 * k + e, c]
+    return out
+
+
+def check_pool_indices(z_oracle, idx_gpu, idx_oracle, p_gpu, p_oracle, rel=2.0 ** -7):
+    """The pooling rule where several answers are correct: a GPU window index
+    may differ from the oracle's only where the oracle's two largest window
+    values are a near tie, |v1 - v2| <= rel * max(|v1|, RMS(z)); there the
+    two pooled values must agree to within that gap plus one bf16 rounding.
+    Everywhere else the index must be the oracle's and P must match to one
+    bf16 rounding.  Returns the boolean mask of windows (shape of P) whose
+    index differs, for masking the gradients that depend on them."""
+    z = np.asarray(z_oracle, np.float64)
+    idx_gpu = np.asarray(idx_gpu)
+    idx_oracle = np.asarray(idx_oracle)
+    rms = float(np.sqrt(np.mean(np.square(z))))
+    diff = idx_gpu != idx_oracle
+    if np.any(diff):
+        top2 = np.sort(window_values(z, diff), axis=1)[:, -2:]
+        near = (top2[:, 1] - top2[:, 0]) <= rel * np.maximum(np.abs(top2[:, 1]), rms)
+        assert np.all(near), "index differs from the oracle's in %d windows without a near tie" % int(
+            np.count_nonzero(~near))
+    pg = np.asarray(p_gpu, np.float64)
+    po = np.asarray(p_oracle, np.float64)
+    prms = float(np.sqrt(np.mean(np.square(po))))
+    tol = (2.0 ** -8) * np.abs(po) + 1e-30
+    tol = np.where(diff, tol + rel * np.maximum(np.abs(po), prms), tol)
+    assert np.all(np.abs(pg - po) <= tol), "pooled values differ beyond rounding"
+    return diff
+
+
+def kink_mask(z_oracle, p_oracle, slope, rel=2.0 ** -8):
+    """Pooled positions whose window maximum z sits at the leaky-ReLU kink,
+    |z| <= rel * RMS(z): there either slope of the derivative is accepted."""
+    z = np.asarray(z_oracle, np.float64)
+    po = np.asarray(p_oracle, np.float64)
+    zmax = np.where(po > 0, po, po / slope)
+    return np.abs(zmax) <= rel * float(np.sqrt(np.mean(np.square(z))))
+
+
+def unpool_neighbourhood_mask(diff, halo=1):
+    """Voxel mask [N,D,H,W] (input resolution of the pool) of every voxel
+    whose conv backward-data value can depend on a window in ``diff``
+    ([N,Dp,Hp,Wp,C] bool): the window's 2^3 voxels grown by ``halo`` voxels
+    on each side."""
+    N, Dp, Hp, Wp = diff.shape[:4]
+    anyc = diff.any(axis=4)
+    mask = np.zeros((N, 2 * Dp, 2 * Hp, 2 * Wp), bool)
+    for n, i, j, k in zip(*np.nonzero(anyc)):
+        mask[n, max(0, 2 * i - halo):2 * i + 2 + halo, max(0, 2 * j - halo):2 * j + 2 + halo,
+             max(0, 2 * k - halo):2 * k + 2 + halo] = True
+    return mask

@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
     assert len(names) >= 17
     for n in names:
         assert hasattr(L, n), n
-    assert L.cf_abi_version() == 1
+    assert L.cf_abi_version() == 2
 
 
 def test_status_strings():
@@ -138,12 +138,55 @@ def test_train_step_validation_and_workspace():
     assert cf.cf_train_step_workspace_size(bad, cf.CF_BF16, 8) == 0
     L = cf.lib()
     arr = (ctypes.c_void_p * 11)(*([0x100000] * 11))
-    st = L.cf_train_step(ctypes.byref(bad), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None)
+    st = L.cf_train_step(ctypes.byref(bad), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None, None)
     assert st == cf.CF_ERR_UNSUPPORTED
-    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 16, None)
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 16, None, None)
     assert st == cf.CF_ERR_WORKSPACE
     arr[3] = None
-    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None)
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 8, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None, None)
     assert st == cf.CF_ERR_INVALID
     m.nblocks = 9
     assert cf.cf_train_step_workspace_size(m, cf.CF_BF16, 8) == 0
+
+
+def test_negative_or_nan_slope_rejected():
+    """Leaky ReLU with slope >= 0 is non-decreasing, which the pooling rule
+    (lrelu of the window maximum) and its backward (sign taken from P)
+    rely on; other slopes are rejected before anything is enqueued."""
+    L = cf.lib()
+    z = cf.dims((1, 4, 4, 4, 32))
+    for slope in (-0.3, float("nan")):
+        assert L.cf_pool3d_fwd(cf.CF_BF16, z, FAKE, slope, FAKE, FAKE, None) == cf.CF_ERR_INVALID
+        assert L.cf_pool3d_bwd(cf.CF_BF16, z, FAKE, FAKE, FAKE, slope, FAKE, None) == cf.CF_ERR_INVALID
+        assert L.cf_conv3d_pool_fwd(cf.CF_BF16, z, FAKE, FAKE, 32, cf.CONV3, slope, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == cf.CF_ERR_INVALID
+        assert L.cf_pool_conv3d_bwd_weight(cf.CF_BF16, cf.dims((1, 4, 4, 4, 4)), FAKE, FAKE, FAKE, FAKE, 32,
+                                           cf.CONV3, slope, FAKE, FAKE, 1 << 30, None) == cf.CF_ERR_INVALID
+        assert b"slope" in L.cf_last_error()
+        m = cf.model_desc(4, 16, [32, 64], (32, 16, 3), slope)
+        assert cf.cf_train_step_workspace_size(m, cf.CF_BF16, 2) == 0
+    # slope 0 (plain ReLU) and 1 (plain max pooling) are valid
+    m = cf.model_desc(4, 16, [32, 64], (32, 16, 3), 0.0)
+    assert cf.cf_train_step_workspace_size(m, cf.CF_BF16, 2) > 0
+
+
+def test_train_step_aux_validation():
+    """A caller-owned second stream must carry every handle; a half-filled
+    cf_step_aux is rejected before anything is enqueued."""
+    L = cf.lib()
+    m = cf.model_desc(4, 16, [32, 64], (32, 16, 3))
+    arr = (ctypes.c_void_p * 8)(*([0x100000] * 8))
+    aux = cf.cf_step_aux()
+    aux.stream = 0x200000
+    aux.join = 0x300000
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 2, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None,
+                         ctypes.byref(aux))
+    assert st == cf.CF_ERR_INVALID and b"fork" in L.cf_last_error()
+    for i in range(cf.CF_MAX_BLOCKS):
+        aux.fork[i] = 0x400000 + 16 * i
+    aux.stream = None
+    st = L.cf_train_step(ctypes.byref(m), cf.CF_BF16, 2, FAKE, FAKE, arr, 1e-3, FAKE, None, FAKE, 1 << 40, None,
+                         ctypes.byref(aux))
+    assert st == cf.CF_ERR_INVALID
+    assert L.cf_step_aux_create(None) == cf.CF_ERR_INVALID
+    assert L.cf_step_aux_destroy(None) == cf.CF_OK

@@ -10,7 +10,7 @@ import torch
 import oracle
 import synthdata as sd
 from cnn_cosmology_volumes_amd import cf
-from gpu_util import (TOL_BF16, TOL_F32, bf16_elementwise_ok, host64, rel_err, to_dev)
+from gpu_util import (TOL_BF16, TOL_F32, bf16_elementwise_ok, check_pool_indices, host64, rel_err, to_dev)
 
 pytestmark = pytest.mark.gpu
 BF, F32 = torch.bfloat16, torch.float32
@@ -291,9 +291,11 @@ def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
     zo = oracle.round_bf16(oracle.conv3d_fwd(x, w))
     po, io = oracle.lrelu_maxpool_fwd(zo, SLOPE)
+    po = oracle.round_bf16(po)
     g = host64(P)
     assert rel_err(g, po) <= TOL_BF16
-    assert np.mean(idx.cpu().numpy() == io) > 0.995   # rare flips where two window values round alike
+    # an index may differ from the oracle's only in a near-tied window
+    check_pool_indices(zo, idx.cpu().numpy(), io, g, po)
 
 
 @pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 6, 8, 8, 64, 64)])

@@ -9,7 +9,7 @@ import torch
 import oracle
 import synthdata as sd
 from cnn_cosmology_volumes_amd import cf
-from gpu_util import TOL_BF16, host64, rel_err, to_dev
+from gpu_util import TOL_BF16, TOL_F32, host64, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 BF, F32 = torch.bfloat16, torch.float32
@@ -43,25 +43,31 @@ def device_params(conv, dense):
     return ps
 
 
-def run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w):
+def run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w, aux=None):
     m = cf.model_desc(4, size, filters, dense_w, SLOPE)
     params = device_params(conv, dense)
     old = [p.clone() for p in params]
     pred = torch.empty((x.shape[0], dense_w[-1]), dtype=F32, device="cuda")
-    loss, _ = cf.cf_train_step(m, to_dev(x, dtype), to_dev(t, F32), params, lr, pred=pred)
+    loss, _ = cf.cf_train_step(m, to_dev(x, dtype), to_dev(t, F32), params, lr, pred=pred, aux=aux)
     torch.cuda.synchronize()
     return loss.item(), host64(pred), old, params
+
+
+# Gradients are recovered from one SGD update with a power-of-two rate: the
+# update W - lr * dW is one fused multiply-add (exact product, one rounding),
+# so (W - W_new) / lr is dW to within 2^-24 of |dW| plus ulp(W) / lr.
+LR_RECOVER = 2.0 ** 20
 
 
 @pytest.mark.parametrize("dtype", [BF, F32])
 def test_train_step_matches_oracle(dtype):
     B, size, filters, dense_w = 2, 16, [32, 64], [32, 16, 3]
     x, conv, dense, t = make_problem(1, B, size, filters, dense_w, dtype)
-    lr = 1.0   # large step so the gradient is recovered exactly from the update
+    lr = LR_RECOVER
     loss, pred, old, new = run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w)
     storage = "bf16" if dtype == BF else "f32"
     ref = oracle.train_step(x, t, conv, dense, lr, SLOPE, storage=storage)
-    tol = TOL_BF16 if dtype == BF else 1e-4
+    tol = TOL_BF16 if dtype == BF else TOL_F32
     assert abs(loss - ref["loss"]) <= tol * ref["loss"]
     assert rel_err(pred, ref["yhat"]) <= tol
     L = len(filters)
@@ -116,15 +122,17 @@ def composed_step(xd, conv_d, dense_d, td, lr):
     return loss
 
 
+@pytest.mark.parametrize("two_streams", [False, True])
 @pytest.mark.parametrize("problem", [(2, 16, [32, 64], [32, 16, 3]), (1, 32, [32, 64, 128], [64, 32, 3])])
-def test_train_step_equals_composition_bitwise(problem):
+def test_train_step_equals_composition_bitwise(problem, two_streams):
     B, size, filters, dense_w = problem
     x, conv, dense, t = make_problem(2, B, size, filters, dense_w, BF)
     m = cf.model_desc(4, size, filters, dense_w, SLOPE)
     xd, td = to_dev(x, BF), to_dev(t, F32)
     p1 = device_params(conv, dense)
     p2 = device_params(conv, dense)
-    loss1, _ = cf.cf_train_step(m, xd, td, p1, 1e-3)
+    aux = cf.StepAux() if two_streams else None
+    loss1, _ = cf.cf_train_step(m, xd, td, p1, 1e-3, aux=aux)
     loss2 = composed_step(xd, p2[:len(filters)], p2[len(filters):], td, 1e-3)
     torch.cuda.synchronize()
     assert torch.equal(loss1, loss2)
@@ -166,10 +174,10 @@ def test_train_step_rejects_bad_arguments():
 
 
 def test_train_step_concurrent_threads_and_streams_match_sequential():
-    """Steps enqueued from two host threads on two streams at once share the
-    library's auxiliary stream and events for the blocks' weight gradients;
+    """Steps enqueued from two host threads on two streams at once, each with
+    its own second stream (cf_step_aux) for the blocks' weight gradients:
     each thread's losses and parameters must equal, bit for bit, the same
-    steps run one after another on one stream."""
+    steps run one after another on one stream without a second stream."""
     import threading
     B, size, filters, dense_w = 2, 32, [32, 64, 128], [64, 32, 3]
     m = cf.model_desc(4, size, filters, dense_w, SLOPE)
@@ -185,6 +193,7 @@ def test_train_step_concurrent_threads_and_streams_match_sequential():
 
     inputs = [(to_dev(x, BF), to_dev(t, F32), device_params(conv, dense)) for x, conv, dense, t in probs]
     streams = [torch.cuda.Stream() for _ in range(2)]
+    auxes = [cf.StepAux() for _ in range(2)]
     torch.cuda.synchronize()
     results, errors = [None, None], []
     start = threading.Barrier(2)
@@ -195,7 +204,8 @@ def test_train_step_concurrent_threads_and_streams_match_sequential():
             s = streams[k]
             with torch.cuda.stream(s):
                 start.wait(timeout=60)
-                losses = [cf.cf_train_step(m, xd, td, p, lr, stream=s)[0].clone() for _ in range(nsteps)]
+                losses = [cf.cf_train_step(m, xd, td, p, lr, stream=s, aux=auxes[k])[0].clone()
+                          for _ in range(nsteps)]
             s.synchronize()
             results[k] = losses
         except Exception as e:   # reported by the main thread
