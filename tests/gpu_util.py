@@ -83,9 +83,14 @@ def check_pool_indices(z_oracle, idx_gpu, idx_oracle, p_gpu, p_oracle, rel=2.0 *
     may differ from the oracle's only where the oracle's two largest window
     values are a near tie, |v1 - v2| <= rel * max(|v1|, RMS(z)); there the
     two pooled values must agree to within that gap plus one bf16 rounding.
-    Everywhere else the index must be the oracle's and P must match to one
-    bf16 rounding.  Returns the boolean mask of windows (shape of P) whose
-    index differs, for masking the gradients that depend on them."""
+    Everywhere else the index must be the oracle's and P must match to
+    within what the two roundings allow: each side's conv output is a bf16
+    rounding of nearly the same sum (fp32 accumulation on the GPU, exact in
+    the oracle), so the two can sit one bf16 ulp apart (up to 2^-7
+    relative), and P = lrelu(Z) is rounded once more on each side (2^-9
+    each); hence 2^-6 relative, plus 1e-3 of RMS(P) for outputs near zero.
+    Returns the boolean mask of windows (shape of P) whose index differs,
+    for masking the gradients that depend on them."""
     z = np.asarray(z_oracle, np.float64)
     idx_gpu = np.asarray(idx_gpu)
     idx_oracle = np.asarray(idx_oracle)
@@ -99,7 +104,7 @@ def check_pool_indices(z_oracle, idx_gpu, idx_oracle, p_gpu, p_oracle, rel=2.0 *
     pg = np.asarray(p_gpu, np.float64)
     po = np.asarray(p_oracle, np.float64)
     prms = float(np.sqrt(np.mean(np.square(po))))
-    tol = (2.0 ** -8) * np.abs(po) + 1e-30
+    tol = (2.0 ** -6) * np.abs(po) + 1e-3 * prms
     tol = np.where(diff, tol + rel * np.maximum(np.abs(po), prms), tol)
     assert np.all(np.abs(pg - po) <= tol), "pooled values differ beyond rounding"
     return diff

@@ -65,9 +65,11 @@ def test_block128_chain_matches_oracle():
     del zo
     assert rel_err(gp, po) <= TOL_BF16
     dzo = oracle.round_bf16(oracle.maxpool_lrelu_bwd(dp, po, io, SLOPE))
-    # dZ: equal to one bf16 rounding outside the ambiguous windows
+    # dZ outside the ambiguous windows: the same pooled gradient times the
+    # same slope, rounded to bf16 on both sides (the GPU multiplies by the
+    # fp32 slope), so at most one bf16 ulp apart (2^-7 relative)
     keep = ~np.repeat(np.repeat(np.repeat(amb, 2, 1), 2, 2), 2, 3)
-    assert np.all(np.abs(gdz - dzo)[keep] <= 2.0 ** -8 * np.abs(dzo)[keep])
+    assert np.all(np.abs(gdz - dzo)[keep] <= 2.0 ** -7 * np.abs(dzo)[keep])
     dwo = oracle.conv3d_bwd_weight(x, dzo)
     dxo = oracle.round_bf16(oracle.conv3d_bwd_data(dzo, w))
     del dzo
