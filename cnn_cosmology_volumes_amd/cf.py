@@ -54,6 +54,7 @@ _SIG = {
     "cf_conv3d_fwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_conv3d_bwd_data": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_conv3d_bwd_weight": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_conv3d_bwd_weight_noalloc": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, _P, _P], ctypes.c_int),
     "cf_conv3d_pool_fwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_int32, cf_conv, ctypes.c_float, _P, _P, _P,
                             ctypes.c_size_t, _P], ctypes.c_int),
     "cf_pool_conv3d_bwd_weight": ([ctypes.c_int, cf_dims, _P, _P, _P, _P, ctypes.c_int32, cf_conv, ctypes.c_float, _P,
@@ -178,6 +179,17 @@ def cf_conv3d_bwd_weight(X, dY, dW=None, ws=None, stream=None):
     ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_BWD_WEIGHT), X.device, ws)
     check(lib().cf_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, CONV3, _ptr(dW), _ptr(ws),
                                      _wsbytes(ws), _stream(stream)))
+    return dW
+
+
+def cf_conv3d_bwd_weight_noalloc(X, dY, dW, stream=None):
+    """As cf_conv3d_bwd_weight, with no workspace: the library's static
+    per-device scratch holds the partial sums.  dW must be given (the call
+    allocates nothing)."""
+    dt = dtype_code(X.dtype)
+    cout = int(dY.shape[4])
+    check(lib().cf_conv3d_bwd_weight_noalloc(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, CONV3, _ptr(dW),
+                                             _stream(stream)))
     return dW
 
 

@@ -6,6 +6,7 @@
 // are the caller's (cf_step_aux).
 #include "cf_internal.h"
 
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -417,6 +418,60 @@ cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const v
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_conv3d_bwd_weight: workspace %zu < %zu bytes", ws_bytes, need);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: workspace null or misaligned");
     CF_TRY_HIP(run_wgrad(p, dtype, x, X, dY, cout, dW, (float*)ws, stream), "conv3d backward-weight");
+    return CF_OK;
+}
+
+// ------------------------------------------- backward-weight, no allocation
+// Scratch of cf_conv3d_bwd_weight_noalloc: the fp32 split partial sums that
+// cf_conv3d_bwd_weight keeps in its workspace.  One copy per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up on the first
+// call there and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[CF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxScratchDevices];
+
+cf_status scratch_address(void** out)
+{
+    int dev = -1;
+    CF_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(CF_ERR_UNSUPPORTED, "cf_conv3d_bwd_weight_noalloc: device %d beyond the %d this build tracks", dev,
+                    kMaxScratchDevices);
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // the same address on every call for this device, so racing first
+        // calls store the same value
+        CF_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+        if (!p) return fail(CF_ERR_HIP, "cf_conv3d_bwd_weight_noalloc: scratch address is null");
+        g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return CF_OK;
+}
+}  // namespace
+
+cf_status cf_conv3d_bwd_weight_noalloc(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
+                                       cf_conv conv, float* dW, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (!X || !dY || !dW) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight_noalloc: null tensor pointer");
+    if (!al16(X) || !al16(dY) || !al16(dW))
+        return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight_noalloc: pointers must be 16-byte aligned");
+    const Wg p = wgrad_path(dtype, x, cout);
+    const size_t need = up256(wgrad_part_bytes(p, dtype, x, cout));
+    if (need > (size_t)CF_NOALLOC_SCRATCH_BYTES)
+        return fail(CF_ERR_WORKSPACE,
+                    "cf_conv3d_bwd_weight_noalloc: this shape needs %zu bytes of partial sums, more than the %zu-byte "
+                    "static scratch; use cf_conv3d_bwd_weight with a workspace", need,
+                    (size_t)CF_NOALLOC_SCRATCH_BYTES);
+    void* part = nullptr;
+    if ((st = scratch_address(&part)) != CF_OK) return st;
+    CF_TRY_HIP(run_wgrad(p, dtype, x, X, dY, cout, dW, (float*)part, stream), "conv3d backward-weight");
     return CF_OK;
 }
 

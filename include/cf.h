@@ -28,7 +28,8 @@
  *  - Every pointer argument is a DEVICE pointer unless stated otherwise and
  *    must be 16-byte aligned.  The caller owns every buffer, stream and
  *    event; the library allocates no device memory and keeps no host state
- *    between calls other than the thread-local text of cf_last_error().
+ *    between calls other than the thread-local text of cf_last_error() and
+ *    the per-device address of cf_conv3d_bwd_weight_noalloc's scratch.
  *  - Every call is asynchronous on `stream` (0 = the null stream) and never
  *    synchronises.  Outputs are overwritten, never accumulated into.
  *  - Arguments are validated before any GPU work is enqueued.  Failures
@@ -131,6 +132,24 @@ cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const vo
  * in a fixed order: results are bitwise reproducible run to run. */
 cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
                                cf_conv conv, float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device scratch behind cf_conv3d_bwd_weight_noalloc (per device). */
+#define CF_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* cf_conv3d_bwd_weight for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, allocation-free serving
+ * loops, harnesses that forbid hipMalloc.  Same operation, arguments (minus
+ * the workspace) and result bit for bit as cf_conv3d_bwd_weight; the split
+ * partial sums live in a static device array of CF_NOALLOC_SCRATCH_BYTES
+ * that each device holds from the library's load until the process ends.
+ * The call allocates nothing.  A shape whose partial sums need more than
+ * that returns CF_ERR_WORKSPACE before anything is enqueued.  Every call on a
+ * device shares that device's array: calls that may overlap in time on one
+ * device (several streams or host threads) race and give wrong results;
+ * serialise them.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress) with that device current. */
+cf_status cf_conv3d_bwd_weight_noalloc(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
+                                       cf_conv conv, float* dW, hipStream_t stream);
 
 /* Fused block forward: exactly cf_conv3d_fwd followed by cf_pool3d_fwd on
  * its output (the conv output rounded to dtype first), i.e. one

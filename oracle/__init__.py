@@ -334,3 +334,75 @@ def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64", trace=
                  for (W, b), (dW, db) in zip(dense_w32, dense_g)]
     return dict(loss=loss, yhat=yhat, conv_w=new_conv, dense_w=new_dense,
                 conv_dw=conv_g, dense_g=dense_g)
+
+
+# ------------------------------------------------------ Adam + LARC + decay
+def poly_decay(lr0, lr_end, decay_steps, power, step):
+    """Polynomial learning-rate decay (CosmoFlow, Sec. III-B: power 1, i.e.
+    linear; Oyama et al., Sec. IV: linear decay to 0.01x of the initial
+    rate): the rate after ``step`` completed updates,
+        (lr0 - lr_end) * (1 - min(step, T) / T) ** power + lr_end."""
+    s = min(float(step), float(decay_steps))
+    return (lr0 - lr_end) * (1.0 - s / float(decay_steps)) ** power + lr_end
+
+
+def adam_larc_step(w, g, m, v, t, lr, beta1, beta2, eps, trust):
+    """One Adam update with LARC's layer-wise clipping, for one parameter
+    tensor (one "layer"), in fp64.
+
+    Adam (Kingma and Ba; the optimizer of CosmoFlow Sec. III-B and Oyama et
+    al. Sec. IV, beta1 0.9, beta2 0.999, eps 1e-8):
+        m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+        u = (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+    LARC (CosmoFlow Sec. III-B: the rate is scaled by the layer's weight
+    norm and clipped at Adam's nominal rate): the tensor's rate is
+        lr_l = min(lr, trust * ||w|| / ||g||),
+    or lr itself when trust <= 0 or either norm is zero.  Then w <- w - lr_l u.
+    t is the 1-based update count.  Returns (w, m, v, lr_l) as new arrays."""
+    w, g, m, v = _f64(w), _f64(g), _f64(m), _f64(v)
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    u = mhat / (np.sqrt(vhat) + eps)
+    wn = float(np.sqrt(np.sum(w * w)))
+    gn = float(np.sqrt(np.sum(g * g)))
+    lr_l = lr
+    if trust > 0.0 and wn > 0.0 and gn > 0.0:
+        lr_l = min(lr, trust * wn / gn)
+    return w - lr_l * u, m, v, lr_l
+
+
+# --------------------------------------------------------------- batch norm
+def batchnorm_fwd(x, gamma, beta, eps):
+    """Training-mode batch normalisation of NDHWC x over (N, D, H, W) per
+    channel (Oyama et al., Sec. IV: a batch-normalisation layer after every
+    convolution; Sec. III: its statistics are each channel's sum and sum of
+    squares): mean = sum / M, var = sumsq / M - mean^2 (biased),
+    xhat = (x - mean) / sqrt(var + eps), y = gamma xhat + beta.
+    Returns (y, mean, invstd)."""
+    x = _f64(x)
+    C = x.shape[-1]
+    flat = x.reshape(-1, C)
+    M = flat.shape[0]
+    mean = np.sum(flat, axis=0) / M
+    var = np.sum(flat * flat, axis=0) / M - mean * mean
+    invstd = 1.0 / np.sqrt(var + eps)
+    y = (flat - mean) * invstd * _f64(gamma) + _f64(beta)
+    return y.reshape(x.shape), mean, invstd
+
+
+def batchnorm_bwd(x, dy, gamma, mean, invstd):
+    """Backward of batchnorm_fwd (chain rule through the batch statistics):
+        dbeta = sum dy;  dgamma = sum dy xhat
+        dx = gamma invstd (dy - dbeta / M - xhat dgamma / M).
+    Returns (dx, dgamma, dbeta)."""
+    x, dy = _f64(x), _f64(dy)
+    C = x.shape[-1]
+    fx, fd = x.reshape(-1, C), dy.reshape(-1, C)
+    M = fx.shape[0]
+    xhat = (fx - mean) * invstd
+    dbeta = np.sum(fd, axis=0)
+    dgamma = np.sum(fd * xhat, axis=0)
+    dx = _f64(gamma) * invstd * (fd - dbeta / M - xhat * dgamma / M)
+    return dx.reshape(x.shape), dgamma, dbeta

@@ -32,6 +32,28 @@ def rel_err(g, o):
     return float(np.max(np.abs(g - o)) / rms)
 
 
+def bf16_ulp(o):
+    """One bf16 quantum at each value of o: 2^(e - 7) for |o| in [2^e, 2^(e+1))
+    (8 significant bits), the subnormal spacing 2^-133 below 2^-126."""
+    a = np.abs(np.asarray(o, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def rel_err_bf16(g, o):
+    """rel_err for a tensor that both sides store in bf16: the part of each
+    difference beyond one bf16 quantum at the oracle's value, over RMS(o).
+    Two correct roundings of sums that differ only in their last fp32 bits
+    land one quantum apart; that is not counted as error."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    rms = np.sqrt(np.mean(o * o))
+    excess = np.maximum(np.abs(g - o) - bf16_ulp(o), 0.0)
+    if rms == 0.0:
+        return float(np.max(excess))
+    return float(np.max(excess) / rms)
+
+
 def bf16_elementwise_ok(g, o, rms_frac=2e-3):
     """Each bf16 output within its own rounding (2^-8 relative) plus a small
     accumulation allowance relative to the tensor's RMS."""

@@ -24,8 +24,8 @@ import oracle
 import synthdata as sd
 from cnn_cosmology_volumes_amd import cf
 from cnn_cosmology_volumes_amd.configs import CONFIGS
-from gpu_util import (TOL_BF16, bf16_elementwise_ok, check_pool_indices, host64, kink_mask, rel_err, to_dev,
-                      unpool_neighbourhood_mask)
+from gpu_util import (TOL_BF16, bf16_ulp, check_pool_indices, host64, kink_mask, rel_err, rel_err_bf16,
+                      to_dev, unpool_neighbourhood_mask)
 
 pytestmark = pytest.mark.gpu
 BF, F32 = torch.bfloat16, torch.float32
@@ -63,7 +63,9 @@ def test_block128_chain_matches_oracle():
     diff = check_pool_indices(zo, gi, io, gp, po)
     amb = diff | kink_mask(zo, po, SLOPE)
     del zo
-    assert rel_err(gp, po) <= TOL_BF16
+    # P and dX are bf16 on both sides: the gate counts what lies beyond one
+    # bf16 quantum (rel_err_bf16); dW is an fp32 sum
+    assert rel_err_bf16(gp, po) <= TOL_BF16
     dzo = oracle.round_bf16(oracle.maxpool_lrelu_bwd(dp, po, io, SLOPE))
     # dZ outside the ambiguous windows: the same pooled gradient times the
     # same slope, rounded to bf16 on both sides (the GPU multiplies by the
@@ -75,13 +77,16 @@ def test_block128_chain_matches_oracle():
     del dzo
     e_dw = rel_err(gdw, dwo)
     vmask = ~unpool_neighbourhood_mask(amb)
-    e_dx = rel_err(gdx[vmask], dxo[vmask])
+    e_dx = rel_err_bf16(gdx[vmask], dxo[vmask])
     print("block 4x128^3x4->32 vs oracle chain: %d index differences (near ties), %d kink windows; "
-          "rel err P %.2e, dW %.2e, dX %.2e" % (int(diff.sum()), int((amb & ~diff).sum()), rel_err(gp, po), e_dw,
+          "rel err P %.2e (%.2e counting the quantum), dW %.2e, dX %.2e" % (
+              int(diff.sum()), int((amb & ~diff).sum()), rel_err_bf16(gp, po), rel_err(gp, po), e_dw,
                                                   e_dx))
     assert e_dw <= TOL_BF16
     assert e_dx <= TOL_BF16
-    assert bf16_elementwise_ok(gdx[vmask], dxo[vmask]) == 0
+    # element-wise: one bf16 quantum plus a small accumulation allowance
+    gx, ox = gdx[vmask], dxo[vmask]
+    assert np.all(np.abs(gx - ox) <= bf16_ulp(ox) + 2e-3 * np.sqrt(np.mean(ox * ox)))
 
 
 def train128_problem():
