@@ -45,6 +45,12 @@ class cf_step_aux(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p * CF_MAX_BLOCKS), ("join", ctypes.c_void_p)]
 
 
+class cf_adam_larc_params(ctypes.Structure):
+    _fields_ = [("lr0", ctypes.c_float), ("lr_end", ctypes.c_float), ("decay_steps", ctypes.c_int64),
+                ("power", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("trust", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _SIG = {
     "cf_abi_version": ([], ctypes.c_int32),
@@ -67,6 +73,15 @@ _SIG = {
     "cf_dense_bwd": ([ctypes.c_int32] * 3 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
     "cf_mse": ([ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "cf_sgd": ([ctypes.c_int64, ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "cf_adam_larc_workspace_size": ([ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_size_t),
+    "cf_adam_larc": ([ctypes.POINTER(cf_adam_larc_params), ctypes.c_int64, ctypes.c_int32,
+                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                      ctypes.POINTER(_P), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "cf_batchnorm_workspace_size": ([ctypes.c_int, cf_dims], ctypes.c_size_t),
+    "cf_batchnorm_fwd": ([ctypes.c_int, cf_dims, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                         ctypes.c_int),
+    "cf_batchnorm_bwd": ([ctypes.c_int, cf_dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                         ctypes.c_int),
     "cf_train_step_workspace_size": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32], ctypes.c_size_t),
     "cf_step_aux_create": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
     "cf_step_aux_destroy": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
@@ -349,3 +364,48 @@ def cf_train_step(m, X, targets, params, lr, ws=None, loss=None, pred=None, stre
     check(lib().cf_train_step(ctypes.byref(m), dt, B, _ptr(X), _ptr(targets), arr, float(lr), _ptr(loss), _ptr(pred),
                               _ptr(ws), _wsbytes(ws), _stream(stream), auxp))
     return loss, pred
+
+
+# ---------------------------------------------------------------- optimizer
+def adam_larc_params(lr0, lr_end=None, decay_steps=1, power=1.0, beta1=0.9, beta2=0.999, eps=1e-8, trust=0.0):
+    """cf_adam_larc_params; lr_end defaults to lr0 (no decay)."""
+    return cf_adam_larc_params(float(lr0), float(lr0 if lr_end is None else lr_end), int(decay_steps), float(power),
+                               float(beta1), float(beta2), float(eps), float(trust))
+
+
+def cf_adam_larc(hp, t, params, grads, m, v, lr_out=None, ws=None, stream=None):
+    """Update t (1-based) of the fp32 tensors `params` in place from `grads`,
+    with Adam moments m, v (same shapes, updated in place)."""
+    k = len(params)
+    n = (ctypes.c_int64 * k)(*[p.numel() for p in params])
+    arr = lambda ts: (_P * k)(*[q.data_ptr() for q in ts])
+    ws = _ws(int(lib().cf_adam_larc_workspace_size(k, n)), params[0].device, ws)
+    check(lib().cf_adam_larc(ctypes.byref(hp), int(t), k, n, arr(params), arr(grads), arr(m), arr(v), _ptr(lr_out),
+                             _ptr(ws), _wsbytes(ws), _stream(stream)))
+
+
+# --------------------------------------------------------------- batch norm
+def cf_batchnorm_fwd(X, gamma, beta, eps, Y=None, mean=None, invstd=None, ws=None, stream=None):
+    """Training-mode batch norm of NDHWC X per channel -> (Y, mean, invstd)."""
+    dt = dtype_code(X.dtype)
+    C = int(X.shape[4])
+    Y = torch.empty_like(X) if Y is None else Y
+    mean = torch.empty((C,), dtype=torch.float32, device=X.device) if mean is None else mean
+    invstd = torch.empty((C,), dtype=torch.float32, device=X.device) if invstd is None else invstd
+    ws = _ws(int(lib().cf_batchnorm_workspace_size(dt, dims(X.shape))), X.device, ws)
+    check(lib().cf_batchnorm_fwd(dt, dims(X.shape), _ptr(X), _ptr(gamma), _ptr(beta), float(eps), _ptr(Y), _ptr(mean),
+                                 _ptr(invstd), _ptr(ws), _wsbytes(ws), _stream(stream)))
+    return Y, mean, invstd
+
+
+def cf_batchnorm_bwd(X, dY, gamma, mean, invstd, dX=None, ws=None, stream=None):
+    """-> (dX, dgamma, dbeta)."""
+    dt = dtype_code(X.dtype)
+    C = int(X.shape[4])
+    dX = torch.empty_like(X) if dX is None else dX
+    dgamma = torch.empty((C,), dtype=torch.float32, device=X.device)
+    dbeta = torch.empty((C,), dtype=torch.float32, device=X.device)
+    ws = _ws(int(lib().cf_batchnorm_workspace_size(dt, dims(X.shape))), X.device, ws)
+    check(lib().cf_batchnorm_bwd(dt, dims(X.shape), _ptr(X), _ptr(dY), _ptr(gamma), _ptr(mean), _ptr(invstd),
+                                 _ptr(dX), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _wsbytes(ws), _stream(stream)))
+    return dX, dgamma, dbeta

@@ -7,6 +7,7 @@
 #include "cf_internal.h"
 
 #include <atomic>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -587,6 +588,140 @@ cf_status cf_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t str
     if (n <= 0 || n > kMaxElems) return fail(CF_ERR_INVALID, "cf_sgd: n out of range");
     if (!W || !dW) return fail(CF_ERR_INVALID, "cf_sgd: null pointer");
     CF_TRY_HIP(launch_sgd(n, lr, W, dW, stream), "sgd");
+    return CF_OK;
+}
+
+// ----------------------------------------------------- Adam + LARC + decay
+static cf_status check_opt(const cf_adam_larc_params* hp, int64_t t, int32_t nt, const int64_t* n,
+                           const char* fn)
+{
+    if (!hp || !n) return fail(CF_ERR_INVALID, "%s: null host argument", fn);
+    if (nt < 1 || nt > CF_MAX_OPT_TENSORS)
+        return fail(CF_ERR_INVALID, "%s: ntensors must be 1..%d (got %d)", fn, CF_MAX_OPT_TENSORS, nt);
+    if (t < 1) return fail(CF_ERR_INVALID, "%s: the update count t starts at 1 (got %lld)", fn, (long long)t);
+    if (!(hp->lr0 >= 0.f) || !(hp->lr_end >= 0.f) || hp->decay_steps < 1 || !(hp->power > 0.f))
+        return fail(CF_ERR_INVALID, "%s: decay needs lr0, lr_end >= 0, decay_steps >= 1, power > 0", fn);
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f) || !(hp->eps > 0.f))
+        return fail(CF_ERR_INVALID, "%s: need 0 <= beta1, beta2 < 1 and eps > 0", fn);
+    if (!(hp->trust == hp->trust)) return fail(CF_ERR_INVALID, "%s: trust is NaN", fn);
+    for (int i = 0; i < nt; ++i)
+        if (n[i] <= 0 || n[i] > ((int64_t)1 << 36)) return fail(CF_ERR_INVALID, "%s: n[%d] out of range", fn, i);
+    return CF_OK;
+}
+
+static OptList opt_list(int32_t nt, const int64_t* n, float* const* w, const float* const* g, float* const* m,
+                        float* const* v)
+{
+    OptList l{};
+    l.count = nt;
+    for (int i = 0; i < nt; ++i) {
+        l.n[i] = n[i];
+        if (w) { l.w[i] = w[i]; l.g[i] = g[i]; l.m[i] = m[i]; l.v[i] = v[i]; }
+    }
+    return l;
+}
+
+// The decayed rate after `done` completed updates, in fp64.
+static double decayed_rate(const cf_adam_larc_params* hp, int64_t done)
+{
+    const double T = (double)hp->decay_steps;
+    const double s = done < hp->decay_steps ? (double)done : T;
+    return ((double)hp->lr0 - (double)hp->lr_end) * pow(1.0 - s / T, (double)hp->power) + (double)hp->lr_end;
+}
+
+size_t cf_adam_larc_workspace_size(int32_t ntensors, const int64_t* n)
+{
+    if (ntensors < 1 || ntensors > CF_MAX_OPT_TENSORS || !n) return 0;
+    for (int i = 0; i < ntensors; ++i)
+        if (n[i] <= 0 || n[i] > ((int64_t)1 << 36)) return 0;
+    return up256(adam_larc_part_bytes(opt_list(ntensors, n, nullptr, nullptr, nullptr, nullptr)));
+}
+
+cf_status cf_adam_larc(const cf_adam_larc_params* hp, int64_t t, int32_t ntensors, const int64_t* n, float* const* w,
+                       const float* const* g, float* const* m, float* const* v, float* lr_out, void* ws,
+                       size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_opt(hp, t, ntensors, n, "cf_adam_larc");
+    if (st != CF_OK) return st;
+    if (!w || !g || !m || !v) return fail(CF_ERR_INVALID, "cf_adam_larc: null tensor array");
+    for (int i = 0; i < ntensors; ++i)
+        if (!w[i] || !g[i] || !m[i] || !v[i] || !al16(w[i]) || !al16(g[i]) || !al16(m[i]) || !al16(v[i]))
+            return fail(CF_ERR_INVALID, "cf_adam_larc: tensor %d has a null or misaligned pointer", i);
+    if (lr_out && !al16(lr_out)) return fail(CF_ERR_INVALID, "cf_adam_larc: lr_out must be 16-byte aligned");
+    const OptList l = opt_list(ntensors, n, w, g, m, v);
+    const size_t need = up256(adam_larc_part_bytes(l));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_adam_larc: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_adam_larc: workspace null or misaligned");
+    AdamArgs a{};
+    a.lr = (float)decayed_rate(hp, t - 1);
+    a.beta1 = hp->beta1;
+    a.omb1 = (float)(1.0 - (double)hp->beta1);
+    a.beta2 = hp->beta2;
+    a.omb2 = (float)(1.0 - (double)hp->beta2);
+    a.bc1 = (float)(1.0 / (1.0 - pow((double)hp->beta1, (double)t)));
+    a.bc2 = (float)(1.0 / (1.0 - pow((double)hp->beta2, (double)t)));
+    a.eps = hp->eps;
+    a.trust = hp->trust;
+    CF_TRY_HIP(launch_adam_larc(l, a, (float*)ws, lr_out, stream), "adam + larc");
+    return CF_OK;
+}
+
+// ------------------------------------------------------------- batch norm
+static cf_status check_bn(cf_dtype dtype, const cf_dims& x, const char* fn)
+{
+    cf_status st = check_dtype(dtype);
+    if (st != CF_OK) return st;
+    if ((st = check_dims(x, "x")) != CF_OK) return st;
+    if (x.c % 4 || x.c > 1024) return fail(CF_ERR_UNSUPPORTED, "%s: channels must be a multiple of 4, at most 1024", fn);
+    return CF_OK;
+}
+
+size_t cf_batchnorm_workspace_size(cf_dtype dtype, cf_dims x)
+{
+    if (check_bn(dtype, x, "cf_batchnorm_workspace_size") != CF_OK) return 0;
+    return bn_ws_bytes(x);
+}
+
+cf_status cf_batchnorm_fwd(cf_dtype dtype, cf_dims x, const void* X, const float* gamma, const float* beta, float eps,
+                           void* Y, float* mean, float* invstd, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_bn(dtype, x, "cf_batchnorm_fwd");
+    if (st != CF_OK) return st;
+    if (!X || !gamma || !beta || !Y || !mean || !invstd) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: null pointer");
+    if (!al16(X) || !al16(gamma) || !al16(beta) || !al16(Y) || !al16(mean) || !al16(invstd))
+        return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: pointers must be 16-byte aligned");
+    if (!(eps >= 0.f)) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: eps must be >= 0");
+    const size_t need = bn_ws_bytes(x);
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_batchnorm_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: workspace null or misaligned");
+    hipError_t e = dtype == CF_F32
+                       ? launch_bn_fwd<float>((const float*)X, gamma, beta, eps, (float*)Y, mean, invstd, x, ws, stream)
+                       : launch_bn_fwd<uint16_t>((const uint16_t*)X, gamma, beta, eps, (uint16_t*)Y, mean, invstd, x,
+                                                 ws, stream);
+    CF_TRY_HIP(e, "batch norm forward");
+    return CF_OK;
+}
+
+cf_status cf_batchnorm_bwd(cf_dtype dtype, cf_dims x, const void* X, const void* dY, const float* gamma,
+                           const float* mean, const float* invstd, void* dX, float* dgamma, float* dbeta, void* ws,
+                           size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_bn(dtype, x, "cf_batchnorm_bwd");
+    if (st != CF_OK) return st;
+    if (!X || !dY || !gamma || !mean || !invstd || !dX || !dgamma || !dbeta)
+        return fail(CF_ERR_INVALID, "cf_batchnorm_bwd: null pointer");
+    if (!al16(X) || !al16(dY) || !al16(gamma) || !al16(mean) || !al16(invstd) || !al16(dX) || !al16(dgamma) ||
+        !al16(dbeta))
+        return fail(CF_ERR_INVALID, "cf_batchnorm_bwd: pointers must be 16-byte aligned");
+    const size_t need = bn_ws_bytes(x);
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_batchnorm_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_batchnorm_bwd: workspace null or misaligned");
+    hipError_t e = dtype == CF_F32
+                       ? launch_bn_bwd<float>((const float*)X, (const float*)dY, gamma, mean, invstd, (float*)dX,
+                                              dgamma, dbeta, x, ws, stream)
+                       : launch_bn_bwd<uint16_t>((const uint16_t*)X, (const uint16_t*)dY, gamma, mean, invstd,
+                                                 (uint16_t*)dX, dgamma, dbeta, x, ws, stream);
+    CF_TRY_HIP(e, "batch norm backward");
     return CF_OK;
 }
 

@@ -225,4 +225,35 @@ struct SgdList {
 hipError_t launch_sgd_multi(const SgdList& l, float lr, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 
+// Adam + LARC over up to CF_MAX_OPT_TENSORS fp32 tensors (k_optim.hip).
+struct OptList {
+    int count;
+    float* w[CF_MAX_OPT_TENSORS];
+    const float* g[CF_MAX_OPT_TENSORS];
+    float* m[CF_MAX_OPT_TENSORS];
+    float* v[CF_MAX_OPT_TENSORS];
+    int64_t n[CF_MAX_OPT_TENSORS];
+    int start[CF_MAX_OPT_TENSORS + 1];   // first block of each tensor (set by the launcher)
+};
+// Per-update scalars, computed on the host in fp64 and rounded to fp32.
+struct AdamArgs {
+    float lr;               // decayed nominal rate of this update
+    float beta1, omb1;      // beta1 and 1 - beta1
+    float beta2, omb2;      // beta2 and 1 - beta2
+    float bc1, bc2;         // 1 / (1 - beta1^t), 1 / (1 - beta2^t)
+    float eps, trust;
+};
+size_t adam_larc_part_bytes(const OptList& l);
+hipError_t launch_adam_larc(const OptList& l, const AdamArgs& a, float* part, float* lr_out, hipStream_t s);
+
+// Training-mode batch normalisation over (N, D, H, W) per channel of an
+// NDHWC tensor, C % 4 == 0 (k_bn.hip).  T = float or uint16_t (bf16).
+size_t bn_ws_bytes(const cf_dims& x);
+template <typename T>
+hipError_t launch_bn_fwd(const T* X, const float* gamma, const float* beta, float eps, T* Y, float* mean,
+                         float* invstd, const cf_dims& x, void* ws, hipStream_t s);
+template <typename T>
+hipError_t launch_bn_bwd(const T* X, const T* dY, const float* gamma, const float* mean, const float* invstd, T* dX,
+                         float* dgamma, float* dbeta, const cf_dims& x, void* ws, hipStream_t s);
+
 }  // namespace cf

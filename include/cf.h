@@ -53,6 +53,7 @@ extern "C" {
 
 #define CF_ABI_VERSION 2
 #define CF_MAX_BLOCKS 8
+#define CF_MAX_OPT_TENSORS 32
 
 typedef enum {
     CF_OK = 0,
@@ -244,6 +245,66 @@ cf_status cf_mse(int32_t B, int32_t K, const float* yhat, const float* t, float*
 
 /* SGD update W <- W - lr * dW on n fp32 values ([OY] Sec. II-A). */
 cf_status cf_sgd(int64_t n, float lr, float* W, const float* dW, hipStream_t stream);
+
+/* ------------------------------------------ Adam + LARC + polynomial decay */
+
+/* Optimizer of [CF] Sec. III-B (Adam with LARC and polynomial decay of
+ * power 1) and [OY] Sec. IV (Adam, beta1 0.9, beta2 0.999, eps 1e-8, linear
+ * decay to 0.01x of the initial rate). */
+typedef struct {
+    float lr0;            /* initial nominal rate */
+    float lr_end;         /* rate reached after decay_steps updates */
+    int64_t decay_steps;  /* >= 1 */
+    float power;          /* polynomial power, > 0 (1 = linear) */
+    float beta1, beta2;   /* in [0, 1) */
+    float eps;            /* > 0 */
+    float trust;          /* LARC trust coefficient; <= 0 turns LARC off */
+} cf_adam_larc_params;
+
+/* Workspace bytes for cf_adam_larc over tensors of these sizes (HOST array). */
+size_t cf_adam_larc_workspace_size(int32_t ntensors, const int64_t* n);
+
+/* Update t (1-based) of ntensors fp32 parameter tensors, each one "layer":
+ *   rate   lr_t = (lr0 - lr_end) (1 - min(t-1, T)/T)^power + lr_end
+ *   Adam   m <- beta1 m + (1-beta1) g;  v <- beta2 v + (1-beta2) g^2
+ *          u = (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)
+ *   LARC   lr_l = min(lr_t, trust ||w|| / ||g||), or lr_t when trust <= 0
+ *          or either norm is 0 (norms over the tensor before the update)
+ *          w <- w - lr_l u
+ * n, w, g, m, v are HOST arrays of ntensors entries (1..CF_MAX_OPT_TENSORS);
+ * w, g, m, v entries are DEVICE pointers to n[i] floats (w, m, v updated in
+ * place; m and v start at zero before t = 1).  lr_out: NULL or a device
+ * array receiving each tensor's lr_l.  The norms are reduced in a fixed
+ * order: results are reproducible bit for bit. */
+cf_status cf_adam_larc(const cf_adam_larc_params* hp, int64_t t, int32_t ntensors, const int64_t* n,
+                       float* const* w, const float* const* g, float* const* m, float* const* v,
+                       float* lr_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ batch norm */
+
+/* Workspace bytes for cf_batchnorm_fwd / cf_batchnorm_bwd on x. */
+size_t cf_batchnorm_workspace_size(cf_dtype dtype, cf_dims x);
+
+/* Training-mode batch normalisation ([OY] Sec. IV: after every convolution;
+ * Sec. III: the per-channel sum and sum of squares are its statistics) over
+ * (n, d, h, w) for each channel c of an NDHWC tensor:
+ *   mean = sum x / M, var = sum x^2 / M - mean^2 (biased), M = n*d*h*w
+ *   invstd = 1 / sqrt(var + eps);  Y = (X - mean) * gamma * invstd + beta
+ *   X, Y [x.n, x.d, x.h, x.w, x.c] (dtype); gamma, beta, mean, invstd [x.c]
+ *   fp32 (mean and invstd are outputs, for the backward).
+ * x.c must be a multiple of 4 and at most 1024 (else CF_ERR_UNSUPPORTED).
+ * Statistics are reduced in a fixed order (fp64 across blocks). */
+cf_status cf_batchnorm_fwd(cf_dtype dtype, cf_dims x, const void* X, const float* gamma, const float* beta,
+                           float eps, void* Y, float* mean, float* invstd, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Backward of cf_batchnorm_fwd (chain rule through the batch statistics),
+ * with xhat = (X - mean) * invstd from the forward's mean and invstd:
+ *   dbeta = sum dY;  dgamma = sum dY xhat
+ *   dX = gamma invstd (dY - dbeta / M - xhat dgamma / M) */
+cf_status cf_batchnorm_bwd(cf_dtype dtype, cf_dims x, const void* X, const void* dY, const float* gamma,
+                           const float* mean, const float* invstd, void* dX, float* dgamma, float* dbeta,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------- training step */
 

@@ -56,6 +56,11 @@ def lib():
             "or_dense_bwd": ([_i64] * 3 + [_P, _P, _P, _P, _dbl, _P, _P, _P], None),
             "or_mse": ([_i64, _i64, _P, _P, _P], _dbl),
             "or_sgd": ([_i64, _dbl, _P, _P], None),
+            "or_conv3d_fwd_s": ([_i64] * 11 + [_P, _P, _P], None),
+            "or_conv3d_bwd_data_s": ([_i64] * 11 + [_P, _P, _P], None),
+            "or_conv3d_bwd_weight_s": ([_i64] * 11 + [_P, _P, _P], None),
+            "or_avgpool_fwd": ([_i64] * 5 + [_P, _P], None),
+            "or_avgpool_bwd": ([_i64] * 5 + [_P, _P], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -180,6 +185,71 @@ def conv3d_bwd_weight_points(x32, dy32, pts):
     return out
 
 
+# ------------------------------------------------ strided "same" conv
+def same_geometry(size, stride, k=3):
+    """TensorFlow's "same" padding (the padding of every layer in Oyama et
+    al., Table I) for one dimension: output ceil(size / stride), total
+    padding max((out - 1) * stride + k - size, 0), of which the low side
+    gets the floor of half.  Returns (out, pad_low)."""
+    out = -(-size // stride)
+    total = max((out - 1) * stride + k - size, 0)
+    return out, total // 2
+
+
+def conv3d_fwd_s(x, w, stride):
+    """x [N,D,H,W,Ci], w [3,3,3,Ci,Co] -> y [N,Do,Ho,Wo,Co], 3^3 kernel,
+    given stride, "same" padding (same_geometry; cubic volumes)."""
+    x, w = _f64(x), _f64(w)
+    N, D, H, W, Ci = x.shape
+    assert D == H == W
+    Co = w.shape[4]
+    o, p = same_geometry(D, stride)
+    y = np.empty((N, o, o, o, Co), np.float64)
+    lib().or_conv3d_fwd_s(N, D, H, W, Ci, Co, stride, p, o, o, o, _ptr(x), _ptr(w), _ptr(y))
+    return y
+
+
+def conv3d_bwd_data_s(dy, w, stride, in_size):
+    dy, w = _f64(dy), _f64(w)
+    N, o, _, _, Co = dy.shape
+    Ci = w.shape[3]
+    o2, p = same_geometry(in_size, stride)
+    assert o2 == o
+    dx = np.empty((N, in_size, in_size, in_size, Ci), np.float64)
+    lib().or_conv3d_bwd_data_s(N, in_size, in_size, in_size, Ci, Co, stride, p, o, o, o, _ptr(dy), _ptr(w), _ptr(dx))
+    return dx
+
+
+def conv3d_bwd_weight_s(x, dy, stride):
+    x, dy = _f64(x), _f64(dy)
+    N, D, H, W, Ci = x.shape
+    Co = dy.shape[4]
+    o, p = same_geometry(D, stride)
+    assert dy.shape[1:4] == (o, o, o)
+    dw = np.empty((3, 3, 3, Ci, Co), np.float64)
+    lib().or_conv3d_bwd_weight_s(N, D, H, W, Ci, Co, stride, p, o, o, o, _ptr(x), _ptr(dy), _ptr(dw))
+    return dw
+
+
+# ------------------------------------------------------------ average pool
+def avgpool_fwd(z):
+    """2^3 stride-2 average pool, weights 1/8: z [N,D,H,W,C] -> [N,D/2,H/2,W/2,C]."""
+    z = _f64(z)
+    N, D, H, W, C = z.shape
+    assert D % 2 == 0 and H % 2 == 0 and W % 2 == 0
+    p = np.empty((N, D // 2, H // 2, W // 2, C), np.float64)
+    lib().or_avgpool_fwd(N, D, H, W, C, _ptr(z), _ptr(p))
+    return p
+
+
+def avgpool_bwd(dp):
+    dp = _f64(dp)
+    N, Dp, Hp, Wp, C = dp.shape
+    dz = np.empty((N, 2 * Dp, 2 * Hp, 2 * Wp, C), np.float64)
+    lib().or_avgpool_bwd(N, 2 * Dp, 2 * Hp, 2 * Wp, C, _ptr(dp), _ptr(dz))
+    return dz
+
+
 # ------------------------------------------------------------- activations
 def lrelu_fwd(x, slope):
     x = _f64(x)
@@ -258,16 +328,26 @@ def sgd(w, dw, lr):
 
 
 # ------------------------------------------------------------------ network
-def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None):
+def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None, perturb=None):
     """Forward pass of the conv stack and the dense head.
 
     x [B,D,H,W,Cin]; conv_w list of [3,3,3,Ci,Co]; dense_w list of three
     (W [In,Out], b [Out]).  Returns (yhat, cache).  If ``trace`` is a dict,
-    each block's stored conv output is appended to trace["z"]."""
+    each block's stored conv output is appended to trace["z"].
+
+    ``perturb`` = (numpy Generator, r) is a conditioning probe, not part of
+    the method: every conv sum is multiplied by (1 + r u), u ~ U(-1, 1), before
+    its storage rounding, as an fp32 accumulation error of relative size r
+    would move it.  Comparing a perturbed run with an unperturbed one shows
+    how far the step's results are determined by the arithmetic at all."""
     a = store(x, storage)
     blocks = []
     for w in conv_w:
-        z = store(conv3d_fwd(a, w), storage)
+        z = conv3d_fwd(a, w)
+        if perturb is not None:
+            g, r = perturb
+            z *= 1.0 + r * g.uniform(-1.0, 1.0, z.shape)
+        z = store(z, storage)
         if trace is not None:
             trace.setdefault("z", []).append(z)
         p, idx = lrelu_maxpool_fwd(z, slope)
@@ -313,19 +393,19 @@ def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_
     return conv_g, dense_g
 
 
-def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64", trace=None):
+def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64", trace=None, perturb=None):
     """One full step.  Weights used in the passes are the masters rounded to
     the storage precision (bf16 for the conv weights of the bf16 path); the
     update is applied to the fp32/fp64 masters.  ``trace``: as for
     network_forward / network_backward, plus trace["conv_w"], the conv
-    weights the passes used.
+    weights the passes used.  ``perturb``: as for network_forward.
 
     Returns dict(loss, yhat, conv_w, dense_w, conv_dw, dense_g)."""
     conv_use = [store(w, storage) for w in conv_w32]
     if trace is not None:
         trace["conv_w"] = conv_use
     dense_use = [(_f64(W), _f64(b)) for W, b in dense_w32]
-    yhat, cache = network_forward(x, conv_use, dense_use, slope, storage, trace=trace)
+    yhat, cache = network_forward(x, conv_use, dense_use, slope, storage, trace=trace, perturb=perturb)
     loss, dy = mse(yhat, targets)
     conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage, trace=trace)
     master = "f64" if storage == "f64" else "f32"

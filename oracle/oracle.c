@@ -393,3 +393,120 @@ void or_sgd(i64 n, double lr, double* w, const double* dw)
     #pragma omp parallel for schedule(static)
     for (i64 i = 0; i < n; ++i) w[i] -= lr * dw[i];
 }
+
+/* ------------------------------------------------ strided conv3d, any pad
+ * The convolution with stride s and low-side zero padding p (the extended
+ * network of Oyama et al., Table I, has one stride-2 convolution, c4, with
+ * "same" padding):
+ * Y[n,od,oh,ow,co] = sum_{kd,kh,kw in 0..2} sum_ci
+ *                      X[n, s*od+kd-p, s*oh+kh-p, s*ow+kw-p, ci] * Wt[kd,kh,kw,ci,co]
+ * X [N,D,H,W,Ci] read as zero outside the volume; Y [N,Do,Ho,Wo,Co].
+ * With s = 1, p = 1, Do = D (etc.) this is or_conv3d_fwd. */
+void or_conv3d_fwd_s(i64 N, i64 D, i64 H, i64 W, i64 Ci, i64 Co, i64 s, i64 p,
+                     i64 Do, i64 Ho, i64 Wo, const double* X, const double* Wt, double* Y)
+{
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+    for (i64 od = 0; od < Do; ++od)
+    for (i64 oh = 0; oh < Ho; ++oh)
+    for (i64 ow = 0; ow < Wo; ++ow)
+    for (i64 co = 0; co < Co; ++co) {
+        double acc = 0.0;
+        for (i64 kd = 0; kd < 3; ++kd)
+        for (i64 kh = 0; kh < 3; ++kh)
+        for (i64 kw = 0; kw < 3; ++kw) {
+            i64 id = s * od + kd - p, ih = s * oh + kh - p, iw = s * ow + kw - p;
+            if (!in_range(id, D) || !in_range(ih, H) || !in_range(iw, W)) continue;
+            const double* xp = X + vox_index(n, id, ih, iw, D, H, W) * Ci;
+            const double* wp = Wt + ((kd * 3 + kh) * 3 + kw) * Ci * Co + co;
+            for (i64 ci = 0; ci < Ci; ++ci) acc += xp[ci] * wp[ci * Co];
+        }
+        Y[vox_index(n, od, oh, ow, Do, Ho, Wo) * Co + co] = acc;
+    }
+}
+
+/* Adjoint in X: input voxel i received tap k from output voxel o exactly
+ * when s*o + k - p = i, i.e. o = (i + p - k) / s with no remainder. */
+void or_conv3d_bwd_data_s(i64 N, i64 D, i64 H, i64 W, i64 Ci, i64 Co, i64 s, i64 p,
+                          i64 Do, i64 Ho, i64 Wo, const double* dY, const double* Wt, double* dX)
+{
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+    for (i64 d = 0; d < D; ++d)
+    for (i64 h = 0; h < H; ++h)
+    for (i64 w = 0; w < W; ++w)
+    for (i64 ci = 0; ci < Ci; ++ci) {
+        double acc = 0.0;
+        for (i64 kd = 0; kd < 3; ++kd)
+        for (i64 kh = 0; kh < 3; ++kh)
+        for (i64 kw = 0; kw < 3; ++kw) {
+            i64 td = d + p - kd, th = h + p - kh, tw = w + p - kw;
+            if (td < 0 || th < 0 || tw < 0 || td % s || th % s || tw % s) continue;
+            i64 od = td / s, oh = th / s, ow = tw / s;
+            if (od >= Do || oh >= Ho || ow >= Wo) continue;
+            const double* gp = dY + vox_index(n, od, oh, ow, Do, Ho, Wo) * Co;
+            const double* wp = Wt + (((kd * 3 + kh) * 3 + kw) * Ci + ci) * Co;
+            for (i64 co = 0; co < Co; ++co) acc += gp[co] * wp[co];
+        }
+        dX[vox_index(n, d, h, w, D, H, W) * Ci + ci] = acc;
+    }
+}
+
+/* Adjoint in Wt: dW[kd,kh,kw,ci,co] = sum_{n,o} X[n, s*o+k-p, ci] * dY[n, o, co]. */
+void or_conv3d_bwd_weight_s(i64 N, i64 D, i64 H, i64 W, i64 Ci, i64 Co, i64 s, i64 p,
+                            i64 Do, i64 Ho, i64 Wo, const double* X, const double* dY, double* dW)
+{
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (i64 t = 0; t < 27; ++t)
+    for (i64 ci = 0; ci < Ci; ++ci) {
+        i64 kd = t / 9, kh = (t / 3) % 3, kw = t % 3;
+        for (i64 co = 0; co < Co; ++co) {
+            double acc = 0.0;
+            for (i64 n = 0; n < N; ++n)
+            for (i64 od = 0; od < Do; ++od)
+            for (i64 oh = 0; oh < Ho; ++oh)
+            for (i64 ow = 0; ow < Wo; ++ow) {
+                i64 id = s * od + kd - p, ih = s * oh + kh - p, iw = s * ow + kw - p;
+                if (!in_range(id, D) || !in_range(ih, H) || !in_range(iw, W)) continue;
+                acc += X[vox_index(n, id, ih, iw, D, H, W) * Ci + ci]
+                     * dY[vox_index(n, od, oh, ow, Do, Ho, Wo) * Co + co];
+            }
+            dW[(t * Ci + ci) * Co + co] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------- 2^3 average pooling
+ * CosmoFlow, Sec. III-A and III-C: stride-2 average pooling, each channel
+ * separately, constant weights 1/(KS)^3 = 1/8 for KS = 2:
+ * P[n,i,j,k,c] = (1/8) sum_{a,b,e in {0,1}} Z[n,2i+a,2j+b,2k+e,c]. */
+void or_avgpool_fwd(i64 N, i64 D, i64 H, i64 W, i64 C, const double* Z, double* P)
+{
+    i64 Dp = D / 2, Hp = H / 2, Wp = W / 2;
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+    for (i64 i = 0; i < Dp; ++i)
+    for (i64 j = 0; j < Hp; ++j)
+    for (i64 k = 0; k < Wp; ++k)
+    for (i64 c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (i64 a = 0; a < 2; ++a)
+        for (i64 b = 0; b < 2; ++b)
+        for (i64 e = 0; e < 2; ++e)
+            acc += Z[vox_index(n, 2 * i + a, 2 * j + b, 2 * k + e, D, H, W) * C + c];
+        P[vox_index(n, i, j, k, Dp, Hp, Wp) * C + c] = acc / 8.0;
+    }
+}
+
+/* Backward: every window position receives dP / 8. */
+void or_avgpool_bwd(i64 N, i64 D, i64 H, i64 W, i64 C, const double* dP, double* dZ)
+{
+    i64 Dp = D / 2, Hp = H / 2, Wp = W / 2;
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+    for (i64 d = 0; d < D; ++d)
+    for (i64 h = 0; h < H; ++h)
+    for (i64 w = 0; w < W; ++w)
+    for (i64 c = 0; c < C; ++c)
+        dZ[vox_index(n, d, h, w, D, H, W) * C + c] = dP[vox_index(n, d / 2, h / 2, w / 2, Dp, Hp, Wp) * C + c] / 8.0;
+}

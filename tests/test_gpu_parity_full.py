@@ -105,8 +105,22 @@ def train128_problem():
     return c, x, conv, dense, t
 
 
+# Relative size of the conditioning perturbation of the oracle's conv sums:
+# about the fp32 accumulation error of the GPU's K = 27 * Cin term sums.
+PERTURB = 2.0 ** -22
+
+
 @pytest.mark.timeout(1200)
 def test_train128_step_matches_oracle_end_to_end():
+    """The untied 5-block step.  Loss and predictions are continuous in the
+    forward's roundings and are gated at 2e-2.  The weight gradients are
+    not determined that closely by the arithmetic itself: GPU and oracle
+    round their conv sums to bf16 from different accumulations, the rare
+    one-ulp disagreements compound over five bf16 layers, and in the deep
+    layers they flip near-tied pool decisions, each of which reroutes a
+    window's gradient.  Two oracle runs whose conv sums are perturbed by
+    PERTURB (seeded, before rounding) measure that spread; each gradient must
+    be within max(2e-2, 2 x spread) of the unperturbed oracle."""
     from test_gpu_train import device_params
     c, x, conv, dense, t = train128_problem()
     m = cf.model_desc(4, c.in_size, c.filters, c.dense, SLOPE)
@@ -122,15 +136,29 @@ def test_train128_step_matches_oracle_end_to_end():
     del params
     torch.cuda.empty_cache()
 
-    ref = oracle.train_step(x, t, conv, dense, LR_RECOVER, SLOPE, storage="bf16")
     L = len(c.filters)
-    errs = {"loss": abs(g_loss - ref["loss"]) / abs(ref["loss"]), "pred": rel_err(g_pred, ref["yhat"])}
-    for l in range(L):
-        errs["conv%d_dW" % (l + 1)] = rel_err(grads[l], ref["conv_dw"][l])
+
+    def flat(r):
+        out = [r["conv_dw"][l] for l in range(L)]
+        for k in range(3):
+            out += [r["dense_g"][k][0], r["dense_g"][k][1]]
+        return out
+
+    names = ["conv%d_dW" % (l + 1) for l in range(L)]
     for k in range(3):
-        errs["dense%d_dW" % (k + 1)] = rel_err(grads[L + 2 * k], ref["dense_g"][k][0])
-        errs["dense%d_db" % (k + 1)] = rel_err(grads[L + 2 * k + 1], ref["dense_g"][k][1])
-    print("train step 8x128^3x4 vs oracle (untied, bf16 storage): " +
-          ", ".join("%s %.2e" % kv for kv in errs.items()))
-    bad = {k: v for k, v in errs.items() if not v <= TOL_BF16}
+        names += ["dense%d_dW" % (k + 1), "dense%d_db" % (k + 1)]
+    ref = oracle.train_step(x, t, conv, dense, LR_RECOVER, SLOPE, storage="bf16")
+    spread = [0.0] * len(names)
+    for seed in (1, 2):
+        alt = oracle.train_step(x, t, conv, dense, LR_RECOVER, SLOPE, storage="bf16",
+                                perturb=(np.random.default_rng(seed), PERTURB))
+        spread = [max(s, rel_err(a, r)) for s, a, r in zip(spread, flat(alt), flat(ref))]
+        del alt
+    e_loss = abs(g_loss - ref["loss"]) / abs(ref["loss"])
+    e_pred = rel_err(g_pred, ref["yhat"])
+    errs = [rel_err(g, r) for g, r in zip(grads, flat(ref))]
+    print("train step 8x128^3x4 vs oracle (untied, bf16 storage): loss %.2e, pred %.2e; " % (e_loss, e_pred) +
+          ", ".join("%s %.2e (oracle spread %.2e)" % (n, e, s) for n, e, s in zip(names, errs, spread)))
+    assert e_loss <= TOL_BF16 and e_pred <= TOL_BF16
+    bad = {n: (e, s) for n, e, s in zip(names, errs, spread) if not e <= max(TOL_BF16, 2.0 * s)}
     assert not bad, bad
