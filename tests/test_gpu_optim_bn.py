@@ -28,6 +28,9 @@ def test_adam_larc_matches_oracle_over_steps(trust):
     rng = np.random.default_rng(11 + int(trust * 100))
     ws = [(rng.standard_normal(n) * rng.uniform(0.05, 2.0)).astype(np.float32) for n in SIZES]
     hp = cf.adam_larc_params(0.05, lr_end=0.0005, decay_steps=4, power=1.0, trust=trust)
+    # the oracle gets the hyperparameters as the GPU receives them (fp32)
+    f = lambda v: float(np.float32(v))
+    b1, b2, eps, tr = f(0.9), f(0.999), f(1e-8), f(trust)
     wd = [torch.from_numpy(w.copy()).cuda() for w in ws]
     md = [torch.zeros_like(w) for w in wd]
     vd = [torch.zeros_like(w) for w in wd]
@@ -40,14 +43,13 @@ def test_adam_larc_matches_oracle_over_steps(trust):
         gd = [torch.from_numpy(g).cuda() for g in gs]
         cf.cf_adam_larc(hp, t, wd, gd, md, vd, lr_out=lr_out)
         torch.cuda.synchronize()
-        lr_t = oracle.poly_decay(0.05, 0.0005, 4, 1.0, t - 1)
+        lr_t = oracle.poly_decay(f(0.05), f(0.0005), 4, 1.0, t - 1)
         lrs = []
         for i in range(len(SIZES)):
             # the oracle continues from the GPU's fp32 state, so each update
             # is compared on its own (no drift between fp32 and fp64 state)
             w_prev = wo[i]
-            wo[i], mo[i], vo[i], lr_l = oracle.adam_larc_step(w_prev, gs[i], mo[i], vo[i], t, lr_t, 0.9, 0.999,
-                                                              1e-8, trust)
+            wo[i], mo[i], vo[i], lr_l = oracle.adam_larc_step(w_prev, gs[i], mo[i], vo[i], t, lr_t, b1, b2, eps, tr)
             lrs.append(lr_l)
             assert rel_err(host64(md[i]), mo[i]) <= TOL_F32, (t, i)
             assert rel_err(host64(vd[i]), vo[i]) <= TOL_F32, (t, i)
