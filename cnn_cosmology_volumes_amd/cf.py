@@ -17,6 +17,7 @@ CF_OK, CF_ERR_INVALID, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_HIP = 0, -1,
 CF_F32, CF_BF16 = 0, 1
 CF_CONV_FWD, CF_CONV_BWD_DATA, CF_CONV_BWD_WEIGHT, CF_CONV_POOL_FWD, CF_POOL_CONV_BWD_WEIGHT = 0, 1, 2, 3, 4
 CF_MAX_BLOCKS = 8
+CF_MAX_OPT_TENSORS = 32
 
 
 class CfError(RuntimeError):
@@ -51,6 +52,24 @@ class cf_adam_larc_params(ctypes.Structure):
                 ("eps", ctypes.c_float), ("trust", ctypes.c_float)]
 
 
+CF_MAX_DENSE = 4
+CF_POOL_MAX, CF_POOL_AVG, CF_POOL_NONE = 0, 1, 2
+CF_OPT_SGD, CF_OPT_ADAM_LARC = 0, 1
+
+
+class cf_net_desc(ctypes.Structure):
+    _fields_ = [("nlayers", ctypes.c_int32), ("cin", ctypes.c_int32), ("d", ctypes.c_int32), ("h", ctypes.c_int32),
+                ("w", ctypes.c_int32), ("filters", ctypes.c_int32 * CF_MAX_BLOCKS),
+                ("stride", ctypes.c_int32 * CF_MAX_BLOCKS), ("pool", ctypes.c_int32 * CF_MAX_BLOCKS),
+                ("batch_norm", ctypes.c_int32), ("bn_eps", ctypes.c_float), ("ndense", ctypes.c_int32),
+                ("dense", ctypes.c_int32 * CF_MAX_DENSE), ("dense_bias", ctypes.c_int32), ("slope", ctypes.c_float)]
+
+
+class cf_optimizer(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_float), ("adam", cf_adam_larc_params),
+                ("t", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _SIG = {
     "cf_abi_version": ([], ctypes.c_int32),
@@ -67,6 +86,8 @@ _SIG = {
                                    _P, ctypes.c_size_t, _P], ctypes.c_int),
     "cf_pool3d_fwd": ([ctypes.c_int, cf_dims, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "cf_pool3d_bwd": ([ctypes.c_int, cf_dims, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "cf_avgpool3d_fwd": ([ctypes.c_int, cf_dims, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "cf_avgpool3d_bwd": ([ctypes.c_int, cf_dims, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "cf_lrelu": ([ctypes.c_int, ctypes.c_int64, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "cf_dense_workspace_size": ([ctypes.c_int32] * 3, ctypes.c_size_t),
     "cf_dense_fwd": ([ctypes.c_int32] * 3 + [_P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -82,6 +103,11 @@ _SIG = {
                          ctypes.c_int),
     "cf_batchnorm_bwd": ([ctypes.c_int, cf_dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                          ctypes.c_int),
+    "cf_net_param_count": ([ctypes.POINTER(cf_net_desc), ctypes.POINTER(ctypes.c_int64)], ctypes.c_int32),
+    "cf_net_train_step_workspace_size": ([ctypes.POINTER(cf_net_desc), ctypes.c_int, ctypes.c_int32], ctypes.c_size_t),
+    "cf_net_train_step": ([ctypes.POINTER(cf_net_desc), ctypes.c_int, ctypes.c_int32, _P, _P, ctypes.POINTER(_P),
+                           ctypes.POINTER(cf_optimizer), ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P, _P,
+                           ctypes.c_size_t, _P], ctypes.c_int),
     "cf_train_step_workspace_size": ([ctypes.POINTER(cf_model_desc), ctypes.c_int, ctypes.c_int32], ctypes.c_size_t),
     "cf_step_aux_create": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
     "cf_step_aux_destroy": ([ctypes.POINTER(cf_step_aux)], ctypes.c_int),
@@ -143,6 +169,21 @@ def dims(shape) -> cf_dims:
 CONV3 = cf_conv(3, 1, 1)
 
 
+def conv_geometry(stride, size):
+    """cf_conv for a 3^3 convolution of the given stride with "same" padding
+    on a volume whose sizes have the parity of `size`."""
+    if stride == 1:
+        return CONV3
+    return cf_conv(3, 2, int(size) & 1)
+
+
+def out_shape(shape, cout, stride):
+    n, d, h, w, _ = (int(v) for v in shape)
+    if stride == 1:
+        return (n, d, h, w, cout)
+    return (n, (d + 1) // 2, (h + 1) // 2, (w + 1) // 2, cout)
+
+
 def _ws(nbytes, device, ws=None):
     if nbytes == 0:
         return ws
@@ -156,44 +197,49 @@ def _wsbytes(ws):
 
 
 # --------------------------------------------------------------------- conv
-def cf_conv3d_workspace_size(dtype, xshape, cout, pass_):
-    return int(lib().cf_conv3d_workspace_size(dtype, dims(xshape), int(cout), CONV3, int(pass_)))
+def cf_conv3d_workspace_size(dtype, xshape, cout, pass_, stride=1):
+    geom = conv_geometry(stride, xshape[1])
+    return int(lib().cf_conv3d_workspace_size(dtype, dims(xshape), int(cout), geom, int(pass_)))
 
 
-def cf_conv3d_fwd(X, W, Y=None, ws=None, stream=None):
-    """X [N,D,H,W,Cin], W [3,3,3,Cin,Cout] (same dtype) -> Y [N,D,H,W,Cout]."""
+def cf_conv3d_fwd(X, W, Y=None, ws=None, stream=None, stride=1):
+    """X [N,D,H,W,Cin], W [3,3,3,Cin,Cout] (same dtype) -> Y [N,D,H,W,Cout]
+    (stride 2: "same" padding, output ceil(D/2) etc.)."""
     dt = dtype_code(X.dtype)
     cout = int(W.shape[4])
     if Y is None:
-        Y = torch.empty(tuple(X.shape[:4]) + (cout,), dtype=X.dtype, device=X.device)
-    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_FWD), X.device, ws)
-    check(lib().cf_conv3d_fwd(dt, dims(X.shape), _ptr(X), _ptr(W), cout, CONV3, _ptr(Y), _ptr(ws), _wsbytes(ws),
-                              _stream(stream)))
+        Y = torch.empty(out_shape(X.shape, cout, stride), dtype=X.dtype, device=X.device)
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_FWD, stride), X.device, ws)
+    check(lib().cf_conv3d_fwd(dt, dims(X.shape), _ptr(X), _ptr(W), cout, conv_geometry(stride, X.shape[1]), _ptr(Y),
+                              _ptr(ws), _wsbytes(ws), _stream(stream)))
     return Y
 
 
-def cf_conv3d_bwd_data(dY, W, dX=None, ws=None, stream=None):
-    """dY [N,D,H,W,Cout], W [3,3,3,Cin,Cout] -> dX [N,D,H,W,Cin]."""
+def cf_conv3d_bwd_data(dY, W, dX=None, ws=None, stream=None, xshape=None, stride=1):
+    """dY [N,D,H,W,Cout], W [3,3,3,Cin,Cout] -> dX [N,D,H,W,Cin]; with
+    stride 2, xshape is the forward input's shape."""
     dt = dtype_code(dY.dtype)
     cin, cout = int(W.shape[3]), int(W.shape[4])
-    xshape = tuple(dY.shape[:4]) + (cin,)
+    if xshape is None:
+        xshape = tuple(dY.shape[:4]) + (cin,)
+    xshape = tuple(int(v) for v in xshape)
     if dX is None:
         dX = torch.empty(xshape, dtype=dY.dtype, device=dY.device)
-    ws = _ws(cf_conv3d_workspace_size(dt, xshape, cout, CF_CONV_BWD_DATA), dY.device, ws)
-    check(lib().cf_conv3d_bwd_data(dt, dims(xshape), _ptr(dY), _ptr(W), cout, CONV3, _ptr(dX), _ptr(ws),
-                                   _wsbytes(ws), _stream(stream)))
+    ws = _ws(cf_conv3d_workspace_size(dt, xshape, cout, CF_CONV_BWD_DATA, stride), dY.device, ws)
+    check(lib().cf_conv3d_bwd_data(dt, dims(xshape), _ptr(dY), _ptr(W), cout, conv_geometry(stride, xshape[1]),
+                                   _ptr(dX), _ptr(ws), _wsbytes(ws), _stream(stream)))
     return dX
 
 
-def cf_conv3d_bwd_weight(X, dY, dW=None, ws=None, stream=None):
-    """X [N,D,H,W,Cin], dY [N,D,H,W,Cout] -> dW [3,3,3,Cin,Cout] fp32."""
+def cf_conv3d_bwd_weight(X, dY, dW=None, ws=None, stream=None, stride=1):
+    """X [N,D,H,W,Cin], dY [N,Do,Ho,Wo,Cout] -> dW [3,3,3,Cin,Cout] fp32."""
     dt = dtype_code(X.dtype)
     cout = int(dY.shape[4])
     if dW is None:
         dW = torch.empty((3, 3, 3, int(X.shape[4]), cout), dtype=torch.float32, device=X.device)
-    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_BWD_WEIGHT), X.device, ws)
-    check(lib().cf_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, CONV3, _ptr(dW), _ptr(ws),
-                                     _wsbytes(ws), _stream(stream)))
+    ws = _ws(cf_conv3d_workspace_size(dt, X.shape, cout, CF_CONV_BWD_WEIGHT, stride), X.device, ws)
+    check(lib().cf_conv3d_bwd_weight(dt, dims(X.shape), _ptr(X), _ptr(dY), cout, conv_geometry(stride, X.shape[1]),
+                                     _ptr(dW), _ptr(ws), _wsbytes(ws), _stream(stream)))
     return dW
 
 
@@ -258,6 +304,24 @@ def cf_pool3d_bwd(dP, P, idx, slope, dZ=None, stream=None):
         dZ = torch.empty(zshape, dtype=dP.dtype, device=dP.device)
     check(lib().cf_pool3d_bwd(dt, dims(zshape), _ptr(dP), _ptr(P), _ptr(idx), float(slope), _ptr(dZ),
                               _stream(stream)))
+    return dZ
+
+
+def cf_avgpool3d_fwd(Z, slope, P=None, stream=None):
+    """Z [N,D,H,W,C] -> P [N,D/2,H/2,W/2,C] = mean over 2^3 of lrelu(Z)."""
+    dt = dtype_code(Z.dtype)
+    N, D, H, W, C = (int(v) for v in Z.shape)
+    if P is None:
+        P = torch.empty((N, D // 2, H // 2, W // 2, C), dtype=Z.dtype, device=Z.device)
+    check(lib().cf_avgpool3d_fwd(dt, dims(Z.shape), _ptr(Z), float(slope), _ptr(P), _stream(stream)))
+    return P
+
+
+def cf_avgpool3d_bwd(dP, Z, slope, dZ=None, stream=None):
+    dt = dtype_code(Z.dtype)
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    check(lib().cf_avgpool3d_bwd(dt, dims(Z.shape), _ptr(dP), _ptr(Z), float(slope), _ptr(dZ), _stream(stream)))
     return dZ
 
 
@@ -409,3 +473,61 @@ def cf_batchnorm_bwd(X, dY, gamma, mean, invstd, dX=None, ws=None, stream=None):
     check(lib().cf_batchnorm_bwd(dt, dims(X.shape), _ptr(X), _ptr(dY), _ptr(gamma), _ptr(mean), _ptr(invstd),
                                  _ptr(dX), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _wsbytes(ws), _stream(stream)))
     return dX, dgamma, dbeta
+
+
+# ------------------------------------------------------ general network step
+def net_desc(in_channels, size, filters, strides=None, pools=None, dense=(128, 64, 3), dense_bias=True,
+             batch_norm=False, bn_eps=1e-5, slope=0.3):
+    """cf_net_desc for a cubic input (or size = (d, h, w)); pools are
+    CF_POOL_* values (default max after every layer)."""
+    m = cf_net_desc()
+    d, h, w = (size, size, size) if isinstance(size, int) else size
+    m.nlayers, m.cin, m.d, m.h, m.w = len(filters), in_channels, d, h, w
+    strides = strides or [1] * len(filters)
+    pools = pools if pools is not None else [CF_POOL_MAX] * len(filters)
+    for i, f in enumerate(filters):
+        m.filters[i], m.stride[i], m.pool[i] = f, strides[i], pools[i]
+    m.batch_norm, m.bn_eps = int(bool(batch_norm)), bn_eps
+    m.ndense = len(dense)
+    for i, f in enumerate(dense):
+        m.dense[i] = f
+    m.dense_bias, m.slope = int(bool(dense_bias)), slope
+    return m
+
+
+def cf_net_param_count(m):
+    n = (ctypes.c_int64 * CF_MAX_OPT_TENSORS)()
+    k = int(lib().cf_net_param_count(ctypes.byref(m), n))
+    if k < 0:
+        raise CfError(CF_ERR_INVALID, lib().cf_last_error().decode())
+    return [int(n[i]) for i in range(k)]
+
+
+def sgd_optimizer(lr):
+    o = cf_optimizer()
+    o.kind, o.lr = CF_OPT_SGD, float(lr)
+    return o
+
+
+def adam_optimizer(hp, t):
+    o = cf_optimizer()
+    o.kind, o.adam, o.t = CF_OPT_ADAM_LARC, hp, int(t)
+    return o
+
+
+def cf_net_train_step(m, X, targets, params, opt, moments=None, ws=None, loss=None, pred=None, stream=None):
+    """One step of the general network; params (and Adam moments (m, v)) in
+    cf_net_param_count's order, updated in place.  Returns (loss, pred)."""
+    dt = dtype_code(X.dtype)
+    B = int(X.shape[0])
+    ws = _ws(int(lib().cf_net_train_step_workspace_size(ctypes.byref(m), dt, B)), X.device, ws)
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=X.device)
+    k = len(params)
+    arr = lambda ts: (_P * k)(*[q.data_ptr() for q in ts])
+    mp = vp = None
+    if moments is not None:
+        mp, vp = arr(moments[0]), arr(moments[1])
+    check(lib().cf_net_train_step(ctypes.byref(m), dt, B, _ptr(X), _ptr(targets), arr(params), ctypes.byref(opt), mp,
+                                  vp, _ptr(loss), _ptr(pred), _ptr(ws), _wsbytes(ws), _stream(stream)))
+    return loss, pred

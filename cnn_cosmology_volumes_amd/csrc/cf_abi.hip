@@ -26,6 +26,19 @@ cf_status fail(cf_status s, const char* fmt, ...)
     return s;
 }
 
+}  // namespace
+
+cf_status report(cf_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+namespace {
+
 cf_status check_hip(hipError_t e, const char* what)
 {
     if (e == hipSuccess) return CF_OK;
@@ -68,8 +81,13 @@ cf_status check_conv(cf_dtype dt, const cf_dims& x, int32_t cout, const cf_conv&
     if (s != CF_OK) return s;
     if ((s = check_dims(x, "x")) != CF_OK) return s;
     if (cout <= 0 || cout > 65536) return fail(CF_ERR_INVALID, "cout must be in 1..65536");
-    if (cv.k != 3 || cv.stride != 1 || cv.pad != 1)
-        return fail(CF_ERR_UNSUPPORTED, "only k=3, stride=1, pad=1 is implemented (got k=%d stride=%d pad=%d)", cv.k,
+    const bool s1 = cv.k == 3 && cv.stride == 1 && cv.pad == 1;
+    const bool s2 = cv.k == 3 && cv.stride == 2 && cv.pad == (int)(x.d & 1) && (x.d & 1) == (x.h & 1) &&
+                    (x.d & 1) == (x.w & 1);
+    if (!s1 && !s2)
+        return fail(CF_ERR_UNSUPPORTED,
+                    "only k=3 with stride 1, pad 1, or stride 2 with \"same\" padding (pad = 1 for odd sizes, 0 for "
+                    "even, all three sizes of one parity) is implemented (got k=%d stride=%d pad=%d)", cv.k,
                     cv.stride, cv.pad);
     const double el = (double)x.n * x.d * x.h * x.w * (double)cout;
     if (el > (double)kMaxElems) return fail(CF_ERR_INVALID, "output tensor too large");
@@ -156,6 +174,13 @@ size_t dgrad_wk_bytes(Fwd p, cf_dtype dt, int64_t cin, int cout)
 }
 
 cf_dims with_c(const cf_dims& x, int64_t c) { cf_dims y = x; y.c = c; return y; }
+
+// Stride 2 runs as the stride-1 convolution sampled at 2o + q (q = 1 - pad)
+// (k_resample.hip).  Output size ceil(size / 2).
+const cf_conv kConv1 = {3, 1, 1};
+int s2_q(const cf_conv& cv) { return 1 - cv.pad; }
+cf_dims s2_out(const cf_dims& x, int64_t c) { return cf_dims{x.n, (x.d + 1) / 2, (x.h + 1) / 2, (x.w + 1) / 2, c}; }
+size_t full_bytes(const cf_dims& x, int64_t c, cf_dtype dt) { return (size_t)(x.n * x.d * x.h * x.w) * c * esize(dt); }
 
 // Enqueue the forward conv given prepared weights `wk` (layout per path; for
 // the direct path `wk` is DHWIO in the data type).
@@ -259,6 +284,11 @@ const char* cf_last_error(void) { return g_err; }
 size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv conv, cf_conv_pass pass)
 {
     if (check_conv(dtype, x, cout, conv) != CF_OK) return 0;
+    if (conv.stride == 2) {
+        if (pass != CF_CONV_FWD && pass != CF_CONV_BWD_DATA && pass != CF_CONV_BWD_WEIGHT) return 0;
+        if (cout % 4) return 0;
+        return cf_conv3d_workspace_size(dtype, x, cout, kConv1, pass) + up256(full_bytes(x, cout, dtype));
+    }
     switch (pass) {
     case CF_CONV_FWD: {
         const Fwd p = fwd_path(dtype, x, cout);
@@ -291,6 +321,7 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
+    if (conv.stride != 1) return fail(CF_ERR_UNSUPPORTED, "cf_conv3d_pool_fwd: stride 1 only");
     if ((x.d & 1) || (x.h & 1) || (x.w & 1))
         return fail(CF_ERR_UNSUPPORTED, "cf_conv3d_pool_fwd: 2^3 stride-2 pooling needs even D, H, W");
     if (!X || !W || !P || !idx) return fail(CF_ERR_INVALID, "cf_conv3d_pool_fwd: null tensor pointer");
@@ -336,6 +367,7 @@ cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, co
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
+    if (conv.stride != 1) return fail(CF_ERR_UNSUPPORTED, "cf_pool_conv3d_bwd_weight: stride 1 only");
     if ((x.d & 1) || (x.h & 1) || (x.w & 1))
         return fail(CF_ERR_UNSUPPORTED, "cf_pool_conv3d_bwd_weight: 2^3 stride-2 pooling needs even D, H, W");
     if (!X || !dP || !P || !idx || !dW) return fail(CF_ERR_INVALID, "cf_pool_conv3d_bwd_weight: null tensor pointer");
@@ -367,8 +399,8 @@ cf_status cf_pool_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, co
     return CF_OK;
 }
 
-cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv, void* Y,
-                        void* ws, size_t ws_bytes, hipStream_t stream)
+static cf_status conv_fwd_s1(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv,
+                             void* Y, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
@@ -389,8 +421,8 @@ cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W,
     return CF_OK;
 }
 
-cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const void* W, int32_t cout, cf_conv conv,
-                             void* dX, void* ws, size_t ws_bytes, hipStream_t stream)
+static cf_status conv_bwd_data_s1(cf_dtype dtype, cf_dims x, const void* dY, const void* W, int32_t cout,
+                                  cf_conv conv, void* dX, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
@@ -407,8 +439,8 @@ cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const vo
     return CF_OK;
 }
 
-cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout, cf_conv conv,
-                               float* dW, void* ws, size_t ws_bytes, hipStream_t stream)
+static cf_status conv_bwd_weight_s1(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout,
+                                    cf_conv conv, float* dW, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
@@ -420,6 +452,91 @@ cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const v
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: workspace null or misaligned");
     CF_TRY_HIP(run_wgrad(p, dtype, x, X, dY, cout, dW, (float*)ws, stream), "conv3d backward-weight");
     return CF_OK;
+}
+
+// Stride-2 checks shared by the three passes: 4-channel groups for the
+// resampling kernels and a workspace for the stride-1 pass plus one
+// full-resolution tensor of `cout` channels.
+static cf_status s2_prepare(cf_dtype dtype, const cf_dims& x, int32_t cout, cf_conv_pass pass, void* ws,
+                            size_t ws_bytes, const char* fn, size_t* s1_bytes)
+{
+    if (cout % 4) return fail(CF_ERR_UNSUPPORTED, "%s: stride 2 needs a multiple of 4 output channels", fn);
+    const size_t s1 = cf_conv3d_workspace_size(dtype, x, cout, kConv1, pass);
+    const size_t need = s1 + up256(full_bytes(x, cout, dtype));
+    if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "%s: workspace null or misaligned", fn);
+    *s1_bytes = s1;
+    return CF_OK;
+}
+
+cf_status cf_conv3d_fwd(cf_dtype dtype, cf_dims x, const void* X, const void* W, int32_t cout, cf_conv conv, void* Y,
+                        void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (conv.stride == 1) return conv_fwd_s1(dtype, x, X, W, cout, conv, Y, ws, ws_bytes, stream);
+    if (!X || !W || !Y) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: null tensor pointer");
+    if (!al16(X) || !al16(W) || !al16(Y)) return fail(CF_ERR_INVALID, "cf_conv3d_fwd: pointers must be 16-byte aligned");
+    size_t s1 = 0;
+    if ((st = s2_prepare(dtype, x, cout, CF_CONV_FWD, ws, ws_bytes, "cf_conv3d_fwd", &s1)) != CF_OK) return st;
+    void* Z = (char*)ws + s1;
+    if ((st = conv_fwd_s1(dtype, x, X, W, cout, kConv1, Z, ws, s1, stream)) != CF_OK) return st;
+    const cf_dims o = s2_out(x, cout);
+    const cf_dims z = with_c(x, cout);
+    hipError_t e = dtype == CF_F32
+                       ? launch_subsample<float>((const float*)Z, (float*)Y, z, (int)o.d, (int)o.h, (int)o.w, s2_q(conv),
+                                                 stream)
+                       : launch_subsample<uint16_t>((const uint16_t*)Z, (uint16_t*)Y, z, (int)o.d, (int)o.h, (int)o.w,
+                                                    s2_q(conv), stream);
+    CF_TRY_HIP(e, "stride-2 subsample");
+    return CF_OK;
+}
+
+cf_status cf_conv3d_bwd_data(cf_dtype dtype, cf_dims x, const void* dY, const void* W, int32_t cout, cf_conv conv,
+                             void* dX, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (conv.stride == 1) return conv_bwd_data_s1(dtype, x, dY, W, cout, conv, dX, ws, ws_bytes, stream);
+    if (!dY || !W || !dX) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: null tensor pointer");
+    if (!al16(dY) || !al16(W) || !al16(dX))
+        return fail(CF_ERR_INVALID, "cf_conv3d_bwd_data: pointers must be 16-byte aligned");
+    size_t s1 = 0;
+    if ((st = s2_prepare(dtype, x, cout, CF_CONV_BWD_DATA, ws, ws_bytes, "cf_conv3d_bwd_data", &s1)) != CF_OK) return st;
+    void* U = (char*)ws + s1;
+    const cf_dims o = s2_out(x, cout);
+    const cf_dims z = with_c(x, cout);
+    hipError_t e = dtype == CF_F32
+                       ? launch_upsample<float>((const float*)dY, (float*)U, z, (int)o.d, (int)o.h, (int)o.w,
+                                                s2_q(conv), stream)
+                       : launch_upsample<uint16_t>((const uint16_t*)dY, (uint16_t*)U, z, (int)o.d, (int)o.h, (int)o.w,
+                                                   s2_q(conv), stream);
+    CF_TRY_HIP(e, "stride-2 upsample");
+    return conv_bwd_data_s1(dtype, x, U, W, cout, kConv1, dX, ws, s1, stream);
+}
+
+cf_status cf_conv3d_bwd_weight(cf_dtype dtype, cf_dims x, const void* X, const void* dY, int32_t cout, cf_conv conv,
+                               float* dW, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cf_status st = check_conv(dtype, x, cout, conv);
+    if (st != CF_OK) return st;
+    if (conv.stride == 1) return conv_bwd_weight_s1(dtype, x, X, dY, cout, conv, dW, ws, ws_bytes, stream);
+    if (!X || !dY || !dW) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: null tensor pointer");
+    if (!al16(X) || !al16(dY) || !al16(dW))
+        return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight: pointers must be 16-byte aligned");
+    size_t s1 = 0;
+    if ((st = s2_prepare(dtype, x, cout, CF_CONV_BWD_WEIGHT, ws, ws_bytes, "cf_conv3d_bwd_weight", &s1)) != CF_OK)
+        return st;
+    void* U = (char*)ws + s1;
+    const cf_dims o = s2_out(x, cout);
+    const cf_dims z = with_c(x, cout);
+    hipError_t e = dtype == CF_F32
+                       ? launch_upsample<float>((const float*)dY, (float*)U, z, (int)o.d, (int)o.h, (int)o.w,
+                                                s2_q(conv), stream)
+                       : launch_upsample<uint16_t>((const uint16_t*)dY, (uint16_t*)U, z, (int)o.d, (int)o.h, (int)o.w,
+                                                   s2_q(conv), stream);
+    CF_TRY_HIP(e, "stride-2 upsample");
+    return conv_bwd_weight_s1(dtype, x, X, U, cout, kConv1, dW, ws, s1, stream);
 }
 
 // ------------------------------------------- backward-weight, no allocation
@@ -460,6 +577,7 @@ cf_status cf_conv3d_bwd_weight_noalloc(cf_dtype dtype, cf_dims x, const void* X,
 {
     cf_status st = check_conv(dtype, x, cout, conv);
     if (st != CF_OK) return st;
+    if (conv.stride != 1) return fail(CF_ERR_UNSUPPORTED, "cf_conv3d_bwd_weight_noalloc: stride 1 only");
     if (!X || !dY || !dW) return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight_noalloc: null tensor pointer");
     if (!al16(X) || !al16(dY) || !al16(dW))
         return fail(CF_ERR_INVALID, "cf_conv3d_bwd_weight_noalloc: pointers must be 16-byte aligned");
@@ -515,6 +633,38 @@ cf_status cf_pool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* P
                        : launch_pool_bwd<uint16_t>((const uint16_t*)dP, (const uint16_t*)P, idx, (uint16_t*)dZ, z, slope,
                                                    stream);
     CF_TRY_HIP(e, "pool backward");
+    return CF_OK;
+}
+
+cf_status cf_avgpool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, void* P, hipStream_t stream)
+{
+    cf_status st = check_pool(dtype, z);
+    if (st != CF_OK) return st;
+    if (z.c % 4) return fail(CF_ERR_UNSUPPORTED, "cf_avgpool3d_fwd: channels must be a multiple of 4");
+    if (!Z || !P) return fail(CF_ERR_INVALID, "cf_avgpool3d_fwd: null pointer");
+    if (!al16(Z) || !al16(P)) return fail(CF_ERR_INVALID, "cf_avgpool3d_fwd: pointers must be 16-byte aligned");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_avgpool3d_fwd: slope must be >= 0 (got %g)", (double)slope);
+    hipError_t e = dtype == CF_F32 ? launch_avgpool_fwd<float>((const float*)Z, (float*)P, z, slope, stream)
+                                   : launch_avgpool_fwd<uint16_t>((const uint16_t*)Z, (uint16_t*)P, z, slope, stream);
+    CF_TRY_HIP(e, "average pool forward");
+    return CF_OK;
+}
+
+cf_status cf_avgpool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* Z, float slope, void* dZ,
+                           hipStream_t stream)
+{
+    cf_status st = check_pool(dtype, z);
+    if (st != CF_OK) return st;
+    if (z.c % 4) return fail(CF_ERR_UNSUPPORTED, "cf_avgpool3d_bwd: channels must be a multiple of 4");
+    if (!dP || !Z || !dZ) return fail(CF_ERR_INVALID, "cf_avgpool3d_bwd: null pointer");
+    if (!al16(dP) || !al16(Z) || !al16(dZ))
+        return fail(CF_ERR_INVALID, "cf_avgpool3d_bwd: pointers must be 16-byte aligned");
+    if (!(slope >= 0.f)) return fail(CF_ERR_INVALID, "cf_avgpool3d_bwd: slope must be >= 0 (got %g)", (double)slope);
+    hipError_t e = dtype == CF_F32
+                       ? launch_avgpool_bwd<float>((const float*)dP, (const float*)Z, (float*)dZ, z, slope, stream)
+                       : launch_avgpool_bwd<uint16_t>((const uint16_t*)dP, (const uint16_t*)Z, (uint16_t*)dZ, z, slope,
+                                                      stream);
+    CF_TRY_HIP(e, "average pool backward");
     return CF_OK;
 }
 
@@ -598,12 +748,8 @@ static cf_status check_opt(const cf_adam_larc_params* hp, int64_t t, int32_t nt,
     if (!hp || !n) return fail(CF_ERR_INVALID, "%s: null host argument", fn);
     if (nt < 1 || nt > CF_MAX_OPT_TENSORS)
         return fail(CF_ERR_INVALID, "%s: ntensors must be 1..%d (got %d)", fn, CF_MAX_OPT_TENSORS, nt);
-    if (t < 1) return fail(CF_ERR_INVALID, "%s: the update count t starts at 1 (got %lld)", fn, (long long)t);
-    if (!(hp->lr0 >= 0.f) || !(hp->lr_end >= 0.f) || hp->decay_steps < 1 || !(hp->power > 0.f))
-        return fail(CF_ERR_INVALID, "%s: decay needs lr0, lr_end >= 0, decay_steps >= 1, power > 0", fn);
-    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f) || !(hp->eps > 0.f))
-        return fail(CF_ERR_INVALID, "%s: need 0 <= beta1, beta2 < 1 and eps > 0", fn);
-    if (!(hp->trust == hp->trust)) return fail(CF_ERR_INVALID, "%s: trust is NaN", fn);
+    cf_status st = check_adam(hp, t, fn);
+    if (st != CF_OK) return st;
     for (int i = 0; i < nt; ++i)
         if (n[i] <= 0 || n[i] > ((int64_t)1 << 36)) return fail(CF_ERR_INVALID, "%s: n[%d] out of range", fn, i);
     return CF_OK;
@@ -619,14 +765,6 @@ static OptList opt_list(int32_t nt, const int64_t* n, float* const* w, const flo
         if (w) { l.w[i] = w[i]; l.g[i] = g[i]; l.m[i] = m[i]; l.v[i] = v[i]; }
     }
     return l;
-}
-
-// The decayed rate after `done` completed updates, in fp64.
-static double decayed_rate(const cf_adam_larc_params* hp, int64_t done)
-{
-    const double T = (double)hp->decay_steps;
-    const double s = done < hp->decay_steps ? (double)done : T;
-    return ((double)hp->lr0 - (double)hp->lr_end) * pow(1.0 - s / T, (double)hp->power) + (double)hp->lr_end;
 }
 
 size_t cf_adam_larc_workspace_size(int32_t ntensors, const int64_t* n)
@@ -652,17 +790,7 @@ cf_status cf_adam_larc(const cf_adam_larc_params* hp, int64_t t, int32_t ntensor
     const size_t need = up256(adam_larc_part_bytes(l));
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_adam_larc: workspace %zu < %zu bytes", ws_bytes, need);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_adam_larc: workspace null or misaligned");
-    AdamArgs a{};
-    a.lr = (float)decayed_rate(hp, t - 1);
-    a.beta1 = hp->beta1;
-    a.omb1 = (float)(1.0 - (double)hp->beta1);
-    a.beta2 = hp->beta2;
-    a.omb2 = (float)(1.0 - (double)hp->beta2);
-    a.bc1 = (float)(1.0 / (1.0 - pow((double)hp->beta1, (double)t)));
-    a.bc2 = (float)(1.0 / (1.0 - pow((double)hp->beta2, (double)t)));
-    a.eps = hp->eps;
-    a.trust = hp->trust;
-    CF_TRY_HIP(launch_adam_larc(l, a, (float*)ws, lr_out, stream), "adam + larc");
+    CF_TRY_HIP(launch_adam_larc(l, adam_args(hp, t), (float*)ws, lr_out, stream), "adam + larc");
     return CF_OK;
 }
 

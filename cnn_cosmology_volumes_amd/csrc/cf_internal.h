@@ -87,6 +87,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// Sets the calling thread's cf_last_error() text; returns s.
+cf_status report(cf_status s, const char* fmt, ...);
+
 // ----------------------------------------------------------------- launchers
 // Every launcher enqueues on `s` and returns hipGetLastError() of the launch.
 
@@ -243,8 +246,23 @@ struct AdamArgs {
     float bc1, bc2;         // 1 / (1 - beta1^t), 1 / (1 - beta2^t)
     float eps, trust;
 };
+// The per-update scalars of update t (>= 1): decayed rate, bias corrections.
+AdamArgs adam_args(const cf_adam_larc_params* hp, int64_t t);
+// Validates hp and t (error text through report()).
+cf_status check_adam(const cf_adam_larc_params* hp, int64_t t, const char* fn);
 size_t adam_larc_part_bytes(const OptList& l);
 hipError_t launch_adam_larc(const OptList& l, const AdamArgs& a, float* part, float* lr_out, hipStream_t s);
+
+// Stride-2 resampling and 2^3 average pooling with leaky ReLU
+// (k_resample.hip); channel counts multiple of 4.
+template <typename T>
+hipError_t launch_subsample(const T* Z, T* Y, const cf_dims& z, int Do, int Ho, int Wo, int q, hipStream_t s);
+template <typename T>
+hipError_t launch_upsample(const T* dY, T* U, const cf_dims& z, int Do, int Ho, int Wo, int q, hipStream_t s);
+template <typename T>
+hipError_t launch_avgpool_fwd(const T* Z, T* P, const cf_dims& z, float slope, hipStream_t s);
+template <typename T>
+hipError_t launch_avgpool_bwd(const T* dP, const T* Z, T* dZ, const cf_dims& z, float slope, hipStream_t s);
 
 // Training-mode batch normalisation over (N, D, H, W) per channel of an
 // NDHWC tensor, C % 4 == 0 (k_bn.hip).  T = float or uint16_t (bf16).

@@ -11,6 +11,8 @@
 // for bit.
 #include "cf_internal.h"
 
+#include <math.h>
+
 namespace cf {
 namespace {
 
@@ -148,6 +150,37 @@ __global__ __launch_bounds__(OPT_T) void adam_larc_kernel(OptList l, const float
 int blocks_for(int64_t n) { return (int)((n + OPT_CHUNK - 1) / OPT_CHUNK); }
 
 }  // namespace
+
+cf_status check_adam(const cf_adam_larc_params* hp, int64_t t, const char* fn)
+{
+    if (!hp) return report(CF_ERR_INVALID, "%s: null optimizer parameters", fn);
+    if (t < 1) return report(CF_ERR_INVALID, "%s: the update count t starts at 1 (got %lld)", fn, (long long)t);
+    if (!(hp->lr0 >= 0.f) || !(hp->lr_end >= 0.f) || hp->decay_steps < 1 || !(hp->power > 0.f))
+        return report(CF_ERR_INVALID, "%s: decay needs lr0, lr_end >= 0, decay_steps >= 1, power > 0", fn);
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f) || !(hp->eps > 0.f))
+        return report(CF_ERR_INVALID, "%s: need 0 <= beta1, beta2 < 1 and eps > 0", fn);
+    if (!(hp->trust == hp->trust)) return report(CF_ERR_INVALID, "%s: trust is NaN", fn);
+    return CF_OK;
+}
+
+AdamArgs adam_args(const cf_adam_larc_params* hp, int64_t t)
+{
+    // the decayed rate after t - 1 completed updates, in fp64
+    const double T = (double)hp->decay_steps;
+    const double done = t - 1 < hp->decay_steps ? (double)(t - 1) : T;
+    AdamArgs a{};
+    a.lr = (float)(((double)hp->lr0 - (double)hp->lr_end) * pow(1.0 - done / T, (double)hp->power) +
+                   (double)hp->lr_end);
+    a.beta1 = hp->beta1;
+    a.omb1 = (float)(1.0 - (double)hp->beta1);
+    a.beta2 = hp->beta2;
+    a.omb2 = (float)(1.0 - (double)hp->beta2);
+    a.bc1 = (float)(1.0 / (1.0 - pow((double)hp->beta1, (double)t)));
+    a.bc2 = (float)(1.0 / (1.0 - pow((double)hp->beta2, (double)t)));
+    a.eps = hp->eps;
+    a.trust = hp->trust;
+    return a;
+}
 
 size_t adam_larc_part_bytes(const OptList& l)
 {

@@ -68,9 +68,20 @@ typedef enum { CF_F32 = 0, CF_BF16 = 1 } cf_dtype;
 /* Packed NDHWC tensor shape. */
 typedef struct { int64_t n, d, h, w, c; } cf_dims;
 
-/* Convolution geometry.  This build supports k = 3, stride = 1, pad = 1
- * (the "same" stride-1 convolution of [OY] Sec. IV); anything else returns
- * CF_ERR_UNSUPPORTED. */
+/* Convolution geometry; `pad` is the zero padding below each dimension.
+ * This build supports k = 3 with
+ *  - stride 1, pad 1: the "same" stride-1 convolution of [OY] Sec. IV;
+ *    the output has the input's d, h, w;
+ *  - stride 2 with TensorFlow's "same" padding ([OY] Table I: c4 has stride
+ *    2, every layer "same" padding): output ceil(d/2) x ceil(h/2) x ceil(w/2)
+ *    and total padding (out - 1) * 2 + 3 - size per dimension, the smaller
+ *    half below, so pad = 1 when d, h, w are odd and 0 when even (all three
+ *    of one parity).  Output voxel o reads input voxels 2o + k - pad,
+ *    k = 0, 1, 2.  Only cf_conv3d_fwd, cf_conv3d_bwd_data and
+ *    cf_conv3d_bwd_weight take stride 2 (cout a multiple of 4); their
+ *    output or upstream-gradient tensors then have the stride-2 output
+ *    shape.
+ * Anything else returns CF_ERR_UNSUPPORTED. */
 typedef struct { int32_t k, stride, pad; } cf_conv;
 
 /* Which pass a conv workspace is sized for. */
@@ -107,7 +118,9 @@ size_t cf_conv3d_workspace_size(cf_dtype dtype, cf_dims x, int32_t cout, cf_conv
 /* Forward 3D convolution ([CF] Sec. III-C; [OY] Sec. IV, Table I):
  *   Y[n,d,h,w,co] = sum_{kd,kh,kw in 0..2} sum_ci X[n,d+kd-1,h+kh-1,w+kw-1,ci]
  *                                                * W[kd,kh,kw,ci,co]
- * with X read as zero outside the volume.
+ * with X read as zero outside the volume (stride 1; for stride 2 see
+ * cf_conv: Y[n,o,...] reads X[n, 2o + kd - pad, ...] and has the stride-2
+ * output shape).
  *   X [x.n, x.d, x.h, x.w, x.c]  (dtype)      input
  *   W [3,3,3, x.c, cout]         (dtype)      weights, DHWIO
  *   Y [x.n, x.d, x.h, x.w, cout] (dtype)      output, overwritten */
@@ -208,6 +221,21 @@ cf_status cf_pool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, v
  *   dZ    [z.n, z.d, z.h, z.w, z.c]       (dtype)  output, fully overwritten */
 cf_status cf_pool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* P,
                         const uint8_t* idx, float slope, void* dZ, hipStream_t stream);
+
+/* Leaky ReLU followed by 2^3 average pooling with stride 2 ([CF] Sec. III-A
+ * stride-2 average pooling; Sec. III-C: each channel separately, constant
+ * weights 1/(KS)^3 = 1/8):
+ *   P[n,i,j,k,c] = (1/8) sum_{a,b,e in {0,1}} lrelu(Z[n,2i+a,2j+b,2k+e,c])
+ * added in (a,b,e) order in fp32, then scaled; slope = 1 gives plain average
+ * pooling (slope >= 0).  z.d, z.h, z.w even; z.c a multiple of 4.
+ *   Z [z.n, z.d, z.h, z.w, z.c], P [z.n, z.d/2, z.h/2, z.w/2, z.c] (dtype) */
+cf_status cf_avgpool3d_fwd(cf_dtype dtype, cf_dims z, const void* Z, float slope, void* P, hipStream_t stream);
+
+/* Backward of cf_avgpool3d_fwd: every window position receives its window's
+ * pooled gradient times 1/8 and the leaky-ReLU derivative at Z (1 if Z > 0,
+ * slope otherwise).  dP as P, Z and dZ [z.n, z.d, z.h, z.w, z.c] (dtype). */
+cf_status cf_avgpool3d_bwd(cf_dtype dtype, cf_dims z, const void* dP, const void* Z, float slope, void* dZ,
+                           hipStream_t stream);
 
 /* Elementwise leaky ReLU ([CF] Sec. III-A).  dy == NULL: out = lrelu(x).
  * Otherwise out = dy * (x > 0 ? 1 : slope) (the backward).  n elements of
@@ -360,6 +388,75 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                         const float* targets, float* const* params, float lr, float* loss_out,
                         float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream,
                         const cf_step_aux* aux);
+
+/* ------------------------------------------------- general network step */
+
+/* What follows each convolution. */
+typedef enum {
+    CF_POOL_MAX = 0,   /* leaky ReLU, 2^3 max pool (cf_pool3d_fwd) */
+    CF_POOL_AVG = 1,   /* leaky ReLU, 2^3 average pool (cf_avgpool3d_fwd) */
+    CF_POOL_NONE = 2   /* leaky ReLU only */
+} cf_pool_kind;
+
+#define CF_MAX_DENSE 4
+
+/* A network of `nlayers` conv layers (3^3, no bias, stride[l] 1 or 2 with
+ * "same" padding) each followed by batch normalisation when batch_norm != 0,
+ * leaky ReLU and pool[l]; then flatten (NDHWC order) and ndense fully
+ * connected layers of widths dense[0..ndense-1] (with biases when
+ * dense_bias != 0; leaky ReLU on all but the last), MSE against the targets.
+ * This covers the benchmark network (stride 1, max pool, biases) and the
+ * extended CosmoFlow network of [OY] Table I (c4 with stride 2, average
+ * pooling as in [CF] Sec. III-A, no pool after c6/c7 at 128^3, fc
+ * 2048-256-4 without bias, BN after every conv as in [OY] Sec. IV). */
+typedef struct {
+    int32_t nlayers;                  /* 1..CF_MAX_BLOCKS */
+    int32_t cin, d, h, w;             /* input volume (channels, sizes) */
+    int32_t filters[CF_MAX_BLOCKS];
+    int32_t stride[CF_MAX_BLOCKS];    /* 1 or 2 */
+    int32_t pool[CF_MAX_BLOCKS];      /* cf_pool_kind */
+    int32_t batch_norm;               /* != 0: BN after every conv */
+    float bn_eps;
+    int32_t ndense;                   /* 1..CF_MAX_DENSE */
+    int32_t dense[CF_MAX_DENSE];
+    int32_t dense_bias;               /* != 0: dense layers have biases */
+    float slope;                      /* leaky-ReLU slope, >= 0 */
+} cf_net_desc;
+
+typedef enum { CF_OPT_SGD = 0, CF_OPT_ADAM_LARC = 1 } cf_opt_kind;
+
+/* The update applied at the end of cf_net_train_step. */
+typedef struct {
+    int32_t kind;                     /* cf_opt_kind */
+    float lr;                         /* SGD: W <- W - lr dW ([OY] Sec. II-A) */
+    cf_adam_larc_params adam;         /* CF_OPT_ADAM_LARC, as cf_adam_larc */
+    int64_t t;                        /* CF_OPT_ADAM_LARC: update count, >= 1 */
+} cf_optimizer;
+
+/* Number of parameter tensors of the network (at most CF_MAX_OPT_TENSORS),
+ * or -1 for an invalid description.  If n is not NULL it receives each
+ * tensor's element count (HOST array).  Order: for each conv layer its
+ * weight [3,3,3,cin,filters] (DHWIO), then gamma [filters] and beta
+ * [filters] when batch_norm; then for each dense layer W [in,out] and, when
+ * dense_bias, b [out]. */
+int32_t cf_net_param_count(const cf_net_desc* net, int64_t* n);
+
+/* Workspace bytes for cf_net_train_step. */
+size_t cf_net_train_step_workspace_size(const cf_net_desc* net, cf_dtype dtype, int32_t B);
+
+/* One training step of `net`: forward, MSE against `targets`
+ * [B, dense[ndense-1]], backward, and the optimizer's update of every
+ * parameter (fp32 masters, `params`: HOST array of DEVICE pointers in
+ * cf_net_param_count's order, updated in place).  For CF_OPT_ADAM_LARC, m
+ * and v are HOST arrays of DEVICE pointers to the Adam moments in the same
+ * order (zero before t = 1); for SGD they are ignored.  CF_BF16 stores every
+ * activation and activation gradient in bf16 (conv weights rounded from the
+ * masters each step); CF_F32 is fp32 throughout.  The first layer's
+ * backward-data is not computed.  Composed of this library's other entry
+ * points' kernels, on `stream`. */
+cf_status cf_net_train_step(const cf_net_desc* net, cf_dtype dtype, int32_t B, const void* X, const float* targets,
+                            float* const* params, const cf_optimizer* opt, float* const* m, float* const* v,
+                            float* loss_out, float* pred_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- status */
 

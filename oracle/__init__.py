@@ -486,3 +486,128 @@ def batchnorm_bwd(x, dy, gamma, mean, invstd):
     dgamma = np.sum(fd * xhat, axis=0)
     dx = _f64(gamma) * invstd * (fd - dbeta / M - xhat * dgamma / M)
     return dx.reshape(x.shape), dgamma, dbeta
+
+
+# ------------------------------------------------- general network step
+def net_param_shapes(cin, layers, dense, batch_norm, dense_bias, in_size):
+    """Parameter shapes in the order the step takes them: per conv layer W
+    [3,3,3,cin,f] (then gamma [f], beta [f] with batch norm); per dense layer
+    W [in,out] (then b [out] with biases).  layers: (filters, stride, pool)
+    with pool in {"max", "avg", "none"}; cubic input of width in_size."""
+    shapes, c, s = [], cin, in_size
+    for f, stride, pool in layers:
+        shapes.append((3, 3, 3, c, f))
+        if batch_norm:
+            shapes += [(f,), (f,)]
+        s = same_geometry(s, stride)[0]
+        if pool != "none":
+            s //= 2
+        c = f
+    fan = s ** 3 * c
+    for o in dense:
+        shapes.append((fan, o))
+        if dense_bias:
+            shapes.append((o,))
+        fan = o
+    return shapes
+
+
+def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, bn_eps=1e-5, dense_bias=True,
+                   storage="f64", opt=("sgd", 1e-3), adam_state=None):
+    """One training step of a general conv network (the extended CosmoFlow
+    network of Oyama et al., Table I and Sec. IV, and the benchmark network
+    alike): per layer a 3^3 "same" conv of the given stride without bias,
+    batch normalisation (optional), leaky ReLU and max / average / no
+    pooling; flatten; dense layers (leaky ReLU but on the last; optional
+    biases); MSE; backward; the update.
+
+    Storage points (rounded to ``storage``): the input, each conv output,
+    batch-norm output, layer output and their gradients; conv weights are
+    the masters rounded to ``storage``.  opt: ("sgd", lr) or ("adam", lr_t,
+    beta1, beta2, eps, trust, t) with adam_state = (m list, v list).
+    Returns dict(loss, yhat, grads, params, adam_state)."""
+    L = len(layers)
+    per = 3 if batch_norm else 1
+    conv_w = [params[l * per] for l in range(L)]
+    gam = [params[l * per + 1] for l in range(L)] if batch_norm else None
+    bet = [params[l * per + 2] for l in range(L)] if batch_norm else None
+    dp_ = 2 if dense_bias else 1
+    dw0 = L * per
+    dW = [_f64(params[dw0 + k * dp_]) for k in range(len(dense))]
+    db = [_f64(params[dw0 + k * dp_ + 1]) if dense_bias else np.zeros(dense[k]) for k in range(len(dense))]
+    wuse = [store(w, storage) for w in conv_w]
+
+    def conv(a, w, s):
+        return conv3d_fwd(a, w) if s == 1 else conv3d_fwd_s(a, w, s)
+
+    a = store(x, storage)
+    cache = []
+    for l, (f, s, pool) in enumerate(layers):
+        z = store(conv(a, wuse[l], s), storage)
+        y, mean, invstd = z, None, None
+        if batch_norm:
+            y, mean, invstd = batchnorm_fwd(z, gam[l], bet[l], bn_eps)
+            y = store(y, storage)
+        idx = None
+        if pool == "max":
+            out, idx = lrelu_maxpool_fwd(y, slope)
+        elif pool == "avg":
+            out = avgpool_fwd(lrelu_fwd(y, slope))
+        else:
+            out = lrelu_fwd(y, slope)
+        out = store(out, storage)
+        cache.append(dict(x=a, z=z, y=y, out=out, idx=idx, mean=mean, invstd=invstd, s=s))
+        a = out
+    B = a.shape[0]
+    h = a.reshape(B, -1)
+    dcache = []
+    for k in range(len(dense)):
+        sk = slope if k + 1 < len(dense) else -1.0
+        pre, yk = dense_fwd(h, dW[k], db[k], sk)
+        dcache.append((h, pre, sk))
+        h = yk
+    loss, g = mse(h, targets)
+    grads = [None] * len(params)
+    for k in reversed(range(len(dense))):
+        hin, pre, sk = dcache[k]
+        g, gw, gb = dense_bwd(hin, dW[k], pre, g, sk, need_dx=True)
+        grads[dw0 + k * dp_] = gw
+        if dense_bias:
+            grads[dw0 + k * dp_ + 1] = gb
+    dA = store(g.reshape(a.shape), storage)
+    for l in reversed(range(L)):
+        c = cache[l]
+        pool = layers[l][2]
+        if pool == "max":
+            dy = maxpool_lrelu_bwd(dA, c["out"], c["idx"], slope)
+        elif pool == "avg":
+            dy = lrelu_bwd(c["y"], avgpool_bwd(dA), slope)
+        else:
+            dy = lrelu_bwd(c["y"], dA, slope)
+        dy = store(dy, storage)
+        dz = dy
+        if batch_norm:
+            dz, gg, gb = batchnorm_bwd(c["z"], dy, gam[l], c["mean"], c["invstd"])
+            dz = store(dz, storage)
+            grads[l * per + 1], grads[l * per + 2] = gg, gb
+        s = c["s"]
+        grads[l * per] = conv3d_bwd_weight(c["x"], dz) if s == 1 else conv3d_bwd_weight_s(c["x"], dz, s)
+        if l > 0:
+            size = c["x"].shape[1]
+            dA = conv3d_bwd_data(dz, wuse[l]) if s == 1 else conv3d_bwd_data_s(dz, wuse[l], s, size)
+            dA = store(dA, storage)
+    master = "f64" if storage == "f64" else "f32"
+    if opt[0] == "sgd":
+        new = [store(sgd(p, gr, opt[1]), master) for p, gr in zip(params, grads)]
+        state = None
+    else:
+        _, lr_t, b1, b2, eps, trust, t = opt
+        ms, vs = adam_state
+        new, nm, nv = [], [], []
+        for p, gr, m_, v_ in zip(params, grads, ms, vs):
+            w_, m2, v2, _ = adam_larc_step(p, gr, m_, v_, t, lr_t, b1, b2, eps, trust)
+            new.append(store(w_, master))
+            nm.append(m2)
+            nv.append(v2)
+        state = (nm, nv)
+    return dict(loss=loss, yhat=h, grads=grads, params=new, adam_state=state)

@@ -1,0 +1,214 @@
+"""GPU parity of the extended-network pieces against the fp64 oracle:
+
+- the stride-2 "same" convolution (cf_conv3d_fwd / _bwd_data / _bwd_weight
+  with stride 2; Oyama et al., Table I, c4) at even and odd sizes;
+- 2^3 average pooling with leaky ReLU (cf_avgpool3d_fwd / _bwd; CosmoFlow
+  Sec. III-A / III-C);
+- cf_net_train_step: the Table I network at 128^3 (stride-2 c4, average
+  pooling, no pool after c6 / c7, fc 2048-256-4 without bias), a network
+  with batch norm and Adam + LARC, and the benchmark network, which must
+  equal cf_train_step bit for bit.
+
+Tolerances as elsewhere: fp32 1e-5, bf16 2e-2 of RMS (beyond one bf16
+quantum for tensors both sides store in bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthdata as sd
+from cnn_cosmology_volumes_amd import cf
+from cnn_cosmology_volumes_amd.configs import oyama_table1_net
+from gpu_util import TOL_BF16, TOL_F32, host64, rel_err, rel_err_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+BF, F32 = torch.bfloat16, torch.float32
+SLOPE = 0.3
+LR_RECOVER = 2.0 ** 20
+POOL = {"max": cf.CF_POOL_MAX, "avg": cf.CF_POOL_AVG, "none": cf.CF_POOL_NONE}
+
+
+# ------------------------------------------------------------ stride 2
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("shape", [(2, 16, 16, 16, 64, 128), (1, 9, 7, 11, 32, 32), (2, 6, 10, 8, 4, 16),
+                                   (1, 5, 5, 5, 8, 12)])
+def test_stride2_conv_matches_oracle(shape, dtype):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape))
+    x = sd.normal(rng, (N, D, H, W, Ci), bf16=(dtype == BF))
+    w = sd.he_normal_conv(rng, Ci, Co)
+    w = sd.bf16_round_f32(w) if dtype == BF else w
+    xd, wd = to_dev(x, dtype), to_dev(w, dtype)
+    y = cf.cf_conv3d_fwd(xd, wd, stride=2)
+    Do, Ho, Wo = (D + 1) // 2, (H + 1) // 2, (W + 1) // 2
+    assert tuple(y.shape) == (N, Do, Ho, Wo, Co)
+    dy = sd.normal(rng, (N, Do, Ho, Wo, Co), bf16=(dtype == BF))
+    dyd = to_dev(dy, dtype)
+    dx = cf.cf_conv3d_bwd_data(dyd, wd, xshape=x.shape, stride=2)
+    dw = cf.cf_conv3d_bwd_weight(xd, dyd, stride=2)
+    torch.cuda.synchronize()
+    # the oracle's rule for non-cubic volumes: its same_geometry per dimension
+    p = (D & 1)
+    yo = np.empty((N, Do, Ho, Wo, Co))
+    lib = oracle.lib()
+    f = lambda a: np.ascontiguousarray(a, np.float64)
+    lib.or_conv3d_fwd_s(N, D, H, W, Ci, Co, 2, p, Do, Ho, Wo, oracle._ptr(f(x)), oracle._ptr(f(w)), oracle._ptr(yo))
+    dxo = np.empty((N, D, H, W, Ci))
+    lib.or_conv3d_bwd_data_s(N, D, H, W, Ci, Co, 2, p, Do, Ho, Wo, oracle._ptr(f(dy)), oracle._ptr(f(w)),
+                             oracle._ptr(dxo))
+    dwo = np.empty((3, 3, 3, Ci, Co))
+    lib.or_conv3d_bwd_weight_s(N, D, H, W, Ci, Co, 2, p, Do, Ho, Wo, oracle._ptr(f(x)), oracle._ptr(f(dy)),
+                               oracle._ptr(dwo))
+    if dtype == F32:
+        assert rel_err(host64(y), yo) <= TOL_F32
+        assert rel_err(host64(dx), dxo) <= TOL_F32
+        assert rel_err(host64(dw), dwo) <= TOL_F32
+    else:
+        assert rel_err(host64(y), yo) <= TOL_BF16
+        assert rel_err(host64(dx), dxo) <= TOL_BF16
+        assert rel_err(host64(dw), dwo) <= 1e-4      # fp32 sums of exact bf16 products
+
+
+def test_stride2_rejects_wrong_padding():
+    x = torch.zeros((1, 8, 8, 8, 32), dtype=BF, device="cuda")
+    w = torch.zeros((3, 3, 3, 32, 32), dtype=BF, device="cuda")
+    y = torch.empty((1, 4, 4, 4, 32), dtype=BF, device="cuda")
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    st = cf.lib().cf_conv3d_fwd(cf.CF_BF16, cf.dims(x.shape), cf._ptr(x), cf._ptr(w), 32, cf.cf_conv(3, 2, 1),
+                                cf._ptr(y), cf._ptr(ws), 1 << 24, cf._stream())
+    assert st == cf.CF_ERR_UNSUPPORTED   # even sizes take pad 0
+
+
+# ------------------------------------------------------------ average pool
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("shape", [(2, 6, 10, 8, 16), (1, 4, 4, 4, 4), (2, 8, 8, 8, 256)])
+def test_avgpool_matches_oracle(shape, dtype):
+    rng = np.random.default_rng(sum(shape) + 1)
+    z = sd.normal(rng, shape, bf16=(dtype == BF))
+    Np, Dp, Hp, Wp = shape[0], shape[1] // 2, shape[2] // 2, shape[3] // 2
+    dp = sd.normal(rng, (Np, Dp, Hp, Wp, shape[4]), bf16=(dtype == BF))
+    zd, dpd = to_dev(z, dtype), to_dev(dp, dtype)
+    P = cf.cf_avgpool3d_fwd(zd, SLOPE)
+    dZ = cf.cf_avgpool3d_bwd(dpd, zd, SLOPE)
+    torch.cuda.synchronize()
+    po = oracle.avgpool_fwd(oracle.lrelu_fwd(z, SLOPE))
+    dzo = oracle.lrelu_bwd(z, oracle.avgpool_bwd(dp), SLOPE)
+    if dtype == F32:
+        assert rel_err(host64(P), po) <= TOL_F32 and rel_err(host64(dZ), dzo) <= TOL_F32
+    else:
+        assert rel_err_bf16(host64(P), oracle.round_bf16(po)) <= TOL_BF16
+        assert rel_err_bf16(host64(dZ), oracle.round_bf16(dzo)) <= TOL_BF16
+
+
+# ------------------------------------------------------------ network step
+def make_net(layers, dense, in_ch, size, batch_norm, dense_bias):
+    return cf.net_desc(in_ch, size, [l[0] for l in layers], [l[1] for l in layers], [POOL[l[2]] for l in layers],
+                       dense=dense, dense_bias=dense_bias, batch_norm=batch_norm, slope=SLOPE)
+
+
+def init_params(rng, shapes, batch_norm):
+    ps = []
+    for i, sh in enumerate(shapes):
+        if len(sh) == 5:
+            ps.append(sd.he_normal_conv(rng, sh[3], sh[4]))
+        elif len(sh) == 2:
+            ps.append(sd.he_normal_dense(rng, sh[0], sh[1])[0])
+        else:
+            ps.append(rng.uniform(0.5, 1.5, sh).astype(np.float32) if batch_norm and len(shapes[i - 1]) == 5
+                      else (rng.standard_normal(sh) * 0.05).astype(np.float32))
+    return ps
+
+
+def run_net(layers, dense, size, B, dtype, batch_norm, dense_bias, seed, opt="sgd"):
+    rng = np.random.default_rng(seed)
+    x = sd.lognormal_poisson_input(rng, rng, (B, size, size, size), 4, bf16=(dtype == BF))
+    t = sd.targets(rng, B, dense[-1])
+    m = make_net(layers, dense, 4, size, batch_norm, dense_bias)
+    shapes = oracle.net_param_shapes(4, layers, dense, batch_norm, dense_bias, size)
+    assert [int(np.prod(s)) for s in shapes] == cf.cf_net_param_count(m)
+    params = init_params(rng, shapes, batch_norm)
+    pd = [to_dev(p, F32) for p in params]
+    old = [host64(p) for p in pd]
+    pred = torch.empty((B, dense[-1]), dtype=F32, device="cuda")
+    if opt == "sgd":
+        o = cf.sgd_optimizer(LR_RECOVER)
+        loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, o, pred=pred)
+    else:
+        hp = cf.adam_larc_params(0.01, lr_end=0.001, decay_steps=10, trust=0.02)
+        mom = ([torch.zeros_like(p) for p in pd], [torch.zeros_like(p) for p in pd])
+        loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, cf.adam_optimizer(hp, 1), moments=mom,
+                                       pred=pred)
+    torch.cuda.synchronize()
+    storage = "bf16" if dtype == BF else "f32"
+    if opt == "sgd":
+        ref = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
+                                    storage=storage, opt=("sgd", LR_RECOVER))
+        grads = [(o_ - host64(p)) / LR_RECOVER for o_, p in zip(old, pd)]
+        return loss.item(), host64(pred), grads, ref
+    f = lambda v: float(np.float32(v))
+    z = [np.zeros(p.shape) for p in params]
+    ref = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
+                                storage=storage, opt=("adam", f(0.01), f(0.9), f(0.999), f(1e-8), f(0.02), 1),
+                                adam_state=(z, z))
+    return loss.item(), host64(pred), [host64(p) for p in pd], ref
+
+
+TABLE1_128 = [(16, 1, "avg"), (32, 1, "avg"), (64, 1, "avg"), (128, 2, "avg"), (256, 1, "avg"), (256, 1, "none"),
+              (256, 1, "none")]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_table1_network_step_matches_oracle(dtype):
+    """The extended network of Oyama et al., Table I, at 128^3 (batch 2):
+    loss, predictions and every weight gradient against the untied oracle.
+    Average pooling has no argmax decisions, so the comparison is direct."""
+    net = oyama_table1_net(128)
+    assert [(L.cout, L.stride, "avg" if L.pool else "none") for L in net.convs] == TABLE1_128
+    loss, pred, grads, ref = run_net(TABLE1_128, [2048, 256, 4], 128, 2, dtype, False, False, 41)
+    tol = TOL_BF16 if dtype == BF else TOL_F32
+    errs = {"loss": abs(loss - ref["loss"]) / ref["loss"], "pred": rel_err(pred, ref["yhat"])}
+    for i, (g, r) in enumerate(zip(grads, ref["grads"])):
+        errs["grad%d" % i] = rel_err(g, r)
+    print("Table I 128^3 network step (%s) vs oracle: %s" % (dtype, ", ".join("%s %.2e" % kv for kv in errs.items())))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+
+
+SMALL_BN = [(16, 1, "avg"), (32, 1, "max"), (64, 2, "avg"), (64, 1, "none")]
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("opt", ["sgd", "adam"])
+def test_bn_network_step_matches_oracle(dtype, opt):
+    """Batch norm after every conv, average / max / no pooling, a stride-2
+    layer, no dense bias; SGD (gradients recovered from the update) or one
+    Adam + LARC update (parameters compared)."""
+    loss, pred, got, ref = run_net(SMALL_BN, [64, 16, 4], 32, 2, dtype, True, False, 42 + (opt == "adam"), opt)
+    tol = TOL_BF16 if dtype == BF else TOL_F32
+    assert abs(loss - ref["loss"]) <= tol * ref["loss"]
+    assert rel_err(pred, ref["yhat"]) <= tol
+    want = ref["grads"] if opt == "sgd" else ref["params"]
+    errs = [rel_err(g, r) for g, r in zip(got, want)]
+    print("BN network (%s, %s) vs oracle: %s" % (dtype, opt, ", ".join("%.2e" % e for e in errs)))
+    assert max(errs) <= tol, errs
+
+
+def test_benchmark_network_through_net_step_equals_train_step():
+    """The 5-block benchmark network run by cf_net_train_step (unfused
+    kernels, single stream) equals cf_train_step (fused kernels, second
+    stream) bit for bit."""
+    from test_gpu_train import device_params, make_problem
+    B, size, filters, dense_w = 2, 32, [32, 64, 128], [64, 32, 3]
+    x, conv, dense, t = make_problem(7, B, size, filters, dense_w, BF)
+    xd, td = to_dev(x, BF), to_dev(t, F32)
+    p1, p2 = device_params(conv, dense), device_params(conv, dense)
+    m = cf.model_desc(4, size, filters, dense_w, SLOPE)
+    aux = cf.StepAux()
+    l1, _ = cf.cf_train_step(m, xd, td, p1, 1e-3, aux=aux)
+    mn = cf.net_desc(4, size, filters, dense=dense_w, slope=SLOPE)
+    l2, _ = cf.cf_net_train_step(mn, xd, td, p2, cf.sgd_optimizer(1e-3))
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2)
+    for a, b in zip(p1, p2):
+        assert torch.equal(a, b)

@@ -147,9 +147,11 @@ def test_train128_step_matches_oracle_end_to_end():
     names = ["conv%d_dW" % (l + 1) for l in range(L)]
     for k in range(3):
         names += ["dense%d_dW" % (k + 1), "dense%d_db" % (k + 1)]
+    print("GPU step done; oracle step (fp64, %d threads) ..." % oracle.num_threads(), flush=True)
     ref = oracle.train_step(x, t, conv, dense, LR_RECOVER, SLOPE, storage="bf16")
     spread = [0.0] * len(names)
     for seed in (1, 2):
+        print("oracle step with perturbed conv sums, seed %d ..." % seed, flush=True)
         alt = oracle.train_step(x, t, conv, dense, LR_RECOVER, SLOPE, storage="bf16",
                                 perturb=(np.random.default_rng(seed), PERTURB))
         spread = [max(s, rel_err(a, r)) for s, a, r in zip(spread, flat(alt), flat(ref))]
