@@ -95,8 +95,10 @@ cf_status check_conv(cf_dtype dt, const cf_dims& x, int32_t cout, const cf_conv&
 }
 
 // ------------------------------------------------------------ path choice
-enum class Fwd { Mfma, C4, Direct };
-enum class Wg { Mfma, C4, Direct };
+cf_dims with_c(const cf_dims& x, int64_t c) { cf_dims y = x; y.c = c; return y; }
+
+enum class Fwd { Mfma, C4, F32Mfma, Direct };
+enum class Wg { Mfma, C4, F32Mfma, Direct };
 
 // The MFMA conv kernels address a tile's six input planes (of `cin`
 // channels) and the weight copy with 32-bit byte offsets; a shape beyond
@@ -117,6 +119,7 @@ Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
         if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
         if (cin == 4 && c4_offsets_fit(x)) return Fwd::C4;
     }
+    if (dt == CF_F32 && conv_f32_mfma_ok(x, cout)) return Fwd::F32Mfma;
     return Fwd::Direct;
 }
 
@@ -125,6 +128,7 @@ Fwd dgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 32 == 0 && cin % 4 == 0 && mfma_offsets_fit(x, cout, cin)) return Fwd::Mfma;
+    if (dt == CF_F32 && conv_f32_mfma_ok(with_c(x, cout), (int)cin)) return Fwd::F32Mfma;
     return Fwd::Direct;
 }
 
@@ -134,6 +138,7 @@ Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
         if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
         if (x.c == 4 && cout == 32 && wgrad_c4_fits(x)) return Wg::C4;
     }
+    if (dt == CF_F32 && x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
     return Wg::Direct;
 }
 
@@ -163,6 +168,7 @@ size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
     switch (p) {
     case Fwd::Mfma: return (size_t)27 * roundup(cout, 128) * (size_t)cin * 2;
     case Fwd::C4: return (size_t)roundup(cout, 128) * 128 * 2;
+    case Fwd::F32Mfma: return conv_f32_wk_bytes((int)cin, cout);
     default: return 0;
     }
 }
@@ -170,10 +176,9 @@ size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
 size_t dgrad_wk_bytes(Fwd p, cf_dtype dt, int64_t cin, int cout)
 {
     if (p == Fwd::Mfma) return (size_t)27 * roundup((int)cin, 128) * (size_t)cout * 2;
+    if (p == Fwd::F32Mfma) return conv_f32_wk_bytes(cout, (int)cin);
     return (size_t)27 * (size_t)cin * cout * esize(dt);
 }
-
-cf_dims with_c(const cf_dims& x, int64_t c) { cf_dims y = x; y.c = c; return y; }
 
 // Stride 2 runs as the stride-1 convolution sampled at 2o + q (q = 1 - pad)
 // (k_resample.hip).  Output size ceil(size / 2).
@@ -195,6 +200,8 @@ hipError_t run_fwd(Fwd p, cf_dtype dt, const cf_dims& x, const void* X, const vo
     }
     case Fwd::C4:
         return launch_conv_c4_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, roundup(cout, 128), s);
+    case Fwd::F32Mfma:
+        return launch_conv_f32_mfma((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
     default:
         if (dt == CF_F32) return launch_conv_direct<float>((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
         return launch_conv_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, s);
@@ -216,6 +223,7 @@ hipError_t run_dgrad(Fwd p, cf_dtype dt, const cf_dims& x, const void* dY, const
         return launch_conv_mfma(plan, (const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, part, y, (int)x.c,
                                 roundup((int)x.c, 128), s);
     }
+    if (p == Fwd::F32Mfma) return launch_conv_f32_mfma((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
     if (dt == CF_F32) return launch_conv_direct<float>((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
     return launch_conv_direct<uint16_t>((const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, y, (int)x.c, s);
 }
@@ -227,6 +235,7 @@ size_t dgrad_part_bytes(Fwd p, const cf_dims& x, int cout)
 
 size_t wgrad_part_bytes(Wg p, cf_dtype dt, const cf_dims& x, int cout)
 {
+    if (p == Wg::F32Mfma) return plan_wgrad_f32(x, cout).part_bytes;
     if (p != Wg::Direct) return plan_wgrad(x, cout).part_bytes;
     return dt == CF_F32 ? wgrad_direct_part_bytes<float>(x, cout) : wgrad_direct_part_bytes<uint16_t>(x, cout);
 }
@@ -234,6 +243,8 @@ size_t wgrad_part_bytes(Wg p, cf_dtype dt, const cf_dims& x, int cout)
 hipError_t run_wgrad(Wg p, cf_dtype dt, const cf_dims& x, const void* X, const void* dY, int cout, float* dW,
                      float* part, hipStream_t s)
 {
+    if (p == Wg::F32Mfma)
+        return launch_wgrad_f32_mfma(plan_wgrad_f32(x, cout), (const float*)X, (const float*)dY, part, dW, x, cout, s);
     if (p != Wg::Direct) {
         const WgradPlan plan = plan_wgrad(x, cout);
         return launch_wgrad(plan, (const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
@@ -248,6 +259,7 @@ hipError_t prep_fwd(Fwd p, const void* W, bool src_f32, int64_t cin, int cout, v
     switch (p) {
     case Fwd::Mfma: return launch_wprep_fwd(W, src_f32, (int)cin, cout, roundup(cout, 128), (uint16_t*)wk, s);
     case Fwd::C4: return launch_wprep_c4(W, src_f32, cout, roundup(cout, 128), (uint16_t*)wk, s);
+    case Fwd::F32Mfma: return launch_wprep_f32((const float*)W, (int)cin, cout, false, (float*)wk, s);
     default: return hipSuccess;
     }
 }
@@ -255,6 +267,7 @@ hipError_t prep_fwd(Fwd p, const void* W, bool src_f32, int64_t cin, int cout, v
 hipError_t prep_dgrad(Fwd p, cf_dtype dt, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
 {
     if (p == Fwd::Mfma) return launch_wprep_dgrad(W, src_f32, (int)cin, cout, roundup((int)cin, 128), (uint16_t*)wk, s);
+    if (p == Fwd::F32Mfma) return launch_wprep_f32((const float*)W, (int)cin, cout, true, (float*)wk, s);
     return launch_wprep_direct_dgrad(W, dt, (int)cin, cout, wk, s);
 }
 
@@ -1056,10 +1069,16 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         else if (Lp.fwd == Fwd::C4)
             wl.job[wl.count++] = WprepJob{2, true, (int)Lp.x.c, Lp.cout, roundup(Lp.cout, 128), params[l],
                                           (uint16_t*)(w + Lp.wk_fwd)};
+        else if (Lp.fwd == Fwd::F32Mfma)
+            CF_TRY_HIP(launch_wprep_f32(params[l], (int)Lp.x.c, Lp.cout, false, (float*)(w + Lp.wk_fwd), stream),
+                       "weight re-layout");
         if (l > 0) {
             if (Lp.dg == Fwd::Mfma) {
                 wl.job[wl.count++] = WprepJob{1, true, (int)Lp.x.c, Lp.cout, roundup((int)Lp.x.c, 128), params[l],
                                               (uint16_t*)(w + Lp.wk_dg)};
+            } else if (Lp.dg == Fwd::F32Mfma) {
+                CF_TRY_HIP(launch_wprep_f32(params[l], (int)Lp.x.c, Lp.cout, true, (float*)(w + Lp.wk_dg), stream),
+                           "weight re-layout");
             } else if (bf) {
                 const int64_t n = (int64_t)27 * Lp.x.c * Lp.cout;
                 hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,

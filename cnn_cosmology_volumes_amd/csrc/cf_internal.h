@@ -158,7 +158,7 @@ hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16
 // Backward-weight on MFMA.  Partial sums per voxel split into `part`
 // ([splits][27*cin*cout] fp32), then a fixed-order reduction into dW.
 struct WgradPlan {
-    int kind;         // 0: cin % 32 == 0; 1: cin == 4
+    int kind;         // 0: cin % 32 == 0; 1: cin == 4; 2: fp32
     int splits;
     int64_t vox_per_split;
     size_t part_bytes;
@@ -175,6 +175,17 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
 hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uint16_t* dP, const uint16_t* P,
                                 const uint8_t* idx, float slope, float* part, float* dW, const cf_dims& x,
                                 hipStream_t s);
+
+// fp32 convolution on the matrix cores (k_conv_f32.hip); channel counts
+// multiples of 4.  Weights re-laid as [27][rup(out,64)][rup(in,16)] fp32
+// (backward-data: flipped taps, in = forward cout, out = forward cin).
+bool conv_f32_mfma_ok(const cf_dims& x, int cout);
+size_t conv_f32_wk_bytes(int in, int out);
+hipError_t launch_wprep_f32(const float* W, int cin, int cout, bool dgrad, float* Wk, hipStream_t s);
+hipError_t launch_conv_f32_mfma(const float* X, const float* Wk, float* Y, const cf_dims& x, int cout, hipStream_t s);
+WgradPlan plan_wgrad_f32(const cf_dims& x, int cout);
+hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float* dY, float* part, float* dW,
+                                 const cf_dims& x, int cout, hipStream_t s);
 
 // Direct (non-MFMA) conv kernels for fp32 and for shapes outside the MFMA
 // paths.  T = float or uint16_t (bf16).  Wt layout is DHWIO for the forward;

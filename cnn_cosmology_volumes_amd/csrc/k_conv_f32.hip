@@ -1,0 +1,302 @@
+// fp32 3^3 convolution on the matrix cores (v_mfma_f32_16x16x4_f32): the
+// forward and backward-data (forward orientation on flipped, transposed
+// weights) and the backward-weight of the fp32 path, for any channel counts
+// that are multiples of 4.  Same definitions as the bf16 kernels (Oyama et
+// al., Sec. IV / Table I: stride 1, "same" zero padding, no bias).
+//
+// Fragments.  One 16x16x4 MFMA takes, per lane l, A[l % 16][l / 16] and
+// B[l / 16][l % 16] and accumulates D[4 (l / 16) + r][l % 16], r = 0..3.  A
+// lane here loads four consecutive K values as one float4 and the wave runs
+// four MFMAs q = 0..3 on them: MFMA q's K index k stands for K value 4k + q,
+// so the four MFMAs cover 16 K values and every operand fetch is one
+// aligned 16-byte read.
+//
+// Forward tile: 64 output channels x a 4x4x4 voxel box per block (4 waves;
+// wave w owns output-channel tiles 2 (w & 1) .. + 1 and the box's depth
+// planes 2 (w >> 1) .. + 1).  The 6x6x6 input halo of 16 channels is staged
+// in LDS per channel chunk; B fragments read it at a per-tap offset, A
+// fragments (weights [tap][co][ci], padded) come from global/L2 one tap ahead.
+//
+// Backward-weight tile: 16 input channels x 64 output channels x all 27 taps
+// per block (wave w owns output channels 16 w .. 16 w + 15), over a fixed
+// range of 4x4x4 boxes.  Per box the input halo is staged transposed as
+// three w-shifted copies XT[kw][ci][hd][hh][w] (so a tap's operand is an
+// aligned float4 of four consecutive voxels) and the output gradient as
+// DT[co][voxel].  Each block writes its fp32 partial dW; a fixed-order
+// reduction adds the splits.
+#include "cf_internal.h"
+#include "wgrad_common.h"
+
+namespace cf {
+namespace {
+
+constexpr int F_T = 256;        // threads per block (4 waves)
+constexpr int F_BM = 64;        // output channels per forward block
+constexpr int F_CC = 16;        // channels per staged chunk
+constexpr int F_B = 4;          // box edge (voxels)
+constexpr int F_H = F_B + 2;    // halo edge
+constexpr int F_HV = F_H * F_H * F_H;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma4(const f4& a, const f4& b, f4 acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ f4 ld4g(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+// Y[n, d, h, w, co] = sum_tap sum_ci X[n, d+kd-1, h+kh-1, w+kw-1, ci] Wk[tap][co][ci]
+// Wk: [27][copad][cipad] fp32, zero beyond cout / cin; copad % 64 == 0, cipad % 16 == 0.
+__global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restrict__ X, const float* __restrict__ Wk,
+                                                            float* __restrict__ Y, int N, int D, int H, int W,
+                                                            int Cin, int Cout, int cipad, int copad, int bD, int bH,
+                                                            int bW)
+{
+    __shared__ f4 halo[F_HV * (F_CC / 4)];       // [halo voxel][4 channel quads]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int b = blockIdx.x;
+    const int ncb = copad / F_BM;
+    const int cb = b % ncb; b /= ncb;
+    const int bw = b % bW; b /= bW;
+    const int bh = b % bH; b /= bH;
+    const int bd = b % bD;
+    const int n = b / bD;
+    const int d0 = bd * F_B, h0 = bh * F_B, w0 = bw * F_B;
+    const int i16 = lane & 15, k4 = lane >> 4;
+    // this lane's voxel in its wave's depth planes: h = i16 / 4, w = i16 % 4
+    const int vh = i16 >> 2, vw = i16 & 3;
+    const int dp0 = 2 * (wave >> 1);
+    const int co_w = cb * F_BM + 32 * (wave & 1);
+    f4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = 0; c0 < Cin; c0 += F_CC) {
+        __syncthreads();
+        for (int i = tid; i < F_HV * 4; i += F_T) {
+            const int q = i & 3, hv = i >> 2;
+            const int hx = hv % F_H, hy = (hv / F_H) % F_H, hz = hv / (F_H * F_H);
+            const int id = d0 + hz - 1, ih = h0 + hy - 1, iw = w0 + hx - 1, ci = c0 + 4 * q;
+            f4 v = f4{0.f, 0.f, 0.f, 0.f};
+            if ((unsigned)id < (unsigned)D && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W && ci < Cin)
+                v = ld4g(X + ((((int64_t)n * D + id) * H + ih) * W + iw) * Cin + ci);
+            halo[i] = v;
+        }
+        __syncthreads();
+        const float* wbase = Wk + (int64_t)(co_w + i16) * cipad + c0 + 4 * k4;
+        const int64_t tapstride = (int64_t)copad * cipad;
+        f4 a0 = ld4g(wbase), a1 = ld4g(wbase + 16 * cipad);
+#pragma unroll 1
+        for (int t = 0; t < 27; ++t) {
+            const int kd = t / 9, kh = (t / 3) % 3, kw = t % 3;
+            f4 n0 = a0, n1 = a1;
+            if (t + 1 < 27) {
+                n0 = ld4g(wbase + (t + 1) * tapstride);
+                n1 = ld4g(wbase + (t + 1) * tapstride + 16 * cipad);
+            }
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) {
+                const int hv = ((dp0 + vt + kd) * F_H + vh + kh) * F_H + vw + kw;
+                const f4 bv = halo[hv * 4 + k4];
+                acc[0][vt] = mfma4(a0, bv, acc[0][vt]);
+                acc[1][vt] = mfma4(a1, bv, acc[1][vt]);
+            }
+            a0 = n0;
+            a1 = n1;
+        }
+    }
+    // D[4 k4 + r][i16]: output channels co_w + 16 ct + 4 k4 + r, voxel i16 of plane dp0 + vt
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+        const int d = d0 + dp0 + vt, h = h0 + vh, w = w0 + vw;
+        if (d >= D || h >= H || w >= W) continue;
+        float* yp = Y + ((((int64_t)n * D + d) * H + h) * W + w) * Cout;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int co = co_w + 16 * ct + 4 * k4;
+            if (co < Cout) *reinterpret_cast<f4*>(yp + co) = acc[ct][vt];
+        }
+    }
+}
+
+constexpr int G_BN = 64;         // output channels per backward-weight block
+constexpr int G_XT = 3 * F_CC * F_H * F_H * 4;   // floats of the three shifted halo copies
+constexpr int G_DT = G_BN * 64;                  // floats of the transposed output gradient
+
+// part[split][tap][ci][co] over the boxes [split * per, min(nbox, (split+1) * per)).
+__global__ __launch_bounds__(F_T) void wgrad_f32_mfma_kernel(const float* __restrict__ X, const float* __restrict__ dY,
+                                                             float* __restrict__ part, int N, int D, int H, int W,
+                                                             int Cin, int Cout, int bD, int bH, int bW, int nci,
+                                                             int nco, int64_t nbox, int per)
+{
+    __shared__ float xt[G_XT];     // [kw][ci 16][hd 6][hh 6][w 4]
+    __shared__ float dt[G_DT];     // [co 64][voxel 64], voxel = (d * 4 + h) * 4 + w
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int b = blockIdx.x;
+    const int cit = b % nci; b /= nci;
+    const int cot = b % nco;
+    const int split = b / nco;
+    const int ci0 = cit * F_CC, co0 = cot * G_BN;
+    const int i16 = lane & 15, k4 = lane >> 4;
+    f4 acc[27];
+#pragma unroll
+    for (int t = 0; t < 27; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    const int64_t bb0 = (int64_t)split * per;
+    const int64_t bb1 = min(nbox, bb0 + per);
+    for (int64_t bx = bb0; bx < bb1; ++bx) {
+        int64_t r = bx;
+        const int bw = (int)(r % bW); r /= bW;
+        const int bh = (int)(r % bH); r /= bH;
+        const int bd = (int)(r % bD);
+        const int n = (int)(r / bD);
+        const int d0 = bd * F_B, h0 = bh * F_B, w0 = bw * F_B;
+        __syncthreads();
+        // input halo: 216 voxels x 4 channel quads, scattered into the three w-shifted copies
+        for (int i = tid; i < F_HV * 4; i += F_T) {
+            const int q = i & 3, hv = i >> 2;
+            const int hx = hv % F_H, hy = (hv / F_H) % F_H, hz = hv / (F_H * F_H);
+            const int id = d0 + hz - 1, ih = h0 + hy - 1, iw = w0 + hx - 1, ci = ci0 + 4 * q;
+            f4 v = f4{0.f, 0.f, 0.f, 0.f};
+            if ((unsigned)id < (unsigned)D && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W && ci < Cin)
+                v = ld4g(X + ((((int64_t)n * D + id) * H + ih) * W + iw) * Cin + ci);
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const int w = hx - kw;
+                if (w < 0 || w >= F_B) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xt[(((kw * F_CC + 4 * q + e) * F_H + hz) * F_H + hy) * 4 + w] = v[e];
+            }
+        }
+        // output gradient: 64 voxels x 16 channel quads, transposed to [co][voxel]
+        for (int i = tid; i < 64 * (G_BN / 4); i += F_T) {
+            const int q = i % (G_BN / 4), v = i / (G_BN / 4);
+            const int vw = v & 3, vh = (v >> 2) & 3, vd = v >> 4;
+            const int d = d0 + vd, h = h0 + vh, w = w0 + vw, co = co0 + 4 * q;
+            f4 g = f4{0.f, 0.f, 0.f, 0.f};
+            if (d < D && h < H && w < W && co < Cout)
+                g = ld4g(dY + ((((int64_t)n * D + d) * H + h) * W + w) * Cout + co);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dt[(4 * q + e) * 64 + v] = g[e];
+        }
+        __syncthreads();
+        // K = the box's 64 voxels: depth plane dp, lane group k4 = h, four w per float4
+#pragma unroll 1
+        for (int dp = 0; dp < F_B; ++dp) {
+            const f4 bv = *reinterpret_cast<const f4*>(&dt[(16 * wave + i16) * 64 + dp * 16 + k4 * 4]);
+#pragma unroll
+            for (int t = 0; t < 27; ++t) {
+                const int kd = t / 9, kh = (t / 3) % 3, kw = t % 3;
+                const f4 av =
+                    *reinterpret_cast<const f4*>(&xt[(((kw * F_CC + i16) * F_H + dp + kd) * F_H + k4 + kh) * 4]);
+                acc[t] = mfma4(av, bv, acc[t]);
+            }
+        }
+    }
+    // D[4 k4 + r][i16] = dW[tap][ci0 + 4 k4 + r][co0 + 16 wave + i16]
+    const int co = co0 + 16 * wave + i16;
+    if (co >= Cout) return;
+    const int64_t dws = (int64_t)27 * Cin * Cout;
+    float* out = part + (int64_t)split * dws;
+#pragma unroll
+    for (int t = 0; t < 27; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ci = ci0 + 4 * k4 + e;
+            if (ci < Cin) out[((int64_t)t * Cin + ci) * Cout + co] = acc[t][e];
+        }
+}
+
+// Wk[t][a][b] (a < apad, b < bpad) from DHWIO W[tap][ci][co] fp32:
+// forward (flip = 0): a = co, b = ci, tap = t;  backward-data (flip = 1):
+// a = ci, b = co, tap = 26 - t.
+__global__ void wprep_f32_kernel(const float* __restrict__ W, float* __restrict__ Wk, int cin, int cout, int apad,
+                                 int bpad, int flip)
+{
+    const int64_t total = (int64_t)27 * apad * bpad;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int bi = (int)(i % bpad);
+    const int ai = (int)((i / bpad) % apad);
+    const int t = (int)(i / ((int64_t)bpad * apad));
+    const int ci = flip ? ai : bi, co = flip ? bi : ai;
+    const int tap = flip ? 26 - t : t;
+    Wk[i] = (ci < cin && co < cout) ? W[((int64_t)tap * cin + ci) * cout + co] : 0.f;
+}
+
+int rup(int v, int m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+bool conv_f32_mfma_ok(const cf_dims& x, int cout)
+{
+    // 32-bit block ids and channel multiples of 4 for the float4 accesses
+    const int64_t nb = x.n * ((x.d + 3) / 4) * ((x.h + 3) / 4) * ((x.w + 3) / 4);
+    return x.c % 4 == 0 && cout % 4 == 0 && nb * ((cout + 63) / 64) < ((int64_t)1 << 31);
+}
+
+size_t conv_f32_wk_bytes(int cin, int cout) { return (size_t)27 * rup(cout, 64) * rup(cin, 16) * 4; }
+
+hipError_t launch_wprep_f32(const float* W, int cin, int cout, bool dgrad, float* Wk, hipStream_t s)
+{
+    // forward: [27][rup(cout, 64)][rup(cin, 16)]; backward-data: in = cout, out = cin
+    const int apad = dgrad ? rup(cin, 64) : rup(cout, 64);
+    const int bpad = dgrad ? rup(cout, 16) : rup(cin, 16);
+    const int64_t total = (int64_t)27 * apad * bpad;
+    hipLaunchKernelGGL(wprep_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, Wk, cin, cout,
+                       apad, bpad, dgrad ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_f32_mfma(const float* X, const float* Wk, float* Y, const cf_dims& x, int cout, hipStream_t s)
+{
+    const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + 3) / 4), bW = (int)((x.w + 3) / 4);
+    const int copad = rup(cout, 64), cipad = rup((int)x.c, 16);
+    const int64_t nb = x.n * bD * bH * bW * (copad / 64);
+    hipLaunchKernelGGL(conv_f32_mfma_kernel, dim3((unsigned)nb), dim3(F_T), 0, s, X, Wk, Y, (int)x.n, (int)x.d,
+                       (int)x.h, (int)x.w, (int)x.c, cout, cipad, copad, bD, bH, bW);
+    return hipGetLastError();
+}
+
+WgradPlan plan_wgrad_f32(const cf_dims& x, int cout)
+{
+    WgradPlan p{};
+    p.kind = 2;
+    const int64_t nbox = x.n * ((x.d + 3) / 4) * ((x.h + 3) / 4) * ((x.w + 3) / 4);
+    const int64_t outer = (int64_t)((x.c + 15) / 16) * ((cout + 63) / 64);
+    const int64_t dw_bytes = (int64_t)27 * x.c * cout * 4;
+    int64_t want = (1024 + outer - 1) / outer;               // about four blocks per CU
+    int64_t cap = (int64_t)(64ll << 20) / dw_bytes;          // bound the partials to ~64 MiB
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want > nbox) want = nbox;
+    if (want < 1) want = 1;
+    const int64_t per = (nbox + want - 1) / want;
+    p.splits = (int)((nbox + per - 1) / per);
+    p.vox_per_split = per;    // boxes per split
+    p.part_bytes = (size_t)p.splits * (size_t)dw_bytes;
+    return p;
+}
+
+hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float* dY, float* part, float* dW,
+                                 const cf_dims& x, int cout, hipStream_t s)
+{
+    const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + 3) / 4), bW = (int)((x.w + 3) / 4);
+    const int nci = (int)((x.c + 15) / 16), nco = (cout + 63) / 64;
+    const int64_t nbox = x.n * bD * bH * bW;
+    hipLaunchKernelGGL(wgrad_f32_mfma_kernel, dim3((unsigned)((int64_t)nci * nco * p.splits)), dim3(F_T), 0, s, X, dY,
+                       part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nci, nco, nbox,
+                       (int)p.vox_per_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_wgrad_reduce(part, dW, (int64_t)27 * x.c * cout, p.splits, s);
+}
+
+}  // namespace cf

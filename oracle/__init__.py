@@ -513,7 +513,7 @@ def net_param_shapes(cin, layers, dense, batch_norm, dense_bias, in_size):
 
 
 def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, bn_eps=1e-5, dense_bias=True,
-                   storage="f64", opt=("sgd", 1e-3), adam_state=None):
+                   storage="f64", opt=("sgd", 1e-3), adam_state=None, perturb=None):
     """One training step of a general conv network (the extended CosmoFlow
     network of Oyama et al., Table I and Sec. IV, and the benchmark network
     alike): per layer a 3^3 "same" conv of the given stride without bias,
@@ -525,6 +525,8 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     batch-norm output, layer output and their gradients; conv weights are
     the masters rounded to ``storage``.  opt: ("sgd", lr) or ("adam", lr_t,
     beta1, beta2, eps, trust, t) with adam_state = (m list, v list).
+    perturb: the conditioning probe of network_forward (conv sums scaled by
+    1 + r u before their storage rounding).
     Returns dict(loss, yhat, grads, params, adam_state)."""
     L = len(layers)
     per = 3 if batch_norm else 1
@@ -543,7 +545,11 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     a = store(x, storage)
     cache = []
     for l, (f, s, pool) in enumerate(layers):
-        z = store(conv(a, wuse[l], s), storage)
+        z = conv(a, wuse[l], s)
+        if perturb is not None:
+            g_, r_ = perturb
+            z *= 1.0 + r_ * g_.uniform(-1.0, 1.0, z.shape)
+        z = store(z, storage)
         y, mean, invstd = z, None, None
         if batch_norm:
             y, mean, invstd = batchnorm_fwd(z, gam[l], bet[l], bn_eps)

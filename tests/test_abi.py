@@ -64,8 +64,10 @@ def test_conv_workspace_sizes():
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 32), 64, cf.CF_CONV_FWD) == 27 * 128 * 32 * 2
     # first layer (4 channels): [roundup(cout,128)][128]
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 128, 128, 128, 4), 32, cf.CF_CONV_FWD) == 128 * 128 * 2
-    # direct fp32 forward needs nothing
-    assert cf.cf_conv3d_workspace_size(cf.CF_F32, (1, 32, 32, 32, 4), 16, cf.CF_CONV_FWD) == 0
+    # fp32 forward on the matrix cores: fp32 weights [27][roundup(cout,64)][roundup(cin,16)]
+    assert cf.cf_conv3d_workspace_size(cf.CF_F32, (1, 32, 32, 32, 4), 16, cf.CF_CONV_FWD) == 27 * 64 * 16 * 4
+    # the direct fp32 kernel (channels not multiples of 4) needs nothing
+    assert cf.cf_conv3d_workspace_size(cf.CF_F32, (1, 32, 32, 32, 3), 16, cf.CF_CONV_FWD) == 0
     # small volume, many channels: split over in-channel chunks adds fp32 partials
     ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 8, 8, 8, 256), 256, cf.CF_CONV_FWD)
     assert ws > 27 * 256 * 256 * 2 and (ws - 27 * 256 * 256 * 2) % (4096 * 256 * 4) == 0
@@ -168,6 +170,20 @@ def test_negative_or_nan_slope_rejected():
     # slope 0 (plain ReLU) and 1 (plain max pooling) are valid
     m = cf.model_desc(4, 16, [32, 64], (32, 16, 3), 0.0)
     assert cf.cf_train_step_workspace_size(m, cf.CF_BF16, 2) > 0
+
+
+def test_noalloc_rejects_oversized_partials_before_any_gpu_call():
+    """cf_conv3d_bwd_weight_noalloc checks its partial sums against the
+    static scratch before touching the device: a 1024 -> 1024 layer's dW
+    alone (113 MB of fp32) exceeds CF_NOALLOC_SCRATCH_BYTES (64 MiB)."""
+    L = cf.lib()
+    st = L.cf_conv3d_bwd_weight_noalloc(cf.CF_F32, cf.dims((1, 2, 2, 2, 1024)), FAKE, FAKE, 1024, cf.CONV3, FAKE, None)
+    assert st == cf.CF_ERR_WORKSPACE and b"static scratch" in L.cf_last_error()
+    st = L.cf_conv3d_bwd_weight_noalloc(cf.CF_BF16, cf.dims((1, 8, 8, 8, 32)), MIS, FAKE, 32, cf.CONV3, FAKE, None)
+    assert st == cf.CF_ERR_INVALID
+    st = L.cf_conv3d_bwd_weight_noalloc(cf.CF_BF16, cf.dims((1, 8, 8, 8, 32)), FAKE, FAKE, 32, cf.cf_conv(3, 2, 0),
+                                        FAKE, None)
+    assert st == cf.CF_ERR_UNSUPPORTED
 
 
 def test_train_step_aux_validation():

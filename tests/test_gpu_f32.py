@@ -1,0 +1,82 @@
+"""GPU parity of the fp32 path on the matrix cores (v_mfma_f32_16x16x4_f32
+convolution kernels) against the fp64 oracle at max rel err <= 1e-5: small
+ragged shapes over whole tensors, and every conv layer of the 8 x 128^3 x 4
+five-block network on sampled outputs (conv outputs at random points and
+the volume corners, weight-gradient entries each a full sum over every
+voxel)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthdata as sd
+from cnn_cosmology_volumes_amd import cf
+from cnn_cosmology_volumes_amd.configs import CONFIGS
+from gpu_util import TOL_F32, host64, rel_err, sample_points, to_dev
+
+pytestmark = pytest.mark.gpu
+F32 = torch.float32
+
+SMALL = [(2, 5, 9, 7, 32, 64), (1, 6, 10, 7, 64, 128), (1, 9, 5, 18, 4, 32), (2, 3, 4, 5, 8, 12),
+         (1, 4, 4, 4, 256, 256), (1, 1, 1, 1, 16, 16), (2, 7, 6, 17, 12, 20)]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_f32_conv_passes_match_oracle(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) * 3)
+    x = sd.normal(rng, (N, D, H, W, Ci), bf16=False)
+    w = sd.he_normal_conv(rng, Ci, Co)
+    dy = sd.normal(rng, (N, D, H, W, Co), bf16=False)
+    xd, wd, dyd = to_dev(x, F32), to_dev(w, F32), to_dev(dy, F32)
+    y = cf.cf_conv3d_fwd(xd, wd)
+    dx = cf.cf_conv3d_bwd_data(dyd, wd)
+    dw = cf.cf_conv3d_bwd_weight(xd, dyd)
+    torch.cuda.synchronize()
+    assert rel_err(host64(y), oracle.conv3d_fwd(x, w)) <= TOL_F32
+    assert rel_err(host64(dx), oracle.conv3d_bwd_data(dy, w)) <= TOL_F32
+    assert rel_err(host64(dw), oracle.conv3d_bwd_weight(x, dy)) <= TOL_F32
+
+
+TRAIN128 = CONFIGS["train_bf16_128c4_b8"]
+LAYERS = []
+_s, _c = TRAIN128.in_size, TRAIN128.in_channels
+for _f in TRAIN128.filters:
+    LAYERS.append((_s, _c, _f))
+    _s, _c = _s // 2, _f
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("layer", range(len(LAYERS)))
+def test_f32_conv_layers_of_the_128_network_sampled(layer):
+    S, Ci, Co = LAYERS[layer]
+    B = TRAIN128.batch
+    st = sd.streams(TRAIN128.seed_id)
+    rng = np.random.default_rng(70 + layer)
+    if layer == 0:
+        x = sd.lognormal_poisson_input(st["field"], st["poisson"], (B, S, S, S), Ci, bf16=False)
+    else:
+        x = np.abs(sd.normal(st["field"], (B, S, S, S, Ci), bf16=False))
+    w = sd.he_normal_conv(st["convw"], Ci, Co)
+    dy = sd.normal(st["upstream"], (B, S, S, S, Co), bf16=False)
+    xd, wd, dyd = to_dev(x, F32), to_dev(w, F32), to_dev(dy, F32)
+    y = cf.cf_conv3d_fwd(xd, wd)
+    dw = cf.cf_conv3d_bwd_weight(xd, dyd)
+    dx = cf.cf_conv3d_bwd_data(dyd, wd) if layer > 0 else None
+    torch.cuda.synchronize()
+    pts = sample_points(rng, tuple(y.shape), 3000)
+    o = oracle.conv3d_fwd_points(x, w, pts)
+    g = host64(y.reshape(-1)[torch.from_numpy(pts).cuda()])
+    assert rel_err(g, o) <= TOL_F32
+    if dx is not None:
+        pts = sample_points(rng, tuple(dx.shape), 3000)
+        o = oracle.conv3d_bwd_data_points(dy, w, pts)
+        g = host64(dx.reshape(-1)[torch.from_numpy(pts).cuda()])
+        assert rel_err(g, o) <= TOL_F32
+    total = 27 * Ci * Co
+    pts = np.array(sorted(set(int(p) for p in rng.integers(0, total, 16)) | {0, total - 1, 13 * Ci * Co}), np.int64)
+    o = oracle.conv3d_bwd_weight_points(x, dy, pts)
+    g = host64(dw.reshape(-1)[torch.from_numpy(pts).cuda()])
+    e = np.max(np.abs(g - o)) / np.sqrt(np.mean(o * o))
+    print("fp32 layer %d (%d^3 x %d -> %d): weight-gradient entries max rel err %.2e" % (layer + 1, S, Ci, Co, e))
+    assert e <= TOL_F32

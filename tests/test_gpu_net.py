@@ -119,79 +119,120 @@ def init_params(rng, shapes, batch_norm):
     return ps
 
 
-def run_net(layers, dense, size, B, dtype, batch_norm, dense_bias, seed, opt="sgd"):
+def net_problem(layers, dense, size, B, dtype, batch_norm, dense_bias, seed):
     rng = np.random.default_rng(seed)
     x = sd.lognormal_poisson_input(rng, rng, (B, size, size, size), 4, bf16=(dtype == BF))
     t = sd.targets(rng, B, dense[-1])
     m = make_net(layers, dense, 4, size, batch_norm, dense_bias)
     shapes = oracle.net_param_shapes(4, layers, dense, batch_norm, dense_bias, size)
     assert [int(np.prod(s)) for s in shapes] == cf.cf_net_param_count(m)
-    params = init_params(rng, shapes, batch_norm)
+    return x, t, m, init_params(rng, shapes, batch_norm)
+
+
+# Relative size of the conditioning perturbation of the oracle's conv sums
+# (about the fp32 accumulation error of the GPU's sums).
+PERTURB = 2.0 ** -22
+
+
+def oracle_spread(x, t, params, layers, dense, batch_norm, dense_bias, storage, ref_grads):
+    """How far the step's gradients are determined by the arithmetic: the
+    largest rel_err between the oracle's gradients and those of two oracle
+    runs whose conv sums are perturbed by PERTURB before rounding.  Leaky-ReLU
+    kinks (either slope is accepted there), near-tied max-pool windows, and
+    at small batches the few terms of the deep layers' and the head's
+    gradients make single decisions weigh heavily."""
+    spread = [0.0] * len(ref_grads)
+    for seed in (1, 2):
+        print("oracle step with perturbed conv sums, seed %d ..." % seed, flush=True)
+        alt = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
+                                    storage=storage, opt=("sgd", LR_RECOVER),
+                                    perturb=(np.random.default_rng(seed), PERTURB))
+        spread = [max(sp, rel_err(a, r)) for sp, a, r in zip(spread, alt["grads"], ref_grads)]
+    return spread
+
+
+def check_net_step(layers, dense, size, B, dtype, batch_norm, dense_bias, seed, label):
+    """SGD step with a power-of-two rate (gradients recovered from the
+    update): loss and predictions gated at the path's tolerance, each
+    gradient at max(tolerance, 2 x the oracle's own spread)."""
+    x, t, m, params = net_problem(layers, dense, size, B, dtype, batch_norm, dense_bias, seed)
     pd = [to_dev(p, F32) for p in params]
     old = [host64(p) for p in pd]
     pred = torch.empty((B, dense[-1]), dtype=F32, device="cuda")
-    if opt == "sgd":
-        o = cf.sgd_optimizer(LR_RECOVER)
-        loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, o, pred=pred)
-    else:
-        hp = cf.adam_larc_params(0.01, lr_end=0.001, decay_steps=10, trust=0.02)
-        mom = ([torch.zeros_like(p) for p in pd], [torch.zeros_like(p) for p in pd])
-        loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, cf.adam_optimizer(hp, 1), moments=mom,
-                                       pred=pred)
+    loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, cf.sgd_optimizer(LR_RECOVER), pred=pred)
     torch.cuda.synchronize()
+    grads = [(o_ - host64(p)) / LR_RECOVER for o_, p in zip(old, pd)]
     storage = "bf16" if dtype == BF else "f32"
-    if opt == "sgd":
-        ref = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
-                                    storage=storage, opt=("sgd", LR_RECOVER))
-        grads = [(o_ - host64(p)) / LR_RECOVER for o_, p in zip(old, pd)]
-        return loss.item(), host64(pred), grads, ref
-    f = lambda v: float(np.float32(v))
-    z = [np.zeros(p.shape) for p in params]
+    print("GPU step done; oracle step ...", flush=True)
     ref = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
-                                storage=storage, opt=("adam", f(0.01), f(0.9), f(0.999), f(1e-8), f(0.02), 1),
-                                adam_state=(z, z))
-    return loss.item(), host64(pred), [host64(p) for p in pd], ref
+                                storage=storage, opt=("sgd", LR_RECOVER))
+    spread = oracle_spread(x, t, params, layers, dense, batch_norm, dense_bias, storage, ref["grads"])
+    tol = TOL_BF16 if dtype == BF else TOL_F32
+    e_loss = abs(loss.item() - ref["loss"]) / ref["loss"]
+    e_pred = rel_err(host64(pred), ref["yhat"])
+    errs = [rel_err(g, r) for g, r in zip(grads, ref["grads"])]
+    print("%s (%s) vs oracle: loss %.2e, pred %.2e; gradients %s" % (
+        label, dtype, e_loss, e_pred, ", ".join("%.2e (spread %.2e)" % es for es in zip(errs, spread))), flush=True)
+    assert e_loss <= tol and e_pred <= tol
+    bad = [(i, e, sp) for i, (e, sp) in enumerate(zip(errs, spread)) if not e <= max(tol, 2.0 * sp)]
+    assert not bad, bad
 
 
 TABLE1_128 = [(16, 1, "avg"), (32, 1, "avg"), (64, 1, "avg"), (128, 2, "avg"), (256, 1, "avg"), (256, 1, "none"),
               (256, 1, "none")]
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("dtype", [BF, F32])
 def test_table1_network_step_matches_oracle(dtype):
-    """The extended network of Oyama et al., Table I, at 128^3 (batch 2):
-    loss, predictions and every weight gradient against the untied oracle.
-    Average pooling has no argmax decisions, so the comparison is direct."""
+    """The extended network of Oyama et al., Table I, at 128^3 (batch 2)."""
     net = oyama_table1_net(128)
     assert [(L.cout, L.stride, "avg" if L.pool else "none") for L in net.convs] == TABLE1_128
-    loss, pred, grads, ref = run_net(TABLE1_128, [2048, 256, 4], 128, 2, dtype, False, False, 41)
-    tol = TOL_BF16 if dtype == BF else TOL_F32
-    errs = {"loss": abs(loss - ref["loss"]) / ref["loss"], "pred": rel_err(pred, ref["yhat"])}
-    for i, (g, r) in enumerate(zip(grads, ref["grads"])):
-        errs["grad%d" % i] = rel_err(g, r)
-    print("Table I 128^3 network step (%s) vs oracle: %s" % (dtype, ", ".join("%s %.2e" % kv for kv in errs.items())))
-    bad = {k: v for k, v in errs.items() if not v <= tol}
-    assert not bad, bad
+    check_net_step(TABLE1_128, [2048, 256, 4], 128, 2, dtype, False, False, 41, "Table I 128^3 network step")
 
 
 SMALL_BN = [(16, 1, "avg"), (32, 1, "max"), (64, 2, "avg"), (64, 1, "none")]
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("dtype", [BF, F32])
-@pytest.mark.parametrize("opt", ["sgd", "adam"])
-def test_bn_network_step_matches_oracle(dtype, opt):
+def test_bn_network_step_matches_oracle(dtype):
     """Batch norm after every conv, average / max / no pooling, a stride-2
-    layer, no dense bias; SGD (gradients recovered from the update) or one
-    Adam + LARC update (parameters compared)."""
-    loss, pred, got, ref = run_net(SMALL_BN, [64, 16, 4], 32, 2, dtype, True, False, 42 + (opt == "adam"), opt)
+    layer, no dense bias."""
+    check_net_step(SMALL_BN, [64, 16, 4], 32, 2, dtype, True, False, 42, "BN network step")
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_bn_network_adam_step_matches_oracle(dtype):
+    """One Adam + LARC update inside cf_net_train_step.  Its first step
+    moves each weight by about lr_l * sign(g), so an element whose gradient
+    is within the arithmetic's spread of zero may legitimately move either
+    way; the update is compared where the oracle's gradient is at least 5%
+    of its tensor's RMS (and the loss and predictions everywhere)."""
+    layers, dense = SMALL_BN, [64, 16, 4]
+    x, t, m, params = net_problem(layers, dense, 32, 2, dtype, True, False, 43)
+    pd = [to_dev(p, F32) for p in params]
+    hp = cf.adam_larc_params(0.01, lr_end=0.001, decay_steps=10, trust=0.02)
+    mom = ([torch.zeros_like(p) for p in pd], [torch.zeros_like(p) for p in pd])
+    pred = torch.empty((2, dense[-1]), dtype=F32, device="cuda")
+    loss, _ = cf.cf_net_train_step(m, to_dev(x, dtype), to_dev(t, F32), pd, cf.adam_optimizer(hp, 1), moments=mom,
+                                   pred=pred)
+    torch.cuda.synchronize()
+    f = lambda v: float(np.float32(v))
+    z = [np.zeros(p.shape) for p in params]
+    storage = "bf16" if dtype == BF else "f32"
+    ref = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=True, dense_bias=False, storage=storage,
+                                opt=("adam", f(0.01), f(0.9), f(0.999), f(1e-8), f(0.02), 1), adam_state=(z, z))
     tol = TOL_BF16 if dtype == BF else TOL_F32
-    assert abs(loss - ref["loss"]) <= tol * ref["loss"]
-    assert rel_err(pred, ref["yhat"]) <= tol
-    want = ref["grads"] if opt == "sgd" else ref["params"]
-    errs = [rel_err(g, r) for g, r in zip(got, want)]
-    print("BN network (%s, %s) vs oracle: %s" % (dtype, opt, ", ".join("%.2e" % e for e in errs)))
-    assert max(errs) <= tol, errs
+    assert abs(loss.item() - ref["loss"]) <= tol * ref["loss"]
+    assert rel_err(host64(pred), ref["yhat"]) <= tol
+    for i, (p, g, want, p0) in enumerate(zip(pd, ref["grads"], ref["params"], params)):
+        got = host64(p)
+        step = np.abs(got - p0)
+        assert np.all(step <= 0.01 * 1.0001 + 1e-7), i          # Adam's first step is at most lr_t
+        sure = np.abs(g) >= 0.05 * np.sqrt(np.mean(g * g))
+        d_got, d_want = (got - p0)[sure], (want - p0)[sure]
+        assert rel_err(d_got, d_want) <= (TOL_BF16 if dtype == BF else 1e-4), i
 
 
 def test_benchmark_network_through_net_step_equals_train_step():

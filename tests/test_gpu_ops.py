@@ -209,7 +209,9 @@ def test_lrelu(dtype):
 DENSE_CASES = [(8, 16384, 128, SLOPE), (8, 128, 64, SLOPE), (8, 64, 3, -1.0), (3, 1000, 77, SLOPE),
                (11, 300, 5, -1.0), (1, 16384, 128, SLOPE),
                # more than one staged batch chunk (32 rows) and column chunk (128), ragged row block
-               (40, 100, 130, SLOPE)]
+               (40, 100, 130, SLOPE),
+               # the head of Oyama et al.'s Table I network: fc 2048 -> 2048 -> 256 -> 4
+               (2, 2048, 2048, SLOPE), (2, 2048, 256, SLOPE), (2, 256, 4, -1.0)]
 
 
 @pytest.mark.parametrize("case", DENSE_CASES)

@@ -2,8 +2,9 @@
 in the library's static per-device scratch) against cf_conv3d_bwd_weight
 with a caller workspace: identical bits, on two calls in a row where the
 second is smaller (the scratch keeps the first call's contents, which the
-second must not see), for each backward-weight path (MFMA for Cin % 32 == 0,
-the 4-channel first layer, the direct fp32 kernel)."""
+second must not see), for each backward-weight path (bf16 MFMA for Cin % 32
+== 0, the 4-channel first layer, fp32 on the matrix cores, the direct fp32
+kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +19,8 @@ CASES = [
     # (dtype, first shape, second smaller shape, cout)
     (BF, (8, 64, 64, 64, 32), (2, 16, 16, 16, 32), 64),      # the 128^3 step's second block, then a small one
     (BF, (2, 34, 20, 18, 4), (1, 6, 10, 14, 4), 32),         # first-layer kernel, ragged boxes
-    (F32, (2, 12, 10, 9, 8), (1, 5, 6, 7, 8), 16),           # direct fp32 kernel
+    (F32, (2, 12, 10, 9, 8), (1, 5, 6, 7, 8), 16),           # fp32 matrix-core kernel
+    (F32, (2, 6, 5, 7, 3), (1, 4, 3, 5, 3), 5),              # direct fp32 kernel (channels not multiples of 4)
 ]
 
 
@@ -43,11 +45,11 @@ def test_noalloc_equals_workspace_entry_point(case):
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
-    # fp32 direct backward-weight of a 256 -> 256 layer: 128 splits of a
-    # 7 MB dW is far beyond the 64 MiB scratch
-    x = torch.zeros((1, 64, 64, 32, 256), dtype=F32, device="cuda")
-    dy = torch.zeros((1, 64, 64, 32, 256), dtype=F32, device="cuda")
-    dw = torch.zeros((3, 3, 3, 256, 256), dtype=F32, device="cuda")
+    # a 1024 -> 1024 layer's dW alone (27 x 1024 x 1024 fp32 = 113 MB) is
+    # beyond the 64 MiB scratch, whatever the split
+    x = torch.zeros((1, 2, 2, 2, 1024), dtype=F32, device="cuda")
+    dy = torch.zeros((1, 2, 2, 2, 1024), dtype=F32, device="cuda")
+    dw = torch.zeros((3, 3, 3, 1024, 1024), dtype=F32, device="cuda")
     with pytest.raises(cf.CfError) as e:
         cf.cf_conv3d_bwd_weight_noalloc(x, dy, dw)
     assert e.value.status == cf.CF_ERR_WORKSPACE
