@@ -54,6 +54,22 @@ def _compile(src: str, obj: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_peak.hip")
+PROBE_LIB = os.path.join(HERE, "libcfprobe.so")
+
+
+def build_probe() -> str:
+    """The matrix-core throughput probe used by bench.py --mfma-peak (a
+    library of its own, not linked into libcf.so)."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + COMMON + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe build failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(jobs: int = 0) -> str:
     """Compile every csrc/*.hip and link libcf.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -68,6 +84,7 @@ def build(jobs: int = 0) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
 
 

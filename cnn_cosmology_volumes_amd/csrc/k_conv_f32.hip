@@ -23,9 +23,15 @@
 // three w-shifted copies XT[kw][ci][hd][hh][w] (so a tap's operand is an
 // aligned float4 of four consecutive voxels) and the output gradient as
 // DT[co][voxel].  Each block writes its fp32 partial dW; a fixed-order
-// reduction adds the splits.
+// reduction adds the splits in fp64.
+//
+// Summation length.  fp32 chains grow their rounding error with their
+// length, and these sums are long (27 x 256 terms per forward output, up to
+// ~10^7 voxels per weight gradient).  The forward accumulates each 16-channel
+// chunk (432 products) in fresh registers and adds the chunk sums into the
+// total; the backward-weight gives each split at most BOX_PER_SPLIT boxes
+// (1024 products per accumulator) and adds the splits in fp64.
 #include "cf_internal.h"
-#include "wgrad_common.h"
 
 namespace cf {
 namespace {
@@ -72,13 +78,18 @@ __global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restr
     const int vh = i16 >> 2, vw = i16 & 3;
     const int dp0 = 2 * (wave >> 1);
     const int co_w = cb * F_BM + 32 * (wave & 1);
-    f4 acc[2][2];
+    f4 tot[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 2; ++c) tot[a][c] = f4{0.f, 0.f, 0.f, 0.f};
 
     for (int c0 = 0; c0 < Cin; c0 += F_CC) {
+        f4 acc[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) acc[a][c] = f4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
         for (int i = tid; i < F_HV * 4; i += F_T) {
             const int q = i & 3, hv = i >> 2;
@@ -111,6 +122,10 @@ __global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restr
             a0 = n0;
             a1 = n1;
         }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) tot[a][c] += acc[a][c];
     }
     // D[4 k4 + r][i16]: output channels co_w + 16 ct + 4 k4 + r, voxel i16 of plane dp0 + vt
 #pragma unroll
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restr
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int co = co_w + 16 * ct + 4 * k4;
-            if (co < Cout) *reinterpret_cast<f4*>(yp + co) = acc[ct][vt];
+            if (co < Cout) *reinterpret_cast<f4*>(yp + co) = tot[ct][vt];
         }
     }
 }
@@ -214,6 +229,48 @@ __global__ __launch_bounds__(F_T) void wgrad_f32_mfma_kernel(const float* __rest
         }
 }
 
+// dW[e] = sum over splits of part[s][e] in fp64: a block owns 64 elements
+// (4 per thread, 16-byte loads); its 16 split-lanes sum the splits s = lane,
+// lane + 16, ... in increasing order and the lane sums are added in lane
+// order, so the result is deterministic.  n is a multiple of 4.
+constexpr int R64_T = 16, R64_E = R64_T * 4, R64_L = 16;
+
+__global__ __launch_bounds__(R64_T * R64_L) void wgrad_reduce_f64_kernel(const float* __restrict__ part,
+                                                                        float* __restrict__ dW, int64_t n, int splits)
+{
+    __shared__ double red[R64_L][R64_T][4];
+    const int el = threadIdx.x % R64_T, sl = threadIdx.x / R64_T;
+    const int64_t i = (int64_t)blockIdx.x * R64_E + 4 * el;
+    const int64_t n4 = n / 4;
+    const f4* p4 = reinterpret_cast<const f4*>(part);
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if (i < n) {
+        int k = sl;
+        for (; k + 7 * R64_L < splits; k += 8 * R64_L) {
+            f4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p4[(int64_t)(k + u * R64_L) * n4 + i / 4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s0 += (double)v[u][0]; s1 += (double)v[u][1]; s2 += (double)v[u][2]; s3 += (double)v[u][3];
+            }
+        }
+        for (; k < splits; k += R64_L) {
+            const f4 v = p4[(int64_t)k * n4 + i / 4];
+            s0 += (double)v[0]; s1 += (double)v[1]; s2 += (double)v[2]; s3 += (double)v[3];
+        }
+    }
+    red[sl][el][0] = s0; red[sl][el][1] = s1; red[sl][el][2] = s2; red[sl][el][3] = s3;
+    __syncthreads();
+    if (sl == 0 && i < n) {
+        for (int e = 0; e < 4; ++e) {
+            double t = red[0][el][e];
+            for (int k = 1; k < R64_L; ++k) t += red[k][el][e];
+            dW[i + e] = (float)t;
+        }
+    }
+}
+
 // Wk[t][a][b] (a < apad, b < bpad) from DHWIO W[tap][ci][co] fp32:
 // forward (flip = 0): a = co, b = ci, tap = t;  backward-data (flip = 1):
 // a = ci, b = co, tap = 26 - t.
@@ -272,8 +329,13 @@ WgradPlan plan_wgrad_f32(const cf_dims& x, int cout)
     const int64_t nbox = x.n * ((x.d + 3) / 4) * ((x.h + 3) / 4) * ((x.w + 3) / 4);
     const int64_t outer = (int64_t)((x.c + 15) / 16) * ((cout + 63) / 64);
     const int64_t dw_bytes = (int64_t)27 * x.c * cout * 4;
-    int64_t want = (1024 + outer - 1) / outer;               // about four blocks per CU
-    int64_t cap = (int64_t)(64ll << 20) / dw_bytes;          // bound the partials to ~64 MiB
+    // at least about four blocks per CU, and at most BOX_PER_SPLIT boxes per
+    // split (the length of each fp32 chain), within ~256 MiB of partials
+    constexpr int64_t BOX_PER_SPLIT = 16;
+    int64_t want = (1024 + outer - 1) / outer;
+    const int64_t need = (nbox + BOX_PER_SPLIT - 1) / BOX_PER_SPLIT;
+    if (want < need) want = need;
+    int64_t cap = (int64_t)(256ll << 20) / dw_bytes;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;
     if (want > nbox) want = nbox;
@@ -296,7 +358,10 @@ hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float
                        (int)p.vox_per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_wgrad_reduce(part, dW, (int64_t)27 * x.c * cout, p.splits, s);
+    const int64_t n = (int64_t)27 * x.c * cout;
+    hipLaunchKernelGGL(wgrad_reduce_f64_kernel, dim3((unsigned)((n + R64_E - 1) / R64_E)), dim3(R64_T * R64_L), 0, s,
+                       (const float*)part, dW, n, p.splits);
+    return hipGetLastError();
 }
 
 }  // namespace cf
