@@ -130,8 +130,13 @@ def net_problem(layers, dense, size, B, dtype, batch_norm, dense_bias, seed):
 
 
 # Relative size of the conditioning perturbation of the oracle's conv sums
-# (about the fp32 accumulation error of the GPU's sums).
+# (about the fp32 accumulation error of the GPU's sums), the number of
+# perturbed oracle runs, and the margin over their largest deviation.  The
+# largest deviation of a gradient is set by its single largest flipped
+# decision, so it varies from run to run: three runs and a factor 3.
 PERTURB = 2.0 ** -22
+SPREAD_SEEDS = (1, 2, 3)
+SPREAD_FACTOR = 3.0
 
 
 def oracle_spread(x, t, params, layers, dense, batch_norm, dense_bias, storage, ref_grads):
@@ -142,7 +147,7 @@ def oracle_spread(x, t, params, layers, dense, batch_norm, dense_bias, storage, 
     at small batches the few terms of the deep layers' and the head's
     gradients make single decisions weigh heavily."""
     spread = [0.0] * len(ref_grads)
-    for seed in (1, 2):
+    for seed in SPREAD_SEEDS:
         print("oracle step with perturbed conv sums, seed %d ..." % seed, flush=True)
         alt = oracle.net_train_step(x, t, params, layers, dense, SLOPE, batch_norm=batch_norm, dense_bias=dense_bias,
                                     storage=storage, opt=("sgd", LR_RECOVER),
@@ -154,7 +159,7 @@ def oracle_spread(x, t, params, layers, dense, batch_norm, dense_bias, storage, 
 def check_net_step(layers, dense, size, B, dtype, batch_norm, dense_bias, seed, label):
     """SGD step with a power-of-two rate (gradients recovered from the
     update): loss and predictions gated at the path's tolerance, each
-    gradient at max(tolerance, 2 x the oracle's own spread)."""
+    gradient at max(tolerance, SPREAD_FACTOR x the oracle's own spread)."""
     x, t, m, params = net_problem(layers, dense, size, B, dtype, batch_norm, dense_bias, seed)
     pd = [to_dev(p, F32) for p in params]
     old = [host64(p) for p in pd]
@@ -174,7 +179,7 @@ def check_net_step(layers, dense, size, B, dtype, batch_norm, dense_bias, seed, 
     print("%s (%s) vs oracle: loss %.2e, pred %.2e; gradients %s" % (
         label, dtype, e_loss, e_pred, ", ".join("%.2e (spread %.2e)" % es for es in zip(errs, spread))), flush=True)
     assert e_loss <= tol and e_pred <= tol
-    bad = [(i, e, sp) for i, (e, sp) in enumerate(zip(errs, spread)) if not e <= max(tol, 2.0 * sp)]
+    bad = [(i, e, sp) for i, (e, sp) in enumerate(zip(errs, spread)) if not e <= max(tol, SPREAD_FACTOR * sp)]
     assert not bad, bad
 
 
