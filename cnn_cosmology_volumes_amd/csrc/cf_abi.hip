@@ -1142,6 +1142,12 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
     const float* W1 = params[L], *b1 = params[L + 1], *W2 = params[L + 2], *b2 = params[L + 3], *W3 = params[L + 4],
                 *b3 = params[L + 5];
     CF_TRY_HIP(launch_dense_fwd(B, P.flat, P.d0, hX, hXb, W1, b1, slope, F(P.pre1), F(P.y1), part, stream), "dense1");
+    // bf16: the dense input gradient goes through the last block's pool
+    // backward inside the dense backward-data kernel, which writes that
+    // block's full-resolution conv-output gradient (dP is never stored)
+    const bool head_unpool = bf && !last.fused;
+    const DenseUnpool dup{(const uint16_t*)(w + last.p), (const uint8_t*)(w + last.idx), (uint16_t*)(w + last.z),
+                          (int)(last.x.d / 2), (int)(last.x.h / 2), (int)(last.x.w / 2), last.cout, slope};
     if (dense_head_fits(B, P.d0, P.d1, P.d2)) {
         // layers 2-3, the loss and their backward in one launch; layer 1's
         // gated output gradient g1 then feeds its weight and data gradients
@@ -1156,8 +1162,9 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         h.g1 = F(P.g1); h.db1 = F(P.db1);
         CF_TRY_HIP(launch_dense_head(h, stream), "dense head");
         CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.g1), F(P.g1), -1.f,
-                                    bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
-                                    F(P.dW1), nullptr, stream), "dense1 backward");
+                                    bf ? nullptr : (float*)(w + last.dp),
+                                    bf && !head_unpool ? (uint16_t*)(w + last.dp) : nullptr, F(P.dW1), nullptr, stream,
+                                    head_unpool ? &dup : nullptr), "dense1 backward");
     } else {
         CF_TRY_HIP(launch_dense_fwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, b2, slope, F(P.pre2), F(P.y2), part, stream),
                    "dense2");
@@ -1170,8 +1177,9 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         CF_TRY_HIP(launch_dense_bwd(B, P.d0, P.d1, F(P.y1), nullptr, W2, F(P.pre2), F(P.dy2), slope, F(P.dy1), nullptr,
                                     F(P.dW2), F(P.db2), stream), "dense2 backward");
         CF_TRY_HIP(launch_dense_bwd(B, P.flat, P.d0, hX, hXb, W1, F(P.pre1), F(P.dy1), slope,
-                                    bf ? nullptr : (float*)(w + last.dp), bf ? (uint16_t*)(w + last.dp) : nullptr,
-                                    F(P.dW1), F(P.db1), stream), "dense1 backward");
+                                    bf ? nullptr : (float*)(w + last.dp),
+                                    bf && !head_unpool ? (uint16_t*)(w + last.dp) : nullptr, F(P.dW1), F(P.db1), stream,
+                                    head_unpool ? &dup : nullptr), "dense1 backward");
     }
 
     // 5. conv blocks backward: pool backward -> data gradient on the caller's
@@ -1196,7 +1204,10 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         float* part_w = F(P.part_w);
         bool forked = false;
         int deferred = -1;    // a block whose weight gradient waits for the next fork
-        bool unpooled = false;   // this block's dz was written by the previous block's backward-data
+        // this block's dz was already written by the kernel that produced its
+        // pooled gradient (the dense backward for the last block, the next
+        // block's backward-data otherwise)
+        bool unpooled = head_unpool;
         cf_status bst = CF_OK;
         for (int l = L - 1; l >= 0 && bst == CF_OK; --l) {
             const LayerPlan& Lp = P.layer[l];
@@ -1247,18 +1258,15 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
                 if (bst != CF_OK) break;
             }
             if (l > 0) {
-                // The deepest block's backward-data, when split, applies the
-                // previous block's pool backward in the reduction of its
-                // partials and writes that block's dz directly; its pooled
-                // gradient dp is read by nothing else (the previous block is
-                // not fused).  Doing the same for the next block down was
-                // slower: the caller's stream then reaches the big
-                // backward-data while the auxiliary stream's weight gradients
-                // still hold the GPU, and the two share it badly.
+                // A backward-data whose output is a non-fused block's pooled
+                // gradient applies that block's pool backward itself (in the
+                // reduction of split partials, or in the epilogue of the
+                // weight-ring kernel) and writes the block's dz directly; the
+                // pooled gradient dp is read by nothing else.
                 const LayerPlan& Lm = P.layer[l - 1];
                 const cf_dims y = with_c(Lp.x, Lp.cout);
-                const bool split = Lp.dg == Fwd::Mfma && plan_conv_mfma(y, (int)Lp.x.c).splits > 1;
-                if (split && bf && !Lm.fused && l == L - 1) {
+                const bool can = Lp.dg == Fwd::Mfma && conv_mfma_can_unpool(plan_conv_mfma(y, (int)Lp.x.c));
+                if (can && bf && !Lm.fused) {
                     bst = check_hip(launch_conv_mfma_unpool(plan_conv_mfma(y, (int)Lp.x.c), (const uint16_t*)dz,
                                                             (const uint16_t*)(w + Lp.wk_dg), part,
                                                             (const uint16_t*)(w + Lm.p), (const uint8_t*)(w + Lm.idx),

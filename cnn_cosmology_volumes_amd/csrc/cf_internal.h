@@ -136,11 +136,15 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
 // and for split plans (the partials' reduction pools; part as for
 // launch_conv_mfma); d, h, w even.
 bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x);
-// A split plan's conv (x: its input, cout: its output channels) whose output
-// is the pooled gradient dP of a 2^3 max-pool: the partials' reduction applies
-// the pool backward (P, idx: the pool's output and window indices, shape of
-// the conv output) and writes dZ (2x the conv output's D, H, W) in place of
-// dP; equal to launch_conv_mfma then the pool backward bit for bit.
+// A conv (x: its input, cout: its output channels) whose output is the
+// pooled gradient dP of a 2^3 max-pool: the pool backward (P, idx: the
+// pool's output and window indices, shape of the conv output) is applied in
+// the partials' reduction (split plans) or the conv epilogue (weight-ring
+// plans), writing dZ (2x the conv output's D, H, W) in place of dP; equal to
+// launch_conv_mfma then the pool backward bit for bit.
+// Which plans can unpool: split plans (in the partials' reduction) and the
+// weight-ring plans (in the conv kernel's epilogue).
+bool conv_mfma_can_unpool(const ConvPlan& p);
 hipError_t launch_conv_mfma_unpool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, float* part,
                                    const uint16_t* P, const uint8_t* idx, uint16_t* dZ, float slope, const cf_dims& x,
                                    int cout, int coutpad, hipStream_t s);
@@ -211,9 +215,19 @@ hipError_t launch_lrelu(const T* x, const T* dy, T* out, int64_t n, float slope,
 size_t dense_fwd_part_bytes(int B, int in, int out);
 hipError_t launch_dense_fwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
                             const float* b, float slope, float* pre, float* Y, float* part, hipStream_t s);
+// Pool backward applied to a dense layer's bf16 input gradient (the pooled
+// gradient of the last conv block, flattened NDHWC [B][Dp][Hp][Wp][C]): P and
+// idx of that pool, slope, and the full-resolution output dZ.
+struct DenseUnpool {
+    const uint16_t* P;
+    const uint8_t* idx;
+    uint16_t* dZ;
+    int Dp, Hp, Wp, C;
+    float slope;
+};
 hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
                             const float* pre, const float* dY, float slope, float* dX, uint16_t* dXb,
-                            float* dW, float* db, hipStream_t s);
+                            float* dW, float* db, hipStream_t s, const DenseUnpool* up = nullptr);
 // Layers 2 and 3 of the head, MSE, their backward and layer 1's gated
 // gradient and bias gradient in one launch (same arithmetic as the
 // standalone kernels).  Fits when the two small layers have In <= 128.

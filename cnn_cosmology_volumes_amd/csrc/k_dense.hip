@@ -221,9 +221,16 @@ __device__ __forceinline__ float dx_dot(float acc, const float* __restrict__ g, 
 // gradient in LDS (each loaded once per block), then every thread extends
 // its chain over the chunk.
 constexpr int DX_RI = 32, DX_OC = 128;
+// With up.dZ set, the bf16 input gradient is the pooled gradient dP of a
+// 2^3 max pool whose output is the (flattened NDHWC) input X: dP is rounded to
+// bf16 as dXb would hold it, then the pool backward is applied as the pool
+// backward kernel does it (times the slope where the pooled value is not
+// positive, at the recorded window position; zero at the other seven), and
+// the full-resolution gradient dZ is written instead of dP.
 __global__ __launch_bounds__(256)
 void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, const float* __restrict__ dY,
-                  float slope, float* __restrict__ dX, uint16_t* __restrict__ dXb, int B, int In, int Out)
+                  float slope, float* __restrict__ dX, uint16_t* __restrict__ dXb, int B, int In, int Out,
+                  DenseUnpool up)
 {
     static_assert(DX_RI * DB == 256, "one output per thread");
     __shared__ float ws[DX_RI][DX_OC + 1];      // +1: the threads of a wave read 8 rows at one column
@@ -267,8 +274,28 @@ void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, co
         }
         if (i < In && bl < nb) {
             const int64_t q = (int64_t)(b0 + bl) * In + i;
-            if (dXb) dXb[q] = f2bf(acc);
-            else dX[q] = acc;
+            if (up.dZ) {
+                float g = bf2f(f2bf(acc));
+                if (!(bf2f(up.P[q]) > 0.f)) g = up.slope * g;
+                const uint16_t gb = f2bf(g);
+                const int c = (int)(i % up.C);
+                int r = (int)(i / up.C);
+                const int pw = r % up.Wp; r /= up.Wp;
+                const int ph = r % up.Hp;
+                const int pd = r / up.Hp;
+                const int sel = up.idx[q];
+                const int D2 = 2 * up.Dp, H2 = 2 * up.Hp, W2 = 2 * up.Wp;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int64_t vox = (((int64_t)(b0 + bl) * D2 + 2 * pd + (k >> 2)) * H2 + 2 * ph + ((k >> 1) & 1)) *
+                                            W2 + 2 * pw + (k & 1);
+                    up.dZ[vox * up.C + c] = k == sel ? gb : (uint16_t)0;
+                }
+            } else if (dXb) {
+                dXb[q] = f2bf(acc);
+            } else {
+                dX[q] = acc;
+            }
         }
     }
 }
@@ -535,8 +562,9 @@ hipError_t launch_dense_fwd(int B, int in, int out, const float* X, const uint16
 
 hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16_t* Xb, const float* W,
                             const float* pre, const float* dY, float slope, float* dX, uint16_t* dXb, float* dW,
-                            float* db, hipStream_t s)
+                            float* db, hipStream_t s, const DenseUnpool* up)
 {
+    const DenseUnpool nu{};
     hipError_t e;
     if (db) {
         hipLaunchKernelGGL(dense_bwd_db, dim3((unsigned)((out + 255) / 256)), dim3(256), 0, s, pre, dY, slope, db, B,
@@ -549,9 +577,9 @@ hipError_t launch_dense_bwd(int B, int in, int out, const float* X, const uint16
                        dim3(256), 0, s, X, Xb, pre, dY, slope, dW, B, in, out);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dX || dXb) {
+    if (dX || dXb || (up && up->dZ)) {
         hipLaunchKernelGGL(dense_bwd_dx, dim3((unsigned)((in + DX_RI - 1) / DX_RI)), dim3(256), 0, s, W, pre, dY, slope, dX, dXb, B,
-                           in, out);
+                           in, out, up ? *up : nu);
         e = hipGetLastError();
     }
     return e;

@@ -105,9 +105,12 @@ def train128_problem():
     return c, x, conv, dense, t
 
 
-# Relative size of the conditioning perturbation of the oracle's conv sums:
-# about the fp32 accumulation error of the GPU's K = 27 * Cin term sums.
+# Relative size of the conditioning perturbation of the oracle's conv sums
+# (about the fp32 accumulation error of the GPU's K = 27 * Cin term sums) and
+# the margin over the perturbed runs' largest deviation, which is set by a
+# gradient's single largest flipped decision and so varies between runs.
 PERTURB = 2.0 ** -22
+SPREAD_FACTOR = 3.0
 
 
 @pytest.mark.timeout(1200)
@@ -120,7 +123,7 @@ def test_train128_step_matches_oracle_end_to_end():
     layers they flip near-tied pool decisions, each of which reroutes a
     window's gradient.  Two oracle runs whose conv sums are perturbed by
     PERTURB (seeded, before rounding) measure that spread; each gradient must
-    be within max(2e-2, 2 x spread) of the unperturbed oracle."""
+    be within max(2e-2, SPREAD_FACTOR x spread) of the unperturbed oracle."""
     from test_gpu_train import device_params
     c, x, conv, dense, t = train128_problem()
     m = cf.model_desc(4, c.in_size, c.filters, c.dense, SLOPE)
@@ -162,5 +165,5 @@ def test_train128_step_matches_oracle_end_to_end():
     print("train step 8x128^3x4 vs oracle (untied, bf16 storage): loss %.2e, pred %.2e; " % (e_loss, e_pred) +
           ", ".join("%s %.2e (oracle spread %.2e)" % (n, e, s) for n, e, s in zip(names, errs, spread)))
     assert e_loss <= TOL_BF16 and e_pred <= TOL_BF16
-    bad = {n: (e, s) for n, e, s in zip(names, errs, spread) if not e <= max(TOL_BF16, 2.0 * s)}
+    bad = {n: (e, s) for n, e, s in zip(names, errs, spread) if not e <= max(TOL_BF16, SPREAD_FACTOR * s)}
     assert not bad, bad

@@ -123,7 +123,12 @@ def composed_step(xd, conv_d, dense_d, td, lr):
 
 
 @pytest.mark.parametrize("two_streams", [False, True])
-@pytest.mark.parametrize("problem", [(2, 16, [32, 64], [32, 16, 3]), (1, 32, [32, 64, 128], [64, 32, 3])])
+# The third shape's block-3 backward-data (32^3 x 128 -> 64, batch 4) is an
+# unsplit weight-ring plan: it applies block 2's pool backward in its
+# epilogue; the second's (8^3) is split and does it in the reduction; the
+# dense backward does it for the last block in all three.
+@pytest.mark.parametrize("problem", [(2, 16, [32, 64], [32, 16, 3]), (1, 32, [32, 64, 128], [64, 32, 3]),
+                                     (4, 64, [32, 64, 128], [64, 32, 3])])
 def test_train_step_equals_composition_bitwise(problem, two_streams):
     B, size, filters, dense_w = problem
     x, conv, dense, t = make_problem(2, B, size, filters, dense_w, BF)
