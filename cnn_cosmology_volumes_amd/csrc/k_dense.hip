@@ -218,8 +218,10 @@ __device__ __forceinline__ float dx_dot(float acc, const float* __restrict__ g, 
 
 // A block owns DX_RI input rows x DB batch rows (one output per thread).
 // Per chunk of DX_OC output columns it stages those rows of W and the gated
-// gradient in LDS (each loaded once per block), then every thread extends
-// its chain over the chunk.
+// gradient in LDS (each loaded once per block); every thread sums the chunk
+// in a chain of its own and adds the chunk sums in chunk order (blocked
+// summation: the fp32 chains stay DX_OC long whatever Out is; with Out <=
+// DX_OC it is the single chain of the fused head kernel).
 constexpr int DX_RI = 32, DX_OC = 128;
 // With up.dZ set, the bf16 input gradient is the pooled gradient dP of a
 // 2^3 max pool whose output is the (flattened NDHWC) input X: dP is rounded to
@@ -270,7 +272,8 @@ void dense_bwd_dx(const float* __restrict__ W, const float* __restrict__ pre, co
                 gs[e / DX_OC][e % DX_OC] = gv[k];
             }
             __syncthreads();
-            acc = dx_dot(acc, gs[bl], ws[r], no);
+            if (oc == 0) acc = dx_dot(0.f, gs[bl], ws[r], no);
+            else acc += dx_dot(0.f, gs[bl], ws[r], no);
         }
         if (i < In && bl < nb) {
             const int64_t q = (int64_t)(b0 + bl) * In + i;

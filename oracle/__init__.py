@@ -328,6 +328,15 @@ def sgd(w, dw, lr):
 
 
 # ------------------------------------------------------------------ network
+def _perturbed(a, perturb):
+    """The conditioning probe: a * (1 + r u), u ~ U(-1, 1) from the probe's
+    generator (perturb = (Generator, r)); a unchanged when perturb is None."""
+    if perturb is None:
+        return a
+    g, r = perturb
+    return a * (1.0 + r * g.uniform(-1.0, 1.0, np.shape(a)))
+
+
 def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None, perturb=None):
     """Forward pass of the conv stack and the dense head.
 
@@ -336,18 +345,16 @@ def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None, pertur
     each block's stored conv output is appended to trace["z"].
 
     ``perturb`` = (numpy Generator, r) is a conditioning probe, not part of
-    the method: every conv sum is multiplied by (1 + r u), u ~ U(-1, 1), before
-    its storage rounding, as an fp32 accumulation error of relative size r
-    would move it.  Comparing a perturbed run with an unperturbed one shows
-    how far the step's results are determined by the arithmetic at all."""
+    the method: every matrix-product result (conv sums, dense pre-activations;
+    in network_backward the dense and conv input gradients) is multiplied by
+    (1 + r u), u ~ U(-1, 1), before its storage rounding, as an fp32
+    accumulation error of relative size r would move it.  Comparing a
+    perturbed run with an unperturbed one shows how far the step's results
+    are determined by the arithmetic at all."""
     a = store(x, storage)
     blocks = []
     for w in conv_w:
-        z = conv3d_fwd(a, w)
-        if perturb is not None:
-            g, r = perturb
-            z *= 1.0 + r * g.uniform(-1.0, 1.0, z.shape)
-        z = store(z, storage)
+        z = store(_perturbed(conv3d_fwd(a, w), perturb), storage)
         if trace is not None:
             trace.setdefault("z", []).append(z)
         p, idx = lrelu_maxpool_fwd(z, slope)
@@ -359,23 +366,27 @@ def network_forward(x, conv_w, dense_w, slope, storage="f64", trace=None, pertur
     dense = []
     for li, (W, b) in enumerate(dense_w):
         s = slope if li < len(dense_w) - 1 else -1.0
-        pre, y = dense_fwd(h, W, b, s)
+        pre, _ = dense_fwd(h, W, b, s)
+        pre = _perturbed(pre, perturb)
+        y = lrelu_fwd(pre, s) if s >= 0 else pre
         dense.append(dict(x=h, pre=pre, slope=s))
         h = y
     return h, dict(blocks=blocks, dense=dense, last_shape=a.shape)
 
 
-def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_dgrad=False, trace=None):
+def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_dgrad=False, trace=None,
+                     perturb=None):
     """Backward pass; returns (conv_dw list, dense grads list of (dW, db)).
     If ``trace`` is a dict, the stored pooled gradient and conv-output
-    gradient of each block are recorded in trace["dp"][l] and trace["dz"][l]."""
+    gradient of each block are recorded in trace["dp"][l] and trace["dz"][l].
+    ``perturb``: the conditioning probe of network_forward."""
     g = dyhat
     dense_g = [None] * len(dense_w)
     for li in reversed(range(len(dense_w))):
         c = cache["dense"][li]
         dx, dw, db = dense_bwd(c["x"], dense_w[li][0], c["pre"], g, c["slope"], need_dx=True)
         dense_g[li] = (dw, db)
-        g = dx
+        g = _perturbed(dx, perturb)
     dp = store(g.reshape(cache["last_shape"]), storage)
     conv_g = [None] * len(conv_w)
     if trace is not None:
@@ -389,7 +400,7 @@ def network_backward(cache, conv_w, dense_w, dyhat, slope, storage="f64", first_
             trace["dz"][l] = dz
         conv_g[l] = conv3d_bwd_weight(blk["x"], dz)
         if l > 0 or first_dgrad:
-            dp = store(conv3d_bwd_data(dz, conv_w[l]), storage)
+            dp = store(_perturbed(conv3d_bwd_data(dz, conv_w[l]), perturb), storage)
     return conv_g, dense_g
 
 
@@ -407,7 +418,7 @@ def train_step(x, targets, conv_w32, dense_w32, lr, slope, storage="f64", trace=
     dense_use = [(_f64(W), _f64(b)) for W, b in dense_w32]
     yhat, cache = network_forward(x, conv_use, dense_use, slope, storage, trace=trace, perturb=perturb)
     loss, dy = mse(yhat, targets)
-    conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage, trace=trace)
+    conv_g, dense_g = network_backward(cache, conv_use, dense_use, dy, slope, storage, trace=trace, perturb=perturb)
     master = "f64" if storage == "f64" else "f32"
     new_conv = [store(sgd(w, g, lr), master) for w, g in zip(conv_w32, conv_g)]
     new_dense = [(store(sgd(W, dW, lr), master), store(sgd(b, db, lr), master))
@@ -525,8 +536,8 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     batch-norm output, layer output and their gradients; conv weights are
     the masters rounded to ``storage``.  opt: ("sgd", lr) or ("adam", lr_t,
     beta1, beta2, eps, trust, t) with adam_state = (m list, v list).
-    perturb: the conditioning probe of network_forward (conv sums scaled by
-    1 + r u before their storage rounding).
+    perturb: the conditioning probe of network_forward (every matrix-product
+    result scaled by 1 + r u before its storage rounding).
     Returns dict(loss, yhat, grads, params, adam_state)."""
     L = len(layers)
     per = 3 if batch_norm else 1
@@ -545,11 +556,7 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     a = store(x, storage)
     cache = []
     for l, (f, s, pool) in enumerate(layers):
-        z = conv(a, wuse[l], s)
-        if perturb is not None:
-            g_, r_ = perturb
-            z *= 1.0 + r_ * g_.uniform(-1.0, 1.0, z.shape)
-        z = store(z, storage)
+        z = store(_perturbed(conv(a, wuse[l], s), perturb), storage)
         y, mean, invstd = z, None, None
         if batch_norm:
             y, mean, invstd = batchnorm_fwd(z, gam[l], bet[l], bn_eps)
@@ -569,7 +576,9 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     dcache = []
     for k in range(len(dense)):
         sk = slope if k + 1 < len(dense) else -1.0
-        pre, yk = dense_fwd(h, dW[k], db[k], sk)
+        pre, _ = dense_fwd(h, dW[k], db[k], sk)
+        pre = _perturbed(pre, perturb)
+        yk = lrelu_fwd(pre, sk) if sk >= 0 else pre
         dcache.append((h, pre, sk))
         h = yk
     loss, g = mse(h, targets)
@@ -577,6 +586,7 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
     for k in reversed(range(len(dense))):
         hin, pre, sk = dcache[k]
         g, gw, gb = dense_bwd(hin, dW[k], pre, g, sk, need_dx=True)
+        g = _perturbed(g, perturb)
         grads[dw0 + k * dp_] = gw
         if dense_bias:
             grads[dw0 + k * dp_ + 1] = gb
@@ -601,7 +611,7 @@ def net_train_step(x, targets, params, layers, dense, slope, batch_norm=False, b
         if l > 0:
             size = c["x"].shape[1]
             dA = conv3d_bwd_data(dz, wuse[l]) if s == 1 else conv3d_bwd_data_s(dz, wuse[l], s, size)
-            dA = store(dA, storage)
+            dA = store(_perturbed(dA, perturb), storage)
     master = "f64" if storage == "f64" else "f32"
     if opt[0] == "sgd":
         new = [store(sgd(p, gr, opt[1]), master) for p, gr in zip(params, grads)]
