@@ -300,11 +300,13 @@ def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     check_pool_indices(zo, idx.cpu().numpy(), io, g, po)
 
 
-@pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 6, 8, 8, 64, 64)])
+@pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 6, 8, 8, 64, 64),
+                                   (2, 8, 16, 32, 4, 32), (1, 6, 10, 18, 4, 32)])
 def test_conv3d_pool_fwd_ties_follow_window_order(shape):
     """Integer inputs and weights in {-1, 0, 1} give conv outputs that tie
-    often inside a window; the fused epilogue (whose window is split over two
-    lanes), and the pooling reduction of a split plan (the last shape), must
+    often inside a window; the fused epilogues (the general one, whose window
+    is split over two lanes, and the 4-channel first layer's), and the pooling
+    reduction of a split plan (the third shape), must
     still pick the first strict maximum in window order, as the separate pool
     kernel does."""
     N, D, H, W, Ci, Co = shape
