@@ -119,7 +119,8 @@ Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
         if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
         if (cin == 4 && c4_offsets_fit(x)) return Fwd::C4;
     }
-    if (dt == CF_F32 && conv_f32_mfma_ok(x, cout)) return Fwd::F32Mfma;
+    // fp32 layers, and bf16 layers of other channel counts (multiples of 4)
+    if (conv_f32_mfma_ok(x, cout)) return Fwd::F32Mfma;
     return Fwd::Direct;
 }
 
@@ -128,7 +129,7 @@ Fwd dgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 32 == 0 && cin % 4 == 0 && mfma_offsets_fit(x, cout, cin)) return Fwd::Mfma;
-    if (dt == CF_F32 && conv_f32_mfma_ok(with_c(x, cout), (int)cin)) return Fwd::F32Mfma;
+    if (conv_f32_mfma_ok(with_c(x, cout), (int)cin)) return Fwd::F32Mfma;
     return Fwd::Direct;
 }
 
@@ -138,7 +139,7 @@ Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
         if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
         if (x.c == 4 && cout == 32 && wgrad_c4_fits(x)) return Wg::C4;
     }
-    if (dt == CF_F32 && x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
+    if (x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
     return Wg::Direct;
 }
 
@@ -201,7 +202,8 @@ hipError_t run_fwd(Fwd p, cf_dtype dt, const cf_dims& x, const void* X, const vo
     case Fwd::C4:
         return launch_conv_c4_fwd((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, roundup(cout, 128), s);
     case Fwd::F32Mfma:
-        return launch_conv_f32_mfma((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
+        if (dt == CF_F32) return launch_conv_f32_mfma((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
+        return launch_conv_f32_mfma((const uint16_t*)X, (const float*)wk, (uint16_t*)Y, x, cout, s);
     default:
         if (dt == CF_F32) return launch_conv_direct<float>((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
         return launch_conv_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, s);
@@ -223,7 +225,10 @@ hipError_t run_dgrad(Fwd p, cf_dtype dt, const cf_dims& x, const void* dY, const
         return launch_conv_mfma(plan, (const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, part, y, (int)x.c,
                                 roundup((int)x.c, 128), s);
     }
-    if (p == Fwd::F32Mfma) return launch_conv_f32_mfma((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
+    if (p == Fwd::F32Mfma && dt == CF_F32)
+        return launch_conv_f32_mfma((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
+    if (p == Fwd::F32Mfma)
+        return launch_conv_f32_mfma((const uint16_t*)dY, (const float*)wk, (uint16_t*)dX, y, (int)x.c, s);
     if (dt == CF_F32) return launch_conv_direct<float>((const float*)dY, (const float*)wk, (float*)dX, y, (int)x.c, s);
     return launch_conv_direct<uint16_t>((const uint16_t*)dY, (const uint16_t*)wk, (uint16_t*)dX, y, (int)x.c, s);
 }
@@ -243,8 +248,11 @@ size_t wgrad_part_bytes(Wg p, cf_dtype dt, const cf_dims& x, int cout)
 hipError_t run_wgrad(Wg p, cf_dtype dt, const cf_dims& x, const void* X, const void* dY, int cout, float* dW,
                      float* part, hipStream_t s)
 {
-    if (p == Wg::F32Mfma)
+    if (p == Wg::F32Mfma && dt == CF_F32)
         return launch_wgrad_f32_mfma(plan_wgrad_f32(x, cout), (const float*)X, (const float*)dY, part, dW, x, cout, s);
+    if (p == Wg::F32Mfma)
+        return launch_wgrad_f32_mfma(plan_wgrad_f32(x, cout), (const uint16_t*)X, (const uint16_t*)dY, part, dW, x,
+                                     cout, s);
     if (p != Wg::Direct) {
         const WgradPlan plan = plan_wgrad(x, cout);
         return launch_wgrad(plan, (const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
@@ -253,13 +261,20 @@ hipError_t run_wgrad(Wg p, cf_dtype dt, const cf_dims& x, const void* X, const v
     return launch_wgrad_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
 }
 
+// The weight source of the fp32 matrix-core kernels: fp32 layers take fp32
+// weights as they are; bf16 layers take bf16 weights, or round fp32 masters.
+F32WSrc f32_wsrc(cf_dtype dt, bool src_f32)
+{
+    return dt == CF_F32 ? F32WSrc::F32 : src_f32 ? F32WSrc::F32RoundBf16 : F32WSrc::Bf16;
+}
+
 // Prepare forward weights from a DHWIO source (fp32 master or bf16).
-hipError_t prep_fwd(Fwd p, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
+hipError_t prep_fwd(Fwd p, cf_dtype dt, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
 {
     switch (p) {
     case Fwd::Mfma: return launch_wprep_fwd(W, src_f32, (int)cin, cout, roundup(cout, 128), (uint16_t*)wk, s);
     case Fwd::C4: return launch_wprep_c4(W, src_f32, cout, roundup(cout, 128), (uint16_t*)wk, s);
-    case Fwd::F32Mfma: return launch_wprep_f32((const float*)W, (int)cin, cout, false, (float*)wk, s);
+    case Fwd::F32Mfma: return launch_wprep_f32(W, f32_wsrc(dt, src_f32), (int)cin, cout, false, (float*)wk, s);
     default: return hipSuccess;
     }
 }
@@ -267,7 +282,7 @@ hipError_t prep_fwd(Fwd p, const void* W, bool src_f32, int64_t cin, int cout, v
 hipError_t prep_dgrad(Fwd p, cf_dtype dt, const void* W, bool src_f32, int64_t cin, int cout, void* wk, hipStream_t s)
 {
     if (p == Fwd::Mfma) return launch_wprep_dgrad(W, src_f32, (int)cin, cout, roundup((int)cin, 128), (uint16_t*)wk, s);
-    if (p == Fwd::F32Mfma) return launch_wprep_f32((const float*)W, (int)cin, cout, true, (float*)wk, s);
+    if (p == Fwd::F32Mfma) return launch_wprep_f32(W, f32_wsrc(dt, src_f32), (int)cin, cout, true, (float*)wk, s);
     return launch_wprep_direct_dgrad(W, dt, (int)cin, cout, wk, s);
 }
 
@@ -351,7 +366,7 @@ cf_status cf_conv3d_pool_fwd(cf_dtype dtype, cf_dims x, const void* X, const voi
     char* w8 = (char*)ws;
     const void* wk = W;
     if (p != Fwd::Direct) {
-        CF_TRY_HIP(prep_fwd(p, W, false, x.c, cout, w8, stream), "weight re-layout");
+        CF_TRY_HIP(prep_fwd(p, dtype, W, false, x.c, cout, w8, stream), "weight re-layout");
         wk = w8;
     }
     if (fused) {
@@ -427,7 +442,7 @@ static cf_status conv_fwd_s1(cf_dtype dtype, cf_dims x, const void* X, const voi
     char* w8 = (char*)ws;
     const void* wk = W;
     if (p != Fwd::Direct) {
-        CF_TRY_HIP(prep_fwd(p, W, false, x.c, cout, w8, stream), "weight re-layout");
+        CF_TRY_HIP(prep_fwd(p, dtype, W, false, x.c, cout, w8, stream), "weight re-layout");
         wk = w8;
     }
     CF_TRY_HIP(run_fwd(p, dtype, x, X, wk, cout, Y, (float*)(w8 ? w8 + wkb : nullptr), stream), "conv3d forward");
@@ -1070,14 +1085,16 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
             wl.job[wl.count++] = WprepJob{2, true, (int)Lp.x.c, Lp.cout, roundup(Lp.cout, 128), params[l],
                                           (uint16_t*)(w + Lp.wk_fwd)};
         else if (Lp.fwd == Fwd::F32Mfma)
-            CF_TRY_HIP(launch_wprep_f32(params[l], (int)Lp.x.c, Lp.cout, false, (float*)(w + Lp.wk_fwd), stream),
+            CF_TRY_HIP(launch_wprep_f32(params[l], f32_wsrc(dtype, true), (int)Lp.x.c, Lp.cout, false,
+                                        (float*)(w + Lp.wk_fwd), stream),
                        "weight re-layout");
         if (l > 0) {
             if (Lp.dg == Fwd::Mfma) {
                 wl.job[wl.count++] = WprepJob{1, true, (int)Lp.x.c, Lp.cout, roundup((int)Lp.x.c, 128), params[l],
                                               (uint16_t*)(w + Lp.wk_dg)};
             } else if (Lp.dg == Fwd::F32Mfma) {
-                CF_TRY_HIP(launch_wprep_f32(params[l], (int)Lp.x.c, Lp.cout, true, (float*)(w + Lp.wk_dg), stream),
+                CF_TRY_HIP(launch_wprep_f32(params[l], f32_wsrc(dtype, true), (int)Lp.x.c, Lp.cout, true,
+                                            (float*)(w + Lp.wk_dg), stream),
                            "weight re-layout");
             } else if (bf) {
                 const int64_t n = (int64_t)27 * Lp.x.c * Lp.cout;

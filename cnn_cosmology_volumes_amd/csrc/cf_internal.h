@@ -142,8 +142,7 @@ bool conv_mfma_can_pool(const ConvPlan& p, const cf_dims& x);
 // the partials' reduction (split plans) or the conv epilogue (weight-ring
 // plans), writing dZ (2x the conv output's D, H, W) in place of dP; equal to
 // launch_conv_mfma then the pool backward bit for bit.
-// Which plans can unpool: split plans (in the partials' reduction) and the
-// weight-ring plans (in the conv kernel's epilogue).
+// Which plans can unpool: split plans (in the partials' reduction).
 bool conv_mfma_can_unpool(const ConvPlan& p);
 hipError_t launch_conv_mfma_unpool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, float* part,
                                    const uint16_t* P, const uint8_t* idx, uint16_t* dZ, float slope, const cf_dims& x,
@@ -180,15 +179,23 @@ hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uin
                                 const uint8_t* idx, float slope, float* part, float* dW, const cf_dims& x,
                                 hipStream_t s);
 
-// fp32 convolution on the matrix cores (k_conv_f32.hip); channel counts
+// Convolution on the fp32 matrix cores (k_conv_f32.hip); channel counts
 // multiples of 4.  Weights re-laid as [27][rup(out,64)][rup(in,16)] fp32
-// (backward-data: flipped taps, in = forward cout, out = forward cin).
+// (backward-data: flipped taps, in = forward cout, out = forward cin).  The
+// activations are fp32, or bf16 (widened on load, rounded on store) for bf16
+// layers outside the bf16 kernels' channel counts; the weight source is fp32
+// as is, fp32 rounded to bf16, or bf16.
+enum class F32WSrc : int { F32 = 0, F32RoundBf16 = 1, Bf16 = 2 };
 bool conv_f32_mfma_ok(const cf_dims& x, int cout);
 size_t conv_f32_wk_bytes(int in, int out);
-hipError_t launch_wprep_f32(const float* W, int cin, int cout, bool dgrad, float* Wk, hipStream_t s);
+hipError_t launch_wprep_f32(const void* W, F32WSrc src, int cin, int cout, bool dgrad, float* Wk, hipStream_t s);
 hipError_t launch_conv_f32_mfma(const float* X, const float* Wk, float* Y, const cf_dims& x, int cout, hipStream_t s);
+hipError_t launch_conv_f32_mfma(const uint16_t* X, const float* Wk, uint16_t* Y, const cf_dims& x, int cout,
+                                hipStream_t s);
 WgradPlan plan_wgrad_f32(const cf_dims& x, int cout);
 hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float* dY, float* part, float* dW,
+                                 const cf_dims& x, int cout, hipStream_t s);
+hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, float* part, float* dW,
                                  const cf_dims& x, int cout, hipStream_t s);
 
 // Direct (non-MFMA) conv kernels for fp32 and for shapes outside the MFMA

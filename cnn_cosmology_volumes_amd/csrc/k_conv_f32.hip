@@ -31,6 +31,14 @@
 // chunk (432 products) in fresh registers and adds the chunk sums into the
 // total; the backward-weight gives each split at most BOX_PER_SPLIT boxes
 // (1024 products per accumulator) and adds the splits in fp64.
+//
+// bf16 storage.  The same kernels serve bf16 layers whose channel counts the
+// bf16 kernels do not cover (multiples of 4 but not of 32, other than the
+// 4-channel first layer): activations and gradients are read as bf16 and
+// widened exactly, the weights are the bf16-rounded values held in fp32, and
+// outputs are rounded to bf16 at the store.  A product of two bf16 values is
+// exact in fp32, so this is the bf16 path's arithmetic (bf16 operands, fp32
+// accumulation) on the fp32 matrix cores.
 #include "cf_internal.h"
 
 namespace cf {
@@ -55,11 +63,24 @@ __device__ __forceinline__ f4 mfma4(const f4& a, const f4& b, f4 acc)
 }
 
 __device__ __forceinline__ f4 ld4g(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 ld4g(const uint16_t* p)
+{
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+              __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ void st4g(float* p, const f4& v) { *reinterpret_cast<f4*>(p) = v; }
+__device__ __forceinline__ void st4g(uint16_t* p, const f4& v)
+{
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
 
 // Y[n, d, h, w, co] = sum_tap sum_ci X[n, d+kd-1, h+kh-1, w+kw-1, ci] Wk[tap][co][ci]
 // Wk: [27][copad][cipad] fp32, zero beyond cout / cin; copad % 64 == 0, cipad % 16 == 0.
-__global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restrict__ X, const float* __restrict__ Wk,
-                                                            float* __restrict__ Y, int N, int D, int H, int W,
+// T: storage type of X and Y (float, or uint16_t for bf16).
+template <typename T>
+__global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const T* __restrict__ X, const float* __restrict__ Wk,
+                                                            T* __restrict__ Y, int N, int D, int H, int W,
                                                             int Cin, int Cout, int cipad, int copad, int bD, int bH,
                                                             int bW)
 {
@@ -132,11 +153,11 @@ __global__ __launch_bounds__(F_T) void conv_f32_mfma_kernel(const float* __restr
     for (int vt = 0; vt < 2; ++vt) {
         const int d = d0 + dp0 + vt, h = h0 + vh, w = w0 + vw;
         if (d >= D || h >= H || w >= W) continue;
-        float* yp = Y + ((((int64_t)n * D + d) * H + h) * W + w) * Cout;
+        T* yp = Y + ((((int64_t)n * D + d) * H + h) * W + w) * Cout;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int co = co_w + 16 * ct + 4 * k4;
-            if (co < Cout) *reinterpret_cast<f4*>(yp + co) = tot[ct][vt];
+            if (co < Cout) st4g(yp + co, tot[ct][vt]);
         }
     }
 }
@@ -146,7 +167,9 @@ constexpr int G_XT = 3 * F_CC * F_H * F_H * 4;   // floats of the three shifted 
 constexpr int G_DT = G_BN * 64;                  // floats of the transposed output gradient
 
 // part[split][tap][ci][co] over the boxes [split * per, min(nbox, (split+1) * per)).
-__global__ __launch_bounds__(F_T) void wgrad_f32_mfma_kernel(const float* __restrict__ X, const float* __restrict__ dY,
+// T: storage type of X and dY (float, or uint16_t for bf16).
+template <typename T>
+__global__ __launch_bounds__(F_T) void wgrad_f32_mfma_kernel(const T* __restrict__ X, const T* __restrict__ dY,
                                                              float* __restrict__ part, int N, int D, int H, int W,
                                                              int Cin, int Cout, int bD, int bH, int bW, int nci,
                                                              int nco, int64_t nbox, int per)
@@ -271,11 +294,12 @@ __global__ __launch_bounds__(R64_T * R64_L) void wgrad_reduce_f64_kernel(const f
     }
 }
 
-// Wk[t][a][b] (a < apad, b < bpad) from DHWIO W[tap][ci][co] fp32:
+// Wk[t][a][b] (a < apad, b < bpad) from DHWIO W[tap][ci][co]:
 // forward (flip = 0): a = co, b = ci, tap = t;  backward-data (flip = 1):
-// a = ci, b = co, tap = 26 - t.
-__global__ void wprep_f32_kernel(const float* __restrict__ W, float* __restrict__ Wk, int cin, int cout, int apad,
-                                 int bpad, int flip)
+// a = ci, b = co, tap = 26 - t.  The source is fp32 taken as is, fp32
+// rounded to bf16 (the bf16 path's weights from fp32 masters), or bf16.
+__global__ void wprep_f32_kernel(const void* __restrict__ W, F32WSrc src, float* __restrict__ Wk, int cin, int cout,
+                                 int apad, int bpad, int flip)
 {
     const int64_t total = (int64_t)27 * apad * bpad;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -285,7 +309,16 @@ __global__ void wprep_f32_kernel(const float* __restrict__ W, float* __restrict_
     const int t = (int)(i / ((int64_t)bpad * apad));
     const int ci = flip ? ai : bi, co = flip ? bi : ai;
     const int tap = flip ? 26 - t : t;
-    Wk[i] = (ci < cin && co < cout) ? W[((int64_t)tap * cin + ci) * cout + co] : 0.f;
+    float v = 0.f;
+    if (ci < cin && co < cout) {
+        const int64_t e = ((int64_t)tap * cin + ci) * cout + co;
+        if (src == F32WSrc::Bf16)
+            v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(W)[e] << 16);
+        else
+            v = static_cast<const float*>(W)[e];
+        if (src == F32WSrc::F32RoundBf16) v = __uint_as_float(pack_bf16x2(v, 0.f) << 16);
+    }
+    Wk[i] = v;
 }
 
 int rup(int v, int m) { return (v + m - 1) / m * m; }
@@ -301,25 +334,37 @@ bool conv_f32_mfma_ok(const cf_dims& x, int cout)
 
 size_t conv_f32_wk_bytes(int cin, int cout) { return (size_t)27 * rup(cout, 64) * rup(cin, 16) * 4; }
 
-hipError_t launch_wprep_f32(const float* W, int cin, int cout, bool dgrad, float* Wk, hipStream_t s)
+hipError_t launch_wprep_f32(const void* W, F32WSrc src, int cin, int cout, bool dgrad, float* Wk, hipStream_t s)
 {
     // forward: [27][rup(cout, 64)][rup(cin, 16)]; backward-data: in = cout, out = cin
     const int apad = dgrad ? rup(cin, 64) : rup(cout, 64);
     const int bpad = dgrad ? rup(cout, 16) : rup(cin, 16);
     const int64_t total = (int64_t)27 * apad * bpad;
-    hipLaunchKernelGGL(wprep_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, Wk, cin, cout,
+    hipLaunchKernelGGL(wprep_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, src, Wk, cin, cout,
                        apad, bpad, dgrad ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t conv_f32_mfma_launch(const T* X, const float* Wk, T* Y, const cf_dims& x, int cout, hipStream_t s)
+{
+    const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + 3) / 4), bW = (int)((x.w + 3) / 4);
+    const int copad = rup(cout, 64), cipad = rup((int)x.c, 16);
+    const int64_t nb = x.n * bD * bH * bW * (copad / 64);
+    hipLaunchKernelGGL(conv_f32_mfma_kernel<T>, dim3((unsigned)nb), dim3(F_T), 0, s, X, Wk, Y, (int)x.n, (int)x.d,
+                       (int)x.h, (int)x.w, (int)x.c, cout, cipad, copad, bD, bH, bW);
     return hipGetLastError();
 }
 
 hipError_t launch_conv_f32_mfma(const float* X, const float* Wk, float* Y, const cf_dims& x, int cout, hipStream_t s)
 {
-    const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + 3) / 4), bW = (int)((x.w + 3) / 4);
-    const int copad = rup(cout, 64), cipad = rup((int)x.c, 16);
-    const int64_t nb = x.n * bD * bH * bW * (copad / 64);
-    hipLaunchKernelGGL(conv_f32_mfma_kernel, dim3((unsigned)nb), dim3(F_T), 0, s, X, Wk, Y, (int)x.n, (int)x.d,
-                       (int)x.h, (int)x.w, (int)x.c, cout, cipad, copad, bD, bH, bW);
-    return hipGetLastError();
+    return conv_f32_mfma_launch(X, Wk, Y, x, cout, s);
+}
+
+hipError_t launch_conv_f32_mfma(const uint16_t* X, const float* Wk, uint16_t* Y, const cf_dims& x, int cout,
+                                hipStream_t s)
+{
+    return conv_f32_mfma_launch(X, Wk, Y, x, cout, s);
 }
 
 WgradPlan plan_wgrad_f32(const cf_dims& x, int cout)
@@ -347,14 +392,15 @@ WgradPlan plan_wgrad_f32(const cf_dims& x, int cout)
     return p;
 }
 
-hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float* dY, float* part, float* dW,
-                                 const cf_dims& x, int cout, hipStream_t s)
+template <typename T>
+hipError_t wgrad_f32_mfma_launch(const WgradPlan& p, const T* X, const T* dY, float* part, float* dW, const cf_dims& x,
+                                 int cout, hipStream_t s)
 {
     const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + 3) / 4), bW = (int)((x.w + 3) / 4);
     const int nci = (int)((x.c + 15) / 16), nco = (cout + 63) / 64;
     const int64_t nbox = x.n * bD * bH * bW;
-    hipLaunchKernelGGL(wgrad_f32_mfma_kernel, dim3((unsigned)((int64_t)nci * nco * p.splits)), dim3(F_T), 0, s, X, dY,
-                       part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nci, nco, nbox,
+    hipLaunchKernelGGL(wgrad_f32_mfma_kernel<T>, dim3((unsigned)((int64_t)nci * nco * p.splits)), dim3(F_T), 0, s, X,
+                       dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nci, nco, nbox,
                        (int)p.vox_per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -362,6 +408,18 @@ hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float
     hipLaunchKernelGGL(wgrad_reduce_f64_kernel, dim3((unsigned)((n + R64_E - 1) / R64_E)), dim3(R64_T * R64_L), 0, s,
                        (const float*)part, dW, n, p.splits);
     return hipGetLastError();
+}
+
+hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const float* X, const float* dY, float* part, float* dW,
+                                 const cf_dims& x, int cout, hipStream_t s)
+{
+    return wgrad_f32_mfma_launch(p, X, dY, part, dW, x, cout, s);
+}
+
+hipError_t launch_wgrad_f32_mfma(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, float* part, float* dW,
+                                 const cf_dims& x, int cout, hipStream_t s)
+{
+    return wgrad_f32_mfma_launch(p, X, dY, part, dW, x, cout, s);
 }
 
 }  // namespace cf

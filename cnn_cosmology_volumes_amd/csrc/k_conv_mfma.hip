@@ -329,20 +329,12 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 // CU); the 64-channel blocks measured faster with AS = 48.
 // POOL as in conv3d_mfma_kernel: a 2^3 window is the fragments (2 pd + a) *
 // JH + b of one lane (a = d, b = h offset) and of its w-neighbour lane.
-// UNPOOL (backward-data whose output is the pooled gradient dP of a 2^3 max
-// pool): the epilogue rounds dP to bf16 as the plain store would, applies
-// the pool backward as the pool backward kernel does (the gradient, times
-// the slope where the pooled value Pin is not positive, goes to the window
-// position pidx records; the other seven positions get zero) and writes dZ
-// (Y, 2D x 2H x 2W) in place of dP: equal to the plain launch followed by the
-// pool backward bit for bit.
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false, bool UNPOOL = false>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
 __global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS>::MINB))
 void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                             uint16_t* __restrict__ Y, float* __restrict__ part,
                             int N, int D, int H, int W, int Cin, int Cout, int CoutPad,
-                            int tD, int tH, int tW, int chunks_per_split, uint8_t* __restrict__ pidx, float slope,
-                            const uint16_t* __restrict__ Pin)
+                            int tD, int tH, int tW, int chunks_per_split, uint8_t* __restrict__ pidx, float slope)
 {
     using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
     constexpr int RPF = 16 / TW;            // h rows per fragment
@@ -568,28 +560,7 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             const int co = co_base + 16 * i + 4 * lg;
             if (co >= Cout) continue;
             const f32x4 r = acc[i][j];
-            if constexpr (UNPOOL) {
-                const uint32_t lo = pack_bf16x2(r[0], r[1]), hi = pack_bf16x2(r[2], r[3]);
-                float g[4] = {__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
-                              __uint_as_float(hi & 0xffff0000u)};
-                const uint2 pp = *reinterpret_cast<const uint2*>(Pin + gv * Cout + co);
-                const float pv[4] = {__uint_as_float(pp.x << 16), __uint_as_float(pp.x & 0xffff0000u),
-                                     __uint_as_float(pp.y << 16), __uint_as_float(pp.y & 0xffff0000u)};
-                const uint32_t ib = *reinterpret_cast<const uint32_t*>(pidx + gv * Cout + co);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) g[c] = pv[c] > 0.f ? g[c] : slope * g[c];
-                const int D2 = 2 * D, H2 = 2 * H, W2 = 2 * W;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int a = q >> 2, b = (q >> 1) & 1, e = q & 1;
-                    float o[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) o[c] = ((ib >> (8 * c)) & 0xffu) == (uint32_t)q ? g[c] : 0.f;
-                    const int64_t vox = (((int64_t)n * D2 + 2 * gd + a) * H2 + 2 * gh + b) * W2 + 2 * gw + e;
-                    *reinterpret_cast<uint2*>(Y + vox * Cout + co) =
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-                }
-            } else if (part) {
+            if (part) {
                 float* dst = part + ((int64_t)blockIdx.z * nvox + gv) * Cout + co;
                 *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
             } else {
@@ -746,10 +717,9 @@ void split_reduce_unpool_bf16(const float* __restrict__ part, const uint16_t* __
     }
 }
 
-template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false, bool UNPOOL = false>
+template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int AS, bool POOL = false>
 hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float* part, const cf_dims& x, int cout,
-                      int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f,
-                      const uint16_t* Pin = nullptr)
+                      int coutpad, int splits, hipStream_t s, uint8_t* pidx = nullptr, float slope = 0.f)
 {
     using T = Tile<BM, WM, WN, TD, TH, TW, LS>;
     // the kernel's 32-bit buffer offsets: a tile's TD + 2 input planes and
@@ -761,9 +731,9 @@ hipError_t launch_kdr(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, float*
     const int nchunks = (int)(x.c / 32);
     const int cps = (nchunks + splits - 1) / splits;
     dim3 grid((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + BM - 1) / BM), (unsigned)splits);
-    hipLaunchKernelGGL((conv3d_mfma_kdr_kernel<BM, WM, WN, TD, TH, TW, LS, AS, POOL, UNPOOL>), grid, dim3(T::NT), 0, s,
+    hipLaunchKernelGGL((conv3d_mfma_kdr_kernel<BM, WM, WN, TD, TH, TW, LS, AS, POOL>), grid, dim3(T::NT), 0, s,
                        X, Wk, Y, splits > 1 ? part : nullptr, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout,
-                       coutpad, tD, tH, tW, cps, pidx, slope, Pin);
+                       coutpad, tD, tH, tW, cps, pidx, slope);
     return hipGetLastError();
 }
 
@@ -876,25 +846,18 @@ hipError_t launch_conv_mfma(const ConvPlan& p, const uint16_t* X, const uint16_t
     return hipGetLastError();
 }
 
-bool conv_mfma_can_unpool(const ConvPlan& p) { return p.splits > 1 || p.ring; }
+// Only split plans apply the pool backward of the layer below (in the
+// reduction of their partials).  An epilogue doing the same in the unsplit
+// weight-ring kernel writes eight 8-byte stores per accumulator and waits on
+// the pooled values and indices at the end of the kernel; in the 128^3 step
+// it measured slower than that kernel plus the separate pool backward.
+bool conv_mfma_can_unpool(const ConvPlan& p) { return p.splits > 1; }
 
 hipError_t launch_conv_mfma_unpool(const ConvPlan& p, const uint16_t* X, const uint16_t* Wk, float* part,
                                    const uint16_t* P, const uint8_t* idx, uint16_t* dZ, float slope, const cf_dims& x,
                                    int cout, int coutpad, hipStream_t s)
 {
     if (cout % 4 != 0 || !conv_mfma_can_unpool(p)) return hipErrorInvalidValue;
-    if (p.splits == 1) {
-        uint8_t* ix = const_cast<uint8_t*>(idx);
-        switch (p.cfg) {
-        case 0: return launch_kdr<64, 32, 128, 4, 4, 16, 32, 48, false, true>(X, Wk, dZ, nullptr, x, cout, coutpad, 1, s,
-                                                                                ix, slope, P);
-        case 1: return launch_kdr<64, 32, 128, 4, 8, 8, 32, 48, false, true>(X, Wk, dZ, nullptr, x, cout, coutpad, 1, s,
-                                                                               ix, slope, P);
-        case 2: return launch_kdr<32, 32, 64, 4, 8, 8, 32, 40, false, true>(X, Wk, dZ, nullptr, x, cout, coutpad, 1, s,
-                                                                              ix, slope, P);
-        default: return hipErrorInvalidValue;
-        }
-    }
     if (!part) return hipErrorInvalidValue;
     const hipError_t e = launch_conv_mfma_kernel(p, X, Wk, nullptr, part, x, cout, coutpad, s);
     if (e != hipSuccess) return e;

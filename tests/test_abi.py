@@ -74,17 +74,25 @@ def test_conv_workspace_sizes():
     # backward-weight: fp32 partials, a whole number of dW copies
     ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 32), 64, cf.CF_CONV_BWD_WEIGHT)
     assert ws % (27 * 32 * 64 * 4) == 0 and ws > 0
-    # the MFMA kernels address a tile's six input planes with 32-bit byte
-    # offsets: planes of 4096 x 4096 x 32 bf16 (6 planes = 6.4 GB) take the
-    # direct kernel, which needs no re-laid weights (bf16 DHWIO as given)
-    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 4096, 4096, 32), 64, cf.CF_CONV_FWD) == 0
+    # the bf16 MFMA kernels address a tile's six input planes with 32-bit
+    # byte offsets: planes of 4096 x 4096 x 32 bf16 (6 planes = 6.4 GB) take
+    # the fp32 matrix-core kernels on bf16 data (64-bit addressing), with
+    # fp32 weights [27][roundup(cout,64)][roundup(cin,16)]
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 4096, 4096, 32), 64, cf.CF_CONV_FWD) == 27 * 64 * 32 * 4
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 2048, 2048, 32), 64, cf.CF_CONV_FWD) == 27 * 128 * 32 * 2
-    # backward-data: the MFMA path keeps [27][roundup(cin,128)][cout]; the
-    # direct path the tap-flipped DHWIO copy [27][cout][cin]
+    # backward-data: the bf16 MFMA path keeps [27][roundup(cin,128)][cout];
+    # the fp32 matrix-core path [27][roundup(cin,64)][roundup(cout,16)] fp32
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 4096, 4096, 32), 64, cf.CF_CONV_BWD_DATA) == \
-        (27 * 32 * 64 * 2 + 255) // 256 * 256
+        27 * 64 * 64 * 4
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 1024, 1024, 32), 64, cf.CF_CONV_BWD_DATA) == \
         27 * 128 * 64 * 2
+    # bf16 layers whose channels are multiples of 4 but not of 32 (the
+    # 16-channel layers of the Table I network) use the fp32 matrix cores too
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_FWD) == 27 * 64 * 16 * 4
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_BWD_WEIGHT) % \
+        (27 * 16 * 32 * 4) == 0
+    # bf16 channels not multiples of 4 keep the direct kernel (bf16 DHWIO as given)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 3), 6, cf.CF_CONV_FWD) == 0
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 32), 32, cf.CF_CONV_FWD + 9) == 0
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 32), -1, cf.CF_CONV_FWD) == 0
 

@@ -37,6 +37,8 @@ CONV_CASES = [
     (1, 3, 4, 5, 32, 4),       # MFMA, BM 16 with 4 valid rows
     (2, 5, 9, 21, 4, 32),      # Cin = 4 layer-1 kernel
     (1, 6, 11, 17, 4, 16),     # Cin = 4, 16 outputs
+    (2, 6, 10, 9, 16, 32),     # 16 channels: fp32 matrix cores on bf16 data
+    (1, 5, 7, 9, 8, 12),       # 8 -> 12 channels: fp32 matrix cores on bf16 data
     (1, 4, 5, 6, 3, 5),        # direct bf16 fallback
     (1, 1, 1, 1, 32, 32),      # single voxel
 ]
@@ -108,6 +110,8 @@ WGRAD_CASES = [
     (1, 6, 10, 7, 64, 32),
     (1, 8, 8, 8, 256, 256),
     (2, 7, 6, 21, 4, 32),     # layer-1 kernel
+    (2, 7, 6, 9, 16, 32),     # 16 channels: fp32 matrix cores on bf16 data
+    (1, 6, 11, 17, 4, 16),    # 4 -> 16 channels: fp32 matrix cores on bf16 data
     (1, 4, 5, 6, 3, 5),       # direct fallback
     (1, 1, 1, 1, 32, 32),
 ]
