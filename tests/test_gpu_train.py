@@ -81,6 +81,29 @@ def test_train_step_matches_oracle(dtype):
         assert rel_err(gb, ref["dense_g"][k][1]) <= tol, k
 
 
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_train_step_update_at_rate_1e3(dtype):
+    """The SGD update at the benchmark configuration's published rate (1e-3)
+    rather than a gradient-recovery rate: each parameter's change must be
+    -1e-3 times the oracle's gradient, within the path's tolerance of the
+    change's RMS beyond the one fp32 rounding of the stored weight."""
+    B, size, filters, dense_w = 2, 16, [32, 64], [32, 16, 3]
+    x, conv, dense, t = make_problem(1, B, size, filters, dense_w, dtype)
+    lr = 1e-3
+    loss, pred, old, new = run_step(x, conv, dense, t, dtype, lr, size, filters, dense_w)
+    storage = "bf16" if dtype == BF else "f32"
+    ref = oracle.train_step(x, t, conv, dense, lr, SLOPE, storage=storage)
+    tol = TOL_BF16 if dtype == BF else TOL_F32
+    assert abs(loss - ref["loss"]) <= tol * ref["loss"]
+    L = len(filters)
+    grads = list(ref["conv_dw"]) + [g for k in range(3) for g in ref["dense_g"][k]]
+    for i, g in enumerate(grads):
+        w0, w1 = host64(old[i]), host64(new[i])
+        want = -np.float64(np.float32(lr)) * g
+        beyond = np.maximum(np.abs((w1 - w0) - want) - 0.5 * np.spacing(np.abs(w1).astype(np.float32)), 0.0)
+        assert beyond.max() <= tol * np.sqrt(np.mean(want * want)), (i, beyond.max())
+
+
 def composed_step(xd, conv_d, dense_d, td, lr):
     """The same step through the individual entry points (bf16)."""
     L = len(conv_d)
