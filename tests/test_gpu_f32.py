@@ -17,8 +17,12 @@ from gpu_util import TOL_F32, host64, rel_err, sample_points, to_dev
 pytestmark = pytest.mark.gpu
 F32 = torch.float32
 
+# Every kernel variant: 4 input channels (taps folded into K / kw into the
+# weight-gradient rows) with 16, 32 and 64 outputs; outputs <= 16, <= 32 and
+# wider on the general mapping.
 SMALL = [(2, 5, 9, 7, 32, 64), (1, 6, 10, 7, 64, 128), (1, 9, 5, 18, 4, 32), (2, 3, 4, 5, 8, 12),
-         (1, 4, 4, 4, 256, 256), (1, 1, 1, 1, 16, 16), (2, 7, 6, 17, 12, 20)]
+         (1, 4, 4, 4, 256, 256), (1, 1, 1, 1, 16, 16), (2, 7, 6, 17, 12, 20), (1, 6, 11, 17, 4, 16),
+         (1, 5, 6, 9, 4, 64)]
 
 
 @pytest.mark.parametrize("shape", SMALL)
