@@ -109,15 +109,13 @@ bool mfma_offsets_fit(const cf_dims& x, int64_t cin, int64_t cout)
     return 6 * x.h * x.w * cin * 2 < lim && 27 * roundup((int)cout, 128) * cin * 2 < lim;
 }
 
-// The Cin = 4 forward addresses a sample with 32-bit byte offsets.
-bool c4_offsets_fit(const cf_dims& x) { return x.d * x.h * x.w * 8 < ((int64_t)1 << 31); }
 
 Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 4 == 0) {
         if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
-        if (cin == 4 && c4_offsets_fit(x)) return Fwd::C4;
+        if (cin == 4 && conv_c4_fits(x)) return Fwd::C4;
     }
     // fp32 layers, and bf16 layers of other channel counts (multiples of 4)
     if (conv_f32_mfma_ok(x, cout)) return Fwd::F32Mfma;
@@ -148,7 +146,7 @@ size_t esize(cf_dtype dt) { return dt == CF_F32 ? 4 : 2; }
 // Fused block kernels exist for the 4-channel first layer in bf16.
 bool fused_pool_fwd_c4(cf_dtype dt, const cf_dims& x, int cout)
 {
-    return dt == CF_BF16 && x.c == 4 && cout % 32 == 0 && c4_offsets_fit(x);
+    return dt == CF_BF16 && x.c == 4 && cout % 32 == 0 && conv_c4_pool_fits(x, cout);
 }
 // The conv + pool forward is fused for Cin = 4 (one launch), and on the
 // MFMA path for plans with 4x4x16 tiles and no channel split (one launch) or

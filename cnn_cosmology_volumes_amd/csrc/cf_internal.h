@@ -155,6 +155,10 @@ hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y
                               int cout, int copad, hipStream_t s);
 // Same conv with leaky ReLU + 2^3 max pooling fused into the epilogue: writes
 // P [n, d/2, h/2, w/2, cout] and idx only (cout % 32 == 0; d, h, w even).
+// Shapes the Cin = 4 forward takes (32-bit offsets within a sample built
+// from 24-bit multiplies; pooled: a sample's P below 2^31 bytes).
+bool conv_c4_fits(const cf_dims& x);
+bool conv_c4_pool_fits(const cf_dims& x, int cout);
 hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx, float slope,
                                    const cf_dims& x, int cout, hipStream_t s);
 

@@ -27,11 +27,26 @@ constexpr int HD = TD + 2, HH = TH + 2, HW = TW + 2, HV = HD * HH * HW;
 //               conv output never goes to HBM.
 constexpr int ZS = 40;          // bf16 per voxel row of the pooled-epilogue tile (80 B)
 
+// q = x / d for the tile decode, on uniform values: the divisor's magic
+// numbers come from the host (make_fastdiv), so the decode is scalar
+// multiplies instead of a per-wave integer division; exact for every 32-bit x.
+struct FastDiv { uint32_t d, m, s; };
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f)
+{
+    return (uint32_t)(((uint64_t)__umulhi(x, f.m) + x) >> f.s);
+}
+FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    return FastDiv{d, (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1), s};
+}
+
 template <int BM, bool POOL>
 __global__ __launch_bounds__(NT)
 void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
                           uint16_t* __restrict__ Y, uint8_t* __restrict__ idx, float slope,
-                          int N, int D, int H, int W, int Cout, int tD, int tH, int tW)
+                          int N, int D, int H, int W, int Cout, FastDiv ftD, FastDiv ftH, FastDiv ftW)
 {
     constexpr int MI = BM / 16, NJ = WN / 16;
     // Halo: 4 bf16 per voxel, plus one zero voxel past the end (read, with
@@ -46,10 +61,15 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
-    const int tw_ = tile % tW; tile /= tW;
-    const int th_ = tile % tH; tile /= tH;
-    const int td_ = tile % tD;
-    const int n = tile / tD;
+    uint32_t q = fdiv(tile, ftW);
+    const int tw_ = (int)(tile - q * ftW.d);
+    tile = q;
+    q = fdiv(tile, ftH);
+    const int th_ = (int)(tile - q * ftH.d);
+    tile = q;
+    q = fdiv(tile, ftD);
+    const int td_ = (int)(tile - q * ftD.d);
+    const int n = (int)q;
     const int d0 = td_ * TD, h0 = th_ * TH, w0 = tw_ * TW;
     const int co_base = blockIdx.y * BM;
     const int64_t plane = (int64_t)H * W;
@@ -81,7 +101,9 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         for (int it = 0; it < IT; ++it) {
             const int r = rr + it * RS;
             const int gd = d0 + r / HH - 1, gh = h0 + r % HH - 1;
-            uint32_t off = (((uint32_t)gd * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) * 8u;
+            // 24-bit multiplies: the host keeps (D + 2)(H + 2) and W below 2^24
+            // (an out-of-volume gd or gh gives garbage that the select drops)
+            uint32_t off = (__umul24(__umul24((uint32_t)gd, (uint32_t)H) + (uint32_t)gh, (uint32_t)W) + (uint32_t)gw) * 8u;
             off = (col_ok && r < NR && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) ? off : 0x80000000u;
             asm volatile("" : "+v"(off));     // a select, not a branch around the load
             v[it] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0));
@@ -194,29 +216,59 @@ void conv3d_c4_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __rest
         float out[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) out[k] = best[k] > 0.f ? best[k] : slope * best[k];
-        const int64_t o = ((((int64_t)n * Dp + gpd) * Hp + gph) * Wp + gpw) * Cout + co;
-        *reinterpret_cast<uint4*>(Y + o) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
-                                                      pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
-        *reinterpret_cast<uint2*>(idx + o) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
-                                                        bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
+        // the sample's pooled outputs start at a scalar 64-bit offset; within
+        // a sample 32 bits suffice (the host keeps a sample's P below 2^31
+        // bytes), with 24-bit multiplies as for the halo
+        const int64_t obase = (int64_t)n * Dp * Hp * Wp * Cout;
+        const uint32_t o = __umul24(__umul24(__umul24((uint32_t)gpd, (uint32_t)Hp) + (uint32_t)gph, (uint32_t)Wp) +
+                                    (uint32_t)gpw, (uint32_t)Cout) + (uint32_t)co;
+        *reinterpret_cast<uint4*>(Y + obase + o) = make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                                                              pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+        *reinterpret_cast<uint2*>(idx + obase + o) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
+                                                                bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
     }
 }
 
+}  // namespace
+
+// The kernel addresses a sample's input with 32-bit byte offsets built from
+// 24-bit multiplies, and (pooled) a sample's P with 32-bit offsets.
+bool conv_c4_fits(const cf_dims& x)
+{
+    return x.d * x.h * x.w * 8 < ((int64_t)1 << 31) && (x.d + 2) * (x.h + 2) < ((int64_t)1 << 24) &&
+           x.w < ((int64_t)1 << 24);
+}
+
+bool conv_c4_pool_fits(const cf_dims& x, int cout)
+{
+    return conv_c4_fits(x) && (x.d / 2) * (x.h / 2) * (x.w / 2) * (int64_t)cout * 2 < ((int64_t)1 << 31);
+}
+
+namespace {
+dim3 c4_grid(const cf_dims& x, int bm, int cout, FastDiv& fd, FastDiv& fh, FastDiv& fw)
+{
+    const int64_t tD = (x.d + TD - 1) / TD, tH = (x.h + TH - 1) / TH, tW = (x.w + TW - 1) / TW;
+    fd = make_fastdiv((uint32_t)tD);
+    fh = make_fastdiv((uint32_t)tH);
+    fw = make_fastdiv((uint32_t)tW);
+    return dim3((unsigned)(x.n * tD * tH * tW), (unsigned)((cout + bm - 1) / bm));
+}
 }  // namespace
 
 hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y, const cf_dims& x, int cout,
                               int copad, hipStream_t s)
 {
     (void)copad;
-    if (x.d * x.h * x.w * 8 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit sample offsets
-    const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
-    const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
+    if (!conv_c4_fits(x)) return hipErrorInvalidValue;
+    FastDiv fd, fh, fw;
     if (cout <= 16) {
-        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<16, false>), dim3(ntile, (unsigned)((cout + 15) / 16)), dim3(NT), 0, s,
-                           X, Wk, Y, nullptr, 0.f, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
+        const dim3 g = c4_grid(x, 16, cout, fd, fh, fw);
+        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<16, false>), g, dim3(NT), 0, s, X, Wk, Y, nullptr, 0.f, (int)x.n,
+                           (int)x.d, (int)x.h, (int)x.w, cout, fd, fh, fw);
     } else {
-        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, false>), dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s,
-                           X, Wk, Y, nullptr, 0.f, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
+        const dim3 g = c4_grid(x, 32, cout, fd, fh, fw);
+        hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, false>), g, dim3(NT), 0, s, X, Wk, Y, nullptr, 0.f, (int)x.n,
+                           (int)x.d, (int)x.h, (int)x.w, cout, fd, fh, fw);
     }
     return hipGetLastError();
 }
@@ -224,11 +276,11 @@ hipError_t launch_conv_c4_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* Y
 hipError_t launch_conv_c4_pool_fwd(const uint16_t* X, const uint16_t* Wk, uint16_t* P, uint8_t* idx, float slope,
                                    const cf_dims& x, int cout, hipStream_t s)
 {
-    if (x.d * x.h * x.w * 8 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit sample offsets
-    const int tD = (int)((x.d + TD - 1) / TD), tH = (int)((x.h + TH - 1) / TH), tW = (int)((x.w + TW - 1) / TW);
-    const unsigned ntile = (unsigned)(x.n * tD * tH * tW);
-    hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, true>), dim3(ntile, (unsigned)((cout + 31) / 32)), dim3(NT), 0, s, X,
-                       Wk, P, idx, slope, (int)x.n, (int)x.d, (int)x.h, (int)x.w, cout, tD, tH, tW);
+    if (!conv_c4_pool_fits(x, cout)) return hipErrorInvalidValue;
+    FastDiv fd, fh, fw;
+    const dim3 g = c4_grid(x, 32, cout, fd, fh, fw);
+    hipLaunchKernelGGL((conv3d_c4_fwd_kernel<32, true>), g, dim3(NT), 0, s, X, Wk, P, idx, slope, (int)x.n, (int)x.d,
+                       (int)x.h, (int)x.w, cout, fd, fh, fw);
     return hipGetLastError();
 }
 
