@@ -135,7 +135,7 @@ Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     if (dt == CF_BF16) {
         if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
-        if (x.c == 4 && cout == 32 && wgrad_c4_fits(x)) return Wg::C4;
+        if (x.c == 4 && (cout == 32 || cout == 16) && wgrad_c4_fits(x)) return Wg::C4;
     }
     if (x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
     return Wg::Direct;
@@ -159,7 +159,11 @@ bool fused_pool_fwd(cf_dtype dt, const cf_dims& x, int cout)
 {
     return fused_pool_fwd_c4(dt, x, cout) || fused_pool_fwd_mfma(dt, x, cout);
 }
-bool fused_pool_wgrad(cf_dtype dt, const cf_dims& x, int cout) { return wgrad_path(dt, x, cout) == Wg::C4; }
+// (the fused kernel takes 32 output channels)
+bool fused_pool_wgrad(cf_dtype dt, const cf_dims& x, int cout)
+{
+    return cout == 32 && wgrad_path(dt, x, cout) == Wg::C4;
+}
 
 // Bytes of re-laid weights each path uses.
 size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)

@@ -435,7 +435,7 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
                         const cf_dims& x, int cout, hipStream_t s)
 {
     if (p.kind == 1) {
-        hipError_t e = launch_wgrad_c4_partials(p, X, dY, nullptr, nullptr, nullptr, 0.f, part, x, s);
+        hipError_t e = launch_wgrad_c4_partials(p, X, dY, nullptr, nullptr, nullptr, 0.f, part, x, cout, s);
         if (e != hipSuccess) return e;
     } else {
         const int bD = (int)((x.d + GW_TD - 1) / GW_TD), bH = (int)((x.h + GW_TH - 1) / GW_TH),

@@ -41,16 +41,19 @@ constexpr int C4_NXB = C4_NR * 3;                          // X blocks: rows x {
 constexpr int C4_NACC = 2 * 3 * 3;                         // co frags x pair frags x kw
 constexpr int C4_NPV = (C4_TD / 2) * (C4_TH / 2) * (C4_TW / 2);   // 32 pooled voxels per box
 
-template <bool FUSED>
+template <bool FUSED, int CO>
 __global__ __launch_bounds__(C4_NT, 2)
 void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY,
                      const uint16_t* __restrict__ dP, const uint16_t* __restrict__ Pv, const uint8_t* __restrict__ pidx,
                      float slope, float* __restrict__ part, int N, int D, int H, int W, int bD, int bH, int bW,
                      int64_t nbox, int boxes_per_split)
 {
-    constexpr int CO = 32;
+    // CO output channels: 32, or 16 (not fused), where the dY staging tasks
+    // of channel groups 4..7 are empty and one output-channel fragment is live
+    static_assert(CO == 32 || (CO == 16 && !FUSED), "output channels");
+    constexpr int NCF = CO / 16;                           // output-channel fragments
     __shared__ __attribute__((aligned(16))) uint16_t xt[2][4 * C4_XPL];
-    __shared__ __attribute__((aligned(16))) uint16_t dt[2][CO * C4_DROW];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][32 * C4_DROW];
     __shared__ __attribute__((aligned(16))) float red[64 * C4_NACC * 4];
     // fused: the box's gated pooled gradient (bf16) and window indices, stored
     // [4-channel group][pooled voxel] so that a thread's 4 pooled voxels x 4
@@ -128,7 +131,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         if (!FUSED) {
             const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * CO, lim);
             const int gh = bp.bh * C4_TH + th_o, gw0 = bp.bw * C4_TW + w0_o;
-            const bool rok = (gd0 + td_o < D) & (gh < H);
+            const bool rok = (gd0 + td_o < D) & (gh < H) & (cg < CO / 4);
             const uint32_t rbase = ((uint32_t)td_o * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -200,6 +203,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         if (!FUSED) {
             uint4 t[4];
             transpose8x4(ud, t);
+            // (CO = 16: groups 4..7 loaded zeros and fill rows 16..31, unread)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 *reinterpret_cast<uint4*>(&dt[buf][(cg * 4 + c) * C4_DROW + oct * 8]) = t[c];
@@ -280,9 +284,9 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         }
     };
 
-    f32x4 acc[2][3][3];            // [co frag][pair frag][kw]
+    f32x4 acc[NCF][3][3];          // [co frag][pair frag][kw]
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NCF; ++i)
 #pragma unroll
         for (int f = 0; f < 3; ++f)
 #pragma unroll
@@ -310,9 +314,9 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             const int s = wave + 4 * ss;                       // k-step of this wave
             const int o = 4 * s + lg;                          // octet of this lane group
             const int td = o / (C4_TH * 2), th = (o / 2) % C4_TH, w0 = (o & 1) * 8;
-            bf16x8 a[2];
+            bf16x8 a[NCF];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NCF; ++i)
                 a[i] = *reinterpret_cast<const bf16x8*>(db + (16 * i + l16) * C4_DROW + o * 8);
 #pragma unroll
             for (int f = 0; f < 3; ++f) {
@@ -329,7 +333,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
                 const bf16x8 b1 = __builtin_bit_cast(bf16x8, s1);
                 const bf16x8 b2 = __builtin_bit_cast(bf16x8, make_uint4(q.y, q.z, q.w, e));
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
+                for (int i = 0; i < NCF; ++i) {
                     acc[i][f][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b0, acc[i][f][0], 0, 0, 0);
                     acc[i][f][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b1, acc[i][f][1], 0, 0, 0);
                     acc[i][f][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2, acc[i][f][2], 0, 0, 0);
@@ -372,7 +376,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         __syncthreads();
         if (wave == w) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NCF; ++i)
 #pragma unroll
                 for (int f = 0; f < 3; ++f)
 #pragma unroll
@@ -382,7 +386,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NCF; ++i)
 #pragma unroll
                 for (int f = 0; f < 3; ++f)
 #pragma unroll
@@ -400,7 +404,7 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
             for (int kw = 0; kw < 3; ++kw) {
                 const int t = pr * 3 + kw;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
+                for (int i = 0; i < NCF; ++i) {
                     const int co = 16 * i + 4 * lg;
                     const f32x4 r = acc[i][f][kw];
                     *reinterpret_cast<float4*>(out + (t * 4 + ci) * CO + co) = make_float4(r[0], r[1], r[2], r[3]);
@@ -414,19 +418,27 @@ void wgrad_c4_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
 
 hipError_t launch_wgrad_c4_partials(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, const uint16_t* dP,
                                     const uint16_t* P, const uint8_t* idx, float slope, float* part, const cf_dims& x,
-                                    hipStream_t s)
+                                    int cout, hipStream_t s)
 {
     const int bD = (int)((x.d + C4_TD - 1) / C4_TD), bH = (int)((x.h + C4_TH - 1) / C4_TH),
               bW = (int)((x.w + C4_TW - 1) / C4_TW);
     const int64_t nbox = x.n * bD * bH * bW;
-    if (dP)
-        hipLaunchKernelGGL(wgrad_c4_kernel<true>, dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, nullptr, dP, P, idx,
-                           slope, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
+    if (dP) {
+        if (cout != 32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((wgrad_c4_kernel<true, 32>), dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, nullptr, dP, P,
+                           idx, slope, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
                            (int)p.vox_per_split);
-    else
-        hipLaunchKernelGGL(wgrad_c4_kernel<false>, dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, dY, nullptr, nullptr,
-                           nullptr, 0.f, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
+    } else if (cout == 32) {
+        hipLaunchKernelGGL((wgrad_c4_kernel<false, 32>), dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, dY, nullptr,
+                           nullptr, nullptr, 0.f, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
                            (int)p.vox_per_split);
+    } else if (cout == 16) {
+        hipLaunchKernelGGL((wgrad_c4_kernel<false, 16>), dim3((unsigned)p.splits), dim3(C4_NT), 0, s, X, dY, nullptr,
+                           nullptr, nullptr, 0.f, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, bD, bH, bW, nbox,
+                           (int)p.vox_per_split);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -434,7 +446,7 @@ hipError_t launch_wgrad_c4_pool(const WgradPlan& p, const uint16_t* X, const uin
                                 const uint8_t* idx, float slope, float* part, float* dW, const cf_dims& x,
                                 hipStream_t s)
 {
-    hipError_t e = launch_wgrad_c4_partials(p, X, nullptr, dP, P, idx, slope, part, x, s);
+    hipError_t e = launch_wgrad_c4_partials(p, X, nullptr, dP, P, idx, slope, part, x, 32, s);
     if (e != hipSuccess) return e;
     return launch_wgrad_reduce(part, dW, (int64_t)27 * 4 * 32, p.splits, s);
 }

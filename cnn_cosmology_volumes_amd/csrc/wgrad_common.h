@@ -56,11 +56,11 @@ __device__ __forceinline__ BoxPos box_uniform(BoxPos p)
 
 // dW[e] = sum over splits of part[s][e] in a fixed order (deterministic).
 hipError_t launch_wgrad_reduce(const float* part, float* dW, int64_t n, int splits, hipStream_t s);
-// The 4-channel backward-weight's fp32 partials ([splits][27*4*32]); with dP,
-// P and idx non-null (fused) the conv-output gradient is rebuilt from the
-// pooled gradient, else it is read from dY.
+// The 4-channel backward-weight's fp32 partials ([splits][27*4*cout]), cout
+// 32 or 16; with dP, P and idx non-null (fused, cout 32) the conv-output
+// gradient is rebuilt from the pooled gradient, else it is read from dY.
 hipError_t launch_wgrad_c4_partials(const WgradPlan& p, const uint16_t* X, const uint16_t* dY, const uint16_t* dP,
                                     const uint16_t* P, const uint8_t* idx, float slope, float* part, const cf_dims& x,
-                                    hipStream_t s);
+                                    int cout, hipStream_t s);
 
 }  // namespace cf
