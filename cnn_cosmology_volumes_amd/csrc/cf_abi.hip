@@ -848,7 +848,7 @@ cf_status cf_batchnorm_fwd(cf_dtype dtype, cf_dims x, const void* X, const float
     if (!X || !gamma || !beta || !Y || !mean || !invstd) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: null pointer");
     if (!al16(X) || !al16(gamma) || !al16(beta) || !al16(Y) || !al16(mean) || !al16(invstd))
         return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: pointers must be 16-byte aligned");
-    if (!(eps >= 0.f)) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: eps must be >= 0");
+    if (!(eps > 0.f) || !(eps < INFINITY)) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: eps must be positive and finite");
     const size_t need = bn_ws_bytes(x);
     if (ws_bytes < need) return fail(CF_ERR_WORKSPACE, "cf_batchnorm_fwd: workspace %zu < %zu bytes", ws_bytes, need);
     if (!ws || !al16(ws)) return fail(CF_ERR_INVALID, "cf_batchnorm_fwd: workspace null or misaligned");

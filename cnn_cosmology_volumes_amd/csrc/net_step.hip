@@ -51,7 +51,7 @@ cf_status check_net(const cf_net_desc* m, cf_dtype dt, int32_t B)
     if (m->cin <= 0 || m->d <= 0 || m->h <= 0 || m->w <= 0) return report(CF_ERR_INVALID, "input shape must be positive");
     if (m->ndense < 1 || m->ndense > CF_MAX_DENSE) return report(CF_ERR_INVALID, "ndense must be 1..%d", CF_MAX_DENSE);
     if (!(m->slope >= 0.f)) return report(CF_ERR_INVALID, "slope must be >= 0");
-    if (m->batch_norm && !(m->bn_eps >= 0.f)) return report(CF_ERR_INVALID, "bn_eps must be >= 0");
+    if (m->batch_norm && !(m->bn_eps > 0.f && m->bn_eps < INFINITY)) return report(CF_ERR_INVALID, "bn_eps must be positive and finite");
     int64_t d = m->d, h = m->h, w = m->w;
     for (int l = 0; l < m->nlayers; ++l) {
         const int f = m->filters[l], s = m->stride[l], p = m->pool[l];

@@ -320,8 +320,10 @@ size_t cf_batchnorm_workspace_size(cf_dtype dtype, cf_dims x);
  *   invstd = 1 / sqrt(var + eps);  Y = (X - mean) * gamma * invstd + beta
  *   X, Y [x.n, x.d, x.h, x.w, x.c] (dtype); gamma, beta, mean, invstd [x.c]
  *   fp32 (mean and invstd are outputs, for the backward).
- * x.c must be a multiple of 4 and at most 1024 (else CF_ERR_UNSUPPORTED).
- * Statistics are reduced in a fixed order (fp64 across blocks). */
+ * x.c must be a multiple of 4 and at most 1024 (else CF_ERR_UNSUPPORTED);
+ * eps must be positive and finite (else CF_ERR_INVALID: a constant channel
+ * would divide by zero).  Statistics are reduced in a fixed order (fp64
+ * across blocks). */
 cf_status cf_batchnorm_fwd(cf_dtype dtype, cf_dims x, const void* X, const float* gamma, const float* beta,
                            float eps, void* Y, float* mean, float* invstd, void* ws, size_t ws_bytes,
                            hipStream_t stream);
@@ -416,7 +418,7 @@ typedef struct {
     int32_t stride[CF_MAX_BLOCKS];    /* 1 or 2 */
     int32_t pool[CF_MAX_BLOCKS];      /* cf_pool_kind */
     int32_t batch_norm;               /* != 0: BN after every conv */
-    float bn_eps;
+    float bn_eps;                     /* > 0 when batch_norm is set */
     int32_t ndense;                   /* 1..CF_MAX_DENSE */
     int32_t dense[CF_MAX_DENSE];
     int32_t dense_bias;               /* != 0: dense layers have biases */

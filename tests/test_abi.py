@@ -214,3 +214,18 @@ def test_train_step_aux_validation():
     assert st == cf.CF_ERR_INVALID
     assert L.cf_step_aux_create(None) == cf.CF_ERR_INVALID
     assert L.cf_step_aux_destroy(None) == cf.CF_OK
+
+
+def test_batchnorm_rejects_nonpositive_eps():
+    """A zero (or negative, NaN, infinite) epsilon is rejected before any
+    GPU work: with eps = 0 a constant channel would divide by zero."""
+    L = cf.lib()
+    x = cf.dims((1, 4, 4, 4, 8))
+    for eps in (0.0, -1e-5, float("nan"), float("inf")):
+        st = L.cf_batchnorm_fwd(cf.CF_BF16, x, FAKE, FAKE, FAKE, eps, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+        assert st == cf.CF_ERR_INVALID, eps
+        assert b"eps" in L.cf_last_error()
+    m = cf.net_desc(4, 16, [16, 32], [1, 1], [cf.CF_POOL_MAX, cf.CF_POOL_MAX], dense=[8, 4], batch_norm=True,
+                    bn_eps=0.0)
+    assert L.cf_net_train_step_workspace_size(ctypes.byref(m), cf.CF_BF16, 2) == 0
+    assert b"bn_eps" in L.cf_last_error()
