@@ -97,8 +97,8 @@ cf_status check_conv(cf_dtype dt, const cf_dims& x, int32_t cout, const cf_conv&
 // ------------------------------------------------------------ path choice
 cf_dims with_c(const cf_dims& x, int64_t c) { cf_dims y = x; y.c = c; return y; }
 
-enum class Fwd { Mfma, C4, F32Mfma, Direct };
-enum class Wg { Mfma, C4, F32Mfma, Direct };
+enum class Fwd { Mfma, C4, F32Mfma, MfmaPad, Direct };
+enum class Wg { Mfma, C4, F32Mfma, MfmaPad, Direct };
 
 // The MFMA conv kernels address a tile's six input planes (of `cin`
 // channels) and the weight copy with 32-bit byte offsets; a shape beyond
@@ -110,12 +110,26 @@ bool mfma_offsets_fit(const cf_dims& x, int64_t cin, int64_t cout)
 }
 
 
+// bf16 layers whose input channels are a multiple of 8 but not of 32 (and
+// more than 4) run the bf16 MFMA kernels on a copy of the input padded with
+// zero channels to the next multiple of 32 (MfmaPad): the zero channels add
+// exact zeros to every sum, at twice the MFMA work for 16 channels, where the
+// fp32 matrix cores would run at a sixteenth of the rate.
+int64_t pad32(int64_t c) { return (c + 31) / 32 * 32; }
+bool pad_path_ok(cf_dtype dt, const cf_dims& x, int cout)
+{
+    return dt == CF_BF16 && x.c > 4 && x.c % 8 == 0 && x.c % 32 != 0 && cout % 4 == 0 &&
+           mfma_offsets_fit(x, pad32(x.c), cout);
+}
+size_t xpad_bytes(const cf_dims& x) { return (size_t)(x.n * x.d * x.h * x.w) * (size_t)pad32(x.c) * 2; }
+
 Fwd fwd_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     const int64_t cin = x.c;
     if (dt == CF_BF16 && cout % 4 == 0) {
         if (cin % 32 == 0 && mfma_offsets_fit(x, cin, cout)) return Fwd::Mfma;
         if (cin == 4 && conv_c4_fits(x)) return Fwd::C4;
+        if (pad_path_ok(dt, x, cout)) return Fwd::MfmaPad;
     }
     // fp32 layers, and bf16 layers of other channel counts (multiples of 4)
     if (conv_f32_mfma_ok(x, cout)) return Fwd::F32Mfma;
@@ -136,6 +150,7 @@ Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
     if (dt == CF_BF16) {
         if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
         if (x.c == 4 && (cout == 32 || cout == 16) && wgrad_c4_fits(x)) return Wg::C4;
+        if (cout % 32 == 0 && pad_path_ok(dt, x, cout)) return Wg::MfmaPad;
     }
     if (x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
     return Wg::Direct;
@@ -172,6 +187,7 @@ size_t fwd_wk_bytes(Fwd p, int64_t cin, int cout)
     case Fwd::Mfma: return (size_t)27 * roundup(cout, 128) * (size_t)cin * 2;
     case Fwd::C4: return (size_t)roundup(cout, 128) * 128 * 2;
     case Fwd::F32Mfma: return conv_f32_wk_bytes((int)cin, cout);
+    case Fwd::MfmaPad: return (size_t)27 * roundup(cout, 128) * (size_t)pad32(cin) * 2;
     default: return 0;
     }
 }
@@ -206,6 +222,16 @@ hipError_t run_fwd(Fwd p, cf_dtype dt, const cf_dims& x, const void* X, const vo
     case Fwd::F32Mfma:
         if (dt == CF_F32) return launch_conv_f32_mfma((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
         return launch_conv_f32_mfma((const uint16_t*)X, (const float*)wk, (uint16_t*)Y, x, cout, s);
+    case Fwd::MfmaPad: {
+        // scratch: the padded input, then the plan's partials
+        const cf_dims xp = with_c(x, pad32(x.c));
+        uint16_t* xpad = reinterpret_cast<uint16_t*>(part);
+        float* part2 = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + up256(xpad_bytes(x)));
+        const hipError_t e = launch_pad_channels((const uint16_t*)X, xpad, x.n * x.d * x.h * x.w, (int)x.c, (int)xp.c, s);
+        if (e != hipSuccess) return e;
+        return launch_conv_mfma(plan_conv_mfma(xp, cout), xpad, (const uint16_t*)wk, (uint16_t*)Y, part2, xp, cout,
+                                roundup(cout, 128), s);
+    }
     default:
         if (dt == CF_F32) return launch_conv_direct<float>((const float*)X, (const float*)wk, (float*)Y, x, cout, s);
         return launch_conv_direct<uint16_t>((const uint16_t*)X, (const uint16_t*)wk, (uint16_t*)Y, x, cout, s);
@@ -214,6 +240,7 @@ hipError_t run_fwd(Fwd p, cf_dtype dt, const cf_dims& x, const void* X, const vo
 
 size_t fwd_part_bytes(Fwd p, const cf_dims& x, int cout)
 {
+    if (p == Fwd::MfmaPad) return up256(xpad_bytes(x)) + plan_conv_mfma(with_c(x, pad32(x.c)), cout).part_bytes;
     return p == Fwd::Mfma ? plan_conv_mfma(x, cout).part_bytes : 0;
 }
 
@@ -243,6 +270,11 @@ size_t dgrad_part_bytes(Fwd p, const cf_dims& x, int cout)
 size_t wgrad_part_bytes(Wg p, cf_dtype dt, const cf_dims& x, int cout)
 {
     if (p == Wg::F32Mfma) return plan_wgrad_f32(x, cout).part_bytes;
+    if (p == Wg::MfmaPad) {
+        // the padded input, the padded gradient [27][pad32(cin)][cout], the partials
+        const cf_dims xp = with_c(x, pad32(x.c));
+        return up256(xpad_bytes(x)) + up256((size_t)27 * xp.c * cout * 4) + plan_wgrad(xp, cout).part_bytes;
+    }
     if (p != Wg::Direct) return plan_wgrad(x, cout).part_bytes;
     return dt == CF_F32 ? wgrad_direct_part_bytes<float>(x, cout) : wgrad_direct_part_bytes<uint16_t>(x, cout);
 }
@@ -255,6 +287,18 @@ hipError_t run_wgrad(Wg p, cf_dtype dt, const cf_dims& x, const void* X, const v
     if (p == Wg::F32Mfma)
         return launch_wgrad_f32_mfma(plan_wgrad_f32(x, cout), (const uint16_t*)X, (const uint16_t*)dY, part, dW, x,
                                      cout, s);
+    if (p == Wg::MfmaPad) {
+        const cf_dims xp = with_c(x, pad32(x.c));
+        char* c8 = reinterpret_cast<char*>(part);
+        uint16_t* xpad = reinterpret_cast<uint16_t*>(c8);
+        float* dwp = reinterpret_cast<float*>(c8 + up256(xpad_bytes(x)));
+        float* part2 = reinterpret_cast<float*>(c8 + up256(xpad_bytes(x)) + up256((size_t)27 * xp.c * cout * 4));
+        hipError_t e = launch_pad_channels((const uint16_t*)X, xpad, x.n * x.d * x.h * x.w, (int)x.c, (int)xp.c, s);
+        if (e != hipSuccess) return e;
+        e = launch_wgrad(plan_wgrad(xp, cout), xpad, (const uint16_t*)dY, part2, dwp, xp, cout, s);
+        if (e != hipSuccess) return e;
+        return launch_unpad_dw(dwp, dW, (int)x.c, (int)xp.c, cout, s);
+    }
     if (p != Wg::Direct) {
         const WgradPlan plan = plan_wgrad(x, cout);
         return launch_wgrad(plan, (const uint16_t*)X, (const uint16_t*)dY, part, dW, x, cout, s);
@@ -277,6 +321,8 @@ hipError_t prep_fwd(Fwd p, cf_dtype dt, const void* W, bool src_f32, int64_t cin
     case Fwd::Mfma: return launch_wprep_fwd(W, src_f32, (int)cin, cout, roundup(cout, 128), (uint16_t*)wk, s);
     case Fwd::C4: return launch_wprep_c4(W, src_f32, cout, roundup(cout, 128), (uint16_t*)wk, s);
     case Fwd::F32Mfma: return launch_wprep_f32(W, f32_wsrc(dt, src_f32), (int)cin, cout, false, (float*)wk, s);
+    case Fwd::MfmaPad:
+        return launch_wprep_fwd_pad(W, src_f32, (int)cin, (int)pad32(cin), cout, roundup(cout, 128), (uint16_t*)wk, s);
     default: return hipSuccess;
     }
 }
@@ -1089,6 +1135,10 @@ cf_status cf_train_step(const cf_model_desc* m, cf_dtype dtype, int32_t B, const
         else if (Lp.fwd == Fwd::F32Mfma)
             CF_TRY_HIP(launch_wprep_f32(params[l], f32_wsrc(dtype, true), (int)Lp.x.c, Lp.cout, false,
                                         (float*)(w + Lp.wk_fwd), stream),
+                       "weight re-layout");
+        else if (Lp.fwd == Fwd::MfmaPad)
+            CF_TRY_HIP(launch_wprep_fwd_pad(params[l], true, (int)Lp.x.c, (int)pad32(Lp.x.c), Lp.cout,
+                                            roundup(Lp.cout, 128), (uint16_t*)(w + Lp.wk_fwd), stream),
                        "weight re-layout");
         if (l > 0) {
             if (Lp.dg == Fwd::Mfma) {

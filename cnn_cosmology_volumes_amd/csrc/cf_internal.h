@@ -99,6 +99,14 @@ cf_status report(cf_status s, const char* fmt, ...);
 // c4:    Wk[co][128] with k = t*4 + ci, zero for t >= 27 (Cin == 4 only)
 hipError_t launch_wprep_fwd(const void* W, bool w_is_f32, int cin, int cout, int copad, uint16_t* Wk, hipStream_t s);
 hipError_t launch_wprep_dgrad(const void* W, bool w_is_f32, int cin, int cout, int cipad, uint16_t* Wk, hipStream_t s);
+// The forward layout with the input channels padded to cinp (zeros beyond cin).
+hipError_t launch_wprep_fwd_pad(const void* W, bool w_is_f32, int cin, int cinp, int cout, int copad, uint16_t* Wk,
+                                hipStream_t s);
+// bf16 activations with cin channels copied into cinp channels, zeros after
+// (cin, cinp multiples of 8); the matching backward-weight result [27][cinp]
+// [cout] cut back to [27][cin][cout].
+hipError_t launch_pad_channels(const uint16_t* X, uint16_t* Y, int64_t nvox, int cin, int cinp, hipStream_t s);
+hipError_t launch_unpad_dw(const float* dWp, float* dW, int cin, int cinp, int cout, hipStream_t s);
 hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, uint16_t* Wk, hipStream_t s);
 // The same re-layouts, several in one launch (identical results).
 struct WprepJob {

@@ -194,4 +194,57 @@ CF_INST(float)
 CF_INST(uint16_t)
 #undef CF_INST
 
+namespace {
+
+// Y[v][c] = X[v][c] for c < cin, 0 for cin <= c < cinp (bf16, NDHWC);
+// one thread per (voxel, 8-channel group), 16-byte loads and stores.
+__global__ void pad_channels_kernel(const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int64_t nvox, int cin,
+                                    int cinp)
+{
+    const int gp = cinp / 8, gi = cin / 8;
+    const int64_t total = nvox * gp;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t v = i / gp;
+        const int g = (int)(i - v * gp);
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (g < gi) val = *reinterpret_cast<const uint4*>(X + v * cin + 8 * g);
+        *reinterpret_cast<uint4*>(Y + v * cinp + 8 * g) = val;
+    }
+}
+
+// dW[t][ci][co] = dWp[t][ci][co] for ci < cin (the rows of the padded input
+// channels are dropped).
+__global__ void unpad_dw_kernel(const float* __restrict__ dWp, float* __restrict__ dW, int cin, int cinp, int cout)
+{
+    const int64_t total = (int64_t)27 * cin * cout;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = e / ((int64_t)cin * cout);
+        const int64_t r = e - t * cin * cout;
+        dW[e] = dWp[t * cinp * cout + r];
+    }
+}
+
+unsigned grid_for(int64_t n)
+{
+    int64_t b = (n + 255) / 256;
+    if (b > 65536) b = 65536;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+hipError_t launch_pad_channels(const uint16_t* X, uint16_t* Y, int64_t nvox, int cin, int cinp, hipStream_t s)
+{
+    if (cin % 8 || cinp % 8 || cinp < cin) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pad_channels_kernel, dim3(grid_for(nvox * (cinp / 8))), dim3(256), 0, s, X, Y, nvox, cin, cinp);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpad_dw(const float* dWp, float* dW, int cin, int cinp, int cout, hipStream_t s)
+{
+    hipLaunchKernelGGL(unpad_dw_kernel, dim3(grid_for((int64_t)27 * cin * cout)), dim3(256), 0, s, dWp, dW, cin, cinp,
+                       cout);
+    return hipGetLastError();
+}
+
 }  // namespace cf

@@ -60,6 +60,20 @@ __global__ void wprep_fwd_kernel(const void* W, bool f32, int cin, int cout, int
         Wk[e] = wk_fwd_elem(W, f32, cin, cout, copad, e);
 }
 
+// fwd with the input channels padded to cinp (zero columns for ci >= cin):
+// Wk[t][co][ci], ci < cinp.
+__global__ void wprep_fwd_pad_kernel(const void* W, bool f32, int cin, int cinp, int cout, int copad, uint16_t* Wk)
+{
+    const int64_t total = (int64_t)27 * copad * cinp;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t u = (uint32_t)e;
+        const int ci = (int)(u % (uint32_t)cinp);
+        const int co = (int)((u / (uint32_t)cinp) % (uint32_t)copad);
+        const int t = (int)(u / ((uint32_t)cinp * (uint32_t)copad));
+        Wk[e] = (ci < cin && co < cout) ? f2bf(wload(W, f32, ((int64_t)t * cin + ci) * cout + co)) : (uint16_t)0;
+    }
+}
+
 __global__ void wprep_dgrad_kernel(const void* W, bool f32, int cin, int cout, int cipad, uint16_t* Wk)
 {
     const int64_t total = (int64_t)27 * cipad * cout;
@@ -190,6 +204,14 @@ hipError_t launch_wprep_fwd(const void* W, bool w_is_f32, int cin, int cout, int
 {
     hipLaunchKernelGGL(wprep_fwd_kernel, dim3(blocks_for((int64_t)27 * copad * cin)), dim3(256), 0, s, W, w_is_f32,
                        cin, cout, copad, Wk);
+    return hipGetLastError();
+}
+
+hipError_t launch_wprep_fwd_pad(const void* W, bool w_is_f32, int cin, int cinp, int cout, int copad, uint16_t* Wk,
+                                hipStream_t s)
+{
+    hipLaunchKernelGGL(wprep_fwd_pad_kernel, dim3(blocks_for((int64_t)27 * copad * cinp)), dim3(256), 0, s, W, w_is_f32,
+                       cin, cinp, cout, copad, Wk);
     return hipGetLastError();
 }
 

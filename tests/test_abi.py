@@ -86,11 +86,15 @@ def test_conv_workspace_sizes():
         27 * 64 * 64 * 4
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 1024, 1024, 32), 64, cf.CF_CONV_BWD_DATA) == \
         27 * 128 * 64 * 2
-    # bf16 layers whose channels are multiples of 4 but not of 32 (the
-    # 16-channel layers of the Table I network) use the fp32 matrix cores too
-    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_FWD) == 27 * 64 * 16 * 4
-    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_BWD_WEIGHT) % \
-        (27 * 16 * 32 * 4) == 0
+    # bf16 layers with input channels a multiple of 8 but not of 32 (the
+    # 16-channel layer of the Table I network) run the bf16 kernels on a copy
+    # of the input padded to 32 channels: padded weights, the padded copy
+    xp = 8 * 64 ** 3 * 32 * 2
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_FWD) == 27 * 128 * 32 * 2 + xp
+    ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, (8, 64, 64, 64, 16), 32, cf.CF_CONV_BWD_WEIGHT)
+    assert (ws - xp - 27 * 32 * 32 * 4) % (27 * 32 * 32 * 4) == 0 and ws > xp
+    # other multiples of 4 (here 12) use the fp32 matrix cores on bf16 data
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (2, 8, 8, 8, 12), 32, cf.CF_CONV_FWD) == 27 * 64 * 16 * 4
     # bf16 channels not multiples of 4 keep the direct kernel (bf16 DHWIO as given)
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 3), 6, cf.CF_CONV_FWD) == 0
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 8, 8, 32), 32, cf.CF_CONV_FWD + 9) == 0

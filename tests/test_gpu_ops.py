@@ -37,8 +37,10 @@ CONV_CASES = [
     (1, 3, 4, 5, 32, 4),       # MFMA, BM 16 with 4 valid rows
     (2, 5, 9, 21, 4, 32),      # Cin = 4 layer-1 kernel
     (1, 6, 11, 17, 4, 16),     # Cin = 4, 16 outputs
-    (2, 6, 10, 9, 16, 32),     # 16 channels: fp32 matrix cores on bf16 data
-    (1, 5, 7, 9, 8, 12),       # 8 -> 12 channels: fp32 matrix cores on bf16 data
+    (2, 6, 10, 9, 16, 32),     # 16 input channels: bf16 kernels on an input padded to 32
+    (1, 5, 7, 9, 8, 12),       # 8 -> 12 channels: padded input (bwd-data on the fp32 matrix cores)
+    (1, 4, 6, 20, 24, 64),     # 24 input channels, padded, 64-channel blocks
+    (2, 5, 6, 7, 12, 20),      # 12 -> 20 channels: fp32 matrix cores on bf16 data
     (1, 4, 5, 6, 3, 5),        # direct bf16 fallback
     (1, 1, 1, 1, 32, 32),      # single voxel
 ]
@@ -110,8 +112,10 @@ WGRAD_CASES = [
     (1, 6, 10, 7, 64, 32),
     (1, 8, 8, 8, 256, 256),
     (2, 7, 6, 21, 4, 32),     # layer-1 kernel
-    (2, 7, 6, 9, 16, 32),     # 16 channels: fp32 matrix cores on bf16 data
-    (1, 6, 11, 17, 4, 16),    # 4 -> 16 channels: fp32 matrix cores on bf16 data
+    (2, 7, 6, 9, 16, 32),     # 16 input channels: bf16 kernel on an input padded to 32
+    (1, 5, 6, 18, 8, 64),     # 8 input channels, padded
+    (1, 6, 11, 17, 4, 16),    # 4 -> 16 channels: first-layer kernel, 16 outputs
+    (2, 5, 6, 7, 12, 20),     # 12 -> 20 channels: fp32 matrix cores on bf16 data
     (1, 4, 5, 6, 3, 5),       # direct fallback
     (1, 1, 1, 1, 32, 32),
 ]
