@@ -148,9 +148,10 @@ Fwd dgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 Wg wgrad_path(cf_dtype dt, const cf_dims& x, int cout)
 {
     if (dt == CF_BF16) {
-        if (x.c % 32 == 0 && cout % 32 == 0) return Wg::Mfma;
+        if (x.c % 32 == 0 && cout % 32 == 0 && wgrad_mfma_fits(x, cout)) return Wg::Mfma;
         if (x.c == 4 && (cout == 32 || cout == 16) && wgrad_c4_fits(x)) return Wg::C4;
-        if (cout % 32 == 0 && pad_path_ok(dt, x, cout)) return Wg::MfmaPad;
+        if (cout % 32 == 0 && pad_path_ok(dt, x, cout) && wgrad_mfma_fits(with_c(x, pad32(x.c)), cout))
+            return Wg::MfmaPad;
     }
     if (x.c % 4 == 0 && cout % 4 == 0) return Wg::F32Mfma;
     return Wg::Direct;

@@ -179,6 +179,9 @@ struct WgradPlan {
     size_t part_bytes;
 };
 WgradPlan plan_wgrad(const cf_dims& x, int cout);
+// The general kernel (Cin % 32 == 0) addresses a box's six input planes and
+// four output-gradient planes with 32-bit byte offsets.
+bool wgrad_mfma_fits(const cf_dims& x, int cout);
 // The Cin == 4 kernel addresses each box through 32-bit offsets from the
 // box's first (d) plane; that needs H * W <= 2^23.
 bool wgrad_c4_fits(const cf_dims& x);

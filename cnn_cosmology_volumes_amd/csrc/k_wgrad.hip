@@ -139,11 +139,19 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
     // Staging: full blocks t = tid + k * NT (dY blocks first, then X blocks
     // for halo w 0-15); edge blocks (X, halo w 16-17) for tid < GW_NXE.
     // 16 consecutive lanes store 16 consecutive 16-byte columns of the same
-    // channel rows.
+    // channel rows.  The dY and X block counts are multiples of 64, so a
+    // wave's role (dY, X, edge, none) is uniform and chosen by a scalar
+    // branch.  The loads are raw buffer loads at 32-bit byte offsets from
+    // the box's first plane (the host keeps six planes below 2^31 bytes); a
+    // lane with nothing to fetch (no task, a voxel outside the volume) gets
+    // an offset beyond the resource and reads zeros without a memory access,
+    // so no load sits under a per-lane branch and each address is one add
+    // on a per-row base.
     // The task indices are re-derived from an opaque copy of the thread id
     // in every load and store: kept live across the compute loop they were
     // spilled, and each scratch reload then waited for the whole in-order
     // queue of the next box's prefetch loads.
+    static_assert(G::NDB % 64 == 0, "wave-uniform staging roles");
     uint4 u[G::KB][8];
     uint4 ue[2];
     auto opaque_tid = [&]() {
@@ -151,58 +159,69 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
         asm volatile("" : "+v"(t));
         return t;
     };
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    constexpr uint32_t OOB = 0x80000000u;
+    // offset or OOB, held in a register so the choice stays a select
+    auto pick = [](bool ok, uint32_t off) {
+        uint32_t r = ok ? off : OOB;
+        asm volatile("" : "+v"(r));
+        return r;
+    };
+    const uint32_t ystride = (uint32_t)Cout * 2u, xstride = (uint32_t)Cin * 2u;   // bytes per voxel
 
     auto load_box = [&](const BoxPos& bp) {
-        const int bw = bp.bw, bh = bp.bh, bd = bp.bd, n = bp.n;
-        const int64_t sbase = (int64_t)n * D;
         const int tid_ = opaque_tid();
+        const int gd0 = bp.bd * GW_TD, bh0 = bp.bh * GW_TH, bw0 = bp.bw * GW_TW;
+        // dY planes gd0 .. gd0 + 3; X halo planes gd0 - 1 .. gd0 + 4 from the
+        // first one inside the volume
+        const int xd0 = gd0 > 0 ? gd0 - 1 : 0;
+        const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * Cout + co0, OOB);
+        const auto rx = buf_rsrc(X + ((int64_t)bp.n * D + xd0) * plane * Cin + ci0, OOB);
 #pragma unroll
         for (int k = 0; k < G::KB; ++k) {
             const int t = tid_ + k * G::NT;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) u[k][j] = make_uint4(0u, 0u, 0u, 0u);
-            if (t < G::NDB) {
+            const int t0 = wu * 64 + k * G::NT;                 // the wave's first task
+            if (t0 < G::NDB) {
                 const int oct = t % GW_NOCT, grp = t / GW_NOCT;
                 const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
-                const int gd = bd * GW_TD + td, gh = bh * GW_TH + th;
-                if (gd < D && gh < H) {
-                    const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
+                const int gh = bh0 + th, gwb = bw0 + w0;
+                const bool rok = (gd0 + td < D) & (gh < H);
+                const uint32_t rb = (((uint32_t)td * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * ystride +
+                                    (uint32_t)grp * 16u;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int gw = bw * GW_TW + w0 + j;
-                        if (gw < W) u[k][j] = *reinterpret_cast<const uint4*>(dY + (rowv + gw) * Cout + co0 + grp * 8);
-                    }
-                }
-            } else if (t < G::NB) {
+                for (int j = 0; j < 8; ++j)
+                    u[k][j] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, pick(rok & (gwb + j < W), rb + j * ystride), 0, 0));
+            } else if (t0 < G::NB) {
                 const int x = t - G::NDB;
                 const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
                 const int row = rem / 2, slot = rem % 2;
                 const int hd = row / GW_HH, hh = row % GW_HH;
-                const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
-                if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
-                    const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
+                const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gwb = bw0 + 8 * slot - 1;
+                const bool rok = (t < G::NB) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
+                const uint32_t rb =
+                    (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * xstride +
+                    (uint32_t)grp * 16u;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int gw = bw * GW_TW + 8 * slot + j - 1;
-                        if ((unsigned)gw < (unsigned)W)
-                            u[k][j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + grp * 8);
-                    }
-                }
+                for (int j = 0; j < 8; ++j)
+                    u[k][j] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rx, pick(rok & ((unsigned)(gwb + j) < (unsigned)W), rb + j * xstride), 0, 0));
             }
+            // (a wave past the last task loads nothing; store_box skips it)
         }
-        ue[0] = ue[1] = make_uint4(0u, 0u, 0u, 0u);
-        if (tid_ < GW_NXE) {
+        if (wu * 64 < GW_NXE) {
             const int erow = tid_ % GW_NR, egrp = tid_ / GW_NR;
             const int hd = erow / GW_HH, hh = erow % GW_HH;
-            const int gd = bd * GW_TD + hd - 1, gh = bh * GW_TH + hh - 1;
-            if ((unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H) {
-                const int64_t rowv = (sbase + gd) * plane + (int64_t)gh * W;
+            const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gw = bw0 + 15;   // halo w = 16 + j
+            const bool rok = (tid_ < GW_NXE) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
+            const uint32_t rb =
+                (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) * xstride +
+                (uint32_t)egrp * 16u;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int gw = bw * GW_TW + 15 + j;             // halo w = 16 + j
-                    if (gw < W) ue[j] = *reinterpret_cast<const uint4*>(X + (rowv + gw) * Cin + ci0 + egrp * 8);
-                }
-            }
+            for (int j = 0; j < 2; ++j)
+                ue[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, pick(rok & (gw + j < W), rb + j * xstride), 0, 0));
         }
     };
     auto store_box = [&](int buf) {
@@ -210,10 +229,11 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 #pragma unroll
         for (int k = 0; k < G::KB; ++k) {
             const int t = tid_ + k * G::NT;
-            if (t >= G::NB) continue;
+            const int t0 = wu * 64 + k * G::NT;
+            if (t0 >= G::NB) continue;
             uint4 tr[8];
             transpose8x8(u[k], tr);
-            if (t < G::NDB) {
+            if (t0 < G::NDB) {
                 const int oct = t % GW_NOCT, grp = t / GW_NOCT;
                 // octet slot (w half, box row): the 4 lane groups of a k-step then
                 // read adjacent 16-byte slots, which the LDS serves without conflict
@@ -221,7 +241,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
                     *reinterpret_cast<uint4*>(&dt[buf][(grp * 8 + c) * GW_DROW + slot * 8]) = tr[c];
-            } else {
+            } else if (t < G::NB) {
                 const int x = t - G::NDB;
                 const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
                 const int row = rem / 2, slot = rem % 2;
@@ -230,7 +250,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
                     *reinterpret_cast<uint4*>(&xt[buf][(grp * 8 + c) * GW_XPL + row * GW_XW + slot * 8]) = tr[c];
             }
         }
-        if (tid_ < GW_NXE) {
+        if (wu * 64 < GW_NXE && tid_ < GW_NXE) {
             const int erow = tid_ % GW_NR, egrp = tid_ / GW_NR;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -254,7 +274,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 
     const int64_t b_begin = (int64_t)split * boxes_per_split;
     const int64_t b_end = min(b_begin + boxes_per_split, nbox);
-    BoxPos bp = box_decode(b_begin, bD, bH, bW);
+    BoxPos bp = box_uniform(box_decode(b_begin, bD, bH, bW));
     load_box(bp);
     store_box(0);
     __syncthreads();
@@ -268,7 +288,7 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
         const uint16_t* xpl = xpl0 + sb * (32 * GW_XPL);
         const bool more = box + 1 < b_end;
         if (more) {
-            bp = box_next(bp, bD, bH, bW);
+            bp = box_uniform(box_next(bp, bD, bH, bW));
             load_box(bp);                      // in flight during this box's MFMAs
         }
 #pragma unroll 1
@@ -390,6 +410,12 @@ void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW,
 }
 
 }  // namespace
+
+bool wgrad_mfma_fits(const cf_dims& x, int cout)
+{
+    const int64_t c = x.c > cout ? x.c : cout;
+    return 6 * x.h * x.w * c * 2 + 64 < ((int64_t)1 << 31);
+}
 
 bool wgrad_c4_fits(const cf_dims& x)
 {

@@ -86,6 +86,16 @@ def test_conv_workspace_sizes():
         27 * 64 * 64 * 4
     assert cf.cf_conv3d_workspace_size(cf.CF_BF16, (1, 8, 1024, 1024, 32), 64, cf.CF_CONV_BWD_DATA) == \
         27 * 128 * 64 * 2
+    # backward-weight addresses a box's six input planes (and four planes of
+    # the output gradient) with 32-bit byte offsets too: beyond that it takes
+    # the fp32 matrix-core kernel, whose partials a fp32 layer of the same
+    # shape uses as well
+    big = (1, 8, 2048, 2048, 32)
+    assert cf.cf_conv3d_workspace_size(cf.CF_BF16, big, 64, cf.CF_CONV_BWD_WEIGHT) == \
+        cf.cf_conv3d_workspace_size(cf.CF_F32, big, 64, cf.CF_CONV_BWD_WEIGHT)
+    ok = (1, 8, 1024, 1024, 32)
+    ws = cf.cf_conv3d_workspace_size(cf.CF_BF16, ok, 64, cf.CF_CONV_BWD_WEIGHT)
+    assert ws % (27 * 32 * 64 * 4) == 0 and ws != cf.cf_conv3d_workspace_size(cf.CF_F32, ok, 64, cf.CF_CONV_BWD_WEIGHT)
     # bf16 layers with input channels a multiple of 8 but not of 32 (the
     # 16-channel layer of the Table I network) run the bf16 kernels on a copy
     # of the input padded to 32 channels: padded weights, the padded copy
