@@ -10,11 +10,8 @@
 namespace cf {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;   // bfloat16 storage word
-
-#define CF_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

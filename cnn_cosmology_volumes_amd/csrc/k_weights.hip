@@ -19,19 +19,11 @@ __device__ __forceinline__ float wload(const void* W, bool f32, int64_t i) {
     return f32 ? reinterpret_cast<const float*>(W)[i] : bf2f(reinterpret_cast<const uint16_t*>(W)[i]);
 }
 
-// Element e of each layout (the single-layout kernels and the batched one
-// share these, so their results are identical).
-// fwd:   Wk[t][co][ci], co < copad (zero rows beyond cout).
+// Element e of the dgrad and c4 layouts (their element-wise paths in the
+// batched kernel below).  The fwd layout, Wk[t][co][ci] with zero rows for
+// co >= cout, goes through that kernel's transposing tiles.
 // Element indices stay far below 2^31 (27 taps x padded channels), so the
 // index arithmetic is 32-bit.
-__device__ __forceinline__ uint16_t wk_fwd_elem(const void* W, bool f32, int cin, int cout, int copad, int64_t e64)
-{
-    const uint32_t e = (uint32_t)e64;
-    const int ci = (int)(e % (uint32_t)cin);
-    const int co = (int)((e / (uint32_t)cin) % (uint32_t)copad);
-    const int t = (int)(e / ((uint32_t)cin * (uint32_t)copad));
-    return co < cout ? f2bf(wload(W, f32, ((int64_t)t * cin + ci) * cout + co)) : (uint16_t)0;
-}
 // dgrad: Wk[t'][ci][co] = W[26 - t'][ci][co], ci < cipad (zero rows beyond cin).
 __device__ __forceinline__ uint16_t wk_dgrad_elem(const void* W, bool f32, int cin, int cout, int cipad, int64_t e64)
 {
@@ -53,13 +45,6 @@ __device__ __forceinline__ uint16_t wk_c4_elem(const void* W, bool f32, int cout
 }
 
 
-__global__ void wprep_fwd_kernel(const void* W, bool f32, int cin, int cout, int copad, uint16_t* Wk)
-{
-    const int64_t total = (int64_t)27 * copad * cin;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
-        Wk[e] = wk_fwd_elem(W, f32, cin, cout, copad, e);
-}
-
 // fwd with the input channels padded to cinp (zero columns for ci >= cin):
 // Wk[t][co][ci], ci < cinp.
 __global__ void wprep_fwd_pad_kernel(const void* W, bool f32, int cin, int cinp, int cout, int copad, uint16_t* Wk)
@@ -72,20 +57,6 @@ __global__ void wprep_fwd_pad_kernel(const void* W, bool f32, int cin, int cinp,
         const int t = (int)(u / ((uint32_t)cinp * (uint32_t)copad));
         Wk[e] = (ci < cin && co < cout) ? f2bf(wload(W, f32, ((int64_t)t * cin + ci) * cout + co)) : (uint16_t)0;
     }
-}
-
-__global__ void wprep_dgrad_kernel(const void* W, bool f32, int cin, int cout, int cipad, uint16_t* Wk)
-{
-    const int64_t total = (int64_t)27 * cipad * cout;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
-        Wk[e] = wk_dgrad_elem(W, f32, cin, cout, cipad, e);
-}
-
-__global__ void wprep_c4_kernel(const void* W, bool f32, int cout, int copad, uint16_t* Wk)
-{
-    const int64_t total = (int64_t)copad * 128;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x)
-        Wk[e] = wk_c4_elem(W, f32, cout, e);
 }
 
 // Several re-layouts in one launch: blockIdx.y picks the job.  The fwd
@@ -200,11 +171,20 @@ unsigned blocks_for(int64_t n) {
 
 }  // namespace
 
+// The single re-layouts are one-job launches of the batched kernel (its
+// transposing and 16-byte paths; the values are the same roundings).
+static hipError_t launch_wprep_one(int kind, const void* W, bool w_is_f32, int cin, int cout, int pad, uint16_t* Wk,
+                            hipStream_t s)
+{
+    WprepList l{};
+    l.count = 1;
+    l.job[0] = WprepJob{kind, w_is_f32, cin, cout, pad, W, Wk};
+    return launch_wprep_multi(l, s);
+}
+
 hipError_t launch_wprep_fwd(const void* W, bool w_is_f32, int cin, int cout, int copad, uint16_t* Wk, hipStream_t s)
 {
-    hipLaunchKernelGGL(wprep_fwd_kernel, dim3(blocks_for((int64_t)27 * copad * cin)), dim3(256), 0, s, W, w_is_f32,
-                       cin, cout, copad, Wk);
-    return hipGetLastError();
+    return launch_wprep_one(0, W, w_is_f32, cin, cout, copad, Wk, s);
 }
 
 hipError_t launch_wprep_fwd_pad(const void* W, bool w_is_f32, int cin, int cinp, int cout, int copad, uint16_t* Wk,
@@ -217,16 +197,12 @@ hipError_t launch_wprep_fwd_pad(const void* W, bool w_is_f32, int cin, int cinp,
 
 hipError_t launch_wprep_dgrad(const void* W, bool w_is_f32, int cin, int cout, int cipad, uint16_t* Wk, hipStream_t s)
 {
-    hipLaunchKernelGGL(wprep_dgrad_kernel, dim3(blocks_for((int64_t)27 * cipad * cout)), dim3(256), 0, s, W, w_is_f32,
-                       cin, cout, cipad, Wk);
-    return hipGetLastError();
+    return launch_wprep_one(1, W, w_is_f32, cin, cout, cipad, Wk, s);
 }
 
 hipError_t launch_wprep_c4(const void* W, bool w_is_f32, int cout, int copad, uint16_t* Wk, hipStream_t s)
 {
-    hipLaunchKernelGGL(wprep_c4_kernel, dim3(blocks_for((int64_t)copad * 128)), dim3(256), 0, s, W, w_is_f32, cout,
-                       copad, Wk);
-    return hipGetLastError();
+    return launch_wprep_one(2, W, w_is_f32, 4, cout, copad, Wk, s);
 }
 
 hipError_t launch_wprep_multi(const WprepList& l_in, hipStream_t s)

@@ -6,12 +6,9 @@
 // convolution itself is the "same"-padded stride-1 one of Oyama et al.,
 // Sec. IV / Table I).  This is a GEMM whose reduction runs over voxels, while
 // NDHWC stores channels contiguously: every MFMA operand needs 8 consecutive
-// voxels of one channel per lane.  gfx950's LDS transpose read
-// (ds_read_b64_tr_b16) provides exactly that from the natural [voxel][channel]
-// tiles: within each 16-lane group, lane 4r+q names row r (a voxel) and
-// columns 4q..4q+3 (channels); lane j receives column j of the 4 rows.  A tap
-// shift only changes which halo row a lane names, so the X halo is staged
-// once per voxel box and reused by all 27 taps.
+// voxels of one channel per lane, so the staging transposes the voxel box
+// into channel-major LDS tiles (below).  The X halo is staged once per voxel
+// box and reused by all 27 taps.
 //
 // Orientation: C[co][ci] += dY^T[co][k] * Xshift[k][ci] (16x16x32 MFMA), so
 // a lane's accumulator holds 4 consecutive co of one ci -> one 16-byte store
@@ -26,16 +23,6 @@
 namespace cf {
 
 namespace {
-
-__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((CF_LDS s16x4*)(p));
-}
-
-__device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
 
 // ---------------------------------------------------------------- general
 // MFMA operands need 8 consecutive voxels of one channel per lane.  While a
