@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs on one sample (median reported)")
     ap.add_argument("--no-ops", action="store_true", help="skip the per-entry-point timing")
     ap.add_argument("--no-fp32", action="store_true", help="skip the fp32-path step timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--mfma-peak", action="store_true", help="only measure the matrix cores' sustained rate")
     ap.add_argument("--profile-op", default=None,
                     help="only run the named entry point of the per-entry-point timing --op-reps times "
@@ -305,7 +306,7 @@ def device_params(torch, dev, conv, dense):
     return ps
 
 
-def train_step_line(a, torch, cf, sd, c, dev, dtype_name):
+def train_step_line(a, torch, cf, sd, c, dev, dtype_name, graph=False):
     """Time cf_train_step on the 128^3 (or 512^3) network; returns the dict
     of step timings (samples/s from the median step)."""
     from cnn_cosmology_volumes_amd.configs import train_step_conv_flops
@@ -347,6 +348,21 @@ def train_step_line(a, torch, cf, sd, c, dev, dtype_name):
     flops = train_step_conv_flops(c.network(), c.batch)
     res = {"ms_median": med, "ms_mean": mean, "wall_s": wall, "loss_first": first[0], "loss_last": float(loss.item()),
            "conv_flops": flops, "per_step_ms": [round(v, 4) for v in per]}
+    if graph:
+        # the same step captured once into a HIP graph (one warm-up step on
+        # the capture stream first), then timed over as many replays
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cf.cf_train_step(m, xd, td, params, c.lr, ws=ws, loss=loss, aux=aux)
+        gmed, gmean, _, _ = timed_steps(torch, g.replay, a.steps, 2, stream)
+        res["graph_ms_median"], res["graph_ms_mean"] = gmed, gmean
+        del g
     aux.close()
     del ws, params, xd
     torch.cuda.empty_cache()
@@ -511,7 +527,7 @@ def main():
         print(json.dumps(other_workload(a, torch, cf, sd, dev)), flush=True)
         return
 
-    r, host = train_step_line(a, torch, cf, sd, c, dev, "bf16")
+    r, host = train_step_line(a, torch, cf, sd, c, dev, "bf16", graph=not a.no_graph)
     ms = r["ms_median"]
     value = c.batch / (ms / 1000.0)
     out = {
@@ -527,6 +543,12 @@ def main():
         "loss_first": r["loss_first"],
         "loss_last": r["loss_last"],
     }
+    if "graph_ms_median" in r:
+        gms = r["graph_ms_median"]
+        out["graph_step"] = {"ms": round(gms, 4), "ms_mean": round(r["graph_ms_mean"], 4),
+                             "samples_per_s": round(c.batch / (gms / 1e3), 2), "steps": a.steps,
+                             "note": "the same step captured once into a HIP graph and replayed; median of the "
+                                     "replays (value is the eager call)"}
     if not a.no_ops:
         ops = op_timings(torch, cf, c, dev, a.op_reps)
         conv_ms = sum(o["ms"] for o in ops if o["kind"] == "conv")
