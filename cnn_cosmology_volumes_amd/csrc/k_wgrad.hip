@@ -351,6 +351,263 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 }
 
 
+// Wave-specialized form of the 64-output-channel kernel.  Waves 0-11 compute
+// exactly as wgrad_mfma_kernel<64> does; waves 12-15 hold no accumulators
+// and only stage: while the compute waves walk box k from one LDS buffer,
+// they load box k + 1 from global memory, transpose it and store it into the
+// other buffer.  One barrier per box for all 16 waves, as before, but the
+// staging's loads, permutes and stores now run beside the MFMA work instead
+// of between boxes.  A staging thread p (0-255) owns dY block p, X block p
+// and either X block 256 + p (p < 32) or edge block p - 32 (p < 176): three
+// sets of eight 16-byte loads, all issued before the first store.
+constexpr int WS_NCW = 12, WS_NPW = 4, WS_NT = (WS_NCW + WS_NPW) * 64, WS_NPT = WS_NPW * 64;
+static_assert(GwCfg<64>::NW == WS_NCW && GwCfg<64>::NDB == WS_NPT && GW_NXB - WS_NPT == 32 &&
+                  32 + GW_NXE <= WS_NPT, "staging task layout");
+
+// Transposes 8 voxels x 8 channels (in[v] = channels of voxel v) and stores
+// channel row c (8 voxels) at dst + c * stride, one row at a time, so only
+// four registers of transposed data are live at once.
+__device__ __forceinline__ void transpose_store8x8(const uint4 (&in)[8], uint16_t* dst, int stride)
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4& lo = in[2 * k];
+            const uint4& hi = in[2 * k + 1];
+            const uint32_t wl = (c >> 1) == 0 ? lo.x : (c >> 1) == 1 ? lo.y : (c >> 1) == 2 ? lo.z : lo.w;
+            const uint32_t wh = (c >> 1) == 0 ? hi.x : (c >> 1) == 1 ? hi.y : (c >> 1) == 2 ? hi.z : hi.w;
+            d[k] = __builtin_amdgcn_perm(wh, wl, sel);
+        }
+        *reinterpret_cast<uint4*>(dst + c * stride) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+
+__global__ __launch_bounds__(WS_NT)
+void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, float* __restrict__ part,
+                     int N, int D, int H, int W, int Cin, int Cout, int bD, int bH, int bW, int nco, int nci,
+                     int64_t nbox, int boxes_per_split)
+{
+    constexpr int BO = 64;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * GW_XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * GW_DROW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int l16 = lane & 15, lg = lane >> 4;
+    uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const int cob = (int)(id % (uint32_t)nco); id /= (uint32_t)nco;
+    const int cib = (int)(id % (uint32_t)nci);
+    const int split = (int)(id / (uint32_t)nci);
+    const int co0 = cob * BO, ci0 = cib * 32;
+    const int64_t plane = (int64_t)H * W;
+    const int64_t b_begin = (int64_t)split * boxes_per_split;
+    const int64_t b_end = min(b_begin + boxes_per_split, nbox);
+
+    // ------------------------------------------------------------ staging
+    constexpr uint32_t OOB = 0x80000000u;
+    auto pick = [](bool ok, uint32_t off) {
+        uint32_t r = ok ? off : OOB;
+        asm volatile("" : "+v"(r));
+        return r;
+    };
+    const uint32_t ystride = (uint32_t)Cout * 2u, xstride = (uint32_t)Cin * 2u;
+    auto stage = [&](const BoxPos& bp, int buf) {
+        int p = tid - WS_NCW * 64;
+        asm volatile("" : "+v"(p));
+        const int gd0 = bp.bd * GW_TD, bh0 = bp.bh * GW_TH, bw0 = bp.bw * GW_TW;
+        const int xd0 = gd0 > 0 ? gd0 - 1 : 0;
+        const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * Cout + co0, OOB);
+        const auto rx = buf_rsrc(X + ((int64_t)bp.n * D + xd0) * plane * Cin + ci0, OOB);
+        uint4 ua[8], ub[8], uc[8];
+        // A: dY block p (octet, 8-channel group)
+        {
+            const int oct = p % GW_NOCT, grp = p / GW_NOCT;
+            const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
+            const int gh = bh0 + th, gwb = bw0 + w0;
+            const bool rok = (gd0 + td < D) & (gh < H);
+            const uint32_t rb =
+                (((uint32_t)td * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * ystride + (uint32_t)grp * 16u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ua[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, pick(rok & (gwb + j < W), rb + j * ystride), 0, 0));
+        }
+        // B and C: X blocks x (halo row, w half, 8-channel group), or C an edge block
+        auto xload = [&](int x, uint4 (&u)[8]) {
+            const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
+            const int row = rem / 2, slot = rem % 2;
+            const int hd = row / GW_HH, hh = row % GW_HH;
+            const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gwb = bw0 + 8 * slot - 1;
+            const bool rok = (x < GW_NXB) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
+            const uint32_t rb =
+                (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * xstride +
+                (uint32_t)grp * 16u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                u[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rx, pick(rok & ((unsigned)(gwb + j) < (unsigned)W), rb + j * xstride),
+                                                     0, 0));
+        };
+        xload(p, ub);
+        const bool c_edge = p >= 32;
+        const int e = p - 32;                                  // edge block (when c_edge and e < GW_NXE)
+        if (wu == WS_NCW) {
+            // wave 12: lanes 0-31 take X block 256 + p, lanes 32-63 edge blocks 0-31
+            if (!c_edge) {
+                xload(WS_NPT + p, uc);
+            }
+        }
+        if (c_edge) {
+            const int erow = e % GW_NR, egrp = e / GW_NR;
+            const int hd = erow / GW_HH, hh = erow % GW_HH;
+            const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gw = bw0 + 15;   // halo w = 16 + j
+            const bool rok = (e < GW_NXE) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
+            const uint32_t rb =
+                (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) * xstride +
+                (uint32_t)egrp * 16u;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                uc[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, pick(rok & (gw + j < W), rb + j * xstride), 0, 0));
+        }
+        // stores: dY block p, X block p, then block C
+        {
+            const int oct = p % GW_NOCT, grp = p / GW_NOCT;
+            const int slot = (oct & 1) * (GW_NOCT / 2) + (oct >> 1);
+            transpose_store8x8(ua, &dt[buf][(grp * 8) * GW_DROW + slot * 8], GW_DROW);
+        }
+        auto xstore = [&](int x, const uint4 (&u)[8]) {
+            const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
+            const int row = rem / 2, slot = rem % 2;
+            transpose_store8x8(u, &xt[buf][(grp * 8) * GW_XPL + row * GW_XW + slot * 8], GW_XPL);
+        };
+        xstore(p, ub);
+        if (!c_edge) {
+            xstore(WS_NPT + p, uc);
+        } else if (e < GW_NXE) {
+            const int erow = e % GW_NR, egrp = e / GW_NR;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                const int h = c >> 1;
+                const uint32_t w0v = h == 0 ? uc[0].x : h == 1 ? uc[0].y : h == 2 ? uc[0].z : uc[0].w;
+                const uint32_t w1v = h == 0 ? uc[1].x : h == 1 ? uc[1].y : h == 2 ? uc[1].z : uc[1].w;
+                *reinterpret_cast<uint32_t*>(&xt[buf][(egrp * 8 + c) * GW_XPL + GW_XE + 2 * erow]) =
+                    __builtin_amdgcn_perm(w1v, w0v, sel);
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ compute
+    const int kd = wave % 3, jf = (wave / 3) % 2, cp = wave / 6;    // meaningful for waves 0-11
+    f32x4 acc[2][3][3];      // [co fragment][kh][kw]
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) acc[c][kh][kw] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* drow0 = dt[0] + (32 * cp + l16) * GW_DROW;
+    const uint16_t* xpl0 = xt[0] + (16 * jf + l16) * GW_XPL + kd * GW_HH * GW_XW;
+    auto compute = [&](int buf) {
+        const uint16_t* drow = drow0 + buf * (BO * GW_DROW);
+        const uint16_t* xpl = xpl0 + buf * (32 * GW_XPL);
+#pragma unroll 1
+        for (int s2 = 0; s2 < GW_TD; ++s2) {
+            const int row = s2 * GW_TH + lg;
+            bf16x8 a[2][2];                                 // [co fragment][octet]
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (h * (GW_NOCT / 2) + row) * 8);
+            const uint16_t* xr = xpl + (s2 * GW_HH + lg) * GW_XW;
+            const uint32_t* er = reinterpret_cast<const uint32_t*>(xpl - kd * GW_HH * GW_XW + GW_XE) +
+                                 (kd + s2) * GW_HH + lg;
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+                const uint16_t* xp = xr + kh * GW_XW;
+                uint4 q0 = *reinterpret_cast<const uint4*>(xp);
+                uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
+                uint32_t e1 = er[kh];
+                asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(q1.x), "+v"(q1.y),
+                             "+v"(q1.z), "+v"(q1.w), "+v"(e1));
+                const uint32_t e0 = q1.x;
+                bf16x8 b[2][3];
+                b[0][0] = __builtin_bit_cast(bf16x8, q0);
+                b[0][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q0.y, q0.x, 16),
+                                                                __builtin_amdgcn_alignbit(q0.z, q0.y, 16),
+                                                                __builtin_amdgcn_alignbit(q0.w, q0.z, 16),
+                                                                __builtin_amdgcn_alignbit(e0, q0.w, 16)));
+                b[0][2] = __builtin_bit_cast(bf16x8, make_uint4(q0.y, q0.z, q0.w, e0));
+                b[1][0] = __builtin_bit_cast(bf16x8, q1);
+                b[1][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q1.y, q1.x, 16),
+                                                                __builtin_amdgcn_alignbit(q1.z, q1.y, 16),
+                                                                __builtin_amdgcn_alignbit(q1.w, q1.z, 16),
+                                                                __builtin_amdgcn_alignbit(e1, q1.w, 16)));
+                b[1][2] = __builtin_bit_cast(bf16x8, make_uint4(q1.y, q1.z, q1.w, e1));
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[h][kw], acc[c][kh][kw], 0, 0, 0);
+            }
+        }
+    };
+
+    // Box b_begin is staged before the loop; in the iteration of box k the
+    // compute waves read buffer (k - b_begin) & 1 while the staging waves
+    // fill the other with box k + 1 (last read in the iteration before,
+    // behind the barrier that ended it).  The two roles run separate loops
+    // (the accumulators are live only in the compute waves' loop), and each
+    // passes one barrier before its loop and one per box: the same count,
+    // which is what the workgroup barrier needs.
+    if (wu >= WS_NCW) {
+        BoxPos bp = box_uniform(box_decode(b_begin, bD, bH, bW));
+        stage(bp, 0);
+        __syncthreads();
+        int buf = 0;
+        for (int64_t box = b_begin; box < b_end; ++box) {
+            if (box + 1 < b_end) {
+                bp = box_uniform(box_next(bp, bD, bH, bW));
+                stage(bp, buf ^ 1);
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+        return;
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int64_t box = b_begin; box < b_end; ++box) {
+        compute(__builtin_amdgcn_readfirstlane(buf));
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // partial[split][tap][ci][co]; lane holds co rows 4 lg..4 lg+3 of column ci
+    const int64_t dwsize = (int64_t)27 * Cin * Cout;
+    const int ci = ci0 + 16 * jf + l16;
+    float* out = part + split * dwsize + (int64_t)ci * Cout + co0 + 32 * cp + 4 * lg;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const int tap = (kd * 3 + kh) * 3 + kw;
+                const f32x4 r = acc[c][kh][kw];
+                *reinterpret_cast<float4*>(out + (int64_t)tap * Cin * Cout + 16 * c) = make_float4(r[0], r[1], r[2], r[3]);
+            }
+}
+
+
 // dW[e] = sum over splits of part[s][e].  A block owns RD_E consecutive
 // elements (4 per thread, 16-byte loads; small blocks, so even a few
 // thousand elements spread over all CUs); its 16 split-lanes each sum the
@@ -457,9 +714,9 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
         const int nci = (int)(x.c / 32);
         if (cout % 64 == 0) {
             const int nco = cout / 64;
-            hipLaunchKernelGGL(wgrad_mfma_kernel<64>, dim3((unsigned)((int64_t)nco * nci * p.splits)),
-                               dim3(GwCfg<64>::NT), 0, s, X, dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w,
-                               (int)x.c, cout, bD, bH, bW, nco, nci, nbox, (int)p.vox_per_split);
+            hipLaunchKernelGGL(wgrad_ws_kernel, dim3((unsigned)((int64_t)nco * nci * p.splits)), dim3(WS_NT), 0, s, X,
+                               dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nco, nci,
+                               nbox, (int)p.vox_per_split);
         } else {
             const int nco = cout / 32;
             hipLaunchKernelGGL(wgrad_mfma_kernel<32>, dim3((unsigned)((int64_t)nco * nci * p.splits)),
