@@ -36,12 +36,10 @@ COMMON = [
 
 
 # Per-file code generation options, chosen by measurement (A/B of whole
-# library builds on the GPU): LLVM's ILP-oriented machine schedulers make the
-# pool kernels and the 4-channel backward-weight faster and other kernels
-# slower, so they are applied per file.
+# library builds on the GPU): LLVM's max-ILP machine scheduler makes the pool
+# kernels faster and other kernels slower, so it is applied per file.
 PER_FILE = {
     "k_pool.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-    "k_wgrad_c4.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
