@@ -129,27 +129,42 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
         for (int j = 0; j < T::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int64_t plane = (int64_t)H * W;
+    // Halo loads: raw buffer loads at 32-bit byte offsets from the tile's
+    // first in-volume depth plane (the host keeps six planes below 2^31
+    // bytes), computed once for all channel chunks; a piece outside the
+    // volume gets an offset beyond the buffer and reads zeros, so no load
+    // sits under a branch.
+    constexpr uint32_t OOB = 0x80000000u;
+    const int dlo = d0 > 0 ? d0 - 1 : 0;
+    const int dhi = min(d0 + TD + 1, D);
+    const uint16_t* xbase = X + ((int64_t)n * D + dlo) * plane * Cin;
+    const uint32_t xbytes = (uint32_t)((int64_t)(dhi - dlo) * plane * Cin * 2);
+    uint32_t hoff[T::IT];
+#pragma unroll
+    for (int it = 0; it < T::IT; ++it) {
+        const int e = threadIdx.x + it * T::NT;
+        const int q = e & 3, hv = e >> 2;
+        const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
+        const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
+        const bool ok = (T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
+                        (unsigned)gw < (unsigned)W;
+        uint32_t r = ok ? (((uint32_t)(gd - dlo) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) *
+                              (uint32_t)(Cin * 2) + (uint32_t)q * 16u
+                        : OOB;
+        asm volatile("" : "+v"(r));     // a select, not a branch around the load
+        hoff[it] = r;
+    }
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
         // Stage the input halo of this 32-channel chunk (zero outside the
         // volume).  All of a thread's global loads are issued before any of
         // its LDS stores, so their latencies overlap instead of adding up.
         {
-            const uint16_t* xs = X + (int64_t)n * D * plane * Cin + c * 32;
+            const auto rx = buf_rsrc(xbase + c * 32, xbytes - (uint32_t)c * 64u);
             uint4 val[T::IT];
 #pragma unroll
-            for (int it = 0; it < T::IT; ++it) {
-                const int e = threadIdx.x + it * T::NT;
-                const int q = e & 3, hv = e >> 2;
-                const int hw_ = hv % T::HW, hh_ = (hv / T::HW) % T::HH, hd_ = hv / (T::HW * T::HH);
-                const int gd = d0 + hd_ - 1, gh = h0 + hh_ - 1, gw = w0 + hw_ - 1;
-                val[it] = make_uint4(0u, 0u, 0u, 0u);
-                if ((T::NE % T::NT == 0 || e < T::NE) && (unsigned)gd < (unsigned)D && (unsigned)gh < (unsigned)H &&
-                    (unsigned)gw < (unsigned)W) {
-                    const int64_t vox = (int64_t)(gd * H + gh) * W + gw;
-                    val[it] = *reinterpret_cast<const uint4*>(xs + vox * Cin + q * 8);
-                }
-            }
+            for (int it = 0; it < T::IT; ++it)
+                val[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, hoff[it], 0, 0));
 #pragma unroll
             for (int it = 0; it < T::IT; ++it) {
                 const int e = threadIdx.x + it * T::NT;
