@@ -415,64 +415,85 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         return r;
     };
     const uint32_t ystride = (uint32_t)Cout * 2u, xstride = (uint32_t)Cin * 2u;
-    auto stage = [&](const BoxPos& bp, int buf) {
+    // Staging-thread constants (box-independent parts of the offsets), set
+    // once before the box loop.  A box adds one scalar per tensor and voxel
+    // j of a task j * voxel bytes, so a load costs an add, a compare and a
+    // select.  (The same j * voxel bytes passed as the instruction's scalar
+    // offset instead gave wrong staged values in testing, so the whole
+    // offset stays in the per-lane operand.)
+    // A: dY block p (octet, 8-channel group): byte offset from the box's
+    // first plane kA + (bh0 * W + bw0) * ystride + j * ystride.
+    // B: X block p; C: X block 256 + p (p < 32) or edge block p - 32: byte
+    // offset from the halo's first in-volume plane
+    // kX + ((e0 * H + bh0) * W + bw0) * xstride + j * xstride, with e0 = 1
+    // unless the box starts at depth 0; kX may be negative, the sum is not
+    // for a voxel inside the volume.
+    struct XTask { int hd, hh, wb; int32_t k; bool live; };
+    auto xtask = [&](int x) {
+        const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
+        const int row = rem / 2, slot = rem % 2;
+        XTask t;
+        t.hd = row / GW_HH; t.hh = row % GW_HH; t.wb = 8 * slot - 1;
+        t.k = (((t.hd - 1) * H + (t.hh - 1)) * W + t.wb) * (int32_t)xstride + grp * 16;
+        t.live = x < GW_NXB;
+        return t;
+    };
+    auto etask = [&](int e) {
+        const int erow = e % GW_NR, egrp = e / GW_NR;
+        XTask t;
+        t.hd = erow / GW_HH; t.hh = erow % GW_HH; t.wb = 15;      // halo w = 16 + j
+        t.k = (((t.hd - 1) * H + (t.hh - 1)) * W + t.wb) * (int32_t)xstride + egrp * 16;
+        t.live = e < GW_NXE;
+        return t;
+    };
+    // voxel j of a row that starts at w = base (>= -1) is inside 0 <= w < W
+    auto wok = [&](int base, int j) { return j == 0 ? (unsigned)base < (unsigned)W : base < W - j; };
+    struct STasks { int32_t kA; int tdA, thA, w0A; XTask tB, tC; };
+    auto stage_tasks = [&](int p) {
+        STasks T;
+        const int oct = p % GW_NOCT, grp = p / GW_NOCT;
+        T.tdA = oct / (GW_TH * 2); T.thA = (oct / 2) % GW_TH; T.w0A = (oct & 1) * 8;
+        T.kA = ((T.tdA * H + T.thA) * W + T.w0A) * (int32_t)ystride + grp * 16;
+        T.tB = xtask(p);
+        T.tC = p < 32 ? xtask(WS_NPT + p) : etask(p - 32);
+        return T;
+    };
+    auto stage = [&](const BoxPos& bp, int buf, const STasks& T) {
         int p = tid - WS_NCW * 64;
         asm volatile("" : "+v"(p));
         const int gd0 = bp.bd * GW_TD, bh0 = bp.bh * GW_TH, bw0 = bp.bw * GW_TW;
         const int xd0 = gd0 > 0 ? gd0 - 1 : 0;
         const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * Cout + co0, OOB);
         const auto rx = buf_rsrc(X + ((int64_t)bp.n * D + xd0) * plane * Cin + ci0, OOB);
+        const int32_t sA = (bh0 * W + bw0) * (int32_t)ystride;
+        const int32_t sX = (((gd0 > 0 ? 1 : 0) * H + bh0) * W + bw0) * (int32_t)xstride;
         uint4 ua[8], ub[8], uc[8];
-        // A: dY block p (octet, 8-channel group)
         {
-            const int oct = p % GW_NOCT, grp = p / GW_NOCT;
-            const int td = oct / (GW_TH * 2), th = (oct / 2) % GW_TH, w0 = (oct & 1) * 8;
-            const int gh = bh0 + th, gwb = bw0 + w0;
-            const bool rok = (gd0 + td < D) & (gh < H);
-            const uint32_t rb =
-                (((uint32_t)td * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * ystride + (uint32_t)grp * 16u;
+            const bool rok = (gd0 + T.tdA < D) & (bh0 + T.thA < H);
+            const uint32_t off = (uint32_t)(T.kA + sA);
+            const int base = bw0 + T.w0A;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                ua[j] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, pick(rok & (gwb + j < W), rb + j * ystride), 0, 0));
+                ua[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rd, pick(rok & wok(base, j), off + j * ystride), 0, 0));
         }
-        // B and C: X blocks x (halo row, w half, 8-channel group), or C an edge block
-        auto xload = [&](int x, uint4 (&u)[8]) {
-            const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
-            const int row = rem / 2, slot = rem % 2;
-            const int hd = row / GW_HH, hh = row % GW_HH;
-            const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gwb = bw0 + 8 * slot - 1;
-            const bool rok = (x < GW_NXB) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
-            const uint32_t rb =
-                (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gwb) * xstride +
-                (uint32_t)grp * 16u;
+        auto xload = [&](const XTask& t, uint4 (&u)[8], int n) {
+            const bool rok = t.live & ((unsigned)(gd0 + t.hd - 1) < (unsigned)D) & ((unsigned)(bh0 + t.hh - 1) < (unsigned)H);
+            const uint32_t off = (uint32_t)(t.k + sX);
+            const int base = bw0 + t.wb;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                u[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rx, pick(rok & ((unsigned)(gwb + j) < (unsigned)W), rb + j * xstride),
-                                                     0, 0));
+                if (j < n)
+                    u[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rx, pick(rok & wok(base, j), off + j * xstride), 0, 0));
         };
-        xload(p, ub);
+        xload(T.tB, ub, 8);
         const bool c_edge = p >= 32;
-        const int e = p - 32;                                  // edge block (when c_edge and e < GW_NXE)
-        if (wu == WS_NCW) {
-            // wave 12: lanes 0-31 take X block 256 + p, lanes 32-63 edge blocks 0-31
-            if (!c_edge) {
-                xload(WS_NPT + p, uc);
-            }
-        }
-        if (c_edge) {
-            const int erow = e % GW_NR, egrp = e / GW_NR;
-            const int hd = erow / GW_HH, hh = erow % GW_HH;
-            const int gd = gd0 + hd - 1, gh = bh0 + hh - 1, gw = bw0 + 15;   // halo w = 16 + j
-            const bool rok = (e < GW_NXE) & ((unsigned)gd < (unsigned)D) & ((unsigned)gh < (unsigned)H);
-            const uint32_t rb =
-                (((uint32_t)(gd - xd0) * (uint32_t)H + (uint32_t)gh) * (uint32_t)W + (uint32_t)gw) * xstride +
-                (uint32_t)egrp * 16u;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                uc[j] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, pick(rok & (gw + j < W), rb + j * xstride), 0, 0));
+        const int e = p - 32;
+        if (!c_edge) {
+            xload(T.tC, uc, 8);
+        } else {
+            xload(T.tC, uc, 2);
         }
         // stores: dY block p, X block p, then block C
         {
@@ -569,14 +590,15 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     // passes one barrier before its loop and one per box: the same count,
     // which is what the workgroup barrier needs.
     if (wu >= WS_NCW) {
+        const STasks T = stage_tasks(tid - WS_NCW * 64);
         BoxPos bp = box_uniform(box_decode(b_begin, bD, bH, bW));
-        stage(bp, 0);
+        stage(bp, 0, T);
         __syncthreads();
         int buf = 0;
         for (int64_t box = b_begin; box < b_end; ++box) {
             if (box + 1 < b_end) {
                 bp = box_uniform(box_next(bp, bD, bH, bW));
-                stage(bp, buf ^ 1);
+                stage(bp, buf ^ 1, T);
             }
             __syncthreads();
             buf ^= 1;
