@@ -357,12 +357,38 @@ void wgrad_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 // they load box k + 1 from global memory, transpose it and store it into the
 // other buffer.  One barrier per box for all 16 waves, as before, but the
 // staging's loads, permutes and stores now run beside the MFMA work instead
-// of between boxes.  A staging thread p (0-255) owns dY block p, X block p
-// and either X block 256 + p (p < 32) or edge block p - 32 (p < 176): three
-// sets of eight 16-byte loads, all issued before the first store.
+// of between boxes.
+//
+// Two box shapes of 256 voxels: 4 x 4 x 16 (TW = 16), and 4 x 8 x 8 for
+// volumes at most 8 voxels wide (TW = 8), where half of a 16-wide box would
+// lie outside the volume and its matrix work would be spent on zeros.  With
+// TW = 16 a staging thread p (0-255) owns dY block p, X block p and either
+// X block 256 + p (p < 32) or edge block p - 32 (p < 176): three sets of
+// eight 16-byte loads, all issued before the first store.  With TW = 8 a
+// halo row holds one 8-voxel block and one edge pair, and thread p owns dY
+// block p, X block p and edge block p (p < 240).
 constexpr int WS_NCW = 12, WS_NPW = 4, WS_NT = (WS_NCW + WS_NPW) * 64, WS_NPT = WS_NPW * 64;
-static_assert(GwCfg<64>::NW == WS_NCW && GwCfg<64>::NDB == WS_NPT && GW_NXB - WS_NPT == 32 &&
-                  32 + GW_NXE <= WS_NPT, "staging task layout");
+
+template <int TW_>
+struct WsGeom {
+    static constexpr int TW = TW_, TD = 4, TH = 256 / (TD * TW);
+    static constexpr int OPR = TW / 8;                      // w-octets per box row
+    static constexpr int VB = TD * TH * TW, NOCT = VB / 8;
+    static constexpr int HH = TH + 2, NR = (TD + 2) * HH;   // halo rows
+    static constexpr int XW = TW;                           // bf16 per XT row: halo w 0 .. TW-1
+    static constexpr int XE = NR * XW;                      // halo w TW, TW+1 of the rows, one bf16 pair each
+    static constexpr int XPL = XE + 2 * NR + 16;            // per-channel plane (an odd multiple of 16 bytes)
+    static constexpr int DROW = VB + 16;                    // dYT row: 544 bytes
+    static constexpr int NXB = NR * OPR * 4;                // X blocks of 8 voxels: rows x octets x 4 ci-groups
+    static constexpr int NXE = NR * 4;                      // X edge blocks: rows x 4 ci-groups
+    static constexpr int NXC = NXB > WS_NPT ? NXB - WS_NPT : 0;   // X blocks staged as a thread's third task
+    static_assert(VB == 256 && (TW == 8 || TW == 16), "box shape");
+    static_assert(((XPL * 2 / 16) & 1) == 1, "plane stride: odd multiple of 16 bytes");
+    static_assert(NOCT * 8 == WS_NPT && NXB - NXC <= WS_NPT && NXC + NXE <= WS_NPT, "staging task layout");
+};
+static_assert(GwCfg<64>::NW == WS_NCW && WsGeom<16>::NR == GW_NR && WsGeom<16>::XPL == GW_XPL &&
+                  WsGeom<16>::NXB == GW_NXB && WsGeom<16>::NXE == GW_NXE && WsGeom<16>::DROW == GW_DROW,
+              "the 16-wide box is the shared-kernel box");
 
 // Transposes 8 voxels x 8 channels (in[v] = channels of voxel v) and stores
 // channel row c (8 voxels) at dst + c * stride, one row at a time, so only
@@ -385,14 +411,16 @@ __device__ __forceinline__ void transpose_store8x8(const uint4 (&in)[8], uint16_
     }
 }
 
+template <int TW>
 __global__ __launch_bounds__(WS_NT)
 void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, float* __restrict__ part,
                      int N, int D, int H, int W, int Cin, int Cout, int bD, int bH, int bW, int nco, int nci,
                      int64_t nbox, int boxes_per_split)
 {
     constexpr int BO = 64;
-    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * GW_XPL];
-    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * GW_DROW];
+    using G = WsGeom<TW>;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * G::XPL];
+    __shared__ __attribute__((aligned(16))) uint16_t dt[2][BO * G::DROW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -430,20 +458,20 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     // for a voxel inside the volume.
     struct XTask { int hd, hh, wb; int32_t k; bool live; };
     auto xtask = [&](int x) {
-        const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
-        const int row = rem / 2, slot = rem % 2;
+        const int grp = x / (G::NR * G::OPR), rem = x % (G::NR * G::OPR);
+        const int row = rem / G::OPR, slot = rem % G::OPR;
         XTask t;
-        t.hd = row / GW_HH; t.hh = row % GW_HH; t.wb = 8 * slot - 1;
+        t.hd = row / G::HH; t.hh = row % G::HH; t.wb = 8 * slot - 1;
         t.k = (((t.hd - 1) * H + (t.hh - 1)) * W + t.wb) * (int32_t)xstride + grp * 16;
-        t.live = x < GW_NXB;
+        t.live = x < G::NXB;
         return t;
     };
     auto etask = [&](int e) {
-        const int erow = e % GW_NR, egrp = e / GW_NR;
+        const int erow = e % G::NR, egrp = e / G::NR;
         XTask t;
-        t.hd = erow / GW_HH; t.hh = erow % GW_HH; t.wb = 15;      // halo w = 16 + j
+        t.hd = erow / G::HH; t.hh = erow % G::HH; t.wb = TW - 1;      // halo w = TW + j
         t.k = (((t.hd - 1) * H + (t.hh - 1)) * W + t.wb) * (int32_t)xstride + egrp * 16;
-        t.live = e < GW_NXE;
+        t.live = e < G::NXE;
         return t;
     };
     // voxel j of a row that starts at w = base (>= -1) is inside 0 <= w < W
@@ -451,17 +479,17 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
     struct STasks { int32_t kA; int tdA, thA, w0A; XTask tB, tC; };
     auto stage_tasks = [&](int p) {
         STasks T;
-        const int oct = p % GW_NOCT, grp = p / GW_NOCT;
-        T.tdA = oct / (GW_TH * 2); T.thA = (oct / 2) % GW_TH; T.w0A = (oct & 1) * 8;
+        const int oct = p % G::NOCT, grp = p / G::NOCT;
+        T.tdA = oct / (G::TH * G::OPR); T.thA = (oct / G::OPR) % G::TH; T.w0A = (oct & (G::OPR - 1)) * 8;
         T.kA = ((T.tdA * H + T.thA) * W + T.w0A) * (int32_t)ystride + grp * 16;
         T.tB = xtask(p);
-        T.tC = p < 32 ? xtask(WS_NPT + p) : etask(p - 32);
+        T.tC = p < G::NXC ? xtask(WS_NPT + p) : etask(p - G::NXC);
         return T;
     };
     auto stage = [&](const BoxPos& bp, int buf, const STasks& T) {
         int p = tid - WS_NCW * 64;
         asm volatile("" : "+v"(p));
-        const int gd0 = bp.bd * GW_TD, bh0 = bp.bh * GW_TH, bw0 = bp.bw * GW_TW;
+        const int gd0 = bp.bd * G::TD, bh0 = bp.bh * G::TH, bw0 = bp.bw * TW;
         const int xd0 = gd0 > 0 ? gd0 - 1 : 0;
         const auto rd = buf_rsrc(dY + ((int64_t)bp.n * D + gd0) * plane * Cout + co0, OOB);
         const auto rx = buf_rsrc(X + ((int64_t)bp.n * D + xd0) * plane * Cin + ci0, OOB);
@@ -488,8 +516,8 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
                                                          rx, pick(rok & wok(base, j), off + j * xstride), 0, 0));
         };
         xload(T.tB, ub, 8);
-        const bool c_edge = p >= 32;
-        const int e = p - 32;
+        const bool c_edge = p >= G::NXC;
+        const int e = p - G::NXC;
         if (!c_edge) {
             xload(T.tC, uc, 8);
         } else {
@@ -497,27 +525,27 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         }
         // stores: dY block p, X block p, then block C
         {
-            const int oct = p % GW_NOCT, grp = p / GW_NOCT;
-            const int slot = (oct & 1) * (GW_NOCT / 2) + (oct >> 1);
-            transpose_store8x8(ua, &dt[buf][(grp * 8) * GW_DROW + slot * 8], GW_DROW);
+            const int oct = p % G::NOCT, grp = p / G::NOCT;
+            const int slot = (oct & (G::OPR - 1)) * (G::NOCT / G::OPR) + (oct >> (G::OPR / 2));
+            transpose_store8x8(ua, &dt[buf][(grp * 8) * G::DROW + slot * 8], G::DROW);
         }
         auto xstore = [&](int x, const uint4 (&u)[8]) {
-            const int grp = x / (GW_NR * 2), rem = x % (GW_NR * 2);
-            const int row = rem / 2, slot = rem % 2;
-            transpose_store8x8(u, &xt[buf][(grp * 8) * GW_XPL + row * GW_XW + slot * 8], GW_XPL);
+            const int grp = x / (G::NR * G::OPR), rem = x % (G::NR * G::OPR);
+            const int row = rem / G::OPR, slot = rem % G::OPR;
+            transpose_store8x8(u, &xt[buf][(grp * 8) * G::XPL + row * G::XW + slot * 8], G::XPL);
         };
-        xstore(p, ub);
+        if (G::NXB >= WS_NPT || p < G::NXB) xstore(p, ub);
         if (!c_edge) {
             xstore(WS_NPT + p, uc);
-        } else if (e < GW_NXE) {
-            const int erow = e % GW_NR, egrp = e / GW_NR;
+        } else if (e < G::NXE) {
+            const int erow = e % G::NR, egrp = e / G::NR;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 const int h = c >> 1;
                 const uint32_t w0v = h == 0 ? uc[0].x : h == 1 ? uc[0].y : h == 2 ? uc[0].z : uc[0].w;
                 const uint32_t w1v = h == 0 ? uc[1].x : h == 1 ? uc[1].y : h == 2 ? uc[1].z : uc[1].w;
-                *reinterpret_cast<uint32_t*>(&xt[buf][(egrp * 8 + c) * GW_XPL + GW_XE + 2 * erow]) =
+                *reinterpret_cast<uint32_t*>(&xt[buf][(egrp * 8 + c) * G::XPL + G::XE + 2 * erow]) =
                     __builtin_amdgcn_perm(w1v, w0v, sel);
             }
         }
@@ -532,52 +560,79 @@ void wgrad_ws_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict_
         for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
             for (int kw = 0; kw < 3; ++kw) acc[c][kh][kw] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* drow0 = dt[0] + (32 * cp + l16) * GW_DROW;
-    const uint16_t* xpl0 = xt[0] + (16 * jf + l16) * GW_XPL + kd * GW_HH * GW_XW;
+    const uint16_t* drow0 = dt[0] + (32 * cp + l16) * G::DROW;
+    const uint16_t* xpl0 = xt[0] + (16 * jf + l16) * G::XPL + kd * G::HH * G::XW;
+    // the three kw operands of one 8-voxel halo row segment q (w 0-7 of the
+    // row's part) whose next two halo voxels are the low half of e: kw = 1
+    // and 2 shift by one and two voxels (MFMA operands need aligned
+    // register quads, so kw = 2 is a copy)
+    auto shifts = [](const uint4& q, uint32_t e, bf16x8 (&b)[3]) {
+        b[0] = __builtin_bit_cast(bf16x8, q);
+        b[1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q.y, q.x, 16),
+                                                     __builtin_amdgcn_alignbit(q.z, q.y, 16),
+                                                     __builtin_amdgcn_alignbit(q.w, q.z, 16),
+                                                     __builtin_amdgcn_alignbit(e, q.w, 16)));
+        b[2] = __builtin_bit_cast(bf16x8, make_uint4(q.y, q.z, q.w, e));
+    };
     auto compute = [&](int buf) {
-        const uint16_t* drow = drow0 + buf * (BO * GW_DROW);
-        const uint16_t* xpl = xpl0 + buf * (32 * GW_XPL);
+        const uint16_t* drow = drow0 + buf * (BO * G::DROW);
+        const uint16_t* xpl = xpl0 + buf * (32 * G::XPL);
 #pragma unroll 1
-        for (int s2 = 0; s2 < GW_TD; ++s2) {
-            const int row = s2 * GW_TH + lg;
-            bf16x8 a[2][2];                                 // [co fragment][octet]
+        for (int s2 = 0; s2 < G::TD; ++s2) {
+            // the 32-voxel reduction step of one MFMA: 4 h rows (one per lane
+            // group) x 8 w voxels.  TW = 16: the two w-octets of rows
+            // s2 * 4 + lg; TW = 8: rows s2 * 8 + lg and s2 * 8 + 4 + lg.
+            bf16x8 a[2][2];                                 // [co fragment][step]
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * GW_DROW + (h * (GW_NOCT / 2) + row) * 8);
-            const uint16_t* xr = xpl + (s2 * GW_HH + lg) * GW_XW;
-            const uint32_t* er = reinterpret_cast<const uint32_t*>(xpl - kd * GW_HH * GW_XW + GW_XE) +
-                                 (kd + s2) * GW_HH + lg;
+                for (int h = 0; h < 2; ++h) {
+                    const int slot = TW == 16 ? h * (G::NOCT / 2) + s2 * G::TH + lg : s2 * G::TH + 4 * h + lg;
+                    a[c][h] = *reinterpret_cast<const bf16x8*>(drow + c * 16 * G::DROW + slot * 8);
+                }
+            if constexpr (TW == 16) {
+                const uint16_t* xr = xpl + (s2 * G::HH + lg) * G::XW;
+                const uint32_t* er = reinterpret_cast<const uint32_t*>(xpl - kd * G::HH * G::XW + G::XE) +
+                                     (kd + s2) * G::HH + lg;
 #pragma unroll
-            for (int kh = 0; kh < 3; ++kh) {
-                const uint16_t* xp = xr + kh * GW_XW;
-                uint4 q0 = *reinterpret_cast<const uint4*>(xp);
-                uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
-                uint32_t e1 = er[kh];
-                asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(q1.x), "+v"(q1.y),
-                             "+v"(q1.z), "+v"(q1.w), "+v"(e1));
-                const uint32_t e0 = q1.x;
-                bf16x8 b[2][3];
-                b[0][0] = __builtin_bit_cast(bf16x8, q0);
-                b[0][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q0.y, q0.x, 16),
-                                                                __builtin_amdgcn_alignbit(q0.z, q0.y, 16),
-                                                                __builtin_amdgcn_alignbit(q0.w, q0.z, 16),
-                                                                __builtin_amdgcn_alignbit(e0, q0.w, 16)));
-                b[0][2] = __builtin_bit_cast(bf16x8, make_uint4(q0.y, q0.z, q0.w, e0));
-                b[1][0] = __builtin_bit_cast(bf16x8, q1);
-                b[1][1] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_alignbit(q1.y, q1.x, 16),
-                                                                __builtin_amdgcn_alignbit(q1.z, q1.y, 16),
-                                                                __builtin_amdgcn_alignbit(q1.w, q1.z, 16),
-                                                                __builtin_amdgcn_alignbit(e1, q1.w, 16)));
-                b[1][2] = __builtin_bit_cast(bf16x8, make_uint4(q1.y, q1.z, q1.w, e1));
+                for (int kh = 0; kh < 3; ++kh) {
+                    const uint16_t* xp = xr + kh * G::XW;
+                    uint4 q0 = *reinterpret_cast<const uint4*>(xp);
+                    uint4 q1 = *reinterpret_cast<const uint4*>(xp + 8);
+                    uint32_t e1 = er[kh];
+                    asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(q1.x), "+v"(q1.y),
+                                 "+v"(q1.z), "+v"(q1.w), "+v"(e1));
+                    bf16x8 b[2][3];
+                    shifts(q0, q1.x, b[0]);
+                    shifts(q1, e1, b[1]);
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int kw = 0; kw < 3; ++kw)
+                        for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
-                        for (int c = 0; c < 2; ++c)
-                            acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[h][kw], acc[c][kh][kw], 0, 0, 0);
+                            for (int c = 0; c < 2; ++c)
+                                acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[h][kw], acc[c][kh][kw], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint16_t* xr = xpl + (s2 * G::HH + 4 * h + lg) * G::XW;
+                    const uint32_t* er = reinterpret_cast<const uint32_t*>(xpl - kd * G::HH * G::XW + G::XE) +
+                                         (kd + s2) * G::HH + 4 * h + lg;
+#pragma unroll
+                    for (int kh = 0; kh < 3; ++kh) {
+                        uint4 q0 = *reinterpret_cast<const uint4*>(xr + kh * G::XW);
+                        uint32_t e0 = er[kh];
+                        asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w), "+v"(e0));
+                        bf16x8 b[3];
+                        shifts(q0, e0, b);
+#pragma unroll
+                        for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                            for (int c = 0; c < 2; ++c)
+                                acc[c][kh][kw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][h], b[kw], acc[c][kh][kw], 0, 0, 0);
+                    }
+                }
             }
         }
     };
@@ -704,8 +759,10 @@ WgradPlan plan_wgrad(const cf_dims& x, int cout)
     } else {
         p.kind = 0;
         const int bo = cout % 64 == 0 ? 64 : 32;
-        const int64_t nbox = x.n * ((x.d + GW_TD - 1) / GW_TD) * ((x.h + GW_TH - 1) / GW_TH) *
-                             ((x.w + GW_TW - 1) / GW_TW);
+        // the 4 x 8 x 8 box where a 16-wide one would be half outside the volume
+        p.tw = bo == 64 && x.w <= 8 ? 8 : 16;
+        const int th = 256 / (4 * p.tw);
+        const int64_t nbox = x.n * ((x.d + 3) / 4) * ((x.h + th - 1) / th) * ((x.w + p.tw - 1) / p.tw);
         const int64_t outer = (int64_t)(cout / bo) * (x.c / 32);
         // one round of blocks over the 256 CUs (one 12-wave or two 6-wave blocks per CU)
         const int64_t conc = bo == 64 ? 256 : 512;
@@ -730,15 +787,21 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
         hipError_t e = launch_wgrad_c4_partials(p, X, dY, nullptr, nullptr, nullptr, 0.f, part, x, cout, s);
         if (e != hipSuccess) return e;
     } else {
-        const int bD = (int)((x.d + GW_TD - 1) / GW_TD), bH = (int)((x.h + GW_TH - 1) / GW_TH),
-                  bW = (int)((x.w + GW_TW - 1) / GW_TW);
+        const int tw = p.tw, th = 256 / (4 * tw);
+        const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + th - 1) / th), bW = (int)((x.w + tw - 1) / tw);
         const int64_t nbox = x.n * bD * bH * bW;
         const int nci = (int)(x.c / 32);
         if (cout % 64 == 0) {
             const int nco = cout / 64;
-            hipLaunchKernelGGL(wgrad_ws_kernel, dim3((unsigned)((int64_t)nco * nci * p.splits)), dim3(WS_NT), 0, s, X,
-                               dY, part, (int)x.n, (int)x.d, (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nco, nci,
-                               nbox, (int)p.vox_per_split);
+            const dim3 grid((unsigned)((int64_t)nco * nci * p.splits));
+            if (tw == 8)
+                hipLaunchKernelGGL(wgrad_ws_kernel<8>, grid, dim3(WS_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
+                                   (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nco, nci, nbox,
+                                   (int)p.vox_per_split);
+            else
+                hipLaunchKernelGGL(wgrad_ws_kernel<16>, grid, dim3(WS_NT), 0, s, X, dY, part, (int)x.n, (int)x.d,
+                                   (int)x.h, (int)x.w, (int)x.c, cout, bD, bH, bW, nco, nci, nbox,
+                                   (int)p.vox_per_split);
         } else {
             const int nco = cout / 32;
             hipLaunchKernelGGL(wgrad_mfma_kernel<32>, dim3((unsigned)((int64_t)nco * nci * p.splits)),

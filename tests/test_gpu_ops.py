@@ -111,6 +111,9 @@ WGRAD_CASES = [
     (2, 5, 9, 19, 32, 64),
     (1, 6, 10, 7, 64, 32),
     (1, 8, 8, 8, 256, 256),
+    (2, 5, 11, 7, 32, 64),    # volumes at most 8 wide: the 4 x 8 x 8 box, ragged in d, h and w
+    (3, 6, 17, 3, 64, 128),
+    (1, 1, 1, 1, 32, 64),
     (2, 7, 6, 21, 4, 32),     # layer-1 kernel
     (2, 7, 6, 9, 16, 32),     # 16 input channels: bf16 kernel on an input padded to 32
     (1, 5, 6, 18, 8, 64),     # 8 input channels, padded
