@@ -174,7 +174,6 @@ struct WgradPlan {
     int splits;
     int64_t vox_per_split;
     size_t part_bytes;
-    int tw;           // kind 0: box width (16, or 8 for volumes at most 8 wide)
 };
 WgradPlan plan_wgrad(const cf_dims& x, int cout);
 // The general kernel (Cin % 32 == 0) addresses a box's six input planes and

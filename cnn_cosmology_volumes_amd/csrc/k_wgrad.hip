@@ -730,6 +730,13 @@ void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dW,
     }
 }
 
+// Box width of the Cin % 32 == 0 kernels: the 4 x 8 x 8 box where a 16-wide
+// one would be half outside the volume (64-channel output blocks only).
+int wgrad_box_w(const cf_dims& x, int cout)
+{
+    return cout % 64 == 0 && x.w <= 8 ? 8 : 16;
+}
+
 }  // namespace
 
 bool wgrad_mfma_fits(const cf_dims& x, int cout)
@@ -759,10 +766,8 @@ WgradPlan plan_wgrad(const cf_dims& x, int cout)
     } else {
         p.kind = 0;
         const int bo = cout % 64 == 0 ? 64 : 32;
-        // the 4 x 8 x 8 box where a 16-wide one would be half outside the volume
-        p.tw = bo == 64 && x.w <= 8 ? 8 : 16;
-        const int th = 256 / (4 * p.tw);
-        const int64_t nbox = x.n * ((x.d + 3) / 4) * ((x.h + th - 1) / th) * ((x.w + p.tw - 1) / p.tw);
+        const int tw = wgrad_box_w(x, cout), th = 256 / (4 * tw);
+        const int64_t nbox = x.n * ((x.d + 3) / 4) * ((x.h + th - 1) / th) * ((x.w + tw - 1) / tw);
         const int64_t outer = (int64_t)(cout / bo) * (x.c / 32);
         // one round of blocks over the 256 CUs (one 12-wave or two 6-wave blocks per CU)
         const int64_t conc = bo == 64 ? 256 : 512;
@@ -787,7 +792,7 @@ hipError_t launch_wgrad(const WgradPlan& p, const uint16_t* X, const uint16_t* d
         hipError_t e = launch_wgrad_c4_partials(p, X, dY, nullptr, nullptr, nullptr, 0.f, part, x, cout, s);
         if (e != hipSuccess) return e;
     } else {
-        const int tw = p.tw, th = 256 / (4 * tw);
+        const int tw = wgrad_box_w(x, cout), th = 256 / (4 * tw);
         const int bD = (int)((x.d + 3) / 4), bH = (int)((x.h + th - 1) / th), bW = (int)((x.w + tw - 1) / tw);
         const int64_t nbox = x.n * bD * bH * bW;
         const int nci = (int)(x.c / 32);
