@@ -172,12 +172,38 @@ def op_timings(torch, cf, c, dev, reps):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+_C_COMMENT_OR_STRING = None
+
+
+def source_digest(paths):
+    """sha256 of the code of `paths` (relative to the repository root) with
+    comments and blank lines left out: C/C++ comments in the kernel sources,
+    whole-line '#' comments in Python files.  String literals are kept.  A
+    change of code changes it; a change of comments does not."""
+    import hashlib
+    import re
+    global _C_COMMENT_OR_STRING
+    if _C_COMMENT_OR_STRING is None:
+        _C_COMMENT_OR_STRING = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
+            text = fh.read()
+        if rel.endswith(".py"):
+            lines = [l for l in text.split("\n") if not l.lstrip().startswith("#")]
+        else:
+            text = _C_COMMENT_OR_STRING.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+            lines = text.split("\n")
+        code = "\n".join(l.rstrip() for l in lines if l.strip())
+        h.update(rel.encode() + b"\0" + code.encode() + b"\0")
+    return h.hexdigest()
+
+
 def measured_traffic(op_name):
     """HBM bytes per launch of `op_name` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (scaled by the same counters on a plain
     copy of known size), or None when there are none for this entry point or
-    its kernel source has changed since they were taken."""
-    import hashlib
+    the code of its kernel sources has changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -188,14 +214,11 @@ def measured_traffic(op_name):
     t = entries.get(op_name)
     if not isinstance(t, dict):
         return None
-    h = hashlib.sha256()
-    for rel in t.get("sources", []):
-        try:
-            with open(os.path.join(ROOT, rel), "rb") as fh:
-                h.update(fh.read())
-        except OSError:
-            return None
-    if h.hexdigest() != t.get("sources_sha256"):
+    try:
+        digest = source_digest(t.get("sources", []))
+    except OSError:
+        return None
+    if digest != t.get("code_sha256"):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -30,12 +30,14 @@ namespace {
 // x 8 channels) in registers and stores them channel-major in LDS, so the
 // MFMA operands are single aligned 16-byte LDS reads:
 //   dYT[co][k]                      k = box voxel, 8 consecutive along w
-//   XT[ci][halo row (d,h)][w]       w = 0..17 of the halo, row padded to 24
-// A k-step of 32 voxels is 4 w-octets, one per 16-lane group.  For tap
-// (kd,kh,kw) the X operand of an octet starting at w0 is XT[..][w0+kw ..
-// w0+kw+7]: the lane reads w0..w0+15 once (two aligned 16-byte reads; the
-// row is padded to 24) and forms the three kw-shifted operands by register
-// selection (kw = 0, 2) and a 16-bit funnel shift (kw = 1).
+//   XT[ci][halo row (d,h)][w]       halo w 0..15; the halo w 16-17 of every
+//                                   row follow the rows of the channel
+//                                   plane, one bf16 pair per row
+// A k-step of 32 voxels is 4 lane groups x 8 voxels along w.  For tap
+// (kd,kh,kw) the X operand of an octet starting at halo w0 is XT[..][w0+kw
+// .. w0+kw+7]: the lane reads the octet and the next two halo values once
+// and forms the three kw-shifted operands by register selection (kw = 0, 2)
+// and a 16-bit funnel shift (kw = 1).
 // Block: BO output channels x 32 input channels.  A wave owns two 16-wide
 // output-channel fragments, one 16-wide input-channel fragment and one kd,
 // i.e. 2 x 9 accumulator tiles.  A lane group walks the two w-octets of one
@@ -44,7 +46,8 @@ namespace {
 // 36 MFMAs a wave issues 4 dY reads and 9 X reads.  LDS instruction issue,
 // not bytes, is what limits these loops on gfx950 (a 4-byte and a 16-byte
 // per-lane read cost about the same), so reads per MFMA is the figure that
-// matters.  Box: 4 x 4 x 16 voxels (halo 6 x 6 x 18).  The next box is
+// matters.  Box: 4 x 4 x 16 voxels (halo 6 x 6 x 18); the wave-specialized
+// kernel also has a 4 x 8 x 8 box for narrow volumes.  The next box is
 // loaded into registers while the current one is computed.
 constexpr int GW_TD = 4, GW_TH = 4, GW_TW = 16;
 constexpr int GW_VB = GW_TD * GW_TH * GW_TW;                 // 256 voxels per box
