@@ -443,13 +443,15 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, pg[k], (int)(step * tap_stride * 2), 0));
     };
     auto pvalid = [&](int k) { return T::NT * (k + 1) <= NPC || (int)threadIdx.x + k * T::NT < NPC; };
-    // 64-channel blocks load the halo of chunk c + 1 during chunk c's first
-    // step and store it when chunk c is done, so its latency hides behind
-    // chunk c's MFMAs; past the last chunk the resource is empty and the
-    // loads read zeros, so the loads are the same on every path.  (The
-    // 32-channel block, at its register bound for three waves per SIMD,
-    // measured slower with it and loads each chunk's halo at its start.)
-    constexpr bool PF = BM == 64;
+    // The halo of chunk c + 1 is loaded into registers during chunk c and
+    // stored when chunk c is done, so its latency hides behind chunk c's
+    // MFMAs; past the last chunk the resource is empty and the loads read
+    // zeros, so the loads are the same on every path.  64-channel blocks
+    // issue the loads in chunk c's first step.  The 32-channel block, at its
+    // register bound for three waves per SIMD, issues them in step 7 of 9:
+    // the registers are then held for two steps only (162 VGPRs; held for
+    // the whole chunk they cost more than the latency they hid).
+    constexpr int PFS = BM == 64 ? 0 : 7;
     uint4 val[T::IT];
     auto hload = [&](int c, bool valid) {
         const auto rx = buf_rsrc(xbase + c * 32, valid ? xbytes - (uint32_t)c * 64u : 0u);
@@ -457,12 +459,11 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
         for (int it = 0; it < T::IT; ++it)
             val[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, hoff[it], 0, 0));
     };
-    if (PF) hload(c_begin, true);
+    hload(c_begin, true);
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
         uint4 ra[PPT];
         {
-            if (!PF) hload(c, true);
             // weight ring prologue: step 0's tiles go to group 0 with the
             // halo, step 1's are held in registers until step 0 stores them
             uint4 w0v[PPT];
@@ -490,7 +491,7 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
         for (int s = 0; s < 9; ++s) {
             const int kh = s / 3, kw = s % 3;
-            if (PF && s == 0) hload(c + 1, c + 1 < c_end);
+            if (s == PFS) hload(c + 1, c + 1 < c_end);
             // ring loads two steps ahead, then this step's operands
             uint4 rn[PPT];
 #pragma unroll
