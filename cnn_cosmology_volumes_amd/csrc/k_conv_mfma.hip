@@ -81,6 +81,88 @@ struct Tile {
 // 32-byte halves are swapped where bit 2 of the voxel's halo w is set.
 __device__ __forceinline__ int halo_chunk(int q, int hw) { return q ^ (((hw >> 2) & 1) << 1); }
 
+// Pooled epilogue of the 4 x 4 x 16 tiles (BM output channels, NT threads),
+// through LDS.  Each wave writes its accumulators, rounded to bf16, into a
+// [tile voxel][channel] tile ZS channels wide that reuses the halo's LDS
+// (every wave has passed a barrier after its last halo read); after a
+// barrier, one thread per (pooled voxel, 8-channel group) reads its 2^3
+// window 16 bytes per voxel, takes the first strict maximum in window order
+// a*4 + b*2 + e (d, h, w offsets), applies leaky ReLU to it and stores P and
+// the index.  These are the separate pool kernel's values.  vox(j) is the
+// tile voxel of fragment j in this lane; the lane's channels of fragment i
+// are co_wave + 16 i + 4 lg .. + 3 within the block.
+template <int BM, int TD, int TH, int TW>
+struct PoolTile {
+    static constexpr int ZS = BM + 8;       // bf16 per tile voxel (144 bytes for BM = 64)
+    static constexpr int SIZE = TD * TH * TW * ZS;
+};
+
+template <int BM, int TD, int TH, int TW, int NT, int MI, int NJ, typename Vox>
+__device__ __forceinline__ void pool_epilogue_lds(uint16_t* __restrict__ zt, const f32x4 (&acc)[MI][NJ], Vox vox,
+                                                  int co_wave, int lg, uint16_t* __restrict__ P,
+                                                  uint8_t* __restrict__ pidx, float slope, int n, int D, int H, int W,
+                                                  int Cout, int co_block, int d0, int h0, int w0)
+{
+    constexpr int ZS = PoolTile<BM, TD, TH, TW>::ZS;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int v = vox(j);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const f32x4 r = acc[i][j];
+            *reinterpret_cast<uint2*>(zt + v * ZS + co_wave + 16 * i + 4 * lg) =
+                make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+        }
+    }
+    __syncthreads();
+    constexpr int PD = TD / 2, PH = TH / 2, PW = TW / 2, NG = BM / 8;
+    const int Dp = D >> 1, Hp = H >> 1, Wp = W >> 1;
+    // 16-byte P and 8-byte index stores where every group is aligned to them
+    const bool wide = Cout % 8 == 0 && (((uintptr_t)P & 15) | ((uintptr_t)pidx & 7)) == 0;
+    for (int e = threadIdx.x; e < PD * PH * PW * NG; e += NT) {
+        const int g = e % NG, pv = e / NG;
+        const int pk = pv % PW, pj = (pv / PW) % PH, pi = pv / (PW * PH);
+        const int gpd = (d0 >> 1) + pi, gph = (h0 >> 1) + pj, gpw = (w0 >> 1) + pk;
+        const int co = co_block + 8 * g;
+        if (gpd >= Dp || gph >= Hp || gpw >= Wp || co >= Cout) continue;
+        float best[8];
+        uint32_t bi[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int a = p >> 2, b = (p >> 1) & 1, c = p & 1;
+            const int v = ((2 * pi + a) * TH + 2 * pj + b) * TW + 2 * pk + c;
+            const uint4 u = *reinterpret_cast<const uint4*>(zt + v * ZS + 8 * g);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float z = __uint_as_float((k & 1) ? (w4[k >> 1] & 0xffff0000u) : (w4[k >> 1] << 16));
+                if (p == 0 || z > best[k]) { best[k] = z; bi[k] = (uint32_t)p; }
+            }
+        }
+        float out[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) out[k] = best[k] > 0.f ? best[k] : slope * best[k];
+        const uint2 plo = make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
+        const uint2 phi = make_uint2(pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+        const uint32_t ilo = bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24);
+        const uint32_t ihi = bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24);
+        const int64_t o = (((int64_t)n * Dp + gpd) * Hp + gph) * Wp * Cout + (int64_t)gpw * Cout + co;
+        if (wide) {
+            *reinterpret_cast<uint4*>(P + o) = make_uint4(plo.x, plo.y, phi.x, phi.y);
+            *reinterpret_cast<uint2*>(pidx + o) = make_uint2(ilo, ihi);
+        } else {
+            // Cout % 4 == 0: the group's first four channels, and the next
+            // four where they exist
+            *reinterpret_cast<uint2*>(P + o) = plo;
+            *reinterpret_cast<uint32_t*>(pidx + o) = ilo;
+            if (co + 8 <= Cout) {
+                *reinterpret_cast<uint2*>(P + o + 4) = phi;
+                *reinterpret_cast<uint32_t*>(pidx + o + 4) = ihi;
+            }
+        }
+    }
+}
+
 template <int BM, int WM, int WN, int TD, int TH, int TW, int LS, int WPE_ = 0, bool POOL = false>
 __global__ __launch_bounds__((Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::NT), (Tile<BM, WM, WN, TD, TH, TW, LS, WPE_>::MINB))
 void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wk,
@@ -255,49 +337,13 @@ void conv3d_mfma_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 
     if constexpr (POOL) {
         static_assert(TW == 16 && WN == 2 * TH * TW && TD % 2 == 0 && TH % 2 == 0, "pooled epilogue mapping");
-        // Fragment j of this wave holds tile voxels (2*wave + j / TH, j % TH, l16).
-        const int Dp = D >> 1, Hp = H >> 1, Wp = W >> 1;
-        const uint32_t c = l16 & 1;                        // window w offset of this lane
-        const int gpd = (d0 >> 1) + wave, gpw = (w0 >> 1) + (l16 >> 1);
-#pragma unroll
-        for (int ph = 0; ph < TH / 2; ++ph) {
-            const int gph = (h0 >> 1) + ph;
-            const bool inside = gpd < Dp && gph < Hp && gpw < Wp;
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i) {
-                const int co = co_base + 16 * i + 4 * lg;
-                float out[4];
-                uint32_t bix[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // this lane's four window members in window order (a, b) = 00, 01, 10, 11
-                    float z[4];
-#pragma unroll
-                    for (int ab = 0; ab < 4; ++ab)
-                        z[ab] = __uint_as_float((uint32_t)f2bf(acc[i][(ab >> 1) * TH + 2 * ph + (ab & 1)][r]) << 16);
-                    // even lanes start from window position 0 like a sequential scan;
-                    // odd lanes from -inf, so a NaN at position 1 is skipped as the
-                    // scan would skip it
-                    float best = c ? -INFINITY : z[0];
-                    uint32_t bp = c;
-#pragma unroll
-                    for (int ab = 0; ab < 4; ++ab)
-                        if (z[ab] > best) { best = z[ab]; bp = 2u * ab + c; }
-                    // combine with the neighbour lane (the other w position): larger
-                    // value, on a tie the earlier window position
-                    const float ob = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(best), 0xB1, 0xF, 0xF, false));
-                    const uint32_t op = (uint32_t)__builtin_amdgcn_mov_dpp((int)bp, 0xB1, 0xF, 0xF, false);
-                    if (ob > best || (ob == best && op < bp)) { best = ob; bp = op; }
-                    out[r] = best > 0.f ? best : slope * best;
-                    bix[r] = bp;
-                }
-                if (c == 0 && inside && co < Cout) {
-                    const int64_t o = (((int64_t)n * Dp + gpd) * Hp + gph) * Wp * Cout + (int64_t)gpw * Cout + co;
-                    *reinterpret_cast<uint2*>(Y + o) = make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
-                    *reinterpret_cast<uint32_t*>(pidx + o) = bix[0] | (bix[1] << 8) | (bix[2] << 16) | (bix[3] << 24);
-                }
-            }
-        }
+        static_assert(PoolTile<BM, TD, TH, TW>::SIZE <= T::HV * LS, "pooled tile fits in the halo's LDS");
+        // every wave's last halo reads come before the tile overwrites them
+        lds_barrier();
+        // fragment j of this wave holds tile voxels (2 * wave + j / TH, j % TH, l16)
+        pool_epilogue_lds<BM, TD, TH, TW, T::NT>(
+            halo, acc, [&](int j) { return ((2 * wave + j / TH) * TH + j % TH) * TW + l16; }, wm * WM, lg, Y, pidx,
+            slope, n, D, H, W, Cout, blockIdx.y * BM, d0, h0, w0);
         return;
     }
 
@@ -530,49 +576,13 @@ void conv3d_mfma_kdr_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     }
 
     if constexpr (POOL) {
-        static_assert(TW == 16 && JH == 2 && TD % 2 == 0, "pooled epilogue mapping");
-        const int Dp = D >> 1, Hp = H >> 1, Wp = W >> 1;
-        const uint32_t c = l16 & 1;                        // window w offset of this lane
-        const int gph = (h0 >> 1) + wave, gpw = (w0 >> 1) + (l16 >> 1);
-#pragma unroll
-        for (int pd = 0; pd < TD / 2; ++pd) {
-            const int gpd = (d0 >> 1) + pd;
-            const bool inside = gpd < Dp && gph < Hp && gpw < Wp;
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i) {
-                const int co = co_base + 16 * i + 4 * lg;
-                float out[4];
-                uint32_t bix[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // this lane's four window members in window order (a, b) = 00, 01, 10, 11
-                    float z[4];
-#pragma unroll
-                    for (int ab = 0; ab < 4; ++ab)
-                        z[ab] = __uint_as_float((uint32_t)f2bf(acc[i][(2 * pd + (ab >> 1)) * JH + (ab & 1)][r]) << 16);
-                    // even lanes start from window position 0 like a sequential scan;
-                    // odd lanes from -inf, so a NaN at position 1 is skipped as the
-                    // scan would skip it
-                    float best = c ? -INFINITY : z[0];
-                    uint32_t bp = c;
-#pragma unroll
-                    for (int ab = 0; ab < 4; ++ab)
-                        if (z[ab] > best) { best = z[ab]; bp = 2u * ab + c; }
-                    // combine with the neighbour lane (the other w position): larger
-                    // value, on a tie the earlier window position
-                    const float ob = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(best), 0xB1, 0xF, 0xF, false));
-                    const uint32_t op = (uint32_t)__builtin_amdgcn_mov_dpp((int)bp, 0xB1, 0xF, 0xF, false);
-                    if (ob > best || (ob == best && op < bp)) { best = ob; bp = op; }
-                    out[r] = best > 0.f ? best : slope * best;
-                    bix[r] = bp;
-                }
-                if (c == 0 && inside && co < Cout) {
-                    const int64_t o = (((int64_t)n * Dp + gpd) * Hp + gph) * Wp * Cout + (int64_t)gpw * Cout + co;
-                    *reinterpret_cast<uint2*>(Y + o) = make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
-                    *reinterpret_cast<uint32_t*>(pidx + o) = bix[0] | (bix[1] << 8) | (bix[2] << 16) | (bix[3] << 24);
-                }
-            }
-        }
+        static_assert(TW == 16 && JH == 2 && TD % 2 == 0 && RPF == 1, "pooled epilogue mapping");
+        static_assert(PoolTile<BM, TD, TH, TW>::SIZE <= T::HV * LS, "pooled tile fits in the halo's LDS");
+        lds_barrier();
+        // fragment j of this wave holds tile voxels (j / JH, wave * JH + j % JH, l16)
+        pool_epilogue_lds<BM, TD, TH, TW, T::NT>(
+            halo, acc, [&](int j) { return ((j / JH) * TH + wave * JH + j % JH) * TW + l16; }, wm * WM, lg, Y, pidx,
+            slope, n, D, H, W, Cout, blockIdx.y * BM, d0, h0, w0);
         return;
     }
 

@@ -311,6 +311,24 @@ def test_conv3d_pool_fwd_equals_conv_then_pool(shape):
     check_pool_indices(zo, idx.cpu().numpy(), io, g, po)
 
 
+# Output channels that are not a multiple of 8 on the pooled epilogue: the
+# last 8-channel group holds 4 channels.  The first shape takes the per-wave
+# weight kernel (one input chunk), the second the weight-ring kernel (two
+# chunks, at least 512 blocks so the reduction is not split).
+@pytest.mark.parametrize("shape", [(1, 6, 10, 34, 32, 36), (2, 16, 32, 64, 64, 100)])
+def test_conv3d_pool_fwd_ragged_channel_groups(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 11)
+    x = act(rng, (N, D, H, W, Ci), BF)
+    w = weights(rng, Ci, Co, BF)
+    xd, wd = to_dev(x, BF), to_dev(w, BF)
+    P, idx = cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+    P2, idx2 = cf.cf_pool3d_fwd(cf.cf_conv3d_fwd(xd, wd), SLOPE)
+    torch.cuda.synchronize()
+    assert P.shape == (N, D // 2, H // 2, W // 2, Co)
+    assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
+
+
 @pytest.mark.parametrize("shape", [(2, 6, 10, 34, 32, 64), (1, 4, 6, 48, 32, 128), (1, 6, 8, 8, 64, 64),
                                    (2, 8, 16, 32, 4, 32), (1, 6, 10, 18, 4, 32)])
 def test_conv3d_pool_fwd_ties_follow_window_order(shape):
