@@ -18,6 +18,7 @@ BF, F32 = torch.bfloat16, torch.float32
 CASES = [
     # (dtype, first shape, second smaller shape, cout)
     (BF, (8, 64, 64, 64, 32), (2, 16, 16, 16, 32), 64),      # the 128^3 step's second block, then a small one
+    (BF, (8, 8, 8, 8, 256), (2, 6, 5, 7, 64), 256),          # volumes at most 8 wide: the 4 x 8 x 8 box
     (BF, (2, 34, 20, 18, 4), (1, 6, 10, 14, 4), 32),         # first-layer kernel, ragged boxes
     (F32, (2, 12, 10, 9, 8), (1, 5, 6, 7, 8), 16),           # fp32 matrix-core kernel
     (F32, (2, 6, 5, 7, 3), (1, 4, 3, 5, 3), 5),              # direct fp32 kernel (channels not multiples of 4)
