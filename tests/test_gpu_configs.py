@@ -245,3 +245,33 @@ def test_train128_training_lowers_loss():
     assert all(np.isfinite(losses)), losses
     assert all(b < a for a, b in zip(losses[:10], losses[1:11])), losses
     assert losses[-1] < 0.1 * losses[0], losses
+
+
+# ------------------------- weight-ring convolutions with many ragged tiles
+# More tiles than one round of resident blocks, ragged against the tiles:
+# backward-data into 32 channels (the 32-channel ring block, two input
+# chunks); the pooled block forward of 64 -> 128 channels (the 64-channel
+# ring block on 4 x 4 x 16 tiles); and a 64 -> 64 forward on a volume 8 wide
+# (the 64-channel ring block on 4 x 8 x 8 tiles).
+@pytest.mark.parametrize("shape", [(5, 18, 34, 66, 64, 32), (4, 16, 34, 66, 64, 128), (40, 16, 30, 8, 64, 64)])
+def test_ring_conv_many_ragged_tiles(shape):
+    N, D, H, W, Ci, Co = shape
+    rng = np.random.default_rng(sum(shape) + 41)
+    x = sd.normal(rng, (N, D, H, W, Ci), bf16=True)
+    w = sd.bf16_round_f32(sd.he_normal_conv(rng, Ci, Co))
+    xd, wd = to_dev(x, torch.bfloat16), to_dev(w, torch.bfloat16)
+    if Co == 32:
+        # backward-data of a Co-input conv: dY has Ci channels, dX has Co
+        wt = sd.bf16_round_f32(sd.he_normal_conv(rng, Co, Ci))
+        dx = cf.cf_conv3d_bwd_data(xd, to_dev(wt, torch.bfloat16))
+        torch.cuda.synchronize()
+        check_conv_dgrad(x, wt, dx, rng)
+        return
+    y = cf.cf_conv3d_fwd(xd, wd)
+    torch.cuda.synchronize()
+    check_conv_fwd(x, w, y, rng)
+    if D % 2 == 0 and H % 2 == 0 and W % 2 == 0:
+        P, idx = cf.cf_conv3d_pool_fwd(xd, wd, SLOPE)
+        P2, idx2 = cf.cf_pool3d_fwd(y, SLOPE)
+        torch.cuda.synchronize()
+        assert torch.equal(P.view(torch.int16), P2.view(torch.int16)) and torch.equal(idx, idx2)
