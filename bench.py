@@ -17,8 +17,10 @@ baseline.  --workload selects one of the other single-GPU workloads instead
 (one JSON line each); --mfma-peak measures the matrix cores' sustained rate.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -172,7 +174,9 @@ def op_timings(torch, cf, c, dev, reps):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-_C_COMMENT_OR_STRING = None
+# a C/C++ comment, or a string or character literal (kept whole, so that a
+# comment marker inside a literal is not taken for a comment)
+_C_COMMENT_OR_STRING = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
 
 
 def source_digest(paths):
@@ -180,11 +184,6 @@ def source_digest(paths):
     comments and blank lines left out: C/C++ comments in the kernel sources,
     whole-line '#' comments in Python files.  String literals are kept.  A
     change of code changes it; a change of comments does not."""
-    import hashlib
-    import re
-    global _C_COMMENT_OR_STRING
-    if _C_COMMENT_OR_STRING is None:
-        _C_COMMENT_OR_STRING = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
     h = hashlib.sha256()
     for rel in paths:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
